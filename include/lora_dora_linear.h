@@ -1,0 +1,241 @@
+/*
+ * lora_dora_linear.h - C interface of the fused LoRA / DoRA adapted linear
+ * layer for AMD Instinct MI355X (gfx950).
+ *
+ * Method (sources are web pages; each entry point cites the passage that
+ * defines it):
+ *   Y = X . W0^T + s . (X . A^T) . B^T              (LoRA bypass, never forming B.A)
+ *   DoRA rows:  Y = g (.) (X . W0^T + s . (X . A^T) . B^T) + b,
+ *               g_n = m_n / max(||W0_n + s . B_n . A||, eps), the norm from the
+ *               closed form rowsum(W0^2)_n + 2s <B_n, (W0 A^T)_n> + s^2 B_n (A A^T) B_n^T.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Shapes: X [M,K], W0 [N,K], A = lora_down [r,K], B = lora_up [N,r],
+ *    Y and dY [M,N], dX [M,K].  Every tensor is dense row-major (last index
+ *    contiguous, leading dimension = row length).
+ *  - Pointers are DEVICE pointers owned by the caller (inputs, outputs and the
+ *    workspace).  The library keeps no state and never allocates.
+ *  - dtype: LDL_BF16 (bf16 storage, fp32 accumulation) or LDL_F32.  U, V,
+ *    gradients of A, B and the DoRA magnitude are always fp32.
+ *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  Calls
+ *    only enqueue work; they never synchronise the host.
+ *  - Errors: the return value is a status.  Every argument is validated on the
+ *    host before anything is enqueued, so an error leaves all outputs
+ *    untouched.  LDL_E_INVAL: null required pointer, negative size, bad dtype;
+ *    LDL_E_UNSUPPORTED: shape outside what the kernels take (listed per call);
+ *    LDL_E_WORKSPACE: ws_bytes below ldl_workspace_bytes(); LDL_E_HIP: a kernel
+ *    launch failed (hipGetLastError is left set).  M == 0 is valid and does
+ *    nothing (weight-gradient outputs are zeroed).
+ *  - Shape limits of the bf16 / int8 kernels: K and N multiples of 64
+ *    (K multiple of 128 for the int8 base), 1 <= r <= 128, every tensor below
+ *    2 GiB.  M is arbitrary.  The fp32 path takes any positive N, K, r.
+ *  - Determinism: every reduction runs in a fixed order; two calls with the
+ *    same inputs give bitwise identical outputs.
+ */
+#ifndef LORA_DORA_LINEAR_H
+#define LORA_DORA_LINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LDL_OK = 0,
+  LDL_E_INVAL = -1,
+  LDL_E_UNSUPPORTED = -2,
+  LDL_E_WORKSPACE = -3,
+  LDL_E_HIP = -4
+} ldl_status;
+
+typedef enum { LDL_F32 = 0, LDL_BF16 = 1 } ldl_dtype;
+
+/* Operation ids for ldl_workspace_bytes. */
+typedef enum {
+  LDL_OP_LORA_FWD = 0,
+  LDL_OP_LORA_BWD = 1,
+  LDL_OP_DORA_FWD = 2,
+  LDL_OP_DORA_BWD = 3,
+  LDL_OP_SWIGLU_FWD = 4, /* N = hidden size H */
+  LDL_OP_SWIGLU_BWD = 5, /* N = hidden size H */
+  LDL_OP_W8A8_FWD = 6,
+  LDL_OP_W8A8_BWD = 7
+} ldl_op;
+
+/* Human-readable text of a status code (static storage). */
+const char* ldl_status_string(int status);
+
+/* Library version as an integer (major*10000 + minor*100 + patch). */
+int ldl_version(void);
+
+/* Tuning switches (process-wide; not thread-safe against concurrent calls).
+ *   LDL_TUNE_FWD_FUSED_DOWNPROJ (0/1, default 0): compute U = X.A^T inside the
+ *     K-loop of the base GEMM from the LDS-staged X tiles (r <= 32, N multiple
+ *     of 128) instead of a separate rank-r pass before it.
+ * Returns LDL_OK, or LDL_E_INVAL for an unknown key or value. */
+typedef enum { LDL_TUNE_FWD_FUSED_DOWNPROJ = 0 } ldl_tune_key;
+int ldl_set_tuning(int key, int value);
+
+/* Bytes of device workspace the entry point `op` needs for these sizes (256-byte
+ * aligned, 0 when none).  Pure host arithmetic; never fails (returns 0 for
+ * invalid sizes, which the entry point then rejects). */
+size_t ldl_workspace_bytes(int op, int M, int N, int K, int r, int dtype);
+
+/* ------------------------------------------------------------------------ LoRA
+ * Forward of the LoRA bypass linear: the rank-r update is folded into the base
+ * GEMM and the [N,K] product B.A is never formed ("How Unsloth's FastLoRA Kernel
+ * Differs from Standard LoRA Implementations", section "Fused Forward Pass
+ * Architecture"; "LoRA/DoRA fast forward: no weight materialization", commit
+ * message; lora_down / lora_up orientation as in "nunchaku-style kernel fusion -
+ * 20-30% faster training", LoRA-epilogue commit).
+ *   Y = X.W0^T + s.(X.A^T).B^T (+ bias)
+ *   X [M,K], W0 [N,K], A [r,K], B [N,r], bias [N] or NULL (dtype of X), Y [M,N].
+ *   U_save [M,r] fp32 or NULL: receives U = X.A^T for the backward.
+ */
+int lora_linear_fwd(int M, int N, int K, int r, float s, int dtype,
+                    const void* X, const void* W0, const void* A, const void* B,
+                    const void* bias, void* Y, float* U_save,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the LoRA linear with W0 frozen.  The LoRA input gradient is folded
+ * into the dX GEMM epilogue; dA, dB come from skinny contractions with the factor
+ * gradients pre-scaled by s ("How Unsloth's FastLoRA Kernel ...", section "Custom
+ * Backward Pass Implementation"; "nunchaku-style kernel fusion ...", LoRA-epilogue
+ * commit: neither direction builds an (M, out_features) intermediate).
+ *   V = dY.B;  dX = dY.W0 + s.V.A;  dA = s.V^T.X;  dB = s.dY^T.U;  dbias = sum_m dY.
+ *   dY [M,N]; X, W0, A, B as in the forward; U_saved [M,r] fp32 from the forward
+ *   (NULL: recomputed).  dX [M,K] (dtype) or NULL; dA [r,K], dB [N,r] fp32
+ *   (overwritten); dbias [N] fp32 or NULL.
+ */
+int lora_linear_bwd(int M, int N, int K, int r, float s, int dtype,
+                    const void* dY, const void* X, const void* W0, const void* A, const void* B,
+                    const float* U_saved, void* dX, float* dA, float* dB, float* dbias,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ DoRA
+ * Row-scaled DoRA ("dora-rows"), bf16 only.  The row norm of W' = W0 + s.B.A uses
+ * the closed form with the cached constant rowsum(W0^2) and the two rank-sized terms
+ * P = W0.A^T [N,r] and G = A.A^T [r,r]; the bias is added after the row scale; the
+ * norm stays in the autograd graph; eps clamps the norm from below
+ * ("LoRA/DoRA fast forward: no weight materialization", commit message, sections
+ * "What" and "Fidelity").
+ */
+
+/* Once per frozen W0: w0_sumsq[n] = sum_k W0[n,k]^2 (fp32 [N]).  Must be recomputed
+ * whenever W0 changes. */
+int dora_prepare(int N, int K, int dtype, const void* W0, float* w0_sumsq, void* stream);
+
+/* Floats in the DoRA state buffer the forward fills and the backward reads:
+ * norm [N] | g [N] | P [N*r] | G [r*r]. */
+size_t dora_state_floats(int N, int r);
+
+/*   Z = X.W0^T + s.(X.A^T).B^T;  Y = g (.) Z + bias,  g_n = m_n / max(nu_n, eps).
+ *   m [N] fp32 magnitude; w0_sumsq [N] from dora_prepare; bias [N] or NULL;
+ *   Y [M,N]; U_save [M,r] fp32 (required); Z_save [M,N] (dtype, required, read by
+ *   the backward for the magnitude gradient); state: dora_state_floats(N,r) fp32
+ *   (required). */
+int dora_linear_fwd(int M, int N, int K, int r, float s, float eps, int dtype,
+                    const void* X, const void* W0, const void* A, const void* B,
+                    const float* m, const float* w0_sumsq, const void* bias,
+                    void* Y, float* U_save, void* Z_save, float* state,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Gradients of the row-scaled DoRA layer, norm kept in the graph:
+ *   dZ = dY.diag(g);  dg_n = sum_m dY[m,n] Z[m,n];  dm = dg / max(nu, eps);
+ *   w_n = -dg_n m_n / (2 nu_n^3) (0 where nu_n <= eps);
+ *   dX = dZ.W0 + s.(dZ.B).A
+ *   dB = s.dZ^T.U + w (.) (2s.P + 2s^2.B.G)
+ *   dA = s.(dZ.B)^T.X + 2s.(w (.) B)^T.W0 + 2s^2.(B^T diag(w) B).A
+ *   Inputs as in the forward plus dY [M,N], U_saved, Z_saved, state.  Outputs
+ *   dX [M,K] (dtype) or NULL; dA [r,K], dB [N,r], dm [N] fp32; dbias [N] fp32 or NULL. */
+int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype,
+                    const void* dY, const void* X, const void* W0, const void* A, const void* B,
+                    const float* m, const float* U_saved, const void* Z_saved, const float* state,
+                    void* dX, float* dA, float* dB, float* dm, float* dbias,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ SwiGLU MLP
+ * LoRA MLP with SwiGLU: e = lora(X; gate), u = lora(X; up), h = silu(e) * u,
+ * out = lora(h; down) ("How Unsloth's FastLoRA Kernel ...", sections "Fused Forward
+ * Pass Architecture" and "Activation Function Fusion").  bf16 only.  The activation
+ * is fused into the epilogue of the up projection (forward) and of the down
+ * projection's input-gradient GEMM (backward).
+ *   X [M,K]; Wg, Wu [H,K]; Ag, Au [r,K]; Bg, Bu [H,r]; Wd [K,H]; Ad [r,H]; Bd [K,r].
+ *   Out [M,K].  Saved for the backward: E_save, Gu_save, H_save [M,H] (bf16) and
+ *   U_save [M,3r] fp32 = [X.Ag^T | X.Au^T | H.Ad^T].  All required.
+ *   Limits: K and H multiples of 64 (and 128 for the down projection's K = H side),
+ *   r <= 64.
+ */
+int swiglu_lora_mlp_fwd(int M, int K, int H, int r, float s_gate, float s_up, float s_down,
+                        const void* X, const void* Wg, const void* Ag, const void* Bg,
+                        const void* Wu, const void* Au, const void* Bu,
+                        const void* Wd, const void* Ad, const void* Bd,
+                        void* Out, void* E_save, void* Gu_save, void* H_save, float* U_save,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the SwiGLU LoRA MLP (weights frozen, factor gradients pre-scaled by
+ * each adapter's s; "How Unsloth's FastLoRA Kernel ...", section "Custom Backward
+ * Pass Implementation").
+ *   dH = dOut.Wd + s_d.(dOut.Bd).Ad;  dE = dH (.) u (.) silu'(e);  dU = dH (.) silu(e);
+ *   dX = dE.Wg + dU.Wu + s_g.(dE.Bg).Ag + s_u.(dU.Bu).Au; factor gradients as in
+ *   lora_linear_bwd for each projection.  dX [M,K] bf16 or NULL; dAg, dAu [r,K],
+ *   dBg, dBu [H,r], dAd [r,H], dBd [K,r] fp32. */
+int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, float s_down,
+                        const void* dOut, const void* X,
+                        const void* Wg, const void* Ag, const void* Bg,
+                        const void* Wu, const void* Au, const void* Bu,
+                        const void* Wd, const void* Ad, const void* Bd,
+                        const void* E_saved, const void* Gu_saved, const void* H_saved,
+                        const float* U_saved,
+                        void* dX, float* dAg, float* dBg, float* dAu, float* dBu,
+                        float* dAd, float* dBd,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ W8A8
+ * int8 weight x int8 activation base with per-row (activation) and per-column
+ * (weight) dequant scales and the rank-tiled LoRA epilogue; the int32 product is
+ * never stored ("nunchaku-style kernel fusion - 20-30% faster training",
+ * LoRA-epilogue commit, the comment on activations and the unification commit).
+ * Quantisation is symmetric with divisor 127: scale = absmax / 127 (fp32),
+ * code = clamp(rint(x / scale), -127, 127) with the quotient in fp32 and ties to
+ * even; a zero row has scale 0 and codes 0.
+ */
+
+/* Per-output-channel weight quantisation, once per frozen W0 (dtype of W0: LDL_F32
+ * or LDL_BF16): Wq [N,K] int8, sw [N] fp32. */
+int w8a8_quantize_weight(int N, int K, int dtype, const void* W0, int8_t* Wq, float* sw, void* stream);
+
+/* Per-row activation quantisation: Xq [M,K] int8, sx [M] fp32 from bf16 X. */
+int w8a8_quantize_rows(int M, int K, const void* X, int8_t* Xq, float* sx, void* stream);
+
+/* Raw int32 product C = Xq.Wq^T (the "raw product" epilogue of the 8-bit core).
+ * C [M,N] int32.  Exact. */
+int int8_gemm_raw(int M, int N, int K, const int8_t* Xq, const int8_t* Wq, int32_t* C, void* stream);
+
+/*   Y = (Xq.Wq^T) . sx[m] . sw[n] + s.(X.A^T).B^T (+ bias), Xq / sx quantised from X
+ *   in the call.  X [M,K] bf16; Wq [N,K] int8; sw [N] fp32; A, B, bias bf16.
+ *   Y [M,N] bf16.  Xq_save [M,K] int8 or NULL, sx_save [M] fp32 or NULL (both NULL or
+ *   both set), U_save [M,r] fp32 or NULL.  The LoRA branch sees X, not Xq. */
+int w8a8_lora_linear_fwd(int M, int N, int K, int r, float s,
+                         const void* X, const int8_t* Wq, const float* sw,
+                         const void* A, const void* B, const void* bias,
+                         void* Y, int8_t* Xq_save, float* sx_save, float* U_save,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Straight-through backward: dX = dY.(diag(sw).Wq + s.B.A) (the dequantised weight,
+ * bf16 MFMA), dA = s.(dY.B)^T.X, dB = s.dY^T.U.  dX [M,K] bf16 or NULL; dA [r,K],
+ * dB [N,r] fp32; U_saved [M,r] fp32 or NULL (recomputed). */
+int w8a8_lora_linear_bwd(int M, int N, int K, int r, float s,
+                         const void* dY, const void* X, const int8_t* Wq, const float* sw,
+                         const void* A, const void* B, const float* U_saved,
+                         void* dX, float* dA, float* dB,
+                         void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_DORA_LINEAR_H */

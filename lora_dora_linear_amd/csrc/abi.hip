@@ -1,0 +1,695 @@
+// C entry points: host-side validation, workspace layout and the launch
+// sequence of each layer.  Nothing here allocates, synchronises or touches an
+// output before every argument has been checked.
+#include <cstring>
+
+#include "../../include/lora_dora_linear.h"
+#include "internal.hpp"
+
+using namespace ldl;
+
+namespace {
+
+int g_fwd_fused = 0;   // LDL_TUNE_FWD_FUSED_DOWNPROJ
+
+constexpr size_t kAlign = 256;
+constexpr size_t kMaxBytes = (size_t)1 << 31;   // buffer resources take 31-bit sizes
+
+// Bump allocator over the caller's workspace; with base == nullptr it only sizes.
+struct Bump {
+  char* base;
+  size_t off = 0;
+  explicit Bump(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t count) {
+    off = (off + kAlign - 1) / kAlign * kAlign;
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+  size_t size() const { return (off + kAlign - 1) / kAlign * kAlign; }
+};
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+inline bool al(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p && !aligned16(p)) return false;
+  return true;
+}
+inline bool nonnull(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!p) return false;
+  return true;
+}
+inline bool small(size_t rows, size_t cols, size_t elt) { return rows * cols * elt < kMaxBytes; }
+inline hipStream_t S(void* st) { return static_cast<hipStream_t>(st); }
+
+#define LDL_TRY(expr)                         \
+  do {                                        \
+    if ((expr) != hipSuccess) return LDL_E_HIP; \
+  } while (0)
+
+// ------------------------------------------------------------------ workspace plans
+struct LoraBwdWs {
+  uint16_t* Bt; float* V; float* U; float* partB; float* csB; float* partA;
+  int nsB, msB, nsA, msA, rp;
+};
+LoraBwdWs plan_lora_bwd(Bump& b, int M, int N, int K, int r, bool need_u) {
+  LoraBwdWs w{};
+  w.rp = colproj_rp(r);
+  colproj_plan(M, N, &w.nsB, &w.msB);
+  colproj_plan(M, K, &w.nsA, &w.msA);
+  w.Bt = b.take<uint16_t>((size_t)r * N);
+  w.V = b.take<float>((size_t)M * r);
+  w.U = need_u ? b.take<float>((size_t)M * r) : nullptr;
+  w.partB = b.take<float>((size_t)w.nsB * N * w.rp);
+  w.csB = b.take<float>((size_t)w.nsB * N);
+  w.partA = b.take<float>((size_t)w.nsA * K * w.rp);
+  return w;
+}
+
+struct DoraBwdWs {
+  uint16_t* Bt; float* V; float* partT; float* cs; float* wB; float* partA; float* partQ; float* Qm;
+  float* partbias; float* csbias;
+  int nsT, msT, nsA, msA, nsW, msW, nsQ, msQ, rp;
+};
+DoraBwdWs plan_dora_bwd(Bump& b, int M, int N, int K, int r) {
+  DoraBwdWs w{};
+  w.rp = colproj_rp(r);
+  colproj_plan(M, N, &w.nsT, &w.msT);
+  colproj_plan(M, K, &w.nsA, &w.msA);
+  colproj_plan(N, K, &w.nsW, &w.msW);
+  colproj_plan(N, r, &w.nsQ, &w.msQ);
+  w.Bt = b.take<uint16_t>((size_t)r * N);
+  w.V = b.take<float>((size_t)M * r);
+  w.partT = b.take<float>((size_t)w.nsT * N * w.rp);
+  w.cs = b.take<float>((size_t)w.nsT * N);
+  w.wB = b.take<float>((size_t)N * r);
+  w.partA = b.take<float>((size_t)(w.nsA + w.nsW) * K * w.rp);
+  w.partQ = b.take<float>((size_t)w.nsQ * r * w.rp);
+  w.Qm = b.take<float>((size_t)r * r);
+  w.partbias = b.take<float>((size_t)w.nsT * N * 16);
+  w.csbias = b.take<float>((size_t)w.nsT * N);
+  return w;
+}
+
+struct MlpBwdWs {
+  uint16_t* Bdt; uint16_t* Bgt; uint16_t* But; float* Vd; float* Vgu; uint16_t* dEGu;
+  float* partDd; float* partAd; float* partBg; float* partBu; float* partAgu;
+  int nsDd, msDd, nsAd, msAd, nsBg, msBg, nsAgu, msAgu, rp, rp2;
+};
+MlpBwdWs plan_mlp_bwd(Bump& b, int M, int K, int H, int r) {
+  MlpBwdWs w{};
+  w.rp = colproj_rp(r);
+  w.rp2 = colproj_rp(2 * r);
+  colproj_plan(M, K, &w.nsDd, &w.msDd);
+  colproj_plan(M, H, &w.nsAd, &w.msAd);
+  colproj_plan(M, H, &w.nsBg, &w.msBg);
+  colproj_plan(M, K, &w.nsAgu, &w.msAgu);
+  w.Bdt = b.take<uint16_t>((size_t)r * K);
+  w.Bgt = b.take<uint16_t>((size_t)r * H);
+  w.But = b.take<uint16_t>((size_t)r * H);
+  w.Vd = b.take<float>((size_t)M * r);
+  w.Vgu = b.take<float>((size_t)M * 2 * r);
+  w.dEGu = b.take<uint16_t>((size_t)M * 2 * H);
+  w.partDd = b.take<float>((size_t)w.nsDd * K * w.rp);
+  w.partAd = b.take<float>((size_t)w.nsAd * H * w.rp);
+  w.partBg = b.take<float>((size_t)w.nsBg * H * w.rp);
+  w.partBu = b.take<float>((size_t)w.nsBg * H * w.rp);
+  w.partAgu = b.take<float>((size_t)w.nsAgu * K * w.rp2);
+  return w;
+}
+
+// ------------------------------------------------------------------ small launch helpers
+GemmParams gp0() {
+  GemmParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.s_epi = 1.f;
+  return p;
+}
+
+hipError_t rowproj(int M, int K, int R, const void* P, int ldp, const void* q0, const void* q1, int R0, int ldq,
+                   float* out, int ldo, float scale, hipStream_t st) {
+  RowProjParams p;
+  p.M = M; p.K = K; p.R = R; p.R0 = R0;
+  p.P = static_cast<const uint16_t*>(P); p.ldp = ldp;
+  p.q0 = static_cast<const uint16_t*>(q0); p.q1 = static_cast<const uint16_t*>(q1 ? q1 : q0); p.ldq = ldq;
+  p.out = out; p.ldo = ldo; p.scale = scale;
+  return launch_rowproj(p, st);
+}
+
+hipError_t colproj(int M, int C, int R, const void* X, int ldx, const float* Sm, int lds, float s_in,
+                   const void* Z, int ldz, int mode, int nsplit, int msplit, float* part, float* cspart,
+                   hipStream_t st) {
+  ColProjParams p;
+  p.M = M; p.C = C; p.R = R;
+  p.X = static_cast<const uint16_t*>(X); p.ldx = ldx;
+  p.S = Sm; p.lds = lds; p.s_in = s_in;
+  p.Z = static_cast<const uint16_t*>(Z); p.ldz = ldz; p.colsum_mode = mode;
+  p.msplit = msplit; p.part = part; p.cspart = cspart;
+  return launch_colproj(p, nsplit, st);
+}
+
+// out[rows, cols] = alpha * sum over nsplit partials (+ row scale) (+ addend)
+hipError_t reduce(int rows, int cols, const float* part, size_t pstride, int nsplit, int rp, bool trans, float alpha,
+                  float* out, int ldo, hipStream_t st, const float* rowscale = nullptr,
+                  const float* Qm = nullptr, int ldq = 0, int rq = 0, const void* Am = nullptr, int lda = 0,
+                  float alpha2 = 0.f) {
+  ReduceParams p;
+  p.rows = rows; p.cols = cols; p.part = part; p.pstride = pstride; p.nsplit = nsplit; p.rp = rp;
+  p.trans = trans ? 1 : 0; p.alpha = alpha; p.rowscale = rowscale;
+  p.Qm = Qm; p.ldq = ldq; p.rq = rq; p.Am = static_cast<const uint16_t*>(Am); p.lda = lda; p.alpha2 = alpha2;
+  p.out = out; p.ldo = ldo;
+  return launch_reduce(p, st);
+}
+
+hipError_t zero(float* p, size_t n, hipStream_t st) { return p ? launch_fill_zero(p, n, st) : hipSuccess; }
+
+// Common shape checks of the bf16 layer: N, K multiples of 64, r in [1, 128], sizes < 2 GiB.
+int check_bf16_layer(int M, int N, int K, int r) {
+  if (M < 0 || N <= 0 || K <= 0 || r <= 0) return LDL_E_INVAL;
+  if (r > 128 || N % 64 || K % 64) return LDL_E_UNSUPPORTED;
+  if (!small(M + 256, K, 2) || !small(N, K, 2) || !small(M + 256, N, 2) || !small(M, 2 * r, 4)) return LDL_E_UNSUPPORTED;
+  return LDL_OK;
+}
+
+// ------------------------------------------------------------------ fp32 path
+hipError_t f32(int M, int N, int K, const float* A, long sam, long sak, const float* B, long sbk, long sbn,
+               float* C, int ldc, float alpha, float beta, const float* bias, hipStream_t st) {
+  F32GemmParams p;
+  p.M = M; p.N = N; p.K = K; p.A = A; p.sam = sam; p.sak = sak; p.B = B; p.sbk = sbk; p.sbn = sbn;
+  p.C = C; p.ldc = ldc; p.alpha = alpha; p.beta = beta; p.bias = bias;
+  return launch_f32_gemm(p, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ldl_status_string(int status) {
+  switch (status) {
+    case LDL_OK: return "ok";
+    case LDL_E_INVAL: return "invalid argument (null pointer, negative size or bad dtype)";
+    case LDL_E_UNSUPPORTED: return "unsupported shape or alignment for these kernels";
+    case LDL_E_WORKSPACE: return "workspace too small";
+    case LDL_E_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int ldl_version(void) { return 100; }
+
+int ldl_set_tuning(int key, int value) {
+  if (key == LDL_TUNE_FWD_FUSED_DOWNPROJ && (value == 0 || value == 1)) {
+    g_fwd_fused = value;
+    return LDL_OK;
+  }
+  return LDL_E_INVAL;
+}
+
+size_t dora_state_floats(int N, int r) {
+  if (N <= 0 || r <= 0) return 0;
+  return (size_t)2 * N + (size_t)N * r + (size_t)r * r;
+}
+
+size_t ldl_workspace_bytes(int op, int M, int N, int K, int r, int dtype) {
+  if (M < 0 || N <= 0 || K <= 0 || r <= 0) return 0;
+  Bump b(nullptr);
+  switch (op) {
+    case LDL_OP_LORA_FWD:
+    case LDL_OP_W8A8_FWD:
+      b.take<float>((size_t)M * r);            // U when not saved by the caller
+      if (op == LDL_OP_W8A8_FWD) { b.take<int8_t>((size_t)M * K); b.take<float>((size_t)M); }
+      break;
+    case LDL_OP_LORA_BWD:
+    case LDL_OP_W8A8_BWD:
+      if (dtype == LDL_F32 && op == LDL_OP_LORA_BWD) { b.take<float>((size_t)M * r); b.take<float>((size_t)M * r); }
+      else plan_lora_bwd(b, M, N, K, r, true);
+      break;
+    case LDL_OP_DORA_FWD:
+      break;
+    case LDL_OP_DORA_BWD:
+      plan_dora_bwd(b, M, N, K, r);
+      break;
+    case LDL_OP_SWIGLU_FWD:
+      break;
+    case LDL_OP_SWIGLU_BWD:
+      plan_mlp_bwd(b, M, K, N, r);
+      break;
+    default:
+      return 0;
+  }
+  return b.size();
+}
+
+// =========================================================================== LoRA
+int lora_linear_fwd(int M, int N, int K, int r, float s, int dtype, const void* X, const void* W0, const void* A,
+                    const void* B, const void* bias, void* Y, float* U_save, void* ws, size_t ws_bytes,
+                    void* stream) {
+  if (!nonnull({W0, A, B}) || (M > 0 && !nonnull({X, Y}))) return LDL_E_INVAL;
+  if (dtype != LDL_F32 && dtype != LDL_BF16) return LDL_E_INVAL;
+  if (M < 0 || N <= 0 || K <= 0 || r <= 0) return LDL_E_INVAL;
+  if (!al({X, W0, A, B, bias, Y, U_save, ws})) return LDL_E_UNSUPPORTED;
+  if (ldl_workspace_bytes(LDL_OP_LORA_FWD, M, N, K, r, dtype) > ws_bytes && !U_save) return LDL_E_WORKSPACE;
+  if (ws_bytes > 0 && !ws) return LDL_E_INVAL;
+  const hipStream_t st = S(stream);
+  Bump wb(ws);
+  float* U = U_save ? U_save : wb.take<float>((size_t)M * r);
+  if (M == 0) return LDL_OK;
+
+  if (dtype == LDL_F32) {
+    const float *x = (const float*)X, *w = (const float*)W0, *a = (const float*)A, *bb = (const float*)B;
+    LDL_TRY(f32(M, r, K, x, K, 1, a, 1, K, U, r, 1.f, 0.f, nullptr, st));
+    LDL_TRY(f32(M, N, K, x, K, 1, w, 1, K, (float*)Y, N, 1.f, 0.f, (const float*)bias, st));
+    LDL_TRY(f32(M, N, r, U, r, 1, bb, 1, r, (float*)Y, N, s, 1.f, nullptr, st));
+    return LDL_OK;
+  }
+
+  const int chk = check_bf16_layer(M, N, K, r);
+  if (chk != LDL_OK) return chk;
+  GemmParams p = gp0();
+  p.M = M; p.N = N; p.K = K;
+  p.a = X; p.lda = K; p.b0 = W0; p.ldb = K; p.kseg = K;
+  p.r_epi = r; p.s_epi = s; p.e0 = B; p.e1 = B; p.e_ldn = r; p.e_ldj = 1; p.e_jsplit = r;
+  p.bias = bias; p.out = Y; p.ldo = N;
+  if (g_fwd_fused && r <= 32 && N % 128 == 0) {
+    p.side = A; p.r_side = r; p.side_save = U_save; p.ld_side_save = r;
+    LDL_TRY(launch_gemm(GK_NT_FUSED, p, st));
+    return LDL_OK;
+  }
+  LDL_TRY(rowproj(M, K, r, X, K, A, nullptr, r, K, U, r, 1.f, st));
+  p.S = U; p.ld_s = r;
+  LDL_TRY(launch_gemm(GK_NT_PLAIN, p, st));
+  return LDL_OK;
+}
+
+int lora_linear_bwd(int M, int N, int K, int r, float s, int dtype, const void* dY, const void* X, const void* W0,
+                    const void* A, const void* B, const float* U_saved, void* dX, float* dA, float* dB, float* dbias,
+                    void* ws, size_t ws_bytes, void* stream) {
+  if (!nonnull({W0, A, B, dA, dB}) || (M > 0 && !nonnull({dY, X}))) return LDL_E_INVAL;
+  if (dtype != LDL_F32 && dtype != LDL_BF16) return LDL_E_INVAL;
+  if (M < 0 || N <= 0 || K <= 0 || r <= 0) return LDL_E_INVAL;
+  if (!al({dY, X, W0, A, B, U_saved, dX, dA, dB, dbias, ws})) return LDL_E_UNSUPPORTED;
+  if (dtype == LDL_BF16) {
+    const int chk = check_bf16_layer(M, N, K, r);
+    if (chk != LDL_OK) return chk;
+  }
+  if (ldl_workspace_bytes(LDL_OP_LORA_BWD, M, N, K, r, dtype) > ws_bytes) return LDL_E_WORKSPACE;
+  if (!ws) return LDL_E_INVAL;
+  const hipStream_t st = S(stream);
+  if (M == 0) {
+    LDL_TRY(zero(dA, (size_t)r * K, st));
+    LDL_TRY(zero(dB, (size_t)N * r, st));
+    LDL_TRY(zero(dbias, (size_t)N, st));
+    return LDL_OK;
+  }
+
+  if (dtype == LDL_F32) {
+    Bump wb(ws);
+    float* V = wb.take<float>((size_t)M * r);
+    float* Uw = wb.take<float>((size_t)M * r);
+    const float *dy = (const float*)dY, *x = (const float*)X, *w = (const float*)W0, *a = (const float*)A,
+                *bb = (const float*)B;
+    const float* U = U_saved;
+    if (!U) {
+      LDL_TRY(f32(M, r, K, x, K, 1, a, 1, K, Uw, r, 1.f, 0.f, nullptr, st));
+      U = Uw;
+    }
+    LDL_TRY(f32(M, r, N, dy, N, 1, bb, r, 1, V, r, 1.f, 0.f, nullptr, st));
+    if (dX) {
+      LDL_TRY(f32(M, K, N, dy, N, 1, w, K, 1, (float*)dX, K, 1.f, 0.f, nullptr, st));
+      LDL_TRY(f32(M, K, r, V, r, 1, a, K, 1, (float*)dX, K, s, 1.f, nullptr, st));
+    }
+    LDL_TRY(f32(r, K, M, V, 1, r, x, K, 1, dA, K, s, 0.f, nullptr, st));
+    LDL_TRY(f32(N, r, M, dy, 1, N, U, r, 1, dB, r, s, 0.f, nullptr, st));
+    if (dbias) LDL_TRY(launch_f32_colsum(dy, M, N, dbias, st));
+    return LDL_OK;
+  }
+
+  Bump wb(ws);
+  LoraBwdWs w = plan_lora_bwd(wb, M, N, K, r, true);
+  const float* U = U_saved;
+  if (!U) {
+    LDL_TRY(rowproj(M, K, r, X, K, A, nullptr, r, K, w.U, r, 1.f, st));
+    U = w.U;
+  }
+  // V = dY.B  (B^T staged so both operands are contiguous along the reduction)
+  LDL_TRY(launch_transpose_scale(static_cast<const uint16_t*>(B), nullptr, N, r, w.Bt, st));
+  LDL_TRY(rowproj(M, N, r, dY, N, w.Bt, nullptr, r, N, w.V, r, 1.f, st));
+  if (dX) {
+    GemmParams p = gp0();
+    p.M = M; p.N = K; p.K = N;
+    p.a = dY; p.lda = N; p.b0 = W0; p.b1 = W0; p.ldb = K; p.kseg = N;
+    p.S = w.V; p.ld_s = r; p.r_epi = r; p.s_epi = s;
+    p.e0 = A; p.e1 = A; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = r;
+    p.out = dX; p.ldo = K;
+    LDL_TRY(launch_gemm(GK_NN_PLAIN, p, st));
+  }
+  // dB = s.dY^T.U  (+ dbias = column sums of dY in the same pass)
+  LDL_TRY(colproj(M, N, r, dY, N, U, r, 1.f, nullptr, 0, dbias ? 2 : 0, w.nsB, w.msB, w.partB, w.csB, st));
+  LDL_TRY(reduce(N, r, w.partB, (size_t)N * w.rp, w.nsB, w.rp, false, s, dB, r, st));
+  if (dbias) LDL_TRY(launch_reduce_colsum(w.csB, w.nsB, N, dbias, st));
+  // dA = s.V^T.X
+  LDL_TRY(colproj(M, K, r, X, K, w.V, r, 1.f, nullptr, 0, 0, w.nsA, w.msA, w.partA, nullptr, st));
+  LDL_TRY(reduce(r, K, w.partA, (size_t)K * w.rp, w.nsA, w.rp, true, s, dA, K, st));
+  return LDL_OK;
+}
+
+// =========================================================================== DoRA
+int dora_prepare(int N, int K, int dtype, const void* W0, float* w0_sumsq, void* stream) {
+  if (!nonnull({W0, w0_sumsq})) return LDL_E_INVAL;
+  if (N <= 0 || K <= 0) return LDL_E_INVAL;
+  if (dtype != LDL_F32 && dtype != LDL_BF16) return LDL_E_INVAL;
+  if (!al({W0, w0_sumsq})) return LDL_E_UNSUPPORTED;
+  if (dtype == LDL_BF16 && K % 8) return LDL_E_UNSUPPORTED;
+  LDL_TRY(launch_rowsumsq(W0, dtype == LDL_BF16, N, K, w0_sumsq, S(stream)));
+  return LDL_OK;
+}
+
+static int dora_check(int M, int N, int K, int r, int dtype) {
+  if (dtype != LDL_BF16) return dtype == LDL_F32 ? LDL_E_UNSUPPORTED : LDL_E_INVAL;
+  const int chk = check_bf16_layer(M, N, K, r);
+  if (chk != LDL_OK) return chk;
+  if (r % 8) return LDL_E_UNSUPPORTED;
+  return LDL_OK;
+}
+
+int dora_linear_fwd(int M, int N, int K, int r, float s, float eps, int dtype, const void* X, const void* W0,
+                    const void* A, const void* B, const float* m, const float* w0_sumsq, const void* bias, void* Y,
+                    float* U_save, void* Z_save, float* state, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  if (!nonnull({W0, A, B, m, w0_sumsq, state}) || (M > 0 && !nonnull({X, Y, U_save, Z_save}))) return LDL_E_INVAL;
+  if (M < 0 || N <= 0 || K <= 0 || r <= 0 || !(eps >= 0.f)) return LDL_E_INVAL;
+  const int chk = dora_check(M, N, K, r, dtype);
+  if (chk != LDL_OK) return chk;
+  if (!al({X, W0, A, B, m, w0_sumsq, bias, Y, U_save, Z_save, state})) return LDL_E_UNSUPPORTED;
+  const hipStream_t st = S(stream);
+  float* norm = state;
+  float* g = state + N;
+  float* P = state + 2 * (size_t)N;
+  float* G = P + (size_t)N * r;
+  // the norm terms: P = W0.A^T, G = A.A^T, then nu and g (independent of M)
+  LDL_TRY(rowproj(N, K, r, W0, K, A, nullptr, r, K, P, r, 1.f, st));
+  LDL_TRY(rowproj(r, K, r, A, K, A, nullptr, r, K, G, r, 1.f, st));
+  LDL_TRY(launch_dora_norm(N, r, s, eps, w0_sumsq, P, G, static_cast<const uint16_t*>(B), m, norm, g, st));
+  if (M == 0) return LDL_OK;
+  LDL_TRY(rowproj(M, K, r, X, K, A, nullptr, r, K, U_save, r, 1.f, st));
+  GemmParams p = gp0();
+  p.M = M; p.N = N; p.K = K;
+  p.a = X; p.lda = K; p.b0 = W0; p.ldb = K; p.kseg = K;
+  p.S = U_save; p.ld_s = r; p.r_epi = r; p.s_epi = s;
+  p.e0 = B; p.e1 = B; p.e_ldn = r; p.e_ldj = 1; p.e_jsplit = r;
+  p.col_scale = g; p.bias = bias;
+  p.out = Y; p.ldo = N; p.out2 = Z_save; p.ldo2 = N;
+  LDL_TRY(launch_gemm(GK_NT_DORA, p, st));
+  return LDL_OK;
+}
+
+int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, const void* dY, const void* X,
+                    const void* W0, const void* A, const void* B, const float* m, const float* U_saved,
+                    const void* Z_saved, const float* state, void* dX, float* dA, float* dB, float* dm,
+                    float* dbias, void* ws, size_t ws_bytes, void* stream) {
+  if (!nonnull({W0, A, B, m, state, dA, dB, dm, ws}) || (M > 0 && !nonnull({dY, X, U_saved, Z_saved})))
+    return LDL_E_INVAL;
+  if (M < 0 || N <= 0 || K <= 0 || r <= 0 || !(eps >= 0.f)) return LDL_E_INVAL;
+  const int chk = dora_check(M, N, K, r, dtype);
+  if (chk != LDL_OK) return chk;
+  if (!al({dY, X, W0, A, B, m, U_saved, Z_saved, state, dX, dA, dB, dm, dbias, ws})) return LDL_E_UNSUPPORTED;
+  if (ldl_workspace_bytes(LDL_OP_DORA_BWD, M, N, K, r, dtype) > ws_bytes) return LDL_E_WORKSPACE;
+  const hipStream_t st = S(stream);
+  const float* norm = state;
+  const float* g = state + N;
+  const float* P = state + 2 * (size_t)N;
+  const float* G = P + (size_t)N * r;
+  Bump wb(ws);
+  DoraBwdWs w = plan_dora_bwd(wb, M, N, K, r);
+  const uint16_t* Bh = static_cast<const uint16_t*>(B);
+
+  // dg and dZ^T.U in one pass over dY (and Z); M == 0 gives zero partials
+  if (M > 0) {
+    LDL_TRY(colproj(M, N, r, dY, N, U_saved, r, 1.f, Z_saved, N, 1, w.nsT, w.msT, w.partT, w.cs, st));
+  } else {
+    LDL_TRY(zero(w.partT, (size_t)w.nsT * N * w.rp, st));
+    LDL_TRY(zero(w.cs, (size_t)w.nsT * N, st));
+  }
+  // dB, dm and wB = 2s.w.B per output row
+  LDL_TRY(launch_dora_finalize(N, r, s, eps, w.partT, w.cs, w.nsT, w.rp, norm, g, m, P, G, Bh, dB, dm, w.wB, st));
+  if (M > 0) {
+    // V = (dY.diag(g)).B
+    LDL_TRY(launch_transpose_scale(Bh, g, N, r, w.Bt, st));
+    LDL_TRY(rowproj(M, N, r, dY, N, w.Bt, nullptr, r, N, w.V, r, 1.f, st));
+    if (dX) {
+      GemmParams p = gp0();
+      p.M = M; p.N = K; p.K = N;
+      p.a = dY; p.lda = N; p.a_colscale = g; p.b0 = W0; p.b1 = W0; p.ldb = K; p.kseg = N;
+      p.S = w.V; p.ld_s = r; p.r_epi = r; p.s_epi = s;
+      p.e0 = A; p.e1 = A; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = r;
+      p.out = dX; p.ldo = K;
+      LDL_TRY(launch_gemm(GK_NN_SCALE, p, st));
+    }
+    // s.V^T.X into the first nsA partials of dA
+    LDL_TRY(colproj(M, K, r, X, K, w.V, r, s, nullptr, 0, 0, w.nsA, w.msA, w.partA, nullptr, st));
+  } else {
+    LDL_TRY(zero(w.partA, (size_t)w.nsA * K * w.rp, st));
+  }
+  // (2s.w.B)^T.W0 into the next nsW partials; Q = B^T.(2s.w.B)
+  LDL_TRY(colproj(N, K, r, W0, K, w.wB, r, 1.f, nullptr, 0, 0, w.nsW, w.msW, w.partA + (size_t)w.nsA * K * w.rp,
+                  nullptr, st));
+  LDL_TRY(colproj(N, r, r, B, r, w.wB, r, 1.f, nullptr, 0, 0, w.nsQ, w.msQ, w.partQ, nullptr, st));
+  LDL_TRY(reduce(r, r, w.partQ, (size_t)r * w.rp, w.nsQ, w.rp, false, 1.f, w.Qm, r, st));
+  // dA = sum of all partials + s.Q.A   (2s^2 B^T diag(w) B A = s.Q.A)
+  LDL_TRY(reduce(r, K, w.partA, (size_t)K * w.rp, w.nsA + w.nsW, w.rp, true, 1.f, dA, K, st, nullptr, w.Qm, r, r, A,
+                 K, s));
+  if (dbias) {
+    if (M > 0) {
+      LDL_TRY(colproj(M, N, 0, dY, N, nullptr, 0, 1.f, nullptr, 0, 2, w.nsT, w.msT, w.partbias, w.csbias, st));
+      LDL_TRY(launch_reduce_colsum(w.csbias, w.nsT, N, dbias, st));
+    } else {
+      LDL_TRY(zero(dbias, (size_t)N, st));
+    }
+  }
+  return LDL_OK;
+}
+
+// =========================================================================== SwiGLU MLP
+static int mlp_check(int M, int K, int H, int r) {
+  if (M < 0 || K <= 0 || H <= 0 || r <= 0) return LDL_E_INVAL;
+  if (r > 64 || K % 64 || H % 64) return LDL_E_UNSUPPORTED;
+  if (!small(M + 256, 2 * (size_t)H, 2) || !small(H, K, 2) || !small(M + 256, K, 2)) return LDL_E_UNSUPPORTED;
+  return LDL_OK;
+}
+
+int swiglu_lora_mlp_fwd(int M, int K, int H, int r, float s_gate, float s_up, float s_down, const void* X,
+                        const void* Wg, const void* Ag, const void* Bg, const void* Wu, const void* Au,
+                        const void* Bu, const void* Wd, const void* Ad, const void* Bd, void* Out, void* E_save,
+                        void* Gu_save, void* H_save, float* U_save, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  if (!nonnull({Wg, Ag, Bg, Wu, Au, Bu, Wd, Ad, Bd}) || (M > 0 && !nonnull({X, Out, E_save, Gu_save, H_save, U_save})))
+    return LDL_E_INVAL;
+  const int chk = mlp_check(M, K, H, r);
+  if (chk != LDL_OK) return chk;
+  if (!al({X, Wg, Ag, Bg, Wu, Au, Bu, Wd, Ad, Bd, Out, E_save, Gu_save, H_save, U_save})) return LDL_E_UNSUPPORTED;
+  if (M == 0) return LDL_OK;
+  const hipStream_t st = S(stream);
+  const int r3 = 3 * r;
+  // [U_g | U_u] = X.[Ag; Au]^T in one pass over X
+  LDL_TRY(rowproj(M, K, 2 * r, X, K, Ag, Au, r, K, U_save, r3, 1.f, st));
+  GemmParams p = gp0();
+  p.M = M; p.N = H; p.K = K;
+  p.a = X; p.lda = K; p.b0 = Wg; p.ldb = K; p.kseg = K;
+  p.S = U_save; p.ld_s = r3; p.r_epi = r; p.s_epi = s_gate;
+  p.e0 = Bg; p.e1 = Bg; p.e_ldn = r; p.e_ldj = 1; p.e_jsplit = r;
+  p.out = E_save; p.ldo = H;
+  LDL_TRY(launch_gemm(GK_NT_PLAIN, p, st));
+  p.b0 = Wu; p.S = U_save + r; p.s_epi = s_up; p.e0 = Bu; p.e1 = Bu;
+  p.out = nullptr; p.aux0 = E_save; p.ld_aux0 = H; p.out2 = Gu_save; p.ldo2 = H; p.out3 = H_save; p.ldo3 = H;
+  LDL_TRY(launch_gemm(GK_NT_SWIGLU, p, st));
+  // U_d = H.Ad^T, then the down projection
+  LDL_TRY(rowproj(M, H, r, H_save, H, Ad, nullptr, r, H, U_save + 2 * r, r3, 1.f, st));
+  GemmParams q = gp0();
+  q.M = M; q.N = K; q.K = H;
+  q.a = H_save; q.lda = H; q.b0 = Wd; q.ldb = H; q.kseg = H;
+  q.S = U_save + 2 * r; q.ld_s = r3; q.r_epi = r; q.s_epi = s_down;
+  q.e0 = Bd; q.e1 = Bd; q.e_ldn = r; q.e_ldj = 1; q.e_jsplit = r;
+  q.out = Out; q.ldo = K;
+  LDL_TRY(launch_gemm(GK_NT_PLAIN, q, st));
+  return LDL_OK;
+}
+
+int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, float s_down, const void* dOut,
+                        const void* X, const void* Wg, const void* Ag, const void* Bg, const void* Wu, const void* Au,
+                        const void* Bu, const void* Wd, const void* Ad, const void* Bd, const void* E_saved,
+                        const void* Gu_saved, const void* H_saved, const float* U_saved, void* dX, float* dAg,
+                        float* dBg, float* dAu, float* dBu, float* dAd, float* dBd, void* ws, size_t ws_bytes,
+                        void* stream) {
+  if (!nonnull({Wg, Ag, Bg, Wu, Au, Bu, Wd, Ad, Bd, dAg, dBg, dAu, dBu, dAd, dBd, ws}) ||
+      (M > 0 && !nonnull({dOut, X, E_saved, Gu_saved, H_saved, U_saved})))
+    return LDL_E_INVAL;
+  const int chk = mlp_check(M, K, H, r);
+  if (chk != LDL_OK) return chk;
+  if (!al({dOut, X, Wg, Ag, Bg, Wu, Au, Bu, Wd, Ad, Bd, E_saved, Gu_saved, H_saved, U_saved, dX, dAg, dBg, dAu, dBu,
+           dAd, dBd, ws}))
+    return LDL_E_UNSUPPORTED;
+  if (ldl_workspace_bytes(LDL_OP_SWIGLU_BWD, M, H, K, r, LDL_BF16) > ws_bytes) return LDL_E_WORKSPACE;
+  const hipStream_t st = S(stream);
+  if (M == 0) {
+    LDL_TRY(zero(dAg, (size_t)r * K, st)); LDL_TRY(zero(dAu, (size_t)r * K, st));
+    LDL_TRY(zero(dBg, (size_t)H * r, st)); LDL_TRY(zero(dBu, (size_t)H * r, st));
+    LDL_TRY(zero(dAd, (size_t)r * H, st)); LDL_TRY(zero(dBd, (size_t)K * r, st));
+    return LDL_OK;
+  }
+  Bump wb(ws);
+  MlpBwdWs w = plan_mlp_bwd(wb, M, K, H, r);
+  const int r3 = 3 * r;
+  const float* Ug = U_saved;
+  const float* Uu = U_saved + r;
+  const float* Ud = U_saved + 2 * r;
+
+  // ---- down projection: V_d = dOut.Bd, dBd = s_d.dOut^T.U_d
+  LDL_TRY(launch_transpose_scale(static_cast<const uint16_t*>(Bd), nullptr, K, r, w.Bdt, st));
+  LDL_TRY(rowproj(M, K, r, dOut, K, w.Bdt, nullptr, r, K, w.Vd, r, 1.f, st));
+  LDL_TRY(colproj(M, K, r, dOut, K, Ud, r3, 1.f, nullptr, 0, 0, w.nsDd, w.msDd, w.partDd, nullptr, st));
+  LDL_TRY(reduce(K, r, w.partDd, (size_t)K * w.rp, w.nsDd, w.rp, false, s_down, dBd, r, st));
+  // ---- dH = dOut.Wd + s_d.V_d.Ad with the SwiGLU backward in the epilogue -> [dE | dGu]
+  {
+    GemmParams p = gp0();
+    p.M = M; p.N = H; p.K = K;
+    p.a = dOut; p.lda = K; p.b0 = Wd; p.b1 = Wd; p.ldb = H; p.kseg = K;
+    p.S = w.Vd; p.ld_s = r; p.r_epi = r; p.s_epi = s_down;
+    p.e0 = Ad; p.e1 = Ad; p.e_ldn = 1; p.e_ldj = H; p.e_jsplit = r;
+    p.aux0 = E_saved; p.ld_aux0 = H; p.aux1 = Gu_saved; p.ld_aux1 = H;
+    p.out = w.dEGu; p.ldo = 2 * H; p.out2 = w.dEGu + H; p.ldo2 = 2 * H;
+    LDL_TRY(launch_gemm(GK_NN_SWIGLU, p, st));
+  }
+  // dAd = s_d.V_d^T.H
+  LDL_TRY(colproj(M, H, r, H_saved, H, w.Vd, r, 1.f, nullptr, 0, 0, w.nsAd, w.msAd, w.partAd, nullptr, st));
+  LDL_TRY(reduce(r, H, w.partAd, (size_t)H * w.rp, w.nsAd, w.rp, true, s_down, dAd, H, st));
+  // ---- gate / up: V_g = s_g.dE.Bg, V_u = s_u.dGu.Bu (pre-scaled), dBg, dBu
+  LDL_TRY(launch_transpose_scale(static_cast<const uint16_t*>(Bg), nullptr, H, r, w.Bgt, st));
+  LDL_TRY(launch_transpose_scale(static_cast<const uint16_t*>(Bu), nullptr, H, r, w.But, st));
+  LDL_TRY(rowproj(M, H, r, w.dEGu, 2 * H, w.Bgt, nullptr, r, H, w.Vgu, 2 * r, s_gate, st));
+  LDL_TRY(rowproj(M, H, r, w.dEGu + H, 2 * H, w.But, nullptr, r, H, w.Vgu + r, 2 * r, s_up, st));
+  LDL_TRY(colproj(M, H, r, w.dEGu, 2 * H, Ug, r3, 1.f, nullptr, 0, 0, w.nsBg, w.msBg, w.partBg, nullptr, st));
+  LDL_TRY(reduce(H, r, w.partBg, (size_t)H * w.rp, w.nsBg, w.rp, false, s_gate, dBg, r, st));
+  LDL_TRY(colproj(M, H, r, w.dEGu + H, 2 * H, Uu, r3, 1.f, nullptr, 0, 0, w.nsBg, w.msBg, w.partBu, nullptr, st));
+  LDL_TRY(reduce(H, r, w.partBu, (size_t)H * w.rp, w.nsBg, w.rp, false, s_up, dBu, r, st));
+  // ---- dX = [dE | dGu].[Wg; Wu] + [V_g | V_u].[Ag; Au]  (one GEMM over the 2H reduction)
+  if (dX) {
+    GemmParams p = gp0();
+    p.M = M; p.N = K; p.K = 2 * H;
+    p.a = w.dEGu; p.lda = 2 * H; p.b0 = Wg; p.b1 = Wu; p.ldb = K; p.kseg = H;
+    p.S = w.Vgu; p.ld_s = 2 * r; p.r_epi = 2 * r; p.s_epi = 1.f;
+    p.e0 = Ag; p.e1 = Au; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = r;
+    p.out = dX; p.ldo = K;
+    LDL_TRY(launch_gemm(GK_NN_PLAIN, p, st));
+  }
+  // dAg, dAu = [V_g | V_u]^T.X in one pass over X
+  LDL_TRY(colproj(M, K, 2 * r, X, K, w.Vgu, 2 * r, 1.f, nullptr, 0, 0, w.nsAgu, w.msAgu, w.partAgu, nullptr, st));
+  LDL_TRY(reduce(r, K, w.partAgu, (size_t)K * w.rp2, w.nsAgu, w.rp2, true, 1.f, dAg, K, st));
+  LDL_TRY(reduce(r, K, w.partAgu + r, (size_t)K * w.rp2, w.nsAgu, w.rp2, true, 1.f, dAu, K, st));
+  return LDL_OK;
+}
+
+// =========================================================================== W8A8
+int w8a8_quantize_weight(int N, int K, int dtype, const void* W0, int8_t* Wq, float* sw, void* stream) {
+  if (!nonnull({W0, Wq, sw})) return LDL_E_INVAL;
+  if (N <= 0 || K <= 0) return LDL_E_INVAL;
+  if (dtype != LDL_F32 && dtype != LDL_BF16) return LDL_E_INVAL;
+  if (K % 8 || !al({W0, Wq, sw})) return LDL_E_UNSUPPORTED;
+  LDL_TRY(launch_quantize_rows(W0, dtype == LDL_F32, N, K, Wq, sw, S(stream)));
+  return LDL_OK;
+}
+
+int w8a8_quantize_rows(int M, int K, const void* X, int8_t* Xq, float* sx, void* stream) {
+  if (M > 0 && !nonnull({X, Xq, sx})) return LDL_E_INVAL;
+  if (M < 0 || K <= 0) return LDL_E_INVAL;
+  if (K % 8 || !al({X, Xq, sx})) return LDL_E_UNSUPPORTED;
+  LDL_TRY(launch_quantize_rows(X, 0, M, K, Xq, sx, S(stream)));
+  return LDL_OK;
+}
+
+int int8_gemm_raw(int M, int N, int K, const int8_t* Xq, const int8_t* Wq, int32_t* C, void* stream) {
+  if (!nonnull({Wq}) || (M > 0 && !nonnull({Xq, C}))) return LDL_E_INVAL;
+  if (M < 0 || N <= 0 || K <= 0) return LDL_E_INVAL;
+  if (N % 64 || K % 128 || !al({Xq, Wq, C})) return LDL_E_UNSUPPORTED;
+  if (!small(M + 256, K, 1) || !small(N, K, 1) || !small(M, N, 4)) return LDL_E_UNSUPPORTED;
+  GemmParams p = gp0();
+  p.M = M; p.N = N; p.K = K; p.a = Xq; p.lda = K; p.b0 = Wq; p.ldb = K; p.kseg = K;
+  p.out = C; p.ldo = N;
+  LDL_TRY(launch_gemm(GK_NT_I8_RAW, p, S(stream)));
+  return LDL_OK;
+}
+
+int w8a8_lora_linear_fwd(int M, int N, int K, int r, float s, const void* X, const int8_t* Wq, const float* sw,
+                         const void* A, const void* B, const void* bias, void* Y, int8_t* Xq_save, float* sx_save,
+                         float* U_save, void* ws, size_t ws_bytes, void* stream) {
+  if (!nonnull({Wq, sw, A, B}) || (M > 0 && !nonnull({X, Y}))) return LDL_E_INVAL;
+  if ((Xq_save == nullptr) != (sx_save == nullptr)) return LDL_E_INVAL;
+  const int chk = check_bf16_layer(M, N, K, r);
+  if (chk != LDL_OK) return chk;
+  if (K % 128) return LDL_E_UNSUPPORTED;
+  if (!al({X, Wq, sw, A, B, bias, Y, Xq_save, sx_save, U_save, ws})) return LDL_E_UNSUPPORTED;
+  if (ldl_workspace_bytes(LDL_OP_W8A8_FWD, M, N, K, r, LDL_BF16) > ws_bytes) return LDL_E_WORKSPACE;
+  if (!ws) return LDL_E_INVAL;
+  if (M == 0) return LDL_OK;
+  const hipStream_t st = S(stream);
+  Bump wb(ws);
+  float* Uw = wb.take<float>((size_t)M * r);
+  int8_t* Xqw = wb.take<int8_t>((size_t)M * K);
+  float* sxw = wb.take<float>((size_t)M);
+  float* U = U_save ? U_save : Uw;
+  int8_t* Xq = Xq_save ? Xq_save : Xqw;
+  float* sx = sx_save ? sx_save : sxw;
+  LDL_TRY(launch_quantize_rows(X, 0, M, K, Xq, sx, st));
+  LDL_TRY(rowproj(M, K, r, X, K, A, nullptr, r, K, U, r, 1.f, st));
+  GemmParams p = gp0();
+  p.M = M; p.N = N; p.K = K;
+  p.a = Xq; p.lda = K; p.b0 = Wq; p.ldb = K; p.kseg = K;
+  p.row_scale = sx; p.col_scale = sw;
+  p.S = U; p.ld_s = r; p.r_epi = r; p.s_epi = s;
+  p.e0 = B; p.e1 = B; p.e_ldn = r; p.e_ldj = 1; p.e_jsplit = r;
+  p.bias = bias; p.out = Y; p.ldo = N;
+  LDL_TRY(launch_gemm(GK_NT_I8_DEQ, p, st));
+  return LDL_OK;
+}
+
+int w8a8_lora_linear_bwd(int M, int N, int K, int r, float s, const void* dY, const void* X, const int8_t* Wq,
+                         const float* sw, const void* A, const void* B, const float* U_saved, void* dX, float* dA,
+                         float* dB, void* ws, size_t ws_bytes, void* stream) {
+  if (!nonnull({Wq, sw, A, B, dA, dB, ws}) || (M > 0 && !nonnull({dY, X}))) return LDL_E_INVAL;
+  const int chk = check_bf16_layer(M, N, K, r);
+  if (chk != LDL_OK) return chk;
+  if (!al({dY, X, Wq, sw, A, B, U_saved, dX, dA, dB, ws})) return LDL_E_UNSUPPORTED;
+  if (ldl_workspace_bytes(LDL_OP_W8A8_BWD, M, N, K, r, LDL_BF16) > ws_bytes) return LDL_E_WORKSPACE;
+  const hipStream_t st = S(stream);
+  if (M == 0) {
+    LDL_TRY(zero(dA, (size_t)r * K, st));
+    LDL_TRY(zero(dB, (size_t)N * r, st));
+    return LDL_OK;
+  }
+  Bump wb(ws);
+  LoraBwdWs w = plan_lora_bwd(wb, M, N, K, r, true);
+  const float* U = U_saved;
+  if (!U) {
+    LDL_TRY(rowproj(M, K, r, X, K, A, nullptr, r, K, w.U, r, 1.f, st));
+    U = w.U;
+  }
+  LDL_TRY(launch_transpose_scale(static_cast<const uint16_t*>(B), nullptr, N, r, w.Bt, st));
+  LDL_TRY(rowproj(M, N, r, dY, N, w.Bt, nullptr, r, N, w.V, r, 1.f, st));
+  if (dX) {
+    GemmParams p = gp0();
+    p.M = M; p.N = K; p.K = N;
+    p.a = dY; p.lda = N; p.a_colscale = sw; p.b0 = Wq; p.b1 = Wq; p.ldb = K; p.kseg = N;
+    p.S = w.V; p.ld_s = r; p.r_epi = r; p.s_epi = s;
+    p.e0 = A; p.e1 = A; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = r;
+    p.out = dX; p.ldo = K;
+    LDL_TRY(launch_gemm(GK_NN_I8_SCALE, p, st));
+  }
+  LDL_TRY(colproj(M, N, r, dY, N, U, r, 1.f, nullptr, 0, 0, w.nsB, w.msB, w.partB, nullptr, st));
+  LDL_TRY(reduce(N, r, w.partB, (size_t)N * w.rp, w.nsB, w.rp, false, s, dB, r, st));
+  LDL_TRY(colproj(M, K, r, X, K, w.V, r, 1.f, nullptr, 0, 0, w.nsA, w.msA, w.partA, nullptr, st));
+  LDL_TRY(reduce(r, K, w.partA, (size_t)K * w.rp, w.nsA, w.rp, true, s, dA, K, st));
+  return LDL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Shared device-side building blocks for the gfx950 (CDNA4) kernels.
+//
+// Everything here is plain HIP for a 64-lane wavefront.  The MFMA fragment
+// conventions used by every kernel in the library:
+//
+//   v_mfma_f32_16x16x32_bf16 (and v_mfma_i32_16x16x64_i8):
+//     operand P (lane l) holds row (l & 15) of a 16-row block and the 16-byte
+//     reduction chunk (l >> 4) of a 32-element (bf16) / 64-element (int8) step;
+//     operand Q likewise for the 16 columns.  The result lane l holds
+//     D[4*(l >> 4) + i][l & 15], i = 0..3.
+//   Both operands always use the same reduction-chunk assignment, so the
+//   order of the reduction inside a chunk never matters.
+//
+//   Kernels pass the output-column operand first and the output-row operand
+//   second, so that a lane's four results are four consecutive output columns
+//   of one output row (one 8-byte bf16 store or one 16-byte fp32 store).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <type_traits>
+
+namespace ldl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ bf16 helpers
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// Round to nearest even (inputs here are finite; NaN is kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ i32x4 as_i32x4(u32x4 v) { return __builtin_bit_cast(i32x4, v); }
+
+// ------------------------------------------------------------------ MFMA wrappers
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 p, u32x4 q, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p), as_bf16x8(q), acc, 0, 0, 0);
+}
+__device__ __forceinline__ i32x4 mfma_i8(u32x4 p, u32x4 q, i32x4 acc) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i32x4(p), as_i32x4(q), acc, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------ LDS swizzle
+// Tiles in LDS are rows of 128 bytes (eight 16-byte chunks).  Chunk c of row
+// `row` lives at chunk c ^ swz(row).  swz makes both access patterns the
+// kernels use conflict free: eight consecutive rows at one chunk (MFMA
+// fragment reads, row-major tile writes) and rows 8 apart at one chunk
+// (transposed tile writes).
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ swz(row)) << 4); }
+
+// ------------------------------------------------------------------ 8x8 transpose of 16-bit values
+// in[i] holds row i (8 values, 2 per dword); out[c] holds column c.
+__device__ __forceinline__ void transpose8x8_b16(const u32x4 in[8], u32x4 out[8]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t a = in[2 * j][c];
+      uint32_t b = in[2 * j + 1][c];
+      out[2 * c][j] = (a & 0xffffu) | (b << 16);
+      out[2 * c + 1][j] = (a >> 16) | (b & 0xffff0000u);
+    }
+  }
+}
+
+// int8 x8 (two dwords) -> bf16 x8 (four dwords), exact (|q| <= 128).
+__device__ __forceinline__ u32x4 i8x8_to_bf16x8(u32x2 v) {
+  u32x4 o;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t w = v[h];
+    float f0 = float(int8_t(w & 0xff));
+    float f1 = float(int8_t((w >> 8) & 0xff));
+    float f2 = float(int8_t((w >> 16) & 0xff));
+    float f3 = float(int8_t(w >> 24));
+    o[2 * h] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+    o[2 * h + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
+  }
+  return o;
+}
+
+// Scale 8 bf16 values by 8 per-element factors, round back to bf16.
+__device__ __forceinline__ u32x4 scale_bf16x8(u32x4 v, f32x4 s0, f32x4 s1) {
+  u32x4 o;
+  o[0] = pack_bf16x2(bf16_lo(v[0]) * s0[0], bf16_hi(v[0]) * s0[1]);
+  o[1] = pack_bf16x2(bf16_lo(v[1]) * s0[2], bf16_hi(v[1]) * s0[3]);
+  o[2] = pack_bf16x2(bf16_lo(v[2]) * s1[0], bf16_hi(v[2]) * s1[1]);
+  o[3] = pack_bf16x2(bf16_lo(v[3]) * s1[2], bf16_hi(v[3]) * s1[3]);
+  return o;
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ __forceinline__ float silu_f(float e) { return e / (1.0f + __expf(-e)); }
+__device__ __forceinline__ float sigmoid_f(float e) { return 1.0f / (1.0f + __expf(-e)); }
+
+}  // namespace ldl

@@ -1,0 +1,100 @@
+// Tile table and launches of the MFMA GEMM families.
+//
+// The block tile is chosen from the output width (it must divide N) and the
+// number of rows.  Tiles whose register footprint stays inside the 512
+// registers a wave may hold at one wave per SIMD (no scratch spills, checked
+// with -Rpass-analysis=kernel-resource-usage) are the only ones listed:
+//   NT bf16         256x256, 256x192, 256x128, 128x128, 128x64
+//   NT fused side   256x128 (down-projection rows computed in the K-loop)
+//   NT int8         256x128, 128x128, 128x64
+//   NN (bf16/int8 Q) 256x128, 128x128, 128x64
+#include "internal.hpp"
+
+namespace ldl {
+
+template <int BM, int BN, bool I8, bool NN, bool BINT8, bool ASCALE, int RSP, bool SLOAD, int EPI>
+static hipError_t run(const GemmParams& p, hipStream_t st) {
+  using C = GemmCfg<BM, BN, I8, NN, BINT8, ASCALE, RSP, SLOAD, EPI>;
+  const int tiles = ((p.M + BM - 1) / BM) * (p.N / BN);
+  hipLaunchKernelGGL(gemm_kernel<C>, dim3(tiles), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+static int pick_bn(GemmKind kind, int N) {
+  const bool wide_ok = (kind == GK_NT_PLAIN || kind == GK_NT_DORA || kind == GK_NT_SWIGLU);
+  const bool b192_ok = (kind == GK_NT_PLAIN || kind == GK_NT_DORA);
+  if (wide_ok && N % 256 == 0) return 256;
+  if (b192_ok && N % 192 == 0) return 192;
+  if (N % 128 == 0) return 128;
+  if (N % 64 == 0) return 64;
+  return 0;
+}
+
+bool gemm_shape_ok(GemmKind kind, int M, int N, int K) {
+  (void)M;
+  const bool i8 = (kind == GK_NT_I8_DEQ || kind == GK_NT_I8_RAW);
+  if (pick_bn(kind, N) == 0) return false;
+  if (kind == GK_NT_FUSED && N % 128 != 0) return false;
+  if (K <= 0 || K % (i8 ? 128 : 64) != 0) return false;
+  return true;
+}
+
+hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
+  if (p.M <= 0) return hipSuccess;
+  const int bn = pick_bn(kind, p.N);
+  const bool big = p.M > 128;
+  switch (kind) {
+    case GK_NT_PLAIN:
+      if (bn == 256) return big ? run<256, 256, false, false, false, false, 0, true, EPI_PLAIN>(p, st)
+                                : run<128, 128, false, false, false, false, 0, true, EPI_PLAIN>(p, st);
+      if (bn == 192) return big ? run<256, 192, false, false, false, false, 0, true, EPI_PLAIN>(p, st)
+                                : run<128, 64, false, false, false, false, 0, true, EPI_PLAIN>(p, st);
+      if (bn == 128) return big ? run<256, 128, false, false, false, false, 0, true, EPI_PLAIN>(p, st)
+                                : run<128, 128, false, false, false, false, 0, true, EPI_PLAIN>(p, st);
+      return run<128, 64, false, false, false, false, 0, true, EPI_PLAIN>(p, st);
+    case GK_NT_DORA:
+      if (bn == 256) return big ? run<256, 256, false, false, false, false, 0, true, EPI_DORA>(p, st)
+                                : run<128, 128, false, false, false, false, 0, true, EPI_DORA>(p, st);
+      if (bn == 192) return big ? run<256, 192, false, false, false, false, 0, true, EPI_DORA>(p, st)
+                                : run<128, 64, false, false, false, false, 0, true, EPI_DORA>(p, st);
+      if (bn == 128) return big ? run<256, 128, false, false, false, false, 0, true, EPI_DORA>(p, st)
+                                : run<128, 128, false, false, false, false, 0, true, EPI_DORA>(p, st);
+      return run<128, 64, false, false, false, false, 0, true, EPI_DORA>(p, st);
+    case GK_NT_SWIGLU:
+      if (bn == 256 && big) return run<256, 256, false, false, false, false, 0, true, EPI_SWIGLU_FWD>(p, st);
+      if (bn >= 128 && big) return run<256, 128, false, false, false, false, 0, true, EPI_SWIGLU_FWD>(p, st);
+      if (bn >= 128) return run<128, 128, false, false, false, false, 0, true, EPI_SWIGLU_FWD>(p, st);
+      return run<128, 64, false, false, false, false, 0, true, EPI_SWIGLU_FWD>(p, st);
+    case GK_NT_FUSED:
+      // down-projection computed in the K-loop; side rows padded to 16 or 32
+      if (p.r_side <= 16) return run<256, 128, false, false, false, false, 16, false, EPI_PLAIN>(p, st);
+      return run<256, 128, false, false, false, false, 32, false, EPI_PLAIN>(p, st);
+    case GK_NT_I8_DEQ:
+      if (bn >= 128) return big ? run<256, 128, true, false, false, false, 0, true, EPI_DEQUANT>(p, st)
+                                : run<128, 128, true, false, false, false, 0, true, EPI_DEQUANT>(p, st);
+      return run<128, 64, true, false, false, false, 0, true, EPI_DEQUANT>(p, st);
+    case GK_NT_I8_RAW:
+      if (bn >= 128) return big ? run<256, 128, true, false, false, false, 0, false, EPI_RAW_I32>(p, st)
+                                : run<128, 128, true, false, false, false, 0, false, EPI_RAW_I32>(p, st);
+      return run<128, 64, true, false, false, false, 0, false, EPI_RAW_I32>(p, st);
+    case GK_NN_PLAIN:
+      if (bn >= 128) return big ? run<256, 128, false, true, false, false, 0, true, EPI_PLAIN>(p, st)
+                                : run<128, 128, false, true, false, false, 0, true, EPI_PLAIN>(p, st);
+      return run<128, 64, false, true, false, false, 0, true, EPI_PLAIN>(p, st);
+    case GK_NN_SCALE:
+      if (bn >= 128) return big ? run<256, 128, false, true, false, true, 0, true, EPI_PLAIN>(p, st)
+                                : run<128, 128, false, true, false, true, 0, true, EPI_PLAIN>(p, st);
+      return run<128, 64, false, true, false, true, 0, true, EPI_PLAIN>(p, st);
+    case GK_NN_I8_SCALE:
+      if (bn >= 128) return big ? run<256, 128, false, true, true, true, 0, true, EPI_PLAIN>(p, st)
+                                : run<128, 128, false, true, true, true, 0, true, EPI_PLAIN>(p, st);
+      return run<128, 64, false, true, true, true, 0, true, EPI_PLAIN>(p, st);
+    case GK_NN_SWIGLU:
+      if (bn >= 128) return big ? run<256, 128, false, true, false, false, 0, true, EPI_SWIGLU_BWD>(p, st)
+                                : run<128, 128, false, true, false, false, 0, true, EPI_SWIGLU_BWD>(p, st);
+      return run<128, 64, false, true, false, false, 0, true, EPI_SWIGLU_BWD>(p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ldl

@@ -1,0 +1,487 @@
+// Block-tiled MFMA GEMM with a fused rank-r LoRA path, for gfx950.
+//
+//   acc[m, n] = sum_k P[m, k] * Q[k, n]      (fp32 or exact int32 accumulate)
+//   out[m, n] = epilogue(acc[m, n] + s_epi * sum_j S[m, j] * E[n, j])
+//
+// Layouts (all row-major, the reduction index k):
+//   P   : [M, K], k contiguous                      (X, dY, H ...)
+//   Q   : NT - [N, K], k contiguous                 (W0 in the forward)
+//         NN - [K, N], n contiguous                 (W0 in the input-gradient GEMM),
+//              up to two segments along k (rows k >= kseg come from b1)
+//   S   : either computed in the same K-loop from the staged P tiles as
+//         S = P . side^T with side [r, K] k contiguous (the down-projection
+//         U = X.A^T of the forward), or read from a precomputed fp32 [M, r_epi]
+//   E   : [N, r_epi] given by element strides (lora_up B in the forward,
+//         lora_down A^T in the input-gradient GEMM), up to two segments along j.
+//
+// This is the fused LoRA linear of "How Unsloth's FastLoRA Kernel Differs from
+// Standard LoRA Implementations" (section "Fused Forward Pass Architecture")
+// and the rank-tiled low-rank epilogue of the 8-bit core in "nunchaku-style
+// kernel fusion - 20-30% faster training" (LoRA-epilogue commit): the [N,K]
+// product B.A and the [M,N] low-rank product are never stored.
+//
+// Tiling: 4 waves (2 x 2), block tile BM x BN, k-tile of 128 bytes per row
+// (64 bf16 or 128 int8), double-buffered LDS, one barrier per k-tile,
+// operands staged through registers so that the NN operand can be transposed
+// (8 x 8 register transpose) and the DoRA / W8A8 column scale applied on load.
+#pragma once
+
+#include "common.hpp"
+
+namespace ldl {
+
+enum EpiKind : int {
+  EPI_PLAIN = 0,      // out = acc + lora (+ bias)                         -> bf16
+  EPI_DORA = 1,       // z = acc + lora; out = z * g[n] (+ bias); out2 = z -> bf16
+  EPI_SWIGLU_FWD = 2, // gu = acc + lora; h = silu(E) * gu; out2 = gu, out3 = h
+  EPI_SWIGLU_BWD = 3, // dh = acc + lora; out = dh*gu*silu'(e), out2 = dh*silu(e)
+  EPI_DEQUANT = 4,    // int8: acc * sx[m] * sw[n] + lora (+ bias)        -> bf16
+  EPI_RAW_I32 = 5,    // int8: raw int32 product
+};
+
+struct GemmParams {
+  int M, N, K;
+  const void* a; int lda;            // P, elements
+  const float* a_colscale;           // NN: P[m,k] *= a_colscale[k] on load
+  const void* b0; const void* b1; int ldb; int kseg;
+  const void* side; int r_side;      // fused down-projection rows [r_side, K]
+  const float* S; int ld_s;          // precomputed S (fp32)
+  int r_epi;                         // rank of the epilogue update (0: none)
+  float s_epi;
+  const void* e0; const void* e1; int e_ldn, e_ldj, e_jsplit;
+  const float* row_scale;            // [M]  (int8 sx)
+  const float* col_scale;            // [N]  (int8 sw / DoRA g)
+  const void* bias;                  // [N] bf16
+  void* out; int ldo;
+  void* out2; int ldo2;
+  void* out3; int ldo3;
+  const void* aux0; int ld_aux0;
+  const void* aux1; int ld_aux1;
+  float* side_save; int ld_side_save;
+};
+
+template <int BM_, int BN_, bool I8_, bool NN_, bool BINT8_, bool ASCALE_, int SIDE_RSP_, bool SLOAD_, int EPI_>
+struct GemmCfg {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr bool kI8 = I8_;          // P and Q int8 (NT only)
+  static constexpr bool kNN = NN_;          // Q is [K, N]
+  static constexpr bool kBInt8 = BINT8_;    // NN: Q int8, upcast to bf16 exactly
+  static constexpr bool kAScale = ASCALE_;  // NN: column scale on P
+  static constexpr int kSideRsp = SIDE_RSP_;// fused side rows (padded to 16), 0: none
+  static constexpr bool kSLoad = SLOAD_;    // epilogue S from global
+  static constexpr int kEpi = EPI_;
+};
+
+template <class C>
+struct GemmSmem {
+  static constexpr int kRows = C::BM + C::BN + C::kSideRsp;
+  static constexpr int kBuf = kRows * 128;
+};
+
+__device__ __forceinline__ u32x4 lds_ld16(const uint8_t* base, int off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+__device__ __forceinline__ void lds_st16(uint8_t* base, int off, u32x4 v) {
+  *reinterpret_cast<u32x4*>(base + off) = v;
+}
+
+// Element (n, j) of the epilogue up-matrix as bf16 bits (zero outside [0, r_epi)).
+__device__ __forceinline__ uint32_t e_elem(const GemmParams& p, int n, int j) {
+  if (j >= p.r_epi) return 0u;
+  const uint16_t* src;
+  int jj = j;
+  if (j < p.e_jsplit) src = static_cast<const uint16_t*>(p.e0);
+  else { src = static_cast<const uint16_t*>(p.e1); jj = j - p.e_jsplit; }
+  return src[(size_t)n * p.e_ldn + (size_t)jj * p.e_ldj];
+}
+
+__device__ __forceinline__ u32x4 e_frag(const GemmParams& p, int n, int j0) {
+  // 8 consecutive ranks j0..j0+7 of row n of E
+  if (p.e_ldj == 1 && j0 + 8 <= p.r_epi && (j0 >= p.e_jsplit || j0 + 8 <= p.e_jsplit)) {
+    const uint16_t* src = (j0 < p.e_jsplit) ? static_cast<const uint16_t*>(p.e0) : static_cast<const uint16_t*>(p.e1);
+    int jj = (j0 < p.e_jsplit) ? j0 : j0 - p.e_jsplit;
+    const uint16_t* q = src + (size_t)n * p.e_ldn + jj;
+    if ((((uintptr_t)q) & 15) == 0) return ld16(q);
+  }
+  u32x4 v;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) v[t] = e_elem(p, n, j0 + 2 * t) | (e_elem(p, n, j0 + 2 * t + 1) << 16);
+  return v;
+}
+
+// Buffer resource over [base, base + bytes): reads past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// Direct buffer -> LDS copy of 16 bytes per lane; lane l lands at lds_base + 16*l.
+__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, soff, 0, 0);
+}
+
+template <class C>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
+  constexpr int BM = C::BM, BN = C::BN;
+  constexpr bool I8 = C::kI8, NN = C::kNN;
+  constexpr int RSP = C::kSideRsp;
+  constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 16, FN = TN / 16;
+  constexpr int BK = I8 ? 128 : 64;     // elements per k-tile
+  constexpr int HALF = FM / 2;
+  static_assert(FM % 2 == 0, "BM/32 must be even");
+  static_assert(!NN || !I8, "NN takes bf16 P");
+  using Acc = typename std::conditional<I8, i32x4, f32x4>::type;
+
+  // two LDS stages, each [BM rows of P | BN rows of Q | RSP side rows] x 128 bytes
+  __shared__ __attribute__((aligned(16))) uint8_t smem0[GemmSmem<C>::kBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t smem1[GemmSmem<C>::kBuf];
+
+  const int M = p.M, N = p.N, K = p.K;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
+
+  // Tile order: consecutive workgroups go round-robin over the 8 XCDs, so
+  // remap ids so that each XCD receives a contiguous range, then walk that
+  // range in groups of GM row-tiles (tiles sharing P rows and Q columns stay
+  // on one XCD's L2).
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  constexpr int GM = 4;
+  const int group = bid / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gm = min(GM, tiles_m - first_m);
+  const int in_g = bid - group * GM * tiles_n;
+  const int tm = first_m + in_g % gm;
+  const int tn = in_g / gm;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 15, lq = lane >> 4;
+
+  const uint32_t lda_b = (uint32_t)p.lda * (I8 ? 1 : 2);
+  const uint32_t ldb_b = (uint32_t)p.ldb * ((I8 || C::kBInt8) ? 1 : 2);
+
+  // Per-lane 32-bit source offsets for the direct copies (operands are below
+  // 4 GiB, checked on the host).  One wave instruction fills 64 consecutive
+  // 16-byte LDS slots = 8 rows; slot (row, phys) receives the logical chunk
+  // phys ^ swz(row) of that row.  Rows past the end of an operand (P rows
+  // >= M, side rows >= r) read as zero through the buffer bounds.
+  const int lrow = lane >> 3, lphys = lane & 7;
+  constexpr int A_INST = BM / 32;             // per wave
+  constexpr int B_INST = NN ? 0 : BN / 32;
+  constexpr int S_INST = (RSP * 8 + 255) / 256;
+  const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(p.a, (uint32_t)M * lda_b);
+  const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(p.b0, NN ? 0u : (uint32_t)N * ldb_b);
+  const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(p.side, RSP ? (uint32_t)p.r_side * (uint32_t)K * 2u : 0u);
+  uint32_t a_off[A_INST];
+#pragma unroll
+  for (int i = 0; i < A_INST; ++i) {
+    const int row = (i * 4 + wave) * 8 + lrow;
+    a_off[i] = (uint32_t)(m0 + row) * lda_b + ((lphys ^ swz(row)) << 4);
+  }
+  uint32_t b_off[B_INST ? B_INST : 1];
+#pragma unroll
+  for (int i = 0; i < B_INST; ++i) {
+    const int row = (i * 4 + wave) * 8 + lrow;
+    b_off[i] = (uint32_t)(n0 + row) * ldb_b + ((lphys ^ swz(row)) << 4);
+  }
+  uint32_t s_off[S_INST ? S_INST : 1];
+#pragma unroll
+  for (int i = 0; i < S_INST; ++i) {
+    const int row = (i * 4 + wave) * 8 + lrow;      // side row
+    s_off[i] = (uint32_t)row * (uint32_t)K * 2u + ((lphys ^ swz(BN + row)) << 4);
+  }
+
+  Acc acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+  f32x4 sacc[RSP ? HALF : 1][RSP ? RSP / 16 : 1];
+  if constexpr (RSP > 0) {
+#pragma unroll
+    for (int i = 0; i < HALF; ++i)
+#pragma unroll
+      for (int j = 0; j < RSP / 16; ++j) sacc[i][j] = f32x4{0, 0, 0, 0};
+  }
+
+  u32x4 rb[NN ? 8 : 1];   // NN: 8 rows x 8 columns of Q staged for the transpose
+
+  // ---------------------------------------------------------------- loaders
+  auto issue_loads = [&](int kt, uint8_t* sbuf) {
+    const uint32_t koff = (uint32_t)kt * 128u;
+#pragma unroll
+    for (int i = 0; i < A_INST; ++i) buf2lds16(rs_a, a_off[i], koff, sbuf + (i * 4 + wave) * 1024);
+    if constexpr (!NN) {
+      uint8_t* sB = sbuf + BM * 128;
+#pragma unroll
+      for (int i = 0; i < B_INST; ++i) buf2lds16(rs_b, b_off[i], koff, sB + (i * 4 + wave) * 1024);
+#pragma unroll
+      for (int i = 0; i < S_INST; ++i)
+        if ((i * 4 + wave) * 8 < RSP) buf2lds16(rs_s, s_off[i], koff, sB + BN * 128 + (i * 4 + wave) * 1024);
+    } else {
+      // Q is [K, N]: this k-tile covers reduction rows kt*64 .. +63.
+      const int kk0 = kt * 64;
+      const uint8_t* pb;
+      int krow0;
+      if (kk0 < p.kseg) { pb = static_cast<const uint8_t*>(p.b0); krow0 = kk0; }
+      else { pb = static_cast<const uint8_t*>(p.b1); krow0 = kk0 - p.kseg; }
+      if (tid < BN) {
+        const int kb = tid % (BN / 8), nb = tid / (BN / 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const size_t rowoff = (size_t)(krow0 + nb * 8 + e) * (size_t)ldb_b;
+          if constexpr (C::kBInt8) {
+            u32x2 v = *reinterpret_cast<const u32x2*>(pb + rowoff + (size_t)(n0 + kb * 8));
+            rb[e] = i8x8_to_bf16x8(v);
+          } else {
+            rb[e] = ld16(pb + rowoff + (size_t)(n0 + kb * 8) * 2);
+          }
+        }
+      }
+    }
+  };
+
+  // NN only: scale (optional) and transpose the staged Q rows into LDS.
+  auto store_q = [&](int kt, uint8_t* sbuf) {
+    if constexpr (NN) {
+      if (tid < BN) {
+        uint8_t* sB = sbuf + BM * 128;
+        const int kb = tid % (BN / 8), nb = tid / (BN / 8);
+        if constexpr (C::kAScale) {
+          const f32x4* sc = reinterpret_cast<const f32x4*>(p.a_colscale + (size_t)kt * 64 + nb * 8);
+          const f32x4 s0 = sc[0], s1 = sc[1];
+          const float f[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const f32x4 se = f32x4{f[e], f[e], f[e], f[e]};
+            rb[e] = scale_bf16x8(rb[e], se, se);
+          }
+        }
+        u32x4 t[8];
+        transpose8x8_b16(rb, t);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) lds_st16(sB, lds_off(kb * 8 + c, nb), t[c]);
+      }
+    }
+  };
+
+  auto compute_ks = [&](const uint8_t* sbuf, auto ks_const) {
+    constexpr int ks = decltype(ks_const)::value;
+    const uint8_t* sA = sbuf;
+    const uint8_t* sB = sbuf + BM * 128;
+    {
+      u32x4 af[FM], bf[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = lds_ld16(sA, lds_off(wm * TM + i * 16 + lr, ks * 4 + lq));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bf[j] = lds_ld16(sB, lds_off(wn * TN + j * 16 + lr, ks * 4 + lq));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          if constexpr (I8) acc[i][j] = mfma_i8(bf[j], af[i], acc[i][j]);
+          else acc[i][j] = mfma_bf16(bf[j], af[i], acc[i][j]);
+        }
+      if constexpr (RSP > 0) {
+#pragma unroll
+        for (int js = 0; js < RSP / 16; ++js) {
+          const u32x4 sf = lds_ld16(sB, lds_off(BN + js * 16 + lr, ks * 4 + lq));
+          if (wn == 0) {
+#pragma unroll
+            for (int i = 0; i < HALF; ++i) sacc[i][js] = mfma_bf16(sf, af[i], sacc[i][js]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < HALF; ++i) sacc[i][js] = mfma_bf16(sf, af[HALF + i], sacc[i][js]);
+          }
+        }
+      }
+    }
+  };
+
+  // ---------------------------------------------------------------- main loop
+  // Stage kt lives in smem[kt & 1].  Per k-tile: wait for the stage's copies,
+  // barrier (which also retires every read of the other stage), start the
+  // copies of the next stage, then run the MFMAs of this one.  (A single
+  // call site for compute() keeps the accumulators in place; unrolling the
+  // two stages made the register allocator rotate them every iteration.)
+  const int KT = K / BK;
+  issue_loads(0, smem0);
+  store_q(0, smem0);
+  for (int kt = 0; kt < KT; ++kt) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    uint8_t* cur = (kt & 1) ? smem1 : smem0;
+    uint8_t* nxt = (kt & 1) ? smem0 : smem1;
+    if (kt + 1 < KT) issue_loads(kt + 1, nxt);
+    compute_ks(cur, std::integral_constant<int, 0>{});
+    if (kt + 1 < KT) store_q(kt + 1, nxt);
+    compute_ks(cur, std::integral_constant<int, 1>{});
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- epilogue
+  const int mrow_base = m0 + wm * TM;        // + i*16 + lr
+  const int ncol_base = n0 + wn * TN;        // + j*16 + 4*lq + e
+
+  // Fused side: publish s_epi * U (bf16) to LDS for the rank-r product, save U (fp32).
+  if constexpr (RSP > 0) {
+    uint16_t* sS = reinterpret_cast<uint16_t*>(smem0);
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) {
+      const int row = wm * TM + (wn * HALF + i) * 16 + lr;
+#pragma unroll
+      for (int js = 0; js < RSP / 16; ++js) {
+        const int j0 = js * 16 + 4 * lq;
+        const f32x4 u = sacc[i][js];
+        u32x2 w;
+        w[0] = pack_bf16x2(u[0] * p.s_epi, u[1] * p.s_epi);
+        w[1] = pack_bf16x2(u[2] * p.s_epi, u[3] * p.s_epi);
+        *reinterpret_cast<u32x2*>(sS + row * RSP + j0) = w;
+        const int m = m0 + row;
+        if (p.side_save != nullptr && tn == 0 && m < M) {
+          float* dst = p.side_save + (size_t)m * p.ld_side_save;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j0 + e < p.r_side) dst[j0 + e] = u[e];
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // The epilogue walks the accumulator tile in column chunks so that the
+  // fp32 copy of an int32 tile never doubles the live registers.
+  constexpr int JC = I8 ? FN / 2 : FN;
+  static_assert(FN % JC == 0, "column chunking");
+  auto epilogue_chunk = [&](auto jc_const) {
+    constexpr int jc = decltype(jc_const)::value;
+    if constexpr (C::kEpi == EPI_RAW_I32) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = mrow_base + i * 16 + lr;
+        if (m >= M) continue;
+#pragma unroll
+        for (int jj = 0; jj < JC; ++jj) {
+          const int n = ncol_base + (jc + jj) * 16 + 4 * lq;
+          *reinterpret_cast<i32x4*>(static_cast<int32_t*>(p.out) + (size_t)m * p.ldo + n) = acc[i][jc + jj];
+        }
+      }
+    } else {
+      f32x4 facc[FM][JC];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < JC; ++jj) {
+          if constexpr (I8) {
+            const int m = mrow_base + i * 16 + lr;
+            const float sxm = (m < M) ? p.row_scale[m] : 0.f;
+            const f32x4 swn = *reinterpret_cast<const f32x4*>(p.col_scale + ncol_base + (jc + jj) * 16 + 4 * lq);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) facc[i][jj][e] = float(acc[i][jc + jj][e]) * sxm * swn[e];
+          } else {
+            facc[i][jj] = acc[i][jc + jj];
+          }
+        }
+
+      if (p.r_epi > 0) {
+        const uint16_t* sS = reinterpret_cast<const uint16_t*>(smem0);
+        const int nsteps = (p.r_epi + 31) / 32;
+        for (int t = 0; t < nsteps; ++t) {
+          const int j0 = t * 32 + lq * 8;
+          u32x4 sf[FM];
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int row = wm * TM + i * 16 + lr;
+            sf[i] = u32x4{0, 0, 0, 0};
+            if constexpr (RSP > 0) {
+              if (j0 < RSP) sf[i] = *reinterpret_cast<const u32x4*>(sS + row * RSP + j0);
+            } else if constexpr (C::kSLoad) {
+              const int m = m0 + row;
+              if (m < M && j0 < p.r_epi) {
+                const float* src = p.S + (size_t)m * p.ld_s + j0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float lo = (j0 + 2 * e < p.r_epi) ? src[2 * e] * p.s_epi : 0.f;
+                  const float hi = (j0 + 2 * e + 1 < p.r_epi) ? src[2 * e + 1] * p.s_epi : 0.f;
+                  sf[i][e] = pack_bf16x2(lo, hi);
+                }
+              }
+            }
+          }
+#pragma unroll
+          for (int jj = 0; jj < JC; ++jj) {
+            const u32x4 ef = e_frag(p, ncol_base + (jc + jj) * 16 + lr, j0);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) facc[i][jj] = mfma_bf16(ef, sf[i], facc[i][jj]);
+          }
+        }
+      }
+
+      // stores: lane holds row m, columns n..n+3
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = mrow_base + i * 16 + lr;
+        if (m >= M) continue;
+#pragma unroll
+        for (int jj = 0; jj < JC; ++jj) {
+          const int n = ncol_base + (jc + jj) * 16 + 4 * lq;
+          const f32x4 v = facc[i][jj];
+          float bias4[4] = {0.f, 0.f, 0.f, 0.f};
+          if (p.bias != nullptr) {
+            const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n);
+            bias4[0] = bf16_lo(bb[0]); bias4[1] = bf16_hi(bb[0]);
+            bias4[2] = bf16_lo(bb[1]); bias4[3] = bf16_hi(bb[1]);
+          }
+          if constexpr (C::kEpi == EPI_PLAIN || C::kEpi == EPI_DEQUANT) {
+            u32x2 w;
+            w[0] = pack_bf16x2(v[0] + bias4[0], v[1] + bias4[1]);
+            w[1] = pack_bf16x2(v[2] + bias4[2], v[3] + bias4[3]);
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (size_t)m * p.ldo + n) = w;
+          } else if constexpr (C::kEpi == EPI_DORA) {
+            const f32x4 g = *reinterpret_cast<const f32x4*>(p.col_scale + n);
+            u32x2 w, z;
+            z[0] = pack_bf16x2(v[0], v[1]);
+            z[1] = pack_bf16x2(v[2], v[3]);
+            w[0] = pack_bf16x2(v[0] * g[0] + bias4[0], v[1] * g[1] + bias4[1]);
+            w[1] = pack_bf16x2(v[2] * g[2] + bias4[2], v[3] * g[3] + bias4[3]);
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (size_t)m * p.ldo + n) = w;
+            if (p.out2 != nullptr)
+              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out2) + (size_t)m * p.ldo2 + n) = z;
+          } else if constexpr (C::kEpi == EPI_SWIGLU_FWD) {
+            const u32x2 ee = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux0) + (size_t)m * p.ld_aux0 + n);
+            const float e4[4] = {bf16_lo(ee[0]), bf16_hi(ee[0]), bf16_lo(ee[1]), bf16_hi(ee[1])};
+            u32x2 gu, h;
+            gu[0] = pack_bf16x2(v[0], v[1]);
+            gu[1] = pack_bf16x2(v[2], v[3]);
+            h[0] = pack_bf16x2(silu_f(e4[0]) * v[0], silu_f(e4[1]) * v[1]);
+            h[1] = pack_bf16x2(silu_f(e4[2]) * v[2], silu_f(e4[3]) * v[3]);
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out2) + (size_t)m * p.ldo2 + n) = gu;
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out3) + (size_t)m * p.ldo3 + n) = h;
+          } else if constexpr (C::kEpi == EPI_SWIGLU_BWD) {
+            const u32x2 ee = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux0) + (size_t)m * p.ld_aux0 + n);
+            const u32x2 gg = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux1) + (size_t)m * p.ld_aux1 + n);
+            const float e4[4] = {bf16_lo(ee[0]), bf16_hi(ee[0]), bf16_lo(ee[1]), bf16_hi(ee[1])};
+            const float g4[4] = {bf16_lo(gg[0]), bf16_hi(gg[0]), bf16_lo(gg[1]), bf16_hi(gg[1])};
+            float de[4], dgu[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float sg = sigmoid_f(e4[e]);
+              de[e] = v[e] * g4[e] * sg * (1.f + e4[e] * (1.f - sg));
+              dgu[e] = v[e] * e4[e] * sg;
+            }
+            u32x2 w0, w1;
+            w0[0] = pack_bf16x2(de[0], de[1]); w0[1] = pack_bf16x2(de[2], de[3]);
+            w1[0] = pack_bf16x2(dgu[0], dgu[1]); w1[1] = pack_bf16x2(dgu[2], dgu[3]);
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (size_t)m * p.ldo + n) = w0;
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out2) + (size_t)m * p.ldo2 + n) = w1;
+          }
+        }
+      }
+    }
+  };
+  epilogue_chunk(std::integral_constant<int, 0>{});
+  if constexpr (JC < FN) epilogue_chunk(std::integral_constant<int, JC>{});
+}
+
+}  // namespace ldl

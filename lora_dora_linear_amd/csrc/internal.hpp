@@ -1,0 +1,81 @@
+// Internal launch interface between the C entry points and the kernels.
+#pragma once
+
+#include "common.hpp"
+#include "gemm_tile.hpp"
+
+namespace ldl {
+
+struct RowProjParams {
+  int M, K, R, R0;                 // Q rows j < R0 come from q0, rows j >= R0 from q1
+  const uint16_t* P; int ldp;      // [M, K] bf16
+  const uint16_t* q0; const uint16_t* q1; int ldq;
+  float* out; int ldo;             // out[m * ldo + j] = scale * sum_k P[m,k] Q[j,k]
+  float scale;
+};
+
+struct ColProjParams {
+  int M, C, R;
+  const uint16_t* X; int ldx;      // [M, C] bf16, C a multiple of 8
+  const float* S; int lds;         // [M, R] fp32
+  float s_in;
+  const uint16_t* Z; int ldz;      // colsum_mode 1: sum_m X*Z, 2: sum_m X
+  int colsum_mode;
+  int msplit;                      // rows per split (multiple of 256)
+  float* part;                     // [nsplit][C][RP]
+  float* cspart;                   // [nsplit][C]
+};
+
+struct ReduceParams {
+  int rows, cols;                  // output shape
+  const float* part; size_t pstride; int nsplit, rp; int trans;
+  float alpha;
+  const float* rowscale;           // optional [rows]
+  const float* Qm; int ldq, rq;    // optional addend alpha2 * Qm[rows, rq] . Am[rq, cols]
+  const uint16_t* Am; int lda;
+  float alpha2;
+  float* out; int ldo;
+};
+
+// GEMM tile families (see gemm_tile.hpp); selected by the entry points.
+enum GemmKind : int {
+  GK_NT_PLAIN, GK_NT_FUSED, GK_NT_DORA, GK_NT_SWIGLU, GK_NT_I8_DEQ, GK_NT_I8_RAW,
+  GK_NN_PLAIN, GK_NN_SCALE, GK_NN_I8_SCALE, GK_NN_SWIGLU
+};
+hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st);
+bool gemm_shape_ok(GemmKind kind, int M, int N, int K);
+
+hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st);
+int colproj_rp(int R);
+void colproj_plan(int M, int C, int* nsplit, int* msplit);
+hipError_t launch_colproj(const ColProjParams& p, int nsplit, hipStream_t st);
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t st);
+hipError_t launch_reduce_colsum(const float* cspart, int nsplit, int C, float* out, hipStream_t st);
+hipError_t launch_transpose_scale(const uint16_t* B, const float* scale, int N, int r, uint16_t* Bt, hipStream_t st);
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t st);
+
+// DoRA helpers
+hipError_t launch_rowsumsq(const void* W0, int dtype_bf16, int N, int K, float* out, hipStream_t st);
+hipError_t launch_dora_norm(int N, int r, float s, float eps, const float* w0_sumsq, const float* P,
+                            const float* G, const uint16_t* B, const float* m, float* norm, float* g, hipStream_t st);
+hipError_t launch_dora_finalize(int N, int r, float s, float eps, const float* partT, const float* cspart,
+                                int nsplit, int rpT, const float* norm, const float* g, const float* m,
+                                const float* P, const float* G, const uint16_t* B,
+                                float* dB, float* dm, float* wB, hipStream_t st);
+
+// W8A8 helpers
+hipError_t launch_quantize_rows(const void* X, int in_f32, int M, int K, int8_t* q, float* scale, hipStream_t st);
+
+// fp32 path: C[m, n] = alpha * sum_k A(m, k) B(k, n) + beta * C[m, n] (+ bias[n])
+struct F32GemmParams {
+  int M, N, K;
+  const float* A; long sam, sak;
+  const float* B; long sbk, sbn;
+  float* C; int ldc;
+  float alpha, beta;
+  const float* bias;
+};
+hipError_t launch_f32_gemm(const F32GemmParams& p, hipStream_t st);
+hipError_t launch_f32_colsum(const float* X, int M, int N, float* out, hipStream_t st);
+
+}  // namespace ldl

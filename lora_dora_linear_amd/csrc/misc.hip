@@ -1,0 +1,256 @@
+// Small per-row kernels: the DoRA norm terms, the int8 quantiser, and the
+// fp32 path (a plain tiled SIMT GEMM, used for fp32 layers, which are small).
+#include "internal.hpp"
+
+namespace ldl {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ============================================================================ DoRA
+// w0_sumsq[n] = sum_k W0[n,k]^2 : one wave per row ("a cached rowsum(W0^2) constant",
+// "LoRA/DoRA fast forward: no weight materialization", commit message).
+template <bool BF16>
+__global__ __launch_bounds__(256) void rowsumsq_kernel(const void* W0, int N, int K, float* out) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  float acc = 0.f;
+  if (BF16) {
+    const uint16_t* row = static_cast<const uint16_t*>(W0) + (size_t)n * K;
+    for (int k = lane * 8; k < K; k += 512) {
+      const u32x4 v = ld16(row + k);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float a = bf16_lo(v[t]), b = bf16_hi(v[t]);
+        acc += a * a + b * b;
+      }
+    }
+  } else {
+    const float* row = static_cast<const float*>(W0) + (size_t)n * K;
+    for (int k = lane; k < K; k += 64) acc += row[k] * row[k];
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) out[n] = acc;
+}
+
+// Closed-form row norm: nu^2 = c + 2s <B_n, P_n> + s^2 B_n G B_n^T, clamped at 0;
+// g = m / max(nu, eps).  One thread per output row; G staged in LDS.
+__global__ __launch_bounds__(256) void dora_norm_kernel(int N, int r, float s, float eps, const float* c,
+                                                        const float* P, const float* G, const uint16_t* B,
+                                                        const float* m, float* norm, float* g) {
+  extern __shared__ float sG[];
+  for (int i = threadIdx.x; i < r * r; i += blockDim.x) sG[i] = G[i];
+  __syncthreads();
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  const uint16_t* bn = B + (size_t)n * r;
+  const float* pn = P + (size_t)n * r;
+  float t1 = 0.f, t2 = 0.f;
+  for (int j = 0; j < r; ++j) {
+    const float bj = bf16_to_f32(bn[j]);
+    t1 += bj * pn[j];
+    float bg = 0.f;
+    for (int l = 0; l < r; ++l) bg += sG[j * r + l] * bf16_to_f32(bn[l]);
+    t2 += bj * bg;
+  }
+  const float nu2 = c[n] + 2.f * s * t1 + s * s * t2;
+  const float nu = sqrtf(fmaxf(nu2, 0.f));
+  norm[n] = nu;
+  g[n] = m[n] / fmaxf(nu, eps);
+}
+
+// Backward per output row, with the norm kept in the graph:
+//   T = sum_splits partT (= dY^T.U row n);  dg = sum_splits cspart (= sum_m dY*Z)
+//   dm = dg / max(nu, eps);  w = -dg m / (2 nu^3) if nu > eps else 0
+//   dB[n,:] = s g_n T + w (2s P_n + 2s^2 (B G)_n);  wB[n,:] = 2s w B_n
+__global__ __launch_bounds__(256) void dora_finalize_kernel(int N, int r, float s, float eps, const float* partT,
+                                                            const float* cspart, int nsplit, int rpT,
+                                                            const float* norm, const float* g, const float* m,
+                                                            const float* P, const float* G, const uint16_t* B,
+                                                            float* dB, float* dm, float* wB) {
+  extern __shared__ float sG[];
+  for (int i = threadIdx.x; i < r * r; i += blockDim.x) sG[i] = G[i];
+  __syncthreads();
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  float dg = 0.f;
+  for (int sp = 0; sp < nsplit; ++sp) dg += cspart[(size_t)sp * N + n];
+  const float nu = norm[n];
+  const float den = fmaxf(nu, eps);
+  dm[n] = dg / den;
+  const float w = (nu > eps) ? (-dg * m[n] / (2.f * nu * nu * nu)) : 0.f;
+  const uint16_t* bn = B + (size_t)n * r;
+  const float gn = g[n];
+  for (int j = 0; j < r; ++j) {
+    float t = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) t += partT[((size_t)sp * N + n) * rpT + j];
+    float bg = 0.f;
+    for (int l = 0; l < r; ++l) bg += bf16_to_f32(bn[l]) * sG[l * r + j];
+    dB[(size_t)n * r + j] = s * gn * t + w * (2.f * s * P[(size_t)n * r + j] + 2.f * s * s * bg);
+    wB[(size_t)n * r + j] = 2.f * s * w * bf16_to_f32(bn[j]);
+  }
+}
+
+hipError_t launch_rowsumsq(const void* W0, int dtype_bf16, int N, int K, float* out, hipStream_t st) {
+  const dim3 grid((N + 3) / 4), block(256);
+  if (dtype_bf16) hipLaunchKernelGGL(rowsumsq_kernel<true>, grid, block, 0, st, W0, N, K, out);
+  else hipLaunchKernelGGL(rowsumsq_kernel<false>, grid, block, 0, st, W0, N, K, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dora_norm(int N, int r, float s, float eps, const float* w0_sumsq, const float* P,
+                            const float* G, const uint16_t* B, const float* m, float* norm, float* g, hipStream_t st) {
+  hipLaunchKernelGGL(dora_norm_kernel, dim3((N + 255) / 256), dim3(256), r * r * sizeof(float), st,
+                     N, r, s, eps, w0_sumsq, P, G, B, m, norm, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_dora_finalize(int N, int r, float s, float eps, const float* partT, const float* cspart,
+                                int nsplit, int rpT, const float* norm, const float* g, const float* m,
+                                const float* P, const float* G, const uint16_t* B,
+                                float* dB, float* dm, float* wB, hipStream_t st) {
+  hipLaunchKernelGGL(dora_finalize_kernel, dim3((N + 255) / 256), dim3(256), r * r * sizeof(float), st,
+                     N, r, s, eps, partT, cspart, nsplit, rpT, norm, g, m, P, G, B, dB, dm, wB);
+  return hipGetLastError();
+}
+
+// ============================================================================ int8 quantiser
+// Symmetric per-row codes: scale = absmax / 127 (fp32), q = clamp(rint(x / scale), +-127)
+// with the quotient in fp32 and ties to even; scale 0 -> q = 0.  One wave per row.
+template <bool F32IN>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const void* X, int M, int K, int8_t* q, float* scale) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  float amax = 0.f;
+  if (F32IN) {
+    const float* x = static_cast<const float*>(X) + (size_t)row * K;
+    for (int k = lane; k < K; k += 64) amax = fmaxf(amax, fabsf(x[k]));
+  } else {
+    const uint16_t* x = static_cast<const uint16_t*>(X) + (size_t)row * K;
+    for (int k = lane * 8; k < K; k += 512) {
+      const u32x4 v = ld16(x + k);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[t])), fabsf(bf16_hi(v[t]))));
+    }
+  }
+  amax = wave_max(amax);
+  const float sc = amax / 127.0f;
+  if (lane == 0) scale[row] = sc;
+  int8_t* qrow = q + (size_t)row * K;
+  auto code = [&](float x) -> int {
+    if (!(sc > 0.f)) return 0;
+    float t = rintf(x / sc);
+    t = fminf(fmaxf(t, -127.f), 127.f);
+    return (int)t;
+  };
+  if (F32IN) {
+    const float* x = static_cast<const float*>(X) + (size_t)row * K;
+    for (int k = lane; k < K; k += 64) qrow[k] = (int8_t)code(x[k]);
+  } else {
+    const uint16_t* x = static_cast<const uint16_t*>(X) + (size_t)row * K;
+    for (int k = lane * 8; k < K; k += 512) {
+      const u32x4 v = ld16(x + k);
+      u32x2 o;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t b0 = (uint32_t)(code(bf16_lo(v[2 * h])) & 0xff);
+        const uint32_t b1 = (uint32_t)(code(bf16_hi(v[2 * h])) & 0xff);
+        const uint32_t b2 = (uint32_t)(code(bf16_lo(v[2 * h + 1])) & 0xff);
+        const uint32_t b3 = (uint32_t)(code(bf16_hi(v[2 * h + 1])) & 0xff);
+        o[h] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+      }
+      *reinterpret_cast<u32x2*>(qrow + k) = o;
+    }
+  }
+}
+
+hipError_t launch_quantize_rows(const void* X, int in_f32, int M, int K, int8_t* q, float* scale, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  const dim3 grid((M + 3) / 4), block(256);
+  if (in_f32) hipLaunchKernelGGL(quantize_rows_kernel<true>, grid, block, 0, st, X, M, K, q, scale);
+  else hipLaunchKernelGGL(quantize_rows_kernel<false>, grid, block, 0, st, X, M, K, q, scale);
+  return hipGetLastError();
+}
+
+// ============================================================================ fp32 path
+// C[m,n] = alpha * sum_k A(m,k) B(k,n) + beta * C[m,n] (+ bias[n]); element strides are
+// arbitrary, so the same kernel serves every product of the fp32 layer.  64x64 tile,
+// 16-deep k slices, 4x4 outputs per thread, fp32 FMA.
+__global__ __launch_bounds__(256) void f32_gemm_kernel(const F32GemmParams p) {
+  __shared__ float sA[16][64 + 1];
+  __shared__ float sB[16][64 + 1];
+  const int tid = threadIdx.x;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int tm = (tid / 16) * 4, tn = (tid % 16) * 4;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < p.K; k0 += 16) {
+    for (int i = tid; i < 64 * 16; i += 256) {
+      const int mm = i / 16, kk = i % 16;
+      const int m = m0 + mm, k = k0 + kk;
+      sA[kk][mm] = (m < p.M && k < p.K) ? p.A[(long)m * p.sam + (long)k * p.sak] : 0.f;
+      const int kk2 = i / 64, nn = i % 64;
+      const int k2 = k0 + kk2, n = n0 + nn;
+      sB[kk2][nn] = (k2 < p.K && n < p.N) ? p.B[(long)k2 * p.sbk + (long)n * p.sbn] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sA[kk][tm + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = sB[kk][tn + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + tm + i;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tn + j;
+      if (n >= p.N) continue;
+      float v = p.alpha * acc[i][j];
+      if (p.beta != 0.f) v += p.beta * p.C[(size_t)m * p.ldc + n];
+      if (p.bias != nullptr) v += p.bias[n];
+      p.C[(size_t)m * p.ldc + n] = v;
+    }
+  }
+}
+
+__global__ void f32_colsum_kernel(const float* X, int M, int N, float* out) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  float acc = 0.f;
+  for (int m = 0; m < M; ++m) acc += X[(size_t)m * N + n];
+  out[n] = acc;
+}
+
+hipError_t launch_f32_gemm(const F32GemmParams& p, hipStream_t st) {
+  if (p.M <= 0 || p.N <= 0) return hipSuccess;
+  const dim3 grid((p.N + 63) / 64, (p.M + 63) / 64), block(256);
+  hipLaunchKernelGGL(f32_gemm_kernel, grid, block, 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_f32_colsum(const float* X, int M, int N, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(f32_colsum_kernel, dim3((N + 255) / 256), dim3(256), 0, st, X, M, N, out);
+  return hipGetLastError();
+}
+
+}  // namespace ldl

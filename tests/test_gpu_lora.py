@@ -1,0 +1,165 @@
+"""GPU parity of the LoRA linear (forward and backward) against the fp64 oracle.
+
+All calls go through the C interface (ctypes binding) on the same seeded inputs
+the oracle receives.  Tolerance: max|gpu - ref| / max|ref| per tensor, 1e-5
+(outputs) and 1e-4 (gradients) for fp32, 5e-3 for bf16.
+"""
+import numpy as np
+import pytest
+
+from lora_dora_linear_amd import inputs
+from oracle import lora as olora
+from tests.gpu_util import assert_close, dev, host, require_gpu, torch
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 5e-3
+
+
+def _run(c, with_bias=False, need_dbias=False):
+    import lora_dora_linear_amd as L
+    kind = c.dtype
+    X, W0, A, B, dY = (dev(c.t[k], kind) for k in ("X", "W0", "A", "B", "dY"))
+    bias = dev(c.t["bias"], kind) if with_bias else None
+    Y, U = L.lora_linear_fwd(X, W0, A, B, c.s, bias=bias)
+    g = L.lora_linear_bwd(dY, X, W0, A, B, c.s, U=U, need_dbias=need_dbias)
+    torch.cuda.synchronize()
+    return Y, U, g
+
+
+def _oracle(c, with_bias=False):
+    X, W0, A, B, dY = (c.f64(k) for k in ("X", "W0", "A", "B", "dY"))
+    bias = c.f64("bias") if with_bias else None
+    return olora.lora_forward(X, W0, A, B, c.s, bias), olora.lora_backward(dY, X, W0, A, B, c.s), X @ A.T
+
+
+# ---------------------------------------------------------------- fp32, the tiny configuration
+@pytest.mark.parametrize("variant", ["s2", "s0", "B0", "W00"])
+def test_fp32_tiny(variant):
+    require_gpu()
+    s = 0.0 if variant == "s0" else 2.0
+    c = inputs.linear_case(1, 64, 256, 256, 8, s, "f32", with_bias=True,
+                           zero_B=(variant == "B0"), zero_W0=(variant == "W00"))
+    Y, U, g = _run(c, with_bias=True, need_dbias=True)
+    Yr, gr, Ur = _oracle(c, with_bias=True)
+    assert_close(host(Y), Yr, 1e-5, "Y")
+    assert_close(host(U), Ur, 1e-5, "U")
+    for k in ("dX", "dA", "dB"):
+        if not np.any(gr[k]):
+            assert not np.any(host(g[k])), k
+        else:
+            assert_close(host(g[k]), gr[k], 1e-4, k)
+    assert_close(host(g["dbias"]), gr["db"], 1e-4, "dbias")
+    if variant in ("s0", "B0"):
+        X, W0 = c.f64("X"), c.f64("W0")
+        assert_close(host(Y), X @ W0.T + c.f64("bias"), 1e-5, "Y vs base")
+
+
+# ---------------------------------------------------------------- bf16 at several tile shapes with a ragged M tail
+SHAPES = [
+    # M, N, K, r     (256x256 tiles, 256x192, 256x128, 128-row tiles; r not a multiple of 16; r = 128)
+    (300, 512, 384, 16),
+    (300, 576, 256, 32),
+    (257, 384, 640, 48),
+    (100, 640, 128, 8),
+    (64, 192, 128, 128),
+]
+
+
+@pytest.mark.parametrize("M,N,K,r", SHAPES)
+def test_bf16_parity(M, N, K, r):
+    require_gpu()
+    c = inputs.linear_case(2, M, N, K, r, 0.5, "bf16", with_bias=True)
+    Y, U, g = _run(c, with_bias=True, need_dbias=True)
+    Yr, gr, Ur = _oracle(c, with_bias=True)
+    assert_close(host(Y), Yr, BF16_TOL, "Y")
+    assert_close(host(U), Ur, 1e-5, "U")
+    for k in ("dX", "dA", "dB"):
+        assert_close(host(g[k]), gr[k], BF16_TOL, k)
+    assert_close(host(g["dbias"]), gr["db"], 1e-5, "dbias")
+
+
+def test_bf16_pure_low_rank_path():
+    """W0 = 0: everything in Y comes from the rank-r epilogue, so it cannot hide under the base term."""
+    require_gpu()
+    c = inputs.linear_case(2, 300, 512, 384, 16, 0.5, "bf16", zero_W0=True)
+    Y, U, g = _run(c)
+    Yr, gr, _ = _oracle(c)
+    assert_close(host(Y), Yr, BF16_TOL, "Y")
+    assert_close(host(g["dX"]), gr["dX"], BF16_TOL, "dX")
+
+
+def test_bf16_zero_delta_bitwise():
+    """s = 0 and B = 0 give bit-identical outputs, equal to X.W0^T within tolerance."""
+    require_gpu()
+    c0 = inputs.linear_case(2, 300, 512, 384, 16, 0.0, "bf16")
+    cB = inputs.linear_case(2, 300, 512, 384, 16, 0.7, "bf16", zero_B=True)
+    Y0, _, g0 = _run(c0)
+    YB, _, gB = _run(cB)
+    assert torch.equal(Y0, YB)
+    assert torch.equal(g0["dX"], gB["dX"])
+    X, W0 = c0.f64("X"), c0.f64("W0")
+    assert_close(host(Y0), X @ W0.T, BF16_TOL, "Y vs X.W0^T")
+    assert not torch.any(g0["dA"]) and not torch.any(g0["dB"])
+    assert not torch.any(gB["dA"])
+
+
+def test_bf16_fused_down_projection():
+    """U = X.A^T computed inside the base GEMM's K-loop matches the separate pass."""
+    require_gpu()
+    import lora_dora_linear_amd as L
+    c = inputs.linear_case(3, 300, 512, 384, 16, 0.5, "bf16", with_bias=True)
+    X, W0, A, B = (dev(c.t[k], "bf16") for k in ("X", "W0", "A", "B"))
+    bias = dev(c.t["bias"], "bf16")
+    Y1, U1 = L.lora_linear_fwd(X, W0, A, B, c.s, bias=bias)
+    L.set_tuning(0, 1)
+    try:
+        Y2, U2 = L.lora_linear_fwd(X, W0, A, B, c.s, bias=bias)
+    finally:
+        L.set_tuning(0, 0)
+    torch.cuda.synchronize()
+    Yr, _, Ur = _oracle(c, with_bias=True)
+    assert_close(host(Y2), Yr, BF16_TOL, "Y fused")
+    assert_close(host(U2), Ur, 1e-5, "U fused")
+    assert_close(host(Y2), host(Y1), BF16_TOL, "fused vs separate")
+
+
+def test_bf16_deterministic():
+    require_gpu()
+    c = inputs.linear_case(4, 300, 512, 384, 16, 0.5, "bf16")
+    Y1, _, g1 = _run(c)
+    Y2, _, g2 = _run(c)
+    assert torch.equal(Y1, Y2)
+    for k in ("dX", "dA", "dB"):
+        assert torch.equal(g1[k], g2[k]), k
+
+
+def test_empty_batch():
+    require_gpu()
+    import lora_dora_linear_amd as L
+    c = inputs.linear_case(5, 0, 256, 256, 16, 0.5, "bf16")
+    X, W0, A, B, dY = (dev(c.t[k], "bf16") for k in ("X", "W0", "A", "B", "dY"))
+    Y, U = L.lora_linear_fwd(X, W0, A, B, c.s)
+    g = L.lora_linear_bwd(dY, X, W0, A, B, c.s, U=U, need_dbias=True)
+    torch.cuda.synchronize()
+    assert Y.shape == (0, 256)
+    assert not torch.any(g["dA"]) and not torch.any(g["dB"]) and not torch.any(g["dbias"])
+
+
+def test_full_size_4096_sampled():
+    """M = K = N = 4096, r = 16, s = 0.5 (the benchmark launch configuration): sampled rows / entries."""
+    require_gpu()
+    c = inputs.linear_case(2, 4096, 4096, 4096, 16, 0.5, "bf16")
+    Y, U, g = _run(c)
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(4096, 24, replace=False))
+    X, W0, A, B, dY = (c.f64(k) for k in ("X", "W0", "A", "B", "dY"))
+    Yr = olora.lora_forward(X[rows], W0, A, B, c.s)
+    assert_close(host(Y[rows]), Yr, BF16_TOL, "Y rows")
+    dXr = olora.lora_backward(dY[rows], X[rows], W0, A, B, c.s)["dX"]
+    assert_close(host(g["dX"][rows]), dXr, BF16_TOL, "dX rows")
+    ncols = np.sort(rng.choice(4096, 16, replace=False))
+    kcols = np.sort(rng.choice(4096, 16, replace=False))
+    smp = olora.lora_weight_grads_sampled(dY, X, A, B, c.s, ncols, kcols)
+    assert_close(host(g["dB"][ncols]), smp["dB_rows"], BF16_TOL, "dB rows")
+    assert_close(host(g["dA"][:, kcols]), smp["dA_cols"], BF16_TOL, "dA cols")
