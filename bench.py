@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Throughput of the fused LoRA linear, forward + backward, on one MI355X.
+
+Default workload: bf16 LoRA linear, M = 4096 tokens, K = N = 4096, r = 16,
+s = 0.5 (X ~ N(0,1), W0, A ~ N(0, 1/K), B ~ N(0, 0.02 variance), dY ~ N(0,1)).
+One step = lora_linear_fwd + lora_linear_bwd (Y, U, dX, dA, dB) with every
+input already resident in HBM.  Algorithmic work per step:
+4MNK + 6Mr(K+N) FLOP (no B.A product, no weight gradient of the frozen W0).
+
+Prints ONE JSON line.  Extra workloads (--workload dora|swiglu|w8a8) print their
+own line in the same format for the other layer variants.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2516.6    # TFLOP/s dense bf16 MFMA, MI355X (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_INT8 = 5033.2    # TOP/s dense int8 MFMA
+PEAK_HBM = 8000.0     # GB/s
+
+METRIC = "fused LoRA/DoRA linear fwd+bwd TFLOP/s and % of bf16 MFMA peak (1 GPU)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="lora", choices=["lora", "dora", "swiglu", "w8a8"])
+    ap.add_argument("--M", type=int, default=None, help="token count override (w8a8 sweep point)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused-downproj", type=int, default=None, choices=[0, 1])
+    return ap.parse_args()
+
+
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def _ptrs(evs):
+    arr = (ctypes.c_void_p * len(evs))()
+    for i, e in enumerate(evs):
+        arr[i] = ctypes.c_void_p(e.cuda_event)
+    return arr
+
+
+def cpu_baseline_lora(M_sample, N, K, r, s):
+    """The fp64 oracle (as it stands) on the first M_sample rows of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from lora_dora_linear_amd import inputs
+    from oracle import lora as olora
+    c = inputs.linear_case(2, M_sample, N, K, r, s, "bf16")
+    X, W0, A, B, dY = (c.f64(k) for k in ("X", "W0", "A", "B", "dY"))
+    t0 = time.perf_counter()
+    olora.lora_forward(X, W0, A, B, s)
+    olora.lora_backward(dY, X, W0, A, B, s)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * M_sample * N * K + 6.0 * M_sample * r * (K + N)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {M_sample} of the 4096 token rows (same N, K, r), fp64 forward + backward, "
+                      f"{dt:.2f} s wall", "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; multi-GPU runs are not part of it "
+                                   "(the data-parallel sharding is described in DESIGN.md)",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from lora_dora_linear_amd import binding, inputs
+    L = binding.lib()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    if args.fused_downproj is not None:
+        binding.set_tuning(0, args.fused_downproj)
+
+    def up(arr, kind):
+        if kind == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
+
+    P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+    st = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)  # noqa: E731
+
+    def check(code, name):
+        if code != 0:
+            raise RuntimeError(f"{name}: {binding.status_string(code)}")
+
+    bf = torch.bfloat16
+    f32 = torch.float32
+    wl = args.workload
+    gemm_kinds = (0, 1)
+    gemm_flops = {}
+    if wl == "lora":
+        M, N, K, r, s = 4096, 4096, 4096, 16, 0.5
+        c = inputs.linear_case(2, M, N, K, r, s, "bf16")
+        X, W0, A, B, dY = (up(c.t[k], "bf16") for k in ("X", "W0", "A", "B", "dY"))
+        Y = torch.empty((M, N), dtype=bf, device=dev)
+        U = torch.empty((M, r), dtype=f32, device=dev)
+        dX = torch.empty((M, K), dtype=bf, device=dev)
+        dA = torch.empty((r, K), dtype=f32, device=dev)
+        dB = torch.empty((N, r), dtype=f32, device=dev)
+        nf = binding.workspace_bytes("lora_fwd", M, N, K, r)
+        nb = binding.workspace_bytes("lora_bwd", M, N, K, r)
+        ws = torch.empty(max(nf, nb, 256), dtype=torch.uint8, device=dev)
+
+        def step():
+            check(L.lora_linear_fwd(M, N, K, r, s, 1, P(X), P(W0), P(A), P(B), None, P(Y), P(U), P(ws), nf, st()),
+                  "lora_linear_fwd")
+            check(L.lora_linear_bwd(M, N, K, r, s, 1, P(dY), P(X), P(W0), P(A), P(B), P(U), P(dX), P(dA), P(dB),
+                                    None, P(ws), nb, st()), "lora_linear_bwd")
+        flops = 4.0 * M * N * K + 6.0 * M * r * (K + N)
+        gemm_flops = {0: 2.0 * M * N * K + 2.0 * M * N * r, 1: 2.0 * M * N * K + 2.0 * M * K * r}
+        config = {"workload": f"bf16 LoRA linear fwd+bwd, M={M} tokens (4x1024), K=N={K}, r={r}, s={s}",
+                  "M": M, "N": N, "K": K, "r": r, "s": s, "B_init": "N(0, 0.02) read as variance"}
+    elif wl == "dora":
+        M, N, K, r, s, eps = 4096, 3072, 3072, 32, 1.0, 1e-12
+        c = inputs.linear_case(3, M, N, K, r, s, "bf16", dora=True)
+        X, W0, A, B, dY = (up(c.t[k], "bf16") for k in ("X", "W0", "A", "B", "dY"))
+        m = up(c.t["m"], "f32")
+        w0sq = torch.empty((N,), dtype=f32, device=dev)
+        check(L.dora_prepare(N, K, 1, P(W0), P(w0sq), st()), "dora_prepare")
+        Y = torch.empty((M, N), dtype=bf, device=dev)
+        Z = torch.empty((M, N), dtype=bf, device=dev)
+        U = torch.empty((M, r), dtype=f32, device=dev)
+        state = torch.empty((binding.dora_state_floats(N, r),), dtype=f32, device=dev)
+        dX = torch.empty((M, K), dtype=bf, device=dev)
+        dA = torch.empty((r, K), dtype=f32, device=dev)
+        dB = torch.empty((N, r), dtype=f32, device=dev)
+        dm = torch.empty((N,), dtype=f32, device=dev)
+        nb = binding.workspace_bytes("dora_bwd", M, N, K, r)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+
+        def step():
+            check(L.dora_linear_fwd(M, N, K, r, s, eps, 1, P(X), P(W0), P(A), P(B), P(m), P(w0sq), None, P(Y), P(U),
+                                    P(Z), P(state), P(ws), 0, st()), "dora_linear_fwd")
+            check(L.dora_linear_bwd(M, N, K, r, s, eps, 1, P(dY), P(X), P(W0), P(A), P(B), P(m), P(U), P(Z),
+                                    P(state), P(dX), P(dA), P(dB), P(dm), None, P(ws), nb, st()), "dora_linear_bwd")
+        lora_flops = 4.0 * M * N * K + 6.0 * M * r * (K + N)
+        dora_flops = 2.0 * N * K * r * 2 + 2.0 * r * r * K       # P = W0.A^T and (w.B)^T.W0, plus G = A.A^T
+        flops = lora_flops + dora_flops
+        gemm_flops = {0: 2.0 * M * N * K + 2.0 * M * N * r, 1: 2.0 * M * N * K + 2.0 * M * K * r}
+        config = {"workload": f"bf16 DoRA (row-scaled) linear fwd+bwd, M={M}, K=N={K}, r={r}, s={s}, eps={eps}",
+                  "M": M, "N": N, "K": K, "r": r, "s": s}
+    elif wl == "swiglu":
+        M, K, H, r, s = 8192, 4096, 14336, 64, 0.25
+        c = inputs.mlp_case(4, M, K, H, r, s)
+        Xd, dO = up(c.t["X"], "bf16"), up(c.t["dY"], "bf16")
+        Wt = {k: up(c.t[k], "bf16") for k in ("Wg", "Ag", "Bg", "Wu", "Au", "Bu", "Wd", "Ad", "Bd")}
+        Out = torch.empty((M, K), dtype=bf, device=dev)
+        E = torch.empty((M, H), dtype=bf, device=dev)
+        Gu = torch.empty((M, H), dtype=bf, device=dev)
+        Hs = torch.empty((M, H), dtype=bf, device=dev)
+        U = torch.empty((M, 3 * r), dtype=f32, device=dev)
+        dX = torch.empty((M, K), dtype=bf, device=dev)
+        gr = {k: torch.empty(sh, dtype=f32, device=dev) for k, sh in
+              (("dAg", (r, K)), ("dBg", (H, r)), ("dAu", (r, K)), ("dBu", (H, r)), ("dAd", (r, H)), ("dBd", (K, r)))}
+        nb = binding.workspace_bytes("swiglu_bwd", M, H, K, r)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        w = [P(Wt[k]) for k in ("Wg", "Ag", "Bg", "Wu", "Au", "Bu", "Wd", "Ad", "Bd")]
+
+        def step():
+            check(L.swiglu_lora_mlp_fwd(M, K, H, r, s, s, s, P(Xd), *w, P(Out), P(E), P(Gu), P(Hs), P(U), P(ws), 0,
+                                        st()), "swiglu_lora_mlp_fwd")
+            check(L.swiglu_lora_mlp_bwd(M, K, H, r, s, s, s, P(dO), P(Xd), *w, P(E), P(Gu), P(Hs), P(U), P(dX),
+                                        P(gr["dAg"]), P(gr["dBg"]), P(gr["dAu"]), P(gr["dBu"]), P(gr["dAd"]),
+                                        P(gr["dBd"]), P(ws), nb, st()), "swiglu_lora_mlp_bwd")
+        base = 2.0 * M * K * H * 3 * 2           # three projections, forward + input gradient
+        lora = 3 * (6.0 * M * r * (K + H))
+        flops = base + lora
+        gemm_kinds = ()
+        config = {"workload": f"bf16 LoRA MLP with fused SwiGLU fwd+bwd, M={M}, K={K}, H={H}, r={r}, s={s}",
+                  "M": M, "K": K, "H": H, "r": r, "s": s}
+    else:
+        M = args.M or 4096
+        N, K, r, s = 5120, 5120, 32, 0.5
+        c = inputs.linear_case(5, M, N, K, r, s, "bf16")
+        X, A, B, dY = (up(c.t[k], "bf16") for k in ("X", "A", "B", "dY"))
+        W0f = up(inputs.normal(5, 1, (N, K), 1.0 / np.sqrt(K), "f32"), "f32")
+        Wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+        sw = torch.empty((N,), dtype=f32, device=dev)
+        check(L.w8a8_quantize_weight(N, K, 0, P(W0f), P(Wq), P(sw), st()), "w8a8_quantize_weight")
+        Y = torch.empty((M, N), dtype=bf, device=dev)
+        Xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+        sx = torch.empty((M,), dtype=f32, device=dev)
+        U = torch.empty((M, r), dtype=f32, device=dev)
+        dX = torch.empty((M, K), dtype=bf, device=dev)
+        dA = torch.empty((r, K), dtype=f32, device=dev)
+        dB = torch.empty((N, r), dtype=f32, device=dev)
+        nf = binding.workspace_bytes("w8a8_fwd", M, N, K, r)
+        nb = binding.workspace_bytes("w8a8_bwd", M, N, K, r)
+        ws = torch.empty(max(nf, nb, 256), dtype=torch.uint8, device=dev)
+
+        def step():
+            check(L.w8a8_lora_linear_fwd(M, N, K, r, s, P(X), P(Wq), P(sw), P(A), P(B), None, P(Y), P(Xq), P(sx),
+                                         P(U), P(ws), nf, st()), "w8a8_lora_linear_fwd")
+            check(L.w8a8_lora_linear_bwd(M, N, K, r, s, P(dY), P(X), P(Wq), P(sw), P(A), P(B), P(U), P(dX), P(dA),
+                                         P(dB), P(ws), nb, st()), "w8a8_lora_linear_bwd")
+        flops = 4.0 * M * N * K + 6.0 * M * r * (K + N)   # int8 ops of the base counted with the bf16 ones
+        gemm_flops = {0: 2.0 * M * N * K + 2.0 * M * N * r, 1: 2.0 * M * N * K + 2.0 * M * K * r}
+        config = {"workload": f"W8A8 int8 base + bf16 LoRA fwd+bwd, M={M}, K=N={K}, r={r}, s={s}",
+                  "M": M, "N": N, "K": K, "r": r, "s": s}
+
+    # ------------------------------------------------------------------ warmup, then the timed region
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K_steps = args.steps
+    evs = {k: (_events(torch, K_steps), _events(torch, K_steps)) for k in gemm_kinds}
+    keep = []
+    for k in gemm_kinds:
+        a, b = _ptrs(evs[k][0]), _ptrs(evs[k][1])
+        keep.append((a, b))
+        check(L.ldl_set_kernel_events(k, a, b, K_steps), "ldl_set_kernel_events")
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(K_steps):
+        step()
+    t_stop.record()
+    torch.cuda.synchronize()
+    for k in gemm_kinds:
+        L.ldl_set_kernel_events(k, None, None, 0)
+    ms = t_start.elapsed_time(t_stop) / K_steps
+    value = flops / (ms * 1e-3) / 1e12
+
+    kern = {}
+    for k in gemm_kinds:
+        times = [a.elapsed_time(b) for a, b in zip(*evs[k])]
+        avg = sum(times) / len(times)
+        kern[k] = {"avg_us": avg * 1e3, "tflops": gemm_flops[k] / (avg * 1e-3) / 1e12}
+
+    out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K_steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16" if wl != "w8a8" else "int8+bf16", "data": "synthetic",
+           "config": config, "pct_bf16_peak": round(100.0 * value / PEAK_BF16, 2)}
+    if kern:
+        dom = max(kern, key=lambda k: kern[k]["avg_us"])
+        names = {0: "forward base GEMM (gemm_kernel NT)", 1: "input-gradient GEMM (gemm_kernel NN)"}
+        peak = PEAK_INT8 if (wl == "w8a8" and dom == 0) else PEAK_BF16
+        out["roofline"] = {"bound": "mfma", "kernel": names[dom], "achieved": round(kern[dom]["tflops"], 1),
+                           "peak": peak, "unit": "TFLOP/s", "frac": round(kern[dom]["tflops"] / peak, 4),
+                           "traffic": None}
+        out["kernels"] = {names[k]: {"avg_us": round(v["avg_us"], 2), "TFLOP/s": round(v["tflops"], 1)}
+                          for k, v in kern.items()}
+    if wl == "lora" and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_lora(512, 4096, 4096, 16, 0.5)
+        out["cpu_baseline"].pop("seconds", None)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

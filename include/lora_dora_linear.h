@@ -79,6 +79,16 @@ int ldl_version(void);
 typedef enum { LDL_TUNE_FWD_FUSED_DOWNPROJ = 0 } ldl_tune_key;
 int ldl_set_tuning(int key, int value);
 
+/* Kernel timing hook for profilers and benchmarks.  While set, the library
+ * records start_events[i] / stop_events[i] (hipEvent_t, passed as void*) on the
+ * call's stream around the i-th launch of the kernel `kind`, for i < count, and
+ * stops recording after `count` launches.  count = 0 (or NULL arrays) turns it
+ * off.  The arrays must stay valid while the hook is set.
+ *   kind 0: the base GEMM of the LoRA / DoRA / W8A8 forward (the [M,N] output GEMM)
+ *   kind 1: the input-gradient GEMM of the LoRA / DoRA / W8A8 backward (the [M,K] dX GEMM)
+ * Returns LDL_OK or LDL_E_INVAL. */
+int ldl_set_kernel_events(int kind, void** start_events, void** stop_events, int count);
+
 /* Bytes of device workspace the entry point `op` needs for these sizes (256-byte
  * aligned, 0 when none).  Pure host arithmetic; never fails (returns 0 for
  * invalid sizes, which the entry point then rejects). */

@@ -27,6 +27,7 @@ SIGNATURES = {
     "ldl_status_string": ([_i], ctypes.c_char_p),
     "ldl_version": ([], _i),
     "ldl_set_tuning": ([_i, _i], _i),
+    "ldl_set_kernel_events": ([_i, ctypes.POINTER(_p), ctypes.POINTER(_p), _i], _i),
     "ldl_workspace_bytes": ([_i, _i, _i, _i, _i, _i], _z),
     "dora_state_floats": ([_i, _i], _z),
     "lora_linear_fwd": ([_i, _i, _i, _i, _f, _i, _p, _p, _p, _p, _p, _p, _p, _p, _z, _p], _i),

@@ -12,6 +12,33 @@ namespace {
 
 int g_fwd_fused = 0;   // LDL_TUNE_FWD_FUSED_DOWNPROJ
 
+// Kernel timing hook (ldl_set_kernel_events).
+struct EventHook {
+  void** start = nullptr;
+  void** stop = nullptr;
+  int count = 0;
+  int next = 0;
+};
+EventHook g_hooks[2];
+
+// Launch a GEMM; when a hook is set for `hook_kind`, bracket it with the caller's events.
+hipError_t gemm_timed(int hook_kind, GemmKind kind, const GemmParams& p, hipStream_t st) {
+  EventHook* h = (hook_kind >= 0 && hook_kind < 2) ? &g_hooks[hook_kind] : nullptr;
+  const bool rec = h && h->count > 0 && h->next < h->count;
+  if (rec) {
+    const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(h->start[h->next]), st);
+    if (e != hipSuccess) return e;
+  }
+  const hipError_t e = launch_gemm(kind, p, st);
+  if (e != hipSuccess) return e;
+  if (rec) {
+    const hipError_t e2 = hipEventRecord(static_cast<hipEvent_t>(h->stop[h->next]), st);
+    ++h->next;
+    return e2;
+  }
+  return hipSuccess;
+}
+
 constexpr size_t kAlign = 256;
 constexpr size_t kMaxBytes = (size_t)1 << 31;   // buffer resources take 31-bit sizes
 
@@ -199,6 +226,16 @@ const char* ldl_status_string(int status) {
 
 int ldl_version(void) { return 100; }
 
+int ldl_set_kernel_events(int kind, void** start_events, void** stop_events, int count) {
+  if (kind < 0 || kind > 1 || count < 0) return LDL_E_INVAL;
+  if (count > 0 && (!start_events || !stop_events)) return LDL_E_INVAL;
+  g_hooks[kind].start = count > 0 ? start_events : nullptr;
+  g_hooks[kind].stop = count > 0 ? stop_events : nullptr;
+  g_hooks[kind].count = count > 0 ? count : 0;
+  g_hooks[kind].next = 0;
+  return LDL_OK;
+}
+
 int ldl_set_tuning(int key, int value) {
   if (key == LDL_TUNE_FWD_FUSED_DOWNPROJ && (value == 0 || value == 1)) {
     g_fwd_fused = value;
@@ -274,12 +311,12 @@ int lora_linear_fwd(int M, int N, int K, int r, float s, int dtype, const void* 
   p.bias = bias; p.out = Y; p.ldo = N;
   if (g_fwd_fused && r <= 32 && N % 128 == 0) {
     p.side = A; p.r_side = r; p.side_save = U_save; p.ld_side_save = r;
-    LDL_TRY(launch_gemm(GK_NT_FUSED, p, st));
+    LDL_TRY(gemm_timed(0, GK_NT_FUSED, p, st));
     return LDL_OK;
   }
   LDL_TRY(rowproj(M, K, r, X, K, A, nullptr, r, K, U, r, 1.f, st));
   p.S = U; p.ld_s = r;
-  LDL_TRY(launch_gemm(GK_NT_PLAIN, p, st));
+  LDL_TRY(gemm_timed(0, GK_NT_PLAIN, p, st));
   return LDL_OK;
 }
 
@@ -343,7 +380,7 @@ int lora_linear_bwd(int M, int N, int K, int r, float s, int dtype, const void* 
     p.S = w.V; p.ld_s = r; p.r_epi = r; p.s_epi = s;
     p.e0 = A; p.e1 = A; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = r;
     p.out = dX; p.ldo = K;
-    LDL_TRY(launch_gemm(GK_NN_PLAIN, p, st));
+    LDL_TRY(gemm_timed(1, GK_NN_PLAIN, p, st));
   }
   // dB = s.dY^T.U  (+ dbias = column sums of dY in the same pass)
   LDL_TRY(colproj(M, N, r, dY, N, U, r, 1.f, nullptr, 0, dbias ? 2 : 0, w.nsB, w.msB, w.partB, w.csB, st));
@@ -401,7 +438,7 @@ int dora_linear_fwd(int M, int N, int K, int r, float s, float eps, int dtype, c
   p.e0 = B; p.e1 = B; p.e_ldn = r; p.e_ldj = 1; p.e_jsplit = r;
   p.col_scale = g; p.bias = bias;
   p.out = Y; p.ldo = N; p.out2 = Z_save; p.ldo2 = N;
-  LDL_TRY(launch_gemm(GK_NT_DORA, p, st));
+  LDL_TRY(gemm_timed(0, GK_NT_DORA, p, st));
   return LDL_OK;
 }
 
@@ -445,7 +482,7 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, c
       p.S = w.V; p.ld_s = r; p.r_epi = r; p.s_epi = s;
       p.e0 = A; p.e1 = A; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = r;
       p.out = dX; p.ldo = K;
-      LDL_TRY(launch_gemm(GK_NN_SCALE, p, st));
+      LDL_TRY(gemm_timed(1, GK_NN_SCALE, p, st));
     }
     // s.V^T.X into the first nsA partials of dA
     LDL_TRY(colproj(M, K, r, X, K, w.V, r, s, nullptr, 0, 0, w.nsA, w.msA, w.partA, nullptr, st));
@@ -649,7 +686,7 @@ int w8a8_lora_linear_fwd(int M, int N, int K, int r, float s, const void* X, con
   p.S = U; p.ld_s = r; p.r_epi = r; p.s_epi = s;
   p.e0 = B; p.e1 = B; p.e_ldn = r; p.e_ldj = 1; p.e_jsplit = r;
   p.bias = bias; p.out = Y; p.ldo = N;
-  LDL_TRY(launch_gemm(GK_NT_I8_DEQ, p, st));
+  LDL_TRY(gemm_timed(0, GK_NT_I8_DEQ, p, st));
   return LDL_OK;
 }
 
@@ -683,7 +720,7 @@ int w8a8_lora_linear_bwd(int M, int N, int K, int r, float s, const void* dY, co
     p.S = w.V; p.ld_s = r; p.r_epi = r; p.s_epi = s;
     p.e0 = A; p.e1 = A; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = r;
     p.out = dX; p.ldo = K;
-    LDL_TRY(launch_gemm(GK_NN_I8_SCALE, p, st));
+    LDL_TRY(gemm_timed(1, GK_NN_I8_SCALE, p, st));
   }
   LDL_TRY(colproj(M, N, r, dY, N, U, r, 1.f, nullptr, 0, 0, w.nsB, w.msB, w.partB, nullptr, st));
   LDL_TRY(reduce(N, r, w.partB, (size_t)N * w.rp, w.nsB, w.rp, false, s, dB, r, st));

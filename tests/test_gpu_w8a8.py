@@ -69,7 +69,7 @@ def _run(c, W0f, need_dx=True):
 def test_w8a8_parity(M, N, K, r):
     require_gpu()
     c, W0f = _case(M, N, K, r)
-    Y, Xq, sx, g = _run(c)
+    Y, Xq, sx, g = _run(c, W0f)
     Wq_ref, sw_ref = ow.quantize_rows_int8(W0f)
     X, A, B, dY = (c.f64(k) for k in ("X", "A", "B", "dY"))
     f = ow.w8a8_forward(X, Wq_ref, sw_ref, A, B, c.s)
@@ -85,7 +85,7 @@ def test_w8a8_full_size_sampled(M):
     """K = N = 5120, r = 32, s = 0.5 at both ends of the M sweep: sampled rows and entries."""
     require_gpu()
     c, W0f = _case(M, 5120, 5120, 32)
-    Y, Xq, sx, g = _run(c)
+    Y, Xq, sx, g = _run(c, W0f)
     Wq_ref, sw_ref = ow.quantize_rows_int8(W0f)
     rng = np.random.default_rng(2)
     rows = np.sort(rng.choice(M, 16, replace=False))
