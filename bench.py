@@ -40,7 +40,11 @@ def parse():
 
 
 def _events(torch, n):
-    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:          # torch creates the underlying hipEvent on first record
+        e.record()
+    torch.cuda.synchronize()
+    return evs
 
 
 def _ptrs(evs):

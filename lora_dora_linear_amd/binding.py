@@ -42,7 +42,7 @@ SIGNATURES = {
     "w8a8_quantize_rows": ([_i, _i, _p, _p, _p, _p], _i),
     "int8_gemm_raw": ([_i, _i, _i, _p, _p, _p, _p], _i),
     "w8a8_lora_linear_fwd": ([_i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _z, _p], _i),
-    "w8a8_lora_linear_bwd": ([_i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _z, _p], _i),
+    "w8a8_lora_linear_bwd": ([_i, _i, _i, _i, _f] + [_p] * 11 + [_z, _p], _i),
 }
 
 

@@ -143,3 +143,15 @@ def test_workspace_query_with_empty_batch(L):
     # M == 0 is valid everywhere; the size queries must not divide by zero
     for op in range(8):
         assert L.ldl_workspace_bytes(op, 0, 256, 256, 16, 1) % 256 == 0
+
+
+def test_binding_argument_counts_match_the_header():
+    from lora_dora_linear_amd import binding
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    decl = {}
+    for m in re.finditer(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|void)\s*\**\s*(\w+)\s*\(([^;]*?)\);", src,
+                         re.M | re.S):
+        decl[m.group(1)] = len([a for a in m.group(2).split(",") if a.strip() and a.strip() != "void"])
+    assert set(decl) == set(binding.SIGNATURES)
+    for name, n in decl.items():
+        assert len(binding.SIGNATURES[name][0]) == n, name
