@@ -54,8 +54,8 @@ def _ptrs(evs):
     return arr
 
 
-def cpu_baseline_lora(M_sample, N, K, r, s):
-    """The fp64 oracle (as it stands) on the first M_sample rows of the same workload."""
+def cpu_baseline_lora(M_sample, N, K, r, s, repeats=3):
+    """The fp64 oracle (as it stands) on the first M_sample rows of the same workload (median of repeats)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -63,15 +63,18 @@ def cpu_baseline_lora(M_sample, N, K, r, s):
     from oracle import lora as olora
     c = inputs.linear_case(2, M_sample, N, K, r, s, "bf16")
     X, W0, A, B, dY = (c.f64(k) for k in ("X", "W0", "A", "B", "dY"))
-    t0 = time.perf_counter()
-    olora.lora_forward(X, W0, A, B, s)
-    olora.lora_backward(dY, X, W0, A, B, s)
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        olora.lora_forward(X, W0, A, B, s)
+        olora.lora_backward(dY, X, W0, A, B, s)
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[len(times) // 2]
     flops = 4.0 * M_sample * N * K + 6.0 * M_sample * r * (K + N)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {M_sample} of the 4096 token rows (same N, K, r), fp64 forward + backward, "
-                      f"{dt:.2f} s wall", "seconds": dt}
+            "sample": f"{M_sample} of the 4096 token rows (same N, K, r), fp64 forward + backward, "
+                      f"median of {repeats}: {dt:.2f} s wall", "seconds": dt}
 
 
 def main():
@@ -263,7 +266,7 @@ def main():
         out["kernels"] = {names[k]: {"avg_us": round(v["avg_us"], 2), "TFLOP/s": round(v["tflops"], 1)}
                           for k, v in kern.items()}
     if wl == "lora" and not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_lora(512, 4096, 4096, 16, 0.5)
+        out["cpu_baseline"] = cpu_baseline_lora(4096, 4096, 4096, 16, 0.5)
         out["cpu_baseline"].pop("seconds", None)
     print(json.dumps(out))
 
