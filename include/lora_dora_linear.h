@@ -73,7 +73,7 @@ int ldl_version(void);
 
 /* Tuning switches (process-wide; not thread-safe against concurrent calls).
  *   LDL_TUNE_FWD_FUSED_DOWNPROJ (0/1, default 0): compute U = X.A^T inside the
- *     K-loop of the base GEMM from the LDS-staged X tiles (r <= 32, N multiple
+ *     K-loop of the base GEMM from the LDS-staged X tiles (r <= 64, N multiple
  *     of 128) instead of a separate rank-r pass before it.
  * Returns LDL_OK, or LDL_E_INVAL for an unknown key or value. */
 typedef enum { LDL_TUNE_FWD_FUSED_DOWNPROJ = 0 } ldl_tune_key;

@@ -309,7 +309,7 @@ int lora_linear_fwd(int M, int N, int K, int r, float s, int dtype, const void* 
   p.a = X; p.lda = K; p.b0 = W0; p.ldb = K; p.kseg = K;
   p.r_epi = r; p.s_epi = s; p.e0 = B; p.e1 = B; p.e_ldn = r; p.e_ldj = 1; p.e_jsplit = r;
   p.bias = bias; p.out = Y; p.ldo = N;
-  if (g_fwd_fused && r <= 32 && N % 128 == 0) {
+  if (g_fwd_fused && r <= 64 && N % 128 == 0) {
     p.side = A; p.r_side = r; p.side_save = U_save; p.ld_side_save = r;
     LDL_TRY(gemm_timed(0, GK_NT_FUSED, p, st));
     return LDL_OK;

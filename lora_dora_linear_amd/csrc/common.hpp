@@ -27,6 +27,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 // ------------------------------------------------------------------ bf16 helpers
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -53,6 +55,15 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 p, u32x4 q, f32x4 acc) {
 }
 __device__ __forceinline__ i32x4 mfma_i8(u32x4 p, u32x4 q, i32x4 acc) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i32x4(p), as_i32x4(q), acc, 0, 0, 0);
+}
+// 32x32 blocks: operand lane l holds row (l & 31) and the 16-byte reduction
+// chunk (l >> 5); result lane l holds D[8*(v >> 2) + 4*(l >> 5) + (v & 3)][l & 31]
+// for v = 0..15.
+__device__ __forceinline__ f32x16 mfma32_bf16(u32x4 p, u32x4 q, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(p), as_bf16x8(q), acc, 0, 0, 0);
+}
+__device__ __forceinline__ i32x16 mfma32_i8(u32x4 p, u32x4 q, i32x16 acc) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(as_i32x4(p), as_i32x4(q), acc, 0, 0, 0);
 }
 
 // ------------------------------------------------------------------ LDS swizzle

@@ -7,7 +7,7 @@
 //   NT bf16         256x256, 256x192, 256x128, 128x128, 128x64
 //   NT fused side   256x128 (down-projection rows computed in the K-loop)
 //   NT int8         256x128, 128x128, 128x64
-//   NN (bf16/int8 Q) 256x128, 128x128, 128x64
+//   NN (bf16/int8 Q) 256x256, 256x192, 256x128, 128x128, 128x64
 #include "internal.hpp"
 
 namespace ldl {
@@ -21,8 +21,10 @@ static hipError_t run(const GemmParams& p, hipStream_t st) {
 }
 
 static int pick_bn(GemmKind kind, int N) {
-  const bool wide_ok = (kind == GK_NT_PLAIN || kind == GK_NT_DORA || kind == GK_NT_SWIGLU);
-  const bool b192_ok = (kind == GK_NT_PLAIN || kind == GK_NT_DORA);
+  const bool wide_ok = (kind == GK_NT_PLAIN || kind == GK_NT_DORA || kind == GK_NT_SWIGLU || kind == GK_NN_PLAIN ||
+                        kind == GK_NN_SCALE || kind == GK_NN_I8_SCALE || kind == GK_NN_SWIGLU);
+  const bool b192_ok = (kind == GK_NT_PLAIN || kind == GK_NT_DORA || kind == GK_NN_PLAIN || kind == GK_NN_SCALE ||
+                        kind == GK_NN_I8_SCALE);
   if (wide_ok && N % 256 == 0) return 256;
   if (b192_ok && N % 192 == 0) return 192;
   if (N % 128 == 0) return 128;
@@ -66,9 +68,9 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
       if (bn >= 128) return run<128, 128, false, false, false, false, 0, true, EPI_SWIGLU_FWD>(p, st);
       return run<128, 64, false, false, false, false, 0, true, EPI_SWIGLU_FWD>(p, st);
     case GK_NT_FUSED:
-      // down-projection computed in the K-loop; side rows padded to 16 or 32
-      if (p.r_side <= 16) return run<256, 128, false, false, false, false, 16, false, EPI_PLAIN>(p, st);
-      return run<256, 128, false, false, false, false, 32, false, EPI_PLAIN>(p, st);
+      // down-projection computed in the K-loop; side rows padded to 32 or 64
+      if (p.r_side <= 32) return run<256, 128, false, false, false, false, 32, false, EPI_PLAIN>(p, st);
+      return run<256, 128, false, false, false, false, 64, false, EPI_PLAIN>(p, st);
     case GK_NT_I8_DEQ:
       if (bn >= 128) return big ? run<256, 128, true, false, false, false, 0, true, EPI_DEQUANT>(p, st)
                                 : run<128, 128, true, false, false, false, 0, true, EPI_DEQUANT>(p, st);
@@ -78,18 +80,25 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
                                 : run<128, 128, true, false, false, false, 0, false, EPI_RAW_I32>(p, st);
       return run<128, 64, true, false, false, false, 0, false, EPI_RAW_I32>(p, st);
     case GK_NN_PLAIN:
+      if (bn == 256 && big) return run<256, 256, false, true, false, false, 0, true, EPI_PLAIN>(p, st);
+      if (bn == 192 && big) return run<256, 192, false, true, false, false, 0, true, EPI_PLAIN>(p, st);
       if (bn >= 128) return big ? run<256, 128, false, true, false, false, 0, true, EPI_PLAIN>(p, st)
                                 : run<128, 128, false, true, false, false, 0, true, EPI_PLAIN>(p, st);
       return run<128, 64, false, true, false, false, 0, true, EPI_PLAIN>(p, st);
     case GK_NN_SCALE:
+      if (bn == 256 && big) return run<256, 256, false, true, false, true, 0, true, EPI_PLAIN>(p, st);
+      if (bn == 192 && big) return run<256, 192, false, true, false, true, 0, true, EPI_PLAIN>(p, st);
       if (bn >= 128) return big ? run<256, 128, false, true, false, true, 0, true, EPI_PLAIN>(p, st)
                                 : run<128, 128, false, true, false, true, 0, true, EPI_PLAIN>(p, st);
       return run<128, 64, false, true, false, true, 0, true, EPI_PLAIN>(p, st);
     case GK_NN_I8_SCALE:
+      if (bn == 256 && big) return run<256, 256, false, true, true, true, 0, true, EPI_PLAIN>(p, st);
+      if (bn == 192 && big) return run<256, 192, false, true, true, true, 0, true, EPI_PLAIN>(p, st);
       if (bn >= 128) return big ? run<256, 128, false, true, true, true, 0, true, EPI_PLAIN>(p, st)
                                 : run<128, 128, false, true, true, true, 0, true, EPI_PLAIN>(p, st);
       return run<128, 64, false, true, true, true, 0, true, EPI_PLAIN>(p, st);
     case GK_NN_SWIGLU:
+      if (bn == 256 && big) return run<256, 256, false, true, false, false, 0, true, EPI_SWIGLU_BWD>(p, st);
       if (bn >= 128) return big ? run<256, 128, false, true, false, false, 0, true, EPI_SWIGLU_BWD>(p, st)
                                 : run<128, 128, false, true, false, false, 0, true, EPI_SWIGLU_BWD>(p, st);
       return run<128, 64, false, true, false, false, 0, true, EPI_SWIGLU_BWD>(p, st);

@@ -20,10 +20,13 @@
 // kernel fusion - 20-30% faster training" (LoRA-epilogue commit): the [N,K]
 // product B.A and the [M,N] low-rank product are never stored.
 //
-// Tiling: 4 waves (2 x 2), block tile BM x BN, k-tile of 128 bytes per row
-// (64 bf16 or 128 int8), double-buffered LDS, one barrier per k-tile,
-// operands staged through registers so that the NN operand can be transposed
-// (8 x 8 register transpose) and the DoRA / W8A8 column scale applied on load.
+// Tiling: 4 waves (2 x 2), block tile BM x BN, wave tile (BM/2) x (BN/2) in
+// 32x32 MFMA blocks (v_mfma_f32_32x32x16_bf16 / v_mfma_i32_32x32x32_i8: one
+// wave per SIMD keeps the matrix pipe ~80 % busy with these, against ~55 %
+// with the 16x16 shapes), k-tile of 128 bytes per row (64 bf16 or 128 int8),
+// a two-stage LDS ring filled by direct buffer-to-LDS copies, one barrier per
+// k-tile.  The NN operand is staged through registers instead, transposed
+// 8 x 8 and optionally row-scaled (DoRA g, W8A8 sw) on its way into LDS.
 #pragma once
 
 #include "common.hpp"
@@ -123,12 +126,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
   constexpr int BM = C::BM, BN = C::BN;
   constexpr bool I8 = C::kI8, NN = C::kNN;
   constexpr int RSP = C::kSideRsp;
-  constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 16, FN = TN / 16;
-  constexpr int BK = I8 ? 128 : 64;     // elements per k-tile
+  constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;   // 32x32 MFMA blocks per wave
+  constexpr int BK = I8 ? 128 : 64;     // elements per k-tile (128 bytes per row)
   constexpr int HALF = FM / 2;
-  static_assert(FM % 2 == 0, "BM/32 must be even");
+  static_assert(FM >= 2 && FM % 2 == 0 && FN >= 1, "wave tile must hold 2x1 32x32 blocks");
+  static_assert(RSP % 32 == 0, "side rows are padded to 32");
   static_assert(!NN || !I8, "NN takes bf16 P");
-  using Acc = typename std::conditional<I8, i32x4, f32x4>::type;
+  using Acc = typename std::conditional<I8, i32x16, f32x16>::type;
 
   // two LDS stages, each [BM rows of P | BN rows of Q | RSP side rows] x 128 bytes
   __shared__ __attribute__((aligned(16))) uint8_t smem0[GemmSmem<C>::kBuf];
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int lr = lane & 15, lq = lane >> 4;
+  const int lr = lane & 31, lq = lane >> 5;    // fragment row / 16-byte chunk within a step
 
   const uint32_t lda_b = (uint32_t)p.lda * (I8 ? 1 : 2);
   const uint32_t ldb_b = (uint32_t)p.ldb * ((I8 || C::kBInt8) ? 1 : 2);
@@ -196,13 +200,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = Acc{0, 0, 0, 0};
-  f32x4 sacc[RSP ? HALF : 1][RSP ? RSP / 16 : 1];
+    for (int j = 0; j < FN; ++j) acc[i][j] = Acc{};
+  f32x16 sacc[RSP ? HALF : 1][RSP ? RSP / 32 : 1];
   if constexpr (RSP > 0) {
 #pragma unroll
     for (int i = 0; i < HALF; ++i)
 #pragma unroll
-      for (int j = 0; j < RSP / 16; ++j) sacc[i][j] = f32x4{0, 0, 0, 0};
+      for (int j = 0; j < RSP / 32; ++j) sacc[i][j] = f32x16{};
   }
 
   u32x4 rb[NN ? 8 : 1];   // NN: 8 rows x 8 columns of Q staged for the transpose
@@ -266,38 +270,44 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
     }
   };
 
-  auto compute_ks = [&](const uint8_t* sbuf, auto ks_const) {
-    constexpr int ks = decltype(ks_const)::value;
+  // One MFMA step = 16 bf16 (or 32 int8) of the reduction = two 16-byte chunks;
+  // a k-tile holds four steps.  Fragments are double-buffered in registers:
+  // the LDS reads of step ks+1 are issued before the MFMAs of step ks, so the
+  // matrix pipe never waits on LDS inside a k-tile.
+  auto load_frags = [&](const uint8_t* sbuf, int ks, u32x4* af, u32x4* bf, u32x4* sf) {
     const uint8_t* sA = sbuf;
     const uint8_t* sB = sbuf + BM * 128;
-    {
-      u32x4 af[FM], bf[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = lds_ld16(sA, lds_off(wm * TM + i * 16 + lr, ks * 4 + lq));
+    for (int i = 0; i < FM; ++i) af[i] = lds_ld16(sA, lds_off(wm * TM + i * 32 + lr, ks * 2 + lq));
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bf[j] = lds_ld16(sB, lds_off(wn * TN + j * 16 + lr, ks * 4 + lq));
+    for (int j = 0; j < FN; ++j) bf[j] = lds_ld16(sB, lds_off(wn * TN + j * 32 + lr, ks * 2 + lq));
+    if constexpr (RSP > 0) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int js = 0; js < RSP / 32; ++js) sf[js] = lds_ld16(sB, lds_off(BN + js * 32 + lr, ks * 2 + lq));
+    }
+  };
+  auto mfmas = [&](const u32x4* af, const u32x4* bf, const u32x4* sf) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          if constexpr (I8) acc[i][j] = mfma_i8(bf[j], af[i], acc[i][j]);
-          else acc[i][j] = mfma_bf16(bf[j], af[i], acc[i][j]);
-        }
-      if constexpr (RSP > 0) {
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int js = 0; js < RSP / 16; ++js) {
-          const u32x4 sf = lds_ld16(sB, lds_off(BN + js * 16 + lr, ks * 4 + lq));
-          if (wn == 0) {
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (I8) acc[i][j] = mfma32_i8(bf[j], af[i], acc[i][j]);
+        else acc[i][j] = mfma32_bf16(bf[j], af[i], acc[i][j]);
+      }
+    if constexpr (RSP > 0) {
 #pragma unroll
-            for (int i = 0; i < HALF; ++i) sacc[i][js] = mfma_bf16(sf, af[i], sacc[i][js]);
-          } else {
+      for (int js = 0; js < RSP / 32; ++js) {
+        if (wn == 0) {
 #pragma unroll
-            for (int i = 0; i < HALF; ++i) sacc[i][js] = mfma_bf16(sf, af[HALF + i], sacc[i][js]);
-          }
+          for (int i = 0; i < HALF; ++i) sacc[i][js] = mfma32_bf16(sf[js], af[i], sacc[i][js]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < HALF; ++i) sacc[i][js] = mfma32_bf16(sf[js], af[HALF + i], sacc[i][js]);
         }
       }
     }
   };
+  constexpr int SF = RSP ? RSP / 32 : 1;
 
   // ---------------------------------------------------------------- main loop
   // Stage kt lives in smem[kt & 1].  Per k-tile: wait for the stage's copies,
@@ -314,36 +324,54 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
     uint8_t* cur = (kt & 1) ? smem1 : smem0;
     uint8_t* nxt = (kt & 1) ? smem0 : smem1;
     if (kt + 1 < KT) issue_loads(kt + 1, nxt);
-    compute_ks(cur, std::integral_constant<int, 0>{});
+    u32x4 fa0[FM], fb0[FN], fs0[SF], fa1[FM], fb1[FN], fs1[SF];
+    load_frags(cur, 0, fa0, fb0, fs0);
+    load_frags(cur, 1, fa1, fb1, fs1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(fa0, fb0, fs0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(cur, 2, fa0, fb0, fs0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(fa1, fb1, fs1);
+    __builtin_amdgcn_sched_barrier(0);
     if (kt + 1 < KT) store_q(kt + 1, nxt);
-    compute_ks(cur, std::integral_constant<int, 1>{});
+    load_frags(cur, 3, fa1, fb1, fs1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(fa0, fb0, fs0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(fa1, fb1, fs1);
   }
   __syncthreads();
 
   // ---------------------------------------------------------------- epilogue
-  const int mrow_base = m0 + wm * TM;        // + i*16 + lr
-  const int ncol_base = n0 + wn * TN;        // + j*16 + 4*lq + e
+  // acc[i][j] lane l, element v: output row m = mrow_base + 32 i + (l & 31),
+  // output columns n = ncol_base + 32 j + 8 (v >> 2) + 4 (l >> 5) + (v & 3).
+  const int mrow_base = m0 + wm * TM;
+  const int ncol_base = n0 + wn * TN + 4 * lq;
 
   // Fused side: publish s_epi * U (bf16) to LDS for the rank-r product, save U (fp32).
   if constexpr (RSP > 0) {
     uint16_t* sS = reinterpret_cast<uint16_t*>(smem0);
 #pragma unroll
     for (int i = 0; i < HALF; ++i) {
-      const int row = wm * TM + (wn * HALF + i) * 16 + lr;
+      const int row = wm * TM + (wn * HALF + i) * 32 + lr;
+      const int m = m0 + row;
 #pragma unroll
-      for (int js = 0; js < RSP / 16; ++js) {
-        const int j0 = js * 16 + 4 * lq;
-        const f32x4 u = sacc[i][js];
-        u32x2 w;
-        w[0] = pack_bf16x2(u[0] * p.s_epi, u[1] * p.s_epi);
-        w[1] = pack_bf16x2(u[2] * p.s_epi, u[3] * p.s_epi);
-        *reinterpret_cast<u32x2*>(sS + row * RSP + j0) = w;
-        const int m = m0 + row;
-        if (p.side_save != nullptr && tn == 0 && m < M) {
-          float* dst = p.side_save + (size_t)m * p.ld_side_save;
+      for (int js = 0; js < RSP / 32; ++js) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (j0 + e < p.r_side) dst[j0 + e] = u[e];
+        for (int g = 0; g < 4; ++g) {
+          const int j0 = js * 32 + 8 * g + 4 * lq;
+          const f32x16 u = sacc[i][js];
+          u32x2 w;
+          w[0] = pack_bf16x2(u[4 * g] * p.s_epi, u[4 * g + 1] * p.s_epi);
+          w[1] = pack_bf16x2(u[4 * g + 2] * p.s_epi, u[4 * g + 3] * p.s_epi);
+          *reinterpret_cast<u32x2*>(sS + row * RSP + j0) = w;
+          if (p.side_save != nullptr && tn == 0 && m < M) {
+            float* dst = p.side_save + (size_t)m * p.ld_side_save;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (j0 + e < p.r_side) dst[j0 + e] = u[4 * g + e];
+          }
         }
       }
     }
@@ -352,33 +380,40 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
 
   // The epilogue walks the accumulator tile in column chunks so that the
   // fp32 copy of an int32 tile never doubles the live registers.
-  constexpr int JC = I8 ? FN / 2 : FN;
+  constexpr int JC = I8 ? 1 : FN;
   static_assert(FN % JC == 0, "column chunking");
   auto epilogue_chunk = [&](auto jc_const) {
     constexpr int jc = decltype(jc_const)::value;
     if constexpr (C::kEpi == EPI_RAW_I32) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int m = mrow_base + i * 16 + lr;
+        const int m = mrow_base + i * 32 + lr;
         if (m >= M) continue;
 #pragma unroll
-        for (int jj = 0; jj < JC; ++jj) {
-          const int n = ncol_base + (jc + jj) * 16 + 4 * lq;
-          *reinterpret_cast<i32x4*>(static_cast<int32_t*>(p.out) + (size_t)m * p.ldo + n) = acc[i][jc + jj];
-        }
+        for (int jj = 0; jj < JC; ++jj)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = ncol_base + (jc + jj) * 32 + 8 * g;
+            const Acc& a = acc[i][jc + jj];
+            *reinterpret_cast<i32x4*>(static_cast<int32_t*>(p.out) + (size_t)m * p.ldo + n) =
+                i32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+          }
       }
     } else {
-      f32x4 facc[FM][JC];
+      f32x16 facc[FM][JC];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int jj = 0; jj < JC; ++jj) {
           if constexpr (I8) {
-            const int m = mrow_base + i * 16 + lr;
+            const int m = mrow_base + i * 32 + lr;
             const float sxm = (m < M) ? p.row_scale[m] : 0.f;
-            const f32x4 swn = *reinterpret_cast<const f32x4*>(p.col_scale + ncol_base + (jc + jj) * 16 + 4 * lq);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) facc[i][jj][e] = float(acc[i][jc + jj][e]) * sxm * swn[e];
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 swn = *reinterpret_cast<const f32x4*>(p.col_scale + ncol_base + (jc + jj) * 32 + 8 * g);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) facc[i][jj][4 * g + e] = float(acc[i][jc + jj][4 * g + e]) * sxm * swn[e];
+            }
           } else {
             facc[i][jj] = acc[i][jc + jj];
           }
@@ -386,13 +421,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
 
       if (p.r_epi > 0) {
         const uint16_t* sS = reinterpret_cast<const uint16_t*>(smem0);
-        const int nsteps = (p.r_epi + 31) / 32;
+        const int nsteps = (p.r_epi + 15) / 16;
         for (int t = 0; t < nsteps; ++t) {
-          const int j0 = t * 32 + lq * 8;
+          const int j0 = t * 16 + lq * 8;
           u32x4 sf[FM];
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
-            const int row = wm * TM + i * 16 + lr;
+            const int row = wm * TM + i * 32 + lr;
             sf[i] = u32x4{0, 0, 0, 0};
             if constexpr (RSP > 0) {
               if (j0 < RSP) sf[i] = *reinterpret_cast<const u32x4*>(sS + row * RSP + j0);
@@ -411,70 +446,74 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
           }
 #pragma unroll
           for (int jj = 0; jj < JC; ++jj) {
-            const u32x4 ef = e_frag(p, ncol_base + (jc + jj) * 16 + lr, j0);
+            const u32x4 ef = e_frag(p, n0 + wn * TN + (jc + jj) * 32 + lr, j0);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) facc[i][jj] = mfma_bf16(ef, sf[i], facc[i][jj]);
+            for (int i = 0; i < FM; ++i) facc[i][jj] = mfma32_bf16(ef, sf[i], facc[i][jj]);
           }
         }
       }
 
-      // stores: lane holds row m, columns n..n+3
+      // stores: lane holds row m and four groups of four consecutive columns
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int m = mrow_base + i * 16 + lr;
+        const int m = mrow_base + i * 32 + lr;
         if (m >= M) continue;
 #pragma unroll
         for (int jj = 0; jj < JC; ++jj) {
-          const int n = ncol_base + (jc + jj) * 16 + 4 * lq;
-          const f32x4 v = facc[i][jj];
-          float bias4[4] = {0.f, 0.f, 0.f, 0.f};
-          if (p.bias != nullptr) {
-            const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n);
-            bias4[0] = bf16_lo(bb[0]); bias4[1] = bf16_hi(bb[0]);
-            bias4[2] = bf16_lo(bb[1]); bias4[3] = bf16_hi(bb[1]);
-          }
-          if constexpr (C::kEpi == EPI_PLAIN || C::kEpi == EPI_DEQUANT) {
-            u32x2 w;
-            w[0] = pack_bf16x2(v[0] + bias4[0], v[1] + bias4[1]);
-            w[1] = pack_bf16x2(v[2] + bias4[2], v[3] + bias4[3]);
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (size_t)m * p.ldo + n) = w;
-          } else if constexpr (C::kEpi == EPI_DORA) {
-            const f32x4 g = *reinterpret_cast<const f32x4*>(p.col_scale + n);
-            u32x2 w, z;
-            z[0] = pack_bf16x2(v[0], v[1]);
-            z[1] = pack_bf16x2(v[2], v[3]);
-            w[0] = pack_bf16x2(v[0] * g[0] + bias4[0], v[1] * g[1] + bias4[1]);
-            w[1] = pack_bf16x2(v[2] * g[2] + bias4[2], v[3] * g[3] + bias4[3]);
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (size_t)m * p.ldo + n) = w;
-            if (p.out2 != nullptr)
-              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out2) + (size_t)m * p.ldo2 + n) = z;
-          } else if constexpr (C::kEpi == EPI_SWIGLU_FWD) {
-            const u32x2 ee = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux0) + (size_t)m * p.ld_aux0 + n);
-            const float e4[4] = {bf16_lo(ee[0]), bf16_hi(ee[0]), bf16_lo(ee[1]), bf16_hi(ee[1])};
-            u32x2 gu, h;
-            gu[0] = pack_bf16x2(v[0], v[1]);
-            gu[1] = pack_bf16x2(v[2], v[3]);
-            h[0] = pack_bf16x2(silu_f(e4[0]) * v[0], silu_f(e4[1]) * v[1]);
-            h[1] = pack_bf16x2(silu_f(e4[2]) * v[2], silu_f(e4[3]) * v[3]);
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out2) + (size_t)m * p.ldo2 + n) = gu;
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out3) + (size_t)m * p.ldo3 + n) = h;
-          } else if constexpr (C::kEpi == EPI_SWIGLU_BWD) {
-            const u32x2 ee = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux0) + (size_t)m * p.ld_aux0 + n);
-            const u32x2 gg = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux1) + (size_t)m * p.ld_aux1 + n);
-            const float e4[4] = {bf16_lo(ee[0]), bf16_hi(ee[0]), bf16_lo(ee[1]), bf16_hi(ee[1])};
-            const float g4[4] = {bf16_lo(gg[0]), bf16_hi(gg[0]), bf16_lo(gg[1]), bf16_hi(gg[1])};
-            float de[4], dgu[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float sg = sigmoid_f(e4[e]);
-              de[e] = v[e] * g4[e] * sg * (1.f + e4[e] * (1.f - sg));
-              dgu[e] = v[e] * e4[e] * sg;
+          for (int g = 0; g < 4; ++g) {
+            const int n = ncol_base + (jc + jj) * 32 + 8 * g;
+            const f32x16& va = facc[i][jj];
+            const float v[4] = {va[4 * g], va[4 * g + 1], va[4 * g + 2], va[4 * g + 3]};
+            float bias4[4] = {0.f, 0.f, 0.f, 0.f};
+            if (p.bias != nullptr) {
+              const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n);
+              bias4[0] = bf16_lo(bb[0]); bias4[1] = bf16_hi(bb[0]);
+              bias4[2] = bf16_lo(bb[1]); bias4[3] = bf16_hi(bb[1]);
             }
-            u32x2 w0, w1;
-            w0[0] = pack_bf16x2(de[0], de[1]); w0[1] = pack_bf16x2(de[2], de[3]);
-            w1[0] = pack_bf16x2(dgu[0], dgu[1]); w1[1] = pack_bf16x2(dgu[2], dgu[3]);
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (size_t)m * p.ldo + n) = w0;
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out2) + (size_t)m * p.ldo2 + n) = w1;
+            if constexpr (C::kEpi == EPI_PLAIN || C::kEpi == EPI_DEQUANT) {
+              u32x2 w;
+              w[0] = pack_bf16x2(v[0] + bias4[0], v[1] + bias4[1]);
+              w[1] = pack_bf16x2(v[2] + bias4[2], v[3] + bias4[3]);
+              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (size_t)m * p.ldo + n) = w;
+            } else if constexpr (C::kEpi == EPI_DORA) {
+              const f32x4 gs = *reinterpret_cast<const f32x4*>(p.col_scale + n);
+              u32x2 w, z;
+              z[0] = pack_bf16x2(v[0], v[1]);
+              z[1] = pack_bf16x2(v[2], v[3]);
+              w[0] = pack_bf16x2(v[0] * gs[0] + bias4[0], v[1] * gs[1] + bias4[1]);
+              w[1] = pack_bf16x2(v[2] * gs[2] + bias4[2], v[3] * gs[3] + bias4[3]);
+              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (size_t)m * p.ldo + n) = w;
+              if (p.out2 != nullptr)
+                *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out2) + (size_t)m * p.ldo2 + n) = z;
+            } else if constexpr (C::kEpi == EPI_SWIGLU_FWD) {
+              const u32x2 ee = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux0) + (size_t)m * p.ld_aux0 + n);
+              const float e4[4] = {bf16_lo(ee[0]), bf16_hi(ee[0]), bf16_lo(ee[1]), bf16_hi(ee[1])};
+              u32x2 gu, h;
+              gu[0] = pack_bf16x2(v[0], v[1]);
+              gu[1] = pack_bf16x2(v[2], v[3]);
+              h[0] = pack_bf16x2(silu_f(e4[0]) * v[0], silu_f(e4[1]) * v[1]);
+              h[1] = pack_bf16x2(silu_f(e4[2]) * v[2], silu_f(e4[3]) * v[3]);
+              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out2) + (size_t)m * p.ldo2 + n) = gu;
+              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out3) + (size_t)m * p.ldo3 + n) = h;
+            } else if constexpr (C::kEpi == EPI_SWIGLU_BWD) {
+              const u32x2 ee = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux0) + (size_t)m * p.ld_aux0 + n);
+              const u32x2 gg = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux1) + (size_t)m * p.ld_aux1 + n);
+              const float e4[4] = {bf16_lo(ee[0]), bf16_hi(ee[0]), bf16_lo(ee[1]), bf16_hi(ee[1])};
+              const float g4[4] = {bf16_lo(gg[0]), bf16_hi(gg[0]), bf16_lo(gg[1]), bf16_hi(gg[1])};
+              float de[4], dgu[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float sg = sigmoid_f(e4[e]);
+                de[e] = v[e] * g4[e] * sg * (1.f + e4[e] * (1.f - sg));
+                dgu[e] = v[e] * e4[e] * sg;
+              }
+              u32x2 w0, w1;
+              w0[0] = pack_bf16x2(de[0], de[1]); w0[1] = pack_bf16x2(de[2], de[3]);
+              w1[0] = pack_bf16x2(dgu[0], dgu[1]); w1[1] = pack_bf16x2(dgu[2], dgu[3]);
+              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (size_t)m * p.ldo + n) = w0;
+              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out2) + (size_t)m * p.ldo2 + n) = w1;
+            }
           }
         }
       }
@@ -482,6 +521,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
   };
   epilogue_chunk(std::integral_constant<int, 0>{});
   if constexpr (JC < FN) epilogue_chunk(std::integral_constant<int, JC>{});
+  if constexpr (2 * JC < FN) epilogue_chunk(std::integral_constant<int, 2 * JC>{});
+  if constexpr (3 * JC < FN) epilogue_chunk(std::integral_constant<int, 3 * JC>{});
+  static_assert(FN <= 4 * JC, "at most four column chunks");
 }
 
 }  // namespace ldl

@@ -18,10 +18,15 @@
 namespace ldl {
 
 // ============================================================================ rowproj
+// 16 output rows per 512-thread block; the eight waves split the reduction
+// (wave w takes the 32-element steps w, w+8, ...), each keeping up to eight
+// 1 KiB row fragments of P in flight, then reduce through LDS.
+constexpr int RP_WAVES = 8;
+
 template <int RP>
-__global__ __launch_bounds__(256) void rowproj_kernel(const RowProjParams p) {
+__global__ __launch_bounds__(512) void rowproj_kernel(const RowProjParams p) {
   constexpr int NB = RP / 16;
-  __shared__ f32x4 red[4][NB][64];
+  __shared__ f32x4 red[RP_WAVES][NB][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
   const int m0 = blockIdx.x * 16;
@@ -45,21 +50,22 @@ __global__ __launch_bounds__(256) void rowproj_kernel(const RowProjParams p) {
 
   const int nsteps = p.K / 32;
   const u32x4 zero = {0, 0, 0, 0};
+  constexpr int U = 8;
   int ks = wave;
-  for (; ks + 12 < nsteps; ks += 16) {
-    u32x4 pf[4];
+  for (; ks + (U - 1) * RP_WAVES < nsteps; ks += U * RP_WAVES) {
+    u32x4 pf[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) pf[u] = mval ? ld16(prow + (ks + 4 * u) * 32) : zero;
+    for (int u = 0; u < U; ++u) pf[u] = mval ? ld16(prow + (ks + u * RP_WAVES) * 32) : zero;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int jb = 0; jb < NB; ++jb) {
-        const u32x4 qf = qval[jb] ? ld16(qrow[jb] + (ks + 4 * u) * 32) : zero;
+        const u32x4 qf = qval[jb] ? ld16(qrow[jb] + (ks + u * RP_WAVES) * 32) : zero;
         acc[jb] = mfma_bf16(qf, pf[u], acc[jb]);
       }
     }
   }
-  for (; ks < nsteps; ks += 4) {
+  for (; ks < nsteps; ks += RP_WAVES) {
     const u32x4 pf = mval ? ld16(prow + ks * 32) : zero;
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb) {
@@ -71,10 +77,12 @@ __global__ __launch_bounds__(256) void rowproj_kernel(const RowProjParams p) {
 #pragma unroll
   for (int jb = 0; jb < NB; ++jb) red[wave][jb][lane] = acc[jb];
   __syncthreads();
-  if (wave == 0 && mval) {
+  // lane holds out[m][jb*16 + 4*lq + i]; waves 0..NB-1 finish one jb each
+  for (int jb = wave; jb < NB; jb += RP_WAVES) {
+    f32x4 v = red[0][jb][lane];
 #pragma unroll
-    for (int jb = 0; jb < NB; ++jb) {
-      const f32x4 v = red[0][jb][lane] + red[1][jb][lane] + red[2][jb][lane] + red[3][jb][lane];
+    for (int w = 1; w < RP_WAVES; ++w) v += red[w][jb][lane];
+    if (mval) {
       const int j0 = jb * 16 + 4 * lq;
       float* dst = p.out + (size_t)m * p.ldo;
 #pragma unroll
@@ -85,14 +93,29 @@ __global__ __launch_bounds__(256) void rowproj_kernel(const RowProjParams p) {
 }
 
 // ============================================================================ colproj
-// LDS tile of X^T: 64 columns x 256 rows of m (512 bytes per column row,
-// 16-byte chunk index XOR-swizzled with swz(c)).
-__device__ __forceinline__ int xt_off(int c, int chunk) { return c * 512 + ((chunk ^ swz(c)) << 4); }
+// Block = 64 columns of X and one split of rows, walked in sub-tiles of MS rows.
+// Per sub-tile: X^T (64 x MS bf16) and S^T as bf16 hi/lo parts (R x MS each) are
+// staged in LDS; each of the four waves owns 16 columns.
+__device__ __forceinline__ int xt_off(int c, int chunk, int rowbytes) {
+  return c * rowbytes + ((chunk ^ swz(c)) << 4);
+}
+
+template <int RP>
+struct ColProjTile {
+  static constexpr int MS = RP <= 64 ? 256 : 128;        // rows per sub-tile
+  static constexpr int XBYTES = 64 * MS * 2;
+  static constexpr int SBYTES = RP * MS * 2;             // one of hi / lo
+};
 
 template <int RP>
 __global__ __launch_bounds__(256) void colproj_kernel(const ColProjParams p) {
+  using T = ColProjTile<RP>;
   constexpr int NB = RP / 16;
-  __shared__ __attribute__((aligned(16))) uint8_t xt[64 * 512];
+  constexpr int MS = T::MS;
+  constexpr int ROWB = MS * 2;          // bytes per transposed row
+  __shared__ __attribute__((aligned(16))) uint8_t xt[T::XBYTES];
+  __shared__ __attribute__((aligned(16))) uint16_t shi[RP * MS];
+  __shared__ __attribute__((aligned(16))) uint16_t slo[RP * MS];
   __shared__ float csred[32][64 + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
@@ -101,10 +124,11 @@ __global__ __launch_bounds__(256) void colproj_kernel(const ColProjParams p) {
   const int mbeg = split * p.msplit;
   const int mend = min(p.M, mbeg + p.msplit);
 
-  // loader role: 8 consecutive columns x 8 consecutive rows
-  const int cb = tid & 7, mb = tid >> 3;
+  // X loader role: 8 consecutive columns x 8 consecutive rows; the MS/8 row
+  // groups x 8 column groups of a sub-tile are spread over the 256 threads
+  const int cb = tid & 7, mb = tid >> 3;       // mb in [0, 32)
   const int cl = c0 + cb * 8;
-  const bool cval = cl < p.C;   // C is a multiple of 8
+  const bool cval = cl < p.C;                   // C is a multiple of 8
 
   f32x4 acc[NB];
 #pragma unroll
@@ -113,60 +137,65 @@ __global__ __launch_bounds__(256) void colproj_kernel(const ColProjParams p) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) cs[e] = 0.f;
 
-  for (int sub = mbeg; sub < mend; sub += 256) {
-    // ---- stage X[sub .. sub+255, c0 .. c0+63] transposed into LDS
-    u32x4 rows[8];
+  for (int sub = mbeg; sub < mend; sub += MS) {
+    __syncthreads();   // previous sub-tile fully consumed
+    // ---- X[sub .. sub+MS, c0 .. c0+63] -> LDS, transposed (8x8 register transposes)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int m = sub + mb * 8 + e;
-      rows[e] = u32x4{0, 0, 0, 0};
-      if (cval && m < mend) {
-        rows[e] = ld16(p.X + (size_t)m * p.ldx + cl);
-        if (p.colsum_mode == 1) {
-          const u32x4 z = ld16(p.Z + (size_t)m * p.ldz + cl);
+    for (int h = 0; h < (MS + 255) / 256; ++h) {
+      const int mg = mb + 32 * h;             // row group of 8
+      if (mg >= MS / 8) break;
+      u32x4 rows[8];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            cs[2 * t] += bf16_lo(rows[e][t]) * bf16_lo(z[t]);
-            cs[2 * t + 1] += bf16_hi(rows[e][t]) * bf16_hi(z[t]);
-          }
-        } else if (p.colsum_mode == 2) {
+      for (int e = 0; e < 8; ++e) {
+        const int m = sub + mg * 8 + e;
+        rows[e] = u32x4{0, 0, 0, 0};
+        if (cval && m < mend) {
+          rows[e] = ld16(p.X + (size_t)m * p.ldx + cl);
+          if (p.colsum_mode == 1) {
+            const u32x4 z = ld16(p.Z + (size_t)m * p.ldz + cl);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            cs[2 * t] += bf16_lo(rows[e][t]);
-            cs[2 * t + 1] += bf16_hi(rows[e][t]);
+            for (int t = 0; t < 4; ++t) {
+              cs[2 * t] += bf16_lo(rows[e][t]) * bf16_lo(z[t]);
+              cs[2 * t + 1] += bf16_hi(rows[e][t]) * bf16_hi(z[t]);
+            }
+          } else if (p.colsum_mode == 2) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              cs[2 * t] += bf16_lo(rows[e][t]);
+              cs[2 * t + 1] += bf16_hi(rows[e][t]);
+            }
           }
         }
       }
-    }
-    u32x4 cols[8];
-    transpose8x8_b16(rows, cols);
-    __syncthreads();   // previous sub-tile fully consumed
+      u32x4 cols[8];
+      transpose8x8_b16(rows, cols);
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) *reinterpret_cast<u32x4*>(xt + xt_off(cb * 8 + cc, mb)) = cols[cc];
+      for (int cc = 0; cc < 8; ++cc) *reinterpret_cast<u32x4*>(xt + xt_off(cb * 8 + cc, mg, ROWB)) = cols[cc];
+    }
+    // ---- S[sub .. sub+MS, 0 .. R) -> LDS as bf16 hi / lo, transposed [j][m]
+    for (int idx = tid; idx < MS * RP; idx += 256) {
+      const int j = idx / MS, mm = idx % MS;   // consecutive threads: consecutive rows m
+      const int m = sub + mm;
+      float v = 0.f;
+      if (j < p.R && m < mend) v = p.S[(size_t)m * p.lds + j] * p.s_in;
+      const uint32_t h = f32_to_bf16_bits(v);
+      const int off = (xt_off(j, mm >> 3, ROWB) >> 1) + (mm & 7);   // same swizzle as the X tile
+      shi[off] = (uint16_t)h;
+      slo[off] = (uint16_t)f32_to_bf16_bits(v - __uint_as_float(h << 16));
+    }
     __syncthreads();
 
-    // ---- 8 reduction steps of 32 rows each
+    // ---- MS/32 reduction steps of 32 rows
     const int c_frag = wave * 16 + lr;
 #pragma unroll 2
-    for (int s = 0; s < 8; ++s) {
-      const int mrow0 = sub + s * 32 + lq * 8;   // rows past mend were staged as zeros
-      const u32x4 xf = *reinterpret_cast<const u32x4*>(xt + xt_off(c_frag, s * 4 + lq));
+    for (int s = 0; s < MS / 32; ++s) {
+      const u32x4 xf = *reinterpret_cast<const u32x4*>(xt + xt_off(c_frag, s * 4 + lq, ROWB));
 #pragma unroll
       for (int jb = 0; jb < NB; ++jb) {
         const int j = jb * 16 + lr;
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int m = mrow0 + e;
-          v[e] = (j < p.R && m < mend) ? p.S[(size_t)m * p.lds + j] * p.s_in : 0.f;
-        }
-        u32x4 hi, lo;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint32_t h0 = f32_to_bf16_bits(v[2 * t]), h1 = f32_to_bf16_bits(v[2 * t + 1]);
-          hi[t] = h0 | (h1 << 16);
-          lo[t] = pack_bf16x2(v[2 * t] - __uint_as_float(h0 << 16), v[2 * t + 1] - __uint_as_float(h1 << 16));
-        }
+        const int so = xt_off(j, s * 4 + lq, ROWB);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(shi) + so);
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(slo) + so);
         acc[jb] = mfma_bf16(hi, xf, acc[jb]);
         acc[jb] = mfma_bf16(lo, xf, acc[jb]);
       }
@@ -181,7 +210,7 @@ __global__ __launch_bounds__(256) void colproj_kernel(const ColProjParams p) {
     for (int jb = 0; jb < NB; ++jb) *reinterpret_cast<f32x4*>(dst + jb * 16 + 4 * lq) = acc[jb];
   }
 
-  // ---- column sums: reduce the 32 row-groups of each column
+  // ---- column sums: reduce the row groups of each column
   if (p.colsum_mode != 0) {
     __syncthreads();
 #pragma unroll
@@ -196,14 +225,20 @@ __global__ __launch_bounds__(256) void colproj_kernel(const ColProjParams p) {
 }
 
 // ============================================================================ reductions
-// out[row, col] = alpha * sum_s part[s][...] (+ row scale) (+ alpha2 * sum_l Qm[row, l] * Am[l, col])
+// out[row, col] = alpha * sum_s part[s][...] (+ row scale) (+ alpha2 * sum_l Qm[row, l] * Am[l, col]).
+// Threads walk the partial buffer in its own order ([C][rp], j fastest) so the
+// split reads are coalesced; `trans` selects whether the partial's column index
+// (j) is the output row (dA = part^T) or the output column (dB).
 __global__ void reduce_parts_kernel(const ReduceParams p) {
-  const size_t total = (size_t)p.rows * p.cols;
+  const int C = p.trans ? p.cols : p.rows;          // partial rows
+  const int R = p.trans ? p.rows : p.cols;          // valid partial columns
+  const size_t total = (size_t)C * p.rp;
   for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += (size_t)gridDim.x * blockDim.x) {
-    const int row = (int)(idx / p.cols), col = (int)(idx % p.cols);
-    const size_t off = p.trans ? ((size_t)col * p.rp + row) : ((size_t)row * p.rp + col);
+    const int c = (int)(idx / p.rp), j = (int)(idx % p.rp);
+    if (j >= R) continue;
     float acc = 0.f;
-    for (int s = 0; s < p.nsplit; ++s) acc += p.part[(size_t)s * p.pstride + off];
+    for (int s = 0; s < p.nsplit; ++s) acc += p.part[(size_t)s * p.pstride + idx];
+    const int row = p.trans ? j : c, col = p.trans ? c : j;
     float v = acc * p.alpha;
     if (p.rowscale != nullptr) v *= p.rowscale[row];
     if (p.Qm != nullptr) {
@@ -241,7 +276,7 @@ __global__ void fill_zero_kernel(float* p, size_t n) {
 // ============================================================================ launchers
 hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st) {
   if (p.M <= 0) return hipSuccess;
-  const dim3 grid((p.M + 15) / 16), block(256);
+  const dim3 grid((p.M + 15) / 16), block(64 * RP_WAVES);
   const int rp = p.R <= 16 ? 16 : p.R <= 32 ? 32 : p.R <= 64 ? 64 : 128;
   switch (rp) {
     case 16: hipLaunchKernelGGL(rowproj_kernel<16>, grid, block, 0, st, p); break;
@@ -260,10 +295,13 @@ void colproj_plan(int M, int C, int* nsplit, int* msplit) {
     *msplit = 256;
     return;
   }
+  // splits are whole multiples of 256 rows (a multiple of every sub-tile height);
+  // aim for ~1024 blocks, at most 32 splits
   const int ctiles = (C + 63) / 64;
   const int mchunks = (M + 255) / 256;
   int want = (1024 + ctiles - 1) / ctiles;
   if (want < 1) want = 1;
+  if (want > 32) want = 32;
   int ns = mchunks < want ? mchunks : want;
   if (ns < 1) ns = 1;
   const int per = (mchunks + ns - 1) / ns;      // 256-row chunks per split
@@ -284,7 +322,7 @@ hipError_t launch_colproj(const ColProjParams& p, int nsplit, hipStream_t st) {
 }
 
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t st) {
-  const size_t total = (size_t)p.rows * p.cols;
+  const size_t total = (size_t)(p.trans ? p.cols : p.rows) * p.rp;
   if (total == 0) return hipSuccess;
   size_t blocks = (total + 255) / 256;
   if (blocks > 4096) blocks = 4096;
