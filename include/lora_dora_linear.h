@@ -171,13 +171,13 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype,
  * LoRA MLP with SwiGLU: e = lora(X; gate), u = lora(X; up), h = silu(e) * u,
  * out = lora(h; down) ("How Unsloth's FastLoRA Kernel ...", sections "Fused Forward
  * Pass Architecture" and "Activation Function Fusion").  bf16 only.  The activation
- * is fused into the epilogue of the up projection (forward) and of the down
- * projection's input-gradient GEMM (backward).
+ * is fused into the epilogue of one GEMM that computes the gate and the up
+ * projection of the same hidden units side by side (forward), and into the
+ * epilogue of the down projection's input-gradient GEMM (backward).
  *   X [M,K]; Wg, Wu [H,K]; Ag, Au [r,K]; Bg, Bu [H,r]; Wd [K,H]; Ad [r,H]; Bd [K,r].
  *   Out [M,K].  Saved for the backward: E_save, Gu_save, H_save [M,H] (bf16) and
  *   U_save [M,3r] fp32 = [X.Ag^T | X.Au^T | H.Ad^T].  All required.
- *   Limits: K and H multiples of 64 (and 128 for the down projection's K = H side),
- *   r <= 64.
+ *   Limits: K and H multiples of 64, r a multiple of 8 and at most 64.
  */
 int swiglu_lora_mlp_fwd(int M, int K, int H, int r, float s_gate, float s_up, float s_down,
                         const void* X, const void* Wg, const void* Ag, const void* Bg,

@@ -511,7 +511,7 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, c
 // =========================================================================== SwiGLU MLP
 static int mlp_check(int M, int K, int H, int r) {
   if (M < 0 || K <= 0 || H <= 0 || r <= 0) return LDL_E_INVAL;
-  if (r > 64 || K % 64 || H % 64) return LDL_E_UNSUPPORTED;
+  if (r > 64 || r % 8 || K % 64 || H % 64) return LDL_E_UNSUPPORTED;
   if (!small(M + 256, 2 * (size_t)H, 2) || !small(H, K, 2) || !small(M + 256, K, 2)) return LDL_E_UNSUPPORTED;
   return LDL_OK;
 }
@@ -531,16 +531,15 @@ int swiglu_lora_mlp_fwd(int M, int K, int H, int r, float s_gate, float s_up, fl
   const int r3 = 3 * r;
   // [U_g | U_u] = X.[Ag; Au]^T in one pass over X
   LDL_TRY(rowproj(M, K, 2 * r, X, K, Ag, Au, r, K, U_save, r3, 1.f, st));
+  // gate and up projections in one GEMM (each tile holds e and u of the same hidden
+  // units) with h = silu(e) * u in the epilogue
   GemmParams p = gp0();
   p.M = M; p.N = H; p.K = K;
-  p.a = X; p.lda = K; p.b0 = Wg; p.ldb = K; p.kseg = K;
-  p.S = U_save; p.ld_s = r3; p.r_epi = r; p.s_epi = s_gate;
-  p.e0 = Bg; p.e1 = Bg; p.e_ldn = r; p.e_ldj = 1; p.e_jsplit = r;
-  p.out = E_save; p.ldo = H;
-  LDL_TRY(launch_gemm(GK_NT_PLAIN, p, st));
-  p.b0 = Wu; p.S = U_save + r; p.s_epi = s_up; p.e0 = Bu; p.e1 = Bu;
-  p.out = nullptr; p.aux0 = E_save; p.ld_aux0 = H; p.out2 = Gu_save; p.ldo2 = H; p.out3 = H_save; p.ldo3 = H;
-  LDL_TRY(launch_gemm(GK_NT_SWIGLU, p, st));
+  p.a = X; p.lda = K; p.b0 = Wg; p.b1 = Wu; p.ldb = K; p.kseg = K;
+  p.S = U_save; p.ld_s = r3; p.r_epi = 2 * r; p.s_epi = s_gate; p.s_epi2 = s_up;
+  p.e0 = Bg; p.e1 = Bu; p.e_ldn = r; p.e_ldj = 1; p.e_jsplit = r;
+  p.out = E_save; p.ldo = H; p.out2 = Gu_save; p.ldo2 = H; p.out3 = H_save; p.ldo3 = H;
+  LDL_TRY(launch_gemm(GK_NT_SWIGLU_DUAL, p, st));
   // U_d = H.Ad^T, then the down projection
   LDL_TRY(rowproj(M, H, r, H_save, H, Ad, nullptr, r, H, U_save + 2 * r, r3, 1.f, st));
   GemmParams q = gp0();

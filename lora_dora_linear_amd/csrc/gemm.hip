@@ -15,7 +15,8 @@ namespace ldl {
 template <int BM, int BN, bool I8, bool NN, bool BINT8, bool ASCALE, int RSP, bool SLOAD, int EPI>
 static hipError_t run(const GemmParams& p, hipStream_t st) {
   using C = GemmCfg<BM, BN, I8, NN, BINT8, ASCALE, RSP, SLOAD, EPI>;
-  const int tiles = ((p.M + BM - 1) / BM) * (p.N / BN);
+  const int out_bn = (EPI == EPI_SWIGLU_DUAL) ? BN / 2 : BN;
+  const int tiles = ((p.M + BM - 1) / BM) * (p.N / out_bn);
   hipLaunchKernelGGL(gemm_kernel<C>, dim3(tiles), dim3(256), 0, st, p);
   return hipGetLastError();
 }
@@ -34,6 +35,7 @@ static int pick_bn(GemmKind kind, int N) {
 
 bool gemm_shape_ok(GemmKind kind, int M, int N, int K) {
   (void)M;
+  if (kind == GK_NT_SWIGLU_DUAL) return N % 64 == 0 && K > 0 && K % 64 == 0;
   const bool i8 = (kind == GK_NT_I8_DEQ || kind == GK_NT_I8_RAW);
   if (pick_bn(kind, N) == 0) return false;
   if (kind == GK_NT_FUSED && N % 128 != 0) return false;
@@ -67,6 +69,11 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
       if (bn >= 128 && big) return run<256, 128, false, false, false, false, 0, true, EPI_SWIGLU_FWD>(p, st);
       if (bn >= 128) return run<128, 128, false, false, false, false, 0, true, EPI_SWIGLU_FWD>(p, st);
       return run<128, 64, false, false, false, false, 0, true, EPI_SWIGLU_FWD>(p, st);
+    case GK_NT_SWIGLU_DUAL:
+      // output width per tile is BN / 2 (hidden units); the tile reads BN/2 gate + BN/2 up rows
+      if (p.N % 128 == 0 && big) return run<256, 256, false, false, false, false, 0, true, EPI_SWIGLU_DUAL>(p, st);
+      if (p.N % 128 == 0) return run<128, 256, false, false, false, false, 0, true, EPI_SWIGLU_DUAL>(p, st);
+      return run<256, 128, false, false, false, false, 0, true, EPI_SWIGLU_DUAL>(p, st);
     case GK_NT_FUSED:
       // down-projection computed in the K-loop; side rows padded to 32 or 64
       if (p.r_side <= 32) return run<256, 128, false, false, false, false, 32, false, EPI_PLAIN>(p, st);

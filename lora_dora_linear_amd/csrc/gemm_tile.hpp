@@ -40,6 +40,7 @@ enum EpiKind : int {
   EPI_SWIGLU_BWD = 3, // dh = acc + lora; out = dh*gu*silu'(e), out2 = dh*silu(e)
   EPI_DEQUANT = 4,    // int8: acc * sx[m] * sw[n] + lora (+ bias)        -> bf16
   EPI_RAW_I32 = 5,    // int8: raw int32 product
+  EPI_SWIGLU_DUAL = 6,// gate and up in one tile: e, u in registers; out = e, out2 = u, out3 = silu(e)*u
 };
 
 struct GemmParams {
@@ -51,6 +52,7 @@ struct GemmParams {
   const float* S; int ld_s;          // precomputed S (fp32)
   int r_epi;                         // rank of the epilogue update (0: none)
   float s_epi;
+  float s_epi2;                      // scale of S columns >= e_jsplit (dual gate/up tile: s_up)
   const void* e0; const void* e1; int e_ldn, e_ldj, e_jsplit;
   const float* row_scale;            // [M]  (int8 sx)
   const float* col_scale;            // [N]  (int8 sw / DoRA g)
@@ -139,7 +141,12 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem1[GemmSmem<C>::kBuf];
 
   const int M = p.M, N = p.N, K = p.K;
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
+  // Dual gate/up tile: BN rows of Q = BN/2 gate rows and the BN/2 up rows of the
+  // same hidden units, arranged per wave as [gate TN/2 | up TN/2], so that the
+  // accumulator blocks j and j + FN/2 of a lane hold e and u of one (m, h).
+  constexpr bool DUAL = (C::kEpi == EPI_SWIGLU_DUAL);
+  constexpr int OUT_BN = DUAL ? BN / 2 : BN;     // output columns per tile
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = N / OUT_BN;
 
   // Tile order: consecutive workgroups go round-robin over the 8 XCDs, so
   // remap ids so that each XCD receives a contiguous range, then walk that
@@ -155,7 +162,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
   const int in_g = bid - group * GM * tiles_n;
   const int tm = first_m + in_g % gm;
   const int tn = in_g / gm;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BM, n0 = tn * OUT_BN;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -176,6 +183,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
   constexpr int S_INST = (RSP * 8 + 255) / 256;
   const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(p.a, (uint32_t)M * lda_b);
   const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(p.b0, NN ? 0u : (uint32_t)N * ldb_b);
+  const __amdgpu_buffer_rsrc_t rs_b2 = make_rsrc(DUAL ? p.b1 : p.b0, NN ? 0u : (uint32_t)N * ldb_b);
   const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(p.side, RSP ? (uint32_t)p.r_side * (uint32_t)K * 2u : 0u);
   uint32_t a_off[A_INST];
 #pragma unroll
@@ -187,7 +195,12 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
 #pragma unroll
   for (int i = 0; i < B_INST; ++i) {
     const int row = (i * 4 + wave) * 8 + lrow;
-    b_off[i] = (uint32_t)(n0 + row) * ldb_b + ((lphys ^ swz(row)) << 4);
+    int qrow = n0 + row;
+    if constexpr (DUAL) {   // tile row -> (gate | up) row of hidden unit h
+      const int within = row % TN;
+      qrow = n0 + (row / TN) * (TN / 2) + within % (TN / 2);
+    }
+    b_off[i] = (uint32_t)qrow * ldb_b + ((lphys ^ swz(row)) << 4);
   }
   uint32_t s_off[S_INST ? S_INST : 1];
 #pragma unroll
@@ -219,7 +232,11 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
     if constexpr (!NN) {
       uint8_t* sB = sbuf + BM * 128;
 #pragma unroll
-      for (int i = 0; i < B_INST; ++i) buf2lds16(rs_b, b_off[i], koff, sB + (i * 4 + wave) * 1024);
+      for (int i = 0; i < B_INST; ++i) {
+        // the up half of each wave's rows comes from the second matrix (uniform per instruction)
+        const bool up = DUAL && ((((i * 4 + wave) * 8) % TN) >= TN / 2);
+        buf2lds16(up ? rs_b2 : rs_b, b_off[i], koff, sB + (i * 4 + wave) * 1024);
+      }
 #pragma unroll
       for (int i = 0; i < S_INST; ++i)
         if ((i * 4 + wave) * 8 < RSP) buf2lds16(rs_s, s_off[i], koff, sB + BN * 128 + (i * 4 + wave) * 1024);
@@ -347,7 +364,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
   // acc[i][j] lane l, element v: output row m = mrow_base + 32 i + (l & 31),
   // output columns n = ncol_base + 32 j + 8 (v >> 2) + 4 (l >> 5) + (v & 3).
   const int mrow_base = m0 + wm * TM;
-  const int ncol_base = n0 + wn * TN + 4 * lq;
+  const int ncol_base = n0 + wn * OUT_BN / 2 + 4 * lq;   // columns of block j: + 32 j (dual: j < FN/2)
 
   // Fused side: publish s_epi * U (bf16) to LDS for the rank-r product, save U (fp32).
   if constexpr (RSP > 0) {
@@ -437,8 +454,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
                 const float* src = p.S + (size_t)m * p.ld_s + j0;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                  const float lo = (j0 + 2 * e < p.r_epi) ? src[2 * e] * p.s_epi : 0.f;
-                  const float hi = (j0 + 2 * e + 1 < p.r_epi) ? src[2 * e + 1] * p.s_epi : 0.f;
+                  // dual tile: up ranks [r, 2r) take s_up (8-rank groups never straddle r, r % 8 == 0)
+                  const float sc = (DUAL && j0 >= p.e_jsplit) ? p.s_epi2 : p.s_epi;
+                  const float lo = (j0 + 2 * e < p.r_epi) ? src[2 * e] * sc : 0.f;
+                  const float hi = (j0 + 2 * e + 1 < p.r_epi) ? src[2 * e + 1] * sc : 0.f;
                   sf[i][e] = pack_bf16x2(lo, hi);
                 }
               }
@@ -446,7 +465,17 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
           }
 #pragma unroll
           for (int jj = 0; jj < JC; ++jj) {
-            const u32x4 ef = e_frag(p, n0 + wn * TN + (jc + jj) * 32 + lr, j0);
+            u32x4 ef;
+            if constexpr (DUAL) {
+              // gate blocks take ranks [0, r) of Bg, up blocks ranks [r, 2r) of Bu
+              constexpr int HB = FN / 2;
+              const bool upb = (jc + jj) >= HB;
+              const int h = n0 + wn * OUT_BN / 2 + ((jc + jj) % HB) * 32 + lr;
+              const bool mine = upb ? (j0 >= p.e_jsplit) : (j0 < p.e_jsplit);
+              ef = mine ? e_frag(p, h, j0) : u32x4{0, 0, 0, 0};
+            } else {
+              ef = e_frag(p, n0 + wn * TN + (jc + jj) * 32 + lr, j0);
+            }
 #pragma unroll
             for (int i = 0; i < FM; ++i) facc[i][jj] = mfma32_bf16(ef, sf[i], facc[i][jj]);
           }
@@ -471,7 +500,21 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
               bias4[0] = bf16_lo(bb[0]); bias4[1] = bf16_hi(bb[0]);
               bias4[2] = bf16_lo(bb[1]); bias4[3] = bf16_hi(bb[1]);
             }
-            if constexpr (C::kEpi == EPI_PLAIN || C::kEpi == EPI_DEQUANT) {
+            if constexpr (DUAL) {
+              if (jj >= FN / 2) continue;
+              const f32x16& vu = facc[i][jj + FN / 2];
+              const float u4[4] = {vu[4 * g], vu[4 * g + 1], vu[4 * g + 2], vu[4 * g + 3]};
+              u32x2 e2, u2, h2;
+              e2[0] = pack_bf16x2(v[0], v[1]);
+              e2[1] = pack_bf16x2(v[2], v[3]);
+              u2[0] = pack_bf16x2(u4[0], u4[1]);
+              u2[1] = pack_bf16x2(u4[2], u4[3]);
+              h2[0] = pack_bf16x2(silu_f(v[0]) * u4[0], silu_f(v[1]) * u4[1]);
+              h2[1] = pack_bf16x2(silu_f(v[2]) * u4[2], silu_f(v[3]) * u4[3]);
+              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (size_t)m * p.ldo + n) = e2;
+              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out2) + (size_t)m * p.ldo2 + n) = u2;
+              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out3) + (size_t)m * p.ldo3 + n) = h2;
+            } else if constexpr (C::kEpi == EPI_PLAIN || C::kEpi == EPI_DEQUANT) {
               u32x2 w;
               w[0] = pack_bf16x2(v[0] + bias4[0], v[1] + bias4[1]);
               w[1] = pack_bf16x2(v[2] + bias4[2], v[3] + bias4[3]);
