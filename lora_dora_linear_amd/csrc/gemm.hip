@@ -5,25 +5,28 @@
 // registers a wave may hold at one wave per SIMD (no scratch spills, checked
 // with -Rpass-analysis=kernel-resource-usage) are the only ones listed:
 //   NT bf16         256x256, 256x192, 256x128, 128x128, 128x64
-//   NT fused side   256x128 (down-projection rows computed in the K-loop)
-//   NT int8         256x128, 128x128, 128x64
+//   NT fused side   256x256, 256x128 (down-projection rows computed in the K-loop)
+//   NT int8         256x256, 256x128, 128x128, 128x64
 //   NN (bf16/int8 Q) 256x256, 256x192, 256x128, 128x128, 128x64
 #include "internal.hpp"
 
 namespace ldl {
 
+// 256x256 tiles run 8 waves (2 x 4 wave grid, two waves per SIMD); the others 4.
 template <int BM, int BN, bool I8, bool NN, bool BINT8, bool ASCALE, int RSP, bool SLOAD, int EPI>
 static hipError_t run(const GemmParams& p, hipStream_t st) {
-  using C = GemmCfg<BM, BN, I8, NN, BINT8, ASCALE, RSP, SLOAD, EPI>;
+  constexpr int WN = (BM == 256 && BN == 256) ? 4 : 2;
+  using C = GemmCfg<BM, BN, I8, NN, BINT8, ASCALE, RSP, SLOAD, EPI, WN>;
   const int out_bn = (EPI == EPI_SWIGLU_DUAL) ? BN / 2 : BN;
   const int tiles = ((p.M + BM - 1) / BM) * (p.N / out_bn);
-  hipLaunchKernelGGL(gemm_kernel<C>, dim3(tiles), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(gemm_kernel<C>, dim3(tiles), dim3(C::kThreads), 0, st, p);
   return hipGetLastError();
 }
 
 static int pick_bn(GemmKind kind, int N) {
   const bool wide_ok = (kind == GK_NT_PLAIN || kind == GK_NT_DORA || kind == GK_NT_SWIGLU || kind == GK_NN_PLAIN ||
-                        kind == GK_NN_SCALE || kind == GK_NN_I8_SCALE || kind == GK_NN_SWIGLU);
+                        kind == GK_NN_SCALE || kind == GK_NN_I8_SCALE || kind == GK_NN_SWIGLU || kind == GK_NT_FUSED ||
+                        kind == GK_NT_I8_DEQ || kind == GK_NT_I8_RAW);
   const bool b192_ok = (kind == GK_NT_PLAIN || kind == GK_NT_DORA || kind == GK_NN_PLAIN || kind == GK_NN_SCALE ||
                         kind == GK_NN_I8_SCALE);
   if (wide_ok && N % 256 == 0) return 256;
@@ -76,13 +79,19 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
       return run<256, 128, false, false, false, false, 0, true, EPI_SWIGLU_DUAL>(p, st);
     case GK_NT_FUSED:
       // down-projection computed in the K-loop; side rows padded to 32 or 64
+      if (bn == 256 && big) {
+        if (p.r_side <= 32) return run<256, 256, false, false, false, false, 32, false, EPI_PLAIN>(p, st);
+        return run<256, 256, false, false, false, false, 64, false, EPI_PLAIN>(p, st);
+      }
       if (p.r_side <= 32) return run<256, 128, false, false, false, false, 32, false, EPI_PLAIN>(p, st);
       return run<256, 128, false, false, false, false, 64, false, EPI_PLAIN>(p, st);
     case GK_NT_I8_DEQ:
+      if (bn == 256 && big) return run<256, 256, true, false, false, false, 0, true, EPI_DEQUANT>(p, st);
       if (bn >= 128) return big ? run<256, 128, true, false, false, false, 0, true, EPI_DEQUANT>(p, st)
                                 : run<128, 128, true, false, false, false, 0, true, EPI_DEQUANT>(p, st);
       return run<128, 64, true, false, false, false, 0, true, EPI_DEQUANT>(p, st);
     case GK_NT_I8_RAW:
+      if (bn == 256 && big) return run<256, 256, true, false, false, false, 0, false, EPI_RAW_I32>(p, st);
       if (bn >= 128) return big ? run<256, 128, true, false, false, false, 0, false, EPI_RAW_I32>(p, st)
                                 : run<128, 128, true, false, false, false, 0, false, EPI_RAW_I32>(p, st);
       return run<128, 64, true, false, false, false, 0, false, EPI_RAW_I32>(p, st);

@@ -65,9 +65,12 @@ struct GemmParams {
   float* side_save; int ld_side_save;
 };
 
-template <int BM_, int BN_, bool I8_, bool NN_, bool BINT8_, bool ASCALE_, int SIDE_RSP_, bool SLOAD_, int EPI_>
+template <int BM_, int BN_, bool I8_, bool NN_, bool BINT8_, bool ASCALE_, int SIDE_RSP_, bool SLOAD_, int EPI_,
+          int WN_ = 2>
 struct GemmCfg {
   static constexpr int BM = BM_, BN = BN_;
+  static constexpr int kWN = WN_;           // waves along N (two along M)
+  static constexpr int kThreads = 128 * WN_;
   static constexpr bool kI8 = I8_;          // P and Q int8 (NT only)
   static constexpr bool kNN = NN_;          // Q is [K, N]
   static constexpr bool kBInt8 = BINT8_;    // NN: Q int8, upcast to bf16 exactly
@@ -124,14 +127,16 @@ __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint32_t vof
 }
 
 template <class C>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
+__global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p) {
   constexpr int BM = C::BM, BN = C::BN;
   constexpr bool I8 = C::kI8, NN = C::kNN;
   constexpr int RSP = C::kSideRsp;
-  constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;   // 32x32 MFMA blocks per wave
+  constexpr int WN = C::kWN, WM = 2, NW = WM * WN;   // wave grid
+  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;   // 32x32 MFMA blocks per wave
   constexpr int BK = I8 ? 128 : 64;     // elements per k-tile (128 bytes per row)
-  constexpr int HALF = FM / 2;
-  static_assert(FM >= 2 && FM % 2 == 0 && FN >= 1, "wave tile must hold 2x1 32x32 blocks");
+  constexpr int SPW = RSP ? FM / WN : 1; // fused side: 32-row blocks per wave
+  static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 block");
+  static_assert(RSP == 0 || (FM % WN == 0), "fused side rows split evenly over the N waves");
   static_assert(RSP % 32 == 0, "side rows are padded to 32");
   static_assert(!NN || !I8, "NN takes bf16 P");
   using Acc = typename std::conditional<I8, i32x16, f32x16>::type;
@@ -166,7 +171,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 31, lq = lane >> 5;    // fragment row / 16-byte chunk within a step
 
   const uint32_t lda_b = (uint32_t)p.lda * (I8 ? 1 : 2);
@@ -178,9 +183,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
   // phys ^ swz(row) of that row.  Rows past the end of an operand (P rows
   // >= M, side rows >= r) read as zero through the buffer bounds.
   const int lrow = lane >> 3, lphys = lane & 7;
-  constexpr int A_INST = BM / 32;             // per wave
-  constexpr int B_INST = NN ? 0 : BN / 32;
-  constexpr int S_INST = (RSP * 8 + 255) / 256;
+  constexpr int A_INST = BM / (8 * NW);       // per wave
+  constexpr int B_INST = NN ? 0 : BN / (8 * NW);
+  constexpr int S_INST = (RSP + 8 * NW - 1) / (8 * NW);
+  static_assert(BM % (8 * NW) == 0 && (NN || BN % (8 * NW) == 0), "tile rows split evenly over the waves");
   const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(p.a, (uint32_t)M * lda_b);
   const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(p.b0, NN ? 0u : (uint32_t)N * ldb_b);
   const __amdgpu_buffer_rsrc_t rs_b2 = make_rsrc(DUAL ? p.b1 : p.b0, NN ? 0u : (uint32_t)N * ldb_b);
@@ -188,13 +194,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
   uint32_t a_off[A_INST];
 #pragma unroll
   for (int i = 0; i < A_INST; ++i) {
-    const int row = (i * 4 + wave) * 8 + lrow;
+    const int row = (i * NW + wave) * 8 + lrow;
     a_off[i] = (uint32_t)(m0 + row) * lda_b + ((lphys ^ swz(row)) << 4);
   }
   uint32_t b_off[B_INST ? B_INST : 1];
 #pragma unroll
   for (int i = 0; i < B_INST; ++i) {
-    const int row = (i * 4 + wave) * 8 + lrow;
+    const int row = (i * NW + wave) * 8 + lrow;
     int qrow = n0 + row;
     if constexpr (DUAL) {   // tile row -> (gate | up) row of hidden unit h
       const int within = row % TN;
@@ -205,7 +211,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
   uint32_t s_off[S_INST ? S_INST : 1];
 #pragma unroll
   for (int i = 0; i < S_INST; ++i) {
-    const int row = (i * 4 + wave) * 8 + lrow;      // side row
+    const int row = (i * NW + wave) * 8 + lrow;      // side row
     s_off[i] = (uint32_t)row * (uint32_t)K * 2u + ((lphys ^ swz(BN + row)) << 4);
   }
 
@@ -214,44 +220,50 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = Acc{};
-  f32x16 sacc[RSP ? HALF : 1][RSP ? RSP / 32 : 1];
+  f32x16 sacc[SPW][RSP ? RSP / 32 : 1];
   if constexpr (RSP > 0) {
 #pragma unroll
-    for (int i = 0; i < HALF; ++i)
+    for (int i = 0; i < SPW; ++i)
 #pragma unroll
       for (int j = 0; j < RSP / 32; ++j) sacc[i][j] = f32x16{};
   }
 
-  u32x4 rb[NN ? 8 : 1];   // NN: 8 rows x 8 columns of Q staged for the transpose
+  // NN: each thread stages RPT rows x 8 columns of Q for the transpose; with 512
+  // threads the 64 x BN k-tile is covered by 4-row slices (RPT_SLOTS = 2 per column group)
+  constexpr int RPT = (NN && NW == 8) ? 4 : 8;
+  constexpr int RPT_SLOTS = 8 / RPT;
+  static_assert(!NN || BN * RPT_SLOTS <= 64 * NW, "enough threads to stage the NN tile");
+  u32x4 rb[NN ? RPT : 1];
 
   // ---------------------------------------------------------------- loaders
   auto issue_loads = [&](int kt, uint8_t* sbuf) {
     const uint32_t koff = (uint32_t)kt * 128u;
 #pragma unroll
-    for (int i = 0; i < A_INST; ++i) buf2lds16(rs_a, a_off[i], koff, sbuf + (i * 4 + wave) * 1024);
+    for (int i = 0; i < A_INST; ++i) buf2lds16(rs_a, a_off[i], koff, sbuf + (i * NW + wave) * 1024);
     if constexpr (!NN) {
       uint8_t* sB = sbuf + BM * 128;
 #pragma unroll
       for (int i = 0; i < B_INST; ++i) {
         // the up half of each wave's rows comes from the second matrix (uniform per instruction)
-        const bool up = DUAL && ((((i * 4 + wave) * 8) % TN) >= TN / 2);
-        buf2lds16(up ? rs_b2 : rs_b, b_off[i], koff, sB + (i * 4 + wave) * 1024);
+        const bool up = DUAL && ((((i * NW + wave) * 8) % TN) >= TN / 2);
+        buf2lds16(up ? rs_b2 : rs_b, b_off[i], koff, sB + (i * NW + wave) * 1024);
       }
 #pragma unroll
       for (int i = 0; i < S_INST; ++i)
-        if ((i * 4 + wave) * 8 < RSP) buf2lds16(rs_s, s_off[i], koff, sB + BN * 128 + (i * 4 + wave) * 1024);
+        if ((i * NW + wave) * 8 < RSP) buf2lds16(rs_s, s_off[i], koff, sB + BN * 128 + (i * NW + wave) * 1024);
     } else {
-      // Q is [K, N]: this k-tile covers reduction rows kt*64 .. +63.
+      // Q is [K, N]: this k-tile covers reduction rows kt*64 .. +63.  Each thread
+      // stages RPT rows x 8 columns (RPT = 8 with 256 threads, 4 with 512).
       const int kk0 = kt * 64;
       const uint8_t* pb;
       int krow0;
       if (kk0 < p.kseg) { pb = static_cast<const uint8_t*>(p.b0); krow0 = kk0; }
       else { pb = static_cast<const uint8_t*>(p.b1); krow0 = kk0 - p.kseg; }
-      if (tid < BN) {
+      if (tid < BN * RPT_SLOTS) {
         const int kb = tid % (BN / 8), nb = tid / (BN / 8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const size_t rowoff = (size_t)(krow0 + nb * 8 + e) * (size_t)ldb_b;
+        for (int e = 0; e < RPT; ++e) {
+          const size_t rowoff = (size_t)(krow0 + nb * RPT + e) * (size_t)ldb_b;
           if constexpr (C::kBInt8) {
             u32x2 v = *reinterpret_cast<const u32x2*>(pb + rowoff + (size_t)(n0 + kb * 8));
             rb[e] = i8x8_to_bf16x8(v);
@@ -266,23 +278,43 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
   // NN only: scale (optional) and transpose the staged Q rows into LDS.
   auto store_q = [&](int kt, uint8_t* sbuf) {
     if constexpr (NN) {
-      if (tid < BN) {
+      if (tid < BN * RPT_SLOTS) {
         uint8_t* sB = sbuf + BM * 128;
         const int kb = tid % (BN / 8), nb = tid / (BN / 8);
         if constexpr (C::kAScale) {
-          const f32x4* sc = reinterpret_cast<const f32x4*>(p.a_colscale + (size_t)kt * 64 + nb * 8);
-          const f32x4 s0 = sc[0], s1 = sc[1];
-          const float f[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+          const f32x4* sc = reinterpret_cast<const f32x4*>(p.a_colscale + (size_t)kt * 64 + nb * RPT);
+          float f[RPT];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
+          for (int q = 0; q < RPT / 4; ++q) {
+            const f32x4 v4 = sc[q];
+            f[4 * q] = v4[0]; f[4 * q + 1] = v4[1]; f[4 * q + 2] = v4[2]; f[4 * q + 3] = v4[3];
+          }
+#pragma unroll
+          for (int e = 0; e < RPT; ++e) {
             const f32x4 se = f32x4{f[e], f[e], f[e], f[e]};
             rb[e] = scale_bf16x8(rb[e], se, se);
           }
         }
-        u32x4 t[8];
-        transpose8x8_b16(rb, t);
+        if constexpr (RPT == 8) {
+          u32x4 t[8];
+          transpose8x8_b16(rb, t);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) lds_st16(sB, lds_off(kb * 8 + c, nb), t[c]);
+          for (int c = 0; c < 8; ++c) lds_st16(sB, lds_off(kb * 8 + c, nb), t[c]);
+        } else {
+          // 4 rows x 8 columns -> 8 columns of 4 values, written as 8-byte halves of a chunk
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            u32x2 lo, hi;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const uint32_t a = rb[2 * j][cc], b = rb[2 * j + 1][cc];
+              lo[j] = (a & 0xffffu) | (b << 16);
+              hi[j] = (a >> 16) | (b & 0xffff0000u);
+            }
+            *reinterpret_cast<u32x2*>(sB + lds_off(kb * 8 + 2 * cc, nb >> 1) + (nb & 1) * 8) = lo;
+            *reinterpret_cast<u32x2*>(sB + lds_off(kb * 8 + 2 * cc + 1, nb >> 1) + (nb & 1) * 8) = hi;
+          }
+        }
       }
     }
   };
@@ -314,12 +346,12 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
     if constexpr (RSP > 0) {
 #pragma unroll
       for (int js = 0; js < RSP / 32; ++js) {
-        if (wn == 0) {
 #pragma unroll
-          for (int i = 0; i < HALF; ++i) sacc[i][js] = mfma32_bf16(sf[js], af[i], sacc[i][js]);
-        } else {
+        for (int w = 0; w < WN; ++w) {
+          if (wn == w) {   // uniform branch keeps the fragment index compile-time
 #pragma unroll
-          for (int i = 0; i < HALF; ++i) sacc[i][js] = mfma32_bf16(sf[js], af[HALF + i], sacc[i][js]);
+            for (int i = 0; i < SPW; ++i) sacc[i][js] = mfma32_bf16(sf[js], af[w * SPW + i], sacc[i][js]);
+          }
         }
       }
     }
@@ -364,14 +396,14 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
   // acc[i][j] lane l, element v: output row m = mrow_base + 32 i + (l & 31),
   // output columns n = ncol_base + 32 j + 8 (v >> 2) + 4 (l >> 5) + (v & 3).
   const int mrow_base = m0 + wm * TM;
-  const int ncol_base = n0 + wn * OUT_BN / 2 + 4 * lq;   // columns of block j: + 32 j (dual: j < FN/2)
+  const int ncol_base = n0 + wn * (OUT_BN / WN) + 4 * lq;   // columns of block j: + 32 j (dual: j < FN/2)
 
   // Fused side: publish s_epi * U (bf16) to LDS for the rank-r product, save U (fp32).
   if constexpr (RSP > 0) {
     uint16_t* sS = reinterpret_cast<uint16_t*>(smem0);
 #pragma unroll
-    for (int i = 0; i < HALF; ++i) {
-      const int row = wm * TM + (wn * HALF + i) * 32 + lr;
+    for (int i = 0; i < SPW; ++i) {
+      const int row = wm * TM + (wn * SPW + i) * 32 + lr;
       const int m = m0 + row;
 #pragma unroll
       for (int js = 0; js < RSP / 32; ++js) {
@@ -470,7 +502,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmParams p) {
               // gate blocks take ranks [0, r) of Bg, up blocks ranks [r, 2r) of Bu
               constexpr int HB = FN / 2;
               const bool upb = (jc + jj) >= HB;
-              const int h = n0 + wn * OUT_BN / 2 + ((jc + jj) % HB) * 32 + lr;
+              const int h = n0 + wn * (OUT_BN / WN) + ((jc + jj) % HB) * 32 + lr;
               const bool mine = upb ? (j0 >= p.e_jsplit) : (j0 < p.e_jsplit);
               ef = mine ? e_frag(p, h, j0) : u32x4{0, 0, 0, 0};
             } else {
