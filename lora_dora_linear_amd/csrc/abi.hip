@@ -78,7 +78,7 @@ inline hipStream_t S(void* st) { return static_cast<hipStream_t>(st); }
 
 // ------------------------------------------------------------------ workspace plans
 struct LoraBwdWs {
-  uint16_t* Bt; float* V; float* U; float* partB; float* csB; float* partA;
+  float* V; float* U; float* partB; float* csB; float* partA;
   int nsB, msB, nsA, msA, rp;
 };
 LoraBwdWs plan_lora_bwd(Bump& b, int M, int N, int K, int r, bool need_u) {
@@ -86,7 +86,6 @@ LoraBwdWs plan_lora_bwd(Bump& b, int M, int N, int K, int r, bool need_u) {
   w.rp = colproj_rp(r);
   colproj_plan(M, N, &w.nsB, &w.msB);
   colproj_plan(M, K, &w.nsA, &w.msA);
-  w.Bt = b.take<uint16_t>((size_t)r * N);
   w.V = b.take<float>((size_t)M * r);
   w.U = need_u ? b.take<float>((size_t)M * r) : nullptr;
   w.partB = b.take<float>((size_t)w.nsB * N * w.rp);
@@ -96,7 +95,7 @@ LoraBwdWs plan_lora_bwd(Bump& b, int M, int N, int K, int r, bool need_u) {
 }
 
 struct DoraBwdWs {
-  uint16_t* Bt; float* V; float* partT; float* cs; float* wB; float* partA; float* partQ; float* Qm;
+  float* V; float* partT; float* cs; float* wB; float* partA; float* partQ; float* Qm;
   float* partbias; float* csbias;
   int nsT, msT, nsA, msA, nsW, msW, nsQ, msQ, rp;
 };
@@ -107,7 +106,6 @@ DoraBwdWs plan_dora_bwd(Bump& b, int M, int N, int K, int r) {
   colproj_plan(M, K, &w.nsA, &w.msA);
   colproj_plan(N, K, &w.nsW, &w.msW);
   colproj_plan(N, r, &w.nsQ, &w.msQ);
-  w.Bt = b.take<uint16_t>((size_t)r * N);
   w.V = b.take<float>((size_t)M * r);
   w.partT = b.take<float>((size_t)w.nsT * N * w.rp);
   w.cs = b.take<float>((size_t)w.nsT * N);
@@ -121,7 +119,7 @@ DoraBwdWs plan_dora_bwd(Bump& b, int M, int N, int K, int r) {
 }
 
 struct MlpBwdWs {
-  uint16_t* Bdt; uint16_t* Bgt; uint16_t* But; float* Vd; float* Vgu; uint16_t* dEGu;
+  float* Vd; float* Vgu; uint16_t* dEGu;
   float* partDd; float* partAd; float* partBg; float* partBu; float* partAgu;
   int nsDd, msDd, nsAd, msAd, nsBg, msBg, nsAgu, msAgu, rp, rp2;
 };
@@ -133,9 +131,6 @@ MlpBwdWs plan_mlp_bwd(Bump& b, int M, int K, int H, int r) {
   colproj_plan(M, H, &w.nsAd, &w.msAd);
   colproj_plan(M, H, &w.nsBg, &w.msBg);
   colproj_plan(M, K, &w.nsAgu, &w.msAgu);
-  w.Bdt = b.take<uint16_t>((size_t)r * K);
-  w.Bgt = b.take<uint16_t>((size_t)r * H);
-  w.But = b.take<uint16_t>((size_t)r * H);
   w.Vd = b.take<float>((size_t)M * r);
   w.Vgu = b.take<float>((size_t)M * 2 * r);
   w.dEGu = b.take<uint16_t>((size_t)M * 2 * H);
@@ -161,33 +156,59 @@ hipError_t rowproj(int M, int K, int R, const void* P, int ldp, const void* q0, 
   p.M = M; p.K = K; p.R = R; p.R0 = R0;
   p.P = static_cast<const uint16_t*>(P); p.ldp = ldp;
   p.q0 = static_cast<const uint16_t*>(q0); p.q1 = static_cast<const uint16_t*>(q1 ? q1 : q0); p.ldq = ldq;
+  p.q_trans = 0; p.q_kscale = nullptr;
   p.out = out; p.ldo = ldo; p.scale = scale;
   return launch_rowproj(p, st);
 }
 
-hipError_t colproj(int M, int C, int R, const void* X, int ldx, const float* Sm, int lds, float s_in,
-                   const void* Z, int ldz, int mode, int nsplit, int msplit, float* part, float* cspart,
-                   hipStream_t st) {
+// out[m, j] = scale * sum_k P[m, k] * bf16(Bq[k, j] * kscale[k]) with Bq a [K, R] matrix, leading dim ldb
+hipError_t rowproj_t(int M, int K, int R, const void* P, int ldp, const void* Bq, int ldb, const float* kscale,
+                     float* out, int ldo, float scale, hipStream_t st) {
+  RowProjParams p;
+  p.M = M; p.K = K; p.R = R; p.R0 = R;
+  p.P = static_cast<const uint16_t*>(P); p.ldp = ldp;
+  p.q0 = p.q1 = static_cast<const uint16_t*>(Bq); p.ldq = ldb;
+  p.q_trans = 1; p.q_kscale = kscale;
+  p.out = out; p.ldo = ldo; p.scale = scale;
+  return launch_rowproj(p, st);
+}
+
+ColProjParams cpp(int M, int C, int R, const void* X, int ldx, const float* Sm, int lds, float s_in,
+                  const void* Z, int ldz, int mode, int msplit, float* part, float* cspart) {
   ColProjParams p;
   p.M = M; p.C = C; p.R = R;
   p.X = static_cast<const uint16_t*>(X); p.ldx = ldx;
   p.S = Sm; p.lds = lds; p.s_in = s_in;
   p.Z = static_cast<const uint16_t*>(Z); p.ldz = ldz; p.colsum_mode = mode;
   p.msplit = msplit; p.part = part; p.cspart = cspart;
-  return launch_colproj(p, nsplit, st);
+  return p;
+}
+
+hipError_t colproj(int M, int C, int R, const void* X, int ldx, const float* Sm, int lds, float s_in,
+                   const void* Z, int ldz, int mode, int nsplit, int msplit, float* part, float* cspart,
+                   hipStream_t st) {
+  return launch_colproj(cpp(M, C, R, X, ldx, Sm, lds, s_in, Z, ldz, mode, msplit, part, cspart), nsplit, st);
 }
 
 // out[rows, cols] = alpha * sum over nsplit partials (+ row scale) (+ addend)
-hipError_t reduce(int rows, int cols, const float* part, size_t pstride, int nsplit, int rp, bool trans, float alpha,
-                  float* out, int ldo, hipStream_t st, const float* rowscale = nullptr,
-                  const float* Qm = nullptr, int ldq = 0, int rq = 0, const void* Am = nullptr, int lda = 0,
-                  float alpha2 = 0.f) {
+ReduceParams rdp(int rows, int cols, const float* part, size_t pstride, int nsplit, int rp, bool trans, float alpha,
+                 float* out, int ldo, const float* rowscale = nullptr,
+                 const float* Qm = nullptr, int ldq = 0, int rq = 0, const void* Am = nullptr, int lda = 0,
+                 float alpha2 = 0.f) {
   ReduceParams p;
   p.rows = rows; p.cols = cols; p.part = part; p.pstride = pstride; p.nsplit = nsplit; p.rp = rp;
   p.trans = trans ? 1 : 0; p.alpha = alpha; p.rowscale = rowscale;
   p.Qm = Qm; p.ldq = ldq; p.rq = rq; p.Am = static_cast<const uint16_t*>(Am); p.lda = lda; p.alpha2 = alpha2;
   p.out = out; p.ldo = ldo;
-  return launch_reduce(p, st);
+  return p;
+}
+
+hipError_t reduce(int rows, int cols, const float* part, size_t pstride, int nsplit, int rp, bool trans, float alpha,
+                  float* out, int ldo, hipStream_t st, const float* rowscale = nullptr,
+                  const float* Qm = nullptr, int ldq = 0, int rq = 0, const void* Am = nullptr, int lda = 0,
+                  float alpha2 = 0.f) {
+  return launch_reduce(rdp(rows, cols, part, pstride, nsplit, rp, trans, alpha, out, ldo, rowscale, Qm, ldq, rq, Am,
+                           lda, alpha2), st);
 }
 
 hipError_t zero(float* p, size_t n, hipStream_t st) { return p ? launch_fill_zero(p, n, st) : hipSuccess; }
@@ -370,9 +391,8 @@ int lora_linear_bwd(int M, int N, int K, int r, float s, int dtype, const void* 
     LDL_TRY(rowproj(M, K, r, X, K, A, nullptr, r, K, w.U, r, 1.f, st));
     U = w.U;
   }
-  // V = dY.B  (B^T staged so both operands are contiguous along the reduction)
-  LDL_TRY(launch_transpose_scale(static_cast<const uint16_t*>(B), nullptr, N, r, w.Bt, st));
-  LDL_TRY(rowproj(M, N, r, dY, N, w.Bt, nullptr, r, N, w.V, r, 1.f, st));
+  // V = dY.B  (B read in place as a [N, r] matrix)
+  LDL_TRY(rowproj_t(M, N, r, dY, N, B, r, nullptr, w.V, r, 1.f, st));
   if (dX) {
     GemmParams p = gp0();
     p.M = M; p.N = K; p.K = N;
@@ -382,13 +402,13 @@ int lora_linear_bwd(int M, int N, int K, int r, float s, int dtype, const void* 
     p.out = dX; p.ldo = K;
     LDL_TRY(gemm_timed(1, GK_NN_PLAIN, p, st));
   }
-  // dB = s.dY^T.U  (+ dbias = column sums of dY in the same pass)
-  LDL_TRY(colproj(M, N, r, dY, N, U, r, 1.f, nullptr, 0, dbias ? 2 : 0, w.nsB, w.msB, w.partB, w.csB, st));
-  LDL_TRY(reduce(N, r, w.partB, (size_t)N * w.rp, w.nsB, w.rp, false, s, dB, r, st));
+  // dB = s.dY^T.U (+ dbias = column sums of dY in the same pass) and dA = s.V^T.X: one launch each
+  // for the split partial sums and for their fixed-order reduction
+  LDL_TRY(launch_colproj2(cpp(M, N, r, dY, N, U, r, 1.f, nullptr, 0, dbias ? 2 : 0, w.msB, w.partB, w.csB), w.nsB,
+                          cpp(M, K, r, X, K, w.V, r, 1.f, nullptr, 0, 0, w.msA, w.partA, nullptr), w.nsA, st));
+  LDL_TRY(launch_reduce2(rdp(N, r, w.partB, (size_t)N * w.rp, w.nsB, w.rp, false, s, dB, r),
+                         rdp(r, K, w.partA, (size_t)K * w.rp, w.nsA, w.rp, true, s, dA, K), st));
   if (dbias) LDL_TRY(launch_reduce_colsum(w.csB, w.nsB, N, dbias, st));
-  // dA = s.V^T.X
-  LDL_TRY(colproj(M, K, r, X, K, w.V, r, 1.f, nullptr, 0, 0, w.nsA, w.msA, w.partA, nullptr, st));
-  LDL_TRY(reduce(r, K, w.partA, (size_t)K * w.rp, w.nsA, w.rp, true, s, dA, K, st));
   return LDL_OK;
 }
 
@@ -471,10 +491,11 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, c
   }
   // dB, dm and wB = 2s.w.B per output row
   LDL_TRY(launch_dora_finalize(N, r, s, eps, w.partT, w.cs, w.nsT, w.rp, norm, g, m, P, G, Bh, dB, dm, w.wB, st));
+  ColProjParams jobs[3];
+  int ns[3], nj = 0;
   if (M > 0) {
-    // V = (dY.diag(g)).B
-    LDL_TRY(launch_transpose_scale(Bh, g, N, r, w.Bt, st));
-    LDL_TRY(rowproj(M, N, r, dY, N, w.Bt, nullptr, r, N, w.V, r, 1.f, st));
+    // V = (dY.diag(g)).B, the scaled B read in place as a [N, r] matrix
+    LDL_TRY(rowproj_t(M, N, r, dY, N, Bh, r, g, w.V, r, 1.f, st));
     if (dX) {
       GemmParams p = gp0();
       p.M = M; p.N = K; p.K = N;
@@ -485,14 +506,17 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, c
       LDL_TRY(gemm_timed(1, GK_NN_SCALE, p, st));
     }
     // s.V^T.X into the first nsA partials of dA
-    LDL_TRY(colproj(M, K, r, X, K, w.V, r, s, nullptr, 0, 0, w.nsA, w.msA, w.partA, nullptr, st));
+    jobs[nj] = cpp(M, K, r, X, K, w.V, r, s, nullptr, 0, 0, w.msA, w.partA, nullptr);
+    ns[nj++] = w.nsA;
   } else {
     LDL_TRY(zero(w.partA, (size_t)w.nsA * K * w.rp, st));
   }
   // (2s.w.B)^T.W0 into the next nsW partials; Q = B^T.(2s.w.B)
-  LDL_TRY(colproj(N, K, r, W0, K, w.wB, r, 1.f, nullptr, 0, 0, w.nsW, w.msW, w.partA + (size_t)w.nsA * K * w.rp,
-                  nullptr, st));
-  LDL_TRY(colproj(N, r, r, B, r, w.wB, r, 1.f, nullptr, 0, 0, w.nsQ, w.msQ, w.partQ, nullptr, st));
+  jobs[nj] = cpp(N, K, r, W0, K, w.wB, r, 1.f, nullptr, 0, 0, w.msW, w.partA + (size_t)w.nsA * K * w.rp, nullptr);
+  ns[nj++] = w.nsW;
+  jobs[nj] = cpp(N, r, r, B, r, w.wB, r, 1.f, nullptr, 0, 0, w.msQ, w.partQ, nullptr);
+  ns[nj++] = w.nsQ;
+  LDL_TRY(launch_colproj_batch(jobs, ns, nj, st));
   LDL_TRY(reduce(r, r, w.partQ, (size_t)r * w.rp, w.nsQ, w.rp, false, 1.f, w.Qm, r, st));
   // dA = sum of all partials + s.Q.A   (2s^2 B^T diag(w) B A = s.Q.A)
   LDL_TRY(reduce(r, K, w.partA, (size_t)K * w.rp, w.nsA + w.nsW, w.rp, true, 1.f, dA, K, st, nullptr, w.Qm, r, r, A,
@@ -581,11 +605,8 @@ int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, fl
   const float* Uu = U_saved + r;
   const float* Ud = U_saved + 2 * r;
 
-  // ---- down projection: V_d = dOut.Bd, dBd = s_d.dOut^T.U_d
-  LDL_TRY(launch_transpose_scale(static_cast<const uint16_t*>(Bd), nullptr, K, r, w.Bdt, st));
-  LDL_TRY(rowproj(M, K, r, dOut, K, w.Bdt, nullptr, r, K, w.Vd, r, 1.f, st));
-  LDL_TRY(colproj(M, K, r, dOut, K, Ud, r3, 1.f, nullptr, 0, 0, w.nsDd, w.msDd, w.partDd, nullptr, st));
-  LDL_TRY(reduce(K, r, w.partDd, (size_t)K * w.rp, w.nsDd, w.rp, false, s_down, dBd, r, st));
+  // ---- down projection: V_d = dOut.Bd (Bd read in place as a [K, r] matrix)
+  LDL_TRY(rowproj_t(M, K, r, dOut, K, Bd, r, nullptr, w.Vd, r, 1.f, st));
   // ---- dH = dOut.Wd + s_d.V_d.Ad with the SwiGLU backward in the epilogue -> [dE | dGu]
   {
     GemmParams p = gp0();
@@ -597,18 +618,20 @@ int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, fl
     p.out = w.dEGu; p.ldo = 2 * H; p.out2 = w.dEGu + H; p.ldo2 = 2 * H;
     LDL_TRY(launch_gemm(GK_NN_SWIGLU, p, st));
   }
-  // dAd = s_d.V_d^T.H
-  LDL_TRY(colproj(M, H, r, H_saved, H, w.Vd, r, 1.f, nullptr, 0, 0, w.nsAd, w.msAd, w.partAd, nullptr, st));
-  LDL_TRY(reduce(r, H, w.partAd, (size_t)H * w.rp, w.nsAd, w.rp, true, s_down, dAd, H, st));
+  // dBd = s_d.dOut^T.U_d and dAd = s_d.V_d^T.H
+  LDL_TRY(launch_colproj2(cpp(M, K, r, dOut, K, Ud, r3, 1.f, nullptr, 0, 0, w.msDd, w.partDd, nullptr), w.nsDd,
+                          cpp(M, H, r, H_saved, H, w.Vd, r, 1.f, nullptr, 0, 0, w.msAd, w.partAd, nullptr), w.nsAd,
+                          st));
+  LDL_TRY(launch_reduce2(rdp(K, r, w.partDd, (size_t)K * w.rp, w.nsDd, w.rp, false, s_down, dBd, r),
+                         rdp(r, H, w.partAd, (size_t)H * w.rp, w.nsAd, w.rp, true, s_down, dAd, H), st));
   // ---- gate / up: V_g = s_g.dE.Bg, V_u = s_u.dGu.Bu (pre-scaled), dBg, dBu
-  LDL_TRY(launch_transpose_scale(static_cast<const uint16_t*>(Bg), nullptr, H, r, w.Bgt, st));
-  LDL_TRY(launch_transpose_scale(static_cast<const uint16_t*>(Bu), nullptr, H, r, w.But, st));
-  LDL_TRY(rowproj(M, H, r, w.dEGu, 2 * H, w.Bgt, nullptr, r, H, w.Vgu, 2 * r, s_gate, st));
-  LDL_TRY(rowproj(M, H, r, w.dEGu + H, 2 * H, w.But, nullptr, r, H, w.Vgu + r, 2 * r, s_up, st));
-  LDL_TRY(colproj(M, H, r, w.dEGu, 2 * H, Ug, r3, 1.f, nullptr, 0, 0, w.nsBg, w.msBg, w.partBg, nullptr, st));
-  LDL_TRY(reduce(H, r, w.partBg, (size_t)H * w.rp, w.nsBg, w.rp, false, s_gate, dBg, r, st));
-  LDL_TRY(colproj(M, H, r, w.dEGu + H, 2 * H, Uu, r3, 1.f, nullptr, 0, 0, w.nsBg, w.msBg, w.partBu, nullptr, st));
-  LDL_TRY(reduce(H, r, w.partBu, (size_t)H * w.rp, w.nsBg, w.rp, false, s_up, dBu, r, st));
+  LDL_TRY(rowproj_t(M, H, r, w.dEGu, 2 * H, Bg, r, nullptr, w.Vgu, 2 * r, s_gate, st));
+  LDL_TRY(rowproj_t(M, H, r, w.dEGu + H, 2 * H, Bu, r, nullptr, w.Vgu + r, 2 * r, s_up, st));
+  LDL_TRY(launch_colproj2(cpp(M, H, r, w.dEGu, 2 * H, Ug, r3, 1.f, nullptr, 0, 0, w.msBg, w.partBg, nullptr), w.nsBg,
+                          cpp(M, H, r, w.dEGu + H, 2 * H, Uu, r3, 1.f, nullptr, 0, 0, w.msBg, w.partBu, nullptr),
+                          w.nsBg, st));
+  LDL_TRY(launch_reduce2(rdp(H, r, w.partBg, (size_t)H * w.rp, w.nsBg, w.rp, false, s_gate, dBg, r),
+                         rdp(H, r, w.partBu, (size_t)H * w.rp, w.nsBg, w.rp, false, s_up, dBu, r), st));
   // ---- dX = [dE | dGu].[Wg; Wu] + [V_g | V_u].[Ag; Au]  (one GEMM over the 2H reduction)
   if (dX) {
     GemmParams p = gp0();
@@ -621,8 +644,8 @@ int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, fl
   }
   // dAg, dAu = [V_g | V_u]^T.X in one pass over X
   LDL_TRY(colproj(M, K, 2 * r, X, K, w.Vgu, 2 * r, 1.f, nullptr, 0, 0, w.nsAgu, w.msAgu, w.partAgu, nullptr, st));
-  LDL_TRY(reduce(r, K, w.partAgu, (size_t)K * w.rp2, w.nsAgu, w.rp2, true, 1.f, dAg, K, st));
-  LDL_TRY(reduce(r, K, w.partAgu + r, (size_t)K * w.rp2, w.nsAgu, w.rp2, true, 1.f, dAu, K, st));
+  LDL_TRY(launch_reduce2(rdp(r, K, w.partAgu, (size_t)K * w.rp2, w.nsAgu, w.rp2, true, 1.f, dAg, K),
+                         rdp(r, K, w.partAgu + r, (size_t)K * w.rp2, w.nsAgu, w.rp2, true, 1.f, dAu, K), st));
   return LDL_OK;
 }
 
@@ -710,8 +733,7 @@ int w8a8_lora_linear_bwd(int M, int N, int K, int r, float s, const void* dY, co
     LDL_TRY(rowproj(M, K, r, X, K, A, nullptr, r, K, w.U, r, 1.f, st));
     U = w.U;
   }
-  LDL_TRY(launch_transpose_scale(static_cast<const uint16_t*>(B), nullptr, N, r, w.Bt, st));
-  LDL_TRY(rowproj(M, N, r, dY, N, w.Bt, nullptr, r, N, w.V, r, 1.f, st));
+  LDL_TRY(rowproj_t(M, N, r, dY, N, B, r, nullptr, w.V, r, 1.f, st));
   if (dX) {
     GemmParams p = gp0();
     p.M = M; p.N = K; p.K = N;
@@ -721,10 +743,10 @@ int w8a8_lora_linear_bwd(int M, int N, int K, int r, float s, const void* dY, co
     p.out = dX; p.ldo = K;
     LDL_TRY(gemm_timed(1, GK_NN_I8_SCALE, p, st));
   }
-  LDL_TRY(colproj(M, N, r, dY, N, U, r, 1.f, nullptr, 0, 0, w.nsB, w.msB, w.partB, nullptr, st));
-  LDL_TRY(reduce(N, r, w.partB, (size_t)N * w.rp, w.nsB, w.rp, false, s, dB, r, st));
-  LDL_TRY(colproj(M, K, r, X, K, w.V, r, 1.f, nullptr, 0, 0, w.nsA, w.msA, w.partA, nullptr, st));
-  LDL_TRY(reduce(r, K, w.partA, (size_t)K * w.rp, w.nsA, w.rp, true, s, dA, K, st));
+  LDL_TRY(launch_colproj2(cpp(M, N, r, dY, N, U, r, 1.f, nullptr, 0, 0, w.msB, w.partB, nullptr), w.nsB,
+                          cpp(M, K, r, X, K, w.V, r, 1.f, nullptr, 0, 0, w.msA, w.partA, nullptr), w.nsA, st));
+  LDL_TRY(launch_reduce2(rdp(N, r, w.partB, (size_t)N * w.rp, w.nsB, w.rp, false, s, dB, r),
+                         rdp(r, K, w.partA, (size_t)K * w.rp, w.nsA, w.rp, true, s, dA, K), st));
   return LDL_OK;
 }
 

@@ -10,6 +10,8 @@ struct RowProjParams {
   int M, K, R, R0;                 // Q rows j < R0 come from q0, rows j >= R0 from q1
   const uint16_t* P; int ldp;      // [M, K] bf16
   const uint16_t* q0; const uint16_t* q1; int ldq;
+  int q_trans;                     // 1: Q(j, k) = q0[k * ldq + j] (a [K, R] matrix such as lora_up B)
+  const float* q_kscale;           // q_trans only, optional: Q(j, k) *= q_kscale[k] (rounded to bf16)
   float* out; int ldo;             // out[m * ldo + j] = scale * sum_k P[m,k] Q[j,k]
   float scale;
 };
@@ -49,9 +51,14 @@ hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st);
 int colproj_rp(int R);
 void colproj_plan(int M, int C, int* nsplit, int* msplit);
 hipError_t launch_colproj(const ColProjParams& p, int nsplit, hipStream_t st);
+// up to kColProjBatch independent column projections in one launch (one launch per job when
+// their rank paddings differ)
+constexpr int kColProjBatch = 3;
+hipError_t launch_colproj_batch(const ColProjParams* jobs, const int* nsplit, int njobs, hipStream_t st);
+hipError_t launch_colproj2(const ColProjParams& a, int nsplit_a, const ColProjParams& b, int nsplit_b, hipStream_t st);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t st);
+hipError_t launch_reduce2(const ReduceParams& a, const ReduceParams& b, hipStream_t st);
 hipError_t launch_reduce_colsum(const float* cspart, int nsplit, int C, float* out, hipStream_t st);
-hipError_t launch_transpose_scale(const uint16_t* B, const float* scale, int N, int r, uint16_t* Bt, hipStream_t st);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t st);
 
 // DoRA helpers

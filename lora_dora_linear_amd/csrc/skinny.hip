@@ -3,7 +3,9 @@
 //
 //   rowproj : out[m, j] = scale * sum_k P[m, k] * Q[j, k]       (U = X.A^T, V = dY.B,
 //             P = W0.A^T, G = A.A^T); P, Q bf16 with k contiguous, both read
-//             straight from global memory into MFMA fragments.
+//             straight from global memory into MFMA fragments.  Q may instead be
+//             a [K, R] matrix read in place (lora_up B), optionally with a
+//             per-k factor applied and rounded to bf16 (DoRA's diag(g).B).
 //   colproj : part[split][c, j] = sum_{m in split} X[m, c] * S[m, j]   (dB = dY^T.U,
 //             dA^T = X^T.V and the DoRA norm terms); X bf16 is staged through
 //             LDS with an 8x8 register transpose so that each lane holds eight
@@ -12,7 +14,8 @@
 //             sum_m X[m, c] * Z[m, c] (DoRA dg) or sum_m X[m, c] (bias gradient).
 //
 // These are the "skinny MFMA contractions" for the factor gradients: each is
-// one pass over the [M, *] operand and bound by HBM bandwidth.
+// one pass over the [M, *] operand and bound by HBM bandwidth.  Up to three
+// independent column projections, and two reductions, share one launch.
 #include "internal.hpp"
 
 namespace ldl {
@@ -40,9 +43,31 @@ __global__ __launch_bounds__(512) void rowproj_kernel(const RowProjParams p) {
   for (int jb = 0; jb < NB; ++jb) {
     const int j = jb * 16 + lr;
     qval[jb] = j < p.R;
-    const uint16_t* base = (j < p.R0) ? (p.q0 + (size_t)j * p.ldq) : (p.q1 + (size_t)(j - p.R0) * p.ldq);
-    qrow[jb] = (qval[jb] ? base : p.q0) + lq * 8;
+    if (p.q_trans) {
+      qrow[jb] = p.q0 + (qval[jb] ? j : 0) + (size_t)(lq * 8) * p.ldq;
+    } else {
+      const uint16_t* base = (j < p.R0) ? (p.q0 + (size_t)j * p.ldq) : (p.q1 + (size_t)(j - p.R0) * p.ldq);
+      qrow[jb] = (qval[jb] ? base : p.q0) + lq * 8;
+    }
   }
+  // Q fragment of step k: 8 consecutive reduction indices k*32 + 8*lq + e of row j
+  auto qload = [&](int jb, int k) -> u32x4 {
+    if (!qval[jb]) return u32x4{0, 0, 0, 0};
+    if (!p.q_trans) return ld16(qrow[jb] + k * 32);
+    const uint16_t* q = qrow[jb] + (size_t)(k * 32) * p.ldq;
+    u32x4 v;
+    if (p.q_kscale == nullptr) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (uint32_t)q[(size_t)(2 * e) * p.ldq] | ((uint32_t)q[(size_t)(2 * e + 1) * p.ldq] << 16);
+    } else {
+      const float* sc = p.q_kscale + k * 32 + lq * 8;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] = pack_bf16x2(bf16_to_f32(q[(size_t)(2 * e) * p.ldq]) * sc[2 * e],
+                           bf16_to_f32(q[(size_t)(2 * e + 1) * p.ldq]) * sc[2 * e + 1]);
+    }
+    return v;
+  };
 
   f32x4 acc[NB];
 #pragma unroll
@@ -50,27 +75,35 @@ __global__ __launch_bounds__(512) void rowproj_kernel(const RowProjParams p) {
 
   const int nsteps = p.K / 32;
   const u32x4 zero = {0, 0, 0, 0};
-  constexpr int U = 8;
+  // every load of a group (P from HBM, Q from L2) is issued before its MFMAs;
+  // each block starts at a different point of the reduction so that the blocks
+  // do not all request the same lines of the small Q at the same time
+  constexpr int U = NB <= 2 ? 8 : (NB == 4 ? 4 : 2);
+  const int groups = nsteps / RP_WAVES;                      // full rounds of 8 steps
+  const int rot = groups > 0 ? (int)(blockIdx.x % (unsigned)groups) * RP_WAVES : 0;
+  auto step_of = [&](int t) { int k = t + rot; return k >= groups * RP_WAVES ? k - groups * RP_WAVES : k; };
   int ks = wave;
-  for (; ks + (U - 1) * RP_WAVES < nsteps; ks += U * RP_WAVES) {
-    u32x4 pf[U];
+  const int full = groups * RP_WAVES;                        // steps covered by the rotation
+  for (; ks + (U - 1) * RP_WAVES < full; ks += U * RP_WAVES) {
+    u32x4 pf[U], qf[U][NB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) pf[u] = mval ? ld16(prow + (ks + u * RP_WAVES) * 32) : zero;
+    for (int u = 0; u < U; ++u) pf[u] = mval ? ld16(prow + step_of(ks + u * RP_WAVES) * 32) : zero;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int jb = 0; jb < NB; ++jb) {
-        const u32x4 qf = qval[jb] ? ld16(qrow[jb] + (ks + u * RP_WAVES) * 32) : zero;
-        acc[jb] = mfma_bf16(qf, pf[u], acc[jb]);
-      }
-    }
+      for (int jb = 0; jb < NB; ++jb)
+        qf[u][jb] = qload(jb, step_of(ks + u * RP_WAVES));
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb) acc[jb] = mfma_bf16(qf[u][jb], pf[u], acc[jb]);
   }
   for (; ks < nsteps; ks += RP_WAVES) {
-    const u32x4 pf = mval ? ld16(prow + ks * 32) : zero;
+    const int k = ks < full ? step_of(ks) : ks;
+    const u32x4 pf = mval ? ld16(prow + k * 32) : zero;
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb) {
-      const u32x4 qf = qval[jb] ? ld16(qrow[jb] + ks * 32) : zero;
-      acc[jb] = mfma_bf16(qf, pf, acc[jb]);
+      acc[jb] = mfma_bf16(qload(jb, k), pf, acc[jb]);
     }
   }
 
@@ -107,8 +140,18 @@ struct ColProjTile {
   static constexpr int SBYTES = RP * MS * 2;             // one of hi / lo
 };
 
+struct ColProjBatch {
+  ColProjParams job[kColProjBatch];
+  int first[kColProjBatch + 1];   // grid.y rows [first[i], first[i+1]) are the splits of job i
+};
+
 template <int RP>
-__global__ __launch_bounds__(256) void colproj_kernel(const ColProjParams p) {
+__global__ __launch_bounds__(256) void colproj_kernel(const ColProjBatch batch) {
+  const int y = blockIdx.y;
+  const int jobi = y >= batch.first[2] ? 2 : (y >= batch.first[1] ? 1 : 0);
+  const ColProjParams& p = batch.job[jobi];
+  const int split = y - batch.first[jobi];
+  if ((int)blockIdx.x * 64 >= p.C) return;
   using T = ColProjTile<RP>;
   constexpr int NB = RP / 16;
   constexpr int MS = T::MS;
@@ -116,11 +159,11 @@ __global__ __launch_bounds__(256) void colproj_kernel(const ColProjParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t xt[T::XBYTES];
   __shared__ __attribute__((aligned(16))) uint16_t shi[RP * MS];
   __shared__ __attribute__((aligned(16))) uint16_t slo[RP * MS];
-  __shared__ float csred[32][64 + 1];
+  static_assert(T::XBYTES >= 32 * 65 * 4, "column-sum scratch reuses the X tile");
+  float (*csred)[65] = reinterpret_cast<float (*)[65]>(xt);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
   const int c0 = blockIdx.x * 64;
-  const int split = blockIdx.y;
   const int mbeg = split * p.msplit;
   const int mend = min(p.M, mbeg + p.msplit);
 
@@ -172,16 +215,36 @@ __global__ __launch_bounds__(256) void colproj_kernel(const ColProjParams p) {
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc) *reinterpret_cast<u32x4*>(xt + xt_off(cb * 8 + cc, mg, ROWB)) = cols[cc];
     }
-    // ---- S[sub .. sub+MS, 0 .. R) -> LDS as bf16 hi / lo, transposed [j][m]
-    for (int idx = tid; idx < MS * RP; idx += 256) {
-      const int j = idx / MS, mm = idx % MS;   // consecutive threads: consecutive rows m
+    // ---- S[sub .. sub+MS, 0 .. R) -> LDS as bf16 hi / lo, transposed [j][m]:
+    // thread t takes row t % MS and a quarter of the columns, 16-byte loads
+    {
+      constexpr int TPR = 256 / MS;                 // threads per row (1 or 2)
+      const int mm = tid % MS, part = tid / MS;
       const int m = sub + mm;
-      float v = 0.f;
-      if (j < p.R && m < mend) v = p.S[(size_t)m * p.lds + j] * p.s_in;
-      const uint32_t h = f32_to_bf16_bits(v);
-      const int off = (xt_off(j, mm >> 3, ROWB) >> 1) + (mm & 7);   // same swizzle as the X tile
-      shi[off] = (uint16_t)h;
-      slo[off] = (uint16_t)f32_to_bf16_bits(v - __uint_as_float(h << 16));
+      const bool rv = m < mend;
+      const bool vec = (p.lds % 4) == 0;
+#pragma unroll
+      for (int q = part * 4; q < RP; q += 4 * TPR) {
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (rv && q < p.R) {
+          const float* src = p.S + (size_t)m * p.lds + q;
+          if (vec && q + 4 <= p.R) {
+            const f32x4 t = *reinterpret_cast<const f32x4*>(src);
+            v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (q + e < p.R) ? src[e] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = v[e] * p.s_in;
+          const uint32_t h = f32_to_bf16_bits(x);
+          const int off = (xt_off(q + e, mm >> 3, ROWB) >> 1) + (mm & 7);   // same swizzle as the X tile
+          shi[off] = (uint16_t)h;
+          slo[off] = (uint16_t)f32_to_bf16_bits(x - __uint_as_float(h << 16));
+        }
+      }
     }
     __syncthreads();
 
@@ -229,17 +292,54 @@ __global__ __launch_bounds__(256) void colproj_kernel(const ColProjParams p) {
 // Threads walk the partial buffer in its own order ([C][rp], j fastest) so the
 // split reads are coalesced; `trans` selects whether the partial's column index
 // (j) is the output row (dA = part^T) or the output column (dB).
-__global__ void reduce_parts_kernel(const ReduceParams p) {
+struct ReduceBatch {
+  ReduceParams job[2];
+  int njobs;
+  int blocks0;                    // blocks [0, blocks0) reduce job 0, the rest job 1
+};
+
+// One block per 64 partial rows c of one job: the [64][rp] slices of all splits
+// are summed in split order (float4 loads, coalesced), staged in LDS, then written
+// out with the finishing terms, consecutive threads on consecutive output columns.
+__global__ __launch_bounds__(256) void reduce_parts_kernel(const ReduceBatch batch) {
+  __shared__ float tile[64 * 129];
+  const int jobi = (int)blockIdx.x >= batch.blocks0 ? 1 : 0;
+  const ReduceParams& p = batch.job[jobi];
+  const int c0 = ((int)blockIdx.x - (jobi ? batch.blocks0 : 0)) * 64;
   const int C = p.trans ? p.cols : p.rows;          // partial rows
   const int R = p.trans ? p.rows : p.cols;          // valid partial columns
-  const size_t total = (size_t)C * p.rp;
-  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += (size_t)gridDim.x * blockDim.x) {
-    const int c = (int)(idx / p.rp), j = (int)(idx % p.rp);
-    if (j >= R) continue;
-    float acc = 0.f;
-    for (int s = 0; s < p.nsplit; ++s) acc += p.part[(size_t)s * p.pstride + idx];
+  if (c0 >= C) return;
+  const int tid = threadIdx.x;
+  const int ld = p.rp + 1;
+  const int nvec = p.rp / 16;                       // float4 per thread: 64 * rp / 4 / 256
+  for (int v = 0; v < nvec; ++v) {
+    const int e = (v * 256 + tid) * 4;              // element offset inside the [64][rp] slice
+    const int cc = e / p.rp, j = e % p.rp;
+    f32x4 acc = {0, 0, 0, 0};
+    if (c0 + cc < C && j < R) {                     // columns >= R are padding (or another job's)
+      const float* src = p.part + (size_t)(c0 + cc) * p.rp + j;
+      int sp = 0;
+      for (; sp + 4 <= p.nsplit; sp += 4) {
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(src + (size_t)(sp + 0) * p.pstride);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(src + (size_t)(sp + 1) * p.pstride);
+        const f32x4 a2 = *reinterpret_cast<const f32x4*>(src + (size_t)(sp + 2) * p.pstride);
+        const f32x4 a3 = *reinterpret_cast<const f32x4*>(src + (size_t)(sp + 3) * p.pstride);
+        acc += a0; acc += a1; acc += a2; acc += a3;
+      }
+      for (; sp < p.nsplit; ++sp) acc += *reinterpret_cast<const f32x4*>(src + (size_t)sp * p.pstride);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tile[cc * ld + j + i] = acc[i];
+  }
+  __syncthreads();
+  const int nc = C - c0 < 64 ? C - c0 : 64;
+  for (int e = tid; e < R * 64; e += 256) {
+    int cc, j;
+    if (p.trans) { j = e >> 6; cc = e & 63; } else { cc = e / R; j = e % R; }
+    if (cc >= nc) continue;
+    const int c = c0 + cc;
     const int row = p.trans ? j : c, col = p.trans ? c : j;
-    float v = acc * p.alpha;
+    float v = tile[cc * ld + j] * p.alpha;
     if (p.rowscale != nullptr) v *= p.rowscale[row];
     if (p.Qm != nullptr) {
       float t = 0.f;
@@ -256,17 +356,6 @@ __global__ void reduce_colsum_kernel(const float* cspart, int nsplit, int C, flo
   float acc = 0.f;
   for (int s = 0; s < nsplit; ++s) acc += cspart[(size_t)s * C + c];
   out[c] = acc;
-}
-
-// Bt[j, n] = bf16(B[n, j] * (scale ? scale[n] : 1)), B [N, r] bf16 -> Bt [r, N] bf16.
-__global__ void transpose_scale_kernel(const uint16_t* B, const float* scale, int N, int r, uint16_t* Bt) {
-  const int n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n >= N) return;
-  const float sc = scale ? scale[n] : 1.f;
-  for (int j = 0; j < r; ++j) {
-    const float v = bf16_to_f32(B[(size_t)n * r + j]);
-    Bt[(size_t)j * N + n] = scale ? (uint16_t)f32_to_bf16_bits(v * sc) : B[(size_t)n * r + j];
-  }
 }
 
 __global__ void fill_zero_kernel(float* p, size_t n) {
@@ -310,33 +399,75 @@ void colproj_plan(int M, int C, int* nsplit, int* msplit) {
   if (*nsplit < 1) *nsplit = 1;
 }
 
-hipError_t launch_colproj(const ColProjParams& p, int nsplit, hipStream_t st) {
-  const dim3 grid((p.C + 63) / 64, nsplit), block(256);
-  switch (colproj_rp(p.R)) {
-    case 16: hipLaunchKernelGGL(colproj_kernel<16>, grid, block, 0, st, p); break;
-    case 32: hipLaunchKernelGGL(colproj_kernel<32>, grid, block, 0, st, p); break;
-    case 64: hipLaunchKernelGGL(colproj_kernel<64>, grid, block, 0, st, p); break;
-    default: hipLaunchKernelGGL(colproj_kernel<128>, grid, block, 0, st, p); break;
+static hipError_t colproj_launch(const ColProjBatch& b, int gx, int gy, int R, hipStream_t st) {
+  const dim3 grid(gx, gy), block(256);
+  switch (colproj_rp(R)) {
+    case 16: hipLaunchKernelGGL(colproj_kernel<16>, grid, block, 0, st, b); break;
+    case 32: hipLaunchKernelGGL(colproj_kernel<32>, grid, block, 0, st, b); break;
+    case 64: hipLaunchKernelGGL(colproj_kernel<64>, grid, block, 0, st, b); break;
+    default: hipLaunchKernelGGL(colproj_kernel<128>, grid, block, 0, st, b); break;
   }
   return hipGetLastError();
 }
 
+hipError_t launch_colproj_batch(const ColProjParams* jobs, const int* nsplit, int njobs, hipStream_t st) {
+  if (njobs < 1 || njobs > kColProjBatch) return hipErrorInvalidValue;
+  for (int i = 1; i < njobs; ++i)
+    if (colproj_rp(jobs[i].R) != colproj_rp(jobs[0].R)) {      // one rank padding per launch
+      for (int k = 0; k < njobs; ++k) {
+        const hipError_t e = launch_colproj_batch(jobs + k, nsplit + k, 1, st);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    }
+  ColProjBatch b;
+  int maxc = 0;
+  b.first[0] = 0;
+  for (int i = 0; i < kColProjBatch; ++i) {
+    b.job[i] = jobs[i < njobs ? i : 0];
+    b.first[i + 1] = b.first[i] + (i < njobs ? nsplit[i] : 0);
+    if (i < njobs && jobs[i].C > maxc) maxc = jobs[i].C;
+  }
+  return colproj_launch(b, (maxc + 63) / 64, b.first[njobs], jobs[0].R, st);
+}
+
+hipError_t launch_colproj(const ColProjParams& p, int nsplit, hipStream_t st) {
+  return launch_colproj_batch(&p, &nsplit, 1, st);
+}
+
+hipError_t launch_colproj2(const ColProjParams& a, int nsplit_a, const ColProjParams& b2, int nsplit_b, hipStream_t st) {
+  const ColProjParams jobs[2] = {a, b2};
+  const int ns[2] = {nsplit_a, nsplit_b};
+  return launch_colproj_batch(jobs, ns, 2, st);
+}
+
+static int reduce_blocks(const ReduceParams& p) { return ((p.trans ? p.cols : p.rows) + 63) / 64; }
+
+hipError_t launch_reduce2(const ReduceParams& a, const ReduceParams& b2, hipStream_t st) {
+  ReduceBatch b;
+  b.job[0] = a;
+  b.job[1] = b2;
+  b.njobs = 2;
+  b.blocks0 = reduce_blocks(a);
+  const int blocks = b.blocks0 + reduce_blocks(b2);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(reduce_parts_kernel, dim3(blocks), dim3(256), 0, st, b);
+  return hipGetLastError();
+}
+
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t st) {
-  const size_t total = (size_t)(p.trans ? p.cols : p.rows) * p.rp;
-  if (total == 0) return hipSuccess;
-  size_t blocks = (total + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(reduce_parts_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p);
+  ReduceBatch b;
+  b.job[0] = p;
+  b.job[1] = p;
+  b.njobs = 1;
+  b.blocks0 = reduce_blocks(p);
+  if (b.blocks0 == 0) return hipSuccess;
+  hipLaunchKernelGGL(reduce_parts_kernel, dim3(b.blocks0), dim3(256), 0, st, b);
   return hipGetLastError();
 }
 
 hipError_t launch_reduce_colsum(const float* cspart, int nsplit, int C, float* out, hipStream_t st) {
   hipLaunchKernelGGL(reduce_colsum_kernel, dim3((C + 255) / 256), dim3(256), 0, st, cspart, nsplit, C, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_scale(const uint16_t* B, const float* scale, int N, int r, uint16_t* Bt, hipStream_t st) {
-  hipLaunchKernelGGL(transpose_scale_kernel, dim3((N + 255) / 256), dim3(256), 0, st, B, scale, N, r, Bt);
   return hipGetLastError();
 }
 
