@@ -24,7 +24,7 @@ static hipError_t run(const GemmParams& p, hipStream_t st) {
 }
 
 static int pick_bn(GemmKind kind, int N) {
-  const bool wide_ok = (kind == GK_NT_PLAIN || kind == GK_NT_DORA || kind == GK_NT_SWIGLU || kind == GK_NN_PLAIN ||
+  const bool wide_ok = (kind == GK_NT_PLAIN || kind == GK_NT_DORA || kind == GK_NN_PLAIN ||
                         kind == GK_NN_SCALE || kind == GK_NN_I8_SCALE || kind == GK_NN_SWIGLU || kind == GK_NT_FUSED ||
                         kind == GK_NT_I8_DEQ || kind == GK_NT_I8_RAW);
   const bool b192_ok = (kind == GK_NT_PLAIN || kind == GK_NT_DORA || kind == GK_NN_PLAIN || kind == GK_NN_SCALE ||
@@ -67,11 +67,6 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
       if (bn == 128) return big ? run<256, 128, false, false, false, false, 0, true, EPI_DORA>(p, st)
                                 : run<128, 128, false, false, false, false, 0, true, EPI_DORA>(p, st);
       return run<128, 64, false, false, false, false, 0, true, EPI_DORA>(p, st);
-    case GK_NT_SWIGLU:
-      if (bn == 256 && big) return run<256, 256, false, false, false, false, 0, true, EPI_SWIGLU_FWD>(p, st);
-      if (bn >= 128 && big) return run<256, 128, false, false, false, false, 0, true, EPI_SWIGLU_FWD>(p, st);
-      if (bn >= 128) return run<128, 128, false, false, false, false, 0, true, EPI_SWIGLU_FWD>(p, st);
-      return run<128, 64, false, false, false, false, 0, true, EPI_SWIGLU_FWD>(p, st);
     case GK_NT_SWIGLU_DUAL:
       // output width per tile is BN / 2 (hidden units); the tile reads BN/2 gate + BN/2 up rows
       if (p.N % 128 == 0 && big) return run<256, 256, false, false, false, false, 0, true, EPI_SWIGLU_DUAL>(p, st);

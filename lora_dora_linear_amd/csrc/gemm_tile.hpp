@@ -36,7 +36,6 @@ namespace ldl {
 enum EpiKind : int {
   EPI_PLAIN = 0,      // out = acc + lora (+ bias)                         -> bf16
   EPI_DORA = 1,       // z = acc + lora; out = z * g[n] (+ bias); out2 = z -> bf16
-  EPI_SWIGLU_FWD = 2, // gu = acc + lora; h = silu(E) * gu; out2 = gu, out3 = h
   EPI_SWIGLU_BWD = 3, // dh = acc + lora; out = dh*gu*silu'(e), out2 = dh*silu(e)
   EPI_DEQUANT = 4,    // int8: acc * sx[m] * sw[n] + lora (+ bias)        -> bf16
   EPI_RAW_I32 = 5,    // int8: raw int32 product
@@ -75,6 +74,9 @@ struct GemmCfg {
   static constexpr bool kNN = NN_;          // Q is [K, N]
   static constexpr bool kBInt8 = BINT8_;    // NN: Q int8, upcast to bf16 exactly
   static constexpr bool kAScale = ASCALE_;  // NN: column scale on P
+  // NN with a plain bf16 Q: Q copied to LDS as-is ([k][n] rows) and read back
+  // transposed by ds_read_b64_tr_b16; otherwise staged through registers
+  static constexpr bool kNNTr = NN_ && !BINT8_ && !ASCALE_ && (BN_ == 64 || BN_ == 128 || BN_ == 256);
   static constexpr int kSideRsp = SIDE_RSP_;// fused side rows (padded to 16), 0: none
   static constexpr bool kSLoad = SLOAD_;    // epilogue S from global
   static constexpr int kEpi = EPI_;
@@ -91,6 +93,15 @@ __device__ __forceinline__ u32x4 lds_ld16(const uint8_t* base, int off) {
 }
 __device__ __forceinline__ void lds_st16(uint8_t* base, int off, u32x4 v) {
   *reinterpret_cast<u32x4*>(base + off) = v;
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes the
+// 16 eight-byte reads form a 16 x 4 matrix D (lane j's read is row j); lane
+// 4a + b of the group receives D[a][b], D[a+4][b], D[a+8][b], D[a+12][b].
+__device__ __forceinline__ u32x2 lds_tr16(const uint8_t* base, int off) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(base + off));
+  return __builtin_bit_cast(u32x2, v);
 }
 
 // Element (n, j) of the epilogue up-matrix as bf16 bits (zero outside [0, r_epi)).
@@ -121,9 +132,15 @@ __device__ __forceinline__ u32x4 e_frag(const GemmParams& p, int n, int j0) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-// Direct buffer -> LDS copy of 16 bytes per lane; lane l lands at lds_base + 16*l.
+// Direct buffer -> LDS copy of 16 bytes per lane; lane l lands at lds_base + 16*l
+// (lds_base wave-uniform, taken from M0).  Written as inline assembly so that
+// the compiler does not treat the copy as an LDS store it must wait for before
+// every later LDS read: the copies always target the stage that no wave is
+// reading, and the kernel waits for them itself (vmcnt(0) + barrier) before
+// that stage is read.
 __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, soff, 0, 0);
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_base;
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(lds_addr) : "memory");
 }
 
 template <class C>
@@ -141,9 +158,11 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
   static_assert(!NN || !I8, "NN takes bf16 P");
   using Acc = typename std::conditional<I8, i32x16, f32x16>::type;
 
-  // two LDS stages, each [BM rows of P | BN rows of Q | RSP side rows] x 128 bytes
-  __shared__ __attribute__((aligned(16))) uint8_t smem0[GemmSmem<C>::kBuf];
-  __shared__ __attribute__((aligned(16))) uint8_t smem1[GemmSmem<C>::kBuf];
+  // two LDS stages, each [BM rows of P | BN rows of Q | RSP side rows] x 128 bytes;
+  // the epilogue reuses both as one output staging tile
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * GemmSmem<C>::kBuf];
+  uint8_t* const smem0 = smem;
+  uint8_t* const smem1 = smem + GemmSmem<C>::kBuf;
 
   const int M = p.M, N = p.N, K = p.K;
   // Dual gate/up tile: BN rows of Q = BN/2 gate rows and the BN/2 up rows of the
@@ -184,12 +203,22 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
   // >= M, side rows >= r) read as zero through the buffer bounds.
   const int lrow = lane >> 3, lphys = lane & 7;
   constexpr int A_INST = BM / (8 * NW);       // per wave
-  constexpr int B_INST = NN ? 0 : BN / (8 * NW);
+  constexpr bool NNTR = C::kNNTr;
+  // NN-tr: the Q k-tile is 64 rows of BN bf16 (BN / 8 chunks of 16 bytes per row);
+  // chunk c of row k sits at physical chunk c ^ tr_swz(k)
+  constexpr int B_INST = NNTR ? BN / (8 * NW) : (NN ? 0 : BN / (8 * NW));
   constexpr int S_INST = (RSP + 8 * NW - 1) / (8 * NW);
+  // rows k .. k+3 of one transposing read land on distinct banks
+  auto tr_swz = [](int k) { return 2 * (k & 3); };
+  // byte offset of element (k, n) (4-column aligned) in the NN-tr Q tile
+  auto tr_off = [&](int k, int n) { return k * (BN * 2) + ((((n >> 3) ^ tr_swz(k))) << 4) + ((n & 4) << 1); };
   static_assert(BM % (8 * NW) == 0 && (NN || BN % (8 * NW) == 0), "tile rows split evenly over the waves");
   const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(p.a, (uint32_t)M * lda_b);
-  const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(p.b0, NN ? 0u : (uint32_t)N * ldb_b);
-  const __amdgpu_buffer_rsrc_t rs_b2 = make_rsrc(DUAL ? p.b1 : p.b0, NN ? 0u : (uint32_t)N * ldb_b);
+  const __amdgpu_buffer_rsrc_t rs_b =
+      make_rsrc(p.b0, NNTR ? (uint32_t)p.kseg * ldb_b : (NN ? 0u : (uint32_t)N * ldb_b));
+  const __amdgpu_buffer_rsrc_t rs_b2 =
+      NNTR ? make_rsrc(p.b1, (uint32_t)(K - p.kseg) * ldb_b)
+           : make_rsrc(DUAL ? p.b1 : p.b0, NN ? 0u : (uint32_t)N * ldb_b);
   const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(p.side, RSP ? (uint32_t)p.r_side * (uint32_t)K * 2u : 0u);
   uint32_t a_off[A_INST];
 #pragma unroll
@@ -200,6 +229,12 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
   uint32_t b_off[B_INST ? B_INST : 1];
 #pragma unroll
   for (int i = 0; i < B_INST; ++i) {
+    if constexpr (NNTR) {
+      const int slot = (i * NW + wave) * 64 + lane;          // 16-byte slot of the k-tile
+      const int krow = slot / (BN / 8), phys = slot % (BN / 8);
+      b_off[i] = (uint32_t)krow * ldb_b + (uint32_t)(n0 + 8 * (phys ^ tr_swz(krow))) * 2u;
+      continue;
+    }
     const int row = (i * NW + wave) * 8 + lrow;
     int qrow = n0 + row;
     if constexpr (DUAL) {   // tile row -> (gate | up) row of hidden unit h
@@ -251,6 +286,14 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
 #pragma unroll
       for (int i = 0; i < S_INST; ++i)
         if ((i * NW + wave) * 8 < RSP) buf2lds16(rs_s, s_off[i], koff, sB + BN * 128 + (i * NW + wave) * 1024);
+    } else if constexpr (NNTR) {
+      // Q is [K, N]: rows kt*64 .. +63 of the segment that holds them (k-tiles never straddle kseg)
+      uint8_t* sB = sbuf + BM * 128;
+      const int kk0 = kt * 64;
+      const bool seg1 = kk0 >= p.kseg;
+      const uint32_t boff = (uint32_t)(seg1 ? kk0 - p.kseg : kk0) * ldb_b;
+#pragma unroll
+      for (int i = 0; i < B_INST; ++i) buf2lds16(seg1 ? rs_b2 : rs_b, b_off[i], boff, sB + (i * NW + wave) * 1024);
     } else {
       // Q is [K, N]: this k-tile covers reduction rows kt*64 .. +63.  Each thread
       // stages RPT rows x 8 columns (RPT = 8 with 256 threads, 4 with 512).
@@ -277,7 +320,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
 
   // NN only: scale (optional) and transpose the staged Q rows into LDS.
   auto store_q = [&](int kt, uint8_t* sbuf) {
-    if constexpr (NN) {
+    if constexpr (NN && !NNTR) {
       if (tid < BN * RPT_SLOTS) {
         uint8_t* sB = sbuf + BM * 128;
         const int kb = tid % (BN / 8), nb = tid / (BN / 8);
@@ -328,8 +371,22 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
     const uint8_t* sB = sbuf + BM * 128;
 #pragma unroll
     for (int i = 0; i < FM; ++i) af[i] = lds_ld16(sA, lds_off(wm * TM + i * 32 + lr, ks * 2 + lq));
+    if constexpr (NNTR) {
+      // lane l needs column wn*TN + 32 j + (l & 31) at k = 16 ks + 8 (l >> 5) + e, e < 8: its
+      // 16-lane group reads 4 k rows x 16 columns per instruction (see lds_tr16), twice
+      const int g = lane >> 4, jl = lane & 15;
+      const int kr = ks * 16 + 8 * (g >> 1) + (jl >> 2);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bf[j] = lds_ld16(sB, lds_off(wn * TN + j * 32 + lr, ks * 2 + lq));
+      for (int j = 0; j < FN; ++j) {
+        const int n = wn * TN + j * 32 + 16 * (g & 1) + 4 * (jl & 3);
+        const u32x2 lo = lds_tr16(sB, tr_off(kr, n));
+        const u32x2 hi = lds_tr16(sB, tr_off(kr + 4, n));
+        bf[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bf[j] = lds_ld16(sB, lds_off(wn * TN + j * 32 + lr, ks * 2 + lq));
+    }
     if constexpr (RSP > 0) {
 #pragma unroll
       for (int js = 0; js < RSP / 32; ++js) sf[js] = lds_ld16(sB, lds_off(BN + js * 32 + lr, ks * 2 + lq));
@@ -358,23 +415,86 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
   };
   constexpr int SF = RSP ? RSP / 32 : 1;
 
+  // Low-rank update dst[i][jj] += (s_epi * S[m, :]) . E[n, :]^T for the column blocks
+  // jc .. jc + NJ - 1 of this wave, in 16-rank MFMA steps (S rounded to bf16 after
+  // scaling; the dual gate/up tile masks the ranks of the other half).
+  auto lora_update = [&](auto& dst, auto jc_const) {
+    constexpr int jc = decltype(jc_const)::value;
+    constexpr int NJ = sizeof(dst[0]) / sizeof(dst[0][0]);
+    if (p.r_epi <= 0) return;
+    const uint16_t* sS = reinterpret_cast<const uint16_t*>(smem0);
+    const int nsteps = (p.r_epi + 15) / 16;
+    for (int t = 0; t < nsteps; ++t) {
+      const int j0 = t * 16 + lq * 8;
+      u32x4 sf[FM];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = wm * TM + i * 32 + lr;
+        sf[i] = u32x4{0, 0, 0, 0};
+        if constexpr (RSP > 0) {
+          if (j0 < RSP) sf[i] = *reinterpret_cast<const u32x4*>(sS + row * RSP + j0);
+        } else if constexpr (C::kSLoad) {
+          const int m = m0 + row;
+          if (m < M && j0 < p.r_epi) {
+            const float* src = p.S + (size_t)m * p.ld_s + j0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              // dual tile: up ranks [r, 2r) take s_up (8-rank groups never straddle r, r % 8 == 0)
+              const float sc = (DUAL && j0 >= p.e_jsplit) ? p.s_epi2 : p.s_epi;
+              const float lo = (j0 + 2 * e < p.r_epi) ? src[2 * e] * sc : 0.f;
+              const float hi = (j0 + 2 * e + 1 < p.r_epi) ? src[2 * e + 1] * sc : 0.f;
+              sf[i][e] = pack_bf16x2(lo, hi);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) {
+        u32x4 ef;
+        if constexpr (DUAL) {
+          // gate blocks take ranks [0, r) of Bg, up blocks ranks [r, 2r) of Bu
+          constexpr int HB = FN / 2;
+          const bool upb = (jc + jj) >= HB;
+          const int h = n0 + wn * (OUT_BN / WN) + ((jc + jj) % HB) * 32 + lr;
+          const bool mine = upb ? (j0 >= p.e_jsplit) : (j0 < p.e_jsplit);
+          ef = mine ? e_frag(p, h, j0) : u32x4{0, 0, 0, 0};
+        } else {
+          ef = e_frag(p, n0 + wn * TN + (jc + jj) * 32 + lr, j0);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) dst[i][jj] = mfma32_bf16(ef, sf[i], dst[i][jj]);
+      }
+    }
+  };
+  // bf16 tiles with a precomputed S start their accumulators from the low-rank
+  // product (computed while the first stage's copies are in flight) instead of
+  // adding it in the epilogue
+  constexpr bool SEED = !I8 && RSP == 0 && C::kSLoad;
+
   // ---------------------------------------------------------------- main loop
-  // Stage kt lives in smem[kt & 1].  Per k-tile: wait for the stage's copies,
-  // barrier (which also retires every read of the other stage), start the
-  // copies of the next stage, then run the MFMAs of this one.  (A single
-  // call site for compute() keeps the accumulators in place; unrolling the
-  // two stages made the register allocator rotate them every iteration.)
+  // Stage kt lives in smem[kt & 1].  The hand-over to the next stage sits
+  // between the last two MFMA steps of a k-tile: wait for the next stage's
+  // copies, barrier (every wave has finished reading this stage, so its
+  // buffer can take the copies of stage kt + 2), start those copies and the
+  // LDS reads of the next stage's first step, then run this stage's last
+  // MFMAs, which hide the barrier and the LDS latency.  (A single call site
+  // per step keeps the accumulators in place; unrolling the two stages made
+  // the register allocator rotate them every iteration.)
   const int KT = K / BK;
+  u32x4 fa0[FM], fb0[FN], fs0[SF], fa1[FM], fb1[FN], fs1[SF];
   issue_loads(0, smem0);
+  if constexpr (SEED) lora_update(acc, std::integral_constant<int, 0>{});
   store_q(0, smem0);
-  for (int kt = 0; kt < KT; ++kt) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    uint8_t* cur = (kt & 1) ? smem1 : smem0;
-    uint8_t* nxt = (kt & 1) ? smem0 : smem1;
-    if (kt + 1 < KT) issue_loads(kt + 1, nxt);
-    u32x4 fa0[FM], fb0[FN], fs0[SF], fa1[FM], fb1[FN], fs1[SF];
-    load_frags(cur, 0, fa0, fb0, fs0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (KT > 1) issue_loads(1, smem1);
+  load_frags(smem0, 0, fa0, fb0, fs0);
+  // settle every LDS / scalar read of the prologue (not the copies in flight)
+  // so that the waits inside the loop can count the fragment reads exactly
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  // steps 0..2 of stage kt (step 0's fragments already in fa0), leaving step 3's in fa1
+  auto first_steps = [&](int kt, uint8_t* cur, uint8_t* nxt, bool more) {
+    __builtin_amdgcn_sched_barrier(0);
     load_frags(cur, 1, fa1, fb1, fs1);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(fa0, fb0, fs0);
@@ -383,11 +503,26 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
     __builtin_amdgcn_sched_barrier(0);
     mfmas(fa1, fb1, fs1);
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < KT) store_q(kt + 1, nxt);
+    if (more) store_q(kt + 1, nxt);
     load_frags(cur, 3, fa1, fb1, fs1);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(fa0, fb0, fs0);
     __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int kt = 0; kt + 1 < KT; ++kt) {
+    uint8_t* cur = (kt & 1) ? smem1 : smem0;
+    uint8_t* nxt = (kt & 1) ? smem0 : smem1;
+    first_steps(kt, cur, nxt, true);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 2 < KT) issue_loads(kt + 2, cur);
+    load_frags(nxt, 0, fa0, fb0, fs0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(fa1, fb1, fs1);
+  }
+  {
+    uint8_t* cur = ((KT - 1) & 1) ? smem1 : smem0;
+    first_steps(KT - 1, cur, cur, false);
     mfmas(fa1, fb1, fs1);
   }
   __syncthreads();
@@ -431,174 +566,206 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
   // fp32 copy of an int32 tile never doubles the live registers.
   constexpr int JC = I8 ? 1 : FN;
   static_assert(FN % JC == 0, "column chunking");
-  auto epilogue_chunk = [&](auto jc_const) {
+  constexpr int EPI = C::kEpi;
+  // bf16 outputs go through LDS (one output array at a time) and leave the
+  // tile as whole 16-byte row segments; the raw int32 product and the fused
+  // side path (whose U tile occupies LDS) store straight from registers.
+  constexpr bool STAGE = (RSP == 0) && (EPI != EPI_RAW_I32);
+  constexpr int NOUT = (EPI == EPI_SWIGLU_DUAL) ? 3 : ((EPI == EPI_DORA || EPI == EPI_SWIGLU_BWD) ? 2 : 1);
+  static_assert(!STAGE || NOUT == 1 || JC == FN, "several staged outputs need the whole tile in registers");
+  static_assert(!STAGE || (size_t)BM * OUT_BN * 2 <= 2 * (size_t)GemmSmem<C>::kBuf, "staging tile fits in LDS");
+  constexpr int NCH = OUT_BN / 8;                         // 16-byte chunks per staged row
+  constexpr int SWM = (NCH & (NCH - 1)) == 0 ? (NCH < 32 ? NCH - 1 : 31) : 7;
+
+  // fp32 tile of column chunk jc: accumulator (dequantised for int8) plus the rank-r update
+  auto make_facc = [&](auto jc_const, f32x16 (&facc)[FM][JC]) {
     constexpr int jc = decltype(jc_const)::value;
-    if constexpr (C::kEpi == EPI_RAW_I32) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int m = mrow_base + i * 32 + lr;
-        if (m >= M) continue;
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int jj = 0; jj < JC; ++jj)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int n = ncol_base + (jc + jj) * 32 + 8 * g;
-            const Acc& a = acc[i][jc + jj];
-            *reinterpret_cast<i32x4*>(static_cast<int32_t*>(p.out) + (size_t)m * p.ldo + n) =
-                i32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-          }
-      }
-    } else {
-      f32x16 facc[FM][JC];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int jj = 0; jj < JC; ++jj) {
-          if constexpr (I8) {
-            const int m = mrow_base + i * 32 + lr;
-            const float sxm = (m < M) ? p.row_scale[m] : 0.f;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const f32x4 swn = *reinterpret_cast<const f32x4*>(p.col_scale + ncol_base + (jc + jj) * 32 + 8 * g);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) facc[i][jj][4 * g + e] = float(acc[i][jc + jj][4 * g + e]) * sxm * swn[e];
-            }
-          } else {
-            facc[i][jj] = acc[i][jc + jj];
-          }
-        }
-
-      if (p.r_epi > 0) {
-        const uint16_t* sS = reinterpret_cast<const uint16_t*>(smem0);
-        const int nsteps = (p.r_epi + 15) / 16;
-        for (int t = 0; t < nsteps; ++t) {
-          const int j0 = t * 16 + lq * 8;
-          u32x4 sf[FM];
-#pragma unroll
-          for (int i = 0; i < FM; ++i) {
-            const int row = wm * TM + i * 32 + lr;
-            sf[i] = u32x4{0, 0, 0, 0};
-            if constexpr (RSP > 0) {
-              if (j0 < RSP) sf[i] = *reinterpret_cast<const u32x4*>(sS + row * RSP + j0);
-            } else if constexpr (C::kSLoad) {
-              const int m = m0 + row;
-              if (m < M && j0 < p.r_epi) {
-                const float* src = p.S + (size_t)m * p.ld_s + j0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  // dual tile: up ranks [r, 2r) take s_up (8-rank groups never straddle r, r % 8 == 0)
-                  const float sc = (DUAL && j0 >= p.e_jsplit) ? p.s_epi2 : p.s_epi;
-                  const float lo = (j0 + 2 * e < p.r_epi) ? src[2 * e] * sc : 0.f;
-                  const float hi = (j0 + 2 * e + 1 < p.r_epi) ? src[2 * e + 1] * sc : 0.f;
-                  sf[i][e] = pack_bf16x2(lo, hi);
-                }
-              }
-            }
-          }
-#pragma unroll
-          for (int jj = 0; jj < JC; ++jj) {
-            u32x4 ef;
-            if constexpr (DUAL) {
-              // gate blocks take ranks [0, r) of Bg, up blocks ranks [r, 2r) of Bu
-              constexpr int HB = FN / 2;
-              const bool upb = (jc + jj) >= HB;
-              const int h = n0 + wn * (OUT_BN / WN) + ((jc + jj) % HB) * 32 + lr;
-              const bool mine = upb ? (j0 >= p.e_jsplit) : (j0 < p.e_jsplit);
-              ef = mine ? e_frag(p, h, j0) : u32x4{0, 0, 0, 0};
-            } else {
-              ef = e_frag(p, n0 + wn * TN + (jc + jj) * 32 + lr, j0);
-            }
-#pragma unroll
-            for (int i = 0; i < FM; ++i) facc[i][jj] = mfma32_bf16(ef, sf[i], facc[i][jj]);
-          }
-        }
-      }
-
-      // stores: lane holds row m and four groups of four consecutive columns
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int m = mrow_base + i * 32 + lr;
-        if (m >= M) continue;
-#pragma unroll
-        for (int jj = 0; jj < JC; ++jj) {
+      for (int jj = 0; jj < JC; ++jj) {
+        if constexpr (I8) {
+          const int m = mrow_base + i * 32 + lr;
+          const float sxm = (m < M) ? p.row_scale[m] : 0.f;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int n = ncol_base + (jc + jj) * 32 + 8 * g;
-            const f32x16& va = facc[i][jj];
-            const float v[4] = {va[4 * g], va[4 * g + 1], va[4 * g + 2], va[4 * g + 3]};
-            float bias4[4] = {0.f, 0.f, 0.f, 0.f};
-            if (p.bias != nullptr) {
-              const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n);
-              bias4[0] = bf16_lo(bb[0]); bias4[1] = bf16_hi(bb[0]);
-              bias4[2] = bf16_lo(bb[1]); bias4[3] = bf16_hi(bb[1]);
-            }
-            if constexpr (DUAL) {
-              if (jj >= FN / 2) continue;
-              const f32x16& vu = facc[i][jj + FN / 2];
-              const float u4[4] = {vu[4 * g], vu[4 * g + 1], vu[4 * g + 2], vu[4 * g + 3]};
-              u32x2 e2, u2, h2;
-              e2[0] = pack_bf16x2(v[0], v[1]);
-              e2[1] = pack_bf16x2(v[2], v[3]);
-              u2[0] = pack_bf16x2(u4[0], u4[1]);
-              u2[1] = pack_bf16x2(u4[2], u4[3]);
-              h2[0] = pack_bf16x2(silu_f(v[0]) * u4[0], silu_f(v[1]) * u4[1]);
-              h2[1] = pack_bf16x2(silu_f(v[2]) * u4[2], silu_f(v[3]) * u4[3]);
-              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (size_t)m * p.ldo + n) = e2;
-              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out2) + (size_t)m * p.ldo2 + n) = u2;
-              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out3) + (size_t)m * p.ldo3 + n) = h2;
-            } else if constexpr (C::kEpi == EPI_PLAIN || C::kEpi == EPI_DEQUANT) {
-              u32x2 w;
-              w[0] = pack_bf16x2(v[0] + bias4[0], v[1] + bias4[1]);
-              w[1] = pack_bf16x2(v[2] + bias4[2], v[3] + bias4[3]);
-              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (size_t)m * p.ldo + n) = w;
-            } else if constexpr (C::kEpi == EPI_DORA) {
-              const f32x4 gs = *reinterpret_cast<const f32x4*>(p.col_scale + n);
-              u32x2 w, z;
-              z[0] = pack_bf16x2(v[0], v[1]);
-              z[1] = pack_bf16x2(v[2], v[3]);
-              w[0] = pack_bf16x2(v[0] * gs[0] + bias4[0], v[1] * gs[1] + bias4[1]);
-              w[1] = pack_bf16x2(v[2] * gs[2] + bias4[2], v[3] * gs[3] + bias4[3]);
-              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (size_t)m * p.ldo + n) = w;
-              if (p.out2 != nullptr)
-                *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out2) + (size_t)m * p.ldo2 + n) = z;
-            } else if constexpr (C::kEpi == EPI_SWIGLU_FWD) {
-              const u32x2 ee = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux0) + (size_t)m * p.ld_aux0 + n);
-              const float e4[4] = {bf16_lo(ee[0]), bf16_hi(ee[0]), bf16_lo(ee[1]), bf16_hi(ee[1])};
-              u32x2 gu, h;
-              gu[0] = pack_bf16x2(v[0], v[1]);
-              gu[1] = pack_bf16x2(v[2], v[3]);
-              h[0] = pack_bf16x2(silu_f(e4[0]) * v[0], silu_f(e4[1]) * v[1]);
-              h[1] = pack_bf16x2(silu_f(e4[2]) * v[2], silu_f(e4[3]) * v[3]);
-              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out2) + (size_t)m * p.ldo2 + n) = gu;
-              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out3) + (size_t)m * p.ldo3 + n) = h;
-            } else if constexpr (C::kEpi == EPI_SWIGLU_BWD) {
-              const u32x2 ee = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux0) + (size_t)m * p.ld_aux0 + n);
-              const u32x2 gg = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux1) + (size_t)m * p.ld_aux1 + n);
-              const float e4[4] = {bf16_lo(ee[0]), bf16_hi(ee[0]), bf16_lo(ee[1]), bf16_hi(ee[1])};
-              const float g4[4] = {bf16_lo(gg[0]), bf16_hi(gg[0]), bf16_lo(gg[1]), bf16_hi(gg[1])};
-              float de[4], dgu[4];
+            const f32x4 swn = *reinterpret_cast<const f32x4*>(p.col_scale + ncol_base + (jc + jj) * 32 + 8 * g);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float sg = sigmoid_f(e4[e]);
-                de[e] = v[e] * g4[e] * sg * (1.f + e4[e] * (1.f - sg));
-                dgu[e] = v[e] * e4[e] * sg;
-              }
-              u32x2 w0, w1;
-              w0[0] = pack_bf16x2(de[0], de[1]); w0[1] = pack_bf16x2(de[2], de[3]);
-              w1[0] = pack_bf16x2(dgu[0], dgu[1]); w1[1] = pack_bf16x2(dgu[2], dgu[3]);
-              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (size_t)m * p.ldo + n) = w0;
-              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out2) + (size_t)m * p.ldo2 + n) = w1;
-            }
+            for (int e = 0; e < 4; ++e) facc[i][jj][4 * g + e] = float(acc[i][jc + jj][4 * g + e]) * sxm * swn[e];
           }
+        } else {
+          facc[i][jj] = acc[i][jc + jj];
+        }
+      }
+    if constexpr (!SEED) lora_update(facc, jc_const);
+  };
+
+  // Output o of the four columns n .. n+3 of row m (values v), as packed bf16.
+  auto out_vals = [&](auto o_const, int m, int n, const float* v, const float* vu) -> u32x2 {
+    constexpr int o = decltype(o_const)::value;
+    u32x2 w;
+    if constexpr (DUAL) {            // o: 0 e, 1 u, 2 silu(e) * u
+      if constexpr (o == 0) { w[0] = pack_bf16x2(v[0], v[1]); w[1] = pack_bf16x2(v[2], v[3]); }
+      else if constexpr (o == 1) { w[0] = pack_bf16x2(vu[0], vu[1]); w[1] = pack_bf16x2(vu[2], vu[3]); }
+      else {
+        w[0] = pack_bf16x2(silu_f(v[0]) * vu[0], silu_f(v[1]) * vu[1]);
+        w[1] = pack_bf16x2(silu_f(v[2]) * vu[2], silu_f(v[3]) * vu[3]);
+      }
+    } else if constexpr (EPI == EPI_PLAIN || EPI == EPI_DEQUANT || EPI == EPI_DORA) {
+      float b4[4] = {0.f, 0.f, 0.f, 0.f};
+      if (p.bias != nullptr && !(EPI == EPI_DORA && o == 1)) {
+        const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n);
+        b4[0] = bf16_lo(bb[0]); b4[1] = bf16_hi(bb[0]); b4[2] = bf16_lo(bb[1]); b4[3] = bf16_hi(bb[1]);
+      }
+      if constexpr (EPI == EPI_DORA && o == 0) {   // y = z * g + bias
+        const f32x4 gs = *reinterpret_cast<const f32x4*>(p.col_scale + n);
+        w[0] = pack_bf16x2(v[0] * gs[0] + b4[0], v[1] * gs[1] + b4[1]);
+        w[1] = pack_bf16x2(v[2] * gs[2] + b4[2], v[3] * gs[3] + b4[3]);
+      } else {                                     // plain / dequantised output, or DoRA's z
+        w[0] = pack_bf16x2(v[0] + b4[0], v[1] + b4[1]);
+        w[1] = pack_bf16x2(v[2] + b4[2], v[3] + b4[3]);
+      }
+    } else if constexpr (EPI == EPI_SWIGLU_BWD) {  // o: 0 de, 1 dgu
+      const u32x2 ee = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux0) + (size_t)m * p.ld_aux0 + n);
+      const float e4[4] = {bf16_lo(ee[0]), bf16_hi(ee[0]), bf16_lo(ee[1]), bf16_hi(ee[1])};
+      float r4[4];
+      if constexpr (o == 0) {
+        const u32x2 gg = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux1) + (size_t)m * p.ld_aux1 + n);
+        const float g4[4] = {bf16_lo(gg[0]), bf16_hi(gg[0]), bf16_lo(gg[1]), bf16_hi(gg[1])};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sg = sigmoid_f(e4[e]);
+          r4[e] = v[e] * g4[e] * sg * (1.f + e4[e] * (1.f - sg));
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r4[e] = v[e] * e4[e] * sigmoid_f(e4[e]);
+      }
+      w[0] = pack_bf16x2(r4[0], r4[1]);
+      w[1] = pack_bf16x2(r4[2], r4[3]);
+    }
+    return w;
+  };
+  auto out_ptr = [&](int o) -> uint16_t* {
+    return static_cast<uint16_t*>(o == 0 ? p.out : (o == 1 ? p.out2 : p.out3));
+  };
+  auto out_ld = [&](int o) -> int { return o == 0 ? p.ldo : (o == 1 ? p.ldo2 : p.ldo3); };
+
+  // Visit the 4-column groups of column chunk jc: f(i, jj, g, m, n_global, col_local, v, vu).
+  auto for_groups = [&](auto jc_const, const f32x16 (&facc)[FM][JC], auto&& f) {
+    constexpr int jc = decltype(jc_const)::value;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = mrow_base + i * 32 + lr;
+#pragma unroll
+      for (int jj = 0; jj < JC; ++jj) {
+        if constexpr (DUAL) {
+          if (jc + jj >= FN / 2) continue;
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int cl = wn * (OUT_BN / WN) + (jc + jj) * 32 + 8 * g + 4 * lq;
+          const f32x16& va = facc[i][jj];
+          const float v[4] = {va[4 * g], va[4 * g + 1], va[4 * g + 2], va[4 * g + 3]};
+          float vu[4] = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (DUAL) {
+            const f32x16& vb = facc[i][jj + FN / 2];
+            vu[0] = vb[4 * g]; vu[1] = vb[4 * g + 1]; vu[2] = vb[4 * g + 2]; vu[3] = vb[4 * g + 3];
+          }
+          f(m, n0 + cl, cl, v, vu);
         }
       }
     }
   };
-  epilogue_chunk(std::integral_constant<int, 0>{});
-  if constexpr (JC < FN) epilogue_chunk(std::integral_constant<int, JC>{});
-  if constexpr (2 * JC < FN) epilogue_chunk(std::integral_constant<int, 2 * JC>{});
-  if constexpr (3 * JC < FN) epilogue_chunk(std::integral_constant<int, 3 * JC>{});
-  static_assert(FN <= 4 * JC, "at most four column chunks");
+
+  if constexpr (STAGE) {
+    // staged row r, 16-byte chunk c lives at r * OUT_BN * 2 + ((c ^ (r & SWM)) << 4)
+    auto st_off = [&](int r, int col) { return r * (OUT_BN * 2) + (((col >> 3) ^ (r & SWM)) << 4) + ((col & 4) << 1); };
+    auto copy_out = [&](int o) {
+      uint16_t* dst = out_ptr(o);
+      const int ldo = out_ld(o);
+      for (int idx = tid; idx < BM * NCH; idx += C::kThreads) {
+        const int r = idx / NCH, c = idx - r * NCH;
+        if (m0 + r < M)
+          st16(dst + (size_t)(m0 + r) * ldo + n0 + c * 8, lds_ld16(smem, r * (OUT_BN * 2) + ((c ^ (r & SWM)) << 4)));
+      }
+    };
+    auto stage_out = [&](auto o_const, auto jc_const, const f32x16 (&facc)[FM][JC]) {
+      for_groups(jc_const, facc, [&](int m, int n, int cl, const float* v, const float* vu) {
+        const u32x2 w = out_vals(o_const, m, n, v, vu);
+        *reinterpret_cast<u32x2*>(smem + st_off(m - m0, cl)) = w;
+      });
+    };
+    if constexpr (JC == FN) {
+      f32x16 facc[FM][JC];
+      make_facc(std::integral_constant<int, 0>{}, facc);
+      auto pass = [&](auto o_const) {
+        constexpr int o = decltype(o_const)::value;
+        if constexpr (o < NOUT) {
+          if (o == 0 || out_ptr(o) != nullptr) {
+            if constexpr (o > 0) __syncthreads();       // the previous output has left LDS
+            stage_out(o_const, std::integral_constant<int, 0>{}, facc);
+            __syncthreads();
+            copy_out(o);
+          }
+        }
+      };
+      pass(std::integral_constant<int, 0>{});
+      pass(std::integral_constant<int, 1>{});
+      pass(std::integral_constant<int, 2>{});
+    } else {
+      // one output (int8 dequantisation): chunk by chunk into the staging tile
+      auto chunk = [&](auto jc_const) {
+        constexpr int jc = decltype(jc_const)::value;
+        if constexpr (jc < FN) {
+          f32x16 facc[FM][JC];
+          make_facc(jc_const, facc);
+          stage_out(std::integral_constant<int, 0>{}, jc_const, facc);
+        }
+      };
+      chunk(std::integral_constant<int, 0>{});
+      chunk(std::integral_constant<int, JC>{});
+      chunk(std::integral_constant<int, 2 * JC>{});
+      chunk(std::integral_constant<int, 3 * JC>{});
+      static_assert(FN <= 4 * JC, "at most four column chunks");
+      __syncthreads();
+      copy_out(0);
+    }
+  } else if constexpr (EPI == EPI_RAW_I32) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = mrow_base + i * 32 + lr;
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = ncol_base + j * 32 + 8 * g;
+          const Acc& a = acc[i][j];
+          *reinterpret_cast<i32x4*>(static_cast<int32_t*>(p.out) + (size_t)m * p.ldo + n) =
+              i32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+        }
+    }
+  } else {
+    // fused side path (plain output only): straight from registers
+    static_assert(EPI == EPI_PLAIN, "fused side tiles have the plain epilogue");
+    auto chunk = [&](auto jc_const) {
+      constexpr int jc = decltype(jc_const)::value;
+      if constexpr (jc < FN) {
+        f32x16 facc[FM][JC];
+        make_facc(jc_const, facc);
+        for_groups(jc_const, facc, [&](int m, int n, int cl, const float* v, const float* vu) {
+          if (m < M)
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (size_t)m * p.ldo + n) =
+                out_vals(std::integral_constant<int, 0>{}, m, n, v, vu);
+        });
+      }
+    };
+    chunk(std::integral_constant<int, 0>{});
+    chunk(std::integral_constant<int, JC>{});
+    chunk(std::integral_constant<int, 2 * JC>{});
+    chunk(std::integral_constant<int, 3 * JC>{});
+  }
 }
 
 }  // namespace ldl

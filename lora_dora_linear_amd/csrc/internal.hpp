@@ -41,7 +41,7 @@ struct ReduceParams {
 
 // GEMM tile families (see gemm_tile.hpp); selected by the entry points.
 enum GemmKind : int {
-  GK_NT_PLAIN, GK_NT_FUSED, GK_NT_DORA, GK_NT_SWIGLU, GK_NT_SWIGLU_DUAL, GK_NT_I8_DEQ, GK_NT_I8_RAW,
+  GK_NT_PLAIN, GK_NT_FUSED, GK_NT_DORA, GK_NT_SWIGLU_DUAL, GK_NT_I8_DEQ, GK_NT_I8_RAW,
   GK_NN_PLAIN, GK_NN_SCALE, GK_NN_I8_SCALE, GK_NN_SWIGLU
 };
 hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st);
