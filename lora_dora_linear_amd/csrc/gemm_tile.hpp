@@ -76,7 +76,9 @@ struct GemmCfg {
   static constexpr bool kAScale = ASCALE_;  // NN: column scale on P
   // NN with a plain bf16 Q: Q copied to LDS as-is ([k][n] rows) and read back
   // transposed by ds_read_b64_tr_b16; otherwise staged through registers
-  static constexpr bool kNNTr = NN_ && !BINT8_ && !ASCALE_ && (BN_ == 64 || BN_ == 128 || BN_ == 256);
+  // (a column scale on P is then applied to the Q fragments after the read, from
+  // a 64-float slice of the scale vector copied with each stage)
+  static constexpr bool kNNTr = NN_ && !BINT8_ && (BN_ == 64 || BN_ == 128 || BN_ == 256);
   static constexpr int kSideRsp = SIDE_RSP_;// fused side rows (padded to 16), 0: none
   static constexpr bool kSLoad = SLOAD_;    // epilogue S from global
   static constexpr int kEpi = EPI_;
@@ -84,7 +86,7 @@ struct GemmCfg {
 
 template <class C>
 struct GemmSmem {
-  static constexpr int kRows = C::BM + C::BN + C::kSideRsp;
+  static constexpr int kRows = C::BM + C::BN + C::kSideRsp + ((C::kNNTr && C::kAScale) ? 8 : 0);
   static constexpr int kBuf = kRows * 128;
 };
 
@@ -220,6 +222,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
       NNTR ? make_rsrc(p.b1, (uint32_t)(K - p.kseg) * ldb_b)
            : make_rsrc(DUAL ? p.b1 : p.b0, NN ? 0u : (uint32_t)N * ldb_b);
   const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(p.side, RSP ? (uint32_t)p.r_side * (uint32_t)K * 2u : 0u);
+  constexpr bool TRSC = NNTR && C::kAScale;    // scale slice: 1 KB after the Q tile, first 256 B used
+  const __amdgpu_buffer_rsrc_t rs_c = make_rsrc(p.a_colscale, TRSC ? (uint32_t)K * 4u : 0u);
   uint32_t a_off[A_INST];
 #pragma unroll
   for (int i = 0; i < A_INST; ++i) {
@@ -294,6 +298,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
       const uint32_t boff = (uint32_t)(seg1 ? kk0 - p.kseg : kk0) * ldb_b;
 #pragma unroll
       for (int i = 0; i < B_INST; ++i) buf2lds16(seg1 ? rs_b2 : rs_b, b_off[i], boff, sB + (i * NW + wave) * 1024);
+      // scale[kt*64 ..] -> lanes 0..15 fill the slice; the rest read ahead (or zero past the end)
+      if constexpr (TRSC) {
+        if (wave == NW - 1) buf2lds16(rs_c, (uint32_t)lane * 16u, (uint32_t)kt * 256u, sB + BN * 128);
+      }
     } else {
       // Q is [K, N]: this k-tile covers reduction rows kt*64 .. +63.  Each thread
       // stages RPT rows x 8 columns (RPT = 8 with 256 threads, 4 with 512).
@@ -383,6 +391,13 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
         const u32x2 hi = lds_tr16(sB, tr_off(kr + 4, n));
         bf[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
+      if constexpr (TRSC) {
+        // Q row k scaled by scale[k]: this lane's eight reduction indices 16 ks + 8 (l >> 5) + e
+        const f32x4* sc = reinterpret_cast<const f32x4*>(sB + BN * 128 + (ks * 16 + 8 * lq) * 4);
+        const f32x4 s0 = sc[0], s1 = sc[1];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bf[j] = scale_bf16x8(bf[j], s0, s1);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < FN; ++j) bf[j] = lds_ld16(sB, lds_off(wn * TN + j * 32 + lr, ks * 2 + lq));
@@ -392,6 +407,9 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
       for (int js = 0; js < RSP / 32; ++js) sf[js] = lds_ld16(sB, lds_off(BN + js * 32 + lr, ks * 2 + lq));
     }
   };
+  // Once a wave has started a cluster of MFMAs it takes issue priority over the
+  // other wave of its SIMD until the cluster ends, so the two waves alternate
+  // between MFMA clusters and their LDS / copy work instead of interleaving both.
   auto mfmas = [&](const u32x4* af, const u32x4* bf, const u32x4* sf) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -399,6 +417,11 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
       for (int j = 0; j < FN; ++j) {
         if constexpr (I8) acc[i][j] = mfma32_i8(bf[j], af[i], acc[i][j]);
         else acc[i][j] = mfma32_bf16(bf[j], af[i], acc[i][j]);
+        if (i == 0 && j == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_setprio(1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     if constexpr (RSP > 0) {
 #pragma unroll
@@ -412,6 +435,9 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
   };
   constexpr int SF = RSP ? RSP / 32 : 1;
 
