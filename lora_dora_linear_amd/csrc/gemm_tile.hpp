@@ -97,15 +97,6 @@ __device__ __forceinline__ void lds_st16(uint8_t* base, int off, u32x4 v) {
   *reinterpret_cast<u32x4*>(base + off) = v;
 }
 
-// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes the
-// 16 eight-byte reads form a 16 x 4 matrix D (lane j's read is row j); lane
-// 4a + b of the group receives D[a][b], D[a+4][b], D[a+8][b], D[a+12][b].
-__device__ __forceinline__ u32x2 lds_tr16(const uint8_t* base, int off) {
-  typedef short v4s __attribute__((ext_vector_type(4)));
-  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(base + off));
-  return __builtin_bit_cast(u32x2, v);
-}
-
 // Element (n, j) of the epilogue up-matrix as bf16 bits (zero outside [0, r_epi)).
 __device__ __forceinline__ uint32_t e_elem(const GemmParams& p, int n, int j) {
   if (j >= p.r_epi) return 0u;
@@ -128,21 +119,6 @@ __device__ __forceinline__ u32x4 e_frag(const GemmParams& p, int n, int j0) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) v[t] = e_elem(p, n, j0 + 2 * t) | (e_elem(p, n, j0 + 2 * t + 1) << 16);
   return v;
-}
-
-// Buffer resource over [base, base + bytes): reads past the end return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-// Direct buffer -> LDS copy of 16 bytes per lane; lane l lands at lds_base + 16*l
-// (lds_base wave-uniform, taken from M0).  Written as inline assembly so that
-// the compiler does not treat the copy as an LDS store it must wait for before
-// every later LDS read: the copies always target the stage that no wave is
-// reading, and the kernel waits for them itself (vmcnt(0) + barrier) before
-// that stage is read.
-__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds_base) {
-  const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_base;
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(lds_addr) : "memory");
 }
 
 template <class C>

@@ -125,6 +125,153 @@ __global__ __launch_bounds__(512) void rowproj_kernel(const RowProjParams p) {
   }
 }
 
+// ============================================================================ rowproj (streamed)
+// Block = 16 rows of P, 4 waves.  The reduction is walked in chunks of KC
+// elements; each chunk's P rows, Q slice and k-scale slice are copied to LDS
+// by direct buffer->LDS copies (every instruction moves 1 KB of whole cache
+// lines) through a ring of STAGES buffers, so STAGES-1 chunks are in flight
+// while one is consumed.  The waves split each chunk's 32-element steps and
+// combine their partial sums at the end.  P and a row-major Q are stored with
+// 16-byte chunk c of row r at physical chunk c ^ (r & 15); a transposed Q
+// (a [K, R] matrix, rows of R bf16) is stored as-is and read back with the
+// transposing LDS read.
+template <int RP>
+struct RowStream {
+  static constexpr int KC = RP <= 32 ? 512 : (RP == 64 ? 256 : 128);   // elements per chunk
+  static constexpr int RL = KC * 2;                  // bytes per staged row
+  static constexpr int PB = 16 * RL;                 // P slice
+  static constexpr int QB = RP * RL;                 // Q slice (RP rows of KC, or KC rows of R <= RP)
+  static constexpr int GB = 4096;                    // k-scale slice: KC floats, four 1 KB copies
+  static constexpr int SB = PB + QB + GB;
+  static constexpr int STAGES = RP <= 16 ? 4 : 3;
+  static constexpr int NI = (PB + QB) / 1024 / 4 + 1;  // copy instructions per wave per chunk
+  static_assert(STAGES * SB <= 160 * 1024, "LDS ring fits");
+  static_assert((PB + QB) % 4096 == 0, "copies split evenly over the four waves");
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int RP>
+__global__ __launch_bounds__(256) void rowstream_kernel(const RowProjParams p) {
+  using T = RowStream<RP>;
+  constexpr int NB = RP / 16, KC = T::KC, RL = T::RL, SB = T::SB, ST = T::STAGES;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[ST * SB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lq = lane >> 4;
+  const int m0 = blockIdx.x * 16;
+  const int nch = (p.K + KC - 1) / KC;
+  const bool tq = p.q_trans != 0;
+
+  const uint32_t ldp_b = (uint32_t)p.ldp * 2u, ldq_b = (uint32_t)p.ldq * 2u;
+  const __amdgpu_buffer_rsrc_t rs_p = make_rsrc(p.P, (uint32_t)p.M * ldp_b);
+  const __amdgpu_buffer_rsrc_t rs_q0 =
+      make_rsrc(p.q0, tq ? (uint32_t)p.K * (uint32_t)p.R * 2u : (uint32_t)p.R0 * ldq_b);
+  const __amdgpu_buffer_rsrc_t rs_q1 = make_rsrc(p.q1, tq ? 0u : (uint32_t)(p.R - p.R0) * ldq_b);
+  const __amdgpu_buffer_rsrc_t rs_g = make_rsrc(p.q_kscale, p.q_kscale ? (uint32_t)p.K * 4u : 0u);
+
+  // per-lane source offsets of this wave's copy instructions (chunk independent)
+  constexpr int NIP = T::PB / 4096, NIQ = T::QB / 4096;
+  uint32_t p_off[NIP], q_off[NIQ];
+  bool q_up[NIQ];
+#pragma unroll
+  for (int i = 0; i < NIP; ++i) {
+    const int b = (i * 4 + wave) * 1024 + lane * 16;
+    const int row = b / RL, phys = (b % RL) >> 4;
+    p_off[i] = (uint32_t)(m0 + row) * ldp_b + (uint32_t)((phys ^ (row & 15)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < NIQ; ++i) {
+    const int b = (i * 4 + wave) * 1024 + lane * 16;
+    if (tq) {
+      q_off[i] = (uint32_t)b;
+      q_up[i] = false;
+    } else {
+      const int row = b / RL, phys = (b % RL) >> 4;
+      const int rowb = (i * 4 + wave) * 1024 / RL;             // first row of the instruction
+      q_up[i] = rowb >= p.R0;                                    // whole instruction in one segment
+      q_off[i] = (uint32_t)(q_up[i] ? row - p.R0 : row) * ldq_b + (uint32_t)((phys ^ (row & 15)) << 4);
+    }
+  }
+  auto issue = [&](int ch) {
+    uint8_t* sb = smem + (ch % ST) * SB;
+#pragma unroll
+    for (int i = 0; i < NIP; ++i) buf2lds16(rs_p, p_off[i], (uint32_t)ch * RL, sb + (i * 4 + wave) * 1024);
+    const uint32_t qs = tq ? (uint32_t)ch * (uint32_t)KC * (uint32_t)p.R * 2u : (uint32_t)ch * RL;
+#pragma unroll
+    for (int i = 0; i < NIQ; ++i) buf2lds16(q_up[i] ? rs_q1 : rs_q0, q_off[i], qs, sb + T::PB + (i * 4 + wave) * 1024);
+    buf2lds16(rs_g, (uint32_t)(wave * 1024 + lane * 16), (uint32_t)ch * KC * 4u, sb + T::PB + T::QB + wave * 1024);
+  };
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int jb = 0; jb < NB; ++jb) acc[jb] = f32x4{0, 0, 0, 0};
+
+#pragma unroll
+  for (int c = 0; c < ST - 1; ++c)
+    if (c < nch) issue(c);
+  for (int ch = 0; ch < nch; ++ch) {
+    // chunks issued after ch that may stay in flight
+    const int after = min(ST - 2, nch - 1 - ch);
+    if (after >= 2) wait_vmcnt<2 * T::NI>();
+    else if (after == 1) wait_vmcnt<T::NI>();
+    else wait_vmcnt<0>();
+    __syncthreads();                         // chunk ch visible; chunk ch-1's buffer free
+    if (ch + ST - 1 < nch) issue(ch + ST - 1);
+    const uint8_t* sb = smem + (ch % ST) * SB;
+    const uint8_t* sq = sb + T::PB;
+    const float* sg = reinterpret_cast<const float*>(sb + T::PB + T::QB);
+    const int nv = min(KC, p.K - ch * KC) / 32;
+    for (int st = wave; st < nv; st += 4) {
+      const int lc = st * 4 + lq;
+      const u32x4 pf = *reinterpret_cast<const u32x4*>(sb + lr * RL + ((lc ^ lr) << 4));
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb) {
+        u32x4 qf;
+        if (tq) {
+          // 8 consecutive k of column jb*16 + lr: two transposing reads of 4 rows each
+          const int k0 = st * 32 + 8 * lq + (lr >> 2);
+          const int off = k0 * p.R * 2 + (jb * 16 + 4 * (lr & 3)) * 2;
+          const u32x2 lo = lds_tr16(sq, off), hi = lds_tr16(sq, off + 4 * p.R * 2);
+          qf = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          if (p.q_kscale != nullptr) {
+            const f32x4* g = reinterpret_cast<const f32x4*>(sg + st * 32 + 8 * lq);
+            qf = scale_bf16x8(qf, g[0], g[1]);
+          }
+        } else {
+          const int j = jb * 16 + lr;
+          qf = *reinterpret_cast<const u32x4*>(sq + j * RL + ((lc ^ lr) << 4));
+        }
+        acc[jb] = mfma_bf16(qf, pf, acc[jb]);
+      }
+    }
+  }
+
+  // combine the four waves' partial sums; lane holds out[m0 + lr][jb*16 + 4*lq + i]
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(smem);      // [4][NB][64]
+#pragma unroll
+  for (int jb = 0; jb < NB; ++jb) red[(wave * NB + jb) * 64 + lane] = acc[jb];
+  __syncthreads();
+  const int m = m0 + lr;
+  for (int jb = wave; jb < NB; jb += 4) {
+    f32x4 v = red[jb * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v += red[(w * NB + jb) * 64 + lane];
+    if (m < p.M) {
+      const int j0 = jb * 16 + 4 * lq;
+      float* dst = p.out + (size_t)m * p.ldo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (j0 + i < p.R) dst[j0 + i] = v[i] * p.scale;
+    }
+  }
+}
+
 // ============================================================================ colproj
 // Block = 64 columns of X and one split of rows, walked in sub-tiles of MS rows.
 // Per sub-tile: X^T (64 x MS bf16) and S^T as bf16 hi/lo parts (R x MS each) are
@@ -363,10 +510,33 @@ __global__ void fill_zero_kernel(float* p, size_t n) {
 }
 
 // ============================================================================ launchers
+// The streamed kernel needs 16-byte aligned rows, and for a transposed Q an
+// R that keeps its rows 8-byte aligned; a two-segment Q must switch segment
+// on a copy-instruction boundary.
+static bool rowstream_ok(const RowProjParams& p, int rp) {
+  const int rl = rp <= 32 ? 1024 : (rp == 64 ? 512 : 256);
+  const int rows_per_inst = 1024 / rl;
+  if (p.ldp % 8 || (((uintptr_t)p.P) & 15) || (((uintptr_t)p.q0) & 15)) return false;
+  if (p.q_kscale && (((uintptr_t)p.q_kscale) & 15)) return false;
+  if (p.q_trans) return p.R % 4 == 0 && p.R0 == p.R;
+  if (p.ldq % 8 || (((uintptr_t)p.q1) & 15)) return false;
+  return p.R0 == p.R || p.R0 % rows_per_inst == 0;
+}
+
 hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st) {
   if (p.M <= 0) return hipSuccess;
-  const dim3 grid((p.M + 15) / 16), block(64 * RP_WAVES);
   const int rp = p.R <= 16 ? 16 : p.R <= 32 ? 32 : p.R <= 64 ? 64 : 128;
+  if (rowstream_ok(p, rp)) {
+    const dim3 grid((p.M + 15) / 16), block(256);
+    switch (rp) {
+      case 16: hipLaunchKernelGGL(rowstream_kernel<16>, grid, block, 0, st, p); break;
+      case 32: hipLaunchKernelGGL(rowstream_kernel<32>, grid, block, 0, st, p); break;
+      case 64: hipLaunchKernelGGL(rowstream_kernel<64>, grid, block, 0, st, p); break;
+      default: hipLaunchKernelGGL(rowstream_kernel<128>, grid, block, 0, st, p); break;
+    }
+    return hipGetLastError();
+  }
+  const dim3 grid((p.M + 15) / 16), block(64 * RP_WAVES);
   switch (rp) {
     case 16: hipLaunchKernelGGL(rowproj_kernel<16>, grid, block, 0, st, p); break;
     case 32: hipLaunchKernelGGL(rowproj_kernel<32>, grid, block, 0, st, p); break;
