@@ -434,6 +434,185 @@ __global__ __launch_bounds__(256) void colproj_kernel(const ColProjBatch batch) 
   }
 }
 
+// ============================================================================ colproj (streamed)
+// Block = 64 columns of X and one split of rows.  Sub-tiles of MS rows of X
+// (and Z for the DoRA column sums) and the matching rows of S (fp32, as
+// stored) are copied to LDS through a 3-stage ring of direct buffer->LDS
+// copies; X^T fragments come from transposing LDS reads, S^T fragments are
+// gathered from the fp32 tile and split into bf16 hi + lo parts.  The four
+// waves split each sub-tile's (32-row step, column block) work items and
+// combine their partial sums at the end.  X rows are stored with 16-byte
+// chunk c of row m at physical chunk c ^ 2 (m & 3).
+template <int RP>
+struct ColStream {
+  static constexpr int MS = RP <= 32 ? 128 : 64;       // rows per sub-tile
+  static constexpr int XB = MS * 128;                  // X (or Z) tile: MS rows x 64 columns
+  static constexpr int SBY = MS * RP * 4;              // S tile: MS rows x up to RP fp32
+  static constexpr int NSTEP = MS / 32;
+  static constexpr int WPS = 4 / NSTEP;                // waves per step
+  static constexpr int CFW = 4 / WPS;                  // 16-column blocks per wave
+  static constexpr int STAGES = 3;
+};
+
+template <int RP, bool HASZ>
+__global__ __launch_bounds__(256) void colstream_kernel(const ColProjBatch batch) {
+  using T = ColStream<RP>;
+  constexpr int NB = RP / 16, MS = T::MS, XB = T::XB, SBY = T::SBY, ST = T::STAGES;
+  constexpr int SB = XB * (HASZ ? 2 : 1) + SBY;        // bytes per stage
+  constexpr int NI = (XB * (HASZ ? 2 : 1) + SBY) / 4096;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[ST * SB];
+  const int y = blockIdx.y;
+  const int jobi = y >= batch.first[2] ? 2 : (y >= batch.first[1] ? 1 : 0);
+  const ColProjParams& p = batch.job[jobi];
+  const int split = y - batch.first[jobi];
+  const int c0 = blockIdx.x * 64;
+  if (c0 >= p.C) return;
+  const int mbeg = split * p.msplit;
+  const int mend = min(p.M, mbeg + p.msplit);
+  const int nsub = mend > mbeg ? (mend - mbeg + MS - 1) / MS : 0;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lq = lane >> 4;
+  const bool zmode = HASZ && p.colsum_mode == 1;
+
+  const uint32_t ldx_b = (uint32_t)p.ldx * 2u, lds_b = (uint32_t)p.lds * 4u, ldz_b = (uint32_t)p.ldz * 2u;
+  // rows past mend read as zero
+  const __amdgpu_buffer_rsrc_t rs_x = make_rsrc(p.X, (uint32_t)mend * ldx_b);
+  const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(p.S, p.R > 0 ? (uint32_t)mend * lds_b : 0u);
+  const __amdgpu_buffer_rsrc_t rs_z = make_rsrc(p.Z, zmode ? (uint32_t)mend * ldz_b : 0u);
+  constexpr int NIX = XB / 4096, NIS = SBY / 4096;
+  uint32_t x_off[NIX], s_off[NIS];
+#pragma unroll
+  for (int i = 0; i < NIX; ++i) {
+    const int b = (i * 4 + wave) * 1024 + lane * 16;
+    const int row = b >> 7, phys = (b >> 4) & 7;
+    x_off[i] = (uint32_t)row * ldx_b + (uint32_t)(c0 + 8 * (phys ^ (2 * (row & 3)))) * 2u;
+  }
+  const int rb = p.R > 0 ? p.R * 4 : 16;               // bytes per staged S row
+#pragma unroll
+  for (int i = 0; i < NIS; ++i) {
+    const int b = (i * 4 + wave) * 1024 + lane * 16;
+    s_off[i] = (uint32_t)(b / rb) * lds_b + (uint32_t)(b % rb);
+  }
+  auto issue = [&](int sub) {
+    uint8_t* sb = smem + (sub % ST) * SB;
+    const uint32_t m = (uint32_t)(mbeg + sub * MS);
+#pragma unroll
+    for (int i = 0; i < NIX; ++i) buf2lds16(rs_x, x_off[i], m * ldx_b, sb + (i * 4 + wave) * 1024);
+#pragma unroll
+    for (int i = 0; i < NIS; ++i) buf2lds16(rs_s, s_off[i], m * lds_b, sb + XB + (i * 4 + wave) * 1024);
+    if constexpr (HASZ) {
+#pragma unroll
+      for (int i = 0; i < NIX; ++i)   // same element layout as X (Z has its own leading dimension)
+        buf2lds16(rs_z, x_off[i] / ldx_b * ldz_b + x_off[i] % ldx_b, m * ldz_b, sb + XB + SBY + (i * 4 + wave) * 1024);
+    }
+  };
+
+  constexpr int CFW = T::CFW;
+  f32x4 acc[CFW][NB];                                   // this wave's column blocks my_cf0 + q
+#pragma unroll
+  for (int q = 0; q < CFW; ++q)
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) acc[q][jb] = f32x4{0, 0, 0, 0};
+  float cs[4] = {0.f, 0.f, 0.f, 0.f};
+  const int my_step = wave % T::NSTEP, my_cf0 = (wave / T::NSTEP) * T::CFW;
+
+#pragma unroll
+  for (int c = 0; c < ST - 1; ++c)
+    if (c < nsub) issue(c);
+  for (int sub = 0; sub < nsub; ++sub) {
+    if (sub + 1 < nsub) wait_vmcnt<NI>();
+    else wait_vmcnt<0>();
+    __syncthreads();                                    // sub-tile visible; sub-1's buffer free
+    if (sub + ST - 1 < nsub) issue(sub + ST - 1);
+    const uint8_t* sb = smem + (sub % ST) * SB;
+    const float* ss = reinterpret_cast<const float*>(sb + XB);
+    const int mrow = my_step * 32 + 8 * lq;             // first of this lane's 8 rows
+    // S^T fragments (rank j = jb*16 + lr, rows mrow .. mrow+7), hi / lo bf16 parts, pre-scaled
+    u32x4 shi[NB], slo[NB];
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) {
+      const int j = jb * 16 + lr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v0 = 0.f, v1 = 0.f;
+        if (j < p.R) {
+          v0 = ss[(mrow + 2 * e) * p.R + j] * p.s_in;
+          v1 = ss[(mrow + 2 * e + 1) * p.R + j] * p.s_in;
+        }
+        const uint32_t h0 = f32_to_bf16_bits(v0), h1 = f32_to_bf16_bits(v1);
+        shi[jb][e] = h0 | (h1 << 16);
+        slo[jb][e] = f32_to_bf16_bits(v0 - __uint_as_float(h0 << 16)) |
+                     (f32_to_bf16_bits(v1 - __uint_as_float(h1 << 16)) << 16);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < T::CFW; ++q) {
+      const int cf = my_cf0 + q;
+      // X^T fragment: column c0 + 16 cf + lr, rows mrow .. mrow+7 (two transposing reads)
+      const int rr = my_step * 32 + 8 * lq + (lr >> 2);
+      const int col = cf * 16 + 4 * (lr & 3);
+      auto xoff = [&](int r) { return r * 128 + (((col >> 3) ^ (2 * (r & 3))) << 4) + ((col & 4) << 1); };
+      const u32x2 lo = lds_tr16(sb, xoff(rr)), hi = lds_tr16(sb, xoff(rr + 4));
+      const u32x4 xf = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb) {
+        acc[q][jb] = mfma_bf16(shi[jb], xf, acc[q][jb]);
+        acc[q][jb] = mfma_bf16(slo[jb], xf, acc[q][jb]);
+      }
+      if (p.colsum_mode == 2) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) cs[q] += bf16_lo(xf[t]) + bf16_hi(xf[t]);
+      } else if (zmode) {
+        const uint8_t* sz = sb + XB + SBY;
+        const u32x2 zl = lds_tr16(sz, xoff(rr)), zh = lds_tr16(sz, xoff(rr + 4));
+        const u32x4 zf = u32x4{zl[0], zl[1], zh[0], zh[1]};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) cs[q] += bf16_lo(xf[t]) * bf16_lo(zf[t]) + bf16_hi(xf[t]) * bf16_hi(zf[t]);
+      }
+    }
+  }
+
+  // combine the waves: lane holds part[c = c0 + 16 cf + lr][j = jb*16 + 4*lq + i]
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(smem);          // [4 waves][CFW][NB][64]
+  static_assert(4 * CFW * NB * 64 * 16 <= ST * SB, "reduction scratch fits");
+#pragma unroll
+  for (int q = 0; q < CFW; ++q)
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) red[((wave * CFW + q) * NB + jb) * 64 + lane] = acc[q][jb];
+  __syncthreads();
+  for (int item = wave; item < 4 * NB; item += 4) {
+    const int cf = item / NB, jb = item % NB;
+    f32x4 v = f32x4{0, 0, 0, 0};
+    for (int w = 0; w < 4; ++w) {                       // waves that own column block cf, in order
+      const int q = cf - (w / T::NSTEP) * CFW;
+      if (q >= 0 && q < CFW) v += red[((w * CFW + q) * NB + jb) * 64 + lane];
+    }
+    const int c = c0 + cf * 16 + lr;
+    if (c < p.C) *reinterpret_cast<f32x4*>(p.part + ((size_t)split * p.C + c) * RP + jb * 16 + 4 * lq) = v;
+  }
+  if (p.colsum_mode != 0) {
+    // column sums: lanes lr of the four 16-lane groups and the waves sharing a column block
+    __syncthreads();
+    float* csr = reinterpret_cast<float*>(smem);        // [4 waves][4 q][64 lanes]
+#pragma unroll
+    for (int q = 0; q < 4; ++q) csr[(wave * 4 + q) * 64 + lane] = cs[q];
+    __syncthreads();
+    if (tid < 64) {
+      const int cf = tid >> 4, l16 = tid & 15;
+      float t = 0.f;
+      for (int w = 0; w < 4; ++w) {
+        const int q = cf - (w / T::NSTEP) * T::CFW;      // this wave's slot for column block cf
+        if (q < 0 || q >= T::CFW) continue;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) t += csr[(w * 4 + q) * 64 + g * 16 + l16];
+      }
+      if (c0 + tid < p.C) p.cspart[(size_t)split * p.C + c0 + tid] = t;
+    }
+  }
+}
+
 // ============================================================================ reductions
 // out[row, col] = alpha * sum_s part[s][...] (+ row scale) (+ alpha2 * sum_l Qm[row, l] * Am[l, col]).
 // Threads walk the partial buffer in its own order ([C][rp], j fastest) so the
@@ -555,10 +734,10 @@ void colproj_plan(int M, int C, int* nsplit, int* msplit) {
     return;
   }
   // splits are whole multiples of 256 rows (a multiple of every sub-tile height);
-  // aim for ~1024 blocks, at most 32 splits
+  // aim for ~512 blocks (two per CU, each streaming several sub-tiles), at most 32 splits
   const int ctiles = (C + 63) / 64;
   const int mchunks = (M + 255) / 256;
-  int want = (1024 + ctiles - 1) / ctiles;
+  int want = (512 + ctiles - 1) / ctiles;
   if (want < 1) want = 1;
   if (want > 32) want = 32;
   int ns = mchunks < want ? mchunks : want;
@@ -580,6 +759,26 @@ static hipError_t colproj_launch(const ColProjBatch& b, int gx, int gy, int R, h
   return hipGetLastError();
 }
 
+// The streamed kernel copies 16-byte pieces: X, Z and S rows must be 16-byte aligned.
+static bool colstream_ok(const ColProjParams& p) {
+  if (p.ldx % 8 || (((uintptr_t)p.X) & 15)) return false;
+  if (p.R > 0 && (p.R % 4 || p.lds % 4 || (((uintptr_t)p.S) & 15))) return false;
+  if (p.colsum_mode == 1 && (p.ldz % 8 || (((uintptr_t)p.Z) & 15))) return false;
+  return p.msplit % 128 == 0;
+}
+
+template <bool HASZ>
+static hipError_t colstream_launch(const ColProjBatch& b, int gx, int gy, int R, hipStream_t st) {
+  const dim3 grid(gx, gy), block(256);
+  switch (colproj_rp(R)) {
+    case 16: hipLaunchKernelGGL((colstream_kernel<16, HASZ>), grid, block, 0, st, b); break;
+    case 32: hipLaunchKernelGGL((colstream_kernel<32, HASZ>), grid, block, 0, st, b); break;
+    case 64: hipLaunchKernelGGL((colstream_kernel<64, HASZ>), grid, block, 0, st, b); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_colproj_batch(const ColProjParams* jobs, const int* nsplit, int njobs, hipStream_t st) {
   if (njobs < 1 || njobs > kColProjBatch) return hipErrorInvalidValue;
   for (int i = 1; i < njobs; ++i)
@@ -597,6 +796,15 @@ hipError_t launch_colproj_batch(const ColProjParams* jobs, const int* nsplit, in
     b.job[i] = jobs[i < njobs ? i : 0];
     b.first[i + 1] = b.first[i] + (i < njobs ? nsplit[i] : 0);
     if (i < njobs && jobs[i].C > maxc) maxc = jobs[i].C;
+  }
+  bool stream = true, hasz = false;
+  for (int i = 0; i < njobs; ++i) {
+    stream = stream && colstream_ok(jobs[i]);
+    hasz = hasz || jobs[i].colsum_mode == 1;
+  }
+  if (stream && colproj_rp(jobs[0].R) <= 64) {      // rank 128: the register-transposing kernel is faster
+    return hasz ? colstream_launch<true>(b, (maxc + 63) / 64, b.first[njobs], jobs[0].R, st)
+                : colstream_launch<false>(b, (maxc + 63) / 64, b.first[njobs], jobs[0].R, st);
   }
   return colproj_launch(b, (maxc + 63) / 64, b.first[njobs], jobs[0].R, st);
 }
