@@ -36,7 +36,54 @@ def parse():
     ap.add_argument("--M", type=int, default=None, help="token count override (w8a8 sweep point)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused-downproj", type=int, default=None, choices=[0, 1])
+    ap.add_argument("--copy-calibrate", type=int, default=None, metavar="MIB",
+                    help="only run device-to-device copies of MIB MiB (reference kernel for the HBM byte counters)")
     return ap.parse_args()
+
+
+# HBM traffic of the dominant kernel, taken with rocprofv3 counter runs and kept
+# with its kernel trace under profiles/; it is reported only while the GEMM
+# sources still hash to the value recorded with the counters.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lora_bf16_4096_r16_gemm_traffic.md")
+GEMM_SOURCES = ("lora_dora_linear_amd/csrc/gemm_tile.hpp", "lora_dora_linear_amd/csrc/gemm.hip",
+                "lora_dora_linear_amd/csrc/common.hpp")
+
+
+def gemm_source_hash():
+    import hashlib
+    h = hashlib.sha1()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel_key):
+    """Bytes per launch (fetch + write, copy-calibrated) recorded for kernel_key, or None if stale/absent."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    for ln in lines:
+        if ln.startswith("traffic-record: "):
+            rec = json.loads(ln[len("traffic-record: "):])
+            if rec.get("kernel") == kernel_key and rec.get("source_sha1") == gemm_source_hash():
+                return rec["fetch_bytes"] * rec["fetch_scale"] + rec["write_bytes"] * rec["write_scale"]
+    return None
+
+
+def copy_calibrate(mib):
+    import torch
+    torch.cuda.set_device(0)
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}))
 
 
 def _events(torch, n):
@@ -79,6 +126,9 @@ def cpu_baseline_lora(M_sample, N, K, r, s, repeats=3):
 
 def main():
     args = parse()
+    if args.copy_calibrate:
+        copy_calibrate(args.copy_calibrate)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; multi-GPU runs are not part of it "
                                    "(the data-parallel sharding is described in DESIGN.md)",
@@ -260,9 +310,10 @@ def main():
         dom = max(kern, key=lambda k: kern[k]["avg_us"])
         names = {0: "forward base GEMM (gemm_kernel NT)", 1: "input-gradient GEMM (gemm_kernel NN)"}
         peak = PEAK_INT8 if (wl == "w8a8" and dom == 0) else PEAK_BF16
+        traffic = recorded_traffic(f"{wl}:{names[dom]}")
         out["roofline"] = {"bound": "mfma", "kernel": names[dom], "achieved": round(kern[dom]["tflops"], 1),
                            "peak": peak, "unit": "TFLOP/s", "frac": round(kern[dom]["tflops"] / peak, 4),
-                           "traffic": None}
+                           "traffic": None if traffic is None else int(traffic)}
         out["kernels"] = {names[k]: {"avg_us": round(v["avg_us"], 2), "TFLOP/s": round(v["tflops"], 1)}
                           for k, v in kern.items()}
     if wl == "lora" and not args.no_cpu_baseline:
