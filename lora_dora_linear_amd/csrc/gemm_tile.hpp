@@ -199,6 +199,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
            : make_rsrc(DUAL ? p.b1 : p.b0, NN ? 0u : (uint32_t)N * ldb_b);
   const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(p.side, RSP ? (uint32_t)p.r_side * (uint32_t)K * 2u : 0u);
   constexpr bool TRSC = NNTR && C::kAScale;    // scale slice: 1 KB after the Q tile, first 256 B used
+  // copy slices per stage (see issue_loads); the register-staged NN operand is loaded whole
+  constexpr int NPART = (NN && !NNTR) ? 1 : 3;
   const __amdgpu_buffer_rsrc_t rs_c = make_rsrc(p.a_colscale, TRSC ? (uint32_t)K * 4u : 0u);
   uint32_t a_off[A_INST];
 #pragma unroll
@@ -251,21 +253,28 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
   u32x4 rb[NN ? RPT : 1];
 
   // ---------------------------------------------------------------- loaders
-  auto issue_loads = [&](int kt, uint8_t* sbuf) {
+  // Copies of a stage are issued in NPART slices (instruction q of this wave goes
+  // with slice q % NPART) spread over the MFMA steps, so that a wave never sits
+  // through a whole stage's worth of copy issue (the address unit accepts them at
+  // a limited rate) while the matrix pipe idles.  part < 0: every slice.
+  auto issue_loads = [&](int kt, uint8_t* sbuf, int part) {
     const uint32_t koff = (uint32_t)kt * 128u;
+    auto mine = [&](int q) { return part < 0 || q % NPART == part; };
 #pragma unroll
-    for (int i = 0; i < A_INST; ++i) buf2lds16(rs_a, a_off[i], koff, sbuf + (i * NW + wave) * 1024);
+    for (int i = 0; i < A_INST; ++i)
+      if (mine(i)) buf2lds16(rs_a, a_off[i], koff, sbuf + (i * NW + wave) * 1024);
     if constexpr (!NN) {
       uint8_t* sB = sbuf + BM * 128;
 #pragma unroll
       for (int i = 0; i < B_INST; ++i) {
         // the up half of each wave's rows comes from the second matrix (uniform per instruction)
         const bool up = DUAL && ((((i * NW + wave) * 8) % TN) >= TN / 2);
-        buf2lds16(up ? rs_b2 : rs_b, b_off[i], koff, sB + (i * NW + wave) * 1024);
+        if (mine(A_INST + i)) buf2lds16(up ? rs_b2 : rs_b, b_off[i], koff, sB + (i * NW + wave) * 1024);
       }
 #pragma unroll
       for (int i = 0; i < S_INST; ++i)
-        if ((i * NW + wave) * 8 < RSP) buf2lds16(rs_s, s_off[i], koff, sB + BN * 128 + (i * NW + wave) * 1024);
+        if ((i * NW + wave) * 8 < RSP && mine(A_INST + B_INST + i))
+          buf2lds16(rs_s, s_off[i], koff, sB + BN * 128 + (i * NW + wave) * 1024);
     } else if constexpr (NNTR) {
       // Q is [K, N]: rows kt*64 .. +63 of the segment that holds them (k-tiles never straddle kseg)
       uint8_t* sB = sbuf + BM * 128;
@@ -273,12 +282,14 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
       const bool seg1 = kk0 >= p.kseg;
       const uint32_t boff = (uint32_t)(seg1 ? kk0 - p.kseg : kk0) * ldb_b;
 #pragma unroll
-      for (int i = 0; i < B_INST; ++i) buf2lds16(seg1 ? rs_b2 : rs_b, b_off[i], boff, sB + (i * NW + wave) * 1024);
+      for (int i = 0; i < B_INST; ++i)
+        if (mine(A_INST + i)) buf2lds16(seg1 ? rs_b2 : rs_b, b_off[i], boff, sB + (i * NW + wave) * 1024);
       // scale[kt*64 ..] -> lanes 0..15 fill the slice; the rest read ahead (or zero past the end)
       if constexpr (TRSC) {
-        if (wave == NW - 1) buf2lds16(rs_c, (uint32_t)lane * 16u, (uint32_t)kt * 256u, sB + BN * 128);
+        if (wave == NW - 1 && mine(A_INST + B_INST)) buf2lds16(rs_c, (uint32_t)lane * 16u, (uint32_t)kt * 256u, sB + BN * 128);
       }
     } else {
+      if (part > 0) return;
       // Q is [K, N]: this k-tile covers reduction rows kt*64 .. +63.  Each thread
       // stages RPT rows x 8 columns (RPT = 8 with 256 threads, 4 with 512).
       const int kk0 = kt * 64;
@@ -484,12 +495,12 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
   // the register allocator rotate them every iteration.)
   const int KT = K / BK;
   u32x4 fa0[FM], fb0[FN], fs0[SF], fa1[FM], fb1[FN], fs1[SF];
-  issue_loads(0, smem0);
+  issue_loads(0, smem0, -1);
   if constexpr (SEED) lora_update(acc, std::integral_constant<int, 0>{});
   store_q(0, smem0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (KT > 1) issue_loads(1, smem1);
+  if (KT > 1) issue_loads(1, smem1, -1);
   load_frags(smem0, 0, fa0, fb0, fs0);
   // settle every LDS / scalar read of the prologue (not the copies in flight)
   // so that the waits inside the loop can count the fragment reads exactly
@@ -498,15 +509,20 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
   auto first_steps = [&](int kt, uint8_t* cur, uint8_t* nxt, bool more) {
     __builtin_amdgcn_sched_barrier(0);
     load_frags(cur, 1, fa1, fb1, fs1);
+    // later slices of stage kt+1's copies (slice 0 went out at the previous hand-over)
+    const bool tail = NPART > 1 && more && kt >= 1;
+    if (tail) issue_loads(kt + 1, nxt, 1);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(fa0, fb0, fs0);
     __builtin_amdgcn_sched_barrier(0);
     load_frags(cur, 2, fa0, fb0, fs0);
+    if (tail && NPART > 2) issue_loads(kt + 1, nxt, 2);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(fa1, fb1, fs1);
     __builtin_amdgcn_sched_barrier(0);
     if (more) store_q(kt + 1, nxt);
     load_frags(cur, 3, fa1, fb1, fs1);
+    if (tail && NPART > 3) issue_loads(kt + 1, nxt, 3);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(fa0, fb0, fs0);
     __builtin_amdgcn_sched_barrier(0);
@@ -517,7 +533,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
     first_steps(kt, cur, nxt, true);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kt + 2 < KT) issue_loads(kt + 2, cur);
+    if (kt + 2 < KT) issue_loads(kt + 2, cur, NPART > 1 ? 0 : -1);
     load_frags(nxt, 0, fa0, fb0, fs0);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(fa1, fb1, fs1);
