@@ -201,6 +201,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
   constexpr bool TRSC = NNTR && C::kAScale;    // scale slice: 1 KB after the Q tile, first 256 B used
   // copy slices per stage (see issue_loads); the register-staged NN operand is loaded whole
   constexpr int NPART = (NN && !NNTR) ? 1 : 3;
+  constexpr bool SPLIT = NPART > 1;
   const __amdgpu_buffer_rsrc_t rs_c = make_rsrc(p.a_colscale, TRSC ? (uint32_t)K * 4u : 0u);
   uint32_t a_off[A_INST];
 #pragma unroll
@@ -253,6 +254,38 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
   u32x4 rb[NN ? RPT : 1];
 
   // ---------------------------------------------------------------- loaders
+  // the wave's copy instructions of one stage, in order: P tile, Q tile, side rows, scale slice
+  constexpr int NCOPY = A_INST + ((NN && !NNTR) ? 0 : B_INST + S_INST + (TRSC ? 1 : 0));
+  auto issue_one = [&](int kt, uint8_t* sbuf, int q) {
+    const uint32_t koff = (uint32_t)kt * 128u;
+    if (q < A_INST) {
+      buf2lds16(rs_a, a_off[q], koff, sbuf + (q * NW + wave) * 1024);
+      return;
+    }
+    q -= A_INST;
+    uint8_t* sB = sbuf + BM * 128;
+    if constexpr (!NN) {
+      if (q < B_INST) {
+        const bool up = DUAL && ((((q * NW + wave) * 8) % TN) >= TN / 2);
+        buf2lds16(up ? rs_b2 : rs_b, b_off[q], koff, sB + (q * NW + wave) * 1024);
+        return;
+      }
+      q -= B_INST;
+      if (q < S_INST && (q * NW + wave) * 8 < RSP) buf2lds16(rs_s, s_off[q], koff, sB + BN * 128 + (q * NW + wave) * 1024);
+    } else if constexpr (NNTR) {
+      const int kk0 = kt * 64;
+      const bool seg1 = kk0 >= p.kseg;
+      const uint32_t boff = (uint32_t)(seg1 ? kk0 - p.kseg : kk0) * ldb_b;
+      if (q < B_INST) {
+        buf2lds16(seg1 ? rs_b2 : rs_b, b_off[q], boff, sB + (q * NW + wave) * 1024);
+        return;
+      }
+      if constexpr (TRSC) {
+        if (wave == NW - 1) buf2lds16(rs_c, (uint32_t)lane * 16u, (uint32_t)kt * 256u, sB + BN * 128);
+      }
+    }
+  };
+
   // Copies of a stage are issued in NPART slices (instruction q of this wave goes
   // with slice q % NPART) spread over the MFMA steps, so that a wave never sits
   // through a whole stage's worth of copy issue (the address unit accepts them at
@@ -397,11 +430,12 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
   // Once a wave has started a cluster of MFMAs it takes issue priority over the
   // other wave of its SIMD until the cluster ends, so the two waves alternate
   // between MFMA clusters and their LDS / copy work instead of interleaving both.
-  auto mfmas = [&](const u32x4* af, const u32x4* bf, const u32x4* sf) {
+  auto mfmas = [&](const u32x4* af, const u32x4* bf, const u32x4* sf, auto&& between) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
+        between(i * FN + j);
         if constexpr (I8) acc[i][j] = mfma32_i8(bf[j], af[i], acc[i][j]);
         else acc[i][j] = mfma32_bf16(bf[j], af[i], acc[i][j]);
         if (i == 0 && j == 0) {
@@ -505,26 +539,44 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
   // settle every LDS / scalar read of the prologue (not the copies in flight)
   // so that the waits inside the loop can count the fragment reads exactly
   __builtin_amdgcn_s_waitcnt(0xc07f);
+  // A stage's copies are spread over three MFMA clusters (the hand-over cluster of
+  // stage kt and the first two of stage kt+1), at most CPC per cluster, each copy
+  // placed between two MFMAs: a copy instruction holds the issuing wave for a
+  // while (the address unit takes them at a limited rate), and in one burst the
+  // waves would leave the matrix pipe idle.
+  constexpr int NMF = FM * FN;
+  constexpr int CPC = (NCOPY + 2) / 3;
+  auto copies_between = [&](int kt, uint8_t* sbuf, int cluster, bool on) {
+    return [&, kt, sbuf, cluster, on](int t) {
+      if (!on) return;
+#pragma unroll
+      for (int u = 0; u < CPC; ++u) {
+        const int q = cluster * CPC + u;
+        if (q < NCOPY && t == u * (NMF / CPC)) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_one(kt, sbuf, q);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+  };
+  auto none = [](int) {};
   // steps 0..2 of stage kt (step 0's fragments already in fa0), leaving step 3's in fa1
   auto first_steps = [&](int kt, uint8_t* cur, uint8_t* nxt, bool more) {
+    const bool tail = SPLIT && more && kt >= 1;          // clusters 1, 2 of stage kt+1's copies
     __builtin_amdgcn_sched_barrier(0);
     load_frags(cur, 1, fa1, fb1, fs1);
-    // later slices of stage kt+1's copies (slice 0 went out at the previous hand-over)
-    const bool tail = NPART > 1 && more && kt >= 1;
-    if (tail) issue_loads(kt + 1, nxt, 1);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(fa0, fb0, fs0);
+    mfmas(fa0, fb0, fs0, copies_between(kt + 1, nxt, 1, tail));
     __builtin_amdgcn_sched_barrier(0);
     load_frags(cur, 2, fa0, fb0, fs0);
-    if (tail && NPART > 2) issue_loads(kt + 1, nxt, 2);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(fa1, fb1, fs1);
+    mfmas(fa1, fb1, fs1, copies_between(kt + 1, nxt, 2, tail));
     __builtin_amdgcn_sched_barrier(0);
     if (more) store_q(kt + 1, nxt);
     load_frags(cur, 3, fa1, fb1, fs1);
-    if (tail && NPART > 3) issue_loads(kt + 1, nxt, 3);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(fa0, fb0, fs0);
+    mfmas(fa0, fb0, fs0, none);
     __builtin_amdgcn_sched_barrier(0);
   };
   for (int kt = 0; kt + 1 < KT; ++kt) {
@@ -533,15 +585,15 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
     first_steps(kt, cur, nxt, true);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kt + 2 < KT) issue_loads(kt + 2, cur, NPART > 1 ? 0 : -1);
+    if (!SPLIT && kt + 2 < KT) issue_loads(kt + 2, cur, -1);
     load_frags(nxt, 0, fa0, fb0, fs0);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(fa1, fb1, fs1);
+    mfmas(fa1, fb1, fs1, copies_between(kt + 2, cur, 0, SPLIT && kt + 2 < KT));
   }
   {
     uint8_t* cur = ((KT - 1) & 1) ? smem1 : smem0;
     first_steps(KT - 1, cur, cur, false);
-    mfmas(fa1, fb1, fs1);
+    mfmas(fa1, fb1, fs1, none);
   }
   __syncthreads();
 
