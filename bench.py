@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--M", type=int, default=None, help="token count override (w8a8 sweep point)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused-downproj", type=int, default=None, choices=[0, 1])
+    ap.add_argument("--gemm-4wave", type=int, default=None, choices=[0, 1],
+                    help="four-wave 256x256 tile for the plain NT products (library default 1)")
     ap.add_argument("--copy-calibrate", type=int, default=None, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (reference kernel for the HBM byte counters)")
     return ap.parse_args()
@@ -144,6 +146,8 @@ def main():
     dev = torch.device("cuda", 0)
     if args.fused_downproj is not None:
         binding.set_tuning(0, args.fused_downproj)
+    if args.gemm_4wave is not None:
+        binding.set_tuning(1, args.gemm_4wave)
 
     def up(arr, kind):
         if kind == "bf16":

@@ -75,8 +75,11 @@ int ldl_version(void);
  *   LDL_TUNE_FWD_FUSED_DOWNPROJ (0/1, default 0): compute U = X.A^T inside the
  *     K-loop of the base GEMM from the LDS-staged X tiles (r <= 64, N multiple
  *     of 128) instead of a separate rank-r pass before it.
+ *   LDL_TUNE_GEMM_4WAVE (0/1, default 1): run the plain bf16 LoRA GEMMs
+ *     (forward and input gradient, N a multiple of 256, M > 128) on the
+ *     four-wave 256x256 tile with 16x16x32 MFMAs; 0 selects the eight-wave tile.
  * Returns LDL_OK, or LDL_E_INVAL for an unknown key or value. */
-typedef enum { LDL_TUNE_FWD_FUSED_DOWNPROJ = 0 } ldl_tune_key;
+typedef enum { LDL_TUNE_FWD_FUSED_DOWNPROJ = 0, LDL_TUNE_GEMM_4WAVE = 1 } ldl_tune_key;
 int ldl_set_tuning(int key, int value);
 
 /* Kernel timing hook for profilers and benchmarks.  While set, the library

@@ -262,6 +262,10 @@ int ldl_set_tuning(int key, int value) {
     g_fwd_fused = value;
     return LDL_OK;
   }
+  if (key == LDL_TUNE_GEMM_4WAVE && (value == 0 || value == 1)) {
+    g_gemm_4wave = value;
+    return LDL_OK;
+  }
   return LDL_E_INVAL;
 }
 

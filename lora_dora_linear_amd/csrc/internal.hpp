@@ -45,6 +45,7 @@ enum GemmKind : int {
   GK_NN_PLAIN, GK_NN_SCALE, GK_NN_I8_SCALE, GK_NN_SWIGLU
 };
 hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st);
+extern int g_gemm_4wave;   // plain bf16 GEMMs on the four-wave 16x16x32 tile (tuning switch)
 bool gemm_shape_ok(GemmKind kind, int M, int N, int K);
 
 hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st);

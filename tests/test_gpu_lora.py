@@ -124,6 +124,35 @@ def test_bf16_fused_down_projection():
     assert_close(host(Y2), host(Y1), BF16_TOL, "fused vs separate")
 
 
+@pytest.mark.parametrize("M,N,K,r", [
+    # the four-wave 256x256 forward tile: odd and single k-tile counts, one and two
+    # 32-rank steps of the low-rank term, ragged row counts
+    (300, 512, 320, 16),
+    (129, 256, 64, 48),
+    (513, 768, 448, 64),
+    (260, 256, 256, 8),
+])
+def test_bf16_four_wave_forward_tile(M, N, K, r):
+    require_gpu()
+    import lora_dora_linear_amd as L
+    c = inputs.linear_case(6, M, N, K, r, 0.5, "bf16", with_bias=True)
+    X, W0, A, B = (dev(c.t[k], "bf16") for k in ("X", "W0", "A", "B"))
+    bias = dev(c.t["bias"], "bf16")
+    Y4, U4 = L.lora_linear_fwd(X, W0, A, B, c.s, bias=bias)
+    L.set_tuning(1, 0)
+    try:
+        Y8, _ = L.lora_linear_fwd(X, W0, A, B, c.s, bias=bias)
+    finally:
+        L.set_tuning(1, 1)
+    Y4b, _ = L.lora_linear_fwd(X, W0, A, B, c.s, bias=bias)
+    torch.cuda.synchronize()
+    Yr, _, Ur = _oracle(c, with_bias=True)
+    assert_close(host(Y4), Yr, BF16_TOL, "Y four-wave")
+    assert_close(host(U4), Ur, 1e-5, "U")
+    assert_close(host(Y8), Yr, BF16_TOL, "Y eight-wave")
+    assert torch.equal(Y4, Y4b)
+
+
 def test_bf16_deterministic():
     require_gpu()
     c = inputs.linear_case(4, 300, 512, 384, 16, 0.5, "bf16")
