@@ -49,14 +49,15 @@ bool gemm_shape_ok(GemmKind kind, int M, int N, int K) {
 
 int g_gemm_4wave = 1;
 
-// Four-wave 256x256 NT tile: plain NT products over a whole number of 256-column
-// tiles with a low-rank term of rank <= 64.
-static hipError_t run16_nt(const GemmParams& p, hipStream_t st) {
+// Four-wave 256x256 tile: plain products over a whole number of 256-column tiles with
+// a low-rank term of rank <= 64 (NN: Q in one segment).
+template <bool NN>
+static hipError_t run16(const GemmParams& p, hipStream_t st) {
   const int tiles = ((p.M + 255) / 256) * (p.N / 256);
   const int ss = (p.r_epi + 31) / 32;
-  if (ss == 0) hipLaunchKernelGGL(gemm16_nt_kernel<0>, dim3(tiles), dim3(256), 0, st, p);
-  else if (ss == 1) hipLaunchKernelGGL(gemm16_nt_kernel<1>, dim3(tiles), dim3(256), 0, st, p);
-  else hipLaunchKernelGGL(gemm16_nt_kernel<2>, dim3(tiles), dim3(256), 0, st, p);
+  if (ss == 0) hipLaunchKernelGGL((gemm16_kernel<NN, 0>), dim3(tiles), dim3(256), 0, st, p);
+  else if (ss == 1) hipLaunchKernelGGL((gemm16_kernel<NN, 1>), dim3(tiles), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((gemm16_kernel<NN, 2>), dim3(tiles), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -64,8 +65,10 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
   if (p.M <= 0) return hipSuccess;
   const int bn = pick_bn(kind, p.N);
   const bool big = p.M > 128;
-  if (g_gemm_4wave && kind == GK_NT_PLAIN && bn == 256 && big && p.side == nullptr && p.r_epi <= 64)
-    return run16_nt(p, st);
+  if (g_gemm_4wave && bn == 256 && big && p.side == nullptr && p.r_epi <= 64) {
+    if (kind == GK_NT_PLAIN) return run16<false>(p, st);
+    if (kind == GK_NN_PLAIN && p.kseg == p.K) return run16<true>(p, st);
+  }
   switch (kind) {
     case GK_NT_PLAIN:
       if (bn == 256) return big ? run<256, 256, false, false, false, false, 0, true, EPI_PLAIN>(p, st)

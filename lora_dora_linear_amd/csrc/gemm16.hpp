@@ -26,11 +26,19 @@ namespace ldl {
 // fragment read cover all banks.
 __device__ __forceinline__ int g16_off(int row, int chunk) { return row * 128 + ((chunk ^ swz(row & 15)) << 4); }
 
-// SS: 32-rank MFMA steps of the low-rank term (r_epi <= 32 SS)
-template <int SS>
-__global__ __launch_bounds__(256, 1) void gemm16_nt_kernel(const GemmParams p) {
+// NN Q tile ([64 k][256 n] as stored): k-row k at k * 512 + (k / 8) * 128, 16-byte
+// chunk c at physical chunk c ^ 2 (k & 3).  A transposing read takes 4 k-rows x 32
+// bytes per 16 lanes: the XOR spreads the 4 rows over distinct banks and the 128-byte
+// pad every 8 rows moves the next 16 lanes' rows (k + 8) onto the other half of the banks.
+constexpr int kG16NNRow = 512, kG16NNPad = 128;
+__host__ __device__ constexpr int g16_nn_row(int k) { return k * kG16NNRow + (k >> 3) * kG16NNPad; }
+
+// NN: Q is [K, N] (else [N, K]); SS: 32-rank MFMA steps of the low-rank term (r_epi <= 32 SS)
+template <bool NN, int SS>
+__global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   constexpr int BM = 256, BN = 256, NW = 4;
-  constexpr int SB = (BM + BN) * 128;               // one stage: P tile then Q tile
+  constexpr int QB = NN ? g16_nn_row(64) : BN * 128;
+  constexpr int SB = BM * 128 + QB;                 // one stage: P tile then Q tile
   __shared__ __attribute__((aligned(16))) uint8_t smem0[SB];
   __shared__ __attribute__((aligned(16))) uint8_t smem1[SB];
 
@@ -54,18 +62,24 @@ __global__ __launch_bounds__(256, 1) void gemm16_nt_kernel(const GemmParams p) {
   const uint32_t lda_b = (uint32_t)p.lda * 2u, ldb_b = (uint32_t)p.ldb * 2u;
 
   const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(p.a, (uint32_t)M * lda_b);
-  const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(p.b0, (uint32_t)N * ldb_b);
+  const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(p.b0, (uint32_t)(NN ? K : N) * ldb_b);
   const __amdgpu_buffer_rsrc_t rs_none = make_rsrc(p.a, 0u);    // copies that read nothing
 
-  // per-lane copy offsets: 8 instructions for each tile; rows past M read as zero
+  // per-lane copy offsets: 8 instructions for each tile (1 KB each); rows past M read as zero
   const int lrow = lane >> 3, lphys = lane & 7;
   uint32_t a_off[8], b_off[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = (i * NW + wave) * 8 + lrow;
     a_off[i] = (uint32_t)(m0 + row) * lda_b + ((lphys ^ swz(row & 15)) << 4);
-    b_off[i] = (uint32_t)(n0 + row) * ldb_b + ((lphys ^ swz(row & 15)) << 4);
+    if constexpr (NN) {           // k-rows 2q, 2q+1 of the stage, 32 chunks each
+      const int k = 2 * (i * NW + wave) + (lane >> 5), chunk = (lane & 31) ^ (2 * (k & 3));
+      b_off[i] = (uint32_t)k * ldb_b + (uint32_t)(n0 + 8 * chunk) * 2u;
+    } else {
+      b_off[i] = (uint32_t)(n0 + row) * ldb_b + ((lphys ^ swz(row & 15)) << 4);
+    }
   }
+  auto q_dst = [&](int i) { const int q = i * NW + wave; return BM * 128 + q * 1024 + (NN ? (q >> 2) * kG16NNPad : 0); };
   auto copy = [](__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
   };
@@ -76,7 +90,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_nt_kernel(const GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) copy(ra, a_off[i], (uint32_t)kt * 128u, sb + (i * NW + wave) * 1024);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) copy(rb, b_off[i], (uint32_t)kt * 128u, sb + BM * 128 + (i * NW + wave) * 1024);
+    for (int i = 0; i < 8; ++i) copy(rb, b_off[i], NN ? (uint32_t)kt * 64u * ldb_b : (uint32_t)kt * 128u, sb + q_dst(i));
   };
 
   f32x4 acc[8][8];
@@ -85,17 +99,45 @@ __global__ __launch_bounds__(256, 1) void gemm16_nt_kernel(const GemmParams p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
 
-  // fragments of 32-element step ks (P rows wm*128 + 16 i + l16, Q rows wn*128 + 16 j + l16,
-  // k = 32 ks + 8 lq ..), read in order of first use: fa[0], fb[0..7], fa[1..7]
+  // fragments of 32-element step ks (P rows wm*128 + 16 i + l16, Q rows or columns
+  // wn*128 + 16 j + l16, k = 32 ks + 8 lq ..), read in order of first use: fa[0], fb[0..7], fa[1..7]
   const int a_base0 = g16_off(wm * 128 + l16, lq), a_base1 = g16_off(wm * 128 + l16, 4 + lq);
   const int b_base0 = BM * 128 + g16_off(wn * 128 + l16, lq), b_base1 = BM * 128 + g16_off(wn * 128 + l16, 4 + lq);
-  auto ldf = [&](const uint8_t* s, int ks, u32x4* fa, u32x4* fb) {
+  auto ldf_rows = [&](const uint8_t* s, int ks, u32x4* fa, u32x4* fb) {   // both tiles k-contiguous rows
     const int a = ks ? a_base1 : a_base0, b = ks ? b_base1 : b_base0;
     fa[0] = lds_ld16(s, a);
 #pragma unroll
     for (int j = 0; j < 8; ++j) fb[j] = lds_ld16(s, b + j * 2048);
 #pragma unroll
     for (int i = 1; i < 8; ++i) fa[i] = lds_ld16(s, a + i * 2048);
+  };
+  // NN: lane l16 of 16-lane group lq reads k-row 32 ks + 8 lq + (l16 >> 2) (+4 for the upper
+  // half), columns 4 (l16 & 3) .. +3 of column block j; the transposing read hands lane l16
+  // column l16 of the block at 4 consecutive k.  Physical chunk of column block j: 2 (j ^ a)
+  // with a = l16 >> 2 = k & 3, so four per-lane bases (j & 3) and constant offsets cover all j.
+  int bq[4];
+  {
+    const int a = l16 >> 2;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      bq[t] = BM * 128 + g16_nn_row(8 * lq + a) + wn * 256 + 8 * (l16 & 3) + 32 * (t ^ a);
+  }
+  auto ldf = [&](const uint8_t* s, int ks, u32x4* fa, u32x4* fb) {
+    if constexpr (NN) {
+      const int a = ks ? a_base1 : a_base0;
+      const int kso = ks * (g16_nn_row(32) - g16_nn_row(0));
+      fa[0] = lds_ld16(s, a);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int o = bq[j & 3] + kso + 128 * (j >> 2);
+        const u32x2 lo = lds_tr16(s, o), hi = lds_tr16(s, o + 4 * kG16NNRow);
+        fb[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+#pragma unroll
+      for (int i = 1; i < 8; ++i) fa[i] = lds_ld16(s, a + i * 2048);
+    } else {
+      ldf_rows(s, ks, fa, fb);
+    }
   };
   // D[n][m]: lane l of acc[i][j] holds n = 16 j + 4 (l >> 4) + v, m = 16 i + (l & 15) of the wave tile
   auto mm = [&](const u32x4* fa, const u32x4* fb) {
@@ -105,12 +147,14 @@ __global__ __launch_bounds__(256, 1) void gemm16_nt_kernel(const GemmParams p) {
       for (int j = 0; j < 8; ++j) acc[i][j] = mfma_bf16(fb[j], fa[i], acc[i][j]);
   };
 
+  constexpr int NRQ = NN ? 2 : 1;       // LDS read instructions per Q fragment
   const int KT = K / 64;
   u32x4 fa0[8], fb0[8], fa1[8], fb1[8];
   copy_stage(0, smem0);
 
   // Low-rank term through the second stage buffer while stage 0 lands: thread t writes
-  // row t of each tile (s.S[m0 + t][..] as bf16, E[n0 + t][..]), zero past r_epi.
+  // row t of each tile (s.S[m0 + t][..] as bf16, E[n0 + t][..]) in the k-contiguous row
+  // layout, zero past r_epi.
   if constexpr (SS > 0) {
     const int m = m0 + tid;
     const float* srow = p.S + (size_t)min(m, M - 1) * p.ld_s;
@@ -128,10 +172,10 @@ __global__ __launch_bounds__(256, 1) void gemm16_nt_kernel(const GemmParams p) {
       lds_st16(smem1, BM * 128 + g16_off(tid, c), e_frag(p, n0 + tid, k));
     }
     __syncthreads();
-    ldf(smem1, 0, fa0, fb0);
+    ldf_rows(smem1, 0, fa0, fb0);
     mm(fa0, fb0);
     if constexpr (SS > 1) {
-      ldf(smem1, 1, fa1, fb1);
+      ldf_rows(smem1, 1, fa1, fb1);
       mm(fa1, fb1);
     }
   }
@@ -159,7 +203,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_nt_kernel(const GemmParams p) {
     for (int q = 0; q < 8; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NRQ, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
@@ -175,7 +219,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_nt_kernel(const GemmParams p) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NRQ, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
     for (int q = 0; q < 8; ++q) {

@@ -125,32 +125,44 @@ def test_bf16_fused_down_projection():
 
 
 @pytest.mark.parametrize("M,N,K,r", [
-    # the four-wave 256x256 forward tile: odd and single k-tile counts, one and two
-    # 32-rank steps of the low-rank term, ragged row counts
+    # the four-wave 256x256 tiles (forward Y when N % 256 == 0, input gradient dX when
+    # K % 256 == 0): odd and single k-tile counts, one and two 32-rank steps of the
+    # low-rank term, ragged row counts
     (300, 512, 320, 16),
+    (300, 320, 512, 16),
     (129, 256, 64, 48),
+    (129, 64, 256, 48),
     (513, 768, 448, 64),
+    (513, 448, 768, 64),
     (260, 256, 256, 8),
 ])
-def test_bf16_four_wave_forward_tile(M, N, K, r):
+def test_bf16_four_wave_tiles(M, N, K, r):
     require_gpu()
     import lora_dora_linear_amd as L
     c = inputs.linear_case(6, M, N, K, r, 0.5, "bf16", with_bias=True)
-    X, W0, A, B = (dev(c.t[k], "bf16") for k in ("X", "W0", "A", "B"))
+    X, W0, A, B, dY = (dev(c.t[k], "bf16") for k in ("X", "W0", "A", "B", "dY"))
     bias = dev(c.t["bias"], "bf16")
-    Y4, U4 = L.lora_linear_fwd(X, W0, A, B, c.s, bias=bias)
+
+    def run():
+        Y, U = L.lora_linear_fwd(X, W0, A, B, c.s, bias=bias)
+        g = L.lora_linear_bwd(dY, X, W0, A, B, c.s, U=U)
+        return Y, U, g["dX"]
+
+    Y4, U4, dX4 = run()
     L.set_tuning(1, 0)
     try:
-        Y8, _ = L.lora_linear_fwd(X, W0, A, B, c.s, bias=bias)
+        Y8, _, dX8 = run()
     finally:
         L.set_tuning(1, 1)
-    Y4b, _ = L.lora_linear_fwd(X, W0, A, B, c.s, bias=bias)
+    Y4b, _, dX4b = run()
     torch.cuda.synchronize()
-    Yr, _, Ur = _oracle(c, with_bias=True)
+    Yr, gr, Ur = _oracle(c, with_bias=True)
     assert_close(host(Y4), Yr, BF16_TOL, "Y four-wave")
     assert_close(host(U4), Ur, 1e-5, "U")
+    assert_close(host(dX4), gr["dX"], BF16_TOL, "dX four-wave")
     assert_close(host(Y8), Yr, BF16_TOL, "Y eight-wave")
-    assert torch.equal(Y4, Y4b)
+    assert_close(host(dX8), gr["dX"], BF16_TOL, "dX eight-wave")
+    assert torch.equal(Y4, Y4b) and torch.equal(dX4, dX4b)
 
 
 def test_bf16_deterministic():
