@@ -47,8 +47,8 @@ def parse():
 # with its kernel trace under profiles/; it is reported only while the GEMM
 # sources still hash to the value recorded with the counters.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lora_bf16_4096_r16_gemm_traffic.md")
-GEMM_SOURCES = ("lora_dora_linear_amd/csrc/gemm_tile.hpp", "lora_dora_linear_amd/csrc/gemm.hip",
-                "lora_dora_linear_amd/csrc/common.hpp")
+GEMM_SOURCES = ("lora_dora_linear_amd/csrc/gemm_tile.hpp", "lora_dora_linear_amd/csrc/gemm16.hpp",
+                "lora_dora_linear_amd/csrc/gemm.hip", "lora_dora_linear_amd/csrc/common.hpp")
 
 
 def gemm_source_hash():
@@ -312,7 +312,10 @@ def main():
            "config": config, "pct_bf16_peak": round(100.0 * value / PEAK_BF16, 2)}
     if kern:
         dom = max(kern, key=lambda k: kern[k]["avg_us"])
-        names = {0: "forward base GEMM (gemm_kernel NT)", 1: "input-gradient GEMM (gemm_kernel NN)"}
+        # the plain LoRA products run on the four-wave tile unless it is switched off
+        four = wl == "lora" and args.gemm_4wave != 0
+        names = {0: "forward base GEMM (" + ("gemm16_kernel NT" if four else "gemm_kernel NT") + ")",
+                 1: "input-gradient GEMM (" + ("gemm16_kernel NN" if four else "gemm_kernel NN") + ")"}
         peak = PEAK_INT8 if (wl == "w8a8" and dom == 0) else PEAK_BF16
         traffic = recorded_traffic(f"{wl}:{names[dom]}")
         out["roofline"] = {"bound": "mfma", "kernel": names[dom], "achieved": round(kern[dom]["tflops"], 1),
