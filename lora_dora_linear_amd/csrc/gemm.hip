@@ -54,10 +54,8 @@ int g_gemm_4wave = 1;
 template <bool NN>
 static hipError_t run16(const GemmParams& p, hipStream_t st) {
   const int tiles = ((p.M + 255) / 256) * (p.N / 256);
-  const int ss = (p.r_epi + 31) / 32;
-  if (ss == 0) hipLaunchKernelGGL((gemm16_kernel<NN, 0>), dim3(tiles), dim3(256), 0, st, p);
-  else if (ss == 1) hipLaunchKernelGGL((gemm16_kernel<NN, 1>), dim3(tiles), dim3(256), 0, st, p);
-  else hipLaunchKernelGGL((gemm16_kernel<NN, 2>), dim3(tiles), dim3(256), 0, st, p);
+  if (p.r_epi > 0) hipLaunchKernelGGL((gemm16_kernel<NN, true>), dim3(tiles), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((gemm16_kernel<NN, false>), dim3(tiles), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -65,7 +63,13 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
   if (p.M <= 0) return hipSuccess;
   const int bn = pick_bn(kind, p.N);
   const bool big = p.M > 128;
-  if (g_gemm_4wave && bn == 256 && big && p.side == nullptr && p.r_epi <= 64) {
+  // the four-wave tile's low-rank loads need 16-byte aligned S rows and E rows (NN: rank
+  // rows of E^T), a rank that is a multiple of 8, and one E segment
+  const auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  const bool seed_ok = p.r_epi == 0 ||
+      (p.r_epi % 8 == 0 && p.ld_s % 4 == 0 && a16(p.S) && a16(p.e0) && p.e_jsplit >= p.r_epi &&
+       (kind == GK_NN_PLAIN ? (p.e_ldn == 1 && p.e_ldj % 8 == 0) : (p.e_ldj == 1 && p.e_ldn % 8 == 0)));
+  if (g_gemm_4wave && bn == 256 && big && p.side == nullptr && p.r_epi <= 64 && seed_ok) {
     if (kind == GK_NT_PLAIN) return run16<false>(p, st);
     if (kind == GK_NN_PLAIN && p.kseg == p.K) return run16<true>(p, st);
   }

@@ -1,5 +1,6 @@
-// Four-wave 256x256 GEMM tile on v_mfma_f32_16x16x32_bf16 for the plain NT
-// product with a low-rank term (LoRA forward: Y = X.W0^T + s.U.B^T (+ bias)).
+// Four-wave 256x256 GEMM tile on v_mfma_f32_16x16x32_bf16 for the plain products
+// with a low-rank term: NT (LoRA forward Y = X.W0^T + s.U.B^T (+ bias)) and NN (input
+// gradient dX = dY.W0 + s.V.A, W0 read as stored).
 //
 // Same data path as gemm_kernel (two 64 KB LDS stages filled by direct
 // buffer->LDS copies, the output staged through LDS), with one wave per SIMD and
@@ -10,10 +11,11 @@
 // of the current step's MFMAs, and the stage copies (16 per wave) over the whole
 // hand-over step.  The two stage buffers are separate arrays and the loop is
 // unrolled by two, so the compiler sees which buffer a copy writes and which a
-// read reads and inserts no waits between them.  The low-rank term enters as
-// extra k-steps before the loop: s.S (rounded to bf16, as the eight-wave seed
-// does) and E are written into the second stage buffer in the tile layout and
-// multiplied with the loop's own step code.
+// read reads and inserts no waits between them.  The low-rank term enters as one
+// more k-tile at the front: s.S (rounded to bf16, as the eight-wave seed does) and E
+// are written into the second stage buffer in the stage layout and multiplied by the
+// loop itself.  Every MFMA sits in the one loop body: MFMAs before the loop made the
+// register allocator shuffle accumulators through VGPRs inside it.
 #pragma once
 
 #include "gemm_tile.hpp"
@@ -33,8 +35,8 @@ __device__ __forceinline__ int g16_off(int row, int chunk) { return row * 128 + 
 constexpr int kG16NNRow = 512, kG16NNPad = 128;
 __host__ __device__ constexpr int g16_nn_row(int k) { return k * kG16NNRow + (k >> 3) * kG16NNPad; }
 
-// NN: Q is [K, N] (else [N, K]); SS: 32-rank MFMA steps of the low-rank term (r_epi <= 32 SS)
-template <bool NN, int SS>
+// NN: Q is [K, N] (else [N, K]); LR: with a low-rank term (r_epi in 8, 16, .., 64)
+template <bool NN, bool LR>
 __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   constexpr int BM = 256, BN = 256, NW = 4;
   constexpr int QB = NN ? g16_nn_row(64) : BN * 128;
@@ -65,20 +67,26 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(p.b0, (uint32_t)(NN ? K : N) * ldb_b);
   const __amdgpu_buffer_rsrc_t rs_none = make_rsrc(p.a, 0u);    // copies that read nothing
 
-  // per-lane copy offsets: 8 instructions for each tile (1 KB each); rows past M read as zero
+  // Copies: 8 instructions per tile per wave, 1 KB each; rows past M read as zero.  Copy i
+  // reads rows 32 i further down (NN: k-rows 8 i) than copy 0 with the same swizzle.  NT
+  // keeps one per-lane offset per operand and adds the wave-uniform step in the scalar
+  // offset; NN keeps all eight per-lane offsets (the register allocator assigns the NN
+  // loop's accumulators with fewer moves that way).
   const int lrow = lane >> 3, lphys = lane & 7;
-  uint32_t a_off[8], b_off[8];
+  constexpr int NOFF = NN ? 8 : 1;
+  uint32_t a_off[NOFF], b_off[NOFF];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NOFF; ++i) {
     const int row = (i * NW + wave) * 8 + lrow;
     a_off[i] = (uint32_t)(m0 + row) * lda_b + ((lphys ^ swz(row & 15)) << 4);
-    if constexpr (NN) {           // k-rows 2q, 2q+1 of the stage, 32 chunks each
+    if constexpr (NN) {           // k-rows 2q, 2q+1 of the stage (q = i NW + wave), 32 chunks each
       const int k = 2 * (i * NW + wave) + (lane >> 5), chunk = (lane & 31) ^ (2 * (k & 3));
       b_off[i] = (uint32_t)k * ldb_b + (uint32_t)(n0 + 8 * chunk) * 2u;
     } else {
       b_off[i] = (uint32_t)(n0 + row) * ldb_b + ((lphys ^ swz(row & 15)) << 4);
     }
   }
+  const uint32_t a_step = NN ? 0u : 32u * lda_b, b_step = NN ? 0u : 32u * ldb_b;
   auto q_dst = [&](int i) { const int q = i * NW + wave; return BM * 128 + q * 1024 + (NN ? (q >> 2) * kG16NNPad : 0); };
   auto copy = [](__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
@@ -87,10 +95,11 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   auto copy_stage = [&](int kt, uint8_t* sb) {
     const bool valid = kt < K / 64;
     const __amdgpu_buffer_rsrc_t ra = valid ? rs_a : rs_none, rb = valid ? rs_b : rs_none;
+    const uint32_t ka = (uint32_t)kt * 128u, kb = NN ? (uint32_t)kt * 64u * ldb_b : (uint32_t)kt * 128u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) copy(ra, a_off[i], (uint32_t)kt * 128u, sb + (i * NW + wave) * 1024);
+    for (int i = 0; i < 8; ++i) copy(ra, a_off[NN ? i : 0], ka + i * a_step, sb + (i * NW + wave) * 1024);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) copy(rb, b_off[i], NN ? (uint32_t)kt * 64u * ldb_b : (uint32_t)kt * 128u, sb + q_dst(i));
+    for (int i = 0; i < 8; ++i) copy(rb, b_off[NN ? i : 0], kb + i * b_step, sb + q_dst(i));
   };
 
   f32x4 acc[8][8];
@@ -103,7 +112,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   // wn*128 + 16 j + l16, k = 32 ks + 8 lq ..), read in order of first use: fa[0], fb[0..7], fa[1..7]
   const int a_base0 = g16_off(wm * 128 + l16, lq), a_base1 = g16_off(wm * 128 + l16, 4 + lq);
   const int b_base0 = BM * 128 + g16_off(wn * 128 + l16, lq), b_base1 = BM * 128 + g16_off(wn * 128 + l16, 4 + lq);
-  auto ldf_rows = [&](const uint8_t* s, int ks, u32x4* fa, u32x4* fb) {   // both tiles k-contiguous rows
+  auto ldf_rows = [&](const uint8_t* s, int ks, u32x4* fa, u32x4* fb) {   // NT: both tiles k-contiguous rows
     const int a = ks ? a_base1 : a_base0, b = ks ? b_base1 : b_base0;
     fa[0] = lds_ld16(s, a);
 #pragma unroll
@@ -144,45 +153,74 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = mfma_bf16(fb[j], fa[i], acc[i][j]);
+      for (int j = 0; j < 8; ++j) {
+        acc[i][j] = mfma_bf16(fb[j], fa[i], acc[i][j]);
+        // NT: keep each result in its accumulator's AGPRs (an empty asm with an AGPR
+        // operand); otherwise the allocator moves some accumulators through VGPRs
+        if constexpr (!NN) asm volatile("" : "+a"(acc[i][j]));
+      }
   };
 
   constexpr int NRQ = NN ? 2 : 1;       // LDS read instructions per Q fragment
   const int KT = K / 64;
   u32x4 fa0[8], fb0[8], fa1[8], fb1[8];
-  copy_stage(0, smem0);
 
-  // Low-rank term through the second stage buffer while stage 0 lands: thread t writes
-  // row t of each tile (s.S[m0 + t][..] as bf16, E[n0 + t][..]) in the k-contiguous row
-  // layout, zero past r_epi.
-  if constexpr (SS > 0) {
-    const int m = m0 + tid;
-    const float* srow = p.S + (size_t)min(m, M - 1) * p.ld_s;
+  // The low-rank term is one more k-tile, "stage -1" in the second stage buffer: its P
+  // tile holds s.S[m0 + t][0..63] as bf16 and its Q tile E's 64 ranks in the layout of a
+  // regular Q stage (zero past r_epi and past M), so the k-loop multiplies it with its own
+  // code and no MFMA runs before the loop.  Its loads go out first, all at once,
+  // branch-free and as 16-byte vectors (indices clamped into range, values zeroed after
+  // the load): thread t loads row t of S and, for NT, row t of E ([N, r]); for NN the E
+  // tile is the rank rows of E^T ([r, N], E[n][j] at n + j e_ldj), 32 16-byte chunks each.
+  // The caller guarantees 16-byte aligned S rows and E rows (or rank rows), r_epi a
+  // multiple of 8 and at most 64, and a single E segment (e_jsplit >= r_epi).
+  f32x4 sv[LR ? 16 : 1];
+  u32x4 ev[LR ? 8 : 1];
+  if constexpr (LR) {
+    const float* srow = p.S + (size_t)min(m0 + tid, M - 1) * p.ld_s;
 #pragma unroll
-    for (int c = 0; c < 4 * SS; ++c) {
-      const int k = 8 * c;
-      u32x4 v;
+    for (int q = 0; q < 16; ++q)
+      sv[q] = (4 * q < p.r_epi) ? *reinterpret_cast<const f32x4*>(srow + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint16_t* e0 = static_cast<const uint16_t*>(p.e0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = (m < M && k + 2 * e < p.r_epi) ? srow[k + 2 * e] * p.s_epi : 0.f;
-        const float hi = (m < M && k + 2 * e + 1 < p.r_epi) ? srow[k + 2 * e + 1] * p.s_epi : 0.f;
-        v[e] = pack_bf16x2(lo, hi);
+    for (int c = 0; c < 8; ++c) {
+      if constexpr (NN) {       // rank row j = 8 c + t / 32, 16-byte chunk t % 32 of its 256 columns
+        const int j = 8 * c + (tid >> 5);
+        ev[c] = *reinterpret_cast<const u32x4*>(e0 + (size_t)min(j, p.r_epi - 1) * p.e_ldj + n0 + 8 * (tid & 31));
+        if (j >= p.r_epi) ev[c] = u32x4{0u, 0u, 0u, 0u};
+      } else {                  // ranks 8 c .. 8 c + 7 of row n0 + t
+        ev[c] = (8 * c < p.r_epi) ? *reinterpret_cast<const u32x4*>(e0 + (size_t)(n0 + tid) * p.e_ldn + 8 * c)
+                                  : u32x4{0u, 0u, 0u, 0u};
       }
-      lds_st16(smem1, g16_off(tid, c), v);
-      lds_st16(smem1, BM * 128 + g16_off(tid, c), e_frag(p, n0 + tid, k));
-    }
-    __syncthreads();
-    ldf_rows(smem1, 0, fa0, fb0);
-    mm(fa0, fb0);
-    if constexpr (SS > 1) {
-      ldf_rows(smem1, 1, fa1, fb1);
-      mm(fa1, fb1);
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  copy_stage(1, smem1);
-  ldf(smem0, 0, fa0, fb0);
+  copy_stage(0, smem0);
+  if constexpr (LR) {
+    const float sc = (m0 + tid < M) ? p.s_epi : 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      u32x4 v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 s4 = sv[2 * c + (q >> 1)];
+        v[q] = pack_bf16x2(s4[2 * (q & 1)] * sc, s4[2 * (q & 1) + 1] * sc);
+      }
+      lds_st16(smem1, g16_off(tid, c), v);
+      if constexpr (NN) {
+        const int j = 8 * c + (tid >> 5), ch = tid & 31;
+        lds_st16(smem1, BM * 128 + g16_nn_row(j) + ((ch ^ (2 * (j & 3))) << 4), ev[c]);
+      } else {
+        lds_st16(smem1, BM * 128 + g16_off(tid, c), ev[c]);
+      }
+    }
+    __syncthreads();
+    ldf(smem1, 0, fa0, fb0);
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    copy_stage(1, smem1);
+    ldf(smem0, 0, fa0, fb0);
+  }
   __builtin_amdgcn_s_waitcnt(0xc07f);     // settle the prologue's LDS / scalar reads
 
   auto tile = [&](auto par_c, int kt) {
@@ -191,7 +229,9 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
     uint8_t* nxt = PAR ? smem0 : smem1;
     // The accumulators enter every tile in AGPRs (an empty asm with an AGPR operand):
     // without this the register allocator moves some of them between register files
-    // inside the loop and runs out of registers for the fragments.
+    // inside the loop and runs out of registers for the fragments.  (Allocation of this
+    // loop is fragile: the pins here and in mm were chosen by compiling the variants and
+    // counting the AGPR moves and spills left in the loop.)
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -228,11 +268,13 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  // One loop body for every k-tile, so the accumulators keep their registers to the end:
-  // an odd count runs one more tile, whose stage the empty copies filled with zeros.
-  for (int kt = 0; kt < KT; kt += 2) {
-    tile(std::integral_constant<int, 0>{}, kt);
-    tile(std::integral_constant<int, 1>{}, kt + 1);
+  // One loop body for every k-tile (from the low-rank tile -1 when there is one), so the
+  // accumulators keep their registers to the end: an odd count runs one more tile, whose
+  // stage the empty copies filled with zeros.
+  constexpr int P0 = LR ? 1 : 0;
+  for (int kt = LR ? -1 : 0; kt < KT; kt += 2) {
+    tile(std::integral_constant<int, P0>{}, kt);
+    tile(std::integral_constant<int, 1 - P0>{}, kt + 1);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the last (empty) copies
   __syncthreads();
