@@ -96,6 +96,7 @@ LoraBwdWs plan_lora_bwd(Bump& b, int M, int N, int K, int r, bool need_u) {
 
 struct DoraBwdWs {
   float* V; float* partT; float* cs; float* wB; float* partA; float* partQ; float* Qm;
+  uint16_t* dYg;                   // dY.diag(g) in bf16 [M, N]
   float* partbias; float* csbias;
   int nsT, msT, nsA, msA, nsW, msW, nsQ, msQ, rp;
 };
@@ -115,6 +116,7 @@ DoraBwdWs plan_dora_bwd(Bump& b, int M, int N, int K, int r) {
   w.Qm = b.take<float>((size_t)r * r);
   w.partbias = b.take<float>((size_t)w.nsT * N * 16);
   w.csbias = b.take<float>((size_t)w.nsT * N);
+  w.dYg = b.take<uint16_t>((size_t)M * N);
   return w;
 }
 
@@ -501,13 +503,15 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, c
     // V = (dY.diag(g)).B, the scaled B read in place as a [N, r] matrix
     LDL_TRY(rowproj_t(M, N, r, dY, N, Bh, r, g, w.V, r, 1.f, st));
     if (dX) {
+      // dX = (dY.diag(g)).W0 + s.V.A: dY.diag(g) rounded to bf16 once, then the plain product
+      LDL_TRY(launch_scale_cols(dY, M, N, N, g, w.dYg, st));
       GemmParams p = gp0();
       p.M = M; p.N = K; p.K = N;
-      p.a = dY; p.lda = N; p.a_colscale = g; p.b0 = W0; p.b1 = W0; p.ldb = K; p.kseg = N;
+      p.a = w.dYg; p.lda = N; p.b0 = W0; p.b1 = W0; p.ldb = K; p.kseg = N;
       p.S = w.V; p.ld_s = r; p.r_epi = r; p.s_epi = s;
       p.e0 = A; p.e1 = A; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = r;
       p.out = dX; p.ldo = K;
-      LDL_TRY(gemm_timed(1, GK_NN_SCALE, p, st));
+      LDL_TRY(gemm_timed(1, GK_NN_PLAIN, p, st));
     }
     // s.V^T.X into the first nsA partials of dA
     jobs[nj] = cpp(M, K, r, X, K, w.V, r, s, nullptr, 0, 0, w.msA, w.partA, nullptr);

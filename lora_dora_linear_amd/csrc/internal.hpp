@@ -66,6 +66,7 @@ hipError_t launch_fill_zero(float* p, size_t n, hipStream_t st);
 hipError_t launch_rowsumsq(const void* W0, int dtype_bf16, int N, int K, float* out, hipStream_t st);
 hipError_t launch_dora_norm(int N, int r, float s, float eps, const float* w0_sumsq, const float* P,
                             const float* G, const uint16_t* B, const float* m, float* norm, float* g, hipStream_t st);
+hipError_t launch_scale_cols(const void* in, int M, int N, int ld, const float* g, void* out, hipStream_t st);
 hipError_t launch_dora_finalize(int N, int r, float s, float eps, const float* partT, const float* cspart,
                                 int nsplit, int rpT, const float* norm, const float* g, const float* m,
                                 const float* P, const float* G, const uint16_t* B,

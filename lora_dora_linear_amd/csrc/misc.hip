@@ -42,62 +42,139 @@ __global__ __launch_bounds__(256) void rowsumsq_kernel(const void* W0, int N, in
   if (lane == 0) out[n] = acc;
 }
 
+// Broadcast of lane l's value (l wave-uniform).
+__device__ __forceinline__ float lane_bcast(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 // Closed-form row norm: nu^2 = c + 2s <B_n, P_n> + s^2 B_n G B_n^T, clamped at 0;
-// g = m / max(nu, eps).  One thread per output row; G staged in LDS.
+// g = m / max(nu, eps).  One wave per output row, lane j holding ranks j and j + 64
+// (r <= 128); G staged in LDS transposed so that lane j reads G[j][l] at consecutive
+// addresses; B_n[l] broadcast from the lane that holds it.
 __global__ __launch_bounds__(256) void dora_norm_kernel(int N, int r, float s, float eps, const float* c,
                                                         const float* P, const float* G, const uint16_t* B,
                                                         const float* m, float* norm, float* g) {
-  extern __shared__ float sG[];
-  for (int i = threadIdx.x; i < r * r; i += blockDim.x) sG[i] = G[i];
-  __syncthreads();
-  const int n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n >= N) return;
+  extern __shared__ float sGt[];                 // sGt[l r + j] = G[j][l]
+  const int lane = threadIdx.x & 63;
+  const int n = min(blockIdx.x * 4 + (threadIdx.x >> 6), N - 1);   // rows past N redo row N-1, unstored
+  // the row's operands first, so their latency overlaps the staging of G
   const uint16_t* bn = B + (size_t)n * r;
   const float* pn = P + (size_t)n * r;
-  float t1 = 0.f, t2 = 0.f;
-  for (int j = 0; j < r; ++j) {
-    const float bj = bf16_to_f32(bn[j]);
-    t1 += bj * pn[j];
-    float bg = 0.f;
-    for (int l = 0; l < r; ++l) bg += sG[j * r + l] * bf16_to_f32(bn[l]);
-    t2 += bj * bg;
+  const bool h0 = lane < r, h1 = lane + 64 < r;
+  const float b0 = h0 ? bf16_to_f32(bn[lane]) : 0.f, b1 = h1 ? bf16_to_f32(bn[lane + 64]) : 0.f;
+  const float p0 = h0 ? pn[lane] : 0.f, p1 = h1 ? pn[lane + 64] : 0.f;
+  const float cn = c[n], mn = m[n];
+  for (int i = threadIdx.x; i < r * r; i += blockDim.x) sGt[(i % r) * r + i / r] = G[i];
+  __syncthreads();
+  float t1 = b0 * p0 + b1 * p1;
+  float bg0 = 0.f, bg1 = 0.f;                    // (G B_n^T)[j] for the lane's ranks
+  for (int l = 0; l < r; ++l) {
+    const float bl = l < 64 ? lane_bcast(b0, l) : lane_bcast(b1, l - 64);
+    if (h0) bg0 += sGt[l * r + lane] * bl;
+    if (h1) bg1 += sGt[l * r + lane + 64] * bl;
   }
-  const float nu2 = c[n] + 2.f * s * t1 + s * s * t2;
-  const float nu = sqrtf(fmaxf(nu2, 0.f));
-  norm[n] = nu;
-  g[n] = m[n] / fmaxf(nu, eps);
+  float t2 = b0 * bg0 + b1 * bg1;
+  t1 = wave_sum(t1);
+  t2 = wave_sum(t2);
+  if (lane == 0 && blockIdx.x * 4 + (threadIdx.x >> 6) < N) {
+    const float nu2 = cn + 2.f * s * t1 + s * s * t2;
+    const float nu = sqrtf(fmaxf(nu2, 0.f));
+    norm[n] = nu;
+    g[n] = mn / fmaxf(nu, eps);
+  }
 }
 
 // Backward per output row, with the norm kept in the graph:
 //   T = sum_splits partT (= dY^T.U row n);  dg = sum_splits cspart (= sum_m dY*Z)
 //   dm = dg / max(nu, eps);  w = -dg m / (2 nu^3) if nu > eps else 0
 //   dB[n,:] = s g_n T + w (2s P_n + 2s^2 (B G)_n);  wB[n,:] = 2s w B_n
+// One wave per output row, lane j computing ranks j and j + 64 (r <= 128); every sum
+// runs in a fixed order (splits in order, l = 0 .. r-1).
 __global__ __launch_bounds__(256) void dora_finalize_kernel(int N, int r, float s, float eps, const float* partT,
                                                             const float* cspart, int nsplit, int rpT,
                                                             const float* norm, const float* g, const float* m,
                                                             const float* P, const float* G, const uint16_t* B,
                                                             float* dB, float* dm, float* wB) {
   extern __shared__ float sG[];
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int n = min(row, N - 1);                 // rows past N redo row N-1, unstored
+  const bool live = row < N;
+  const bool h0 = lane < r, h1 = lane + 64 < r;
+  // loads first (their latency overlaps the staging of G): the split partials of dg and of
+  // T for the lane's ranks, eight splits in flight, each sum in split order
+  float dg = 0.f, t0 = 0.f, t1 = 0.f;
+  {
+    const float* cp = cspart + n;
+    const float* tp = partT + (size_t)n * rpT + lane;
+    const size_t ts = (size_t)N * rpT;
+    int sp = 0;
+    for (; sp + 8 <= nsplit; sp += 8) {
+      float c8[8], a8[8], b8[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        c8[q] = cp[(size_t)(sp + q) * N];
+        a8[q] = h0 ? tp[(sp + q) * ts] : 0.f;
+        b8[q] = h1 ? tp[(sp + q) * ts + 64] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) { dg += c8[q]; t0 += a8[q]; t1 += b8[q]; }
+    }
+    for (; sp < nsplit; ++sp) {
+      dg += cp[(size_t)sp * N];
+      if (h0) t0 += tp[sp * ts];
+      if (h1) t1 += tp[sp * ts + 64];
+    }
+  }
+  const uint16_t* bn = B + (size_t)n * r;
+  const float b0 = h0 ? bf16_to_f32(bn[lane]) : 0.f, b1 = h1 ? bf16_to_f32(bn[lane + 64]) : 0.f;
+  const float p0 = h0 ? P[(size_t)n * r + lane] : 0.f, p1 = h1 ? P[(size_t)n * r + lane + 64] : 0.f;
+  const float nu = norm[n], gn = g[n], mn = m[n];
   for (int i = threadIdx.x; i < r * r; i += blockDim.x) sG[i] = G[i];
   __syncthreads();
-  const int n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n >= N) return;
-  float dg = 0.f;
-  for (int sp = 0; sp < nsplit; ++sp) dg += cspart[(size_t)sp * N + n];
-  const float nu = norm[n];
   const float den = fmaxf(nu, eps);
-  dm[n] = dg / den;
-  const float w = (nu > eps) ? (-dg * m[n] / (2.f * nu * nu * nu)) : 0.f;
-  const uint16_t* bn = B + (size_t)n * r;
-  const float gn = g[n];
-  for (int j = 0; j < r; ++j) {
-    float t = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) t += partT[((size_t)sp * N + n) * rpT + j];
-    float bg = 0.f;
-    for (int l = 0; l < r; ++l) bg += bf16_to_f32(bn[l]) * sG[l * r + j];
-    dB[(size_t)n * r + j] = s * gn * t + w * (2.f * s * P[(size_t)n * r + j] + 2.f * s * s * bg);
-    wB[(size_t)n * r + j] = 2.f * s * w * bf16_to_f32(bn[j]);
+  if (lane == 0 && live) dm[n] = dg / den;
+  const float w = (nu > eps) ? (-dg * mn / (2.f * nu * nu * nu)) : 0.f;
+  float bg0 = 0.f, bg1 = 0.f;                    // (B_n G)[j] for the lane's ranks
+  for (int l = 0; l < r; ++l) {
+    const float bl = l < 64 ? lane_bcast(b0, l) : lane_bcast(b1, l - 64);
+    if (h0) bg0 += bl * sG[l * r + lane];
+    if (h1) bg1 += bl * sG[l * r + lane + 64];
   }
+  if (!live) return;
+  if (h0) {
+    dB[(size_t)n * r + lane] = s * gn * t0 + w * (2.f * s * p0 + 2.f * s * s * bg0);
+    wB[(size_t)n * r + lane] = 2.f * s * w * b0;
+  }
+  if (h1) {
+    dB[(size_t)n * r + lane + 64] = s * gn * t1 + w * (2.f * s * p1 + 2.f * s * s * bg1);
+    wB[(size_t)n * r + lane + 64] = 2.f * s * w * b1;
+  }
+}
+
+// out[m, n] = bf16(in[m, n] * g[n]) (round to nearest even): the DoRA backward's dY.diag(g),
+// written once so the input-gradient product runs as a plain bf16 GEMM (the same values
+// a fragment-wise scaling would feed the MFMAs).  8 columns per thread, rows of ld elements.
+__global__ __launch_bounds__(256) void scale_cols_kernel(const uint16_t* in, int M, int N, int ld, const float* g,
+                                                         uint16_t* out) {
+  const int per_row = N / 8;
+  const size_t total = (size_t)M * per_row;
+  for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (size_t)gridDim.x * blockDim.x) {
+    const int m = (int)(t / per_row), c = (int)(t % per_row) * 8;
+    const u32x4 v = ld16(in + (size_t)m * ld + c);
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(g + c), s1 = *reinterpret_cast<const f32x4*>(g + c + 4);
+    st16(out + (size_t)m * ld + c, scale_bf16x8(v, s0, s1));
+  }
+}
+
+hipError_t launch_scale_cols(const void* in, int M, int N, int ld, const float* g, void* out, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  const size_t total = (size_t)M * (N / 8);
+  size_t blocks = (total + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(scale_cols_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const uint16_t*>(in), M,
+                     N, ld, g, static_cast<uint16_t*>(out));
+  return hipGetLastError();
 }
 
 hipError_t launch_rowsumsq(const void* W0, int dtype_bf16, int N, int K, float* out, hipStream_t st) {
@@ -109,7 +186,7 @@ hipError_t launch_rowsumsq(const void* W0, int dtype_bf16, int N, int K, float* 
 
 hipError_t launch_dora_norm(int N, int r, float s, float eps, const float* w0_sumsq, const float* P,
                             const float* G, const uint16_t* B, const float* m, float* norm, float* g, hipStream_t st) {
-  hipLaunchKernelGGL(dora_norm_kernel, dim3((N + 255) / 256), dim3(256), r * r * sizeof(float), st,
+  hipLaunchKernelGGL(dora_norm_kernel, dim3((N + 3) / 4), dim3(256), r * r * sizeof(float), st,
                      N, r, s, eps, w0_sumsq, P, G, B, m, norm, g);
   return hipGetLastError();
 }
@@ -118,7 +195,7 @@ hipError_t launch_dora_finalize(int N, int r, float s, float eps, const float* p
                                 int nsplit, int rpT, const float* norm, const float* g, const float* m,
                                 const float* P, const float* G, const uint16_t* B,
                                 float* dB, float* dm, float* wB, hipStream_t st) {
-  hipLaunchKernelGGL(dora_finalize_kernel, dim3((N + 255) / 256), dim3(256), r * r * sizeof(float), st,
+  hipLaunchKernelGGL(dora_finalize_kernel, dim3((N + 3) / 4), dim3(256), r * r * sizeof(float), st,
                      N, r, s, eps, partT, cspart, nsplit, rpT, norm, g, m, P, G, B, dB, dm, wB);
   return hipGetLastError();
 }

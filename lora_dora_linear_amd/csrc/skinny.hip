@@ -624,33 +624,52 @@ struct ReduceBatch {
   int blocks0;                    // blocks [0, blocks0) reduce job 0, the rest job 1
 };
 
-// One block per 64 partial rows c of one job: the [64][rp] slices of all splits
-// are summed in split order (float4 loads, coalesced), staged in LDS, then written
-// out with the finishing terms, consecutive threads on consecutive output columns.
+// One block per 32 partial rows c of one job: the [32][rp] slices of all splits
+// are summed in split order (float4 loads, coalesced, eight splits in flight),
+// staged in LDS, then written out with the finishing terms, consecutive threads on
+// consecutive output columns.  The optional Qm.Am addend (transposed jobs only: the
+// partial rows are the output columns) reads both operands from dynamic LDS: Qm
+// [rows, rq] (row stride rq + 1) and the block's 32 columns of Am [rq, cols].
+constexpr int kReduceRows = 32;
 __global__ __launch_bounds__(256) void reduce_parts_kernel(const ReduceBatch batch) {
-  __shared__ float tile[64 * 129];
+  constexpr int RB = kReduceRows;
+  __shared__ float tile[RB * 129];
+  extern __shared__ float dyn[];
   const int jobi = (int)blockIdx.x >= batch.blocks0 ? 1 : 0;
   const ReduceParams& p = batch.job[jobi];
-  const int c0 = ((int)blockIdx.x - (jobi ? batch.blocks0 : 0)) * 64;
+  const int c0 = ((int)blockIdx.x - (jobi ? batch.blocks0 : 0)) * RB;
   const int C = p.trans ? p.cols : p.rows;          // partial rows
   const int R = p.trans ? p.rows : p.cols;          // valid partial columns
   if (c0 >= C) return;
   const int tid = threadIdx.x;
   const int ld = p.rp + 1;
-  const int nvec = p.rp / 16;                       // float4 per thread: 64 * rp / 4 / 256
-  for (int v = 0; v < nvec; ++v) {
-    const int e = (v * 256 + tid) * 4;              // element offset inside the [64][rp] slice
+  const int nc = C - c0 < RB ? C - c0 : RB;
+  const bool addend = p.Qm != nullptr;
+  float* sQ = dyn;
+  float* sA = dyn + R * (p.rq + 1);
+  if (addend) {                                     // stage the addend's operands first
+    for (int e = tid; e < R * p.rq; e += 256) {
+      const int rr = e / p.rq, l = e % p.rq;
+      sQ[rr * (p.rq + 1) + l] = p.Qm[(size_t)rr * p.ldq + l];
+    }
+    for (int e = tid; e < p.rq * RB; e += 256) {
+      const int l = e / RB, cc = e % RB;
+      sA[e] = cc < nc ? bf16_to_f32(p.Am[(size_t)l * p.lda + c0 + cc]) : 0.f;
+    }
+  }
+  for (int e4 = tid; e4 < RB * p.rp / 4; e4 += 256) {
+    const int e = e4 * 4;                           // element offset inside the [RB][rp] slice
     const int cc = e / p.rp, j = e % p.rp;
     f32x4 acc = {0, 0, 0, 0};
     if (c0 + cc < C && j < R) {                     // columns >= R are padding (or another job's)
       const float* src = p.part + (size_t)(c0 + cc) * p.rp + j;
       int sp = 0;
-      for (; sp + 4 <= p.nsplit; sp += 4) {
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(src + (size_t)(sp + 0) * p.pstride);
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(src + (size_t)(sp + 1) * p.pstride);
-        const f32x4 a2 = *reinterpret_cast<const f32x4*>(src + (size_t)(sp + 2) * p.pstride);
-        const f32x4 a3 = *reinterpret_cast<const f32x4*>(src + (size_t)(sp + 3) * p.pstride);
-        acc += a0; acc += a1; acc += a2; acc += a3;
+      for (; sp + 8 <= p.nsplit; sp += 8) {
+        f32x4 a[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) a[q] = *reinterpret_cast<const f32x4*>(src + (size_t)(sp + q) * p.pstride);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc += a[q];
       }
       for (; sp < p.nsplit; ++sp) acc += *reinterpret_cast<const f32x4*>(src + (size_t)sp * p.pstride);
     }
@@ -658,18 +677,18 @@ __global__ __launch_bounds__(256) void reduce_parts_kernel(const ReduceBatch bat
     for (int i = 0; i < 4; ++i) tile[cc * ld + j + i] = acc[i];
   }
   __syncthreads();
-  const int nc = C - c0 < 64 ? C - c0 : 64;
-  for (int e = tid; e < R * 64; e += 256) {
+  for (int e = tid; e < R * RB; e += 256) {
     int cc, j;
-    if (p.trans) { j = e >> 6; cc = e & 63; } else { cc = e / R; j = e % R; }
+    if (p.trans) { j = e / RB; cc = e % RB; } else { cc = e / R; j = e % R; }
     if (cc >= nc) continue;
     const int c = c0 + cc;
     const int row = p.trans ? j : c, col = p.trans ? c : j;
     float v = tile[cc * ld + j] * p.alpha;
     if (p.rowscale != nullptr) v *= p.rowscale[row];
-    if (p.Qm != nullptr) {
+    if (addend) {
+      const float* q = sQ + j * (p.rq + 1);
       float t = 0.f;
-      for (int l = 0; l < p.rq; ++l) t += p.Qm[(size_t)row * p.ldq + l] * bf16_to_f32(p.Am[(size_t)l * p.lda + col]);
+      for (int l = 0; l < p.rq; ++l) t += q[l] * sA[l * RB + cc];
       v += p.alpha2 * t;
     }
     p.out[(size_t)row * p.ldo + col] = v;
@@ -819,7 +838,29 @@ hipError_t launch_colproj2(const ColProjParams& a, int nsplit_a, const ColProjPa
   return launch_colproj_batch(jobs, ns, 2, st);
 }
 
-static int reduce_blocks(const ReduceParams& p) { return ((p.trans ? p.cols : p.rows) + 63) / 64; }
+static int reduce_blocks(const ReduceParams& p) {
+  return ((p.trans ? p.cols : p.rows) + kReduceRows - 1) / kReduceRows;
+}
+// dynamic LDS of the Qm.Am addend (0 without one)
+static size_t reduce_lds(const ReduceParams& p) {
+  if (p.Qm == nullptr) return 0;
+  return ((size_t)p.rows * (p.rq + 1) + (size_t)p.rq * kReduceRows) * sizeof(float);
+}
+static hipError_t reduce_launch(const ReduceBatch& b, int blocks, size_t lds, hipStream_t st) {
+  for (int i = 0; i < b.njobs; ++i)           // the addend is staged for transposed jobs only
+    if (b.job[i].Qm != nullptr && !b.job[i].trans) return hipErrorInvalidValue;
+  if (lds > 48 * 1024) {
+    static bool raised = false;
+    if (!raised) {
+      const hipError_t e = hipFuncSetAttribute((const void*)reduce_parts_kernel,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, 120 * 1024);
+      if (e != hipSuccess) return e;
+      raised = true;
+    }
+  }
+  hipLaunchKernelGGL(reduce_parts_kernel, dim3(blocks), dim3(256), lds, st, b);
+  return hipGetLastError();
+}
 
 hipError_t launch_reduce2(const ReduceParams& a, const ReduceParams& b2, hipStream_t st) {
   ReduceBatch b;
@@ -829,8 +870,8 @@ hipError_t launch_reduce2(const ReduceParams& a, const ReduceParams& b2, hipStre
   b.blocks0 = reduce_blocks(a);
   const int blocks = b.blocks0 + reduce_blocks(b2);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(reduce_parts_kernel, dim3(blocks), dim3(256), 0, st, b);
-  return hipGetLastError();
+  const size_t la = reduce_lds(a), lb = reduce_lds(b2);
+  return reduce_launch(b, blocks, la > lb ? la : lb, st);
 }
 
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t st) {
@@ -840,8 +881,7 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t st) {
   b.njobs = 1;
   b.blocks0 = reduce_blocks(p);
   if (b.blocks0 == 0) return hipSuccess;
-  hipLaunchKernelGGL(reduce_parts_kernel, dim3(b.blocks0), dim3(256), 0, st, b);
-  return hipGetLastError();
+  return reduce_launch(b, b.blocks0, reduce_lds(p), st);
 }
 
 hipError_t launch_reduce_colsum(const float* cspart, int nsplit, int C, float* out, hipStream_t st) {
