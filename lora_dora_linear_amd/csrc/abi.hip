@@ -158,6 +158,20 @@ hipError_t rowproj(int M, int K, int R, const void* P, int ldp, const void* q0, 
   p.M = M; p.K = K; p.R = R; p.R0 = R0;
   p.P = static_cast<const uint16_t*>(P); p.ldp = ldp;
   p.q0 = static_cast<const uint16_t*>(q0); p.q1 = static_cast<const uint16_t*>(q1 ? q1 : q0); p.ldq = ldq;
+  p.P1 = nullptr; p.p_split = M;
+  p.q_trans = 0; p.q_kscale = nullptr;
+  p.out = out; p.ldo = ldo; p.scale = scale;
+  return launch_rowproj(p, st);
+}
+
+// rowproj over the rows of P followed by the rows of P1 (M0 + M1 rows, both with leading dim ldp)
+hipError_t rowproj2(int M0, int M1, int K, int R, const void* P, const void* P1, int ldp, const void* q0, int ldq,
+                    float* out, int ldo, float scale, hipStream_t st) {
+  RowProjParams p;
+  p.M = M0 + M1; p.K = K; p.R = R; p.R0 = R;
+  p.P = static_cast<const uint16_t*>(P); p.ldp = ldp;
+  p.P1 = static_cast<const uint16_t*>(P1); p.p_split = M0;
+  p.q0 = p.q1 = static_cast<const uint16_t*>(q0); p.ldq = ldq;
   p.q_trans = 0; p.q_kscale = nullptr;
   p.out = out; p.ldo = ldo; p.scale = scale;
   return launch_rowproj(p, st);
@@ -169,6 +183,7 @@ hipError_t rowproj_t(int M, int K, int R, const void* P, int ldp, const void* Bq
   RowProjParams p;
   p.M = M; p.K = K; p.R = R; p.R0 = R;
   p.P = static_cast<const uint16_t*>(P); p.ldp = ldp;
+  p.P1 = nullptr; p.p_split = M;
   p.q0 = p.q1 = static_cast<const uint16_t*>(Bq); p.ldq = ldb;
   p.q_trans = 1; p.q_kscale = kscale;
   p.out = out; p.ldo = ldo; p.scale = scale;
@@ -452,8 +467,8 @@ int dora_linear_fwd(int M, int N, int K, int r, float s, float eps, int dtype, c
   float* P = state + 2 * (size_t)N;
   float* G = P + (size_t)N * r;
   // the norm terms: P = W0.A^T, G = A.A^T, then nu and g (independent of M)
-  LDL_TRY(rowproj(N, K, r, W0, K, A, nullptr, r, K, P, r, 1.f, st));
-  LDL_TRY(rowproj(r, K, r, A, K, A, nullptr, r, K, G, r, 1.f, st));
+  // (G is stored right after P with the same row length: one launch over the rows of W0 then A)
+  LDL_TRY(rowproj2(N, r, K, r, W0, A, K, A, K, P, r, 1.f, st));
   LDL_TRY(launch_dora_norm(N, r, s, eps, w0_sumsq, P, G, static_cast<const uint16_t*>(B), m, norm, g, st));
   if (M == 0) return LDL_OK;
   LDL_TRY(rowproj(M, K, r, X, K, A, nullptr, r, K, U_save, r, 1.f, st));

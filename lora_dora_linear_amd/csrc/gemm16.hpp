@@ -35,9 +35,11 @@ __device__ __forceinline__ int g16_off(int row, int chunk) { return row * 128 + 
 constexpr int kG16NNRow = 512, kG16NNPad = 128;
 __host__ __device__ constexpr int g16_nn_row(int k) { return k * kG16NNRow + (k >> 3) * kG16NNPad; }
 
-// NN: Q is [K, N] (else [N, K]); LR: with a low-rank term (r_epi in 8, 16, .., 64)
-template <bool NN, bool LR>
+// NN: Q is [K, N] (else [N, K]); LR: with a low-rank term (r_epi in 8, 16, .., 64);
+// DORA (NT only): two outputs, out2 = z (the unscaled sum) and out = z * col_scale[n] + bias[n]
+template <bool NN, bool LR, bool DORA = false>
 __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
+  static_assert(!(NN && DORA), "the row-scaled epilogue is a forward (NT) epilogue");
   constexpr int BM = 256, BN = 256, NW = 4;
   constexpr int QB = NN ? g16_nn_row(64) : BN * 128;
   constexpr int SB = BM * 128 + QB;                 // one stage: P tile then Q tile
@@ -281,38 +283,79 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
 
   static_assert(128 * 512 <= SB, "half of the output tile fits in a stage buffer");
   // ---- epilogue: bias, bf16, staged through LDS (rows < 128 in smem0, the rest in smem1),
-  // written out as whole 16-byte row segments
+  // written out as whole 16-byte row segments.  DORA writes z first, then y = z g + bias
+  // (both from the fp32 accumulators).
   auto st_ptr = [&](int r, int col) -> uint8_t* {
     uint8_t* base = r < 128 ? smem0 : smem1;
     const int rr = r & 127;
     return base + rr * 512 + ((((col >> 3) ^ (rr & 31))) << 4) + ((col & 4) << 1);
   };
+  auto emit = [&](auto z_c, void* dst, int ldo) {
+    constexpr bool Z = decltype(z_c)::value;       // DORA's unscaled output
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = wm * 128 + i * 16 + l16;
+    for (int i = 0; i < 8; ++i) {
+      const int r = wm * 128 + i * 16 + l16;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int cl = wn * 128 + j * 16 + 4 * lq;
-      float b4[4] = {0.f, 0.f, 0.f, 0.f};
-      if (p.bias != nullptr) {
-        const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n0 + cl);
-        b4[0] = bf16_lo(bb[0]); b4[1] = bf16_hi(bb[0]); b4[2] = bf16_lo(bb[1]); b4[3] = bf16_hi(bb[1]);
+      for (int j = 0; j < 8; ++j) {
+        const int cl = wn * 128 + j * 16 + 4 * lq;
+        float b4[4] = {0.f, 0.f, 0.f, 0.f};
+        if (!Z && p.bias != nullptr) {
+          const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n0 + cl);
+          b4[0] = bf16_lo(bb[0]); b4[1] = bf16_hi(bb[0]); b4[2] = bf16_lo(bb[1]); b4[3] = bf16_hi(bb[1]);
+        }
+        f32x4 v = acc[i][j];
+        if constexpr (DORA && !Z) v *= *reinterpret_cast<const f32x4*>(p.col_scale + n0 + cl);
+        u32x2 w;
+        w[0] = pack_bf16x2(v[0] + b4[0], v[1] + b4[1]);
+        w[1] = pack_bf16x2(v[2] + b4[2], v[3] + b4[3]);
+        *reinterpret_cast<u32x2*>(st_ptr(r, cl)) = w;
       }
-      const f32x4 v = acc[i][j];
-      u32x2 w;
-      w[0] = pack_bf16x2(v[0] + b4[0], v[1] + b4[1]);
-      w[1] = pack_bf16x2(v[2] + b4[2], v[3] + b4[3]);
-      *reinterpret_cast<u32x2*>(st_ptr(r, cl)) = w;
     }
-  }
-  __syncthreads();
-  uint16_t* out = static_cast<uint16_t*>(p.out);
-  for (int idx = tid; idx < BM * 32; idx += 256) {
-    const int r = idx >> 5, c = idx & 31;
-    if (m0 + r < M) {
-      const uint8_t* base = r < 128 ? smem0 : smem1;
-      const int rr = r & 127;
-      st16(out + (size_t)(m0 + r) * p.ldo + n0 + c * 8, lds_ld16(base, rr * 512 + ((c ^ (rr & 31)) << 4)));
+    __syncthreads();
+    uint16_t* out = static_cast<uint16_t*>(dst);
+    for (int idx = tid; idx < BM * 32; idx += 256) {
+      const int r = idx >> 5, c = idx & 31;
+      if (m0 + r < M) {
+        const uint8_t* base = r < 128 ? smem0 : smem1;
+        const int rr = r & 127;
+        st16(out + (size_t)(m0 + r) * ldo + n0 + c * 8, lds_ld16(base, rr * 512 + ((c ^ (rr & 31)) << 4)));
+      }
+    }
+  };
+  if constexpr (DORA) {
+    emit(std::true_type{}, p.out2, p.ldo2);
+    __syncthreads();                               // the staging buffers are free again
+    emit(std::false_type{}, p.out, p.ldo);
+  } else {
+    // (written out rather than through emit: the lambda changed the register allocation of
+    // the NN k-loop and cost ~10 % there)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = wm * 128 + i * 16 + l16;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int cl = wn * 128 + j * 16 + 4 * lq;
+        float b4[4] = {0.f, 0.f, 0.f, 0.f};
+        if (p.bias != nullptr) {
+          const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n0 + cl);
+          b4[0] = bf16_lo(bb[0]); b4[1] = bf16_hi(bb[0]); b4[2] = bf16_lo(bb[1]); b4[3] = bf16_hi(bb[1]);
+        }
+        const f32x4 v = acc[i][j];
+        u32x2 w;
+        w[0] = pack_bf16x2(v[0] + b4[0], v[1] + b4[1]);
+        w[1] = pack_bf16x2(v[2] + b4[2], v[3] + b4[3]);
+        *reinterpret_cast<u32x2*>(st_ptr(r, cl)) = w;
+      }
+    }
+    __syncthreads();
+    uint16_t* out = static_cast<uint16_t*>(p.out);
+    for (int idx = tid; idx < BM * 32; idx += 256) {
+      const int r = idx >> 5, c = idx & 31;
+      if (m0 + r < M) {
+        const uint8_t* base = r < 128 ? smem0 : smem1;
+        const int rr = r & 127;
+        st16(out + (size_t)(m0 + r) * p.ldo + n0 + c * 8, lds_ld16(base, rr * 512 + ((c ^ (rr & 31)) << 4)));
+      }
     }
   }
 }

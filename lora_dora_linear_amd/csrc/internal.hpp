@@ -8,7 +8,8 @@ namespace ldl {
 
 struct RowProjParams {
   int M, K, R, R0;                 // Q rows j < R0 come from q0, rows j >= R0 from q1
-  const uint16_t* P; int ldp;      // [M, K] bf16
+  const uint16_t* P; int ldp;      // [M, K] bf16; rows m >= p_split come from P1 (row m - p_split)
+  const uint16_t* P1; int p_split; // P1 == nullptr: one segment (p_split = M)
   const uint16_t* q0; const uint16_t* q1; int ldq;
   int q_trans;                     // 1: Q(j, k) = q0[k * ldq + j] (a [K, R] matrix such as lora_up B)
   const float* q_kscale;           // q_trans only, optional: Q(j, k) *= q_kscale[k] (rounded to bf16)

@@ -35,7 +35,8 @@ __global__ __launch_bounds__(512) void rowproj_kernel(const RowProjParams p) {
   const int m0 = blockIdx.x * 16;
   const int m = m0 + lr;
   const bool mval = m < p.M;
-  const uint16_t* prow = p.P + (size_t)(mval ? m : 0) * p.ldp + lq * 8;
+  const uint16_t* prow = (p.P1 != nullptr && m >= p.p_split ? p.P1 + (size_t)(m - p.p_split) * p.ldp
+                                                             : p.P + (size_t)(mval ? m : 0) * p.ldp) + lq * 8;
 
   const uint16_t* qrow[NB];
   bool qval[NB];
@@ -135,18 +136,20 @@ __global__ __launch_bounds__(512) void rowproj_kernel(const RowProjParams p) {
 // 16-byte chunk c of row r at physical chunk c ^ (r & 15); a transposed Q
 // (a [K, R] matrix, rows of R bf16) is stored as-is and read back with the
 // transposing LDS read.
-template <int RP>
+template <int RP, bool KS>
 struct RowStream {
   static constexpr int KC = RP <= 32 ? 512 : (RP == 64 ? 256 : 128);   // elements per chunk
   static constexpr int RL = KC * 2;                  // bytes per staged row
   static constexpr int PB = 16 * RL;                 // P slice
   static constexpr int QB = RP * RL;                 // Q slice (RP rows of KC, or KC rows of R <= RP)
-  static constexpr int GB = 4096;                    // k-scale slice: KC floats, four 1 KB copies
+  static constexpr int GB = KS ? 4096 : 0;           // k-scale slice: KC floats, four 1 KB copies
   static constexpr int SB = PB + QB + GB;
-  static constexpr int STAGES = RP <= 16 ? 4 : 3;
-  static constexpr int NI = (PB + QB) / 1024 / 4 + 1;  // copy instructions per wave per chunk
-  static_assert(STAGES * SB <= 160 * 1024, "LDS ring fits");
+  // as many ring stages as the LDS holds (at most 5): STAGES-1 chunks stay in flight
+  static constexpr int STAGES = (160 * 1024) / SB > 5 ? 5 : (160 * 1024) / SB;
+  static constexpr int NI = (PB + QB) / 1024 / 4 + (KS ? 1 : 0);  // copy instructions per wave per chunk
+  static_assert(STAGES >= 3 && STAGES * SB <= 160 * 1024, "LDS ring fits");
   static_assert((PB + QB) % 4096 == 0, "copies split evenly over the four waves");
+  static_assert((STAGES - 2) * NI < 64, "outstanding copies fit the vmcnt counter");
 };
 
 template <int N>
@@ -155,9 +158,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int RP>
+template <int RP, bool KS>
 __global__ __launch_bounds__(256) void rowstream_kernel(const RowProjParams p) {
-  using T = RowStream<RP>;
+  using T = RowStream<RP, KS>;
   constexpr int NB = RP / 16, KC = T::KC, RL = T::RL, SB = T::SB, ST = T::STAGES;
   __shared__ __attribute__((aligned(16))) uint8_t smem[ST * SB];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -168,7 +171,11 @@ __global__ __launch_bounds__(256) void rowstream_kernel(const RowProjParams p) {
   const bool tq = p.q_trans != 0;
 
   const uint32_t ldp_b = (uint32_t)p.ldp * 2u, ldq_b = (uint32_t)p.ldq * 2u;
-  const __amdgpu_buffer_rsrc_t rs_p = make_rsrc(p.P, (uint32_t)p.M * ldp_b);
+  // a block's 16 rows lie in one P segment (the split is a multiple of 16)
+  const bool seg1 = p.P1 != nullptr && m0 >= p.p_split;
+  const int pm0 = seg1 ? m0 - p.p_split : m0;
+  const __amdgpu_buffer_rsrc_t rs_p = seg1 ? make_rsrc(p.P1, (uint32_t)(p.M - p.p_split) * ldp_b)
+                                           : make_rsrc(p.P, (uint32_t)(p.P1 != nullptr ? p.p_split : p.M) * ldp_b);
   const __amdgpu_buffer_rsrc_t rs_q0 =
       make_rsrc(p.q0, tq ? (uint32_t)p.K * (uint32_t)p.R * 2u : (uint32_t)p.R0 * ldq_b);
   const __amdgpu_buffer_rsrc_t rs_q1 = make_rsrc(p.q1, tq ? 0u : (uint32_t)(p.R - p.R0) * ldq_b);
@@ -182,7 +189,7 @@ __global__ __launch_bounds__(256) void rowstream_kernel(const RowProjParams p) {
   for (int i = 0; i < NIP; ++i) {
     const int b = (i * 4 + wave) * 1024 + lane * 16;
     const int row = b / RL, phys = (b % RL) >> 4;
-    p_off[i] = (uint32_t)(m0 + row) * ldp_b + (uint32_t)((phys ^ (row & 15)) << 4);
+    p_off[i] = (uint32_t)(pm0 + row) * ldp_b + (uint32_t)((phys ^ (row & 15)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < NIQ; ++i) {
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(256) void rowstream_kernel(const RowProjParams p) {
     const uint32_t qs = tq ? (uint32_t)ch * (uint32_t)KC * (uint32_t)p.R * 2u : (uint32_t)ch * RL;
 #pragma unroll
     for (int i = 0; i < NIQ; ++i) buf2lds16(q_up[i] ? rs_q1 : rs_q0, q_off[i], qs, sb + T::PB + (i * 4 + wave) * 1024);
-    buf2lds16(rs_g, (uint32_t)(wave * 1024 + lane * 16), (uint32_t)ch * KC * 4u, sb + T::PB + T::QB + wave * 1024);
+    if constexpr (KS) buf2lds16(rs_g, (uint32_t)(wave * 1024 + lane * 16), (uint32_t)ch * KC * 4u, sb + T::PB + T::QB + wave * 1024);
   };
 
   f32x4 acc[NB];
@@ -217,7 +224,8 @@ __global__ __launch_bounds__(256) void rowstream_kernel(const RowProjParams p) {
   for (int ch = 0; ch < nch; ++ch) {
     // chunks issued after ch that may stay in flight
     const int after = min(ST - 2, nch - 1 - ch);
-    if (after >= 2) wait_vmcnt<2 * T::NI>();
+    if (after >= 3) wait_vmcnt<(ST > 4 ? 3 : 0) * T::NI>();
+    else if (after == 2) wait_vmcnt<2 * T::NI>();
     else if (after == 1) wait_vmcnt<T::NI>();
     else wait_vmcnt<0>();
     __syncthreads();                         // chunk ch visible; chunk ch-1's buffer free
@@ -238,7 +246,7 @@ __global__ __launch_bounds__(256) void rowstream_kernel(const RowProjParams p) {
           const int off = k0 * p.R * 2 + (jb * 16 + 4 * (lr & 3)) * 2;
           const u32x2 lo = lds_tr16(sq, off), hi = lds_tr16(sq, off + 4 * p.R * 2);
           qf = u32x4{lo[0], lo[1], hi[0], hi[1]};
-          if (p.q_kscale != nullptr) {
+          if constexpr (KS) {
             const f32x4* g = reinterpret_cast<const f32x4*>(sg + st * 32 + 8 * lq);
             qf = scale_bf16x8(qf, g[0], g[1]);
           }
@@ -715,10 +723,16 @@ static bool rowstream_ok(const RowProjParams& p, int rp) {
   const int rl = rp <= 32 ? 1024 : (rp == 64 ? 512 : 256);
   const int rows_per_inst = 1024 / rl;
   if (p.ldp % 8 || (((uintptr_t)p.P) & 15) || (((uintptr_t)p.q0) & 15)) return false;
+  if (p.P1 != nullptr && (p.p_split % 16 || (((uintptr_t)p.P1) & 15))) return false;
   if (p.q_kscale && (((uintptr_t)p.q_kscale) & 15)) return false;
   if (p.q_trans) return p.R % 4 == 0 && p.R0 == p.R;
   if (p.ldq % 8 || (((uintptr_t)p.q1) & 15)) return false;
   return p.R0 == p.R || p.R0 % rows_per_inst == 0;
+}
+
+template <int RP, bool KS>
+static void rowstream_launch(const RowProjParams& p, dim3 grid, dim3 block, hipStream_t st) {
+  hipLaunchKernelGGL((rowstream_kernel<RP, KS>), grid, block, 0, st, p);
 }
 
 hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st) {
@@ -726,11 +740,12 @@ hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st) {
   const int rp = p.R <= 16 ? 16 : p.R <= 32 ? 32 : p.R <= 64 ? 64 : 128;
   if (rowstream_ok(p, rp)) {
     const dim3 grid((p.M + 15) / 16), block(256);
+    const bool ks = p.q_kscale != nullptr;
     switch (rp) {
-      case 16: hipLaunchKernelGGL(rowstream_kernel<16>, grid, block, 0, st, p); break;
-      case 32: hipLaunchKernelGGL(rowstream_kernel<32>, grid, block, 0, st, p); break;
-      case 64: hipLaunchKernelGGL(rowstream_kernel<64>, grid, block, 0, st, p); break;
-      default: hipLaunchKernelGGL(rowstream_kernel<128>, grid, block, 0, st, p); break;
+      case 16: ks ? rowstream_launch<16, true>(p, grid, block, st) : rowstream_launch<16, false>(p, grid, block, st); break;
+      case 32: ks ? rowstream_launch<32, true>(p, grid, block, st) : rowstream_launch<32, false>(p, grid, block, st); break;
+      case 64: ks ? rowstream_launch<64, true>(p, grid, block, st) : rowstream_launch<64, false>(p, grid, block, st); break;
+      default: ks ? rowstream_launch<128, true>(p, grid, block, st) : rowstream_launch<128, false>(p, grid, block, st); break;
     }
     return hipGetLastError();
   }
