@@ -84,8 +84,9 @@ struct LoraBwdWs {
 LoraBwdWs plan_lora_bwd(Bump& b, int M, int N, int K, int r, bool need_u) {
   LoraBwdWs w{};
   w.rp = colproj_rp(r);
-  colproj_plan(M, N, &w.nsB, &w.msB);
-  colproj_plan(M, K, &w.nsA, &w.msA);
+  // dB and dA share one launch: half the block target each
+  colproj_plan(M, N, &w.nsB, &w.msB, 256);
+  colproj_plan(M, K, &w.nsA, &w.msA, 256);
   w.V = b.take<float>((size_t)M * r);
   w.U = need_u ? b.take<float>((size_t)M * r) : nullptr;
   w.partB = b.take<float>((size_t)w.nsB * N * w.rp);

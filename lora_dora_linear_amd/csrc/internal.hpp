@@ -51,7 +51,8 @@ bool gemm_shape_ok(GemmKind kind, int M, int N, int K);
 
 hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st);
 int colproj_rp(int R);
-void colproj_plan(int M, int C, int* nsplit, int* msplit);
+// split plan of a column projection over M rows and C columns, aiming at `blocks` blocks
+void colproj_plan(int M, int C, int* nsplit, int* msplit, int blocks = 512);
 hipError_t launch_colproj(const ColProjParams& p, int nsplit, hipStream_t st);
 // up to kColProjBatch independent column projections in one launch (one launch per job when
 // their rank paddings differ)

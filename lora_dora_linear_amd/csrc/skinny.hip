@@ -761,17 +761,18 @@ hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st) {
 
 int colproj_rp(int R) { return R <= 16 ? 16 : R <= 32 ? 32 : R <= 64 ? 64 : 128; }
 
-void colproj_plan(int M, int C, int* nsplit, int* msplit) {
+void colproj_plan(int M, int C, int* nsplit, int* msplit, int blocks) {
   if (M <= 0) {
     *nsplit = 1;
     *msplit = 256;
     return;
   }
   // splits are whole multiples of 256 rows (a multiple of every sub-tile height);
-  // aim for ~512 blocks (two per CU, each streaming several sub-tiles), at most 32 splits
+  // aim for `blocks` blocks of this job (~512 per launch: two per CU, each streaming
+  // several sub-tiles; jobs that share a launch split the target), at most 32 splits
   const int ctiles = (C + 63) / 64;
   const int mchunks = (M + 255) / 256;
-  int want = (512 + ctiles - 1) / ctiles;
+  int want = (blocks + ctiles - 1) / ctiles;
   if (want < 1) want = 1;
   if (want > 32) want = 32;
   int ns = mchunks < want ? mchunks : want;
