@@ -312,8 +312,9 @@ def main():
            "config": config, "pct_bf16_peak": round(100.0 * value / PEAK_BF16, 2)}
     if kern:
         dom = max(kern, key=lambda k: kern[k]["avg_us"])
-        # the plain LoRA products run on the four-wave tile unless it is switched off
-        four = wl == "lora" and args.gemm_4wave != 0
+        # the LoRA and DoRA products (N a multiple of 256) run on the four-wave tile unless
+        # it is switched off
+        four = wl in ("lora", "dora") and args.gemm_4wave != 0
         names = {0: "forward base GEMM (" + ("gemm16_kernel NT" if four else "gemm_kernel NT") + ")",
                  1: "input-gradient GEMM (" + ("gemm16_kernel NN" if four else "gemm_kernel NN") + ")"}
         peak = PEAK_INT8 if (wl == "w8a8" and dom == 0) else PEAK_BF16

@@ -516,11 +516,11 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, c
   ColProjParams jobs[3];
   int ns[3], nj = 0;
   if (M > 0) {
-    // V = (dY.diag(g)).B, the scaled B read in place as a [N, r] matrix
-    LDL_TRY(rowproj_t(M, N, r, dY, N, Bh, r, g, w.V, r, 1.f, st));
     if (dX) {
-      // dX = (dY.diag(g)).W0 + s.V.A: dY.diag(g) rounded to bf16 once, then the plain product
+      // dY.diag(g) rounded to bf16 once; V = (dY.diag(g)).B and dX = (dY.diag(g)).W0 + s.V.A
+      // are then plain products of it (B read in place as a [N, r] matrix)
       LDL_TRY(launch_scale_cols(dY, M, N, N, g, w.dYg, st));
+      LDL_TRY(rowproj_t(M, N, r, w.dYg, N, Bh, r, nullptr, w.V, r, 1.f, st));
       GemmParams p = gp0();
       p.M = M; p.N = K; p.K = N;
       p.a = w.dYg; p.lda = N; p.b0 = W0; p.b1 = W0; p.ldb = K; p.kseg = N;
@@ -528,6 +528,9 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, c
       p.e0 = A; p.e1 = A; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = r;
       p.out = dX; p.ldo = K;
       LDL_TRY(gemm_timed(1, GK_NN_PLAIN, p, st));
+    } else {
+      // V = (dY.diag(g)).B with g applied to B's rows on load (no scaled copy of dY)
+      LDL_TRY(rowproj_t(M, N, r, dY, N, Bh, r, g, w.V, r, 1.f, st));
     }
     // s.V^T.X into the first nsA partials of dA
     jobs[nj] = cpp(M, K, r, X, K, w.V, r, s, nullptr, 0, 0, w.msA, w.partA, nullptr);
