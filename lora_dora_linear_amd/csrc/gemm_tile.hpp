@@ -78,7 +78,10 @@ struct GemmCfg {
   // transposed by ds_read_b64_tr_b16; otherwise staged through registers
   // (a column scale on P is then applied to the Q fragments after the read, from
   // a 64-float slice of the scale vector copied with each stage)
-  static constexpr bool kNNTr = NN_ && !BINT8_ && (BN_ == 64 || BN_ == 128 || BN_ == 256);
+  static constexpr bool kNNTr = NN_ && (BN_ == 64 || BN_ == 128 || BN_ == 256);
+  // int8 Q on the transposed path: its rows copied as stored into an int8 staging tile and
+  // widened (times the row scale) into the bf16 Q tile at the stage hand-over
+  static constexpr bool kQ8 = kNNTr && BINT8_;
   static constexpr int kSideRsp = SIDE_RSP_;// fused side rows (padded to 16), 0: none
   static constexpr bool kSLoad = SLOAD_;    // epilogue S from global
   static constexpr int kEpi = EPI_;
@@ -86,7 +89,7 @@ struct GemmCfg {
 
 template <class C>
 struct GemmSmem {
-  static constexpr int kRows = C::BM + C::BN + C::kSideRsp + ((C::kNNTr && C::kAScale) ? 8 : 0);
+  static constexpr int kRows = C::BM + C::BN + C::kSideRsp + ((C::kNNTr && C::kAScale && !C::kQ8) ? 8 : 0);
   static constexpr int kBuf = kRows * 128;
 };
 
@@ -141,6 +144,9 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * GemmSmem<C>::kBuf];
   uint8_t* const smem0 = smem;
   uint8_t* const smem1 = smem + GemmSmem<C>::kBuf;
+  // int8 Q: one stage of Q rows as stored ([64][BN] bytes) and its 64 row scales (1 KB copy)
+  constexpr bool Q8 = C::kQ8;
+  __shared__ __attribute__((aligned(16))) uint8_t s8[Q8 ? 64 * BN + 1024 : 16];
 
   const int M = p.M, N = p.N, K = p.K;
   // Dual gate/up tile: BN rows of Q = BN/2 gate rows and the BN/2 up rows of the
@@ -184,7 +190,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
   constexpr bool NNTR = C::kNNTr;
   // NN-tr: the Q k-tile is 64 rows of BN bf16 (BN / 8 chunks of 16 bytes per row);
   // chunk c of row k sits at physical chunk c ^ tr_swz(k)
-  constexpr int B_INST = NNTR ? BN / (8 * NW) : (NN ? 0 : BN / (8 * NW));
+  constexpr int B_INST = NNTR ? (Q8 ? BN / (16 * NW) : BN / (8 * NW)) : (NN ? 0 : BN / (8 * NW));
+  static_assert(!Q8 || BN % (16 * NW) == 0, "int8 Q rows split evenly over the waves");
   constexpr int S_INST = (RSP + 8 * NW - 1) / (8 * NW);
   // rows k .. k+3 of one transposing read land on distinct banks
   auto tr_swz = [](int k) { return 2 * (k & 3); };
@@ -198,11 +205,11 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
       NNTR ? make_rsrc(p.b1, (uint32_t)(K - p.kseg) * ldb_b)
            : make_rsrc(DUAL ? p.b1 : p.b0, NN ? 0u : (uint32_t)N * ldb_b);
   const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(p.side, RSP ? (uint32_t)p.r_side * (uint32_t)K * 2u : 0u);
-  constexpr bool TRSC = NNTR && C::kAScale;    // scale slice: 1 KB after the Q tile, first 256 B used
+  constexpr bool TRSC = NNTR && C::kAScale && !Q8;   // scale slice: 1 KB after the Q tile, first 256 B used
   // copy slices per stage (see issue_loads); the register-staged NN operand is loaded whole
   constexpr int NPART = (NN && !NNTR) ? 1 : 3;
   constexpr bool SPLIT = NPART > 1;
-  const __amdgpu_buffer_rsrc_t rs_c = make_rsrc(p.a_colscale, TRSC ? (uint32_t)K * 4u : 0u);
+  const __amdgpu_buffer_rsrc_t rs_c = make_rsrc(p.a_colscale, (TRSC || Q8) ? (uint32_t)K * 4u : 0u);
   uint32_t a_off[A_INST];
 #pragma unroll
   for (int i = 0; i < A_INST; ++i) {
@@ -212,7 +219,12 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
   uint32_t b_off[B_INST ? B_INST : 1];
 #pragma unroll
   for (int i = 0; i < B_INST; ++i) {
-    if constexpr (NNTR) {
+    if constexpr (Q8) {           // 16 int8 of row krow, stored as is: s8[krow][16 c16 ..]
+      const int slot = (i * NW + wave) * 64 + lane;
+      const int krow = slot / (BN / 16), c16 = slot % (BN / 16);
+      b_off[i] = (uint32_t)krow * ldb_b + (uint32_t)(n0 + 16 * c16);
+      continue;
+    } else if constexpr (NNTR) {
       const int slot = (i * NW + wave) * 64 + lane;          // 16-byte slot of the k-tile
       const int krow = slot / (BN / 8), phys = slot % (BN / 8);
       b_off[i] = (uint32_t)krow * ldb_b + (uint32_t)(n0 + 8 * (phys ^ tr_swz(krow))) * 2u;
@@ -255,7 +267,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
 
   // ---------------------------------------------------------------- loaders
   // the wave's copy instructions of one stage, in order: P tile, Q tile, side rows, scale slice
-  constexpr int NCOPY = A_INST + ((NN && !NNTR) ? 0 : B_INST + S_INST + (TRSC ? 1 : 0));
+  constexpr int NCOPY = A_INST + ((NN && !NNTR) ? 0 : B_INST + S_INST + ((TRSC || Q8) ? 1 : 0));
   auto issue_one = [&](int kt, uint8_t* sbuf, int q) {
     const uint32_t koff = (uint32_t)kt * 128u;
     if (q < A_INST) {
@@ -277,11 +289,11 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
       const bool seg1 = kk0 >= p.kseg;
       const uint32_t boff = (uint32_t)(seg1 ? kk0 - p.kseg : kk0) * ldb_b;
       if (q < B_INST) {
-        buf2lds16(seg1 ? rs_b2 : rs_b, b_off[q], boff, sB + (q * NW + wave) * 1024);
+        buf2lds16(seg1 ? rs_b2 : rs_b, b_off[q], boff, (Q8 ? s8 : sB) + (q * NW + wave) * 1024);
         return;
       }
-      if constexpr (TRSC) {
-        if (wave == NW - 1) buf2lds16(rs_c, (uint32_t)lane * 16u, (uint32_t)kt * 256u, sB + BN * 128);
+      if constexpr (TRSC || Q8) {
+        if (wave == NW - 1) buf2lds16(rs_c, (uint32_t)lane * 16u, (uint32_t)kt * 256u, Q8 ? s8 + 64 * BN : sB + BN * 128);
       }
     }
   };
@@ -316,10 +328,11 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
       const uint32_t boff = (uint32_t)(seg1 ? kk0 - p.kseg : kk0) * ldb_b;
 #pragma unroll
       for (int i = 0; i < B_INST; ++i)
-        if (mine(A_INST + i)) buf2lds16(seg1 ? rs_b2 : rs_b, b_off[i], boff, sB + (i * NW + wave) * 1024);
+        if (mine(A_INST + i)) buf2lds16(seg1 ? rs_b2 : rs_b, b_off[i], boff, (Q8 ? s8 : sB) + (i * NW + wave) * 1024);
       // scale[kt*64 ..] -> lanes 0..15 fill the slice; the rest read ahead (or zero past the end)
-      if constexpr (TRSC) {
-        if (wave == NW - 1 && mine(A_INST + B_INST)) buf2lds16(rs_c, (uint32_t)lane * 16u, (uint32_t)kt * 256u, sB + BN * 128);
+      if constexpr (TRSC || Q8) {
+        if (wave == NW - 1 && mine(A_INST + B_INST))
+          buf2lds16(rs_c, (uint32_t)lane * 16u, (uint32_t)kt * 256u, Q8 ? s8 + 64 * BN : sB + BN * 128);
       }
     } else {
       if (part > 0) return;
@@ -518,6 +531,38 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
   // adding it in the epilogue
   constexpr bool SEED = !I8 && RSP == 0 && C::kSLoad;
 
+  // int8 Q: widen the landed stage in s8 into sbuf's Q tile (the transposed-path layout the
+  // bf16 copies produce), row k times its scale: (u - 128) s for the biased byte u = q + 128
+  // is one fma, rounded once to fp32 and once to bf16 (as bf16(q) * s rounded to bf16).
+  // Thread t takes 16-byte units t, t + threads, .. (consecutive lanes, consecutive bytes).
+  auto convert_q8 = [&](uint8_t* sbuf) {
+    if constexpr (Q8) {
+      typedef float f2 __attribute__((ext_vector_type(2)));
+      typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+      uint8_t* sB = sbuf + BM * 128;
+      const float* sc8 = reinterpret_cast<const float*>(s8 + 64 * BN);
+#pragma unroll
+      for (int u = tid; u < 4 * BN; u += C::kThreads) {
+        const int k = u / (BN / 16), c16 = u % (BN / 16);
+        const u32x4 v = lds_ld16(s8, u * 16);
+        const float sc = sc8[k], c0 = -128.f * sc;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          u32x4 o;
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            const uint32_t w = v[2 * h + d] ^ 0x80808080u;
+            const f2 lo = {__builtin_fmaf((float)(w & 0xffu), sc, c0), __builtin_fmaf((float)((w >> 8) & 0xffu), sc, c0)};
+            const f2 hi = {__builtin_fmaf((float)((w >> 16) & 0xffu), sc, c0), __builtin_fmaf((float)(w >> 24), sc, c0)};
+            o[2 * d] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, b2));
+            o[2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, b2));
+          }
+          lds_st16(sB, k * (BN * 2) + (((2 * c16 + h) ^ tr_swz(k)) << 4), o);
+        }
+      }
+    }
+  };
+
   // ---------------------------------------------------------------- main loop
   // Stage kt lives in smem[kt & 1].  The hand-over to the next stage sits
   // between the last two MFMA steps of a k-tile: wait for the next stage's
@@ -534,6 +579,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
   store_q(0, smem0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if constexpr (Q8) {
+    convert_q8(smem0);
+    __syncthreads();
+  }
   if (KT > 1) issue_loads(1, smem1, -1);
   load_frags(smem0, 0, fa0, fb0, fs0);
   // settle every LDS / scalar read of the prologue (not the copies in flight)
@@ -585,6 +634,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
     first_steps(kt, cur, nxt, true);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if constexpr (Q8) {              // stage kt+1's int8 rows have landed; s8 is free after this
+      convert_q8(nxt);
+      __syncthreads();
+    }
     if (!SPLIT && kt + 2 < KT) issue_loads(kt + 2, cur, -1);
     load_frags(nxt, 0, fa0, fb0, fs0);
     __builtin_amdgcn_sched_barrier(0);
