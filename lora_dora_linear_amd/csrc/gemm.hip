@@ -59,6 +59,15 @@ static hipError_t run16(const GemmParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// 256x128 tiles instead of 256x256 when twice as many tiles still fit one round over the
+// 256 CUs (small M): the half-size tiles then keep twice the CUs busy.  With more tiles
+// the four-wave 256x128 tile's lower rate per flop outweighs saved tail rounds (measured
+// at 4096 and 8192 tokens, 5120 columns).
+static bool half_tiles_pay(int M, int N) {
+  const long t256 = (long)((M + 255) / 256) * (N / 256);
+  return 2 * t256 <= 256;
+}
+
 hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
   if (p.M <= 0) return hipSuccess;
   const int bn = pick_bn(kind, p.N);
@@ -105,7 +114,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
       if (p.r_side <= 32) return run<256, 128, false, false, false, false, 32, false, EPI_PLAIN>(p, st);
       return run<256, 128, false, false, false, false, 64, false, EPI_PLAIN>(p, st);
     case GK_NT_I8_DEQ:
-      if (bn == 256 && big) return run<256, 256, true, false, false, false, 0, true, EPI_DEQUANT>(p, st);
+      if (bn == 256 && big && !half_tiles_pay(p.M, p.N)) return run<256, 256, true, false, false, false, 0, true, EPI_DEQUANT>(p, st);
       if (bn >= 128) return big ? run<256, 128, true, false, false, false, 0, true, EPI_DEQUANT>(p, st)
                                 : run<128, 128, true, false, false, false, 0, true, EPI_DEQUANT>(p, st);
       return run<128, 64, true, false, false, false, 0, true, EPI_DEQUANT>(p, st);
@@ -127,7 +136,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
                                 : run<128, 128, false, true, false, true, 0, true, EPI_PLAIN>(p, st);
       return run<128, 64, false, true, false, true, 0, true, EPI_PLAIN>(p, st);
     case GK_NN_I8_SCALE:
-      if (bn == 256 && big) return run<256, 256, false, true, true, true, 0, true, EPI_PLAIN>(p, st);
+      if (bn == 256 && big && !half_tiles_pay(p.M, p.N)) return run<256, 256, false, true, true, true, 0, true, EPI_PLAIN>(p, st);
       if (bn == 192 && big) return run<256, 192, false, true, true, true, 0, true, EPI_PLAIN>(p, st);
       if (bn >= 128) return big ? run<256, 128, false, true, true, true, 0, true, EPI_PLAIN>(p, st)
                                 : run<128, 128, false, true, true, true, 0, true, EPI_PLAIN>(p, st);
