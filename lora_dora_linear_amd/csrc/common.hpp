@@ -144,7 +144,11 @@ __device__ __forceinline__ u32x2 lds_tr16(const uint8_t* base, int off) {
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
-__device__ __forceinline__ float silu_f(float e) { return e / (1.0f + __expf(-e)); }
-__device__ __forceinline__ float sigmoid_f(float e) { return 1.0f / (1.0f + __expf(-e)); }
+// sigma(e) = 1 / (1 + exp(-e)) with the hardware reciprocal (1 ulp): the library is built
+// with IEEE fp32 division for the int8 quantiser, which made every epilogue division a
+// long instruction sequence; the activations only feed bf16 outputs.  exp(-e) = inf for
+// very negative e gives rcp(inf) = 0.
+__device__ __forceinline__ float sigmoid_f(float e) { return __builtin_amdgcn_rcpf(1.0f + __expf(-e)); }
+__device__ __forceinline__ float silu_f(float e) { return e * sigmoid_f(e); }
 
 }  // namespace ldl

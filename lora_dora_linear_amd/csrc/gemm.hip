@@ -49,13 +49,14 @@ bool gemm_shape_ok(GemmKind kind, int M, int N, int K) {
 
 int g_gemm_4wave = 1;
 
-// Four-wave 256x256 tile: plain (and DoRA row-scaled NT) products over a whole number of
-// 256-column tiles with a low-rank term of rank <= 64 (NN: Q in one segment).
-template <bool NN, bool DORA = false>
+// Four-wave 256x256 tile: plain products, DoRA's row-scaled NT and the SwiGLU-backward NN
+// epilogue, over a whole number of 256-column tiles with a low-rank term of rank <= 64
+// (NN: Q in one segment).
+template <bool NN, bool DORA = false, bool SWB = false>
 static hipError_t run16(const GemmParams& p, hipStream_t st) {
   const int tiles = ((p.M + 255) / 256) * (p.N / 256);
-  if (p.r_epi > 0) hipLaunchKernelGGL((gemm16_kernel<NN, true, DORA>), dim3(tiles), dim3(256), 0, st, p);
-  else hipLaunchKernelGGL((gemm16_kernel<NN, false, DORA>), dim3(tiles), dim3(256), 0, st, p);
+  if (p.r_epi > 0) hipLaunchKernelGGL((gemm16_kernel<NN, true, DORA, SWB>), dim3(tiles), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((gemm16_kernel<NN, false, DORA, SWB>), dim3(tiles), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -77,11 +78,13 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
   const auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
   const bool seed_ok = p.r_epi == 0 ||
       (p.r_epi % 8 == 0 && p.ld_s % 4 == 0 && a16(p.S) && a16(p.e0) && p.e_jsplit >= p.r_epi &&
-       (kind == GK_NN_PLAIN ? (p.e_ldn == 1 && p.e_ldj % 8 == 0) : (p.e_ldj == 1 && p.e_ldn % 8 == 0)));
+       ((kind == GK_NN_PLAIN || kind == GK_NN_SWIGLU) ? (p.e_ldn == 1 && p.e_ldj % 8 == 0)
+                                                      : (p.e_ldj == 1 && p.e_ldn % 8 == 0)));
   if (g_gemm_4wave && bn == 256 && big && p.side == nullptr && p.r_epi <= 64 && seed_ok) {
     if (kind == GK_NT_PLAIN) return run16<false>(p, st);
     if (kind == GK_NT_DORA) return run16<false, true>(p, st);
     if (kind == GK_NN_PLAIN && p.kseg == p.K) return run16<true>(p, st);
+    if (kind == GK_NN_SWIGLU && p.kseg == p.K) return run16<true, false, true>(p, st);
   }
   switch (kind) {
     case GK_NT_PLAIN:

@@ -36,10 +36,13 @@ constexpr int kG16NNRow = 512, kG16NNPad = 128;
 __host__ __device__ constexpr int g16_nn_row(int k) { return k * kG16NNRow + (k >> 3) * kG16NNPad; }
 
 // NN: Q is [K, N] (else [N, K]); LR: with a low-rank term (r_epi in 8, 16, .., 64);
-// DORA (NT only): two outputs, out2 = z (the unscaled sum) and out = z * col_scale[n] + bias[n]
-template <bool NN, bool LR, bool DORA = false>
+// DORA (NT only): two outputs, out2 = z (the unscaled sum) and out = z * col_scale[n] + bias[n];
+// SWB (NN only): the SwiGLU backward of the product dh with e = aux0, u = aux1:
+// out = dh u sigma(e) (1 + e (1 - sigma(e))) (de) and out2 = dh e sigma(e) (du)
+template <bool NN, bool LR, bool DORA = false, bool SWB = false>
 __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   static_assert(!(NN && DORA), "the row-scaled epilogue is a forward (NT) epilogue");
+  static_assert(!SWB || (NN && !DORA), "the SwiGLU backward epilogue is an NN epilogue");
   constexpr int BM = 256, BN = 256, NW = 4;
   constexpr int QB = NN ? g16_nn_row(64) : BN * 128;
   constexpr int SB = BM * 128 + QB;                 // one stage: P tile then Q tile
@@ -326,6 +329,54 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
     emit(std::true_type{}, p.out2, p.ldo2);
     __syncthreads();                               // the staging buffers are free again
     emit(std::false_type{}, p.out, p.ldo);
+  } else if constexpr (SWB) {
+    // two passes through the staging tile: de into out, then du into out2; e and u are read
+    // for the lane's four columns of each accumulator block (8 bytes each)
+    auto emit_swb = [&](auto o_c, void* dst, int ldo) {
+      constexpr int O = decltype(o_c)::value;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = wm * 128 + i * 16 + l16;
+        const size_t m = (size_t)min(m0 + r, M - 1);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int cl = wn * 128 + j * 16 + 4 * lq;
+          const u32x2 ee = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux0) + m * p.ld_aux0 + n0 + cl);
+          const float e4[4] = {bf16_lo(ee[0]), bf16_hi(ee[0]), bf16_lo(ee[1]), bf16_hi(ee[1])};
+          const f32x4 v = acc[i][j];
+          float r4[4];
+          if constexpr (O == 0) {
+            const u32x2 uu = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux1) + m * p.ld_aux1 + n0 + cl);
+            const float u4[4] = {bf16_lo(uu[0]), bf16_hi(uu[0]), bf16_lo(uu[1]), bf16_hi(uu[1])};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float sg = sigmoid_f(e4[e]);
+              r4[e] = v[e] * u4[e] * sg * (1.f + e4[e] * (1.f - sg));
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r4[e] = v[e] * e4[e] * sigmoid_f(e4[e]);
+          }
+          u32x2 w;
+          w[0] = pack_bf16x2(r4[0], r4[1]);
+          w[1] = pack_bf16x2(r4[2], r4[3]);
+          *reinterpret_cast<u32x2*>(st_ptr(r, cl)) = w;
+        }
+      }
+      __syncthreads();
+      uint16_t* out = static_cast<uint16_t*>(dst);
+      for (int idx = tid; idx < BM * 32; idx += 256) {
+        const int rr0 = idx >> 5, c = idx & 31;
+        if (m0 + rr0 < M) {
+          const uint8_t* base = rr0 < 128 ? smem0 : smem1;
+          const int rr = rr0 & 127;
+          st16(out + (size_t)(m0 + rr0) * ldo + n0 + c * 8, lds_ld16(base, rr * 512 + ((c ^ (rr & 31)) << 4)));
+        }
+      }
+    };
+    emit_swb(std::integral_constant<int, 0>{}, p.out, p.ldo);
+    __syncthreads();
+    emit_swb(std::integral_constant<int, 1>{}, p.out2, p.ldo2);
   } else {
     // (written out rather than through emit: the lambda changed the register allocation of
     // the NN k-loop and cost ~10 % there)
