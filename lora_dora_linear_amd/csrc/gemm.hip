@@ -52,12 +52,19 @@ int g_gemm_4wave = 1;
 // Four-wave 256x256 tile: plain products, DoRA's row-scaled NT and the SwiGLU-backward NN
 // epilogue, over a whole number of 256-column tiles with a low-rank term of rank <= 64
 // (NN: Q in one segment).
-template <bool NN, bool DORA = false, bool SWB = false>
+template <bool NN, bool DORA = false, bool SWB = false, int BN = 256>
 static hipError_t run16(const GemmParams& p, hipStream_t st) {
-  const int tiles = ((p.M + 255) / 256) * (p.N / 256);
-  if (p.r_epi > 0) hipLaunchKernelGGL((gemm16_kernel<NN, true, DORA, SWB>), dim3(tiles), dim3(256), 0, st, p);
-  else hipLaunchKernelGGL((gemm16_kernel<NN, false, DORA, SWB>), dim3(tiles), dim3(256), 0, st, p);
+  const int tiles = ((p.M + 255) / 256) * (p.N / BN);
+  if (p.r_epi > 0) hipLaunchKernelGGL((gemm16_kernel<NN, true, DORA, SWB, BN>), dim3(tiles), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((gemm16_kernel<NN, false, DORA, SWB, BN>), dim3(tiles), dim3(256), 0, st, p);
   return hipGetLastError();
+}
+
+// 192-column four-wave NT tiles when the 256-column tiles leave CUs idle in their only round
+// and the 192-column ones still fit it (3072 columns at 4096 rows: 192 -> 256 tiles)
+static bool b192_fills(int M, int N) {
+  const long t256 = (long)((M + 255) / 256) * (N / 256), t192 = (long)((M + 255) / 256) * (N / 192);
+  return N % 192 == 0 && t256 < 256 && t192 <= 256 && t192 > t256;
 }
 
 // 256x128 tiles instead of 256x256 when twice as many tiles still fit one round over the
@@ -80,6 +87,11 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
       (p.r_epi % 8 == 0 && p.ld_s % 4 == 0 && a16(p.S) && a16(p.e0) && p.e_jsplit >= p.r_epi &&
        ((kind == GK_NN_PLAIN || kind == GK_NN_SWIGLU) ? (p.e_ldn == 1 && p.e_ldj % 8 == 0)
                                                       : (p.e_ldj == 1 && p.e_ldn % 8 == 0)));
+  if (g_gemm_4wave && big && p.side == nullptr && p.r_epi <= 64 && seed_ok &&
+      (kind == GK_NT_PLAIN || kind == GK_NT_DORA) && b192_fills(p.M, p.N)) {
+    if (kind == GK_NT_PLAIN) return run16<false, false, false, 192>(p, st);
+    return run16<false, true, false, 192>(p, st);
+  }
   if (g_gemm_4wave && bn == 256 && big && p.side == nullptr && p.r_epi <= 64 && seed_ok) {
     if (kind == GK_NT_PLAIN) return run16<false>(p, st);
     if (kind == GK_NT_DORA) return run16<false, true>(p, st);

@@ -39,11 +39,15 @@ __host__ __device__ constexpr int g16_nn_row(int k) { return k * kG16NNRow + (k 
 // DORA (NT only): two outputs, out2 = z (the unscaled sum) and out = z * col_scale[n] + bias[n];
 // SWB (NN only): the SwiGLU backward of the product dh with e = aux0, u = aux1:
 // out = dh u sigma(e) (1 + e (1 - sigma(e))) (de) and out2 = dh e sigma(e) (du)
-template <bool NN, bool LR, bool DORA = false, bool SWB = false>
+// BN_: tile width, 256, or 192 for NT (3072 columns at 4096 rows then make 256 tiles, one full
+// round of the 256 CUs, where 256-column tiles leave a quarter of the chip idle)
+template <bool NN, bool LR, bool DORA = false, bool SWB = false, int BN_ = 256>
 __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
+  static_assert(BN_ == 256 || (!NN && BN_ == 192), "tile widths: 256, or 192 for NT");
   static_assert(!(NN && DORA), "the row-scaled epilogue is a forward (NT) epilogue");
   static_assert(!SWB || (NN && !DORA), "the SwiGLU backward epilogue is an NN epilogue");
-  constexpr int BM = 256, BN = 256, NW = 4;
+  constexpr int BM = 256, BN = BN_, NW = 4;
+  constexpr int FN = BN / 32;                       // 16-column fragments per wave (wave tile BN / 2)
   constexpr int QB = NN ? g16_nn_row(64) : BN * 128;
   constexpr int SB = BM * 128 + QB;                 // one stage: P tile then Q tile
   __shared__ __attribute__((aligned(16))) uint8_t smem0[SB];
@@ -104,24 +108,24 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) copy(ra, a_off[NN ? i : 0], ka + i * a_step, sb + (i * NW + wave) * 1024);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) copy(rb, b_off[NN ? i : 0], kb + i * b_step, sb + q_dst(i));
+    for (int i = 0; i < (NN ? 8 : FN); ++i) copy(rb, b_off[NN ? i : 0], kb + i * b_step, sb + q_dst(i));
   };
 
-  f32x4 acc[8][8];
+  f32x4 acc[8][FN];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
 
   // fragments of 32-element step ks (P rows wm*128 + 16 i + l16, Q rows or columns
   // wn*128 + 16 j + l16, k = 32 ks + 8 lq ..), read in order of first use: fa[0], fb[0..7], fa[1..7]
   const int a_base0 = g16_off(wm * 128 + l16, lq), a_base1 = g16_off(wm * 128 + l16, 4 + lq);
-  const int b_base0 = BM * 128 + g16_off(wn * 128 + l16, lq), b_base1 = BM * 128 + g16_off(wn * 128 + l16, 4 + lq);
+  const int b_base0 = BM * 128 + g16_off(wn * (BN / 2) + l16, lq), b_base1 = BM * 128 + g16_off(wn * (BN / 2) + l16, 4 + lq);
   auto ldf_rows = [&](const uint8_t* s, int ks, u32x4* fa, u32x4* fb) {   // NT: both tiles k-contiguous rows
     const int a = ks ? a_base1 : a_base0, b = ks ? b_base1 : b_base0;
     fa[0] = lds_ld16(s, a);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) fb[j] = lds_ld16(s, b + j * 2048);
+    for (int j = 0; j < FN; ++j) fb[j] = lds_ld16(s, b + j * 2048);
 #pragma unroll
     for (int i = 1; i < 8; ++i) fa[i] = lds_ld16(s, a + i * 2048);
   };
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < FN; ++j) {
         acc[i][j] = mfma_bf16(fb[j], fa[i], acc[i][j]);
         // NT: keep each result in its accumulator's AGPRs (an empty asm with an AGPR
         // operand); otherwise the allocator moves some accumulators through VGPRs
@@ -168,7 +172,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
 
   constexpr int NRQ = NN ? 2 : 1;       // LDS read instructions per Q fragment
   const int KT = K / 64;
-  u32x4 fa0[8], fb0[8], fa1[8], fb1[8];
+  u32x4 fa0[8], fb0[FN], fa1[8], fb1[FN];
 
   // The low-rank term is one more k-tile, "stage -1" in the second stage buffer: its P
   // tile holds s.S[m0 + t][0..63] as bf16 and its Q tile E's 64 ranks in the layout of a
@@ -193,9 +197,10 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
         const int j = 8 * c + (tid >> 5);
         ev[c] = *reinterpret_cast<const u32x4*>(e0 + (size_t)min(j, p.r_epi - 1) * p.e_ldj + n0 + 8 * (tid & 31));
         if (j >= p.r_epi) ev[c] = u32x4{0u, 0u, 0u, 0u};
-      } else {                  // ranks 8 c .. 8 c + 7 of row n0 + t
-        ev[c] = (8 * c < p.r_epi) ? *reinterpret_cast<const u32x4*>(e0 + (size_t)(n0 + tid) * p.e_ldn + 8 * c)
-                                  : u32x4{0u, 0u, 0u, 0u};
+      } else {                  // ranks 8 c .. 8 c + 7 of row n0 + t (t < BN)
+        ev[c] = (8 * c < p.r_epi && (BN == 256 || tid < BN))
+                    ? *reinterpret_cast<const u32x4*>(e0 + (size_t)(n0 + tid) * p.e_ldn + 8 * c)
+                    : u32x4{0u, 0u, 0u, 0u};
       }
     }
   }
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
       if constexpr (NN) {
         const int j = 8 * c + (tid >> 5), ch = tid & 31;
         lds_st16(smem1, BM * 128 + g16_nn_row(j) + ((ch ^ (2 * (j & 3))) << 4), ev[c]);
-      } else {
+      } else if (BN == 256 || tid < BN) {
         lds_st16(smem1, BM * 128 + g16_off(tid, c), ev[c]);
       }
     }
@@ -240,18 +245,25 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+      for (int j = 0; j < FN; ++j) asm volatile("" : "+a"(acc[i][j]));
+    // Schedule of a step (8 FN MFMAs): NG groups of {read, 2 MFMAs, read(s), 2 MFMAs} carry
+    // the 8 + FN fragment reads (NN: 8 + 16), the other MR MFMAs follow; in the hand-over
+    // step one stage copy goes with each group and the other NC2 copies with MPC MFMAs each.
+    constexpr int NG = NN ? 8 : (8 + FN) / 2;
+    constexpr int MR = 8 * FN - 4 * NG;
+    constexpr int NC2 = (NN ? 16 : 8 + FN) - NG;
+    constexpr int MPC = (MR + NC2 - 1) / NC2;
     // step 0 of this stage, with the reads of step 1 over its first half
     __builtin_amdgcn_sched_barrier(0);
     ldf(cur, 1, fa1, fb1);
     mm(fa0, fb0);
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < NG; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, NRQ, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MR, 0);
     __builtin_amdgcn_sched_barrier(0);
     // hand-over: the next stage has landed and every wave is done with this one
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -260,16 +272,16 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
     copy_stage(kt + 2, cur);
     ldf(nxt, 0, fa0, fb0);
     mm(fa1, fb1);
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < NG; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, NRQ, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < NC2; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MPC, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -284,14 +296,17 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the last (empty) copies
   __syncthreads();
 
-  static_assert(128 * 512 <= SB, "half of the output tile fits in a stage buffer");
+  // staging rows of SROW bytes; 16-byte chunk c of row rr at c ^ (rr & SWZM) (256 columns: all
+  // 32 chunks; 192: within each group of 8, so it stays inside the 24 chunks of the row)
+  constexpr int SROW = BN * 2, SWZM = BN == 256 ? 31 : 7, NCH = BN / 8;
+  static_assert(128 * SROW <= SB, "half of the output tile fits in a stage buffer");
   // ---- epilogue: bias, bf16, staged through LDS (rows < 128 in smem0, the rest in smem1),
   // written out as whole 16-byte row segments.  DORA writes z first, then y = z g + bias
   // (both from the fp32 accumulators).
   auto st_ptr = [&](int r, int col) -> uint8_t* {
     uint8_t* base = r < 128 ? smem0 : smem1;
     const int rr = r & 127;
-    return base + rr * 512 + ((((col >> 3) ^ (rr & 31))) << 4) + ((col & 4) << 1);
+    return base + rr * SROW + ((((col >> 3) ^ (rr & SWZM))) << 4) + ((col & 4) << 1);
   };
   auto emit = [&](auto z_c, void* dst, int ldo) {
     constexpr bool Z = decltype(z_c)::value;       // DORA's unscaled output
@@ -299,8 +314,8 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
     for (int i = 0; i < 8; ++i) {
       const int r = wm * 128 + i * 16 + l16;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int cl = wn * 128 + j * 16 + 4 * lq;
+      for (int j = 0; j < FN; ++j) {
+        const int cl = wn * (BN / 2) + j * 16 + 4 * lq;
         float b4[4] = {0.f, 0.f, 0.f, 0.f};
         if (!Z && p.bias != nullptr) {
           const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n0 + cl);
@@ -316,12 +331,12 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
     }
     __syncthreads();
     uint16_t* out = static_cast<uint16_t*>(dst);
-    for (int idx = tid; idx < BM * 32; idx += 256) {
-      const int r = idx >> 5, c = idx & 31;
+    for (int idx = tid; idx < BM * NCH; idx += 256) {
+      const int r = idx / NCH, c = idx % NCH;
       if (m0 + r < M) {
         const uint8_t* base = r < 128 ? smem0 : smem1;
         const int rr = r & 127;
-        st16(out + (size_t)(m0 + r) * ldo + n0 + c * 8, lds_ld16(base, rr * 512 + ((c ^ (rr & 31)) << 4)));
+        st16(out + (size_t)(m0 + r) * ldo + n0 + c * 8, lds_ld16(base, rr * SROW + ((c ^ (rr & SWZM)) << 4)));
       }
     }
   };
@@ -384,8 +399,8 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
     for (int i = 0; i < 8; ++i) {
       const int r = wm * 128 + i * 16 + l16;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int cl = wn * 128 + j * 16 + 4 * lq;
+      for (int j = 0; j < FN; ++j) {
+        const int cl = wn * (BN / 2) + j * 16 + 4 * lq;
         float b4[4] = {0.f, 0.f, 0.f, 0.f};
         if (p.bias != nullptr) {
           const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n0 + cl);
@@ -400,12 +415,12 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
     }
     __syncthreads();
     uint16_t* out = static_cast<uint16_t*>(p.out);
-    for (int idx = tid; idx < BM * 32; idx += 256) {
-      const int r = idx >> 5, c = idx & 31;
+    for (int idx = tid; idx < BM * NCH; idx += 256) {
+      const int r = idx / NCH, c = idx % NCH;
       if (m0 + r < M) {
         const uint8_t* base = r < 128 ? smem0 : smem1;
         const int rr = r & 127;
-        st16(out + (size_t)(m0 + r) * p.ldo + n0 + c * 8, lds_ld16(base, rr * 512 + ((c ^ (rr & 31)) << 4)));
+        st16(out + (size_t)(m0 + r) * p.ldo + n0 + c * 8, lds_ld16(base, rr * SROW + ((c ^ (rr & SWZM)) << 4)));
       }
     }
   }
