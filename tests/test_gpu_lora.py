@@ -135,6 +135,10 @@ def test_bf16_fused_down_projection():
     (513, 768, 448, 64),
     (513, 448, 768, 64),
     (260, 256, 256, 8),
+    # the 192-column four-wave forward tile (N a multiple of 192 whose 256-column tiles
+    # underfill the chip; 768 above takes it too): odd k-tile count, N not a multiple of 256
+    (300, 384, 320, 16),
+    (129, 576, 256, 8),
 ])
 def test_bf16_four_wave_tiles(M, N, K, r):
     require_gpu()
