@@ -75,9 +75,12 @@ int ldl_version(void);
  *   LDL_TUNE_FWD_FUSED_DOWNPROJ (0/1, default 0): compute U = X.A^T inside the
  *     K-loop of the base GEMM from the LDS-staged X tiles (r <= 64, N multiple
  *     of 128) instead of a separate rank-r pass before it.
- *   LDL_TUNE_GEMM_4WAVE (0/1, default 1): run the plain bf16 LoRA GEMMs
- *     (forward and input gradient, N a multiple of 256, M > 128) on the
- *     four-wave 256x256 tile with 16x16x32 MFMAs; 0 selects the eight-wave tile.
+ *   LDL_TUNE_GEMM_4WAVE (0/1, default 1): run the bf16 GEMMs with a low-rank
+ *     term of rank <= 64 and M > 128 on the four-wave tile with 16x16x32 MFMAs:
+ *     the LoRA forward and input gradient and the DoRA forward (N a multiple of
+ *     256, or of 192 when 256-wide tiles would leave CUs idle), the DoRA input
+ *     gradient and the SwiGLU MLP's down-projection input gradient (N a multiple
+ *     of 256); 0 selects the eight-wave tile for all of them.
  * Returns LDL_OK, or LDL_E_INVAL for an unknown key or value. */
 typedef enum { LDL_TUNE_FWD_FUSED_DOWNPROJ = 0, LDL_TUNE_GEMM_4WAVE = 1 } ldl_tune_key;
 int ldl_set_tuning(int key, int value);
