@@ -164,9 +164,10 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         acc[i][j] = mfma_bf16(fb[j], fa[i], acc[i][j]);
-        // NT: keep each result in its accumulator's AGPRs (an empty asm with an AGPR
-        // operand); otherwise the allocator moves some accumulators through VGPRs
-        if constexpr (!NN) asm volatile("" : "+a"(acc[i][j]));
+        // NT 256: keep each result in its accumulator's AGPRs (an empty asm with an AGPR
+        // operand); otherwise the allocator moves some accumulators through VGPRs.  (At
+        // 192 columns the pins cost ~70 AGPR moves per k-tile and are left out.)
+        if constexpr (!NN && BN == 256) asm volatile("" : "+a"(acc[i][j]));
       }
   };
 
