@@ -251,10 +251,55 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* X, int M
   }
 }
 
+// bf16 rows of K <= 512 QV elements (K a multiple of 512): the same codes from one read of
+// the row, kept in registers (QV 16-byte pieces per lane) between the absmax and the codes.
+constexpr int kQuantRegPieces = 16;
+__global__ __launch_bounds__(256) void quantize_rows_reg_kernel(const uint16_t* X, int M, int K, int8_t* q,
+                                                                float* scale) {
+  constexpr int QV = kQuantRegPieces;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int nv = K / 512;
+  const uint16_t* x = X + (size_t)row * K + lane * 8;
+  u32x4 v[QV];
+#pragma unroll
+  for (int i = 0; i < QV; ++i) v[i] = i < nv ? ld16(x + i * 512) : u32x4{0u, 0u, 0u, 0u};
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < QV; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[i][t])), fabsf(bf16_hi(v[i][t]))));
+  amax = wave_max(amax);
+  const float sc = amax / 127.0f;
+  if (lane == 0) scale[row] = sc;
+  auto code = [&](float xv) -> uint32_t {
+    if (!(sc > 0.f)) return 0u;
+    float t = rintf(xv / sc);
+    t = fminf(fmaxf(t, -127.f), 127.f);
+    return (uint32_t)((int)t & 0xff);
+  };
+  int8_t* qrow = q + (size_t)row * K + lane * 8;
+#pragma unroll
+  for (int i = 0; i < QV; ++i) {
+    if (i < nv) {
+      u32x2 o;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        o[h] = code(bf16_lo(v[i][2 * h])) | (code(bf16_hi(v[i][2 * h])) << 8) |
+               (code(bf16_lo(v[i][2 * h + 1])) << 16) | (code(bf16_hi(v[i][2 * h + 1])) << 24);
+      *reinterpret_cast<u32x2*>(qrow + i * 512) = o;
+    }
+  }
+}
+
 hipError_t launch_quantize_rows(const void* X, int in_f32, int M, int K, int8_t* q, float* scale, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   const dim3 grid((M + 3) / 4), block(256);
   if (in_f32) hipLaunchKernelGGL(quantize_rows_kernel<true>, grid, block, 0, st, X, M, K, q, scale);
+  else if (K % 512 == 0 && K <= 512 * kQuantRegPieces &&
+           (reinterpret_cast<uintptr_t>(X) & 15) == 0 && (reinterpret_cast<uintptr_t>(q) & 7) == 0)
+    hipLaunchKernelGGL(quantize_rows_reg_kernel, grid, block, 0, st, static_cast<const uint16_t*>(X), M, K, q, scale);
   else hipLaunchKernelGGL(quantize_rows_kernel<false>, grid, block, 0, st, X, M, K, q, scale);
   return hipGetLastError();
 }

@@ -43,6 +43,23 @@ def test_quantizers_bit_exact():
     assert not torch.any(zq) and not torch.any(zs)
 
 
+@pytest.mark.parametrize("K", [512, 5120, 8192])
+def test_quantize_rows_bit_exact_one_read(K):
+    """Rows of a multiple of 512 up to 8192 elements are quantised from one read of the row
+    (kept in registers); codes and scales must equal the oracle's bit for bit."""
+    require_gpu()
+    import lora_dora_linear_amd as L
+    rng = np.random.default_rng(K)
+    x = rng.standard_normal((130, K)).astype(np.float32)
+    x[7] = 0.0                                       # a zero row: scale 0, codes 0
+    bits = inputs.f32_to_bf16_bits(x)
+    Xq, sx = L.w8a8_quantize_rows(dev(bits, "bf16"))
+    torch.cuda.synchronize()
+    q_ref, s_ref = ow.quantize_rows_int8(inputs.bf16_bits_to_f32(bits))
+    np.testing.assert_array_equal(Xq.cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(sx.cpu().numpy(), s_ref)
+
+
 @pytest.mark.parametrize("M,N,K", [(300, 512, 640), (100, 192, 256), (1024, 1024, 1024)])
 def test_int8_raw_product_exact(M, N, K):
     require_gpu()
