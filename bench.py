@@ -134,8 +134,9 @@ def main():
         copy_calibrate(args.copy_calibrate)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; multi-GPU runs are not part of it "
-                                   "(the data-parallel sharding is described in DESIGN.md)",
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the layer's data-parallel "
+                                   "sharding over several GPUs (rows of X per GPU, one all-reduce of "
+                                   "the factor gradients) is not implemented",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
 
