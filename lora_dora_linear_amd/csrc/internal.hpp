@@ -69,6 +69,9 @@ hipError_t launch_rowsumsq(const void* W0, int dtype_bf16, int N, int K, float* 
 hipError_t launch_dora_norm(int N, int r, float s, float eps, const float* w0_sumsq, const float* P,
                             const float* G, const uint16_t* B, const float* m, float* norm, float* g, hipStream_t st);
 hipError_t launch_scale_cols(const void* in, int M, int N, int ld, const float* g, void* out, hipStream_t st);
+
+// SwiGLU helper: h = silu(e) * u over bf16 [M, N] arrays with row stride ld
+hipError_t launch_silu_mul(const void* E, const void* U, int M, int N, int ld, void* H, hipStream_t st);
 hipError_t launch_dora_finalize(int N, int r, float s, float eps, const float* partT, const float* cspart,
                                 int nsplit, int rpT, const float* norm, const float* g, const float* m,
                                 const float* P, const float* G, const uint16_t* B,

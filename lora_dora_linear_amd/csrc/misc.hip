@@ -177,6 +177,35 @@ hipError_t launch_scale_cols(const void* in, int M, int N, int ld, const float* 
   return hipGetLastError();
 }
 
+// h[m, n] = bf16(silu(e[m, n]) * u[m, n]) (round to nearest even) from the stored bf16 gate
+// and up products: the SwiGLU activation when those come from two separate GEMMs.  The
+// products are taken from the same bf16 values the backward reads.  8 columns per thread.
+__global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* E, const uint16_t* U, int M, int N, int ld,
+                                                       uint16_t* H) {
+  const unsigned per_row = (unsigned)N / 8u;
+  const size_t total = (size_t)M * per_row;
+  for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (size_t)gridDim.x * blockDim.x) {
+    const size_t m = t / per_row, c = (t % per_row) * 8;
+    const size_t o = m * (size_t)ld + c;
+    const u32x4 e = ld16(E + o), u = ld16(U + o);
+    u32x4 h;
+    for (int i = 0; i < 4; ++i)
+      h[i] = pack_bf16x2(silu_f(bf16_lo(e[i])) * bf16_lo(u[i]), silu_f(bf16_hi(e[i])) * bf16_hi(u[i]));
+    st16(H + o, h);
+  }
+}
+
+hipError_t launch_silu_mul(const void* E, const void* U, int M, int N, int ld, void* H, hipStream_t st) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (N % 8 || ld % 8 || ld < N) return hipErrorInvalidValue;
+  const size_t total = (size_t)M * (N / 8);
+  size_t blocks = (total + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const uint16_t*>(E),
+                     static_cast<const uint16_t*>(U), M, N, ld, static_cast<uint16_t*>(H));
+  return hipGetLastError();
+}
+
 hipError_t launch_rowsumsq(const void* W0, int dtype_bf16, int N, int K, float* out, hipStream_t st) {
   const dim3 grid((N + 3) / 4), block(256);
   if (dtype_bf16) hipLaunchKernelGGL(rowsumsq_kernel<true>, grid, block, 0, st, W0, N, K, out);
