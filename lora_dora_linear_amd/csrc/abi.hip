@@ -79,6 +79,7 @@ inline hipStream_t S(void* st) { return static_cast<hipStream_t>(st); }
 // ------------------------------------------------------------------ workspace plans
 struct LoraBwdWs {
   float* V; float* U; float* partB; float* csB; float* partA;
+  uint32_t* pkB; uint32_t* pkA;    // packed S of the two column projections
   int nsB, msB, nsA, msA, rp;
 };
 LoraBwdWs plan_lora_bwd(Bump& b, int M, int N, int K, int r, bool need_u) {
@@ -92,6 +93,8 @@ LoraBwdWs plan_lora_bwd(Bump& b, int M, int N, int K, int r, bool need_u) {
   w.partB = b.take<float>((size_t)w.nsB * N * w.rp);
   w.csB = b.take<float>((size_t)w.nsB * N);
   w.partA = b.take<float>((size_t)w.nsA * K * w.rp);
+  w.pkB = b.take<uint32_t>(colproj_spk_words(M, r));
+  w.pkA = b.take<uint32_t>(colproj_spk_words(M, r));
   return w;
 }
 
@@ -99,6 +102,7 @@ struct DoraBwdWs {
   float* V; float* partT; float* cs; float* wB; float* partA; float* partQ; float* Qm;
   uint16_t* dYg;                   // dY.diag(g) in bf16 [M, N]
   float* partbias; float* csbias;
+  uint32_t* pkT; uint32_t* pkA; uint32_t* pkW; uint32_t* pkQ;
   int nsT, msT, nsA, msA, nsW, msW, nsQ, msQ, rp;
 };
 DoraBwdWs plan_dora_bwd(Bump& b, int M, int N, int K, int r) {
@@ -118,12 +122,17 @@ DoraBwdWs plan_dora_bwd(Bump& b, int M, int N, int K, int r) {
   w.partbias = b.take<float>((size_t)w.nsT * N * 16);
   w.csbias = b.take<float>((size_t)w.nsT * N);
   w.dYg = b.take<uint16_t>((size_t)M * N);
+  w.pkT = b.take<uint32_t>(colproj_spk_words(M, r));
+  w.pkA = b.take<uint32_t>(colproj_spk_words(M, r));
+  w.pkW = b.take<uint32_t>(colproj_spk_words(N, r));
+  w.pkQ = b.take<uint32_t>(colproj_spk_words(N, r));
   return w;
 }
 
 struct MlpBwdWs {
   float* Vd; float* Vgu; uint16_t* dEGu;
   float* partDd; float* partAd; float* partBg; float* partBu; float* partAgu;
+  uint32_t* pkDd; uint32_t* pkAd; uint32_t* pkBg; uint32_t* pkBu; uint32_t* pkAgu;
   int nsDd, msDd, nsAd, msAd, nsBg, msBg, nsAgu, msAgu, rp, rp2;
 };
 MlpBwdWs plan_mlp_bwd(Bump& b, int M, int K, int H, int r) {
@@ -142,6 +151,11 @@ MlpBwdWs plan_mlp_bwd(Bump& b, int M, int K, int H, int r) {
   w.partBg = b.take<float>((size_t)w.nsBg * H * w.rp);
   w.partBu = b.take<float>((size_t)w.nsBg * H * w.rp);
   w.partAgu = b.take<float>((size_t)w.nsAgu * K * w.rp2);
+  w.pkDd = b.take<uint32_t>(colproj_spk_words(M, r));
+  w.pkAd = b.take<uint32_t>(colproj_spk_words(M, r));
+  w.pkBg = b.take<uint32_t>(colproj_spk_words(M, r));
+  w.pkBu = b.take<uint32_t>(colproj_spk_words(M, r));
+  w.pkAgu = b.take<uint32_t>(colproj_spk_words(M, 2 * r));
   return w;
 }
 
@@ -199,13 +213,21 @@ ColProjParams cpp(int M, int C, int R, const void* X, int ldx, const float* Sm, 
   p.S = Sm; p.lds = lds; p.s_in = s_in;
   p.Z = static_cast<const uint16_t*>(Z); p.ldz = ldz; p.colsum_mode = mode;
   p.msplit = msplit; p.part = part; p.cspart = cspart;
+  p.spk = nullptr;
+  return p;
+}
+
+// the same job with its packed-S workspace
+ColProjParams pk(ColProjParams p, uint32_t* spk) {
+  p.spk = spk;
   return p;
 }
 
 hipError_t colproj(int M, int C, int R, const void* X, int ldx, const float* Sm, int lds, float s_in,
                    const void* Z, int ldz, int mode, int nsplit, int msplit, float* part, float* cspart,
-                   hipStream_t st) {
-  return launch_colproj(cpp(M, C, R, X, ldx, Sm, lds, s_in, Z, ldz, mode, msplit, part, cspart), nsplit, st);
+                   hipStream_t st, uint32_t* spk = nullptr) {
+  return launch_colproj(pk(cpp(M, C, R, X, ldx, Sm, lds, s_in, Z, ldz, mode, msplit, part, cspart), spk), nsplit,
+                        st);
 }
 
 // out[rows, cols] = alpha * sum over nsplit partials (+ row scale) (+ addend)
@@ -426,8 +448,9 @@ int lora_linear_bwd(int M, int N, int K, int r, float s, int dtype, const void* 
   }
   // dB = s.dY^T.U (+ dbias = column sums of dY in the same pass) and dA = s.V^T.X: one launch each
   // for the split partial sums and for their fixed-order reduction
-  LDL_TRY(launch_colproj2(cpp(M, N, r, dY, N, U, r, 1.f, nullptr, 0, dbias ? 2 : 0, w.msB, w.partB, w.csB), w.nsB,
-                          cpp(M, K, r, X, K, w.V, r, 1.f, nullptr, 0, 0, w.msA, w.partA, nullptr), w.nsA, st));
+  LDL_TRY(launch_colproj2(pk(cpp(M, N, r, dY, N, U, r, 1.f, nullptr, 0, dbias ? 2 : 0, w.msB, w.partB, w.csB), w.pkB),
+                          w.nsB, pk(cpp(M, K, r, X, K, w.V, r, 1.f, nullptr, 0, 0, w.msA, w.partA, nullptr), w.pkA),
+                          w.nsA, st));
   LDL_TRY(launch_reduce2(rdp(N, r, w.partB, (size_t)N * w.rp, w.nsB, w.rp, false, s, dB, r),
                          rdp(r, K, w.partA, (size_t)K * w.rp, w.nsA, w.rp, true, s, dA, K), st));
   if (dbias) LDL_TRY(launch_reduce_colsum(w.csB, w.nsB, N, dbias, st));
@@ -506,7 +529,7 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, c
 
   // dg and dZ^T.U in one pass over dY (and Z); M == 0 gives zero partials
   if (M > 0) {
-    LDL_TRY(colproj(M, N, r, dY, N, U_saved, r, 1.f, Z_saved, N, 1, w.nsT, w.msT, w.partT, w.cs, st));
+    LDL_TRY(colproj(M, N, r, dY, N, U_saved, r, 1.f, Z_saved, N, 1, w.nsT, w.msT, w.partT, w.cs, st, w.pkT));
   } else {
     LDL_TRY(zero(w.partT, (size_t)w.nsT * N * w.rp, st));
     LDL_TRY(zero(w.cs, (size_t)w.nsT * N, st));
@@ -533,15 +556,16 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, c
       LDL_TRY(rowproj_t(M, N, r, dY, N, Bh, r, g, w.V, r, 1.f, st));
     }
     // s.V^T.X into the first nsA partials of dA
-    jobs[nj] = cpp(M, K, r, X, K, w.V, r, s, nullptr, 0, 0, w.msA, w.partA, nullptr);
+    jobs[nj] = pk(cpp(M, K, r, X, K, w.V, r, s, nullptr, 0, 0, w.msA, w.partA, nullptr), w.pkA);
     ns[nj++] = w.nsA;
   } else {
     LDL_TRY(zero(w.partA, (size_t)w.nsA * K * w.rp, st));
   }
   // (2s.w.B)^T.W0 into the next nsW partials; Q = B^T.(2s.w.B)
-  jobs[nj] = cpp(N, K, r, W0, K, w.wB, r, 1.f, nullptr, 0, 0, w.msW, w.partA + (size_t)w.nsA * K * w.rp, nullptr);
+  jobs[nj] = pk(cpp(N, K, r, W0, K, w.wB, r, 1.f, nullptr, 0, 0, w.msW, w.partA + (size_t)w.nsA * K * w.rp, nullptr),
+                w.pkW);
   ns[nj++] = w.nsW;
-  jobs[nj] = cpp(N, r, r, B, r, w.wB, r, 1.f, nullptr, 0, 0, w.msQ, w.partQ, nullptr);
+  jobs[nj] = pk(cpp(N, r, r, B, r, w.wB, r, 1.f, nullptr, 0, 0, w.msQ, w.partQ, nullptr), w.pkQ);
   ns[nj++] = w.nsQ;
   LDL_TRY(launch_colproj_batch(jobs, ns, nj, st));
   LDL_TRY(reduce(r, r, w.partQ, (size_t)r * w.rp, w.nsQ, w.rp, false, 1.f, w.Qm, r, st));
@@ -646,16 +670,19 @@ int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, fl
     LDL_TRY(launch_gemm(GK_NN_SWIGLU, p, st));
   }
   // dBd = s_d.dOut^T.U_d and dAd = s_d.V_d^T.H
-  LDL_TRY(launch_colproj2(cpp(M, K, r, dOut, K, Ud, r3, 1.f, nullptr, 0, 0, w.msDd, w.partDd, nullptr), w.nsDd,
-                          cpp(M, H, r, H_saved, H, w.Vd, r, 1.f, nullptr, 0, 0, w.msAd, w.partAd, nullptr), w.nsAd,
-                          st));
+  LDL_TRY(launch_colproj2(pk(cpp(M, K, r, dOut, K, Ud, r3, 1.f, nullptr, 0, 0, w.msDd, w.partDd, nullptr), w.pkDd),
+                          w.nsDd,
+                          pk(cpp(M, H, r, H_saved, H, w.Vd, r, 1.f, nullptr, 0, 0, w.msAd, w.partAd, nullptr), w.pkAd),
+                          w.nsAd, st));
   LDL_TRY(launch_reduce2(rdp(K, r, w.partDd, (size_t)K * w.rp, w.nsDd, w.rp, false, s_down, dBd, r),
                          rdp(r, H, w.partAd, (size_t)H * w.rp, w.nsAd, w.rp, true, s_down, dAd, H), st));
   // ---- gate / up: V_g = s_g.dE.Bg, V_u = s_u.dGu.Bu (pre-scaled), dBg, dBu
   LDL_TRY(rowproj_t(M, H, r, w.dEGu, 2 * H, Bg, r, nullptr, w.Vgu, 2 * r, s_gate, st));
   LDL_TRY(rowproj_t(M, H, r, w.dEGu + H, 2 * H, Bu, r, nullptr, w.Vgu + r, 2 * r, s_up, st));
-  LDL_TRY(launch_colproj2(cpp(M, H, r, w.dEGu, 2 * H, Ug, r3, 1.f, nullptr, 0, 0, w.msBg, w.partBg, nullptr), w.nsBg,
-                          cpp(M, H, r, w.dEGu + H, 2 * H, Uu, r3, 1.f, nullptr, 0, 0, w.msBg, w.partBu, nullptr),
+  LDL_TRY(launch_colproj2(pk(cpp(M, H, r, w.dEGu, 2 * H, Ug, r3, 1.f, nullptr, 0, 0, w.msBg, w.partBg, nullptr), w.pkBg),
+                          w.nsBg,
+                          pk(cpp(M, H, r, w.dEGu + H, 2 * H, Uu, r3, 1.f, nullptr, 0, 0, w.msBg, w.partBu, nullptr),
+                             w.pkBu),
                           w.nsBg, st));
   LDL_TRY(launch_reduce2(rdp(H, r, w.partBg, (size_t)H * w.rp, w.nsBg, w.rp, false, s_gate, dBg, r),
                          rdp(H, r, w.partBu, (size_t)H * w.rp, w.nsBg, w.rp, false, s_up, dBu, r), st));
@@ -670,7 +697,8 @@ int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, fl
     LDL_TRY(launch_gemm(GK_NN_PLAIN, p, st));
   }
   // dAg, dAu = [V_g | V_u]^T.X in one pass over X
-  LDL_TRY(colproj(M, K, 2 * r, X, K, w.Vgu, 2 * r, 1.f, nullptr, 0, 0, w.nsAgu, w.msAgu, w.partAgu, nullptr, st));
+  LDL_TRY(colproj(M, K, 2 * r, X, K, w.Vgu, 2 * r, 1.f, nullptr, 0, 0, w.nsAgu, w.msAgu, w.partAgu, nullptr, st,
+                  w.pkAgu));
   LDL_TRY(launch_reduce2(rdp(r, K, w.partAgu, (size_t)K * w.rp2, w.nsAgu, w.rp2, true, 1.f, dAg, K),
                          rdp(r, K, w.partAgu + r, (size_t)K * w.rp2, w.nsAgu, w.rp2, true, 1.f, dAu, K), st));
   return LDL_OK;
@@ -770,8 +798,9 @@ int w8a8_lora_linear_bwd(int M, int N, int K, int r, float s, const void* dY, co
     p.out = dX; p.ldo = K;
     LDL_TRY(gemm_timed(1, GK_NN_I8_SCALE, p, st));
   }
-  LDL_TRY(launch_colproj2(cpp(M, N, r, dY, N, U, r, 1.f, nullptr, 0, 0, w.msB, w.partB, nullptr), w.nsB,
-                          cpp(M, K, r, X, K, w.V, r, 1.f, nullptr, 0, 0, w.msA, w.partA, nullptr), w.nsA, st));
+  LDL_TRY(launch_colproj2(pk(cpp(M, N, r, dY, N, U, r, 1.f, nullptr, 0, 0, w.msB, w.partB, nullptr), w.pkB), w.nsB,
+                          pk(cpp(M, K, r, X, K, w.V, r, 1.f, nullptr, 0, 0, w.msA, w.partA, nullptr), w.pkA), w.nsA,
+                          st));
   LDL_TRY(launch_reduce2(rdp(N, r, w.partB, (size_t)N * w.rp, w.nsB, w.rp, false, s, dB, r),
                          rdp(r, K, w.partA, (size_t)K * w.rp, w.nsA, w.rp, true, s, dA, K), st));
   return LDL_OK;

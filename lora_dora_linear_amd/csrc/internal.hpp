@@ -27,6 +27,8 @@ struct ColProjParams {
   int msplit;                      // rows per split (multiple of 256)
   float* part;                     // [nsplit][C][RP]
   float* cspart;                   // [nsplit][C]
+  uint32_t* spk;                   // workspace for S pre-split into bf16 hi / lo fragments,
+                                   // colproj_spk_words(M, R) words (used from rank 32 up)
 };
 
 struct ReduceParams {
@@ -51,6 +53,8 @@ bool gemm_shape_ok(GemmKind kind, int M, int N, int K);
 
 hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st);
 int colproj_rp(int R);
+// size in 32-bit words of the packed S a column projection of M rows and rank R needs
+size_t colproj_spk_words(int M, int R);
 // split plan of a column projection over M rows and C columns, aiming at `blocks` blocks
 void colproj_plan(int M, int C, int* nsplit, int* msplit, int blocks = 512);
 hipError_t launch_colproj(const ColProjParams& p, int nsplit, hipStream_t st);

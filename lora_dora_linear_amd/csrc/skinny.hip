@@ -451,6 +451,14 @@ __global__ __launch_bounds__(256) void colproj_kernel(const ColProjBatch batch) 
 // waves split each sub-tile's (32-row step, column block) work items and
 // combine their partial sums at the end.  X rows are stored with 16-byte
 // chunk c of row m at physical chunk c ^ 2 (m & 3).
+//
+// From rank 32 up (PK) S comes pre-split: pack_s_kernel writes s_in * S once as bf16
+// hi + lo parts in MFMA fragment order (per 8-row group g: RP 16-byte chunks of hi, chunk j
+// = rows 8g .. 8g+7 of rank column j, then RP chunks of lo), so a sub-tile's S is one
+// contiguous copy and each fragment one 16-byte LDS read.  Building the fragments from
+// the fp32 tile in every block costs more than the MFMAs at rank 64 (measured: 331 us of
+// which ~180 us went to it at 8192 rows x 2 x 14336 columns).  The values fed to the MFMAs
+// are the same bits either way.
 template <int RP>
 struct ColStream {
   // rows per sub-tile: 64 from rank 32 up keeps the 3-stage ring at 48 KB, so three blocks
@@ -462,11 +470,13 @@ struct ColStream {
   static constexpr int WPS = 4 / NSTEP;                // waves per step
   static constexpr int CFW = 4 / WPS;                  // 16-column blocks per wave
   static constexpr int STAGES = 3;
+  static constexpr bool PK = RP >= 32;                 // S pre-split into packed hi / lo fragments
 };
 
 template <int RP, bool HASZ>
 __global__ __launch_bounds__(256) void colstream_kernel(const ColProjBatch batch) {
   using T = ColStream<RP>;
+  constexpr bool PK = T::PK;
   constexpr int NB = RP / 16, MS = T::MS, XB = T::XB, SBY = T::SBY, ST = T::STAGES;
   constexpr int SB = XB * (HASZ ? 2 : 1) + SBY;        // bytes per stage
   constexpr int NI = (XB * (HASZ ? 2 : 1) + SBY) / 4096;
@@ -488,7 +498,11 @@ __global__ __launch_bounds__(256) void colstream_kernel(const ColProjBatch batch
   const uint32_t ldx_b = (uint32_t)p.ldx * 2u, lds_b = (uint32_t)p.lds * 4u, ldz_b = (uint32_t)p.ldz * 2u;
   // rows past mend read as zero
   const __amdgpu_buffer_rsrc_t rs_x = make_rsrc(p.X, (uint32_t)mend * ldx_b);
-  const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(p.S, p.R > 0 ? (uint32_t)mend * lds_b : 0u);
+  // packed S: the whole array (rows past mend are finite and meet zero X rows; groups are
+  // zero-filled past M)
+  const __amdgpu_buffer_rsrc_t rs_s =
+      PK ? make_rsrc(p.spk, p.R > 0 ? (uint32_t)((p.M + 7) / 8) * (32u * RP) : 0u)
+         : make_rsrc(p.S, p.R > 0 ? (uint32_t)mend * lds_b : 0u);
   const __amdgpu_buffer_rsrc_t rs_z = make_rsrc(p.Z, zmode ? (uint32_t)mend * ldz_b : 0u);
   constexpr int NIX = XB / 4096, NIS = SBY / 4096;
   uint32_t x_off[NIX], s_off[NIS];
@@ -502,7 +516,7 @@ __global__ __launch_bounds__(256) void colstream_kernel(const ColProjBatch batch
 #pragma unroll
   for (int i = 0; i < NIS; ++i) {
     const int b = (i * 4 + wave) * 1024 + lane * 16;
-    s_off[i] = (uint32_t)(b / rb) * lds_b + (uint32_t)(b % rb);
+    s_off[i] = PK ? (uint32_t)b : (uint32_t)(b / rb) * lds_b + (uint32_t)(b % rb);
   }
   auto issue = [&](int sub) {
     uint8_t* sb = smem + (sub % ST) * SB;
@@ -510,7 +524,8 @@ __global__ __launch_bounds__(256) void colstream_kernel(const ColProjBatch batch
 #pragma unroll
     for (int i = 0; i < NIX; ++i) buf2lds16(rs_x, x_off[i], m * ldx_b, sb + (i * 4 + wave) * 1024);
 #pragma unroll
-    for (int i = 0; i < NIS; ++i) buf2lds16(rs_s, s_off[i], m * lds_b, sb + XB + (i * 4 + wave) * 1024);
+    for (int i = 0; i < NIS; ++i)
+      buf2lds16(rs_s, s_off[i], PK ? m * (4u * RP) : m * lds_b, sb + XB + (i * 4 + wave) * 1024);
     if constexpr (HASZ) {
 #pragma unroll
       for (int i = 0; i < NIX; ++i)   // same element layout as X (Z has its own leading dimension)
@@ -540,6 +555,14 @@ __global__ __launch_bounds__(256) void colstream_kernel(const ColProjBatch batch
     const int mrow = my_step * 32 + 8 * lq;             // first of this lane's 8 rows
     // S^T fragments (rank j = jb*16 + lr, rows mrow .. mrow+7), hi / lo bf16 parts, pre-scaled
     u32x4 shi[NB], slo[NB];
+    if constexpr (PK) {
+      const uint8_t* sp = sb + XB + (my_step * 4 + lq) * (32 * RP) + lr * 16;
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb) {
+        shi[jb] = *reinterpret_cast<const u32x4*>(sp + jb * 256);
+        slo[jb] = *reinterpret_cast<const u32x4*>(sp + RP * 16 + jb * 256);
+      }
+    } else {
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb) {
       const int j = jb * 16 + lr;
@@ -555,6 +578,7 @@ __global__ __launch_bounds__(256) void colstream_kernel(const ColProjBatch batch
         slo[jb][e] = f32_to_bf16_bits(v0 - __uint_as_float(h0 << 16)) |
                      (f32_to_bf16_bits(v1 - __uint_as_float(h1 << 16)) << 16);
       }
+    }
     }
 #pragma unroll
     for (int q = 0; q < T::CFW; ++q) {
@@ -763,6 +787,63 @@ hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st) {
 
 int colproj_rp(int R) { return R <= 16 ? 16 : R <= 32 ? 32 : R <= 64 ? 64 : 128; }
 
+size_t colproj_spk_words(int M, int R) { return M > 0 && R > 0 ? (size_t)((M + 7) / 8) * 8 * colproj_rp(R) : 0; }
+
+// Packed S for the streamed column projection (rank padding RP >= 32): for 8-row group g
+// and rank column j < RP, the 8 values v = s_in * S[8g + k, j] (zero past M and for
+// j >= R) as bf16 hi = rne(v) at 16-byte chunk g * 2RP + j and lo = rne(v - hi) at chunk
+// g * 2RP + RP + j.  One thread per (g, j); blockIdx.y selects the job.
+struct PackSBatch {
+  const float* S[kColProjBatch];
+  int lds[kColProjBatch], M[kColProjBatch], R[kColProjBatch];
+  float s_in[kColProjBatch];
+  uint32_t* out[kColProjBatch];
+};
+
+template <int RP>
+__global__ __launch_bounds__(256) void pack_s_kernel(const PackSBatch b) {
+  const int job = blockIdx.y;
+  const int M = b.M[job], R = b.R[job];
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= ((M + 7) / 8) * RP) return;
+  const int g = t / RP, j = t % RP;
+  u32x4 hi, lo;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int m0 = 8 * g + 2 * e;
+    float v0 = 0.f, v1 = 0.f;
+    if (j < R) {
+      if (m0 < M) v0 = b.S[job][(size_t)m0 * b.lds[job] + j] * b.s_in[job];
+      if (m0 + 1 < M) v1 = b.S[job][(size_t)(m0 + 1) * b.lds[job] + j] * b.s_in[job];
+    }
+    const uint32_t h0 = f32_to_bf16_bits(v0), h1 = f32_to_bf16_bits(v1);
+    hi[e] = h0 | (h1 << 16);
+    lo[e] = f32_to_bf16_bits(v0 - __uint_as_float(h0 << 16)) | (f32_to_bf16_bits(v1 - __uint_as_float(h1 << 16)) << 16);
+  }
+  uint32_t* o = b.out[job] + (size_t)g * (8 * RP);
+  *reinterpret_cast<u32x4*>(o + 4 * j) = hi;
+  *reinterpret_cast<u32x4*>(o + 4 * (RP + j)) = lo;
+}
+
+static hipError_t pack_s_launch(const ColProjParams* jobs, int njobs, int RP, hipStream_t st) {
+  PackSBatch b{};
+  int nj = 0, maxt = 0;
+  for (int i = 0; i < njobs; ++i) {
+    if (jobs[i].R <= 0 || jobs[i].M <= 0) continue;
+    b.S[nj] = jobs[i].S; b.lds[nj] = jobs[i].lds; b.M[nj] = jobs[i].M; b.R[nj] = jobs[i].R;
+    b.s_in[nj] = jobs[i].s_in; b.out[nj] = jobs[i].spk;
+    const int tcount = ((jobs[i].M + 7) / 8) * RP;
+    if (tcount > maxt) maxt = tcount;
+    ++nj;
+  }
+  if (nj == 0) return hipSuccess;
+  const dim3 grid((maxt + 255) / 256, nj);
+  if (RP == 32) hipLaunchKernelGGL(pack_s_kernel<32>, grid, dim3(256), 0, st, b);
+  else if (RP == 64) hipLaunchKernelGGL(pack_s_kernel<64>, grid, dim3(256), 0, st, b);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 void colproj_plan(int M, int C, int* nsplit, int* msplit, int blocks) {
   if (M <= 0) {
     *nsplit = 1;
@@ -796,10 +877,15 @@ static hipError_t colproj_launch(const ColProjBatch& b, int gx, int gy, int R, h
   return hipGetLastError();
 }
 
-// The streamed kernel copies 16-byte pieces: X, Z and S rows must be 16-byte aligned.
+// The streamed kernel copies 16-byte pieces: X, Z and S rows (below rank 32) must be
+// 16-byte aligned; from rank 32 up it reads S from the packed copy in spk.
 static bool colstream_ok(const ColProjParams& p) {
   if (p.ldx % 8 || (((uintptr_t)p.X) & 15)) return false;
-  if (p.R > 0 && (p.R % 4 || p.lds % 4 || (((uintptr_t)p.S) & 15))) return false;
+  if (p.R > 0 && colproj_rp(p.R) >= 32) {
+    if (p.spk == nullptr || (((uintptr_t)p.spk) & 15)) return false;
+  } else if (p.R > 0 && (p.R % 4 || p.lds % 4 || (((uintptr_t)p.S) & 15))) {
+    return false;
+  }
   if (p.colsum_mode == 1 && (p.ldz % 8 || (((uintptr_t)p.Z) & 15))) return false;
   return p.msplit % 128 == 0;
 }
@@ -840,6 +926,10 @@ hipError_t launch_colproj_batch(const ColProjParams* jobs, const int* nsplit, in
     hasz = hasz || jobs[i].colsum_mode == 1;
   }
   if (stream && colproj_rp(jobs[0].R) <= 64) {      // rank 128: the register-transposing kernel is faster
+    if (colproj_rp(jobs[0].R) >= 32) {
+      const hipError_t e = pack_s_launch(jobs, njobs, colproj_rp(jobs[0].R), st);
+      if (e != hipSuccess) return e;
+    }
     return hasz ? colstream_launch<true>(b, (maxc + 63) / 64, b.first[njobs], jobs[0].R, st)
                 : colstream_launch<false>(b, (maxc + 63) / 64, b.first[njobs], jobs[0].R, st);
   }
