@@ -206,6 +206,45 @@ hipError_t launch_silu_mul(const void* E, const void* U, int M, int N, int ld, v
   return hipGetLastError();
 }
 
+// SwiGLU backward from the stored bf16 dh, e and u (8 columns per thread):
+// de = dh u sigma(e) (1 + e (1 - sigma(e))) overwrites dh in place, du = dh e sigma(e).
+// Each thread reads its own dh chunk before writing de there.
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(uint16_t* dE, int ld_de, const uint16_t* E, int ld_e,
+                                                         const uint16_t* U, int ld_u, uint16_t* dU, int ld_du, int M,
+                                                         int N) {
+  const unsigned per_row = (unsigned)N / 8u;
+  const size_t total = (size_t)M * per_row;
+  for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (size_t)gridDim.x * blockDim.x) {
+    const size_t m = t / per_row, c = (t % per_row) * 8;
+    const u32x4 d = ld16(dE + m * (size_t)ld_de + c), e = ld16(E + m * (size_t)ld_e + c),
+                u = ld16(U + m * (size_t)ld_u + c);
+    u32x4 de, du;
+    for (int i = 0; i < 4; ++i) {
+      const float e0 = bf16_lo(e[i]), e1 = bf16_hi(e[i]), d0 = bf16_lo(d[i]), d1 = bf16_hi(d[i]);
+      const float s0 = sigmoid_f(e0), s1 = sigmoid_f(e1);
+      de[i] = pack_bf16x2(d0 * bf16_lo(u[i]) * s0 * (1.f + e0 * (1.f - s0)),
+                          d1 * bf16_hi(u[i]) * s1 * (1.f + e1 * (1.f - s1)));
+      du[i] = pack_bf16x2(d0 * e0 * s0, d1 * e1 * s1);
+    }
+    st16(dE + m * (size_t)ld_de + c, de);
+    st16(dU + m * (size_t)ld_du + c, du);
+  }
+}
+
+hipError_t launch_swiglu_bwd(void* dE, int ld_de, const void* E, int ld_e, const void* U, int ld_u, void* dU,
+                             int ld_du, int M, int N, hipStream_t st) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (N % 8 || ld_de % 8 || ld_e % 8 || ld_u % 8 || ld_du % 8 || ld_de < N || ld_e < N || ld_u < N || ld_du < N)
+    return hipErrorInvalidValue;
+  const size_t total = (size_t)M * (N / 8);
+  size_t blocks = (total + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<uint16_t*>(dE), ld_de,
+                     static_cast<const uint16_t*>(E), ld_e, static_cast<const uint16_t*>(U), ld_u,
+                     static_cast<uint16_t*>(dU), ld_du, M, N);
+  return hipGetLastError();
+}
+
 hipError_t launch_rowsumsq(const void* W0, int dtype_bf16, int N, int K, float* out, hipStream_t st) {
   const dim3 grid((N + 3) / 4), block(256);
   if (dtype_bf16) hipLaunchKernelGGL(rowsumsq_kernel<true>, grid, block, 0, st, W0, N, K, out);
