@@ -246,7 +246,8 @@ def main():
         base = 2.0 * M * K * H * 3 * 2           # three projections, forward + input gradient
         lora = 3 * (6.0 * M * r * (K + H))
         flops = base + lora
-        gemm_kinds = ()
+        # timed: the down projection (NT, four-wave) and dX over the 2H reduction (NN, eight-wave)
+        gemm_flops = {0: 2.0 * M * K * H + 2.0 * M * K * r, 1: 2.0 * M * K * 2 * H + 2.0 * M * K * 2 * r}
         config = {"workload": f"bf16 LoRA MLP with fused SwiGLU fwd+bwd, M={M}, K={K}, H={H}, r={r}, s={s}",
                   "M": M, "K": K, "H": H, "r": r, "s": s}
     else:
@@ -320,6 +321,10 @@ def main():
         four = wl in ("lora", "dora") and args.gemm_4wave != 0
         names = {0: "forward base GEMM (" + ("gemm16_kernel NT" if four else "gemm_kernel NT") + ")",
                  1: "input-gradient GEMM (" + ("gemm16_kernel NN" if four else "gemm_kernel NN") + ")"}
+        if wl == "swiglu":
+            names = {0: "down-projection GEMM (" + ("gemm16_kernel NT" if args.gemm_4wave != 0 else "gemm_kernel NT")
+                        + ")",
+                     1: "input-gradient GEMM over gate and up (gemm_kernel NN)"}
         peak = PEAK_INT8 if (wl == "w8a8" and dom == 0) else PEAK_BF16
         traffic = recorded_traffic(f"{wl}:{names[dom]}")
         out["roofline"] = {"bound": "mfma", "kernel": names[dom], "achieved": round(kern[dom]["tflops"], 1),

@@ -623,7 +623,7 @@ int swiglu_lora_mlp_fwd(int M, int K, int H, int r, float s_gate, float s_up, fl
   q.S = U_save + 2 * r; q.ld_s = r3; q.r_epi = r; q.s_epi = s_down;
   q.e0 = Bd; q.e1 = Bd; q.e_ldn = r; q.e_ldj = 1; q.e_jsplit = r;
   q.out = Out; q.ldo = K;
-  LDL_TRY(launch_gemm(GK_NT_PLAIN, q, st));
+  LDL_TRY(gemm_timed(0, GK_NT_PLAIN, q, st));
   return LDL_OK;
 }
 
@@ -694,7 +694,7 @@ int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, fl
     p.S = w.Vgu; p.ld_s = 2 * r; p.r_epi = 2 * r; p.s_epi = 1.f;
     p.e0 = Ag; p.e1 = Au; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = r;
     p.out = dX; p.ldo = K;
-    LDL_TRY(launch_gemm(GK_NN_PLAIN, p, st));
+    LDL_TRY(gemm_timed(1, GK_NN_PLAIN, p, st));
   }
   // dAg, dAu = [V_g | V_u]^T.X in one pass over X
   LDL_TRY(colproj(M, K, 2 * r, X, K, w.Vgu, 2 * r, 1.f, nullptr, 0, 0, w.nsAgu, w.msAgu, w.partAgu, nullptr, st,
