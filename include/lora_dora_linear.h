@@ -81,8 +81,12 @@ int ldl_version(void);
  *     256, or of 192 when 256-wide tiles would leave CUs idle), the DoRA input
  *     gradient and the SwiGLU MLP's down-projection input gradient (N a multiple
  *     of 256); 0 selects the eight-wave tile for all of them.
+ *   LDL_TUNE_ROWSTREAM_32 (0/1/2, default 1): row projections of rank 33..64
+ *     (U = X.A^T, V = dY.B and their like) on 32-row blocks that stage the rank
+ *     factor once per 32 rows: 1 when those blocks still fill the 256 CUs
+ *     (M >= 8161), 2 whenever the rank allows, 0 never.  Results are identical.
  * Returns LDL_OK, or LDL_E_INVAL for an unknown key or value. */
-typedef enum { LDL_TUNE_FWD_FUSED_DOWNPROJ = 0, LDL_TUNE_GEMM_4WAVE = 1 } ldl_tune_key;
+typedef enum { LDL_TUNE_FWD_FUSED_DOWNPROJ = 0, LDL_TUNE_GEMM_4WAVE = 1, LDL_TUNE_ROWSTREAM_32 = 2 } ldl_tune_key;
 int ldl_set_tuning(int key, int value);
 
 /* Kernel timing hook for profilers and benchmarks.  While set, the library

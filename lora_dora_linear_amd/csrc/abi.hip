@@ -306,6 +306,10 @@ int ldl_set_tuning(int key, int value) {
     g_gemm_4wave = value;
     return LDL_OK;
   }
+  if (key == LDL_TUNE_ROWSTREAM_32 && value >= 0 && value <= 2) {
+    g_rowstream32 = value;
+    return LDL_OK;
+  }
   return LDL_E_INVAL;
 }
 

@@ -136,11 +136,16 @@ __global__ __launch_bounds__(512) void rowproj_kernel(const RowProjParams p) {
 // 16-byte chunk c of row r at physical chunk c ^ (r & 15); a transposed Q
 // (a [K, R] matrix, rows of R bf16) is stored as-is and read back with the
 // transposing LDS read.
-template <int RP, bool KS>
+//
+// BMR = 32 (rank 64): a block takes 32 rows, two 16-row MFMA tiles that share each Q
+// fragment, so the [K, 64] (or [64, K]) rank factor is staged once per 32 rows instead of
+// per 16; every output row sees the same k-steps on the same wave in the same order as
+// with 16-row blocks (identical results).
+template <int RP, bool KS, int BMR = 16>
 struct RowStream {
   static constexpr int KC = RP <= 32 ? 512 : (RP == 64 ? 256 : 128);   // elements per chunk
   static constexpr int RL = KC * 2;                  // bytes per staged row
-  static constexpr int PB = 16 * RL;                 // P slice
+  static constexpr int PB = BMR * RL;                // P slice
   static constexpr int QB = RP * RL;                 // Q slice (RP rows of KC, or KC rows of R <= RP)
   static constexpr int GB = KS ? 4096 : 0;           // k-scale slice: KC floats, four 1 KB copies
   static constexpr int SB = PB + QB + GB;
@@ -158,20 +163,21 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int RP, bool KS>
+template <int RP, bool KS, int BMR = 16>
 __global__ __launch_bounds__(256) void rowstream_kernel(const RowProjParams p) {
-  using T = RowStream<RP, KS>;
+  using T = RowStream<RP, KS, BMR>;
   constexpr int NB = RP / 16, KC = T::KC, RL = T::RL, SB = T::SB, ST = T::STAGES;
+  constexpr int NH = BMR / 16;                       // 16-row MFMA tiles per block
   __shared__ __attribute__((aligned(16))) uint8_t smem[ST * SB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lq = lane >> 4;
-  const int m0 = blockIdx.x * 16;
+  const int m0 = blockIdx.x * BMR;
   const int nch = (p.K + KC - 1) / KC;
   const bool tq = p.q_trans != 0;
 
   const uint32_t ldp_b = (uint32_t)p.ldp * 2u, ldq_b = (uint32_t)p.ldq * 2u;
-  // a block's 16 rows lie in one P segment (the split is a multiple of 16)
+  // a block's BMR rows lie in one P segment (the split is a multiple of BMR)
   const bool seg1 = p.P1 != nullptr && m0 >= p.p_split;
   const int pm0 = seg1 ? m0 - p.p_split : m0;
   const __amdgpu_buffer_rsrc_t rs_p = seg1 ? make_rsrc(p.P1, (uint32_t)(p.M - p.p_split) * ldp_b)
@@ -214,9 +220,11 @@ __global__ __launch_bounds__(256) void rowstream_kernel(const RowProjParams p) {
     if constexpr (KS) buf2lds16(rs_g, (uint32_t)(wave * 1024 + lane * 16), (uint32_t)ch * KC * 4u, sb + T::PB + T::QB + wave * 1024);
   };
 
-  f32x4 acc[NB];
+  f32x4 acc[NH][NB];
 #pragma unroll
-  for (int jb = 0; jb < NB; ++jb) acc[jb] = f32x4{0, 0, 0, 0};
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) acc[h][jb] = f32x4{0, 0, 0, 0};
 
 #pragma unroll
   for (int c = 0; c < ST - 1; ++c)
@@ -236,7 +244,9 @@ __global__ __launch_bounds__(256) void rowstream_kernel(const RowProjParams p) {
     const int nv = min(KC, p.K - ch * KC) / 32;
     for (int st = wave; st < nv; st += 4) {
       const int lc = st * 4 + lq;
-      const u32x4 pf = *reinterpret_cast<const u32x4*>(sb + lr * RL + ((lc ^ lr) << 4));
+      u32x4 pf[NH];
+#pragma unroll
+      for (int h = 0; h < NH; ++h) pf[h] = *reinterpret_cast<const u32x4*>(sb + (h * 16 + lr) * RL + ((lc ^ lr) << 4));
 #pragma unroll
       for (int jb = 0; jb < NB; ++jb) {
         u32x4 qf;
@@ -254,22 +264,27 @@ __global__ __launch_bounds__(256) void rowstream_kernel(const RowProjParams p) {
           const int j = jb * 16 + lr;
           qf = *reinterpret_cast<const u32x4*>(sq + j * RL + ((lc ^ lr) << 4));
         }
-        acc[jb] = mfma_bf16(qf, pf, acc[jb]);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) acc[h][jb] = mfma_bf16(qf, pf[h], acc[h][jb]);
       }
     }
   }
 
-  // combine the four waves' partial sums; lane holds out[m0 + lr][jb*16 + 4*lq + i]
+  // combine the four waves' partial sums; lane holds out[m0 + 16h + lr][jb*16 + 4*lq + i]
   __syncthreads();
-  f32x4* red = reinterpret_cast<f32x4*>(smem);      // [4][NB][64]
+  f32x4* red = reinterpret_cast<f32x4*>(smem);      // [4][NH][NB][64]
+  static_assert(4 * NH * NB * 64 * 16 <= ST * SB, "reduction scratch fits");
 #pragma unroll
-  for (int jb = 0; jb < NB; ++jb) red[(wave * NB + jb) * 64 + lane] = acc[jb];
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) red[((wave * NH + h) * NB + jb) * 64 + lane] = acc[h][jb];
   __syncthreads();
-  const int m = m0 + lr;
-  for (int jb = wave; jb < NB; jb += 4) {
-    f32x4 v = red[jb * 64 + lane];
+  for (int it = wave; it < NH * NB; it += 4) {
+    const int h = it / NB, jb = it % NB;
+    const int m = m0 + h * 16 + lr;
+    f32x4 v = red[(h * NB + jb) * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) v += red[(w * NB + jb) * 64 + lane];
+    for (int w = 1; w < 4; ++w) v += red[((w * NH + h) * NB + jb) * 64 + lane];
     if (m < p.M) {
       const int j0 = jb * 16 + 4 * lq;
       float* dst = p.out + (size_t)m * p.ldo;
@@ -761,10 +776,23 @@ static void rowstream_launch(const RowProjParams& p, dim3 grid, dim3 block, hipS
   hipLaunchKernelGGL((rowstream_kernel<RP, KS>), grid, block, 0, st, p);
 }
 
+// 32-row blocks at rank 64 (no k-scale): taken when they still give every CU a block
+// (mode 1), always (mode 2, for tests) or never (mode 0)
+int g_rowstream32 = 1;
+static bool rowstream32(const RowProjParams& p, int rp) {
+  if (rp != 64 || p.q_kscale != nullptr || g_rowstream32 == 0) return false;
+  if (p.P1 != nullptr && p.p_split % 32) return false;
+  return g_rowstream32 == 2 || (p.M + 31) / 32 >= 256;
+}
+
 hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st) {
   if (p.M <= 0) return hipSuccess;
   const int rp = p.R <= 16 ? 16 : p.R <= 32 ? 32 : p.R <= 64 ? 64 : 128;
   if (rowstream_ok(p, rp)) {
+    if (rowstream32(p, rp)) {
+      hipLaunchKernelGGL((rowstream_kernel<64, false, 32>), dim3((p.M + 31) / 32), dim3(256), 0, st, p);
+      return hipGetLastError();
+    }
     const dim3 grid((p.M + 15) / 16), block(256);
     const bool ks = p.q_kscale != nullptr;
     switch (rp) {

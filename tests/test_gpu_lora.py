@@ -169,6 +169,33 @@ def test_bf16_four_wave_tiles(M, N, K, r):
     assert torch.equal(Y4, Y4b) and torch.equal(dX4, dX4b)
 
 
+@pytest.mark.parametrize("M,N,K,r", [(300, 512, 640, 64), (129, 384, 256, 48)])
+def test_bf16_row_projection_32_row_blocks(M, N, K, r):
+    """Rank 33..64 row projections (U = X.A^T, V = dY.B with B read transposed) on 32-row
+    blocks, forced at small M: the same bits as on 16-row blocks, and against the oracle
+    (ragged last block, ragged last chunk of K)."""
+    require_gpu()
+    import lora_dora_linear_amd as L
+    c = inputs.linear_case(8, M, N, K, r, 0.5, "bf16")
+    runs = []
+    for mode in (2, 0):
+        L.set_tuning(2, mode)
+        try:
+            Y, U, g = _run(c)
+        finally:
+            L.set_tuning(2, 1)
+        runs.append((Y, U, g))
+    (Y2, U2, g2), (Y0, U0, g0) = runs
+    assert torch.equal(U2, U0) and torch.equal(Y2, Y0)
+    for k in ("dX", "dA", "dB"):
+        assert torch.equal(g2[k], g0[k]), k
+    Yr, gr, Ur = _oracle(c)
+    assert_close(host(U2), Ur, 1e-5, "U")
+    assert_close(host(Y2), Yr, BF16_TOL, "Y")
+    for k in ("dX", "dA", "dB"):
+        assert_close(host(g2[k]), gr[k], BF16_TOL, k)
+
+
 def test_bf16_deterministic():
     require_gpu()
     c = inputs.linear_case(4, 300, 512, 384, 16, 0.5, "bf16")

@@ -81,6 +81,30 @@ def test_swiglu_gate_up_routes(M, K, H, r):
     assert_close(host(saved1["H"]), osw.silu(E) * Gu, 2.0 ** -8, "H from stored E, Gu")
 
 
+def test_swiglu_row_projection_32_row_blocks():
+    """r = 32: the gate/up row projection runs rank 64 over two factor segments [Ag; Au];
+    forced onto 32-row blocks it gives the same bits as on 16-row blocks."""
+    require_gpu()
+    import lora_dora_linear_amd as L
+    c = inputs.mlp_case(9, 300, 256, 512, 32, 0.25)
+    runs = []
+    for mode in (2, 0):
+        L.set_tuning(2, mode)
+        try:
+            runs.append(_run(c))
+        finally:
+            L.set_tuning(2, 1)
+    (O2, s2, g2), (O0, s0, g0) = runs
+    assert torch.equal(O2, O0)
+    for k in s0:
+        assert torch.equal(s2[k], s0[k]), k
+    for k in g0:
+        assert torch.equal(g2[k], g0[k]), k
+    X = c.f64("X")
+    P = [c.proj(p) for p in ("gate", "up", "down")]
+    assert_close(host(O2), osw.swiglu_mlp_forward(X, *P)["O"], TOL, "Out")
+
+
 def test_swiglu_zero_adapters_is_plain_mlp():
     require_gpu()
     c = inputs.mlp_case(4, 200, 256, 384, 16, 0.25, zero_B=True)
