@@ -81,7 +81,7 @@ int ldl_version(void);
  *     256, or of 192 when 256-wide tiles would leave CUs idle), the DoRA input
  *     gradient and the SwiGLU MLP's down-projection input gradient (N a multiple
  *     of 256); 0 selects the eight-wave tile for all of them.
- *   LDL_TUNE_ROWSTREAM_32 (0/1/2, default 1): row projections of rank 33..64
+ *   LDL_TUNE_ROWSTREAM_32 (0/1/2, default 1): row projections of rank 33..128
  *     (U = X.A^T, V = dY.B and their like) on 32-row blocks that stage the rank
  *     factor once per 32 rows: 1 when those blocks still fill the 256 CUs
  *     (M >= 8161), 2 whenever the rank allows, 0 never.  Results are identical.

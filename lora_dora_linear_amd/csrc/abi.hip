@@ -134,6 +134,7 @@ struct MlpBwdWs {
   float* partDd; float* partAd; float* partBg; float* partBu; float* partAgu;
   uint32_t* pkDd; uint32_t* pkAd; uint32_t* pkBg; uint32_t* pkBu; uint32_t* pkAgu;
   int nsDd, msDd, nsAd, msAd, nsBg, msBg, nsAgu, msAgu, rp, rp2;
+  bool agu_split;                  // dAg, dAu as two rank-r jobs (2r pads to 128)
 };
 MlpBwdWs plan_mlp_bwd(Bump& b, int M, int K, int H, int r) {
   MlpBwdWs w{};
@@ -142,7 +143,10 @@ MlpBwdWs plan_mlp_bwd(Bump& b, int M, int K, int H, int r) {
   colproj_plan(M, K, &w.nsDd, &w.msDd);
   colproj_plan(M, H, &w.nsAd, &w.msAd);
   colproj_plan(M, H, &w.nsBg, &w.msBg);
-  colproj_plan(M, K, &w.nsAgu, &w.msAgu);
+  // rank 2r padded to 128 runs on the register-transposing kernel; two rank-r jobs (same
+  // partial and packed-factor sizes) run on the streamed one instead
+  w.agu_split = w.rp2 > 64;
+  colproj_plan(M, K, &w.nsAgu, &w.msAgu, w.agu_split ? 256 : 512);
   w.Vd = b.take<float>((size_t)M * r);
   w.Vgu = b.take<float>((size_t)M * 2 * r);
   w.dEGu = b.take<uint16_t>((size_t)M * 2 * H);
@@ -701,10 +705,21 @@ int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, fl
     LDL_TRY(gemm_timed(1, GK_NN_PLAIN, p, st));
   }
   // dAg, dAu = [V_g | V_u]^T.X in one pass over X
-  LDL_TRY(colproj(M, K, 2 * r, X, K, w.Vgu, 2 * r, 1.f, nullptr, 0, 0, w.nsAgu, w.msAgu, w.partAgu, nullptr, st,
-                  w.pkAgu));
-  LDL_TRY(launch_reduce2(rdp(r, K, w.partAgu, (size_t)K * w.rp2, w.nsAgu, w.rp2, true, 1.f, dAg, K),
-                         rdp(r, K, w.partAgu + r, (size_t)K * w.rp2, w.nsAgu, w.rp2, true, 1.f, dAu, K), st));
+  if (w.agu_split) {
+    float* partAu = w.partAgu + (size_t)w.nsAgu * K * w.rp;
+    LDL_TRY(launch_colproj2(
+        pk(cpp(M, K, r, X, K, w.Vgu, 2 * r, 1.f, nullptr, 0, 0, w.msAgu, w.partAgu, nullptr), w.pkAgu), w.nsAgu,
+        pk(cpp(M, K, r, X, K, w.Vgu + r, 2 * r, 1.f, nullptr, 0, 0, w.msAgu, partAu, nullptr),
+           w.pkAgu + colproj_spk_words(M, r)),
+        w.nsAgu, st));
+    LDL_TRY(launch_reduce2(rdp(r, K, w.partAgu, (size_t)K * w.rp, w.nsAgu, w.rp, true, 1.f, dAg, K),
+                           rdp(r, K, partAu, (size_t)K * w.rp, w.nsAgu, w.rp, true, 1.f, dAu, K), st));
+  } else {
+    LDL_TRY(colproj(M, K, 2 * r, X, K, w.Vgu, 2 * r, 1.f, nullptr, 0, 0, w.nsAgu, w.msAgu, w.partAgu, nullptr, st,
+                    w.pkAgu));
+    LDL_TRY(launch_reduce2(rdp(r, K, w.partAgu, (size_t)K * w.rp2, w.nsAgu, w.rp2, true, 1.f, dAg, K),
+                           rdp(r, K, w.partAgu + r, (size_t)K * w.rp2, w.nsAgu, w.rp2, true, 1.f, dAu, K), st));
+  }
   return LDL_OK;
 }
 

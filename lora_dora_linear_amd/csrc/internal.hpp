@@ -53,7 +53,7 @@ bool gemm_shape_ok(GemmKind kind, int M, int N, int K);
 
 hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st);
 int colproj_rp(int R);
-extern int g_rowstream32;   // rank-64 row projections on 32-row blocks: 0 never, 1 auto, 2 always
+extern int g_rowstream32;   // rank 33..128 row projections on 32-row blocks: 0 never, 1 auto, 2 always
 // size in 32-bit words of the packed S a column projection of M rows and rank R needs
 size_t colproj_spk_words(int M, int R);
 // split plan of a column projection over M rows and C columns, aiming at `blocks` blocks

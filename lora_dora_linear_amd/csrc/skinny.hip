@@ -137,8 +137,8 @@ __global__ __launch_bounds__(512) void rowproj_kernel(const RowProjParams p) {
 // (a [K, R] matrix, rows of R bf16) is stored as-is and read back with the
 // transposing LDS read.
 //
-// BMR = 32 (rank 64): a block takes 32 rows, two 16-row MFMA tiles that share each Q
-// fragment, so the [K, 64] (or [64, K]) rank factor is staged once per 32 rows instead of
+// BMR = 32 (rank 64 and 128): a block takes 32 rows, two 16-row MFMA tiles that share each Q
+// fragment, so the [K, RP] (or [RP, K]) rank factor is staged once per 32 rows instead of
 // per 16; every output row sees the same k-steps on the same wave in the same order as
 // with 16-row blocks (identical results).
 template <int RP, bool KS, int BMR = 16>
@@ -776,11 +776,11 @@ static void rowstream_launch(const RowProjParams& p, dim3 grid, dim3 block, hipS
   hipLaunchKernelGGL((rowstream_kernel<RP, KS>), grid, block, 0, st, p);
 }
 
-// 32-row blocks at rank 64 (no k-scale): taken when they still give every CU a block
-// (mode 1), always (mode 2, for tests) or never (mode 0)
+// 32-row blocks at rank 64 and 128 (no k-scale): taken when they still give every CU a
+// block (mode 1), always (mode 2, for tests) or never (mode 0)
 int g_rowstream32 = 1;
 static bool rowstream32(const RowProjParams& p, int rp) {
-  if (rp != 64 || p.q_kscale != nullptr || g_rowstream32 == 0) return false;
+  if ((rp != 64 && rp != 128) || p.q_kscale != nullptr || g_rowstream32 == 0) return false;
   if (p.P1 != nullptr && p.p_split % 32) return false;
   return g_rowstream32 == 2 || (p.M + 31) / 32 >= 256;
 }
@@ -790,7 +790,8 @@ hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st) {
   const int rp = p.R <= 16 ? 16 : p.R <= 32 ? 32 : p.R <= 64 ? 64 : 128;
   if (rowstream_ok(p, rp)) {
     if (rowstream32(p, rp)) {
-      hipLaunchKernelGGL((rowstream_kernel<64, false, 32>), dim3((p.M + 31) / 32), dim3(256), 0, st, p);
+      if (rp == 64) hipLaunchKernelGGL((rowstream_kernel<64, false, 32>), dim3((p.M + 31) / 32), dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((rowstream_kernel<128, false, 32>), dim3((p.M + 31) / 32), dim3(256), 0, st, p);
       return hipGetLastError();
     }
     const dim3 grid((p.M + 15) / 16), block(256);

@@ -169,9 +169,9 @@ def test_bf16_four_wave_tiles(M, N, K, r):
     assert torch.equal(Y4, Y4b) and torch.equal(dX4, dX4b)
 
 
-@pytest.mark.parametrize("M,N,K,r", [(300, 512, 640, 64), (129, 384, 256, 48)])
+@pytest.mark.parametrize("M,N,K,r", [(300, 512, 640, 64), (129, 384, 256, 48), (200, 256, 192, 128)])
 def test_bf16_row_projection_32_row_blocks(M, N, K, r):
-    """Rank 33..64 row projections (U = X.A^T, V = dY.B with B read transposed) on 32-row
+    """Rank 33..128 row projections (U = X.A^T, V = dY.B with B read transposed) on 32-row
     blocks, forced at small M: the same bits as on 16-row blocks, and against the oracle
     (ragged last block, ragged last chunk of K)."""
     require_gpu()

@@ -81,12 +81,13 @@ def test_swiglu_gate_up_routes(M, K, H, r):
     assert_close(host(saved1["H"]), osw.silu(E) * Gu, 2.0 ** -8, "H from stored E, Gu")
 
 
-def test_swiglu_row_projection_32_row_blocks():
-    """r = 32: the gate/up row projection runs rank 64 over two factor segments [Ag; Au];
-    forced onto 32-row blocks it gives the same bits as on 16-row blocks."""
+@pytest.mark.parametrize("r", [32, 64])
+def test_swiglu_row_projection_32_row_blocks(r):
+    """The gate/up row projection runs rank 2r over two factor segments [Ag; Au] (64 and
+    128 here); forced onto 32-row blocks it gives the same bits as on 16-row blocks."""
     require_gpu()
     import lora_dora_linear_amd as L
-    c = inputs.mlp_case(9, 300, 256, 512, 32, 0.25)
+    c = inputs.mlp_case(9, 300, 256, 512, r, 0.25)
     runs = []
     for mode in (2, 0):
         L.set_tuning(2, mode)
