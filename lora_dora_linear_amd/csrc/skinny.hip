@@ -474,12 +474,16 @@ __global__ __launch_bounds__(256) void colproj_kernel(const ColProjBatch batch) 
 // the fp32 tile in every block costs more than the MFMAs at rank 64 (measured: 331 us of
 // which ~180 us went to it at 8192 rows x 2 x 14336 columns).  The values fed to the MFMAs
 // are the same bits either way.
-template <int RP>
+//
+// NH = 2 (rank 64, packed S, no column sums): a block takes 128 columns as two 64-column
+// halves, each staged and read exactly as a 64-column block, sharing one S tile; 32-row
+// sub-tiles keep the ring at 48 KB.
+template <int RP, int NH = 1>
 struct ColStream {
   // rows per sub-tile: 64 from rank 32 up keeps the 3-stage ring at 48 KB, so three blocks
   // share a CU (128 rows measured 15-20 % slower at rank 32, 64 rows slower at rank 16)
-  static constexpr int MS = RP <= 16 ? 128 : 64;
-  static constexpr int XB = MS * 128;                  // X (or Z) tile: MS rows x 64 columns
+  static constexpr int MS = NH == 2 ? 32 : (RP <= 16 ? 128 : 64);
+  static constexpr int XB = MS * 128;                  // X (or Z) tile: MS rows x 64 columns (one half)
   static constexpr int SBY = MS * RP * 4;              // S tile: MS rows x up to RP fp32
   static constexpr int NSTEP = MS / 32;
   static constexpr int WPS = 4 / NSTEP;                // waves per step
@@ -488,19 +492,20 @@ struct ColStream {
   static constexpr bool PK = RP >= 32;                 // S pre-split into packed hi / lo fragments
 };
 
-template <int RP, bool HASZ>
+template <int RP, bool HASZ, int NH = 1>
 __global__ __launch_bounds__(256) void colstream_kernel(const ColProjBatch batch) {
-  using T = ColStream<RP>;
+  using T = ColStream<RP, NH>;
   constexpr bool PK = T::PK;
+  static_assert(NH == 1 || (NH == 2 && PK && !HASZ), "two halves: packed S, no Z");
   constexpr int NB = RP / 16, MS = T::MS, XB = T::XB, SBY = T::SBY, ST = T::STAGES;
-  constexpr int SB = XB * (HASZ ? 2 : 1) + SBY;        // bytes per stage
-  constexpr int NI = (XB * (HASZ ? 2 : 1) + SBY) / 4096;
+  constexpr int SB = XB * NH * (HASZ ? 2 : 1) + SBY;   // bytes per stage
+  constexpr int NI = SB / 4096;
   __shared__ __attribute__((aligned(16))) uint8_t smem[ST * SB];
   const int y = blockIdx.y;
   const int jobi = y >= batch.first[2] ? 2 : (y >= batch.first[1] ? 1 : 0);
   const ColProjParams& p = batch.job[jobi];
   const int split = y - batch.first[jobi];
-  const int c0 = blockIdx.x * 64;
+  const int c0 = blockIdx.x * 64 * NH;
   if (c0 >= p.C) return;
   const int mbeg = split * p.msplit;
   const int mend = min(p.M, mbeg + p.msplit);
@@ -520,13 +525,15 @@ __global__ __launch_bounds__(256) void colstream_kernel(const ColProjBatch batch
          : make_rsrc(p.S, p.R > 0 ? (uint32_t)mend * lds_b : 0u);
   const __amdgpu_buffer_rsrc_t rs_z = make_rsrc(p.Z, zmode ? (uint32_t)mend * ldz_b : 0u);
   constexpr int NIX = XB / 4096, NIS = SBY / 4096;
-  uint32_t x_off[NIX], s_off[NIS];
+  uint32_t x_off[NH][NIX], s_off[NIS];
 #pragma unroll
-  for (int i = 0; i < NIX; ++i) {
-    const int b = (i * 4 + wave) * 1024 + lane * 16;
-    const int row = b >> 7, phys = (b >> 4) & 7;
-    x_off[i] = (uint32_t)row * ldx_b + (uint32_t)(c0 + 8 * (phys ^ (2 * (row & 3)))) * 2u;
-  }
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int i = 0; i < NIX; ++i) {
+      const int b = (i * 4 + wave) * 1024 + lane * 16;
+      const int row = b >> 7, phys = (b >> 4) & 7;
+      x_off[h][i] = (uint32_t)row * ldx_b + (uint32_t)(c0 + 64 * h + 8 * (phys ^ (2 * (row & 3)))) * 2u;
+    }
   const int rb = p.R > 0 ? p.R * 4 : 16;               // bytes per staged S row
 #pragma unroll
   for (int i = 0; i < NIS; ++i) {
@@ -537,21 +544,24 @@ __global__ __launch_bounds__(256) void colstream_kernel(const ColProjBatch batch
     uint8_t* sb = smem + (sub % ST) * SB;
     const uint32_t m = (uint32_t)(mbeg + sub * MS);
 #pragma unroll
-    for (int i = 0; i < NIX; ++i) buf2lds16(rs_x, x_off[i], m * ldx_b, sb + (i * 4 + wave) * 1024);
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int i = 0; i < NIX; ++i) buf2lds16(rs_x, x_off[h][i], m * ldx_b, sb + h * XB + (i * 4 + wave) * 1024);
 #pragma unroll
     for (int i = 0; i < NIS; ++i)
-      buf2lds16(rs_s, s_off[i], PK ? m * (4u * RP) : m * lds_b, sb + XB + (i * 4 + wave) * 1024);
+      buf2lds16(rs_s, s_off[i], PK ? m * (4u * RP) : m * lds_b, sb + NH * XB + (i * 4 + wave) * 1024);
     if constexpr (HASZ) {
 #pragma unroll
       for (int i = 0; i < NIX; ++i)   // same element layout as X (Z has its own leading dimension)
-        buf2lds16(rs_z, x_off[i] / ldx_b * ldz_b + x_off[i] % ldx_b, m * ldz_b, sb + XB + SBY + (i * 4 + wave) * 1024);
+        buf2lds16(rs_z, x_off[0][i] / ldx_b * ldz_b + x_off[0][i] % ldx_b, m * ldz_b,
+                  sb + XB + SBY + (i * 4 + wave) * 1024);
     }
   };
 
   constexpr int CFW = T::CFW;
-  f32x4 acc[CFW][NB];                                   // this wave's column blocks my_cf0 + q
+  f32x4 acc[NH * CFW][NB];                              // this wave's column blocks: half h, my_cf0 + q
 #pragma unroll
-  for (int q = 0; q < CFW; ++q)
+  for (int q = 0; q < NH * CFW; ++q)
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb) acc[q][jb] = f32x4{0, 0, 0, 0};
   float cs[4] = {0.f, 0.f, 0.f, 0.f};
@@ -571,7 +581,7 @@ __global__ __launch_bounds__(256) void colstream_kernel(const ColProjBatch batch
     // S^T fragments (rank j = jb*16 + lr, rows mrow .. mrow+7), hi / lo bf16 parts, pre-scaled
     u32x4 shi[NB], slo[NB];
     if constexpr (PK) {
-      const uint8_t* sp = sb + XB + (my_step * 4 + lq) * (32 * RP) + lr * 16;
+      const uint8_t* sp = sb + NH * XB + (my_step * 4 + lq) * (32 * RP) + lr * 16;
 #pragma unroll
       for (int jb = 0; jb < NB; ++jb) {
         shi[jb] = *reinterpret_cast<const u32x4*>(sp + jb * 256);
@@ -596,20 +606,24 @@ __global__ __launch_bounds__(256) void colstream_kernel(const ColProjBatch batch
     }
     }
 #pragma unroll
-    for (int q = 0; q < T::CFW; ++q) {
+    for (int qq = 0; qq < NH * T::CFW; ++qq) {
+      const int q = qq % T::CFW;
       const int cf = my_cf0 + q;
-      // X^T fragment: column c0 + 16 cf + lr, rows mrow .. mrow+7 (two transposing reads)
+      const uint8_t* sx = sb + (qq / T::CFW) * XB;      // this column block's half
+      // X^T fragment: column c0 + 64 h + 16 cf + lr, rows mrow .. mrow+7 (two transposing reads)
       const int rr = my_step * 32 + 8 * lq + (lr >> 2);
       const int col = cf * 16 + 4 * (lr & 3);
       auto xoff = [&](int r) { return r * 128 + (((col >> 3) ^ (2 * (r & 3))) << 4) + ((col & 4) << 1); };
-      const u32x2 lo = lds_tr16(sb, xoff(rr)), hi = lds_tr16(sb, xoff(rr + 4));
+      const u32x2 lo = lds_tr16(sx, xoff(rr)), hi = lds_tr16(sx, xoff(rr + 4));
       const u32x4 xf = u32x4{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
       for (int jb = 0; jb < NB; ++jb) {
-        acc[q][jb] = mfma_bf16(shi[jb], xf, acc[q][jb]);
-        acc[q][jb] = mfma_bf16(slo[jb], xf, acc[q][jb]);
+        acc[qq][jb] = mfma_bf16(shi[jb], xf, acc[qq][jb]);
+        acc[qq][jb] = mfma_bf16(slo[jb], xf, acc[qq][jb]);
       }
-      if (p.colsum_mode == 2) {
+      if constexpr (NH > 1) {
+        // no column sums with two halves
+      } else if (p.colsum_mode == 2) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) cs[q] += bf16_lo(xf[t]) + bf16_hi(xf[t]);
       } else if (zmode) {
@@ -622,26 +636,27 @@ __global__ __launch_bounds__(256) void colstream_kernel(const ColProjBatch batch
     }
   }
 
-  // combine the waves: lane holds part[c = c0 + 16 cf + lr][j = jb*16 + 4*lq + i]
+  // combine the waves: lane holds part[c = c0 + 64 h + 16 cf + lr][j = jb*16 + 4*lq + i]
   __syncthreads();
-  f32x4* red = reinterpret_cast<f32x4*>(smem);          // [4 waves][CFW][NB][64]
-  static_assert(4 * CFW * NB * 64 * 16 <= ST * SB, "reduction scratch fits");
+  f32x4* red = reinterpret_cast<f32x4*>(smem);          // [4 waves][NH][CFW][NB][64]
+  static_assert(4 * NH * CFW * NB * 64 * 16 <= ST * SB, "reduction scratch fits");
 #pragma unroll
-  for (int q = 0; q < CFW; ++q)
+  for (int q = 0; q < NH * CFW; ++q)
 #pragma unroll
-    for (int jb = 0; jb < NB; ++jb) red[((wave * CFW + q) * NB + jb) * 64 + lane] = acc[q][jb];
+    for (int jb = 0; jb < NB; ++jb) red[((wave * NH * CFW + q) * NB + jb) * 64 + lane] = acc[q][jb];
   __syncthreads();
-  for (int item = wave; item < 4 * NB; item += 4) {
-    const int cf = item / NB, jb = item % NB;
+  for (int item = wave; item < NH * 4 * NB; item += 4) {
+    const int hc = item / NB, jb = item % NB;
+    const int h = hc / 4, cf = hc % 4;
     f32x4 v = f32x4{0, 0, 0, 0};
     for (int w = 0; w < 4; ++w) {                       // waves that own column block cf, in order
       const int q = cf - (w / T::NSTEP) * CFW;
-      if (q >= 0 && q < CFW) v += red[((w * CFW + q) * NB + jb) * 64 + lane];
+      if (q >= 0 && q < CFW) v += red[((w * NH * CFW + h * CFW + q) * NB + jb) * 64 + lane];
     }
-    const int c = c0 + cf * 16 + lr;
+    const int c = c0 + 64 * h + cf * 16 + lr;
     if (c < p.C) *reinterpret_cast<f32x4*>(p.part + ((size_t)split * p.C + c) * RP + jb * 16 + 4 * lq) = v;
   }
-  if (p.colsum_mode != 0) {
+  if (NH == 1 && p.colsum_mode != 0) {
     // column sums: lanes lr of the four 16-lane groups and the waves sharing a column block
     __syncthreads();
     float* csr = reinterpret_cast<float*>(smem);        // [4 waves][4 q][64 lanes]
@@ -922,6 +937,16 @@ static bool colstream_ok(const ColProjParams& p) {
 template <bool HASZ>
 static hipError_t colstream_launch(const ColProjBatch& b, int gx, int gy, int R, hipStream_t st) {
   const dim3 grid(gx, gy), block(256);
+  // rank 64 without column sums: 128-column blocks of two halves sharing each staged S tile
+  // (half the S traffic per X byte; 149 -> 108 us for dBg + dBu at 8192 x 14336)
+  if (!HASZ && colproj_rp(R) == 64) {
+    bool sums = false;
+    for (int i = 0; i < kColProjBatch; ++i) sums = sums || b.job[i].colsum_mode != 0;
+    if (!sums) {
+      hipLaunchKernelGGL((colstream_kernel<64, false, 2>), dim3((gx + 1) / 2, gy), block, 0, st, b);
+      return hipGetLastError();
+    }
+  }
   switch (colproj_rp(R)) {
     case 16: hipLaunchKernelGGL((colstream_kernel<16, HASZ>), grid, block, 0, st, b); break;
     case 32: hipLaunchKernelGGL((colstream_kernel<32, HASZ>), grid, block, 0, st, b); break;
