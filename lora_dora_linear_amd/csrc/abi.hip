@@ -141,7 +141,9 @@ MlpBwdWs plan_mlp_bwd(Bump& b, int M, int K, int H, int r) {
   w.rp = colproj_rp(r);
   w.rp2 = colproj_rp(2 * r);
   colproj_plan(M, K, &w.nsDd, &w.msDd);
-  colproj_plan(M, H, &w.nsAd, &w.msAd);
+  // dAd (H columns) shares its launch with dBd (K columns): more row splits for the wide
+  // job keep its heavy blocks from landing one or two to a CU
+  colproj_plan(M, H, &w.nsAd, &w.msAd, 1024);
   colproj_plan(M, H, &w.nsBg, &w.msBg);
   // rank 2r padded to 128 runs on the register-transposing kernel; two rank-r jobs (same
   // partial and packed-factor sizes) run on the streamed one instead
