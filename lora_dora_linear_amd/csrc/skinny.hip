@@ -475,7 +475,7 @@ __global__ __launch_bounds__(256) void colproj_kernel(const ColProjBatch batch) 
 // which ~180 us went to it at 8192 rows x 2 x 14336 columns).  The values fed to the MFMAs
 // are the same bits either way.
 //
-// NH = 2 (rank 64, packed S, no column sums): a block takes 128 columns as two 64-column
+// NH = 2 (rank 32 and 64, packed S, no column sums): a block takes 128 columns as two 64-column
 // halves, each staged and read exactly as a 64-column block, sharing one S tile; 32-row
 // sub-tiles keep the ring at 48 KB.
 template <int RP, int NH = 1>
@@ -937,13 +937,15 @@ static bool colstream_ok(const ColProjParams& p) {
 template <bool HASZ>
 static hipError_t colstream_launch(const ColProjBatch& b, int gx, int gy, int R, hipStream_t st) {
   const dim3 grid(gx, gy), block(256);
-  // rank 64 without column sums: 128-column blocks of two halves sharing each staged S tile
-  // (half the S traffic per X byte; 149 -> 108 us for dBg + dBu at 8192 x 14336)
-  if (!HASZ && colproj_rp(R) == 64) {
+  // rank 32 and 64 without column sums: 128-column blocks of two halves sharing each staged
+  // S tile (half the S traffic per X byte; 149 -> 108 us for dBg + dBu at 8192 x 14336,
+  // r 64; about 1 us per launch at r 32)
+  if (!HASZ && (colproj_rp(R) == 64 || colproj_rp(R) == 32)) {
     bool sums = false;
     for (int i = 0; i < kColProjBatch; ++i) sums = sums || b.job[i].colsum_mode != 0;
     if (!sums) {
-      hipLaunchKernelGGL((colstream_kernel<64, false, 2>), dim3((gx + 1) / 2, gy), block, 0, st, b);
+      if (colproj_rp(R) == 64) hipLaunchKernelGGL((colstream_kernel<64, false, 2>), dim3((gx + 1) / 2, gy), block, 0, st, b);
+      else hipLaunchKernelGGL((colstream_kernel<32, false, 2>), dim3((gx + 1) / 2, gy), block, 0, st, b);
       return hipGetLastError();
     }
   }
