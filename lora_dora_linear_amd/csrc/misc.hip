@@ -200,7 +200,7 @@ hipError_t launch_silu_mul(const void* E, const void* U, int M, int N, int ld, v
   if (N % 8 || ld % 8 || ld < N) return hipErrorInvalidValue;
   const size_t total = (size_t)M * (N / 8);
   size_t blocks = (total + 255) / 256;
-  if (blocks > 2048) blocks = 2048;
+  if (blocks > 8192) blocks = 8192;   // ~7 grid-stride steps a thread at 8192 x 14336 (2048 blocks: 145 -> 133 us)
   hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const uint16_t*>(E),
                      static_cast<const uint16_t*>(U), M, N, ld, static_cast<uint16_t*>(H));
   return hipGetLastError();
@@ -238,7 +238,7 @@ hipError_t launch_swiglu_bwd(void* dE, int ld_de, const void* E, int ld_e, const
     return hipErrorInvalidValue;
   const size_t total = (size_t)M * (N / 8);
   size_t blocks = (total + 255) / 256;
-  if (blocks > 2048) blocks = 2048;
+  if (blocks > 8192) blocks = 8192;   // ~7 grid-stride steps a thread at 8192 x 14336 (2048 blocks: 222 -> 213 us)
   hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<uint16_t*>(dE), ld_de,
                      static_cast<const uint16_t*>(E), ld_e, static_cast<const uint16_t*>(U), ld_u,
                      static_cast<uint16_t*>(dU), ld_du, M, N);
