@@ -475,14 +475,14 @@ __global__ __launch_bounds__(256) void colproj_kernel(const ColProjBatch batch) 
 // which ~180 us went to it at 8192 rows x 2 x 14336 columns).  The values fed to the MFMAs
 // are the same bits either way.
 //
-// NH = 2 (rank 32 and 64, packed S, no column sums): a block takes 128 columns as two 64-column
-// halves, each staged and read exactly as a 64-column block, sharing one S tile; 32-row
-// sub-tiles keep the ring at 48 KB.
+// NH = 2 (no column sums): a block takes 128 columns as two 64-column halves, each staged
+// and read exactly as a 64-column block, sharing one S tile; 32-row sub-tiles (64 at rank
+// 16, where the S tile of 32 rows would be under one 4 KB copy round) keep the ring small.
 template <int RP, int NH = 1>
 struct ColStream {
   // rows per sub-tile: 64 from rank 32 up keeps the 3-stage ring at 48 KB, so three blocks
   // share a CU (128 rows measured 15-20 % slower at rank 32, 64 rows slower at rank 16)
-  static constexpr int MS = NH == 2 ? 32 : (RP <= 16 ? 128 : 64);
+  static constexpr int MS = NH == 2 ? (RP <= 16 ? 64 : 32) : (RP <= 16 ? 128 : 64);
   static constexpr int XB = MS * 128;                  // X (or Z) tile: MS rows x 64 columns (one half)
   static constexpr int SBY = MS * RP * 4;              // S tile: MS rows x up to RP fp32
   static constexpr int NSTEP = MS / 32;
@@ -496,7 +496,7 @@ template <int RP, bool HASZ, int NH = 1>
 __global__ __launch_bounds__(256) void colstream_kernel(const ColProjBatch batch) {
   using T = ColStream<RP, NH>;
   constexpr bool PK = T::PK;
-  static_assert(NH == 1 || (NH == 2 && PK && !HASZ), "two halves: packed S, no Z");
+  static_assert(NH == 1 || (NH == 2 && !HASZ), "two halves: no Z");
   constexpr int NB = RP / 16, MS = T::MS, XB = T::XB, SBY = T::SBY, ST = T::STAGES;
   constexpr int SB = XB * NH * (HASZ ? 2 : 1) + SBY;   // bytes per stage
   constexpr int NI = SB / 4096;
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(256) void colstream_kernel(const ColProjBatch batch
     __syncthreads();                                    // sub-tile visible; sub-1's buffer free
     if (sub + ST - 1 < nsub) issue(sub + ST - 1);
     const uint8_t* sb = smem + (sub % ST) * SB;
-    const float* ss = reinterpret_cast<const float*>(sb + XB);
+    const float* ss = reinterpret_cast<const float*>(sb + NH * XB);
     const int mrow = my_step * 32 + 8 * lq;             // first of this lane's 8 rows
     // S^T fragments (rank j = jb*16 + lr, rows mrow .. mrow+7), hi / lo bf16 parts, pre-scaled
     u32x4 shi[NB], slo[NB];
@@ -937,15 +937,16 @@ static bool colstream_ok(const ColProjParams& p) {
 template <bool HASZ>
 static hipError_t colstream_launch(const ColProjBatch& b, int gx, int gy, int R, hipStream_t st) {
   const dim3 grid(gx, gy), block(256);
-  // rank 32 and 64 without column sums: 128-column blocks of two halves sharing each staged
-  // S tile (half the S traffic per X byte; 149 -> 108 us for dBg + dBu at 8192 x 14336,
-  // r 64; about 1 us per launch at r 32)
-  if (!HASZ && (colproj_rp(R) == 64 || colproj_rp(R) == 32)) {
+  // without column sums: 128-column blocks of two halves sharing each staged S tile (half
+  // the S traffic per X byte; 149 -> 108 us for dBg + dBu at 8192 x 14336, r 64; about
+  // 1 us per launch at r 32 and at r 16)
+  if (!HASZ && colproj_rp(R) <= 64) {
     bool sums = false;
     for (int i = 0; i < kColProjBatch; ++i) sums = sums || b.job[i].colsum_mode != 0;
     if (!sums) {
       if (colproj_rp(R) == 64) hipLaunchKernelGGL((colstream_kernel<64, false, 2>), dim3((gx + 1) / 2, gy), block, 0, st, b);
-      else hipLaunchKernelGGL((colstream_kernel<32, false, 2>), dim3((gx + 1) / 2, gy), block, 0, st, b);
+      else if (colproj_rp(R) == 32) hipLaunchKernelGGL((colstream_kernel<32, false, 2>), dim3((gx + 1) / 2, gy), block, 0, st, b);
+      else hipLaunchKernelGGL((colstream_kernel<16, false, 2>), dim3((gx + 1) / 2, gy), block, 0, st, b);
       return hipGetLastError();
     }
   }
