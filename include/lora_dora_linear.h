@@ -79,8 +79,11 @@ int ldl_version(void);
  *     term of rank <= 64 and M > 128 on the four-wave tile with 16x16x32 MFMAs:
  *     the LoRA forward and input gradient and the DoRA forward (N a multiple of
  *     256, or of 192 when 256-wide tiles would leave CUs idle), the DoRA input
- *     gradient and the SwiGLU MLP's down-projection input gradient (N a multiple
- *     of 256); 0 selects the eight-wave tile for all of them.
+ *     gradient and, in the SwiGLU MLP (hidden width a multiple of 256), the gate
+ *     and up products (two plain products and a streaming silu(e)*u pass instead
+ *     of the dual gate/up tile) and the down projection's input gradient (a plain
+ *     product and a streaming SwiGLU-backward pass instead of the fused
+ *     epilogue); 0 selects the eight-wave tiles and fused epilogues for all of them.
  *   LDL_TUNE_ROWSTREAM_32 (0/1/2, default 1): row projections of rank 33..128
  *     (U = X.A^T, V = dY.B and their like) on 32-row blocks that stage the rank
  *     factor once per 32 rows: 1 when those blocks still fill the 256 CUs
