@@ -85,9 +85,10 @@ struct LoraBwdWs {
 LoraBwdWs plan_lora_bwd(Bump& b, int M, int N, int K, int r, bool need_u) {
   LoraBwdWs w{};
   w.rp = colproj_rp(r);
-  // dB and dA share one launch: half the block target each
-  colproj_plan(M, N, &w.nsB, &w.msB, 256);
-  colproj_plan(M, K, &w.nsA, &w.msA, 256);
+  // dB and dA share one launch; planned for 512 blocks each against 64-column tiles, which
+  // the 128-column blocks of two halves make 256 blocks each (two per CU in all)
+  colproj_plan(M, N, &w.nsB, &w.msB, 512);
+  colproj_plan(M, K, &w.nsA, &w.msA, 512);
   w.V = b.take<float>((size_t)M * r);
   w.U = need_u ? b.take<float>((size_t)M * r) : nullptr;
   w.partB = b.take<float>((size_t)w.nsB * N * w.rp);
