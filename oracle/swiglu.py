@@ -101,3 +101,43 @@ def swiglu_mlp_backward(dO, X, gate, up, down):
 def swiglu_mlp_dx_rows(dO_rows, X_rows, gate, up, down):
     """dX for a subset of rows only: each row of dX depends on its own row of X and dO."""
     return swiglu_mlp_backward(dO_rows, X_rows, gate, up, down)["dX"]
+
+
+def swiglu_mlp_grads_sampled(dO, X, gate, up, down, h_idx, k_idx):
+    """The factor-gradient definitions of swiglu_mlp_backward restricted to chosen entries.
+
+    The activations E, Gu, H and the hidden-side gradient dH = dO.Wd' are built in full
+    (every entry below is a reduction over all tokens); the weight-shaped gradients
+    G_p are formed only for the requested rows / columns:
+      G_gate = dE^T.X, G_up = dGu^T.X ([H,K]):  rows h_idx -> dB_gate[h_idx], dB_up[h_idx];
+                                                columns k_idx -> dA_gate[:, k_idx], dA_up[:, k_idx]
+      G_down = dO^T.H ([K,H]):                  rows k_idx -> dB_down[k_idx];
+                                                columns h_idx -> dA_down[:, h_idx]
+    with dA_p = s_p.B_p^T.G_p and dB_p = s_p.G_p.A_p^T.  Used at sizes where the full
+    [H,K] products would take too long on the host.
+    """
+    dO, X = _f64(dO), _f64(X)
+    h_idx, k_idx = np.asarray(h_idx), np.asarray(k_idx)
+    Wg = adapted_weight(*gate)
+    Wu = adapted_weight(*up)
+    Wd = adapted_weight(*down)
+    E = X @ Wg.T
+    Gu = X @ Wu.T
+    H = silu(E) * Gu
+    dH = dO @ Wd
+    dE = dH * Gu * silu_grad(E)
+    dGu = dH * silu(E)
+    out = {}
+    for name, (W, A, B, s), dZ in (("gate", gate, dE), ("up", up, dGu)):
+        A, B = _f64(A), _f64(B)
+        G_rows = dZ[:, h_idx].T @ X           # [len(h_idx), K]
+        G_cols = dZ.T @ X[:, k_idx]           # [H, len(k_idx)]
+        out["dB_" + name + "_rows"] = float(s) * (G_rows @ A.T)
+        out["dA_" + name + "_cols"] = float(s) * (B.T @ G_cols)
+    W, A, B, s = down
+    A, B = _f64(A), _f64(B)
+    Gd_rows = dO[:, k_idx].T @ H              # [len(k_idx), H]
+    Gd_cols = dO.T @ H[:, h_idx]              # [K, len(h_idx)]
+    out["dB_down_rows"] = float(s) * (Gd_rows @ A.T)
+    out["dA_down_cols"] = float(s) * (B.T @ Gd_cols)
+    return out

@@ -90,3 +90,18 @@ def test_finite_differences():
                     vals.append(loss(X, pp["gate"], pp["up"], pp["down"]))
                 fd[idx] = (vals[0] - vals[1]) / (2 * h)
             np.testing.assert_allclose(gr[which + name], fd, rtol=1e-6, atol=1e-7)
+
+
+def test_sampled_factor_gradients_equal_the_full_backward():
+    M, K, H, r = 7, 6, 9, 3
+    X = _rand(70, M, K)
+    gate, up, down = _proj(71, H, K, r, 0.7), _proj(74, H, K, r, 1.3), _proj(77, K, H, r, 0.45)
+    dO = _rand(80, M, K)
+    full = swiglu.swiglu_mlp_backward(dO, X, gate, up, down)
+    h_idx, k_idx = np.array([0, 4, 8]), np.array([1, 5])
+    smp = swiglu.swiglu_mlp_grads_sampled(dO, X, gate, up, down, h_idx, k_idx)
+    for p in ("gate", "up"):
+        np.testing.assert_allclose(smp["dB_" + p + "_rows"], full["dB_" + p][h_idx], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(smp["dA_" + p + "_cols"], full["dA_" + p][:, k_idx], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(smp["dB_down_rows"], full["dB_down"][k_idx], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(smp["dA_down_cols"], full["dA_down"][:, h_idx], rtol=1e-12, atol=1e-12)

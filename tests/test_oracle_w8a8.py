@@ -102,3 +102,25 @@ def test_zero_row_gives_zero_scale():
     q, sc = w8a8.quantize_rows_int8(X)
     assert sc[0] == 0 and not q[0].any()
     assert q[1, 3] == -127
+
+
+def test_hand_worked_forward_and_backward():
+    """The dequantised base plus the low-rank update from the unquantised input, and the
+    straight-through backward, on a hand-worked example with power-of-two scales."""
+    g = json.load(open(os.path.join(GOLD, "w8a8_forward.json")))
+    e = g["expected"]
+    X, W0 = np.array(g["X"], np.float64), np.array(g["W0"], np.float64)
+    A, B = np.array(g["A"], np.float64), np.array(g["B"], np.float64)
+    bias, dY, s = np.array(g["bias"], np.float64), np.array(g["dY"], np.float64), g["s"]
+    Wq, sw = w8a8.quantize_rows_int8(W0)
+    np.testing.assert_array_equal(Wq, np.array(e["Wq"], np.int8))
+    np.testing.assert_array_equal(sw, np.array(e["sw"], np.float32))
+    f = w8a8.w8a8_forward(X, Wq, sw, A, B, s, bias)
+    np.testing.assert_array_equal(f["Xq"], np.array(e["Xq"], np.int8))
+    np.testing.assert_array_equal(f["sx"], np.array(e["sx"], np.float32))
+    np.testing.assert_array_equal(f["acc"], np.array(e["acc"], np.int64))
+    # dyadic values: the float64 result is exact
+    np.testing.assert_array_equal(f["Y"], np.array(e["Y"], np.float64))
+    b = w8a8.w8a8_backward(dY, X, Wq, sw, A, B, s)
+    for k in ("dX", "dA", "dB"):
+        np.testing.assert_array_equal(b[k], np.array(e[k], np.float64), err_msg=k)
