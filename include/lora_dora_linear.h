@@ -79,10 +79,10 @@ int ldl_version(void);
  *     term of rank <= 64 and M > 128 on the four-wave tile with 16x16x32 MFMAs:
  *     the LoRA forward and input gradient and the DoRA forward (N a multiple of
  *     256, or of 192 when 256-wide tiles would leave CUs idle), the DoRA input
- *     gradient and, in the SwiGLU MLP (hidden width a multiple of 256), the gate
- *     and up products (two plain products and a streaming silu(e)*u pass instead
- *     of the dual gate/up tile) and the down projection's input gradient (a plain
- *     product and a streaming SwiGLU-backward pass instead of the fused
+ *     gradient and, in the SwiGLU MLP, the gate/up dual tile (hidden width a
+ *     multiple of 128; the activation formed in its epilogue) and the down
+ *     projection's input gradient (hidden width a multiple of 256: a plain
+ *     product followed by a streaming SwiGLU-backward pass instead of the fused
  *     epilogue); 0 selects the eight-wave tiles and fused epilogues for all of them.
  *   LDL_TUNE_ROWSTREAM_32 (0/1/2, default 1): row projections of rank 33..128
  *     (U = X.A^T, V = dY.B and their like) on 32-row blocks that stage the rank
@@ -183,10 +183,12 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype,
 /* ------------------------------------------------------------------------ SwiGLU MLP
  * LoRA MLP with SwiGLU: e = lora(X; gate), u = lora(X; up), h = silu(e) * u,
  * out = lora(h; down) ("How Unsloth's FastLoRA Kernel ...", sections "Fused Forward
- * Pass Architecture" and "Activation Function Fusion").  bf16 only.  The activation
- * is fused into the epilogue of one GEMM that computes the gate and the up
- * projection of the same hidden units side by side (forward), and into the
- * epilogue of the down projection's input-gradient GEMM (backward).
+ * Pass Architecture" and "Activation Function Fusion").  bf16 only.  Forward: the
+ * activation is formed in the epilogue of one GEMM that computes the gate and the up
+ * projection of the same hidden units side by side, from its fp32 accumulators.
+ * Backward: the down projection's input gradient dh is either followed by one
+ * streaming pass over dh, e and u (four-wave route, hidden width a multiple of 256)
+ * or has the SwiGLU backward in its epilogue (other shapes).
  *   X [M,K]; Wg, Wu [H,K]; Ag, Au [r,K]; Bg, Bu [H,r]; Wd [K,H]; Ad [r,H]; Bd [K,r].
  *   Out [M,K].  Saved for the backward: E_save, Gu_save, H_save [M,H] (bf16) and
  *   U_save [M,3r] fp32 = [X.Ag^T | X.Au^T | H.Ad^T].  All required.

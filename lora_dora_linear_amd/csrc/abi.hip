@@ -617,8 +617,10 @@ int swiglu_lora_mlp_fwd(int M, int K, int H, int r, float s_gate, float s_up, fl
   const int r3 = 3 * r;
   // [U_g | U_u] = X.[Ag; Au]^T in one pass over X
   LDL_TRY(rowproj(M, K, 2 * r, X, K, Ag, Au, r, K, U_save, r3, 1.f, st));
-  // gate and up projections in one GEMM (each tile holds e and u of the same hidden
-  // units) with h = silu(e) * u in the epilogue
+  // gate and up projections in one GEMM (each tile holds e and u of the same hidden units
+  // side by side: the four-wave dual tile, or the eight-wave one for 128 tokens or fewer or
+  // hidden widths not a multiple of 128) with h = silu(e) * u formed from the fp32
+  // accumulators in the epilogue
   GemmParams p = gp0();
   p.M = M; p.N = H; p.K = K;
   p.a = X; p.lda = K; p.b0 = Wg; p.b1 = Wu; p.ldb = K; p.kseg = K;

@@ -49,14 +49,40 @@ bool gemm_shape_ok(GemmKind kind, int M, int N, int K) {
 
 int g_gemm_4wave = 1;
 
+static bool a16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; }
+
 // Four-wave 256x256 tile: plain products, DoRA's row-scaled NT and the SwiGLU-backward NN
 // epilogue, over a whole number of 256-column tiles with a low-rank term of rank <= 64
 // (NN: Q in one segment).
+// The low-rank term takes one k-tile of 64 rank slots; where 2 r fit in it, s.S enters as a
+// bf16 pair hi + lo (its rounding error then ~2^-17 relative instead of ~2^-9) at no extra cost.
 template <bool NN, bool DORA = false, bool SWB = false, int BN = 256>
-static hipError_t run16(const GemmParams& p, hipStream_t st) {
+static hipError_t run16(const GemmParams& p0, hipStream_t st) {
+  GemmParams p = p0;
+  p.seed_hilo = (p.r_epi > 0 && 2 * p.r_epi <= 64) ? 1 : 0;
   const int tiles = ((p.M + 255) / 256) * (p.N / BN);
-  if (p.r_epi > 0) hipLaunchKernelGGL((gemm16_kernel<NN, true, DORA, SWB, BN>), dim3(tiles), dim3(256), 0, st, p);
-  else hipLaunchKernelGGL((gemm16_kernel<NN, false, DORA, SWB, BN>), dim3(tiles), dim3(256), 0, st, p);
+  if (p.r_epi > 0) hipLaunchKernelGGL((gemm16_kernel<NN, 1, DORA, SWB, BN>), dim3(tiles), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((gemm16_kernel<NN, 0, DORA, SWB, BN>), dim3(tiles), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+// SwiGLU gate and up in one four-wave tile per 128 hidden units: Q rows = 128 gate rows then
+// the 128 up rows of the same units, e = X.Wg^T + s_g.U_g.Bg^T and u = X.Wu^T + s_u.U_u.Bu^T
+// in the two column halves, h = silu(e) u formed from the fp32 accumulators in the
+// epilogue (outputs e, u, h).  The two low-rank terms are two k-tiles in front of the loop.
+// (Measured against two plain four-wave products plus a streaming pass forming h from the
+// stored bf16 e and u, 8192 x 4096 x 14336 r = 64: the same step time, 5.41 ms, and h
+// rounded once instead of after two other roundings.)
+static bool dual16_ok(const GemmParams& p) {
+  const int r = p.e_jsplit;
+  return g_gemm_4wave && p.M > 128 && p.N % 128 == 0 && p.side == nullptr && p.r_epi == 2 * r &&
+         r > 0 && r <= 64 && r % 8 == 0 && p.ld_s % 4 == 0 && a16(p.S) && a16(p.e0) && a16(p.e1) && p.e_ldj == 1 &&
+         p.e_ldn % 8 == 0 && p.ldo % 8 == 0 && p.ldo2 % 8 == 0 && p.ldo3 % 8 == 0 && a16(p.out) && a16(p.out2) &&
+         a16(p.out3);
+}
+static hipError_t run16_dual(const GemmParams& p, hipStream_t st) {
+  const int tiles = ((p.M + 255) / 256) * (p.N / 128);
+  hipLaunchKernelGGL((gemm16_kernel<false, 2, false, false, 256, true>), dim3(tiles), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -76,7 +102,6 @@ static bool half_tiles_pay(int M, int N) {
   return 2 * t256 <= 256;
 }
 
-static bool a16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; }
 
 // The four-wave tile's low-rank loads need 16-byte aligned S rows and E rows (NN: rank
 // rows of E^T), a rank that is a multiple of 8, and one E segment.
@@ -85,28 +110,6 @@ static bool seed_ok(GemmKind kind, const GemmParams& p) {
       (p.r_epi % 8 == 0 && p.ld_s % 4 == 0 && a16(p.S) && a16(p.e0) && p.e_jsplit >= p.r_epi &&
        ((kind == GK_NN_PLAIN || kind == GK_NN_SWIGLU) ? (p.e_ldn == 1 && p.e_ldj % 8 == 0)
                                                       : (p.e_ldj == 1 && p.e_ldn % 8 == 0)));
-}
-
-// Gate and up projections as two four-wave NT products, E = X.Wg^T + s_g.U_g.Bg^T and
-// Gu = X.Wu^T + s_u.U_u.Bu^T, then H = silu(E) * Gu in one streaming pass over the two
-// stored bf16 arrays.  The dual tile holds both accumulators and writes three outputs per
-// tile, which keeps its MFMAs about 40 % busy against about 62 % for the plain four-wave
-// tile (8192 x 14336 x 4096 bf16): the extra pass, 6 bytes per hidden unit, costs less
-// than that difference.  Taken when both halves run on the four-wave tile.
-static bool split_halves(const GemmParams& p, GemmParams& g, GemmParams& u) {
-  if (!g_gemm_4wave || p.M <= 128 || p.N % 256 != 0 || p.side != nullptr) return false;
-  if (p.r_epi % 2 != 0 || p.r_epi / 2 > 64 || p.e_jsplit != p.r_epi / 2) return false;
-  if (p.ldo != p.ldo2 || p.ldo != p.ldo3 || p.ldo % 8 != 0 || !a16(p.out) || !a16(p.out2) || !a16(p.out3))
-    return false;
-  const int r = p.r_epi / 2;
-  g = p;
-  g.r_epi = r; g.e1 = p.e0; g.s_epi2 = p.s_epi;
-  g.out2 = nullptr; g.out3 = nullptr;
-  u = g;
-  u.b0 = p.b1; u.b1 = p.b1; u.e0 = p.e1; u.e1 = p.e1; u.s_epi = p.s_epi2; u.s_epi2 = p.s_epi2;
-  if (r > 0) u.S = p.S + r;
-  u.out = p.out2;
-  return seed_ok(GK_NT_PLAIN, g) && seed_ok(GK_NT_PLAIN, u);
 }
 
 // The down projection's input gradient as a plain four-wave NN product dh (bf16, written
@@ -130,15 +133,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
   if (p.M <= 0) return hipSuccess;
   const int bn = pick_bn(kind, p.N);
   const bool big = p.M > 128;
-  if (kind == GK_NT_SWIGLU_DUAL) {
-    GemmParams g, u;
-    if (split_halves(p, g, u)) {
-      hipError_t e = launch_gemm(GK_NT_PLAIN, g, st);
-      if (e == hipSuccess) e = launch_gemm(GK_NT_PLAIN, u, st);
-      if (e == hipSuccess) e = launch_silu_mul(p.out, p.out2, p.M, p.N, p.ldo, p.out3, st);
-      return e;
-    }
-  }
+  if (kind == GK_NT_SWIGLU_DUAL && dual16_ok(p)) return run16_dual(p, st);
   if (kind == GK_NN_SWIGLU) {
     GemmParams h;
     if (swb_split(p, h)) {
@@ -202,19 +197,22 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
       return run<128, 64, true, false, false, false, 0, false, EPI_RAW_I32>(p, st);
     case GK_NN_PLAIN:
       if (bn == 256 && big) return run<256, 256, false, true, false, false, 0, true, EPI_PLAIN>(p, st);
-      if (bn == 192 && big) return run<256, 192, false, true, false, false, 0, true, EPI_PLAIN>(p, st);
+      if (bn == 192) return big ? run<256, 192, false, true, false, false, 0, true, EPI_PLAIN>(p, st)
+                                : run<128, 64, false, true, false, false, 0, true, EPI_PLAIN>(p, st);
       if (bn >= 128) return big ? run<256, 128, false, true, false, false, 0, true, EPI_PLAIN>(p, st)
                                 : run<128, 128, false, true, false, false, 0, true, EPI_PLAIN>(p, st);
       return run<128, 64, false, true, false, false, 0, true, EPI_PLAIN>(p, st);
     case GK_NN_SCALE:
       if (bn == 256 && big) return run<256, 256, false, true, false, true, 0, true, EPI_PLAIN>(p, st);
-      if (bn == 192 && big) return run<256, 192, false, true, false, true, 0, true, EPI_PLAIN>(p, st);
+      if (bn == 192) return big ? run<256, 192, false, true, false, true, 0, true, EPI_PLAIN>(p, st)
+                                : run<128, 64, false, true, false, true, 0, true, EPI_PLAIN>(p, st);
       if (bn >= 128) return big ? run<256, 128, false, true, false, true, 0, true, EPI_PLAIN>(p, st)
                                 : run<128, 128, false, true, false, true, 0, true, EPI_PLAIN>(p, st);
       return run<128, 64, false, true, false, true, 0, true, EPI_PLAIN>(p, st);
     case GK_NN_I8_SCALE:
       if (bn == 256 && big && !half_tiles_pay(p.M, p.N)) return run<256, 256, false, true, true, true, 0, true, EPI_PLAIN>(p, st);
-      if (bn == 192 && big) return run<256, 192, false, true, true, true, 0, true, EPI_PLAIN>(p, st);
+      if (bn == 192) return big ? run<256, 192, false, true, true, true, 0, true, EPI_PLAIN>(p, st)
+                                : run<128, 64, false, true, true, true, 0, true, EPI_PLAIN>(p, st);
       if (bn >= 128) return big ? run<256, 128, false, true, true, true, 0, true, EPI_PLAIN>(p, st)
                                 : run<128, 128, false, true, true, true, 0, true, EPI_PLAIN>(p, st);
       return run<128, 64, false, true, true, true, 0, true, EPI_PLAIN>(p, st);

@@ -11,9 +11,9 @@
 // of the current step's MFMAs, and the stage copies (16 per wave) over the whole
 // hand-over step.  The two stage buffers are separate arrays and the loop is
 // unrolled by two, so the compiler sees which buffer a copy writes and which a
-// read reads and inserts no waits between them.  The low-rank term enters as one
-// more k-tile at the front: s.S (rounded to bf16, as the eight-wave seed does) and E
-// are written into the second stage buffer in the stage layout and multiplied by the
+// read reads and inserts no waits between them.  The low-rank term enters as one or
+// two more k-tiles at the front: s.S (as a bf16 pair hi + lo where the rank slots allow)
+// and E are written into the stage buffers in the stage layout and multiplied by the
 // loop itself.  Every MFMA sits in the one loop body: MFMAs before the loop made the
 // register allocator shuffle accumulators through VGPRs inside it.
 #pragma once
@@ -35,18 +35,27 @@ __device__ __forceinline__ int g16_off(int row, int chunk) { return row * 128 + 
 constexpr int kG16NNRow = 512, kG16NNPad = 128;
 __host__ __device__ constexpr int g16_nn_row(int k) { return k * kG16NNRow + (k >> 3) * kG16NNPad; }
 
-// NN: Q is [K, N] (else [N, K]); LR: with a low-rank term (r_epi in 8, 16, .., 64);
+// NN: Q is [K, N] (else [N, K]); LR: number of low-rank k-tiles in front of the loop (0: no
+// low-rank term; 1: rank r_epi <= 64 of one segment; 2: the dual tile's gate and up terms);
 // DORA (NT only): two outputs, out2 = z (the unscaled sum) and out = z * col_scale[n] + bias[n];
 // SWB (NN only): the SwiGLU backward of the product dh with e = aux0, u = aux1:
 // out = dh u sigma(e) (1 + e (1 - sigma(e))) (de) and out2 = dh e sigma(e) (du)
 // BN_: tile width, 256, or 192 for NT (3072 columns at 4096 rows then make 256 tiles, one full
 // round of the 256 CUs, where 256-column tiles leave a quarter of the chip idle)
-template <bool NN, bool LR, bool DORA = false, bool SWB = false, int BN_ = 256>
+// SWF (NT only, the SwiGLU forward): each tile covers 128 hidden units; its Q rows are the 128
+// gate rows (b0) then the 128 up rows (b1) of those units, so the waves with wn = 0 hold
+// e and the waves with wn = 1 hold u of the same (token, unit) in the same lanes.  Outputs:
+// out = e, out2 = u, out3 = h = silu(e) u, all from the fp32 accumulators (e is handed to
+// the u waves through LDS).
+template <bool NN, int LR, bool DORA = false, bool SWB = false, int BN_ = 256, bool SWF = false>
 __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   static_assert(BN_ == 256 || (!NN && BN_ == 192), "tile widths: 256, or 192 for NT");
   static_assert(!(NN && DORA), "the row-scaled epilogue is a forward (NT) epilogue");
   static_assert(!SWB || (NN && !DORA), "the SwiGLU backward epilogue is an NN epilogue");
+  static_assert(!SWF || (!NN && !DORA && !SWB && BN_ == 256 && LR != 1), "the dual tile is a plain 256-wide NT tile");
+  static_assert(LR >= 0 && LR <= 2 && (LR != 2 || SWF), "two low-rank k-tiles: the dual tile's two segments");
   constexpr int BM = 256, BN = BN_, NW = 4;
+  constexpr int TNO = SWF ? 128 : BN;               // output columns (hidden units) per tile
   constexpr int FN = BN / 32;                       // 16-column fragments per wave (wave tile BN / 2)
   constexpr int QB = NN ? g16_nn_row(64) : BN * 128;
   constexpr int SB = BM * 128 + QB;                 // one stage: P tile then Q tile
@@ -54,7 +63,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem1[SB];
 
   const int M = p.M, N = p.N, K = p.K;
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = N / TNO;
   // XCD-contiguous tile ranges, walked in groups of 4 row-tiles (as gemm_kernel)
   int bid = blockIdx.x;
   const int nblk = gridDim.x;
@@ -64,7 +73,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   const int first_m = group * GM;
   const int gm = min(GM, tiles_m - first_m);
   const int in_g = bid - group * GM * tiles_n;
-  const int m0 = (first_m + in_g % gm) * BM, n0 = (in_g / gm) * BN;
+  const int m0 = (first_m + in_g % gm) * BM, n0 = (in_g / gm) * TNO;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -74,6 +83,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
 
   const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(p.a, (uint32_t)M * lda_b);
   const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(p.b0, (uint32_t)(NN ? K : N) * ldb_b);
+  const __amdgpu_buffer_rsrc_t rs_b1 = SWF ? make_rsrc(p.b1, (uint32_t)N * ldb_b) : rs_b;   // dual: up rows
   const __amdgpu_buffer_rsrc_t rs_none = make_rsrc(p.a, 0u);    // copies that read nothing
 
   // Copies: 8 instructions per tile per wave, 1 KB each; rows past M read as zero.  Copy i
@@ -104,11 +114,17 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   auto copy_stage = [&](int kt, uint8_t* sb) {
     const bool valid = kt < K / 64;
     const __amdgpu_buffer_rsrc_t ra = valid ? rs_a : rs_none, rb = valid ? rs_b : rs_none;
+    const __amdgpu_buffer_rsrc_t rb1 = valid ? rs_b1 : rs_none;
     const uint32_t ka = (uint32_t)kt * 128u, kb = NN ? (uint32_t)kt * 64u * ldb_b : (uint32_t)kt * 128u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) copy(ra, a_off[NN ? i : 0], ka + i * a_step, sb + (i * NW + wave) * 1024);
 #pragma unroll
-    for (int i = 0; i < (NN ? 8 : FN); ++i) copy(rb, b_off[NN ? i : 0], kb + i * b_step, sb + q_dst(i));
+    for (int i = 0; i < (NN ? 8 : FN); ++i) {
+      if constexpr (SWF)    // Q rows 0..127 gate rows n0.., rows 128..255 up rows n0..
+        copy(i < FN / 2 ? rb : rb1, b_off[0], kb + (i & (FN / 2 - 1)) * b_step, sb + q_dst(i));
+      else
+        copy(rb, b_off[NN ? i : 0], kb + i * b_step, sb + q_dst(i));
+    }
   };
 
   f32x4 acc[8][FN];
@@ -175,58 +191,103 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   const int KT = K / 64;
   u32x4 fa0[8], fb0[FN], fa1[8], fb1[FN];
 
-  // The low-rank term is one more k-tile, "stage -1" in the second stage buffer: its P
-  // tile holds s.S[m0 + t][0..63] as bf16 and its Q tile E's 64 ranks in the layout of a
-  // regular Q stage (zero past r_epi and past M), so the k-loop multiplies it with its own
-  // code and no MFMA runs before the loop.  Its loads go out first, all at once,
-  // branch-free and as 16-byte vectors (indices clamped into range, values zeroed after
-  // the load): thread t loads row t of S and, for NT, row t of E ([N, r]); for NN the E
-  // tile is the rank rows of E^T ([r, N], E[n][j] at n + j e_ldj), 32 16-byte chunks each.
-  // The caller guarantees 16-byte aligned S rows and E rows (or rank rows), r_epi a
-  // multiple of 8 and at most 64, and a single E segment (e_jsplit >= r_epi).
-  f32x4 sv[LR ? 16 : 1];
-  u32x4 ev[LR ? 8 : 1];
-  if constexpr (LR) {
-    const float* srow = p.S + (size_t)min(m0 + tid, M - 1) * p.ld_s;
+  // The low-rank term enters as LR more k-tiles in front ("stages" -LR .. -1, in the stage
+  // buffers they would use): their P tile holds s.S[m0 + t][..] as bf16 and their Q tile E in
+  // the layout of a regular Q stage, so the k-loop multiplies them with its own code and no
+  // MFMA runs before the loop.  Their loads go out first, all at once, branch-free and as
+  // 16-byte vectors (indices clamped into range, values zeroed after the load): thread t loads
+  // row t of S and, for NT, row t of E ([N, r]); for NN the E tile is the rank rows of E^T
+  // ([r, N], E[n][j] at n + j e_ldj), 32 16-byte chunks each.
+  //   One segment (LR = 1): rank slots are chunks of 8; with p.seed_hilo (2 r_epi <= 64)
+  // chunks [0, r/8) hold the bf16 rounding hi of s.S and chunks [r/8, r/4) the rounding of
+  // the remainder s.S - hi, both against the same E ranks, so the low-rank term keeps ~16
+  // bits of s.S; otherwise chunks [0, r/8) hold hi only.
+  //   Dual tile (LR = 2): k-tile -2 carries the gate term (s_epi.S[.., 0 .. r) against Bg on
+  // Q rows 0..127, zero on the up rows) and k-tile -1 the up term (s_epi2.S[.., r .. 2r)
+  // against Bu on rows 128..255), r = e_jsplit <= 64, bf16 hi only.
+  // The caller guarantees 16-byte aligned S rows and E rows (or rank rows), ranks that are
+  // multiples of 8, and (LR = 1) a single E segment (e_jsplit >= r_epi).
+  const uint16_t* e0 = static_cast<const uint16_t*>(p.e0);
+  const bool live = m0 + tid < M;
+  const float* srow = p.S + (size_t)min(m0 + tid, M - 1) * p.ld_s;
+  auto pack8 = [](f32x4 a, f32x4 b, float sc, bool lo) {
+    const float x[8] = {a[0] * sc, a[1] * sc, a[2] * sc, a[3] * sc, b[0] * sc, b[1] * sc, b[2] * sc, b[3] * sc};
+    u32x4 v;
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
-      sv[q] = (4 * q < p.r_epi) ? *reinterpret_cast<const f32x4*>(srow + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint16_t* e0 = static_cast<const uint16_t*>(p.e0);
+    for (int q = 0; q < 4; ++q) {
+      uint32_t h0 = f32_to_bf16_bits(x[2 * q]), h1 = f32_to_bf16_bits(x[2 * q + 1]);
+      if (lo) {
+        h0 = f32_to_bf16_bits(x[2 * q] - __uint_as_float(h0 << 16));
+        h1 = f32_to_bf16_bits(x[2 * q + 1] - __uint_as_float(h1 << 16));
+      }
+      v[q] = h0 | (h1 << 16);
+    }
+    return v;
+  };
+  if constexpr (LR == 1) {
+    const int cps = p.r_epi >> 3;                     // chunks per part
+    const int nparts = p.seed_hilo ? 2 : 1;
+    f32x4 sa[8], sb[8];
+    u32x4 ev[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      if constexpr (NN) {       // rank row j = 8 c + t / 32, 16-byte chunk t % 32 of its 256 columns
-        const int j = 8 * c + (tid >> 5);
-        ev[c] = *reinterpret_cast<const u32x4*>(e0 + (size_t)min(j, p.r_epi - 1) * p.e_ldj + n0 + 8 * (tid & 31));
-        if (j >= p.r_epi) ev[c] = u32x4{0u, 0u, 0u, 0u};
-      } else {                  // ranks 8 c .. 8 c + 7 of row n0 + t (t < BN)
-        ev[c] = (8 * c < p.r_epi && (BN == 256 || tid < BN))
-                    ? *reinterpret_cast<const u32x4*>(e0 + (size_t)(n0 + tid) * p.e_ldn + 8 * c)
-                    : u32x4{0u, 0u, 0u, 0u};
+      const int part = c / cps, j0 = 8 * (c - part * cps);
+      const int jl = part < nparts ? j0 : 0;           // clamped rank offset
+      sa[c] = *reinterpret_cast<const f32x4*>(srow + jl);
+      sb[c] = *reinterpret_cast<const f32x4*>(srow + jl + 4);
+      if constexpr (NN) {       // rank row jl + t / 32, 16-byte chunk t % 32 of its 256 columns
+        ev[c] = *reinterpret_cast<const u32x4*>(e0 + (size_t)(jl + (tid >> 5)) * p.e_ldj + n0 + 8 * (tid & 31));
+      } else {                  // ranks jl .. jl + 7 of row n0 + t (t < BN)
+        const int n = (BN == 256 || tid < BN) ? n0 + tid : n0;
+        ev[c] = *reinterpret_cast<const u32x4*>(e0 + (size_t)n * p.e_ldn + jl);
       }
     }
-  }
-  copy_stage(0, smem0);
-  if constexpr (LR) {
-    const float sc = (m0 + tid < M) ? p.s_epi : 0.f;
+    copy_stage(0, smem0);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      u32x4 v;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 s4 = sv[2 * c + (q >> 1)];
-        v[q] = pack_bf16x2(s4[2 * (q & 1)] * sc, s4[2 * (q & 1) + 1] * sc);
-      }
-      lds_st16(smem1, g16_off(tid, c), v);
+      const int part = c / cps;
+      const bool on = part < nparts;
+      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+      lds_st16(smem1, g16_off(tid, c), on ? pack8(sa[c], sb[c], live ? p.s_epi : 0.f, part == 1) : z);
       if constexpr (NN) {
         const int j = 8 * c + (tid >> 5), ch = tid & 31;
-        lds_st16(smem1, BM * 128 + g16_nn_row(j) + ((ch ^ (2 * (j & 3))) << 4), ev[c]);
+        lds_st16(smem1, BM * 128 + g16_nn_row(j) + ((ch ^ (2 * (j & 3))) << 4), on ? ev[c] : z);
       } else if (BN == 256 || tid < BN) {
-        lds_st16(smem1, BM * 128 + g16_off(tid, c), ev[c]);
+        lds_st16(smem1, BM * 128 + g16_off(tid, c), on ? ev[c] : z);
       }
     }
     __syncthreads();
     ldf(smem1, 0, fa0, fb0);
+  } else if constexpr (LR == 2) {
+    const int rs = p.e_jsplit;                        // rank of each segment
+    const int own = tid >> 7;                         // segment of this thread's Q row (wave-uniform)
+    const uint16_t* erow = (own ? static_cast<const uint16_t*>(p.e1) : e0) + (size_t)(n0 + (tid & 127)) * p.e_ldn;
+    // one segment at a time (the loads of both at once do not fit the registers)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      f32x4 sa[8], sb[8];
+      u32x4 ev[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int jl = 8 * c < rs ? 8 * c : 0;
+        sa[c] = *reinterpret_cast<const f32x4*>(srow + g * rs + jl);
+        sb[c] = *reinterpret_cast<const f32x4*>(srow + g * rs + jl + 4);
+        if (own == g) ev[c] = *reinterpret_cast<const u32x4*>(erow + jl);
+      }
+      uint8_t* buf = g ? smem1 : smem0;
+      const float sc = live ? (g ? p.s_epi2 : p.s_epi) : 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const bool on = 8 * c < rs;
+        const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+        lds_st16(buf, g16_off(tid, c), on ? pack8(sa[c], sb[c], sc, false) : z);
+        lds_st16(buf, BM * 128 + g16_off(tid, c), (on && own == g) ? ev[c] : z);
+      }
+    }
+    __syncthreads();
+    ldf(smem0, 0, fa0, fb0);
   } else {
+    copy_stage(0, smem0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     copy_stage(1, smem1);
@@ -289,8 +350,8 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   // One loop body for every k-tile (from the low-rank tile -1 when there is one), so the
   // accumulators keep their registers to the end: an odd count runs one more tile, whose
   // stage the empty copies filled with zeros.
-  constexpr int P0 = LR ? 1 : 0;
-  for (int kt = LR ? -1 : 0; kt < KT; kt += 2) {
+  constexpr int P0 = LR & 1;
+  for (int kt = -LR; kt < KT; kt += 2) {
     tile(std::integral_constant<int, P0>{}, kt);
     tile(std::integral_constant<int, 1 - P0>{}, kt + 1);
   }
@@ -393,6 +454,80 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
     emit_swb(std::integral_constant<int, 0>{}, p.out, p.ldo);
     __syncthreads();
     emit_swb(std::integral_constant<int, 1>{}, p.out2, p.ldo2);
+  } else if constexpr (SWF) {
+    // Dual tile: waves wn = 0 hold e, waves wn = 1 hold u of the same (token, unit) in the
+    // same lanes.  Pass 1 stages both as bf16 (e in staging columns 0..127, u in 128..255)
+    // and writes them to out (e) and out2 (u).  Pass 2 hands the fp32 e to the u waves
+    // through LDS (lane-linear: each lane writes and reads 16 contiguous bytes per block),
+    // which form h = silu(e) u and stage it; it is then written to out3.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = wm * 128 + i * 16 + l16;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const f32x4 v = acc[i][j];
+        u32x2 w;
+        w[0] = pack_bf16x2(v[0], v[1]);
+        w[1] = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<u32x2*>(st_ptr(r, wn * 128 + j * 16 + 4 * lq)) = w;
+      }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < BM * 32; idx += 256) {
+      const int r = idx >> 5, c = idx & 31;
+      if (m0 + r < M) {
+        const uint8_t* base = r < 128 ? smem0 : smem1;
+        const int rr = r & 127;
+        uint16_t* dst = c < 16 ? static_cast<uint16_t*>(p.out) + (size_t)(m0 + r) * p.ldo
+                               : static_cast<uint16_t*>(p.out2) + (size_t)(m0 + r) * p.ldo2;
+        st16(dst + n0 + 8 * (c & 15), lds_ld16(base, rr * SROW + ((c ^ (rr & SWZM)) << 4)));
+      }
+    }
+    __syncthreads();
+    // pass 2, in quarters of each wave's rows (i = 2q, 2q + 1): every wave writes those fp32
+    // accumulators to smem0 (lane-linear, 16 KB per wave); then wave (wm, wn) reads e (from
+    // wave (wm, 0)) and u (from wave (wm, 1)) of the column blocks j = 4 wn .. 4 wn + 3, forms
+    // h and stages it as bf16 in smem1 ([256 rows][128 units], 256-byte rows, 16-byte chunk c
+    // of row r at c ^ (r & 15)).  The accumulators are only read, by every wave alike.
+    auto xoff = [&](int w, int i, int j) { return (((w * 2 + i) * 8 + j) * 64 + lane) * 16; };
+    auto h_ptr = [&](int r, int col) -> uint8_t* {
+      return smem1 + r * 256 + ((((col >> 3) ^ (r & 15))) << 4) + ((col & 4) << 1);
+    };
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          // through a VGPR copy: a store straight from the accumulator registers changed how
+          // the k-loop's accumulators were allocated (moves inside the loop)
+          f32x4 v = acc[2 * q + i][j];
+          asm volatile("" : "+v"(v));
+          *reinterpret_cast<f32x4*>(smem0 + xoff(wave, i, j)) = v;
+        }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 128 + (2 * q + i) * 16 + l16;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = 4 * wn + jj;
+          const f32x4 e = *reinterpret_cast<const f32x4*>(smem0 + xoff(2 * wm, i, j));
+          const f32x4 u = *reinterpret_cast<const f32x4*>(smem0 + xoff(2 * wm + 1, i, j));
+          u32x2 w;
+          w[0] = pack_bf16x2(silu_f(e[0]) * u[0], silu_f(e[1]) * u[1]);
+          w[1] = pack_bf16x2(silu_f(e[2]) * u[2], silu_f(e[3]) * u[3]);
+          *reinterpret_cast<u32x2*>(h_ptr(r, j * 16 + 4 * lq)) = w;
+        }
+      }
+      __syncthreads();
+    }
+    for (int idx = tid; idx < BM * 16; idx += 256) {
+      const int r = idx >> 4, c = idx & 15;
+      if (m0 + r < M)
+        st16(static_cast<uint16_t*>(p.out3) + (size_t)(m0 + r) * p.ldo3 + n0 + 8 * c,
+             lds_ld16(smem1, r * 256 + ((c ^ (r & 15)) << 4)));
+    }
   } else {
     // (written out rather than through emit: the lambda changed the register allocation of
     // the NN k-loop and cost ~10 % there)

@@ -62,6 +62,7 @@ struct GemmParams {
   const void* aux0; int ld_aux0;
   const void* aux1; int ld_aux1;
   float* side_save; int ld_side_save;
+  int seed_hilo;                     // four-wave tile: low-rank term as bf16 hi + lo (set by the launcher)
 };
 
 template <int BM_, int BN_, bool I8_, bool NN_, bool BINT8_, bool ASCALE_, int SIDE_RSP_, bool SLOAD_, int EPI_,

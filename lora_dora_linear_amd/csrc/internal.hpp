@@ -75,8 +75,6 @@ hipError_t launch_dora_norm(int N, int r, float s, float eps, const float* w0_su
                             const float* G, const uint16_t* B, const float* m, float* norm, float* g, hipStream_t st);
 hipError_t launch_scale_cols(const void* in, int M, int N, int ld, const float* g, void* out, hipStream_t st);
 
-// SwiGLU helper: h = silu(e) * u over bf16 [M, N] arrays with row stride ld
-hipError_t launch_silu_mul(const void* E, const void* U, int M, int N, int ld, void* H, hipStream_t st);
 // SwiGLU backward over bf16 [M, N] arrays: dh (read from dE) -> de in place, du written
 hipError_t launch_swiglu_bwd(void* dE, int ld_de, const void* E, int ld_e, const void* U, int ld_u, void* dU,
                              int ld_du, int M, int N, hipStream_t st);

@@ -16,8 +16,9 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // ============================================================================ DoRA
-// w0_sumsq[n] = sum_k W0[n,k]^2 : one wave per row ("a cached rowsum(W0^2) constant",
-// "LoRA/DoRA fast forward: no weight materialization", commit message).
+// w0_sumsq[n] = sum_k W0[n,k]^2 : one wave per row.  The squared row norm of the frozen base
+// weight is kept from call to call; only the two rank-sized terms of the norm change per step
+// ("LoRA/DoRA fast forward: no weight materialization", commit message).
 template <bool BF16>
 __global__ __launch_bounds__(256) void rowsumsq_kernel(const void* W0, int N, int K, float* out) {
   const int lane = threadIdx.x & 63;
@@ -174,35 +175,6 @@ hipError_t launch_scale_cols(const void* in, int M, int N, int ld, const float* 
   if (blocks > 2048) blocks = 2048;
   hipLaunchKernelGGL(scale_cols_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const uint16_t*>(in), M,
                      N, ld, g, static_cast<uint16_t*>(out));
-  return hipGetLastError();
-}
-
-// h[m, n] = bf16(silu(e[m, n]) * u[m, n]) (round to nearest even) from the stored bf16 gate
-// and up products: the SwiGLU activation when those come from two separate GEMMs.  The
-// products are taken from the same bf16 values the backward reads.  8 columns per thread.
-__global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* E, const uint16_t* U, int M, int N, int ld,
-                                                       uint16_t* H) {
-  const unsigned per_row = (unsigned)N / 8u;
-  const size_t total = (size_t)M * per_row;
-  for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (size_t)gridDim.x * blockDim.x) {
-    const size_t m = t / per_row, c = (t % per_row) * 8;
-    const size_t o = m * (size_t)ld + c;
-    const u32x4 e = ld16(E + o), u = ld16(U + o);
-    u32x4 h;
-    for (int i = 0; i < 4; ++i)
-      h[i] = pack_bf16x2(silu_f(bf16_lo(e[i])) * bf16_lo(u[i]), silu_f(bf16_hi(e[i])) * bf16_hi(u[i]));
-    st16(H + o, h);
-  }
-}
-
-hipError_t launch_silu_mul(const void* E, const void* U, int M, int N, int ld, void* H, hipStream_t st) {
-  if (M <= 0 || N <= 0) return hipSuccess;
-  if (N % 8 || ld % 8 || ld < N) return hipErrorInvalidValue;
-  const size_t total = (size_t)M * (N / 8);
-  size_t blocks = (total + 255) / 256;
-  if (blocks > 8192) blocks = 8192;   // ~7 grid-stride steps a thread at 8192 x 14336 (2048 blocks: 145 -> 133 us)
-  hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const uint16_t*>(E),
-                     static_cast<const uint16_t*>(U), M, N, ld, static_cast<uint16_t*>(H));
   return hipGetLastError();
 }
 

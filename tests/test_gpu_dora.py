@@ -87,3 +87,78 @@ def test_dora_full_size_3072():
     assert_close(host(state[:3072]), f["nu"], 1e-5, "norm")
     for k in ("dX", "dA", "dB", "dm"):
         assert_close(host(g[k]), gr[k], TOL, k)
+
+
+@pytest.mark.parametrize("M,N,K,r", [(64, 384, 256, 32), (100, 256, 192, 16)])
+def test_dora_small_batch_tiles(M, N, K, r):
+    """At most 128 tokens: the 128-row tiles of the row-scaled forward and of the input gradient."""
+    require_gpu()
+    eps = 1e-12
+    c = inputs.linear_case(13, M, N, K, r, 0.5, "bf16", with_bias=True, dora=True)
+    Y, Z, state, g, _ = _run(c, eps, with_bias=True, need_dbias=True)
+    f, gr = _oracle(c, eps, with_bias=True)
+    assert_close(host(Y), f["Y"], TOL, "Y")
+    assert_close(host(Z), f["Z"], TOL, "Z")
+    for k in ("dX", "dA", "dB", "dm"):
+        assert_close(host(g[k]), gr[k], TOL, k)
+    assert_close(host(g["dbias"]), gr["db"], 1e-5, "dbias")
+
+
+def test_dora_zero_row_eps_clamp():
+    """A row of W' that is exactly zero (W0 and B rows zero): the closed-form norm is 0, the
+    clamp max(nu, eps) gives g = m / eps and no gradient flows through the norm there."""
+    require_gpu()
+    eps = 1e-12
+    c = inputs.linear_case(14, 200, 256, 192, 16, 0.75, "bf16", dora=True)
+    c.t["W0"][5] = 0
+    c.t["B"][5] = 0
+    c.t["m"][5] = np.float32(0.75)
+    Y, Z, state, g, _ = _run(c, eps)
+    f, gr = _oracle(c, eps)
+    N = c.N
+    nu, gg = host(state[:N]), host(state[N:2 * N])
+    assert nu[5] == 0.0
+    assert_close(gg, f["g"], 1e-5, "g")
+    assert abs(gg[5] - 0.75 / eps) <= 1e-6 * (0.75 / eps)
+    assert_close(host(Y), f["Y"], TOL, "Y")
+    for k in ("dX", "dA", "dB", "dm"):
+        got = host(g[k])
+        assert np.all(np.isfinite(got)), k
+        assert_close(got, gr[k], TOL, k)
+
+
+def test_dora_zero_strength():
+    """s = 0: the formula with g = m / ||W0_n|| (no short-circuit); the factor gradients vanish."""
+    require_gpu()
+    eps = 1e-12
+    c = inputs.linear_case(15, 300, 384, 256, 32, 0.0, "bf16", dora=True)
+    Y, Z, state, g, _ = _run(c, eps)
+    f, gr = _oracle(c, eps)
+    W0 = c.f64("W0")
+    assert_close(host(state[c.N:2 * c.N]), c.t["m"] / np.sqrt(np.sum(W0 * W0, axis=1)), 1e-5, "g")
+    assert_close(host(Y), f["Y"], TOL, "Y")
+    assert_close(host(g["dX"]), gr["dX"], TOL, "dX")
+    assert_close(host(g["dm"]), gr["dm"], TOL, "dm")
+    assert not torch.any(g["dA"]) and not torch.any(g["dB"])
+
+
+@pytest.mark.parametrize("M,N,K,r", [(300, 384, 256, 32), (4096, 3072, 3072, 32)])
+def test_dora_without_input_gradient(M, N, K, r):
+    """dX not requested: V = (dY.diag(g)).B is projected with g applied to B's rows on load
+    (the k-scaled row projection); dA, dB, dm against the oracle and against the dX route."""
+    require_gpu()
+    import lora_dora_linear_amd as L
+    eps = 1e-12
+    c = inputs.linear_case(16, M, N, K, r, 1.0, "bf16", dora=True)
+    X, W0, A, B, dY = (dev(c.t[k], "bf16") for k in ("X", "W0", "A", "B", "dY"))
+    m = dev(c.t["m"], "f32")
+    c0 = L.dora_prepare(W0)
+    Y, U, Z, state = L.dora_linear_fwd(X, W0, A, B, m, c0, c.s, eps)
+    g0 = L.dora_linear_bwd(dY, X, W0, A, B, m, U, Z, state, c.s, eps, need_dx=False)
+    g1 = L.dora_linear_bwd(dY, X, W0, A, B, m, U, Z, state, c.s, eps, need_dx=True)
+    torch.cuda.synchronize()
+    assert g0["dX"] is None
+    _, gr = _oracle(c, eps)
+    for k in ("dA", "dB", "dm"):
+        assert_close(host(g0[k]), gr[k], TOL, k)
+        assert_close(host(g0[k]), host(g1[k]), TOL, k + " vs dX route")

@@ -89,6 +89,29 @@ def test_bf16_pure_low_rank_path():
     assert_close(host(g["dX"]), gr["dX"], BF16_TOL, "dX")
 
 
+def _excess_over_rounding(gpu_bf16, ref):
+    """max over elements of (|gpu - ref| - half a bf16 unit in the last place of ref), at least
+    0, divided by max|ref|: the error left once the output's own rounding is allowed for."""
+    g = host(gpu_bf16)
+    ref = np.asarray(ref, np.float64)
+    half_ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-300))) - 8)
+    return float(np.max(np.maximum(np.abs(g - ref) - half_ulp, 0.0)) / np.max(np.abs(ref)))
+
+
+def test_bf16_low_rank_term_keeps_precision():
+    """W0 = 0 on the four-wave tiles (rank 16): the low-rank term enters the MFMAs as the bf16
+    pair hi + lo of s.U (resp. s.V), so beyond the output's own rounding Y and dX carry only
+    fp32-level error (~1e-6 of max|ref|).  A single bf16 rounding of s.U would leave ~1e-3."""
+    require_gpu()
+    c = inputs.linear_case(19, 300, 512, 512, 16, 0.5, "bf16", zero_W0=True)
+    Y, U, g = _run(c)
+    Yr, gr, _ = _oracle(c)
+    for name, got, ref in (("Y", Y, Yr), ("dX", g["dX"], gr["dX"])):
+        e = _excess_over_rounding(got, ref)
+        print(f"{name}: error beyond the bf16 rounding = {e:.2e} of max|ref|")
+        assert e < 2e-5, (name, e)
+
+
 def test_bf16_zero_delta_bitwise():
     """s = 0 and B = 0 give bit-identical outputs, equal to X.W0^T within tolerance."""
     require_gpu()
@@ -235,3 +258,50 @@ def test_full_size_4096_sampled():
     smp = olora.lora_weight_grads_sampled(dY, X, A, B, c.s, ncols, kcols)
     assert_close(host(g["dB"][ncols]), smp["dB_rows"], BF16_TOL, "dB rows")
     assert_close(host(g["dA"][:, kcols]), smp["dA_cols"], BF16_TOL, "dA cols")
+
+
+@pytest.mark.parametrize("dtype,M,N,K,r", [("bf16", 300, 512, 384, 16), ("f32", 64, 256, 256, 8)])
+def test_without_input_gradient(dtype, M, N, K, r):
+    """dX not requested: the factor gradients are the same bits as with dX."""
+    require_gpu()
+    import lora_dora_linear_amd as L
+    c = inputs.linear_case(17, M, N, K, r, 0.5, dtype)
+    X, W0, A, B, dY = (dev(c.t[k], dtype) for k in ("X", "W0", "A", "B", "dY"))
+    Y, U = L.lora_linear_fwd(X, W0, A, B, c.s)
+    g0 = L.lora_linear_bwd(dY, X, W0, A, B, c.s, U=U, need_dx=False)
+    g1 = L.lora_linear_bwd(dY, X, W0, A, B, c.s, U=U, need_dx=True)
+    g2 = L.lora_linear_bwd(dY, X, W0, A, B, c.s, U=None, need_dx=False)
+    torch.cuda.synchronize()
+    assert g0["dX"] is None
+    _, gr, _ = _oracle(c)
+    tol = BF16_TOL if dtype == "bf16" else 1e-4
+    for k in ("dA", "dB"):
+        assert_close(host(g0[k]), gr[k], tol, k)
+        assert torch.equal(g0[k], g1[k]), k
+        assert torch.equal(g0[k], g2[k]), k + " with U recomputed"
+
+
+def test_fp32_tiny_latency():
+    """c1 (fp32, 64 x 256 x 256, r = 8): forward + backward time on the GPU, printed (launch-bound)."""
+    require_gpu()
+    import lora_dora_linear_amd as L
+    c = inputs.linear_case(1, 64, 256, 256, 8, 2.0, "f32")
+    X, W0, A, B, dY = (dev(c.t[k], "f32") for k in ("X", "W0", "A", "B", "dY"))
+
+    def step():
+        Y, U = L.lora_linear_fwd(X, W0, A, B, c.s)
+        return L.lora_linear_bwd(dY, X, W0, A, B, c.s, U=U)
+
+    for _ in range(20):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(200):
+        g = step()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) / 200 * 1e3
+    print(f"c1 fp32 tiny LoRA fwd+bwd: {us:.1f} us per step (binding calls included)")
+    _, gr, _ = _oracle(c)
+    assert_close(host(g["dX"]), gr["dX"], 1e-4, "dX")

@@ -72,17 +72,18 @@ def test_int8_raw_product_exact(M, N, K):
     np.testing.assert_array_equal(C.cpu().numpy().astype(np.int64), ow.int_product(a, b))
 
 
-def _run(c, W0f, need_dx=True):
+def _run(c, W0f, need_dx=True, bias=None):
     import lora_dora_linear_amd as L
     X, A, B, dY = (dev(c.t[k], "bf16") for k in ("X", "A", "B", "dY"))
     Wq, sw = L.w8a8_quantize_weight(dev(W0f, "f32"))
-    Y, Xq, sx, U = L.w8a8_lora_linear_fwd(X, Wq, sw, A, B, c.s)
+    Y, Xq, sx, U = L.w8a8_lora_linear_fwd(X, Wq, sw, A, B, c.s, bias=None if bias is None else dev(bias, "bf16"))
     g = L.w8a8_lora_linear_bwd(dY, X, Wq, sw, A, B, c.s, U=U, need_dx=need_dx)
     torch.cuda.synchronize()
     return Y, Xq, sx, g
 
 
-@pytest.mark.parametrize("M,N,K,r", [(300, 512, 640, 32), (129, 256, 256, 16)])
+@pytest.mark.parametrize("M,N,K,r", [(300, 512, 640, 32), (129, 256, 256, 16), (64, 384, 256, 32),
+                                     (100, 192, 384, 16)])
 def test_w8a8_parity(M, N, K, r):
     require_gpu()
     c, W0f = _case(M, N, K, r)
@@ -97,9 +98,9 @@ def test_w8a8_parity(M, N, K, r):
         assert_close(host(g[k]), b[k], TOL, k)
 
 
-@pytest.mark.parametrize("M", [1024, 16384])
+@pytest.mark.parametrize("M", [1024, 2048, 4096, 8192, 16384])
 def test_w8a8_full_size_sampled(M):
-    """K = N = 5120, r = 32, s = 0.5 at both ends of the M sweep: sampled rows and entries."""
+    """K = N = 5120, r = 32, s = 0.5 at every point of the M sweep: sampled rows and entries."""
     require_gpu()
     c, W0f = _case(M, 5120, 5120, 32)
     Y, Xq, sx, g = _run(c, W0f)
@@ -116,3 +117,23 @@ def test_w8a8_full_size_sampled(M):
     smp = olora.lora_weight_grads_sampled(dY, X, A, B, c.s, ncols, kcols)
     assert_close(host(g["dB"][ncols]), smp["dB_rows"], TOL, "dB rows")
     assert_close(host(g["dA"][:, kcols]), smp["dA_cols"], TOL, "dA cols")
+
+
+def test_w8a8_bias_and_no_input_gradient():
+    """Bias added after the dequantised base and the low-rank term; with dX not requested
+    the factor gradients are the same bits."""
+    require_gpu()
+    c, W0f = _case(300, 512, 640, 32, seed=18)
+    bias = inputs.normal(18, 6, (512,), 0.5, "bf16")
+    Y, Xq, sx, g = _run(c, W0f, need_dx=True, bias=bias)
+    Y2, _, _, g2 = _run(c, W0f, need_dx=False, bias=bias)
+    Wq_ref, sw_ref = ow.quantize_rows_int8(W0f)
+    X, A, B, dY = (c.f64(k) for k in ("X", "A", "B", "dY"))
+    f = ow.w8a8_forward(X, Wq_ref, sw_ref, A, B, c.s, bias=inputs.bf16_bits_to_f64(bias))
+    assert_close(host(Y), f["Y"], TOL, "Y with bias")
+    assert torch.equal(Y, Y2)
+    assert g2["dX"] is None
+    b = ow.w8a8_backward(dY, X, Wq_ref, sw_ref, A, B, c.s)
+    for k in ("dA", "dB"):
+        assert_close(host(g2[k]), b[k], TOL, k)
+        assert torch.equal(g[k], g2[k]), k
