@@ -138,6 +138,26 @@ int lora_linear_bwd(int M, int N, int K, int r, float s, int dtype,
                     const float* U_saved, void* dX, float* dA, float* dB, float* dbias,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* The LoRA backward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and arguments as lora_linear_bwd without the workspace, which comes
+ * from a fixed device-resident scratch array of ldl_noalloc_scratch_bytes() bytes
+ * (32 MiB) that the library holds on each device it runs on until the process ends.
+ * The call makes no allocation of any kind.  The device is the calling thread's
+ * current device, which must be the one `stream` belongs to.  Sizes whose workspace
+ * (ldl_workspace_bytes(LDL_OP_LORA_BWD, ...)) exceeds the scratch return
+ * LDL_E_WORKSPACE before anything is enqueued.  All calls on one device share its
+ * scratch, and it keeps the last call's contents: calls that overlap in time on one
+ * device (different streams, or different host threads) race and give wrong results;
+ * serialise them.  LDL_E_HIP also reports a failed lookup of the device's scratch. */
+int lora_linear_bwd_noalloc(int M, int N, int K, int r, float s, int dtype,
+                            const void* dY, const void* X, const void* W0, const void* A, const void* B,
+                            const float* U_saved, void* dX, float* dA, float* dB, float* dbias,
+                            void* stream);
+
+/* Size in bytes of the per-device scratch array lora_linear_bwd_noalloc uses. */
+size_t ldl_noalloc_scratch_bytes(void);
+
 /* ------------------------------------------------------------------------ DoRA
  * Row-scaled DoRA ("dora-rows"), bf16 only.  The row norm of W' = W0 + s.B.A uses
  * the closed form with the cached constant rowsum(W0^2) and the two rank-sized terms

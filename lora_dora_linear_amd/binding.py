@@ -32,6 +32,8 @@ SIGNATURES = {
     "dora_state_floats": ([_i, _i], _z),
     "lora_linear_fwd": ([_i, _i, _i, _i, _f, _i, _p, _p, _p, _p, _p, _p, _p, _p, _z, _p], _i),
     "lora_linear_bwd": ([_i, _i, _i, _i, _f, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _z, _p], _i),
+    "lora_linear_bwd_noalloc": ([_i, _i, _i, _i, _f, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p], _i),
+    "ldl_noalloc_scratch_bytes": ([], _z),
     "dora_prepare": ([_i, _i, _i, _p, _p, _p], _i),
     "dora_linear_fwd": ([_i, _i, _i, _i, _f, _f, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _z, _p], _i),
     "dora_linear_bwd": ([_i, _i, _i, _i, _f, _f, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
@@ -156,6 +158,26 @@ def lora_linear_bwd(dY, X, W0, A, B, s, U=None, need_dx=True, need_dbias=False):
     ws, n = _ws("lora_bwd", M, N, K, r, _dt(X), dev)
     _check(lib().lora_linear_bwd(M, N, K, r, float(s), _dt(X), _ptr(dY), _ptr(X), _ptr(W0), _ptr(A), _ptr(B), _ptr(U),
                                  _ptr(dX), _ptr(dA), _ptr(dB), _ptr(db), _ptr(ws), n, _stream()), "lora_linear_bwd")
+    return {"dX": dX, "dA": dA, "dB": dB, "dbias": db}
+
+
+def lora_linear_bwd_noalloc(dY, X, W0, A, B, s, U=None, need_dx=True, need_dbias=False):
+    """lora_linear_bwd on the library's fixed per-device scratch (no workspace is allocated)."""
+    M, K = X.shape
+    N, r = B.shape
+    dt = X.dtype
+    for t, n, sh in ((dY, "dY", (M, N)), (X, "X", (M, K)), (W0, "W0", (N, K)), (A, "A", (r, K)), (B, "B", (N, r))):
+        _need(t, n, dt, sh)
+    if U is not None:
+        _need(U, "U", torch.float32, (M, r))
+    dev = X.device
+    dX = torch.empty((M, K), dtype=dt, device=dev) if need_dx else None
+    dA = torch.empty((r, K), dtype=torch.float32, device=dev)
+    dB = torch.empty((N, r), dtype=torch.float32, device=dev)
+    db = torch.empty((N,), dtype=torch.float32, device=dev) if need_dbias else None
+    _check(lib().lora_linear_bwd_noalloc(M, N, K, r, float(s), _dt(X), _ptr(dY), _ptr(X), _ptr(W0), _ptr(A), _ptr(B),
+                                         _ptr(U), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(db), _stream()),
+           "lora_linear_bwd_noalloc")
     return {"dX": dX, "dA": dA, "dB": dB, "dbias": db}
 
 

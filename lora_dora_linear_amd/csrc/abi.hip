@@ -2,6 +2,7 @@
 // sequence of each layer.  Nothing here allocates, synchronises or touches an
 // output before every argument has been checked.
 #include <cstring>
+#include <mutex>
 
 #include "../../include/lora_dora_linear.h"
 #include "internal.hpp"
@@ -9,6 +10,29 @@
 using namespace ldl;
 
 namespace {
+
+// Device-resident scratch for lora_linear_bwd_noalloc: callers that cannot allocate (HIP graph
+// capture, tight serving loops) pass no workspace.  One copy per device, held until the process
+// ends.  Host code never uses the array's name as an address: each device's copy is looked up
+// once with hipGetSymbolAddress (with that device current) and that pointer is passed on.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The calling thread's current device's copy of the scratch array, or nullptr on a HIP error.
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 int g_fwd_fused = 0;   // LDL_TUNE_FWD_FUSED_DOWNPROJ
 
@@ -467,6 +491,18 @@ int lora_linear_bwd(int M, int N, int K, int r, float s, int dtype, const void* 
   if (dbias) LDL_TRY(launch_reduce_colsum(w.csB, w.nsB, N, dbias, st));
   return LDL_OK;
 }
+
+int lora_linear_bwd_noalloc(int M, int N, int K, int r, float s, int dtype, const void* dY, const void* X,
+                            const void* W0, const void* A, const void* B, const float* U_saved, void* dX, float* dA,
+                            float* dB, float* dbias, void* stream) {
+  if (ldl_workspace_bytes(LDL_OP_LORA_BWD, M, N, K, r, dtype) > kScratchBytes) return LDL_E_WORKSPACE;
+  void* ws = scratch_for_current_device();
+  if (!ws) return LDL_E_HIP;
+  return lora_linear_bwd(M, N, K, r, s, dtype, dY, X, W0, A, B, U_saved, dX, dA, dB, dbias, ws, kScratchBytes,
+                         stream);
+}
+
+size_t ldl_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 // =========================================================================== DoRA
 int dora_prepare(int N, int K, int dtype, const void* W0, float* w0_sumsq, void* stream) {
