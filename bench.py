@@ -183,10 +183,10 @@ def main():
         ws = torch.empty(max(nf, nb, 256), dtype=torch.uint8, device=dev)
 
         def step():
-            check(L.lora_linear_fwd(M, N, K, r, s, 1, P(X), P(W0), P(A), P(B), None, P(Y), P(U), P(ws), nf, st()),
-                  "lora_linear_fwd")
-            check(L.lora_linear_bwd(M, N, K, r, s, 1, P(dY), P(X), P(W0), P(A), P(B), P(U), P(dX), P(dA), P(dB),
-                                    None, P(ws), nb, st()), "lora_linear_bwd")
+            check(L.lora_linear_fwd(M, N, K, r, s, 1, P(X), K, P(W0), K, P(A), P(B), None, P(Y), N, P(U), r, P(ws),
+                                    nf, st()), "lora_linear_fwd")
+            check(L.lora_linear_bwd(M, N, K, r, s, 1, P(dY), N, P(X), K, P(W0), K, P(A), P(B), P(U), r, P(dX), K,
+                                    P(dA), P(dB), None, P(ws), nb, st()), "lora_linear_bwd")
         flops = 4.0 * M * N * K + 6.0 * M * r * (K + N)
         gemm_flops = {0: 2.0 * M * N * K + 2.0 * M * N * r, 1: 2.0 * M * N * K + 2.0 * M * K * r}
         config = {"workload": f"bf16 LoRA linear fwd+bwd, M={M} tokens (4x1024), K=N={K}, r={r}, s={s}",
@@ -197,7 +197,7 @@ def main():
         X, W0, A, B, dY = (up(c.t[k], "bf16") for k in ("X", "W0", "A", "B", "dY"))
         m = up(c.t["m"], "f32")
         w0sq = torch.empty((N,), dtype=f32, device=dev)
-        check(L.dora_prepare(N, K, 1, P(W0), P(w0sq), st()), "dora_prepare")
+        check(L.dora_prepare(N, K, 1, P(W0), K, P(w0sq), st()), "dora_prepare")
         Y = torch.empty((M, N), dtype=bf, device=dev)
         Z = torch.empty((M, N), dtype=bf, device=dev)
         U = torch.empty((M, r), dtype=f32, device=dev)
@@ -210,10 +210,11 @@ def main():
         ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
 
         def step():
-            check(L.dora_linear_fwd(M, N, K, r, s, eps, 1, P(X), P(W0), P(A), P(B), P(m), P(w0sq), None, P(Y), P(U),
-                                    P(Z), P(state), P(ws), 0, st()), "dora_linear_fwd")
-            check(L.dora_linear_bwd(M, N, K, r, s, eps, 1, P(dY), P(X), P(W0), P(A), P(B), P(m), P(U), P(Z),
-                                    P(state), P(dX), P(dA), P(dB), P(dm), None, P(ws), nb, st()), "dora_linear_bwd")
+            check(L.dora_linear_fwd(M, N, K, r, s, eps, 1, P(X), K, P(W0), K, P(A), P(B), P(m), P(w0sq), None, P(Y),
+                                    N, P(U), r, P(Z), N, P(state), P(ws), 0, st()), "dora_linear_fwd")
+            check(L.dora_linear_bwd(M, N, K, r, s, eps, 1, P(dY), N, P(X), K, P(W0), K, P(A), P(B), P(m), P(U), r,
+                                    P(Z), N, P(state), P(dX), K, P(dA), P(dB), P(dm), None, P(ws), nb, st()),
+                  "dora_linear_bwd")
         lora_flops = 4.0 * M * N * K + 6.0 * M * r * (K + N)
         dora_flops = 2.0 * N * K * r * 2 + 2.0 * r * r * K       # P = W0.A^T and (w.B)^T.W0, plus G = A.A^T
         flops = lora_flops + dora_flops
@@ -238,11 +239,11 @@ def main():
         w = [P(Wt[k]) for k in ("Wg", "Ag", "Bg", "Wu", "Au", "Bu", "Wd", "Ad", "Bd")]
 
         def step():
-            check(L.swiglu_lora_mlp_fwd(M, K, H, r, s, s, s, P(Xd), *w, P(Out), P(E), P(Gu), P(Hs), P(U), P(ws), 0,
-                                        st()), "swiglu_lora_mlp_fwd")
-            check(L.swiglu_lora_mlp_bwd(M, K, H, r, s, s, s, P(dO), P(Xd), *w, P(E), P(Gu), P(Hs), P(U), P(dX),
-                                        P(gr["dAg"]), P(gr["dBg"]), P(gr["dAu"]), P(gr["dBu"]), P(gr["dAd"]),
-                                        P(gr["dBd"]), P(ws), nb, st()), "swiglu_lora_mlp_bwd")
+            check(L.swiglu_lora_mlp_fwd(M, K, H, r, s, s, s, P(Xd), K, *w, P(Out), K, P(E), P(Gu), P(Hs), P(U),
+                                        P(ws), 0, st()), "swiglu_lora_mlp_fwd")
+            check(L.swiglu_lora_mlp_bwd(M, K, H, r, s, s, s, P(dO), K, P(Xd), K, *w, P(E), P(Gu), P(Hs), P(U),
+                                        P(dX), K, P(gr["dAg"]), P(gr["dBg"]), P(gr["dAu"]), P(gr["dBu"]),
+                                        P(gr["dAd"]), P(gr["dBd"]), P(ws), nb, st()), "swiglu_lora_mlp_bwd")
         base = 2.0 * M * K * H * 3 * 2           # three projections, forward + input gradient
         lora = 3 * (6.0 * M * r * (K + H))
         flops = base + lora
@@ -258,7 +259,7 @@ def main():
         W0f = up(inputs.normal(5, 1, (N, K), 1.0 / np.sqrt(K), "f32"), "f32")
         Wq = torch.empty((N, K), dtype=torch.int8, device=dev)
         sw = torch.empty((N,), dtype=f32, device=dev)
-        check(L.w8a8_quantize_weight(N, K, 0, P(W0f), P(Wq), P(sw), st()), "w8a8_quantize_weight")
+        check(L.w8a8_quantize_weight(N, K, 0, P(W0f), K, P(Wq), P(sw), st()), "w8a8_quantize_weight")
         Y = torch.empty((M, N), dtype=bf, device=dev)
         Xq = torch.empty((M, K), dtype=torch.int8, device=dev)
         sx = torch.empty((M,), dtype=f32, device=dev)
@@ -271,10 +272,10 @@ def main():
         ws = torch.empty(max(nf, nb, 256), dtype=torch.uint8, device=dev)
 
         def step():
-            check(L.w8a8_lora_linear_fwd(M, N, K, r, s, P(X), P(Wq), P(sw), P(A), P(B), None, P(Y), P(Xq), P(sx),
-                                         P(U), P(ws), nf, st()), "w8a8_lora_linear_fwd")
-            check(L.w8a8_lora_linear_bwd(M, N, K, r, s, P(dY), P(X), P(Wq), P(sw), P(A), P(B), P(U), P(dX), P(dA),
-                                         P(dB), P(ws), nb, st()), "w8a8_lora_linear_bwd")
+            check(L.w8a8_lora_linear_fwd(M, N, K, r, s, P(X), K, P(Wq), K, P(sw), P(A), P(B), None, P(Y), N, P(Xq),
+                                         P(sx), P(U), r, P(ws), nf, st()), "w8a8_lora_linear_fwd")
+            check(L.w8a8_lora_linear_bwd(M, N, K, r, s, P(dY), N, P(X), K, P(Wq), K, P(sw), P(A), P(B), P(U), r,
+                                         P(dX), K, P(dA), P(dB), P(ws), nb, st()), "w8a8_lora_linear_bwd")
         flops = 4.0 * M * N * K + 6.0 * M * r * (K + N)   # int8 ops of the base counted with the bf16 ones
         gemm_flops = {0: 2.0 * M * N * K + 2.0 * M * N * r, 1: 2.0 * M * N * K + 2.0 * M * K * r}
         config = {"workload": f"W8A8 int8 base + bf16 LoRA fwd+bwd, M={M}, K=N={K}, r={r}, s={s}",

@@ -12,8 +12,16 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Shapes: X [M,K], W0 [N,K], A = lora_down [r,K], B = lora_up [N,r],
- *    Y and dY [M,N], dX [M,K].  Every tensor is dense row-major (last index
- *    contiguous, leading dimension = row length).
+ *    Y and dY [M,N], dX [M,K].  Every tensor is row-major (last index
+ *    contiguous).  Operands passed with a leading-dimension argument (ldx, ldw,
+ *    ldy, lddy, lddx, ldu, ldz, ...) may be strided views such as column slices
+ *    of a wider buffer: ld is the distance between consecutive rows in elements,
+ *    0 selects the row length (dense).  An ld below the row length is
+ *    LDL_E_INVAL; for the bf16 / int8 kernels rows must start on 16-byte
+ *    boundaries (ld a multiple of 8 bf16 elements, 16 int8 elements, or 4 fp32
+ *    elements for U), else LDL_E_UNSUPPORTED.  The fp32 path takes any ld.
+ *    Operands without an ld argument (A, B, bias, m, the DoRA state, the SwiGLU
+ *    weights and saved activations, the factor gradients) are dense.
  *  - Pointers are DEVICE pointers owned by the caller (inputs, outputs and the
  *    workspace).  The library keeps no state and never allocates.
  *  - dtype: LDL_BF16 (bf16 storage, fp32 accumulation) or LDL_F32.  U, V,
@@ -115,12 +123,13 @@ size_t ldl_workspace_bytes(int op, int M, int N, int K, int r, int dtype);
  * message; lora_down / lora_up orientation as in "nunchaku-style kernel fusion -
  * 20-30% faster training", LoRA-epilogue commit).
  *   Y = X.W0^T + s.(X.A^T).B^T (+ bias)
- *   X [M,K], W0 [N,K], A [r,K], B [N,r], bias [N] or NULL (dtype of X), Y [M,N].
- *   U_save [M,r] fp32 or NULL: receives U = X.A^T for the backward.
+ *   X [M,K] (row stride ldx), W0 [N,K] (ldw), A [r,K], B [N,r], bias [N] or NULL
+ *   (dtype of X), Y [M,N] (ldy).  U_save [M,r] fp32 (ldu) or NULL: receives
+ *   U = X.A^T for the backward.
  */
 int lora_linear_fwd(int M, int N, int K, int r, float s, int dtype,
-                    const void* X, const void* W0, const void* A, const void* B,
-                    const void* bias, void* Y, float* U_save,
+                    const void* X, int ldx, const void* W0, int ldw, const void* A, const void* B,
+                    const void* bias, void* Y, int ldy, float* U_save, int ldu,
                     void* ws, size_t ws_bytes, void* stream);
 
 /* Backward of the LoRA linear with W0 frozen.  The LoRA input gradient is folded
@@ -129,13 +138,14 @@ int lora_linear_fwd(int M, int N, int K, int r, float s, int dtype,
  * Backward Pass Implementation"; "nunchaku-style kernel fusion ...", LoRA-epilogue
  * commit: neither direction builds an (M, out_features) intermediate).
  *   V = dY.B;  dX = dY.W0 + s.V.A;  dA = s.V^T.X;  dB = s.dY^T.U;  dbias = sum_m dY.
- *   dY [M,N]; X, W0, A, B as in the forward; U_saved [M,r] fp32 from the forward
- *   (NULL: recomputed).  dX [M,K] (dtype) or NULL; dA [r,K], dB [N,r] fp32
- *   (overwritten); dbias [N] fp32 or NULL.
+ *   dY [M,N] (lddy); X, W0, A, B as in the forward; U_saved [M,r] fp32 (ldu) from
+ *   the forward (NULL: recomputed).  dX [M,K] (dtype, lddx) or NULL; dA [r,K],
+ *   dB [N,r] fp32 (overwritten); dbias [N] fp32 or NULL.
  */
 int lora_linear_bwd(int M, int N, int K, int r, float s, int dtype,
-                    const void* dY, const void* X, const void* W0, const void* A, const void* B,
-                    const float* U_saved, void* dX, float* dA, float* dB, float* dbias,
+                    const void* dY, int lddy, const void* X, int ldx, const void* W0, int ldw,
+                    const void* A, const void* B, const float* U_saved, int ldu,
+                    void* dX, int lddx, float* dA, float* dB, float* dbias,
                     void* ws, size_t ws_bytes, void* stream);
 
 /* The LoRA backward for callers that cannot allocate device memory (code under HIP
@@ -151,8 +161,9 @@ int lora_linear_bwd(int M, int N, int K, int r, float s, int dtype,
  * device (different streams, or different host threads) race and give wrong results;
  * serialise them.  LDL_E_HIP also reports a failed lookup of the device's scratch. */
 int lora_linear_bwd_noalloc(int M, int N, int K, int r, float s, int dtype,
-                            const void* dY, const void* X, const void* W0, const void* A, const void* B,
-                            const float* U_saved, void* dX, float* dA, float* dB, float* dbias,
+                            const void* dY, int lddy, const void* X, int ldx, const void* W0, int ldw,
+                            const void* A, const void* B, const float* U_saved, int ldu,
+                            void* dX, int lddx, float* dA, float* dB, float* dbias,
                             void* stream);
 
 /* Size in bytes of the per-device scratch array lora_linear_bwd_noalloc uses. */
@@ -167,23 +178,23 @@ size_t ldl_noalloc_scratch_bytes(void);
  * "What" and "Fidelity").
  */
 
-/* Once per frozen W0: w0_sumsq[n] = sum_k W0[n,k]^2 (fp32 [N]).  Must be recomputed
- * whenever W0 changes. */
-int dora_prepare(int N, int K, int dtype, const void* W0, float* w0_sumsq, void* stream);
+/* Once per frozen W0 [N,K] (row stride ldw): w0_sumsq[n] = sum_k W0[n,k]^2 (fp32 [N]).
+ * Must be recomputed whenever W0 changes. */
+int dora_prepare(int N, int K, int dtype, const void* W0, int ldw, float* w0_sumsq, void* stream);
 
 /* Floats in the DoRA state buffer the forward fills and the backward reads:
  * norm [N] | g [N] | P [N*r] | G [r*r]. */
 size_t dora_state_floats(int N, int r);
 
 /*   Z = X.W0^T + s.(X.A^T).B^T;  Y = g (.) Z + bias,  g_n = m_n / max(nu_n, eps).
- *   m [N] fp32 magnitude; w0_sumsq [N] from dora_prepare; bias [N] or NULL;
- *   Y [M,N]; U_save [M,r] fp32 (required); Z_save [M,N] (dtype, required, read by
- *   the backward for the magnitude gradient); state: dora_state_floats(N,r) fp32
- *   (required). */
+ *   X [M,K] (ldx), W0 [N,K] (ldw); m [N] fp32 magnitude; w0_sumsq [N] from
+ *   dora_prepare; bias [N] or NULL; Y [M,N] (ldy); U_save [M,r] fp32 (ldu, required);
+ *   Z_save [M,N] (dtype, ldz, required, read by the backward for the magnitude
+ *   gradient); state: dora_state_floats(N,r) fp32 (required). */
 int dora_linear_fwd(int M, int N, int K, int r, float s, float eps, int dtype,
-                    const void* X, const void* W0, const void* A, const void* B,
+                    const void* X, int ldx, const void* W0, int ldw, const void* A, const void* B,
                     const float* m, const float* w0_sumsq, const void* bias,
-                    void* Y, float* U_save, void* Z_save, float* state,
+                    void* Y, int ldy, float* U_save, int ldu, void* Z_save, int ldz, float* state,
                     void* ws, size_t ws_bytes, void* stream);
 
 /* Gradients of the row-scaled DoRA layer, norm kept in the graph:
@@ -192,12 +203,14 @@ int dora_linear_fwd(int M, int N, int K, int r, float s, float eps, int dtype,
  *   dX = dZ.W0 + s.(dZ.B).A
  *   dB = s.dZ^T.U + w (.) (2s.P + 2s^2.B.G)
  *   dA = s.(dZ.B)^T.X + 2s.(w (.) B)^T.W0 + 2s^2.(B^T diag(w) B).A
- *   Inputs as in the forward plus dY [M,N], U_saved, Z_saved, state.  Outputs
- *   dX [M,K] (dtype) or NULL; dA [r,K], dB [N,r], dm [N] fp32; dbias [N] fp32 or NULL. */
+ *   Inputs as in the forward plus dY [M,N] (lddy), U_saved (ldu), Z_saved (ldz),
+ *   state.  Outputs dX [M,K] (dtype, lddx) or NULL; dA [r,K], dB [N,r], dm [N] fp32;
+ *   dbias [N] fp32 or NULL. */
 int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype,
-                    const void* dY, const void* X, const void* W0, const void* A, const void* B,
-                    const float* m, const float* U_saved, const void* Z_saved, const float* state,
-                    void* dX, float* dA, float* dB, float* dm, float* dbias,
+                    const void* dY, int lddy, const void* X, int ldx, const void* W0, int ldw,
+                    const void* A, const void* B, const float* m, const float* U_saved, int ldu,
+                    const void* Z_saved, int ldz, const float* state,
+                    void* dX, int lddx, float* dA, float* dB, float* dm, float* dbias,
                     void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ SwiGLU MLP
@@ -209,16 +222,16 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype,
  * Backward: the down projection's input gradient dh is either followed by one
  * streaming pass over dh, e and u (four-wave route, hidden width a multiple of 256)
  * or has the SwiGLU backward in its epilogue (other shapes).
- *   X [M,K]; Wg, Wu [H,K]; Ag, Au [r,K]; Bg, Bu [H,r]; Wd [K,H]; Ad [r,H]; Bd [K,r].
- *   Out [M,K].  Saved for the backward: E_save, Gu_save, H_save [M,H] (bf16) and
- *   U_save [M,3r] fp32 = [X.Ag^T | X.Au^T | H.Ad^T].  All required.
+ *   X [M,K] (ldx); Wg, Wu [H,K]; Ag, Au [r,K]; Bg, Bu [H,r]; Wd [K,H]; Ad [r,H];
+ *   Bd [K,r].  Out [M,K] (ldout).  Saved for the backward: E_save, Gu_save, H_save
+ *   [M,H] (bf16) and U_save [M,3r] fp32 = [X.Ag^T | X.Au^T | H.Ad^T].  All required.
  *   Limits: K and H multiples of 64, r a multiple of 8 and at most 64.
  */
 int swiglu_lora_mlp_fwd(int M, int K, int H, int r, float s_gate, float s_up, float s_down,
-                        const void* X, const void* Wg, const void* Ag, const void* Bg,
+                        const void* X, int ldx, const void* Wg, const void* Ag, const void* Bg,
                         const void* Wu, const void* Au, const void* Bu,
                         const void* Wd, const void* Ad, const void* Bd,
-                        void* Out, void* E_save, void* Gu_save, void* H_save, float* U_save,
+                        void* Out, int ldout, void* E_save, void* Gu_save, void* H_save, float* U_save,
                         void* ws, size_t ws_bytes, void* stream);
 
 /* Backward of the SwiGLU LoRA MLP (weights frozen, factor gradients pre-scaled by
@@ -226,16 +239,16 @@ int swiglu_lora_mlp_fwd(int M, int K, int H, int r, float s_gate, float s_up, fl
  * Pass Implementation").
  *   dH = dOut.Wd + s_d.(dOut.Bd).Ad;  dE = dH (.) u (.) silu'(e);  dU = dH (.) silu(e);
  *   dX = dE.Wg + dU.Wu + s_g.(dE.Bg).Ag + s_u.(dU.Bu).Au; factor gradients as in
- *   lora_linear_bwd for each projection.  dX [M,K] bf16 or NULL; dAg, dAu [r,K],
- *   dBg, dBu [H,r], dAd [r,H], dBd [K,r] fp32. */
+ *   lora_linear_bwd for each projection.  dOut [M,K] (lddout), X (ldx); dX [M,K]
+ *   bf16 (lddx) or NULL; dAg, dAu [r,K], dBg, dBu [H,r], dAd [r,H], dBd [K,r] fp32. */
 int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, float s_down,
-                        const void* dOut, const void* X,
+                        const void* dOut, int lddout, const void* X, int ldx,
                         const void* Wg, const void* Ag, const void* Bg,
                         const void* Wu, const void* Au, const void* Bu,
                         const void* Wd, const void* Ad, const void* Bd,
                         const void* E_saved, const void* Gu_saved, const void* H_saved,
                         const float* U_saved,
-                        void* dX, float* dAg, float* dBg, float* dAu, float* dBu,
+                        void* dX, int lddx, float* dAg, float* dBg, float* dAu, float* dBu,
                         float* dAd, float* dBd,
                         void* ws, size_t ws_bytes, void* stream);
 
@@ -249,34 +262,37 @@ int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, fl
  * even; a zero row has scale 0 and codes 0.
  */
 
-/* Per-output-channel weight quantisation, once per frozen W0 (dtype of W0: LDL_F32
- * or LDL_BF16): Wq [N,K] int8, sw [N] fp32. */
-int w8a8_quantize_weight(int N, int K, int dtype, const void* W0, int8_t* Wq, float* sw, void* stream);
+/* Per-output-channel weight quantisation, once per frozen W0 [N,K] (row stride ldw;
+ * dtype of W0: LDL_F32 or LDL_BF16): Wq [N,K] int8 (dense), sw [N] fp32. */
+int w8a8_quantize_weight(int N, int K, int dtype, const void* W0, int ldw, int8_t* Wq, float* sw, void* stream);
 
-/* Per-row activation quantisation: Xq [M,K] int8, sx [M] fp32 from bf16 X. */
-int w8a8_quantize_rows(int M, int K, const void* X, int8_t* Xq, float* sx, void* stream);
+/* Per-row activation quantisation: Xq [M,K] int8 (dense), sx [M] fp32 from bf16 X (ldx). */
+int w8a8_quantize_rows(int M, int K, const void* X, int ldx, int8_t* Xq, float* sx, void* stream);
 
 /* Raw int32 product C = Xq.Wq^T (the "raw product" epilogue of the 8-bit core).
- * C [M,N] int32.  Exact. */
-int int8_gemm_raw(int M, int N, int K, const int8_t* Xq, const int8_t* Wq, int32_t* C, void* stream);
+ * Xq [M,K] (ldxq), Wq [N,K] (ldwq), C [M,N] int32 (ldc).  Exact. */
+int int8_gemm_raw(int M, int N, int K, const int8_t* Xq, int ldxq, const int8_t* Wq, int ldwq,
+                  int32_t* C, int ldc, void* stream);
 
 /*   Y = (Xq.Wq^T) . sx[m] . sw[n] + s.(X.A^T).B^T (+ bias), Xq / sx quantised from X
- *   in the call.  X [M,K] bf16; Wq [N,K] int8; sw [N] fp32; A, B, bias bf16.
- *   Y [M,N] bf16.  Xq_save [M,K] int8 or NULL, sx_save [M] fp32 or NULL (both NULL or
- *   both set), U_save [M,r] fp32 or NULL.  The LoRA branch sees X, not Xq. */
+ *   in the call.  X [M,K] bf16 (ldx); Wq [N,K] int8 (ldw); sw [N] fp32; A, B, bias
+ *   bf16.  Y [M,N] bf16 (ldy).  Xq_save [M,K] int8 (dense) or NULL, sx_save [M] fp32
+ *   or NULL (both NULL or both set), U_save [M,r] fp32 (ldu) or NULL.  The LoRA
+ *   branch sees X, not Xq. */
 int w8a8_lora_linear_fwd(int M, int N, int K, int r, float s,
-                         const void* X, const int8_t* Wq, const float* sw,
+                         const void* X, int ldx, const int8_t* Wq, int ldw, const float* sw,
                          const void* A, const void* B, const void* bias,
-                         void* Y, int8_t* Xq_save, float* sx_save, float* U_save,
+                         void* Y, int ldy, int8_t* Xq_save, float* sx_save, float* U_save, int ldu,
                          void* ws, size_t ws_bytes, void* stream);
 
 /* Straight-through backward: dX = dY.(diag(sw).Wq + s.B.A) (the dequantised weight,
- * bf16 MFMA), dA = s.(dY.B)^T.X, dB = s.dY^T.U.  dX [M,K] bf16 or NULL; dA [r,K],
- * dB [N,r] fp32; U_saved [M,r] fp32 or NULL (recomputed). */
+ * bf16 MFMA), dA = s.(dY.B)^T.X, dB = s.dY^T.U.  dY [M,N] (lddy), X (ldx), Wq (ldw);
+ * dX [M,K] bf16 (lddx) or NULL; dA [r,K], dB [N,r] fp32; U_saved [M,r] fp32 (ldu) or
+ * NULL (recomputed). */
 int w8a8_lora_linear_bwd(int M, int N, int K, int r, float s,
-                         const void* dY, const void* X, const int8_t* Wq, const float* sw,
-                         const void* A, const void* B, const float* U_saved,
-                         void* dX, float* dA, float* dB,
+                         const void* dY, int lddy, const void* X, int ldx, const int8_t* Wq, int ldw,
+                         const float* sw, const void* A, const void* B, const float* U_saved, int ldu,
+                         void* dX, int lddx, float* dA, float* dB,
                          void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus

@@ -204,19 +204,19 @@ hipError_t rowproj(int M, int K, int R, const void* P, int ldp, const void* q0, 
   p.M = M; p.K = K; p.R = R; p.R0 = R0;
   p.P = static_cast<const uint16_t*>(P); p.ldp = ldp;
   p.q0 = static_cast<const uint16_t*>(q0); p.q1 = static_cast<const uint16_t*>(q1 ? q1 : q0); p.ldq = ldq;
-  p.P1 = nullptr; p.p_split = M;
+  p.P1 = nullptr; p.p_split = M; p.ldp1 = ldp;
   p.q_trans = 0; p.q_kscale = nullptr;
   p.out = out; p.ldo = ldo; p.scale = scale;
   return launch_rowproj(p, st);
 }
 
-// rowproj over the rows of P followed by the rows of P1 (M0 + M1 rows, both with leading dim ldp)
-hipError_t rowproj2(int M0, int M1, int K, int R, const void* P, const void* P1, int ldp, const void* q0, int ldq,
-                    float* out, int ldo, float scale, hipStream_t st) {
+// rowproj over the rows of P (leading dim ldp) followed by the rows of P1 (leading dim ldp1)
+hipError_t rowproj2(int M0, int M1, int K, int R, const void* P, int ldp, const void* P1, int ldp1, const void* q0,
+                    int ldq, float* out, int ldo, float scale, hipStream_t st) {
   RowProjParams p;
   p.M = M0 + M1; p.K = K; p.R = R; p.R0 = R;
   p.P = static_cast<const uint16_t*>(P); p.ldp = ldp;
-  p.P1 = static_cast<const uint16_t*>(P1); p.p_split = M0;
+  p.P1 = static_cast<const uint16_t*>(P1); p.p_split = M0; p.ldp1 = ldp1;
   p.q0 = p.q1 = static_cast<const uint16_t*>(q0); p.ldq = ldq;
   p.q_trans = 0; p.q_kscale = nullptr;
   p.out = out; p.ldo = ldo; p.scale = scale;
@@ -229,7 +229,7 @@ hipError_t rowproj_t(int M, int K, int R, const void* P, int ldp, const void* Bq
   RowProjParams p;
   p.M = M; p.K = K; p.R = R; p.R0 = R;
   p.P = static_cast<const uint16_t*>(P); p.ldp = ldp;
-  p.P1 = nullptr; p.p_split = M;
+  p.P1 = nullptr; p.p_split = M; p.ldp1 = ldp;
   p.q0 = p.q1 = static_cast<const uint16_t*>(Bq); p.ldq = ldb;
   p.q_trans = 1; p.q_kscale = kscale;
   p.out = out; p.ldo = ldo; p.scale = scale;
@@ -291,6 +291,25 @@ int check_bf16_layer(int M, int N, int K, int r) {
   if (!small(M + 256, K, 2) || !small(N, K, 2) || !small(M + 256, N, 2) || !small(M, 2 * r, 4)) return LDL_E_UNSUPPORTED;
   return LDL_OK;
 }
+
+// Leading dimension (elements) of a row-major operand with `cols` columns: 0 selects `cols`.
+// Below `cols` is an invalid argument; rows that are not a whole number of `mult`-element
+// groups (16 bytes for the bf16 / int8 kernels, 4 fp32 values for U) are unsupported.
+int fix_ld(int& ld, int cols, int mult) {
+  if (ld == 0) ld = cols;
+  if (ld < cols) return LDL_E_INVAL;
+  return ld % mult == 0 ? LDL_OK : LDL_E_UNSUPPORTED;
+}
+
+#define LDL_LD(ld, cols, mult)                      \
+  do {                                              \
+    const int e_ld = fix_ld((ld), (cols), (mult));  \
+    if (e_ld != LDL_OK) return e_ld;                \
+  } while (0)
+
+// Row-major operands of `rows` rows with leading dimension ld stay below 2 GiB (buffer
+// resources take 31-bit sizes; 256 rows of margin for the row tiles past the end).
+inline bool fits(int rows, int ld, size_t elt) { return small((size_t)rows + 256, (size_t)ld, elt); }
 
 // ------------------------------------------------------------------ fp32 path
 hipError_t f32(int M, int N, int K, const float* A, long sam, long sak, const float* B, long sbk, long sbn,
@@ -380,25 +399,30 @@ size_t ldl_workspace_bytes(int op, int M, int N, int K, int r, int dtype) {
 }
 
 // =========================================================================== LoRA
-int lora_linear_fwd(int M, int N, int K, int r, float s, int dtype, const void* X, const void* W0, const void* A,
-                    const void* B, const void* bias, void* Y, float* U_save, void* ws, size_t ws_bytes,
-                    void* stream) {
+int lora_linear_fwd(int M, int N, int K, int r, float s, int dtype, const void* X, int ldx, const void* W0, int ldw,
+                    const void* A, const void* B, const void* bias, void* Y, int ldy, float* U_save, int ldu,
+                    void* ws, size_t ws_bytes, void* stream) {
   if (!nonnull({W0, A, B}) || (M > 0 && !nonnull({X, Y}))) return LDL_E_INVAL;
   if (dtype != LDL_F32 && dtype != LDL_BF16) return LDL_E_INVAL;
   if (M < 0 || N <= 0 || K <= 0 || r <= 0) return LDL_E_INVAL;
+  const int g = dtype == LDL_BF16 ? 8 : 1, gu = dtype == LDL_BF16 ? 4 : 1;
+  LDL_LD(ldx, K, g); LDL_LD(ldw, K, g); LDL_LD(ldy, N, g); LDL_LD(ldu, r, gu);
   if (!al({X, W0, A, B, bias, Y, U_save, ws})) return LDL_E_UNSUPPORTED;
+  const size_t e = dtype == LDL_BF16 ? 2 : 4;
+  if (!fits(M, ldx, e) || !fits(N, ldw, e) || !fits(M, ldy, e) || !fits(M, ldu, 4)) return LDL_E_UNSUPPORTED;
   if (ldl_workspace_bytes(LDL_OP_LORA_FWD, M, N, K, r, dtype) > ws_bytes && !U_save) return LDL_E_WORKSPACE;
   if (ws_bytes > 0 && !ws) return LDL_E_INVAL;
   const hipStream_t st = S(stream);
   Bump wb(ws);
   float* U = U_save ? U_save : wb.take<float>((size_t)M * r);
+  const int lu = U_save ? ldu : r;
   if (M == 0) return LDL_OK;
 
   if (dtype == LDL_F32) {
     const float *x = (const float*)X, *w = (const float*)W0, *a = (const float*)A, *bb = (const float*)B;
-    LDL_TRY(f32(M, r, K, x, K, 1, a, 1, K, U, r, 1.f, 0.f, nullptr, st));
-    LDL_TRY(f32(M, N, K, x, K, 1, w, 1, K, (float*)Y, N, 1.f, 0.f, (const float*)bias, st));
-    LDL_TRY(f32(M, N, r, U, r, 1, bb, 1, r, (float*)Y, N, s, 1.f, nullptr, st));
+    LDL_TRY(f32(M, r, K, x, ldx, 1, a, 1, K, U, lu, 1.f, 0.f, nullptr, st));
+    LDL_TRY(f32(M, N, K, x, ldx, 1, w, 1, ldw, (float*)Y, ldy, 1.f, 0.f, (const float*)bias, st));
+    LDL_TRY(f32(M, N, r, U, lu, 1, bb, 1, r, (float*)Y, ldy, s, 1.f, nullptr, st));
     return LDL_OK;
   }
 
@@ -406,27 +430,32 @@ int lora_linear_fwd(int M, int N, int K, int r, float s, int dtype, const void* 
   if (chk != LDL_OK) return chk;
   GemmParams p = gp0();
   p.M = M; p.N = N; p.K = K;
-  p.a = X; p.lda = K; p.b0 = W0; p.ldb = K; p.kseg = K;
+  p.a = X; p.lda = ldx; p.b0 = W0; p.ldb = ldw; p.kseg = K;
   p.r_epi = r; p.s_epi = s; p.e0 = B; p.e1 = B; p.e_ldn = r; p.e_ldj = 1; p.e_jsplit = r;
-  p.bias = bias; p.out = Y; p.ldo = N;
+  p.bias = bias; p.out = Y; p.ldo = ldy;
   if (g_fwd_fused && r <= 64 && N % 128 == 0) {
-    p.side = A; p.r_side = r; p.side_save = U_save; p.ld_side_save = r;
+    p.side = A; p.r_side = r; p.side_save = U_save; p.ld_side_save = ldu;
     LDL_TRY(gemm_timed(0, GK_NT_FUSED, p, st));
     return LDL_OK;
   }
-  LDL_TRY(rowproj(M, K, r, X, K, A, nullptr, r, K, U, r, 1.f, st));
-  p.S = U; p.ld_s = r;
+  LDL_TRY(rowproj(M, K, r, X, ldx, A, nullptr, r, K, U, lu, 1.f, st));
+  p.S = U; p.ld_s = lu;
   LDL_TRY(gemm_timed(0, GK_NT_PLAIN, p, st));
   return LDL_OK;
 }
 
-int lora_linear_bwd(int M, int N, int K, int r, float s, int dtype, const void* dY, const void* X, const void* W0,
-                    const void* A, const void* B, const float* U_saved, void* dX, float* dA, float* dB, float* dbias,
-                    void* ws, size_t ws_bytes, void* stream) {
+int lora_linear_bwd(int M, int N, int K, int r, float s, int dtype, const void* dY, int lddy, const void* X, int ldx,
+                    const void* W0, int ldw, const void* A, const void* B, const float* U_saved, int ldu, void* dX,
+                    int lddx, float* dA, float* dB, float* dbias, void* ws, size_t ws_bytes, void* stream) {
   if (!nonnull({W0, A, B, dA, dB}) || (M > 0 && !nonnull({dY, X}))) return LDL_E_INVAL;
   if (dtype != LDL_F32 && dtype != LDL_BF16) return LDL_E_INVAL;
   if (M < 0 || N <= 0 || K <= 0 || r <= 0) return LDL_E_INVAL;
+  const int g = dtype == LDL_BF16 ? 8 : 1, gu = dtype == LDL_BF16 ? 4 : 1;
+  LDL_LD(lddy, N, g); LDL_LD(ldx, K, g); LDL_LD(ldw, K, g); LDL_LD(ldu, r, gu); LDL_LD(lddx, K, g);
   if (!al({dY, X, W0, A, B, U_saved, dX, dA, dB, dbias, ws})) return LDL_E_UNSUPPORTED;
+  const size_t e = dtype == LDL_BF16 ? 2 : 4;
+  if (!fits(M, lddy, e) || !fits(M, ldx, e) || !fits(N, ldw, e) || !fits(M, ldu, 4) || !fits(M, lddx, e))
+    return LDL_E_UNSUPPORTED;
   if (dtype == LDL_BF16) {
     const int chk = check_bf16_layer(M, N, K, r);
     if (chk != LDL_OK) return chk;
@@ -448,70 +477,76 @@ int lora_linear_bwd(int M, int N, int K, int r, float s, int dtype, const void* 
     const float *dy = (const float*)dY, *x = (const float*)X, *w = (const float*)W0, *a = (const float*)A,
                 *bb = (const float*)B;
     const float* U = U_saved;
+    int lu = ldu;
     if (!U) {
-      LDL_TRY(f32(M, r, K, x, K, 1, a, 1, K, Uw, r, 1.f, 0.f, nullptr, st));
+      LDL_TRY(f32(M, r, K, x, ldx, 1, a, 1, K, Uw, r, 1.f, 0.f, nullptr, st));
       U = Uw;
+      lu = r;
     }
-    LDL_TRY(f32(M, r, N, dy, N, 1, bb, r, 1, V, r, 1.f, 0.f, nullptr, st));
+    LDL_TRY(f32(M, r, N, dy, lddy, 1, bb, r, 1, V, r, 1.f, 0.f, nullptr, st));
     if (dX) {
-      LDL_TRY(f32(M, K, N, dy, N, 1, w, K, 1, (float*)dX, K, 1.f, 0.f, nullptr, st));
-      LDL_TRY(f32(M, K, r, V, r, 1, a, K, 1, (float*)dX, K, s, 1.f, nullptr, st));
+      LDL_TRY(f32(M, K, N, dy, lddy, 1, w, ldw, 1, (float*)dX, lddx, 1.f, 0.f, nullptr, st));
+      LDL_TRY(f32(M, K, r, V, r, 1, a, K, 1, (float*)dX, lddx, s, 1.f, nullptr, st));
     }
-    LDL_TRY(f32(r, K, M, V, 1, r, x, K, 1, dA, K, s, 0.f, nullptr, st));
-    LDL_TRY(f32(N, r, M, dy, 1, N, U, r, 1, dB, r, s, 0.f, nullptr, st));
-    if (dbias) LDL_TRY(launch_f32_colsum(dy, M, N, dbias, st));
+    LDL_TRY(f32(r, K, M, V, 1, r, x, ldx, 1, dA, K, s, 0.f, nullptr, st));
+    LDL_TRY(f32(N, r, M, dy, 1, lddy, U, lu, 1, dB, r, s, 0.f, nullptr, st));
+    if (dbias) LDL_TRY(launch_f32_colsum(dy, M, N, lddy, dbias, st));
     return LDL_OK;
   }
 
   Bump wb(ws);
   LoraBwdWs w = plan_lora_bwd(wb, M, N, K, r, true);
   const float* U = U_saved;
+  int lu = ldu;
   if (!U) {
-    LDL_TRY(rowproj(M, K, r, X, K, A, nullptr, r, K, w.U, r, 1.f, st));
+    LDL_TRY(rowproj(M, K, r, X, ldx, A, nullptr, r, K, w.U, r, 1.f, st));
     U = w.U;
+    lu = r;
   }
   // V = dY.B  (B read in place as a [N, r] matrix)
-  LDL_TRY(rowproj_t(M, N, r, dY, N, B, r, nullptr, w.V, r, 1.f, st));
+  LDL_TRY(rowproj_t(M, N, r, dY, lddy, B, r, nullptr, w.V, r, 1.f, st));
   if (dX) {
     GemmParams p = gp0();
     p.M = M; p.N = K; p.K = N;
-    p.a = dY; p.lda = N; p.b0 = W0; p.b1 = W0; p.ldb = K; p.kseg = N;
+    p.a = dY; p.lda = lddy; p.b0 = W0; p.b1 = W0; p.ldb = ldw; p.kseg = N;
     p.S = w.V; p.ld_s = r; p.r_epi = r; p.s_epi = s;
     p.e0 = A; p.e1 = A; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = r;
-    p.out = dX; p.ldo = K;
+    p.out = dX; p.ldo = lddx;
     LDL_TRY(gemm_timed(1, GK_NN_PLAIN, p, st));
   }
   // dB = s.dY^T.U (+ dbias = column sums of dY in the same pass) and dA = s.V^T.X: one launch each
   // for the split partial sums and for their fixed-order reduction
-  LDL_TRY(launch_colproj2(pk(cpp(M, N, r, dY, N, U, r, 1.f, nullptr, 0, dbias ? 2 : 0, w.msB, w.partB, w.csB), w.pkB),
-                          w.nsB, pk(cpp(M, K, r, X, K, w.V, r, 1.f, nullptr, 0, 0, w.msA, w.partA, nullptr), w.pkA),
-                          w.nsA, st));
+  LDL_TRY(launch_colproj2(
+      pk(cpp(M, N, r, dY, lddy, U, lu, 1.f, nullptr, 0, dbias ? 2 : 0, w.msB, w.partB, w.csB), w.pkB), w.nsB,
+      pk(cpp(M, K, r, X, ldx, w.V, r, 1.f, nullptr, 0, 0, w.msA, w.partA, nullptr), w.pkA), w.nsA, st));
   LDL_TRY(launch_reduce2(rdp(N, r, w.partB, (size_t)N * w.rp, w.nsB, w.rp, false, s, dB, r),
                          rdp(r, K, w.partA, (size_t)K * w.rp, w.nsA, w.rp, true, s, dA, K), st));
   if (dbias) LDL_TRY(launch_reduce_colsum(w.csB, w.nsB, N, dbias, st));
   return LDL_OK;
 }
 
-int lora_linear_bwd_noalloc(int M, int N, int K, int r, float s, int dtype, const void* dY, const void* X,
-                            const void* W0, const void* A, const void* B, const float* U_saved, void* dX, float* dA,
-                            float* dB, float* dbias, void* stream) {
+int lora_linear_bwd_noalloc(int M, int N, int K, int r, float s, int dtype, const void* dY, int lddy, const void* X,
+                            int ldx, const void* W0, int ldw, const void* A, const void* B, const float* U_saved,
+                            int ldu, void* dX, int lddx, float* dA, float* dB, float* dbias, void* stream) {
   if (ldl_workspace_bytes(LDL_OP_LORA_BWD, M, N, K, r, dtype) > kScratchBytes) return LDL_E_WORKSPACE;
   void* ws = scratch_for_current_device();
   if (!ws) return LDL_E_HIP;
-  return lora_linear_bwd(M, N, K, r, s, dtype, dY, X, W0, A, B, U_saved, dX, dA, dB, dbias, ws, kScratchBytes,
-                         stream);
+  return lora_linear_bwd(M, N, K, r, s, dtype, dY, lddy, X, ldx, W0, ldw, A, B, U_saved, ldu, dX, lddx, dA, dB, dbias,
+                         ws, kScratchBytes, stream);
 }
 
 size_t ldl_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 // =========================================================================== DoRA
-int dora_prepare(int N, int K, int dtype, const void* W0, float* w0_sumsq, void* stream) {
+int dora_prepare(int N, int K, int dtype, const void* W0, int ldw, float* w0_sumsq, void* stream) {
   if (!nonnull({W0, w0_sumsq})) return LDL_E_INVAL;
   if (N <= 0 || K <= 0) return LDL_E_INVAL;
   if (dtype != LDL_F32 && dtype != LDL_BF16) return LDL_E_INVAL;
   if (!al({W0, w0_sumsq})) return LDL_E_UNSUPPORTED;
+  LDL_LD(ldw, K, dtype == LDL_BF16 ? 8 : 1);
+  if (!fits(N, ldw, dtype == LDL_BF16 ? 2 : 4)) return LDL_E_UNSUPPORTED;
   if (dtype == LDL_BF16 && K % 8) return LDL_E_UNSUPPORTED;
-  LDL_TRY(launch_rowsumsq(W0, dtype == LDL_BF16, N, K, w0_sumsq, S(stream)));
+  LDL_TRY(launch_rowsumsq(W0, dtype == LDL_BF16, N, K, ldw, w0_sumsq, S(stream)));
   return LDL_OK;
 }
 
@@ -523,15 +558,19 @@ static int dora_check(int M, int N, int K, int r, int dtype) {
   return LDL_OK;
 }
 
-int dora_linear_fwd(int M, int N, int K, int r, float s, float eps, int dtype, const void* X, const void* W0,
-                    const void* A, const void* B, const float* m, const float* w0_sumsq, const void* bias, void* Y,
-                    float* U_save, void* Z_save, float* state, void* ws, size_t ws_bytes, void* stream) {
+int dora_linear_fwd(int M, int N, int K, int r, float s, float eps, int dtype, const void* X, int ldx, const void* W0,
+                    int ldw, const void* A, const void* B, const float* m, const float* w0_sumsq, const void* bias,
+                    void* Y, int ldy, float* U_save, int ldu, void* Z_save, int ldz, float* state, void* ws,
+                    size_t ws_bytes, void* stream) {
   (void)ws; (void)ws_bytes;
   if (!nonnull({W0, A, B, m, w0_sumsq, state}) || (M > 0 && !nonnull({X, Y, U_save, Z_save}))) return LDL_E_INVAL;
   if (M < 0 || N <= 0 || K <= 0 || r <= 0 || !(eps >= 0.f)) return LDL_E_INVAL;
   const int chk = dora_check(M, N, K, r, dtype);
   if (chk != LDL_OK) return chk;
+  LDL_LD(ldx, K, 8); LDL_LD(ldw, K, 8); LDL_LD(ldy, N, 8); LDL_LD(ldu, r, 4); LDL_LD(ldz, N, 8);
   if (!al({X, W0, A, B, m, w0_sumsq, bias, Y, U_save, Z_save, state})) return LDL_E_UNSUPPORTED;
+  if (!fits(M, ldx, 2) || !fits(N, ldw, 2) || !fits(M, ldy, 2) || !fits(M, ldu, 4) || !fits(M, ldz, 2))
+    return LDL_E_UNSUPPORTED;
   const hipStream_t st = S(stream);
   float* norm = state;
   float* g = state + N;
@@ -539,31 +578,36 @@ int dora_linear_fwd(int M, int N, int K, int r, float s, float eps, int dtype, c
   float* G = P + (size_t)N * r;
   // the norm terms: P = W0.A^T, G = A.A^T, then nu and g (independent of M)
   // (G is stored right after P with the same row length: one launch over the rows of W0 then A)
-  LDL_TRY(rowproj2(N, r, K, r, W0, A, K, A, K, P, r, 1.f, st));
+  LDL_TRY(rowproj2(N, r, K, r, W0, ldw, A, K, A, K, P, r, 1.f, st));
   LDL_TRY(launch_dora_norm(N, r, s, eps, w0_sumsq, P, G, static_cast<const uint16_t*>(B), m, norm, g, st));
   if (M == 0) return LDL_OK;
-  LDL_TRY(rowproj(M, K, r, X, K, A, nullptr, r, K, U_save, r, 1.f, st));
+  LDL_TRY(rowproj(M, K, r, X, ldx, A, nullptr, r, K, U_save, ldu, 1.f, st));
   GemmParams p = gp0();
   p.M = M; p.N = N; p.K = K;
-  p.a = X; p.lda = K; p.b0 = W0; p.ldb = K; p.kseg = K;
-  p.S = U_save; p.ld_s = r; p.r_epi = r; p.s_epi = s;
+  p.a = X; p.lda = ldx; p.b0 = W0; p.ldb = ldw; p.kseg = K;
+  p.S = U_save; p.ld_s = ldu; p.r_epi = r; p.s_epi = s;
   p.e0 = B; p.e1 = B; p.e_ldn = r; p.e_ldj = 1; p.e_jsplit = r;
   p.col_scale = g; p.bias = bias;
-  p.out = Y; p.ldo = N; p.out2 = Z_save; p.ldo2 = N;
+  p.out = Y; p.ldo = ldy; p.out2 = Z_save; p.ldo2 = ldz;
   LDL_TRY(gemm_timed(0, GK_NT_DORA, p, st));
   return LDL_OK;
 }
 
-int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, const void* dY, const void* X,
-                    const void* W0, const void* A, const void* B, const float* m, const float* U_saved,
-                    const void* Z_saved, const float* state, void* dX, float* dA, float* dB, float* dm,
-                    float* dbias, void* ws, size_t ws_bytes, void* stream) {
+int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, const void* dY, int lddy, const void* X,
+                    int ldx, const void* W0, int ldw, const void* A, const void* B, const float* m,
+                    const float* U_saved, int ldu, const void* Z_saved, int ldz, const float* state, void* dX,
+                    int lddx, float* dA, float* dB, float* dm, float* dbias, void* ws, size_t ws_bytes,
+                    void* stream) {
   if (!nonnull({W0, A, B, m, state, dA, dB, dm, ws}) || (M > 0 && !nonnull({dY, X, U_saved, Z_saved})))
     return LDL_E_INVAL;
   if (M < 0 || N <= 0 || K <= 0 || r <= 0 || !(eps >= 0.f)) return LDL_E_INVAL;
   const int chk = dora_check(M, N, K, r, dtype);
   if (chk != LDL_OK) return chk;
+  LDL_LD(lddy, N, 8); LDL_LD(ldx, K, 8); LDL_LD(ldw, K, 8); LDL_LD(ldu, r, 4); LDL_LD(ldz, N, 8); LDL_LD(lddx, K, 8);
   if (!al({dY, X, W0, A, B, m, U_saved, Z_saved, state, dX, dA, dB, dm, dbias, ws})) return LDL_E_UNSUPPORTED;
+  if (!fits(M, lddy, 2) || !fits(M, ldx, 2) || !fits(N, ldw, 2) || !fits(M, ldu, 4) || !fits(M, ldz, 2) ||
+      !fits(M, lddx, 2))
+    return LDL_E_UNSUPPORTED;
   if (ldl_workspace_bytes(LDL_OP_DORA_BWD, M, N, K, r, dtype) > ws_bytes) return LDL_E_WORKSPACE;
   const hipStream_t st = S(stream);
   const float* norm = state;
@@ -576,7 +620,7 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, c
 
   // dg and dZ^T.U in one pass over dY (and Z); M == 0 gives zero partials
   if (M > 0) {
-    LDL_TRY(colproj(M, N, r, dY, N, U_saved, r, 1.f, Z_saved, N, 1, w.nsT, w.msT, w.partT, w.cs, st, w.pkT));
+    LDL_TRY(colproj(M, N, r, dY, lddy, U_saved, ldu, 1.f, Z_saved, ldz, 1, w.nsT, w.msT, w.partT, w.cs, st, w.pkT));
   } else {
     LDL_TRY(zero(w.partT, (size_t)w.nsT * N * w.rp, st));
     LDL_TRY(zero(w.cs, (size_t)w.nsT * N, st));
@@ -589,28 +633,28 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, c
     if (dX) {
       // dY.diag(g) rounded to bf16 once; V = (dY.diag(g)).B and dX = (dY.diag(g)).W0 + s.V.A
       // are then plain products of it (B read in place as a [N, r] matrix)
-      LDL_TRY(launch_scale_cols(dY, M, N, N, g, w.dYg, st));
+      LDL_TRY(launch_scale_cols(dY, M, N, lddy, g, w.dYg, N, st));
       LDL_TRY(rowproj_t(M, N, r, w.dYg, N, Bh, r, nullptr, w.V, r, 1.f, st));
       GemmParams p = gp0();
       p.M = M; p.N = K; p.K = N;
-      p.a = w.dYg; p.lda = N; p.b0 = W0; p.b1 = W0; p.ldb = K; p.kseg = N;
+      p.a = w.dYg; p.lda = N; p.b0 = W0; p.b1 = W0; p.ldb = ldw; p.kseg = N;
       p.S = w.V; p.ld_s = r; p.r_epi = r; p.s_epi = s;
       p.e0 = A; p.e1 = A; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = r;
-      p.out = dX; p.ldo = K;
+      p.out = dX; p.ldo = lddx;
       LDL_TRY(gemm_timed(1, GK_NN_PLAIN, p, st));
     } else {
       // V = (dY.diag(g)).B with g applied to B's rows on load (no scaled copy of dY)
-      LDL_TRY(rowproj_t(M, N, r, dY, N, Bh, r, g, w.V, r, 1.f, st));
+      LDL_TRY(rowproj_t(M, N, r, dY, lddy, Bh, r, g, w.V, r, 1.f, st));
     }
     // s.V^T.X into the first nsA partials of dA
-    jobs[nj] = pk(cpp(M, K, r, X, K, w.V, r, s, nullptr, 0, 0, w.msA, w.partA, nullptr), w.pkA);
+    jobs[nj] = pk(cpp(M, K, r, X, ldx, w.V, r, s, nullptr, 0, 0, w.msA, w.partA, nullptr), w.pkA);
     ns[nj++] = w.nsA;
   } else {
     LDL_TRY(zero(w.partA, (size_t)w.nsA * K * w.rp, st));
   }
   // (2s.w.B)^T.W0 into the next nsW partials; Q = B^T.(2s.w.B)
-  jobs[nj] = pk(cpp(N, K, r, W0, K, w.wB, r, 1.f, nullptr, 0, 0, w.msW, w.partA + (size_t)w.nsA * K * w.rp, nullptr),
-                w.pkW);
+  jobs[nj] = pk(cpp(N, K, r, W0, ldw, w.wB, r, 1.f, nullptr, 0, 0, w.msW, w.partA + (size_t)w.nsA * K * w.rp,
+                    nullptr), w.pkW);
   ns[nj++] = w.nsW;
   jobs[nj] = pk(cpp(N, r, r, B, r, w.wB, r, 1.f, nullptr, 0, 0, w.msQ, w.partQ, nullptr), w.pkQ);
   ns[nj++] = w.nsQ;
@@ -621,7 +665,7 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, c
                  K, s));
   if (dbias) {
     if (M > 0) {
-      LDL_TRY(colproj(M, N, 0, dY, N, nullptr, 0, 1.f, nullptr, 0, 2, w.nsT, w.msT, w.partbias, w.csbias, st));
+      LDL_TRY(colproj(M, N, 0, dY, lddy, nullptr, 0, 1.f, nullptr, 0, 2, w.nsT, w.msT, w.partbias, w.csbias, st));
       LDL_TRY(launch_reduce_colsum(w.csbias, w.nsT, N, dbias, st));
     } else {
       LDL_TRY(zero(dbias, (size_t)N, st));
@@ -638,28 +682,31 @@ static int mlp_check(int M, int K, int H, int r) {
   return LDL_OK;
 }
 
-int swiglu_lora_mlp_fwd(int M, int K, int H, int r, float s_gate, float s_up, float s_down, const void* X,
+int swiglu_lora_mlp_fwd(int M, int K, int H, int r, float s_gate, float s_up, float s_down, const void* X, int ldx,
                         const void* Wg, const void* Ag, const void* Bg, const void* Wu, const void* Au,
-                        const void* Bu, const void* Wd, const void* Ad, const void* Bd, void* Out, void* E_save,
-                        void* Gu_save, void* H_save, float* U_save, void* ws, size_t ws_bytes, void* stream) {
+                        const void* Bu, const void* Wd, const void* Ad, const void* Bd, void* Out, int ldout,
+                        void* E_save, void* Gu_save, void* H_save, float* U_save, void* ws, size_t ws_bytes,
+                        void* stream) {
   (void)ws; (void)ws_bytes;
   if (!nonnull({Wg, Ag, Bg, Wu, Au, Bu, Wd, Ad, Bd}) || (M > 0 && !nonnull({X, Out, E_save, Gu_save, H_save, U_save})))
     return LDL_E_INVAL;
   const int chk = mlp_check(M, K, H, r);
   if (chk != LDL_OK) return chk;
+  LDL_LD(ldx, K, 8); LDL_LD(ldout, K, 8);
+  if (!fits(M, ldx, 2) || !fits(M, ldout, 2)) return LDL_E_UNSUPPORTED;
   if (!al({X, Wg, Ag, Bg, Wu, Au, Bu, Wd, Ad, Bd, Out, E_save, Gu_save, H_save, U_save})) return LDL_E_UNSUPPORTED;
   if (M == 0) return LDL_OK;
   const hipStream_t st = S(stream);
   const int r3 = 3 * r;
   // [U_g | U_u] = X.[Ag; Au]^T in one pass over X
-  LDL_TRY(rowproj(M, K, 2 * r, X, K, Ag, Au, r, K, U_save, r3, 1.f, st));
+  LDL_TRY(rowproj(M, K, 2 * r, X, ldx, Ag, Au, r, K, U_save, r3, 1.f, st));
   // gate and up projections in one GEMM (each tile holds e and u of the same hidden units
   // side by side: the four-wave dual tile, or the eight-wave one for 128 tokens or fewer or
   // hidden widths not a multiple of 128) with h = silu(e) * u formed from the fp32
   // accumulators in the epilogue
   GemmParams p = gp0();
   p.M = M; p.N = H; p.K = K;
-  p.a = X; p.lda = K; p.b0 = Wg; p.b1 = Wu; p.ldb = K; p.kseg = K;
+  p.a = X; p.lda = ldx; p.b0 = Wg; p.b1 = Wu; p.ldb = K; p.kseg = K;
   p.S = U_save; p.ld_s = r3; p.r_epi = 2 * r; p.s_epi = s_gate; p.s_epi2 = s_up;
   p.e0 = Bg; p.e1 = Bu; p.e_ldn = r; p.e_ldj = 1; p.e_jsplit = r;
   p.out = E_save; p.ldo = H; p.out2 = Gu_save; p.ldo2 = H; p.out3 = H_save; p.ldo3 = H;
@@ -671,22 +718,24 @@ int swiglu_lora_mlp_fwd(int M, int K, int H, int r, float s_gate, float s_up, fl
   q.a = H_save; q.lda = H; q.b0 = Wd; q.ldb = H; q.kseg = H;
   q.S = U_save + 2 * r; q.ld_s = r3; q.r_epi = r; q.s_epi = s_down;
   q.e0 = Bd; q.e1 = Bd; q.e_ldn = r; q.e_ldj = 1; q.e_jsplit = r;
-  q.out = Out; q.ldo = K;
+  q.out = Out; q.ldo = ldout;
   LDL_TRY(gemm_timed(0, GK_NT_PLAIN, q, st));
   return LDL_OK;
 }
 
 int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, float s_down, const void* dOut,
-                        const void* X, const void* Wg, const void* Ag, const void* Bg, const void* Wu, const void* Au,
-                        const void* Bu, const void* Wd, const void* Ad, const void* Bd, const void* E_saved,
-                        const void* Gu_saved, const void* H_saved, const float* U_saved, void* dX, float* dAg,
-                        float* dBg, float* dAu, float* dBu, float* dAd, float* dBd, void* ws, size_t ws_bytes,
-                        void* stream) {
+                        int lddout, const void* X, int ldx, const void* Wg, const void* Ag, const void* Bg,
+                        const void* Wu, const void* Au, const void* Bu, const void* Wd, const void* Ad, const void* Bd,
+                        const void* E_saved, const void* Gu_saved, const void* H_saved, const float* U_saved,
+                        void* dX, int lddx, float* dAg, float* dBg, float* dAu, float* dBu, float* dAd, float* dBd,
+                        void* ws, size_t ws_bytes, void* stream) {
   if (!nonnull({Wg, Ag, Bg, Wu, Au, Bu, Wd, Ad, Bd, dAg, dBg, dAu, dBu, dAd, dBd, ws}) ||
       (M > 0 && !nonnull({dOut, X, E_saved, Gu_saved, H_saved, U_saved})))
     return LDL_E_INVAL;
   const int chk = mlp_check(M, K, H, r);
   if (chk != LDL_OK) return chk;
+  LDL_LD(lddout, K, 8); LDL_LD(ldx, K, 8); LDL_LD(lddx, K, 8);
+  if (!fits(M, lddout, 2) || !fits(M, ldx, 2) || !fits(M, lddx, 2)) return LDL_E_UNSUPPORTED;
   if (!al({dOut, X, Wg, Ag, Bg, Wu, Au, Bu, Wd, Ad, Bd, E_saved, Gu_saved, H_saved, U_saved, dX, dAg, dBg, dAu, dBu,
            dAd, dBd, ws}))
     return LDL_E_UNSUPPORTED;
@@ -706,12 +755,12 @@ int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, fl
   const float* Ud = U_saved + 2 * r;
 
   // ---- down projection: V_d = dOut.Bd (Bd read in place as a [K, r] matrix)
-  LDL_TRY(rowproj_t(M, K, r, dOut, K, Bd, r, nullptr, w.Vd, r, 1.f, st));
+  LDL_TRY(rowproj_t(M, K, r, dOut, lddout, Bd, r, nullptr, w.Vd, r, 1.f, st));
   // ---- dH = dOut.Wd + s_d.V_d.Ad with the SwiGLU backward in the epilogue -> [dE | dGu]
   {
     GemmParams p = gp0();
     p.M = M; p.N = H; p.K = K;
-    p.a = dOut; p.lda = K; p.b0 = Wd; p.b1 = Wd; p.ldb = H; p.kseg = K;
+    p.a = dOut; p.lda = lddout; p.b0 = Wd; p.b1 = Wd; p.ldb = H; p.kseg = K;
     p.S = w.Vd; p.ld_s = r; p.r_epi = r; p.s_epi = s_down;
     p.e0 = Ad; p.e1 = Ad; p.e_ldn = 1; p.e_ldj = H; p.e_jsplit = r;
     p.aux0 = E_saved; p.ld_aux0 = H; p.aux1 = Gu_saved; p.ld_aux1 = H;
@@ -719,7 +768,7 @@ int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, fl
     LDL_TRY(launch_gemm(GK_NN_SWIGLU, p, st));
   }
   // dBd = s_d.dOut^T.U_d and dAd = s_d.V_d^T.H
-  LDL_TRY(launch_colproj2(pk(cpp(M, K, r, dOut, K, Ud, r3, 1.f, nullptr, 0, 0, w.msDd, w.partDd, nullptr), w.pkDd),
+  LDL_TRY(launch_colproj2(pk(cpp(M, K, r, dOut, lddout, Ud, r3, 1.f, nullptr, 0, 0, w.msDd, w.partDd, nullptr), w.pkDd),
                           w.nsDd,
                           pk(cpp(M, H, r, H_saved, H, w.Vd, r, 1.f, nullptr, 0, 0, w.msAd, w.partAd, nullptr), w.pkAd),
                           w.nsAd, st));
@@ -742,21 +791,21 @@ int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, fl
     p.a = w.dEGu; p.lda = 2 * H; p.b0 = Wg; p.b1 = Wu; p.ldb = K; p.kseg = H;
     p.S = w.Vgu; p.ld_s = 2 * r; p.r_epi = 2 * r; p.s_epi = 1.f;
     p.e0 = Ag; p.e1 = Au; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = r;
-    p.out = dX; p.ldo = K;
+    p.out = dX; p.ldo = lddx;
     LDL_TRY(gemm_timed(1, GK_NN_PLAIN, p, st));
   }
   // dAg, dAu = [V_g | V_u]^T.X in one pass over X
   if (w.agu_split) {
     float* partAu = w.partAgu + (size_t)w.nsAgu * K * w.rp;
     LDL_TRY(launch_colproj2(
-        pk(cpp(M, K, r, X, K, w.Vgu, 2 * r, 1.f, nullptr, 0, 0, w.msAgu, w.partAgu, nullptr), w.pkAgu), w.nsAgu,
-        pk(cpp(M, K, r, X, K, w.Vgu + r, 2 * r, 1.f, nullptr, 0, 0, w.msAgu, partAu, nullptr),
+        pk(cpp(M, K, r, X, ldx, w.Vgu, 2 * r, 1.f, nullptr, 0, 0, w.msAgu, w.partAgu, nullptr), w.pkAgu), w.nsAgu,
+        pk(cpp(M, K, r, X, ldx, w.Vgu + r, 2 * r, 1.f, nullptr, 0, 0, w.msAgu, partAu, nullptr),
            w.pkAgu + colproj_spk_words(M, r)),
         w.nsAgu, st));
     LDL_TRY(launch_reduce2(rdp(r, K, w.partAgu, (size_t)K * w.rp, w.nsAgu, w.rp, true, 1.f, dAg, K),
                            rdp(r, K, partAu, (size_t)K * w.rp, w.nsAgu, w.rp, true, 1.f, dAu, K), st));
   } else {
-    LDL_TRY(colproj(M, K, 2 * r, X, K, w.Vgu, 2 * r, 1.f, nullptr, 0, 0, w.nsAgu, w.msAgu, w.partAgu, nullptr, st,
+    LDL_TRY(colproj(M, K, 2 * r, X, ldx, w.Vgu, 2 * r, 1.f, nullptr, 0, 0, w.nsAgu, w.msAgu, w.partAgu, nullptr, st,
                     w.pkAgu));
     LDL_TRY(launch_reduce2(rdp(r, K, w.partAgu, (size_t)K * w.rp2, w.nsAgu, w.rp2, true, 1.f, dAg, K),
                            rdp(r, K, w.partAgu + r, (size_t)K * w.rp2, w.nsAgu, w.rp2, true, 1.f, dAu, K), st));
@@ -765,43 +814,52 @@ int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, fl
 }
 
 // =========================================================================== W8A8
-int w8a8_quantize_weight(int N, int K, int dtype, const void* W0, int8_t* Wq, float* sw, void* stream) {
+int w8a8_quantize_weight(int N, int K, int dtype, const void* W0, int ldw, int8_t* Wq, float* sw, void* stream) {
   if (!nonnull({W0, Wq, sw})) return LDL_E_INVAL;
   if (N <= 0 || K <= 0) return LDL_E_INVAL;
   if (dtype != LDL_F32 && dtype != LDL_BF16) return LDL_E_INVAL;
   if (K % 8 || !al({W0, Wq, sw})) return LDL_E_UNSUPPORTED;
-  LDL_TRY(launch_quantize_rows(W0, dtype == LDL_F32, N, K, Wq, sw, S(stream)));
+  LDL_LD(ldw, K, dtype == LDL_BF16 ? 8 : 1);
+  if (!fits(N, ldw, dtype == LDL_BF16 ? 2 : 4) || !fits(N, K, 1)) return LDL_E_UNSUPPORTED;
+  LDL_TRY(launch_quantize_rows(W0, dtype == LDL_F32, N, K, ldw, Wq, sw, S(stream)));
   return LDL_OK;
 }
 
-int w8a8_quantize_rows(int M, int K, const void* X, int8_t* Xq, float* sx, void* stream) {
+int w8a8_quantize_rows(int M, int K, const void* X, int ldx, int8_t* Xq, float* sx, void* stream) {
   if (M > 0 && !nonnull({X, Xq, sx})) return LDL_E_INVAL;
   if (M < 0 || K <= 0) return LDL_E_INVAL;
   if (K % 8 || !al({X, Xq, sx})) return LDL_E_UNSUPPORTED;
-  LDL_TRY(launch_quantize_rows(X, 0, M, K, Xq, sx, S(stream)));
+  LDL_LD(ldx, K, 8);
+  if (!fits(M, ldx, 2)) return LDL_E_UNSUPPORTED;
+  LDL_TRY(launch_quantize_rows(X, 0, M, K, ldx, Xq, sx, S(stream)));
   return LDL_OK;
 }
 
-int int8_gemm_raw(int M, int N, int K, const int8_t* Xq, const int8_t* Wq, int32_t* C, void* stream) {
+int int8_gemm_raw(int M, int N, int K, const int8_t* Xq, int ldxq, const int8_t* Wq, int ldwq, int32_t* C, int ldc,
+                  void* stream) {
   if (!nonnull({Wq}) || (M > 0 && !nonnull({Xq, C}))) return LDL_E_INVAL;
   if (M < 0 || N <= 0 || K <= 0) return LDL_E_INVAL;
   if (N % 64 || K % 128 || !al({Xq, Wq, C})) return LDL_E_UNSUPPORTED;
-  if (!small(M + 256, K, 1) || !small(N, K, 1) || !small(M, N, 4)) return LDL_E_UNSUPPORTED;
+  LDL_LD(ldxq, K, 16); LDL_LD(ldwq, K, 16); LDL_LD(ldc, N, 4);
+  if (!fits(M, ldxq, 1) || !fits(N, ldwq, 1) || !fits(M, ldc, 4)) return LDL_E_UNSUPPORTED;
   GemmParams p = gp0();
-  p.M = M; p.N = N; p.K = K; p.a = Xq; p.lda = K; p.b0 = Wq; p.ldb = K; p.kseg = K;
-  p.out = C; p.ldo = N;
+  p.M = M; p.N = N; p.K = K; p.a = Xq; p.lda = ldxq; p.b0 = Wq; p.ldb = ldwq; p.kseg = K;
+  p.out = C; p.ldo = ldc;
   LDL_TRY(launch_gemm(GK_NT_I8_RAW, p, S(stream)));
   return LDL_OK;
 }
 
-int w8a8_lora_linear_fwd(int M, int N, int K, int r, float s, const void* X, const int8_t* Wq, const float* sw,
-                         const void* A, const void* B, const void* bias, void* Y, int8_t* Xq_save, float* sx_save,
-                         float* U_save, void* ws, size_t ws_bytes, void* stream) {
+int w8a8_lora_linear_fwd(int M, int N, int K, int r, float s, const void* X, int ldx, const int8_t* Wq, int ldw,
+                         const float* sw, const void* A, const void* B, const void* bias, void* Y, int ldy,
+                         int8_t* Xq_save, float* sx_save, float* U_save, int ldu, void* ws, size_t ws_bytes,
+                         void* stream) {
   if (!nonnull({Wq, sw, A, B}) || (M > 0 && !nonnull({X, Y}))) return LDL_E_INVAL;
   if ((Xq_save == nullptr) != (sx_save == nullptr)) return LDL_E_INVAL;
   const int chk = check_bf16_layer(M, N, K, r);
   if (chk != LDL_OK) return chk;
   if (K % 128) return LDL_E_UNSUPPORTED;
+  LDL_LD(ldx, K, 8); LDL_LD(ldw, K, 16); LDL_LD(ldy, N, 8); LDL_LD(ldu, r, 4);
+  if (!fits(M, ldx, 2) || !fits(N, ldw, 1) || !fits(M, ldy, 2) || !fits(M, ldu, 4)) return LDL_E_UNSUPPORTED;
   if (!al({X, Wq, sw, A, B, bias, Y, Xq_save, sx_save, U_save, ws})) return LDL_E_UNSUPPORTED;
   if (ldl_workspace_bytes(LDL_OP_W8A8_FWD, M, N, K, r, LDL_BF16) > ws_bytes) return LDL_E_WORKSPACE;
   if (!ws) return LDL_E_INVAL;
@@ -812,27 +870,32 @@ int w8a8_lora_linear_fwd(int M, int N, int K, int r, float s, const void* X, con
   int8_t* Xqw = wb.take<int8_t>((size_t)M * K);
   float* sxw = wb.take<float>((size_t)M);
   float* U = U_save ? U_save : Uw;
+  const int lu = U_save ? ldu : r;
   int8_t* Xq = Xq_save ? Xq_save : Xqw;
   float* sx = sx_save ? sx_save : sxw;
-  LDL_TRY(launch_quantize_rows(X, 0, M, K, Xq, sx, st));
-  LDL_TRY(rowproj(M, K, r, X, K, A, nullptr, r, K, U, r, 1.f, st));
+  LDL_TRY(launch_quantize_rows(X, 0, M, K, ldx, Xq, sx, st));
+  LDL_TRY(rowproj(M, K, r, X, ldx, A, nullptr, r, K, U, lu, 1.f, st));
   GemmParams p = gp0();
   p.M = M; p.N = N; p.K = K;
-  p.a = Xq; p.lda = K; p.b0 = Wq; p.ldb = K; p.kseg = K;
+  p.a = Xq; p.lda = K; p.b0 = Wq; p.ldb = ldw; p.kseg = K;
   p.row_scale = sx; p.col_scale = sw;
-  p.S = U; p.ld_s = r; p.r_epi = r; p.s_epi = s;
+  p.S = U; p.ld_s = lu; p.r_epi = r; p.s_epi = s;
   p.e0 = B; p.e1 = B; p.e_ldn = r; p.e_ldj = 1; p.e_jsplit = r;
-  p.bias = bias; p.out = Y; p.ldo = N;
+  p.bias = bias; p.out = Y; p.ldo = ldy;
   LDL_TRY(gemm_timed(0, GK_NT_I8_DEQ, p, st));
   return LDL_OK;
 }
 
-int w8a8_lora_linear_bwd(int M, int N, int K, int r, float s, const void* dY, const void* X, const int8_t* Wq,
-                         const float* sw, const void* A, const void* B, const float* U_saved, void* dX, float* dA,
-                         float* dB, void* ws, size_t ws_bytes, void* stream) {
+int w8a8_lora_linear_bwd(int M, int N, int K, int r, float s, const void* dY, int lddy, const void* X, int ldx,
+                         const int8_t* Wq, int ldw, const float* sw, const void* A, const void* B,
+                         const float* U_saved, int ldu, void* dX, int lddx, float* dA, float* dB, void* ws,
+                         size_t ws_bytes, void* stream) {
   if (!nonnull({Wq, sw, A, B, dA, dB, ws}) || (M > 0 && !nonnull({dY, X}))) return LDL_E_INVAL;
   const int chk = check_bf16_layer(M, N, K, r);
   if (chk != LDL_OK) return chk;
+  LDL_LD(lddy, N, 8); LDL_LD(ldx, K, 8); LDL_LD(ldw, K, 16); LDL_LD(ldu, r, 4); LDL_LD(lddx, K, 8);
+  if (!fits(M, lddy, 2) || !fits(M, ldx, 2) || !fits(N, ldw, 1) || !fits(M, ldu, 4) || !fits(M, lddx, 2))
+    return LDL_E_UNSUPPORTED;
   if (!al({dY, X, Wq, sw, A, B, U_saved, dX, dA, dB, ws})) return LDL_E_UNSUPPORTED;
   if (ldl_workspace_bytes(LDL_OP_W8A8_BWD, M, N, K, r, LDL_BF16) > ws_bytes) return LDL_E_WORKSPACE;
   const hipStream_t st = S(stream);
@@ -844,23 +907,25 @@ int w8a8_lora_linear_bwd(int M, int N, int K, int r, float s, const void* dY, co
   Bump wb(ws);
   LoraBwdWs w = plan_lora_bwd(wb, M, N, K, r, true);
   const float* U = U_saved;
+  int lu = ldu;
   if (!U) {
-    LDL_TRY(rowproj(M, K, r, X, K, A, nullptr, r, K, w.U, r, 1.f, st));
+    LDL_TRY(rowproj(M, K, r, X, ldx, A, nullptr, r, K, w.U, r, 1.f, st));
     U = w.U;
+    lu = r;
   }
-  LDL_TRY(rowproj_t(M, N, r, dY, N, B, r, nullptr, w.V, r, 1.f, st));
+  LDL_TRY(rowproj_t(M, N, r, dY, lddy, B, r, nullptr, w.V, r, 1.f, st));
   if (dX) {
     GemmParams p = gp0();
     p.M = M; p.N = K; p.K = N;
-    p.a = dY; p.lda = N; p.a_colscale = sw; p.b0 = Wq; p.b1 = Wq; p.ldb = K; p.kseg = N;
+    p.a = dY; p.lda = lddy; p.a_colscale = sw; p.b0 = Wq; p.b1 = Wq; p.ldb = ldw; p.kseg = N;
     p.S = w.V; p.ld_s = r; p.r_epi = r; p.s_epi = s;
     p.e0 = A; p.e1 = A; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = r;
-    p.out = dX; p.ldo = K;
+    p.out = dX; p.ldo = lddx;
     LDL_TRY(gemm_timed(1, GK_NN_I8_SCALE, p, st));
   }
-  LDL_TRY(launch_colproj2(pk(cpp(M, N, r, dY, N, U, r, 1.f, nullptr, 0, 0, w.msB, w.partB, nullptr), w.pkB), w.nsB,
-                          pk(cpp(M, K, r, X, K, w.V, r, 1.f, nullptr, 0, 0, w.msA, w.partA, nullptr), w.pkA), w.nsA,
-                          st));
+  LDL_TRY(launch_colproj2(
+      pk(cpp(M, N, r, dY, lddy, U, lu, 1.f, nullptr, 0, 0, w.msB, w.partB, nullptr), w.pkB), w.nsB,
+      pk(cpp(M, K, r, X, ldx, w.V, r, 1.f, nullptr, 0, 0, w.msA, w.partA, nullptr), w.pkA), w.nsA, st));
   LDL_TRY(launch_reduce2(rdp(N, r, w.partB, (size_t)N * w.rp, w.nsB, w.rp, false, s, dB, r),
                          rdp(r, K, w.partA, (size_t)K * w.rp, w.nsA, w.rp, true, s, dA, K), st));
   return LDL_OK;

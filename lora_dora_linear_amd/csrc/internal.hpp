@@ -10,6 +10,7 @@ struct RowProjParams {
   int M, K, R, R0;                 // Q rows j < R0 come from q0, rows j >= R0 from q1
   const uint16_t* P; int ldp;      // [M, K] bf16; rows m >= p_split come from P1 (row m - p_split)
   const uint16_t* P1; int p_split; // P1 == nullptr: one segment (p_split = M)
+  int ldp1;                        // leading dimension of P1
   const uint16_t* q0; const uint16_t* q1; int ldq;
   int q_trans;                     // 1: Q(j, k) = q0[k * ldq + j] (a [K, R] matrix such as lora_up B)
   const float* q_kscale;           // q_trans only, optional: Q(j, k) *= q_kscale[k] (rounded to bf16)
@@ -70,10 +71,11 @@ hipError_t launch_reduce_colsum(const float* cspart, int nsplit, int C, float* o
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t st);
 
 // DoRA helpers
-hipError_t launch_rowsumsq(const void* W0, int dtype_bf16, int N, int K, float* out, hipStream_t st);
+hipError_t launch_rowsumsq(const void* W0, int dtype_bf16, int N, int K, int ldw, float* out, hipStream_t st);
 hipError_t launch_dora_norm(int N, int r, float s, float eps, const float* w0_sumsq, const float* P,
                             const float* G, const uint16_t* B, const float* m, float* norm, float* g, hipStream_t st);
-hipError_t launch_scale_cols(const void* in, int M, int N, int ld, const float* g, void* out, hipStream_t st);
+hipError_t launch_scale_cols(const void* in, int M, int N, int ld, const float* g, void* out, int ldo,
+                             hipStream_t st);
 
 // SwiGLU backward over bf16 [M, N] arrays: dh (read from dE) -> de in place, du written
 hipError_t launch_swiglu_bwd(void* dE, int ld_de, const void* E, int ld_e, const void* U, int ld_u, void* dU,
@@ -84,7 +86,8 @@ hipError_t launch_dora_finalize(int N, int r, float s, float eps, const float* p
                                 float* dB, float* dm, float* wB, hipStream_t st);
 
 // W8A8 helpers
-hipError_t launch_quantize_rows(const void* X, int in_f32, int M, int K, int8_t* q, float* scale, hipStream_t st);
+hipError_t launch_quantize_rows(const void* X, int in_f32, int M, int K, int ldx, int8_t* q, float* scale,
+                                hipStream_t st);
 
 // fp32 path: C[m, n] = alpha * sum_k A(m, k) B(k, n) + beta * C[m, n] (+ bias[n])
 struct F32GemmParams {
@@ -96,6 +99,6 @@ struct F32GemmParams {
   const float* bias;
 };
 hipError_t launch_f32_gemm(const F32GemmParams& p, hipStream_t st);
-hipError_t launch_f32_colsum(const float* X, int M, int N, float* out, hipStream_t st);
+hipError_t launch_f32_colsum(const float* X, int M, int N, int ld, float* out, hipStream_t st);
 
 }  // namespace ldl

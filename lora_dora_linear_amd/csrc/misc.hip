@@ -20,13 +20,13 @@ __device__ __forceinline__ float wave_max(float v) {
 // weight is kept from call to call; only the two rank-sized terms of the norm change per step
 // ("LoRA/DoRA fast forward: no weight materialization", commit message).
 template <bool BF16>
-__global__ __launch_bounds__(256) void rowsumsq_kernel(const void* W0, int N, int K, float* out) {
+__global__ __launch_bounds__(256) void rowsumsq_kernel(const void* W0, int N, int K, int ldw, float* out) {
   const int lane = threadIdx.x & 63;
   const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= N) return;
   float acc = 0.f;
   if (BF16) {
-    const uint16_t* row = static_cast<const uint16_t*>(W0) + (size_t)n * K;
+    const uint16_t* row = static_cast<const uint16_t*>(W0) + (size_t)n * ldw;
     for (int k = lane * 8; k < K; k += 512) {
       const u32x4 v = ld16(row + k);
 #pragma unroll
@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void rowsumsq_kernel(const void* W0, int N, in
       }
     }
   } else {
-    const float* row = static_cast<const float*>(W0) + (size_t)n * K;
+    const float* row = static_cast<const float*>(W0) + (size_t)n * ldw;
     for (int k = lane; k < K; k += 64) acc += row[k] * row[k];
   }
   acc = wave_sum(acc);
@@ -157,24 +157,25 @@ __global__ __launch_bounds__(256) void dora_finalize_kernel(int N, int r, float 
 // written once so the input-gradient product runs as a plain bf16 GEMM (the same values
 // a fragment-wise scaling would feed the MFMAs).  8 columns per thread, rows of ld elements.
 __global__ __launch_bounds__(256) void scale_cols_kernel(const uint16_t* in, int M, int N, int ld, const float* g,
-                                                         uint16_t* out) {
+                                                         uint16_t* out, int ldo) {
   const int per_row = N / 8;
   const size_t total = (size_t)M * per_row;
   for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (size_t)gridDim.x * blockDim.x) {
     const int m = (int)(t / per_row), c = (int)(t % per_row) * 8;
     const u32x4 v = ld16(in + (size_t)m * ld + c);
     const f32x4 s0 = *reinterpret_cast<const f32x4*>(g + c), s1 = *reinterpret_cast<const f32x4*>(g + c + 4);
-    st16(out + (size_t)m * ld + c, scale_bf16x8(v, s0, s1));
+    st16(out + (size_t)m * ldo + c, scale_bf16x8(v, s0, s1));
   }
 }
 
-hipError_t launch_scale_cols(const void* in, int M, int N, int ld, const float* g, void* out, hipStream_t st) {
+hipError_t launch_scale_cols(const void* in, int M, int N, int ld, const float* g, void* out, int ldo,
+                             hipStream_t st) {
   if (M <= 0) return hipSuccess;
   const size_t total = (size_t)M * (N / 8);
   size_t blocks = (total + 255) / 256;
   if (blocks > 2048) blocks = 2048;
   hipLaunchKernelGGL(scale_cols_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const uint16_t*>(in), M,
-                     N, ld, g, static_cast<uint16_t*>(out));
+                     N, ld, g, static_cast<uint16_t*>(out), ldo);
   return hipGetLastError();
 }
 
@@ -217,10 +218,10 @@ hipError_t launch_swiglu_bwd(void* dE, int ld_de, const void* E, int ld_e, const
   return hipGetLastError();
 }
 
-hipError_t launch_rowsumsq(const void* W0, int dtype_bf16, int N, int K, float* out, hipStream_t st) {
+hipError_t launch_rowsumsq(const void* W0, int dtype_bf16, int N, int K, int ldw, float* out, hipStream_t st) {
   const dim3 grid((N + 3) / 4), block(256);
-  if (dtype_bf16) hipLaunchKernelGGL(rowsumsq_kernel<true>, grid, block, 0, st, W0, N, K, out);
-  else hipLaunchKernelGGL(rowsumsq_kernel<false>, grid, block, 0, st, W0, N, K, out);
+  if (dtype_bf16) hipLaunchKernelGGL(rowsumsq_kernel<true>, grid, block, 0, st, W0, N, K, ldw, out);
+  else hipLaunchKernelGGL(rowsumsq_kernel<false>, grid, block, 0, st, W0, N, K, ldw, out);
   return hipGetLastError();
 }
 
@@ -244,16 +245,17 @@ hipError_t launch_dora_finalize(int N, int r, float s, float eps, const float* p
 // Symmetric per-row codes: scale = absmax / 127 (fp32), q = clamp(rint(x / scale), +-127)
 // with the quotient in fp32 and ties to even; scale 0 -> q = 0.  One wave per row.
 template <bool F32IN>
-__global__ __launch_bounds__(256) void quantize_rows_kernel(const void* X, int M, int K, int8_t* q, float* scale) {
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const void* X, int M, int K, int ldx, int8_t* q,
+                                                            float* scale) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
   float amax = 0.f;
   if (F32IN) {
-    const float* x = static_cast<const float*>(X) + (size_t)row * K;
+    const float* x = static_cast<const float*>(X) + (size_t)row * ldx;
     for (int k = lane; k < K; k += 64) amax = fmaxf(amax, fabsf(x[k]));
   } else {
-    const uint16_t* x = static_cast<const uint16_t*>(X) + (size_t)row * K;
+    const uint16_t* x = static_cast<const uint16_t*>(X) + (size_t)row * ldx;
     for (int k = lane * 8; k < K; k += 512) {
       const u32x4 v = ld16(x + k);
 #pragma unroll
@@ -271,10 +273,10 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* X, int M
     return (int)t;
   };
   if (F32IN) {
-    const float* x = static_cast<const float*>(X) + (size_t)row * K;
+    const float* x = static_cast<const float*>(X) + (size_t)row * ldx;
     for (int k = lane; k < K; k += 64) qrow[k] = (int8_t)code(x[k]);
   } else {
-    const uint16_t* x = static_cast<const uint16_t*>(X) + (size_t)row * K;
+    const uint16_t* x = static_cast<const uint16_t*>(X) + (size_t)row * ldx;
     for (int k = lane * 8; k < K; k += 512) {
       const u32x4 v = ld16(x + k);
       u32x2 o;
@@ -294,14 +296,14 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* X, int M
 // bf16 rows of K <= 512 QV elements (K a multiple of 512): the same codes from one read of
 // the row, kept in registers (QV 16-byte pieces per lane) between the absmax and the codes.
 constexpr int kQuantRegPieces = 16;
-__global__ __launch_bounds__(256) void quantize_rows_reg_kernel(const uint16_t* X, int M, int K, int8_t* q,
+__global__ __launch_bounds__(256) void quantize_rows_reg_kernel(const uint16_t* X, int M, int K, int ldx, int8_t* q,
                                                                 float* scale) {
   constexpr int QV = kQuantRegPieces;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
   const int nv = K / 512;
-  const uint16_t* x = X + (size_t)row * K + lane * 8;
+  const uint16_t* x = X + (size_t)row * ldx + lane * 8;
   u32x4 v[QV];
 #pragma unroll
   for (int i = 0; i < QV; ++i) v[i] = i < nv ? ld16(x + i * 512) : u32x4{0u, 0u, 0u, 0u};
@@ -333,14 +335,17 @@ __global__ __launch_bounds__(256) void quantize_rows_reg_kernel(const uint16_t* 
   }
 }
 
-hipError_t launch_quantize_rows(const void* X, int in_f32, int M, int K, int8_t* q, float* scale, hipStream_t st) {
+// X rows of leading dimension ldx (16-byte aligned rows for bf16), codes written as dense [M, K].
+hipError_t launch_quantize_rows(const void* X, int in_f32, int M, int K, int ldx, int8_t* q, float* scale,
+                                hipStream_t st) {
   if (M <= 0) return hipSuccess;
   const dim3 grid((M + 3) / 4), block(256);
-  if (in_f32) hipLaunchKernelGGL(quantize_rows_kernel<true>, grid, block, 0, st, X, M, K, q, scale);
+  if (in_f32) hipLaunchKernelGGL(quantize_rows_kernel<true>, grid, block, 0, st, X, M, K, ldx, q, scale);
   else if (K % 512 == 0 && K <= 512 * kQuantRegPieces &&
            (reinterpret_cast<uintptr_t>(X) & 15) == 0 && (reinterpret_cast<uintptr_t>(q) & 7) == 0)
-    hipLaunchKernelGGL(quantize_rows_reg_kernel, grid, block, 0, st, static_cast<const uint16_t*>(X), M, K, q, scale);
-  else hipLaunchKernelGGL(quantize_rows_kernel<false>, grid, block, 0, st, X, M, K, q, scale);
+    hipLaunchKernelGGL(quantize_rows_reg_kernel, grid, block, 0, st, static_cast<const uint16_t*>(X), M, K, ldx, q,
+                       scale);
+  else hipLaunchKernelGGL(quantize_rows_kernel<false>, grid, block, 0, st, X, M, K, ldx, q, scale);
   return hipGetLastError();
 }
 
@@ -395,11 +400,11 @@ __global__ __launch_bounds__(256) void f32_gemm_kernel(const F32GemmParams p) {
   }
 }
 
-__global__ void f32_colsum_kernel(const float* X, int M, int N, float* out) {
+__global__ void f32_colsum_kernel(const float* X, int M, int N, int ld, float* out) {
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
   if (n >= N) return;
   float acc = 0.f;
-  for (int m = 0; m < M; ++m) acc += X[(size_t)m * N + n];
+  for (int m = 0; m < M; ++m) acc += X[(size_t)m * ld + n];
   out[n] = acc;
 }
 
@@ -410,8 +415,8 @@ hipError_t launch_f32_gemm(const F32GemmParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_f32_colsum(const float* X, int M, int N, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(f32_colsum_kernel, dim3((N + 255) / 256), dim3(256), 0, st, X, M, N, out);
+hipError_t launch_f32_colsum(const float* X, int M, int N, int ld, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(f32_colsum_kernel, dim3((N + 255) / 256), dim3(256), 0, st, X, M, N, ld, out);
   return hipGetLastError();
 }
 

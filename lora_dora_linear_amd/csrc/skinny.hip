@@ -35,7 +35,7 @@ __global__ __launch_bounds__(512) void rowproj_kernel(const RowProjParams p) {
   const int m0 = blockIdx.x * 16;
   const int m = m0 + lr;
   const bool mval = m < p.M;
-  const uint16_t* prow = (p.P1 != nullptr && m >= p.p_split ? p.P1 + (size_t)(m - p.p_split) * p.ldp
+  const uint16_t* prow = (p.P1 != nullptr && m >= p.p_split ? p.P1 + (size_t)(m - p.p_split) * p.ldp1
                                                              : p.P + (size_t)(mval ? m : 0) * p.ldp) + lq * 8;
 
   const uint16_t* qrow[NB];
@@ -176,9 +176,9 @@ __global__ __launch_bounds__(256) void rowstream_kernel(const RowProjParams p) {
   const int nch = (p.K + KC - 1) / KC;
   const bool tq = p.q_trans != 0;
 
-  const uint32_t ldp_b = (uint32_t)p.ldp * 2u, ldq_b = (uint32_t)p.ldq * 2u;
   // a block's BMR rows lie in one P segment (the split is a multiple of BMR)
   const bool seg1 = p.P1 != nullptr && m0 >= p.p_split;
+  const uint32_t ldp_b = (uint32_t)(seg1 ? p.ldp1 : p.ldp) * 2u, ldq_b = (uint32_t)p.ldq * 2u;
   const int pm0 = seg1 ? m0 - p.p_split : m0;
   const __amdgpu_buffer_rsrc_t rs_p = seg1 ? make_rsrc(p.P1, (uint32_t)(p.M - p.p_split) * ldp_b)
                                            : make_rsrc(p.P, (uint32_t)(p.P1 != nullptr ? p.p_split : p.M) * ldp_b);
@@ -779,7 +779,7 @@ static bool rowstream_ok(const RowProjParams& p, int rp) {
   const int rl = rp <= 32 ? 1024 : (rp == 64 ? 512 : 256);
   const int rows_per_inst = 1024 / rl;
   if (p.ldp % 8 || (((uintptr_t)p.P) & 15) || (((uintptr_t)p.q0) & 15)) return false;
-  if (p.P1 != nullptr && (p.p_split % 16 || (((uintptr_t)p.P1) & 15))) return false;
+  if (p.P1 != nullptr && (p.p_split % 16 || p.ldp1 % 8 || (((uintptr_t)p.P1) & 15))) return false;
   if (p.q_kscale && (((uintptr_t)p.q_kscale) & 15)) return false;
   if (p.q_trans) return p.R % 4 == 0 && p.R0 == p.R;
   if (p.ldq % 8 || (((uintptr_t)p.q1) & 15)) return false;

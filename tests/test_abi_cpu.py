@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     for n in ("lora_linear_fwd", "lora_linear_bwd", "dora_linear_fwd", "dora_linear_bwd", "dora_prepare",
               "swiglu_lora_mlp_fwd", "swiglu_lora_mlp_bwd", "w8a8_lora_linear_fwd", "w8a8_lora_linear_bwd",
               "w8a8_quantize_weight", "w8a8_quantize_rows", "int8_gemm_raw", "ldl_workspace_bytes",
-              "ldl_status_string", "dora_state_floats", "ldl_set_tuning", "ldl_version"):
+              "ldl_status_string", "dora_state_floats", "ldl_set_tuning", "ldl_version", "lora_linear_bwd_noalloc",
+              "ldl_noalloc_scratch_bytes"):
         assert n in names, n
 
 
@@ -60,7 +61,7 @@ def test_workspace_sizes(L):
     assert L.ldl_workspace_bytes(1, -1, 64, 64, 16, 1) == 0
     assert L.ldl_workspace_bytes(99, 64, 64, 64, 16, 1) == 0
     assert L.dora_state_floats(3072, 32) == 2 * 3072 + 3072 * 32 + 32 * 32
-    # the backward needs at least V (M x r fp32) and B^T
+    # the backward needs at least V (M x r fp32)
     assert L.ldl_workspace_bytes(1, 4096, 4096, 4096, 16, 1) >= 4096 * 16 * 4
 
 
@@ -81,65 +82,136 @@ MIS = ctypes.c_void_p(0x100008)   # not 16-byte aligned
 NUL = None
 
 
+def lora_fwd_args(M=64, N=64, K=64, r=16, dtype=1, **kw):
+    a = dict(X=P, ldx=0, W0=P, ldw=0, A=P, B=P, bias=NUL, Y=P, ldy=0, U=P, ldu=0, ws=P, nws=1 << 20)
+    a.update(kw)
+    return (M, N, K, r, 0.5, dtype, a["X"], a["ldx"], a["W0"], a["ldw"], a["A"], a["B"], a["bias"], a["Y"],
+            a["ldy"], a["U"], a["ldu"], a["ws"], a["nws"], NUL)
+
+
+def lora_bwd_args(L, M=64, N=64, K=64, r=16, dtype=1, **kw):
+    need = L.ldl_workspace_bytes(1, M, N, K, r, dtype) if M >= 0 else 0
+    a = dict(dY=P, lddy=0, X=P, ldx=0, W0=P, ldw=0, A=P, B=P, U=NUL, ldu=0, dX=P, lddx=0, dA=P, dB=P, db=NUL,
+             ws=P, nws=need)
+    a.update(kw)
+    return (M, N, K, r, 0.5, dtype, a["dY"], a["lddy"], a["X"], a["ldx"], a["W0"], a["ldw"], a["A"], a["B"],
+            a["U"], a["ldu"], a["dX"], a["lddx"], a["dA"], a["dB"], a["db"], a["ws"], a["nws"], NUL)
+
+
 def test_lora_fwd_validation(L):
     f = L.lora_linear_fwd
-    # null weight
-    assert f(64, 64, 64, 16, 0.5, 1, P, NUL, P, P, NUL, P, P, P, 1 << 20, NUL) == INVAL
-    # bad dtype, negative sizes
-    assert f(64, 64, 64, 16, 0.5, 7, P, P, P, P, NUL, P, P, P, 1 << 20, NUL) == INVAL
-    assert f(-1, 64, 64, 16, 0.5, 1, P, P, P, P, NUL, P, P, P, 1 << 20, NUL) == INVAL
-    assert f(64, 64, 64, 0, 0.5, 1, P, P, P, P, NUL, P, P, P, 1 << 20, NUL) == INVAL
-    # shapes the bf16 kernels do not take
-    assert f(64, 100, 64, 16, 0.5, 1, P, P, P, P, NUL, P, P, P, 1 << 20, NUL) == UNSUP
-    assert f(64, 64, 96, 16, 0.5, 1, P, P, P, P, NUL, P, P, P, 1 << 20, NUL) == UNSUP
-    assert f(64, 64, 64, 129, 0.5, 1, P, P, P, P, NUL, P, P, P, 1 << 20, NUL) == UNSUP
-    # misaligned pointer
-    assert f(64, 64, 64, 16, 0.5, 1, MIS, P, P, P, NUL, P, P, P, 1 << 20, NUL) == UNSUP
-    # no U_save and no workspace
-    assert f(64, 64, 64, 16, 0.5, 1, P, P, P, P, NUL, P, NUL, NUL, 0, NUL) == WS
+    assert f(*lora_fwd_args(W0=NUL)) == INVAL                          # null weight
+    assert f(*lora_fwd_args(dtype=7)) == INVAL                         # bad dtype
+    assert f(*lora_fwd_args(M=-1)) == INVAL
+    assert f(*lora_fwd_args(r=0)) == INVAL
+    assert f(*lora_fwd_args(N=100)) == UNSUP                           # shapes the bf16 kernels do not take
+    assert f(*lora_fwd_args(K=96)) == UNSUP
+    assert f(*lora_fwd_args(r=129)) == UNSUP
+    assert f(*lora_fwd_args(X=MIS)) == UNSUP                           # misaligned pointer
+    assert f(*lora_fwd_args(U=NUL, ws=NUL, nws=0)) == WS               # no U_save and no workspace
+
+
+def test_leading_dimension_validation(L):
+    f = L.lora_linear_fwd
+    # below the row length: invalid; not a whole number of 16-byte groups: unsupported
+    assert f(*lora_fwd_args(ldx=32)) == INVAL
+    assert f(*lora_fwd_args(ldw=-8)) == INVAL
+    assert f(*lora_fwd_args(ldy=63)) == INVAL
+    assert f(*lora_fwd_args(ldu=8)) == INVAL
+    assert f(*lora_fwd_args(ldx=68)) == UNSUP
+    assert f(*lora_fwd_args(ldy=100)) == UNSUP
+    assert f(*lora_fwd_args(ldu=18)) == UNSUP
+    # the fp32 path takes any leading dimension at least the row length (the call then stops
+    # at the missing workspace, before anything is enqueued)
+    assert f(*lora_fwd_args(dtype=0, ldx=97, ldy=101, ldw=96, N=100, K=96, U=NUL, ldu=0, ws=NUL, nws=0)) == WS
+    assert f(*lora_fwd_args(ldx=72, ldy=80, ldw=128, U=NUL, ws=NUL, nws=0)) == WS
+    # a leading dimension whose rows reach past 2 GiB
+    assert f(*lora_fwd_args(M=70000, ldx=1 << 15, K=64)) == UNSUP
+    b = L.lora_linear_bwd
+    assert b(*lora_bwd_args(L, lddy=56)) == INVAL
+    assert b(*lora_bwd_args(L, lddx=60)) == INVAL
+    assert b(*lora_bwd_args(L, lddx=72, ws=NUL)) == INVAL               # valid ld, then the null workspace
+    assert b(*lora_bwd_args(L, lddy=66)) == UNSUP
+    d = L.dora_prepare
+    assert d(64, 64, 1, P, 32, P, NUL) == INVAL
+    assert d(64, 64, 1, P, 68, P, NUL) == UNSUP
+    q = L.w8a8_quantize_rows
+    assert q(64, 128, P, 120, P, P, NUL) == INVAL
+    assert q(64, 128, P, 132, P, P, NUL) == UNSUP
+    r = L.int8_gemm_raw
+    assert r(64, 128, 128, P, 136, P, 0, P, 0, NUL) == UNSUP           # int8 rows: multiples of 16 bytes
+    assert r(64, 128, 128, P, 0, P, 0, P, 100, NUL) == INVAL
 
 
 def test_lora_bwd_validation(L):
     f = L.lora_linear_bwd
+    assert f(*lora_bwd_args(L, dA=NUL)) == INVAL
     need = L.ldl_workspace_bytes(1, 64, 64, 64, 16, 1)
-    assert f(64, 64, 64, 16, 0.5, 1, P, P, P, P, P, NUL, P, NUL, P, NUL, P, need, NUL) == INVAL  # dA null
-    assert f(64, 64, 64, 16, 0.5, 1, P, P, P, P, P, NUL, P, P, P, NUL, P, need - 256, NUL) == WS
-    assert f(64, 64, 72, 16, 0.5, 1, P, P, P, P, P, NUL, P, P, P, NUL, P, need, NUL) == UNSUP
+    assert f(*lora_bwd_args(L, nws=need - 256)) == WS
+    assert f(*lora_bwd_args(L, K=72)) == UNSUP
+    n = L.lora_linear_bwd_noalloc
+    cap = L.ldl_noalloc_scratch_bytes()
+    assert cap == 32 << 20
+    big = lora_bwd_args(L, M=16384, N=8192, K=8192, r=128)
+    assert L.ldl_workspace_bytes(1, 16384, 8192, 8192, 128, 1) > cap
+    assert n(*(big[:21] + (NUL,))) == WS                                # refused before any HIP call
+
+
+def dora_fwd_args(**kw):
+    a = dict(M=64, N=64, K=64, r=16, eps=1e-12, dtype=1, X=P, ldx=0, W0=P, ldw=0, A=P, B=P, m=P, c=P, bias=NUL,
+             Y=P, ldy=0, U=P, ldu=0, Z=P, ldz=0, state=P)
+    a.update(kw)
+    return (a["M"], a["N"], a["K"], a["r"], 1.0, a["eps"], a["dtype"], a["X"], a["ldx"], a["W0"], a["ldw"], a["A"],
+            a["B"], a["m"], a["c"], a["bias"], a["Y"], a["ldy"], a["U"], a["ldu"], a["Z"], a["ldz"], a["state"], NUL,
+            0, NUL)
 
 
 def test_dora_validation(L):
-    assert L.dora_prepare(64, 64, 1, NUL, P, NUL) == INVAL
-    assert L.dora_prepare(0, 64, 1, P, P, NUL) == INVAL
+    assert L.dora_prepare(64, 64, 1, NUL, 0, P, NUL) == INVAL
+    assert L.dora_prepare(0, 64, 1, P, 0, P, NUL) == INVAL
     f = L.dora_linear_fwd
     # fp32 DoRA is not offered; r must be a multiple of 8; state required
-    assert f(64, 64, 64, 16, 1.0, 1e-12, 0, P, P, P, P, P, P, NUL, P, P, P, P, NUL, 0, NUL) == UNSUP
-    assert f(64, 64, 64, 12, 1.0, 1e-12, 1, P, P, P, P, P, P, NUL, P, P, P, P, NUL, 0, NUL) == UNSUP
-    assert f(64, 64, 64, 16, 1.0, 1e-12, 1, P, P, P, P, P, P, NUL, P, P, P, NUL, NUL, 0, NUL) == INVAL
-    assert f(64, 64, 64, 16, 1.0, -1.0, 1, P, P, P, P, P, P, NUL, P, P, P, P, NUL, 0, NUL) == INVAL
+    assert f(*dora_fwd_args(dtype=0)) == UNSUP
+    assert f(*dora_fwd_args(r=12)) == UNSUP
+    assert f(*dora_fwd_args(state=NUL)) == INVAL
+    assert f(*dora_fwd_args(eps=-1.0)) == INVAL
+    assert f(*dora_fwd_args(ldz=40)) == INVAL
     b = L.dora_linear_bwd
     need = L.ldl_workspace_bytes(3, 64, 64, 64, 16, 1)
-    args = [64, 64, 64, 16, 1.0, 1e-12, 1, P, P, P, P, P, P, P, P, P, P, P, P, P, NUL, P, need, NUL]
+    args = [64, 64, 64, 16, 1.0, 1e-12, 1, P, 0, P, 0, P, 0, P, P, P, P, 0, P, 0, P, P, 0, P, P, P, NUL, P, need, NUL]
     a2 = list(args); a2[-2] = need - 256
     assert b(*a2) == WS
-    a3 = list(args); a3[18] = NUL   # dm
+    a3 = list(args); a3[25] = NUL   # dm
     assert b(*a3) == INVAL
 
 
 def test_swiglu_and_w8a8_validation(L):
     f = L.swiglu_lora_mlp_fwd
-    ps = [P] * 15 + [NUL]        # 15 tensors, then the (absent) workspace
-    assert f(64, 64, 64, 65, 0.25, 0.25, 0.25, *ps, 0, NUL) == UNSUP      # r > 64
-    assert f(64, 96, 64, 16, 0.25, 0.25, 0.25, *ps, 0, NUL) == UNSUP      # K not a multiple of 64
-    ps2 = list(ps); ps2[1] = NUL
-    assert f(64, 64, 64, 16, 0.25, 0.25, 0.25, *ps2, 0, NUL) == INVAL
+
+    def sw(M=64, K=64, H=64, r=16, **kw):
+        a = dict(X=P, ldx=0, Wg=P, Out=P, ldo=0)
+        a.update(kw)
+        return (M, K, H, r, 0.25, 0.25, 0.25, a["X"], a["ldx"], a["Wg"], P, P, P, P, P, P, P, P, a["Out"], a["ldo"],
+                P, P, P, P, NUL, 0, NUL)
+    assert f(*sw(r=65)) == UNSUP              # r > 64
+    assert f(*sw(K=96)) == UNSUP              # K not a multiple of 64
+    assert f(*sw(Wg=NUL)) == INVAL
+    assert f(*sw(ldo=32)) == INVAL
     w = L.w8a8_lora_linear_fwd
     need = L.ldl_workspace_bytes(6, 64, 128, 128, 16, 1)
-    assert w(64, 128, 192, 16, 0.5, P, P, P, P, P, NUL, P, NUL, NUL, NUL, P, 1 << 22, NUL) == UNSUP  # K % 128
-    assert w(64, 128, 128, 16, 0.5, P, P, P, P, P, NUL, P, P, NUL, NUL, P, need, NUL) == INVAL       # Xq w/o sx
-    assert w(64, 128, 128, 16, 0.5, P, P, P, P, P, NUL, P, NUL, NUL, NUL, P, need - 256, NUL) == WS
-    assert L.int8_gemm_raw(64, 128, 96, P, P, P, NUL) == UNSUP
-    assert L.w8a8_quantize_weight(64, 64, 3, P, P, P, NUL) == INVAL
-    assert L.w8a8_quantize_rows(64, 12, P, P, P, NUL) == UNSUP
+
+    def wa(M=64, N=128, K=128, **kw):
+        a = dict(ldx=0, ldw=0, Xq=NUL, sx=NUL, ws=P, nws=need, ldy=0)
+        a.update(kw)
+        return (M, N, K, 16, 0.5, P, a["ldx"], P, a["ldw"], P, P, P, NUL, P, a["ldy"], a["Xq"], a["sx"], NUL, 0,
+                a["ws"], a["nws"], NUL)
+    assert w(*wa(K=192, nws=1 << 22)) == UNSUP                                   # K % 128
+    assert w(*wa(Xq=P)) == INVAL                                                 # Xq without sx
+    assert w(*wa(nws=need - 256)) == WS
+    assert w(*wa(ldw=136)) == UNSUP                                              # int8 rows of 16 bytes
+    assert L.int8_gemm_raw(64, 128, 96, P, 0, P, 0, P, 0, NUL) == UNSUP
+    assert L.w8a8_quantize_weight(64, 64, 3, P, 0, P, P, NUL) == INVAL
+    assert L.w8a8_quantize_rows(64, 12, P, 0, P, P, NUL) == UNSUP
 
 
 def test_workspace_query_with_empty_batch(L):

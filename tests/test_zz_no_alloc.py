@@ -63,7 +63,8 @@ def test_noalloc_takes_no_device_memory_and_rejects_oversize():
     dB = torch.empty((1024, 16), dtype=torch.float32, device="cuda")
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    args = (1024, 1024, 1024, 16, 0.5, 1, P(dY), P(X), P(W0), P(A), P(B), P(U), P(dX), P(dA), P(dB), None, stream)
+    args = (1024, 1024, 1024, 16, 0.5, 1, P(dY), 1024, P(X), 1024, P(W0), 1024, P(A), P(B), P(U), 16, P(dX), 1024,
+            P(dA), P(dB), None, stream)
     assert lib.lora_linear_bwd_noalloc(*args) == 0
     torch.cuda.synchronize()
     free0 = torch.cuda.mem_get_info()[0]
@@ -76,5 +77,5 @@ def test_noalloc_takes_no_device_memory_and_rejects_oversize():
     assert cap == 32 << 20
     big = (16384, 8192, 8192, 128)
     assert lib.ldl_workspace_bytes(1, *big, 1) > cap
-    bad = (*big, 0.5, 1, P(dY), P(X), P(W0), P(A), P(B), None, P(dX), P(dA), P(dB), None, stream)
+    bad = (*big, 0.5, 1, P(dY), 0, P(X), 0, P(W0), 0, P(A), P(B), None, 0, P(dX), 0, P(dA), P(dB), None, stream)
     assert lib.lora_linear_bwd_noalloc(*bad) == LDL_E_WORKSPACE
