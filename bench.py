@@ -34,7 +34,7 @@ def parse():
     # 200 untimed steps reach the sustained clock, 1000 timed steps take about 0.3 s
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="lora", choices=["lora", "dora", "swiglu", "w8a8"])
+    ap.add_argument("--workload", default="lora", choices=["lora", "dora", "swiglu", "w8a8", "tiny"])
     ap.add_argument("--M", type=int, default=None, help="token count override (w8a8 sweep point)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused-downproj", type=int, default=None, choices=[0, 1])
@@ -105,9 +105,20 @@ def _ptrs(evs):
     return arr
 
 
-def cpu_baseline_lora(M_sample, N, K, r, s, repeats=3):
-    """The fp64 oracle (as it stands) on the first M_sample rows of the same workload (median of repeats)."""
-    import numpy as np
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_lora(M_sample, N, K, r, s, min_seconds=10.0, min_repeats=3):
+    """The fp64 oracle (as it stands) on the first M_sample rows of the same workload, repeated
+    until about min_seconds of CPU work (median of the repeats)."""
     from threadpoolctl import threadpool_info
 
     from lora_dora_linear_amd import inputs
@@ -115,7 +126,7 @@ def cpu_baseline_lora(M_sample, N, K, r, s, repeats=3):
     c = inputs.linear_case(2, M_sample, N, K, r, s, "bf16")
     X, W0, A, B, dY = (c.f64(k) for k in ("X", "W0", "A", "B", "dY"))
     times = []
-    for _ in range(repeats):
+    while len(times) < min_repeats or sum(times) < min_seconds:
         t0 = time.perf_counter()
         olora.lora_forward(X, W0, A, B, s)
         olora.lora_backward(dY, X, W0, A, B, s)
@@ -124,8 +135,72 @@ def cpu_baseline_lora(M_sample, N, K, r, s, repeats=3):
     flops = 4.0 * M_sample * N * K + 6.0 * M_sample * r * (K + N)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{M_sample} of the 4096 token rows (same N, K, r), fp64 forward + backward, "
-                      f"median of {repeats}: {dt:.2f} s wall", "seconds": dt}
+            "sample": f"{M_sample} of the 4096 token rows (same N, K, r), fp64 forward + backward materialising "
+                      f"B.A and dY^T.X, median of {len(times)} runs ({sum(times):.1f} s of CPU work): {dt:.2f} s each",
+            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(), "blas_threads": int(threads), "seconds": dt}
+
+
+def tiny(args, torch, np, binding, inputs, L, up, P, st, check):
+    """The fp32 workload of 64 tokens, K = N = 256, r = 8, s = 2: launch-bound, so the line
+    reports the step time, eagerly and as one replayed HIP graph of the same launches."""
+    M, N, K, r, s = 64, 256, 256, 8, 2.0
+    dev = torch.device("cuda", 0)
+    c = inputs.linear_case(1, M, N, K, r, s, "f32")
+    X, W0, A, B, dY = (up(c.t[k], "f32") for k in ("X", "W0", "A", "B", "dY"))
+    f32 = torch.float32
+    Y = torch.empty((M, N), dtype=f32, device=dev)
+    U = torch.empty((M, r), dtype=f32, device=dev)
+    dX = torch.empty((M, K), dtype=f32, device=dev)
+    dA = torch.empty((r, K), dtype=f32, device=dev)
+    dB = torch.empty((N, r), dtype=f32, device=dev)
+    nb = binding.workspace_bytes("lora_bwd", M, N, K, r, 0)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+
+    def step():
+        check(L.lora_linear_fwd(M, N, K, r, s, 0, P(X), K, P(W0), K, P(A), P(B), None, P(Y), N, P(U), r, P(ws), 0,
+                                st()), "lora_linear_fwd")
+        check(L.lora_linear_bwd(M, N, K, r, s, 0, P(dY), N, P(X), K, P(W0), K, P(A), P(B), P(U), r, P(dX), K, P(dA),
+                                P(dB), None, P(ws), nb, st()), "lora_linear_bwd")
+
+    K_steps = args.steps
+    for _ in range(args.warmup):
+        step()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(K_steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / K_steps
+    # the same step captured once and replayed (launch overhead of the nine kernels gone)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        step()
+        torch.cuda.current_stream().synchronize()
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(K_steps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_graph = t0.elapsed_time(t1) / K_steps
+    flops = 4.0 * M * N * K + 6.0 * M * r * (K + N)
+    print(json.dumps({"metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 4), "unit": "TFLOP/s", "n_gpus": 1,
+                      "steps": K_steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+                      "us_per_step": round(ms * 1e3, 2), "us_per_step_graph_replay": round(ms_graph * 1e3, 2),
+                      "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+                      "data": "synthetic",
+                      "config": {"workload": f"fp32 LoRA linear fwd+bwd, M={M}, K=N={K}, r={r}, s={s} "
+                                             "(launch-bound: report the step time)",
+                                 "M": M, "N": N, "K": K, "r": r, "s": s}}))
 
 
 def main():
@@ -167,6 +242,9 @@ def main():
     bf = torch.bfloat16
     f32 = torch.float32
     wl = args.workload
+    if wl == "tiny":
+        tiny(args, torch, np, binding, inputs, L, up, P, st, check)
+        return
     gemm_kinds = (0, 1)
     gemm_flops = {}
     if wl == "lora":

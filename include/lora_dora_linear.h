@@ -83,7 +83,7 @@ int ldl_version(void);
  *   LDL_TUNE_FWD_FUSED_DOWNPROJ (0/1, default 0): compute U = X.A^T inside the
  *     K-loop of the base GEMM from the LDS-staged X tiles (r <= 64, N multiple
  *     of 128) instead of a separate rank-r pass before it.
- *   LDL_TUNE_GEMM_4WAVE (0/1, default 1): run the bf16 GEMMs with a low-rank
+ *   LDL_TUNE_GEMM_4WAVE (0/1/2, default 1): run the bf16 GEMMs with a low-rank
  *     term of rank <= 64 and M > 128 on the four-wave tile with 16x16x32 MFMAs:
  *     the LoRA forward and input gradient and the DoRA forward (N a multiple of
  *     256, or of 192 when 256-wide tiles would leave CUs idle), the DoRA input
@@ -91,7 +91,9 @@ int ldl_version(void);
  *     multiple of 128; the activation formed in its epilogue) and the down
  *     projection's input gradient (hidden width a multiple of 256: a plain
  *     product followed by a streaming SwiGLU-backward pass instead of the fused
- *     epilogue); 0 selects the eight-wave tiles and fused epilogues for all of them.
+ *     epilogue), and the W8A8 int8 forward (N a multiple of 256, unless 256 x 128
+ *     tiles fit the chip in one round; 2 takes the four-wave int8 tile whenever the
+ *     shape allows); 0 selects the eight-wave tiles and fused epilogues for all of them.
  *   LDL_TUNE_ROWSTREAM_32 (0/1/2, default 1): row projections of rank 33..128
  *     (U = X.A^T, V = dY.B and their like) on 32-row blocks that stage the rank
  *     factor once per 32 rows: 1 when those blocks still fill the 256 CUs

@@ -352,7 +352,7 @@ int ldl_set_tuning(int key, int value) {
     g_fwd_fused = value;
     return LDL_OK;
   }
-  if (key == LDL_TUNE_GEMM_4WAVE && (value == 0 || value == 1)) {
+  if (key == LDL_TUNE_GEMM_4WAVE && value >= 0 && value <= 2) {
     g_gemm_4wave = value;
     return LDL_OK;
   }
@@ -360,6 +360,7 @@ int ldl_set_tuning(int key, int value) {
     g_rowstream32 = value;
     return LDL_OK;
   }
+
   return LDL_E_INVAL;
 }
 

@@ -80,6 +80,16 @@ static bool dual16_ok(const GemmParams& p) {
          p.e_ldn % 8 == 0 && p.ldo % 8 == 0 && p.ldo2 % 8 == 0 && p.ldo3 % 8 == 0 && a16(p.out) && a16(p.out2) &&
          a16(p.out3);
 }
+// W8A8 forward on the four-wave tile: int8 16x16x64 MFMAs into exact int32 accumulators, then
+// the dequantisation and the low-rank k-tile on fp32 accumulators after the loop.
+static hipError_t run16_i8(const GemmParams& p0, hipStream_t st) {
+  GemmParams p = p0;
+  p.seed_hilo = (p.r_epi > 0 && 2 * p.r_epi <= 64) ? 1 : 0;
+  const int tiles = ((p.M + 255) / 256) * (p.N / 256);
+  hipLaunchKernelGGL((gemm16_kernel<false, 0, false, false, 256, false, true>), dim3(tiles), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
 static hipError_t run16_dual(const GemmParams& p, hipStream_t st) {
   const int tiles = ((p.M + 255) / 256) * (p.N / 128);
   hipLaunchKernelGGL((gemm16_kernel<false, 2, false, false, 256, true>), dim3(tiles), dim3(256), 0, st, p);
@@ -144,6 +154,13 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
     }
   }
   const bool seed = seed_ok(kind, p);
+  // (measured at 5120 x 5120, r = 32: 2048 tokens 88 -> 72 us, 4096 182 -> 145, 8192 303 -> 245,
+  // 16384 523 -> 415 us against the eight-wave tile; at 1024 tokens the eight-wave 256 x 128
+  // tiles, twice as many in the one round, stay faster: 67 against 71 us)
+  if (kind == GK_NT_I8_DEQ && g_gemm_4wave && big && bn == 256 && (g_gemm_4wave == 2 || !half_tiles_pay(p.M, p.N)) &&
+      p.side == nullptr &&
+      p.r_epi <= 64 && seed && p.K % 128 == 0 && a16(p.col_scale))
+    return run16_i8(p, st);
   if (g_gemm_4wave && big && p.side == nullptr && p.r_epi <= 64 && seed &&
       (kind == GK_NT_PLAIN || kind == GK_NT_DORA) && b192_fills(p.M, p.N)) {
     if (kind == GK_NT_PLAIN) return run16<false, false, false, 192>(p, st);

@@ -47,13 +47,19 @@ __host__ __device__ constexpr int g16_nn_row(int k) { return k * kG16NNRow + (k 
 // e and the waves with wn = 1 hold u of the same (token, unit) in the same lanes.  Outputs:
 // out = e, out2 = u, out3 = h = silu(e) u, all from the fp32 accumulators (e is handed to
 // the u waves through LDS).
-template <bool NN, int LR, bool DORA = false, bool SWB = false, int BN_ = 256, bool SWF = false>
+// I8 (NT only, the W8A8 forward): P and Q are int8 with 128 k per k-tile (the same 128-byte
+// LDS rows and 16-byte fragments), v_mfma_i32_16x16x64_i8 into exact int32 accumulators,
+// dequantised after the loop to acc . row_scale[m] . col_scale[n] in fp32; the low-rank term
+// is then one bf16 k-tile on those fp32 accumulators (LR = 0 in the loop).
+template <bool NN, int LR, bool DORA = false, bool SWB = false, int BN_ = 256, bool SWF = false, bool I8 = false>
 __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   static_assert(BN_ == 256 || (!NN && BN_ == 192), "tile widths: 256, or 192 for NT");
   static_assert(!(NN && DORA), "the row-scaled epilogue is a forward (NT) epilogue");
   static_assert(!SWB || (NN && !DORA), "the SwiGLU backward epilogue is an NN epilogue");
   static_assert(!SWF || (!NN && !DORA && !SWB && BN_ == 256 && LR != 1), "the dual tile is a plain 256-wide NT tile");
   static_assert(LR >= 0 && LR <= 2 && (LR != 2 || SWF), "two low-rank k-tiles: the dual tile's two segments");
+  static_assert(!I8 || (!NN && !DORA && !SWB && !SWF && LR == 0 && BN_ == 256), "int8: the plain 256-wide NT tile");
+  constexpr int KB = I8 ? 128 : 64;                 // reduction elements per k-tile (128 bytes per row)
   constexpr int BM = 256, BN = BN_, NW = 4;
   constexpr int TNO = SWF ? 128 : BN;               // output columns (hidden units) per tile
   constexpr int FN = BN / 32;                       // 16-column fragments per wave (wave tile BN / 2)
@@ -79,7 +85,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int l16 = lane & 15, lq = lane >> 4;
-  const uint32_t lda_b = (uint32_t)p.lda * 2u, ldb_b = (uint32_t)p.ldb * 2u;
+  const uint32_t lda_b = (uint32_t)p.lda * (I8 ? 1u : 2u), ldb_b = (uint32_t)p.ldb * (I8 ? 1u : 2u);
 
   const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(p.a, (uint32_t)M * lda_b);
   const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(p.b0, (uint32_t)(NN ? K : N) * ldb_b);
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   };
   // copies of stage kt into sb; stages past the last read nothing and land as zeros
   auto copy_stage = [&](int kt, uint8_t* sb) {
-    const bool valid = kt < K / 64;
+    const bool valid = kt < K / KB;
     const __amdgpu_buffer_rsrc_t ra = valid ? rs_a : rs_none, rb = valid ? rs_b : rs_none;
     const __amdgpu_buffer_rsrc_t rb1 = valid ? rs_b1 : rs_none;
     const uint32_t ka = (uint32_t)kt * 128u, kb = NN ? (uint32_t)kt * 64u * ldb_b : (uint32_t)kt * 128u;
@@ -127,11 +133,12 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
     }
   };
 
-  f32x4 acc[8][FN];
+  using AccT = typename std::conditional<I8, i32x4, f32x4>::type;
+  AccT acc[8][FN];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+    for (int j = 0; j < FN; ++j) acc[i][j] = AccT{0, 0, 0, 0};
 
   // fragments of 32-element step ks (P rows wm*128 + 16 i + l16, Q rows or columns
   // wn*128 + 16 j + l16, k = 32 ks + 8 lq ..), read in order of first use: fa[0], fb[0..7], fa[1..7]
@@ -179,7 +186,8 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        acc[i][j] = mfma_bf16(fb[j], fa[i], acc[i][j]);
+        if constexpr (I8) acc[i][j] = mfma_i8(fb[j], fa[i], acc[i][j]);
+        else acc[i][j] = mfma_bf16(fb[j], fa[i], acc[i][j]);
         // NT 256: keep each result in its accumulator's AGPRs (an empty asm with an AGPR
         // operand); otherwise the allocator moves some accumulators through VGPRs.  (At
         // 192 columns the pins cost ~70 AGPR moves per k-tile and are left out.)
@@ -188,7 +196,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   };
 
   constexpr int NRQ = NN ? 2 : 1;       // LDS read instructions per Q fragment
-  const int KT = K / 64;
+  const int KT = K / KB;
   u32x4 fa0[8], fb0[FN], fa1[8], fb1[FN];
 
   // The low-rank term enters as LR more k-tiles in front ("stages" -LR .. -1, in the stage
@@ -383,7 +391,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
           const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n0 + cl);
           b4[0] = bf16_lo(bb[0]); b4[1] = bf16_hi(bb[0]); b4[2] = bf16_lo(bb[1]); b4[3] = bf16_hi(bb[1]);
         }
-        f32x4 v = acc[i][j];
+        auto v = acc[i][j];         // (fp32 in every kernel that calls this)
         if constexpr (DORA && !Z) v *= *reinterpret_cast<const f32x4*>(p.col_scale + n0 + cl);
         u32x2 w;
         w[0] = pack_bf16x2(v[0] + b4[0], v[1] + b4[1]);
@@ -402,7 +410,81 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
       }
     }
   };
-  if constexpr (DORA) {
+  if constexpr (I8) {
+    // dequantise the exact int32 products in place: acc . sx[m] . sw[n] in fp32 (the fp32 bits
+    // kept in the same registers)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float sxm = p.row_scale[min(m0 + wm * 128 + i * 16 + l16, M - 1)];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const f32x4 swn = *reinterpret_cast<const f32x4*>(p.col_scale + n0 + wn * (BN / 2) + j * 16 + 4 * lq);
+        const i32x4 a = acc[i][j];
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (float)a[e] * sxm * swn[e];
+        acc[i][j] = __builtin_bit_cast(i32x4, v);
+      }
+    }
+    if (p.r_epi > 0) {
+      // the low-rank term s.S.E^T as one bf16 k-tile in smem0 (layout of the loop's seed tile:
+      // hi + lo of s.S where 2 r <= 64, else hi), multiplied into the fp32 accumulators
+      const int cps = p.r_epi >> 3;
+      const int nparts = p.seed_hilo ? 2 : 1;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int part = c / cps, j0 = 8 * (c - part * cps);
+        const bool on = part < nparts;
+        const int jl = on ? j0 : 0;
+        const f32x4 sa = *reinterpret_cast<const f32x4*>(srow + jl);
+        const f32x4 sb = *reinterpret_cast<const f32x4*>(srow + jl + 4);
+        const u32x4 ev = *reinterpret_cast<const u32x4*>(e0 + (size_t)(n0 + tid) * p.e_ldn + jl);
+        const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+        lds_st16(smem0, g16_off(tid, c), on ? pack8(sa, sb, live ? p.s_epi : 0.f, part == 1) : z);
+        lds_st16(smem0, BM * 128 + g16_off(tid, c), on ? ev : z);
+      }
+      __syncthreads();
+      u32x4 fa[8], fb[FN];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        ldf_rows(smem0, ks, fa, fb);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_bit_cast(i32x4, mfma_bf16(fb[j], fa[i], __builtin_bit_cast(f32x4, acc[i][j])));
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = wm * 128 + i * 16 + l16;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int cl = wn * (BN / 2) + j * 16 + 4 * lq;
+        float b4[4] = {0.f, 0.f, 0.f, 0.f};
+        if (p.bias != nullptr) {
+          const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n0 + cl);
+          b4[0] = bf16_lo(bb[0]); b4[1] = bf16_hi(bb[0]); b4[2] = bf16_lo(bb[1]); b4[3] = bf16_hi(bb[1]);
+        }
+        const f32x4 v = __builtin_bit_cast(f32x4, acc[i][j]);
+        u32x2 w;
+        w[0] = pack_bf16x2(v[0] + b4[0], v[1] + b4[1]);
+        w[1] = pack_bf16x2(v[2] + b4[2], v[3] + b4[3]);
+        *reinterpret_cast<u32x2*>(st_ptr(r, cl)) = w;
+      }
+    }
+    __syncthreads();
+    uint16_t* out = static_cast<uint16_t*>(p.out);
+    for (int idx = tid; idx < BM * NCH; idx += 256) {
+      const int r = idx / NCH, c = idx % NCH;
+      if (m0 + r < M) {
+        const uint8_t* base = r < 128 ? smem0 : smem1;
+        const int rr = r & 127;
+        st16(out + (size_t)(m0 + r) * p.ldo + n0 + c * 8, lds_ld16(base, rr * SROW + ((c ^ (rr & SWZM)) << 4)));
+      }
+    }
+  } else if constexpr (DORA) {
     emit(std::true_type{}, p.out2, p.ldo2);
     __syncthreads();                               // the staging buffers are free again
     emit(std::false_type{}, p.out, p.ldo);

@@ -69,6 +69,9 @@ def test_tuning_switch(L):
     assert L.ldl_set_tuning(0, 1) == OK
     assert L.ldl_set_tuning(0, 0) == OK
     assert L.ldl_set_tuning(0, 7) == INVAL
+    for v in (0, 2, 1):
+        assert L.ldl_set_tuning(1, v) == OK
+    assert L.ldl_set_tuning(1, 3) == INVAL
     assert L.ldl_set_tuning(42, 0) == INVAL
     for v in (0, 2, 1):
         assert L.ldl_set_tuning(2, v) == OK

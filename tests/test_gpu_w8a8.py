@@ -137,3 +137,33 @@ def test_w8a8_bias_and_no_input_gradient():
     for k in ("dA", "dB"):
         assert_close(host(g2[k]), b[k], TOL, k)
         assert torch.equal(g[k], g2[k]), k
+
+
+@pytest.mark.parametrize("M,N,K,r", [(300, 512, 640, 32), (513, 768, 256, 16), (129, 256, 384, 48)])
+def test_w8a8_int8_forward_routes(M, N, K, r):
+    """The W8A8 forward on the four-wave int8 tile (exact int32 accumulators dequantised after
+    the loop, then the low-rank k-tile; the default when N is a multiple of 256 and 256 x 128
+    tiles would not fit the chip in one round, forced here) and, four-wave tiles switched off,
+    on the eight-wave tile: both against the oracle; ragged row tails, rank 16 / 32 with the
+    hi + lo low-rank term and rank 48 without."""
+    require_gpu()
+    import lora_dora_linear_amd as L
+    c, W0f = _case(M, N, K, r, seed=19)
+    X, A, B = (dev(c.t[k], "bf16") for k in ("X", "A", "B"))
+    bias = inputs.normal(19, 6, (N,), 0.5, "bf16")
+    Wq, sw = L.w8a8_quantize_weight(dev(W0f, "f32"))
+    L.set_tuning(1, 2)         # the four-wave int8 tile at these small sizes too
+    try:
+        Y4, Xq, sx, U = L.w8a8_lora_linear_fwd(X, Wq, sw, A, B, c.s, bias=dev(bias, "bf16"))
+    finally:
+        L.set_tuning(1, 1)
+    L.set_tuning(1, 0)
+    try:
+        Y8, _, _, _ = L.w8a8_lora_linear_fwd(X, Wq, sw, A, B, c.s, bias=dev(bias, "bf16"))
+    finally:
+        L.set_tuning(1, 1)
+    torch.cuda.synchronize()
+    Wq_ref, sw_ref = ow.quantize_rows_int8(W0f)
+    f = ow.w8a8_forward(c.f64("X"), Wq_ref, sw_ref, c.f64("A"), c.f64("B"), c.s, bias=inputs.bf16_bits_to_f64(bias))
+    assert_close(host(Y4), f["Y"], TOL, "Y four-wave")
+    assert_close(host(Y8), f["Y"], TOL, "Y eight-wave")
