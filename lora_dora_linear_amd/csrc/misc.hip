@@ -351,52 +351,54 @@ hipError_t launch_quantize_rows(const void* X, int in_f32, int M, int K, int ldx
 
 // ============================================================================ fp32 path
 // C[m,n] = alpha * sum_k A(m,k) B(k,n) + beta * C[m,n] (+ bias[n]); element strides are
-// arbitrary, so the same kernel serves every product of the fp32 layer.  64x64 tile,
-// 16-deep k slices, 4x4 outputs per thread, fp32 FMA.
+// arbitrary, so the same kernel serves every product of the fp32 layer.  On
+// v_mfma_f32_16x16x4_f32 (fp32 products and accumulation): one wave per 16 x 16 output tile,
+// four waves per block (32 x 32).  The reduction index of MFMA c of a chunk is
+// k0 + 4 c + (lane >> 4) on both operands; each lane loads its row of A and its column of B
+// for the 16 MFMAs of the next chunk (64 k) while the current chunk is multiplied, so a
+// small product waits for memory about once per chunk rather than once per load.  Rows,
+// columns and k past the ends load as zero.
+constexpr int kF32Chunk = 16;
 __global__ __launch_bounds__(256) void f32_gemm_kernel(const F32GemmParams p) {
-  __shared__ float sA[16][64 + 1];
-  __shared__ float sB[16][64 + 1];
-  const int tid = threadIdx.x;
-  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
-  const int tm = (tid / 16) * 4, tn = (tid % 16) * 4;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < p.K; k0 += 16) {
-    for (int i = tid; i < 64 * 16; i += 256) {
-      const int mm = i / 16, kk = i % 16;
-      const int m = m0 + mm, k = k0 + kk;
-      sA[kk][mm] = (m < p.M && k < p.K) ? p.A[(long)m * p.sam + (long)k * p.sak] : 0.f;
-      const int kk2 = i / 64, nn = i % 64;
-      const int k2 = k0 + kk2, n = n0 + nn;
-      sB[kk2][nn] = (k2 < p.K && n < p.N) ? p.B[(long)k2 * p.sbk + (long)n * p.sbn] : 0.f;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m0 = blockIdx.y * 32 + (wave >> 1) * 16, n0 = blockIdx.x * 32 + (wave & 1) * 16;
+  const int lr = lane & 15, q = lane >> 4;
+  const bool va = m0 + lr < p.M, vb = n0 + lr < p.N;
+  const float* a = p.A + (long)(va ? m0 + lr : 0) * p.sam;
+  const float* b = p.B + (long)(vb ? n0 + lr : 0) * p.sbn;
+  float fa[kF32Chunk], fb[kF32Chunk], na[kF32Chunk], nb[kF32Chunk];
+  auto load = [&](int k0, float* xa, float* xb) {
+#pragma unroll
+    for (int c = 0; c < kF32Chunk; ++c) {
+      const int k = k0 + 4 * c + q;
+      const bool kv = k < p.K;
+      xa[c] = (va && kv) ? a[(long)k * p.sak] : 0.f;
+      xb[c] = (vb && kv) ? b[(long)k * p.sbk] : 0.f;
     }
-    __syncthreads();
+  };
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  load(0, fa, fb);
+  for (int k0 = 0; k0 < p.K; k0 += 4 * kF32Chunk) {
+    const bool more = k0 + 4 * kF32Chunk < p.K;
+    if (more) load(k0 + 4 * kF32Chunk, na, nb);
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float a[4], b[4];
+    for (int c = 0; c < kF32Chunk; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[c], fb[c], acc, 0, 0, 0);
+    if (more) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = sA[kk][tm + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = sB[kk][tn + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+      for (int c = 0; c < kF32Chunk; ++c) { fa[c] = na[c]; fb[c] = nb[c]; }
     }
-    __syncthreads();
   }
+  // lane holds D[4 q + i][lr] of the 16 x 16 tile
+  const int n = n0 + lr;
+  if (n >= p.N) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int m = m0 + tm + i;
+    const int m = m0 + 4 * q + i;
     if (m >= p.M) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + tn + j;
-      if (n >= p.N) continue;
-      float v = p.alpha * acc[i][j];
-      if (p.beta != 0.f) v += p.beta * p.C[(size_t)m * p.ldc + n];
-      if (p.bias != nullptr) v += p.bias[n];
-      p.C[(size_t)m * p.ldc + n] = v;
-    }
+    float v = p.alpha * acc[i];
+    if (p.beta != 0.f) v += p.beta * p.C[(size_t)m * p.ldc + n];
+    if (p.bias != nullptr) v += p.bias[n];
+    p.C[(size_t)m * p.ldc + n] = v;
   }
 }
 
@@ -410,7 +412,7 @@ __global__ void f32_colsum_kernel(const float* X, int M, int N, int ld, float* o
 
 hipError_t launch_f32_gemm(const F32GemmParams& p, hipStream_t st) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
-  const dim3 grid((p.N + 63) / 64, (p.M + 63) / 64), block(256);
+  const dim3 grid((p.N + 31) / 32, (p.M + 31) / 32), block(256);
   hipLaunchKernelGGL(f32_gemm_kernel, grid, block, 0, st, p);
   return hipGetLastError();
 }
