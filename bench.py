@@ -34,7 +34,7 @@ def parse():
     # 200 untimed steps reach the sustained clock, 1000 timed steps take about 0.3 s
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="lora", choices=["lora", "dora", "swiglu", "w8a8", "tiny"])
+    ap.add_argument("--workload", default="lora", choices=["lora", "dora", "swiglu", "w8a8", "tiny", "merge"])
     ap.add_argument("--M", type=int, default=None, help="token count override (w8a8 sweep point)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused-downproj", type=int, default=None, choices=[0, 1])
@@ -203,6 +203,58 @@ def tiny(args, torch, np, binding, inputs, L, up, P, st, check):
                                  "M": M, "N": N, "K": K, "r": r, "s": s}}))
 
 
+def merge(args, torch, np, binding, inputs, L, up, P, st, check):
+    """LoRA merge of a 4096 x 4096 bf16 weight with a rank-16 adapter: W = W0 + s.B.A (one
+    HBM-bound kernel: read W0, write W) and the merge backward (dA, dB from a weight
+    gradient).  The roofline is the forward kernel's HBM rate."""
+    N, K, r, s = 4096, 4096, 16, 0.5
+    dev = torch.device("cuda", 0)
+    c = inputs.linear_case(2, 1, N, K, r, s, "bf16")
+    W0, A, B = (up(c.t[k], "bf16") for k in ("W0", "A", "B"))
+    dW = up(inputs.normal(2, 7, (N, K), 1.0, "bf16"), "bf16")
+    W = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    dA = torch.empty((r, K), dtype=torch.float32, device=dev)
+    dB = torch.empty((N, r), dtype=torch.float32, device=dev)
+    nb = binding.workspace_bytes("merge_bwd", 0, N, K, r)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+    K_steps = args.steps
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(K_steps)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(K_steps)]
+
+    def step(i=None):
+        if i is not None:
+            e0[i].record()
+        check(L.lora_merge_fwd(N, K, r, s, 1, P(W0), K, P(A), P(B), P(W), K, st()), "lora_merge_fwd")
+        if i is not None:
+            e1[i].record()
+        check(L.lora_merge_bwd(N, K, r, s, 1, P(dW), K, P(A), P(B), P(dA), P(dB), P(ws), nb, st()), "lora_merge_bwd")
+
+    for _ in range(args.warmup):
+        step()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(K_steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / K_steps
+    fwd_us = 1e3 * sum(a.elapsed_time(b) for a, b in zip(e0, e1)) / K_steps
+    fwd_bytes = 2.0 * N * K * 2 + (N + K) * r * 2          # read W0, write W, read the factors
+    gbs = fwd_bytes / (fwd_us * 1e-6) / 1e9
+    flops = 2.0 * N * K * r + 4.0 * N * K * r
+    print(json.dumps({"metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+                      "n_gpus": 1, "steps": K_steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+                      "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                      "data": "synthetic",
+                      "config": {"workload": f"bf16 LoRA merge fwd+bwd, N=K={K}, r={r}, s={s}", "N": N, "K": K,
+                                 "r": r, "s": s},
+                      "roofline": {"bound": "hbm", "kernel": "merge forward (merge_kernel)",
+                                   "achieved": round(gbs, 1), "peak": PEAK_HBM, "unit": "GB/s",
+                                   "frac": round(gbs / PEAK_HBM, 4), "traffic": None},
+                      "kernels": {"merge forward (merge_kernel)": {"avg_us": round(fwd_us, 2)}}}))
+
+
 def main():
     args = parse()
     if args.copy_calibrate:
@@ -244,6 +296,9 @@ def main():
     wl = args.workload
     if wl == "tiny":
         tiny(args, torch, np, binding, inputs, L, up, P, st, check)
+        return
+    if wl == "merge":
+        merge(args, torch, np, binding, inputs, L, up, P, st, check)
         return
     gemm_kinds = (0, 1)
     gemm_flops = {}

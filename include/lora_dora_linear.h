@@ -70,7 +70,8 @@ typedef enum {
   LDL_OP_SWIGLU_FWD = 4, /* N = hidden size H */
   LDL_OP_SWIGLU_BWD = 5, /* N = hidden size H */
   LDL_OP_W8A8_FWD = 6,
-  LDL_OP_W8A8_BWD = 7
+  LDL_OP_W8A8_BWD = 7,
+  LDL_OP_MERGE_BWD = 8   /* M unused; N x K weight */
 } ldl_op;
 
 /* Human-readable text of a status code (static storage). */
@@ -170,6 +171,24 @@ int lora_linear_bwd_noalloc(int M, int N, int K, int r, float s, int dtype,
 
 /* Size in bytes of the per-device scratch array lora_linear_bwd_noalloc uses. */
 size_t ldl_noalloc_scratch_bytes(void);
+
+/* ------------------------------------------------------------------------ LoRA merge
+ * The adapted weight formed explicitly, for export or for merging an adapter into its base
+ * weight: the merge forward (the delta) and merge backward of the lora family ("Fused
+ * Kernels (experimental)", section "What is fused").  The rank-r product is generated tile
+ * by tile in registers and written once.
+ *   W = W0 + s.B.A   (W0 NULL: W = s.B.A).  W0, W [N,K] (row strides ldw, ldo; W == W0
+ *   merges in place and needs ldo == ldw); A [r,K], B [N,r].  dtype LDL_BF16 or LDL_F32.
+ *   Limits: K a multiple of 64 (bf16) or 8 (fp32), r <= 128. */
+int lora_merge_fwd(int N, int K, int r, float s, int dtype, const void* W0, int ldw,
+                   const void* A, const void* B, void* W, int ldo, void* stream);
+
+/* Gradients of the factors from a gradient dW [N,K] (row stride lddw) of the merged weight:
+ *   dA = s.B^T.dW [r,K],  dB = s.dW.A^T [N,r]  (fp32, overwritten).
+ *   Workspace: ldl_workspace_bytes(LDL_OP_MERGE_BWD, 0, N, K, r, dtype). */
+int lora_merge_bwd(int N, int K, int r, float s, int dtype, const void* dW, int lddw,
+                   const void* A, const void* B, float* dA, float* dB,
+                   void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ DoRA
  * Row-scaled DoRA ("dora-rows"), bf16 only.  The row norm of W' = W0 + s.B.A uses

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "liblora_dora_linear.so")
 
 LDL_F32, LDL_BF16 = 0, 1
 OPS = {"lora_fwd": 0, "lora_bwd": 1, "dora_fwd": 2, "dora_bwd": 3,
-       "swiglu_fwd": 4, "swiglu_bwd": 5, "w8a8_fwd": 6, "w8a8_bwd": 7}
+       "swiglu_fwd": 4, "swiglu_bwd": 5, "w8a8_fwd": 6, "w8a8_bwd": 7, "merge_bwd": 8}
 
 _lib = None
 
@@ -36,6 +36,8 @@ SIGNATURES = {
     "lora_linear_bwd_noalloc": ([_i, _i, _i, _i, _f, _i, _p, _i, _p, _i, _p, _i, _p, _p, _p, _i, _p, _i, _p, _p,
                                  _p, _p], _i),
     "ldl_noalloc_scratch_bytes": ([], _z),
+    "lora_merge_fwd": ([_i, _i, _i, _f, _i, _p, _i, _p, _p, _p, _i, _p], _i),
+    "lora_merge_bwd": ([_i, _i, _i, _f, _i, _p, _i, _p, _p, _p, _p, _p, _z, _p], _i),
     "dora_prepare": ([_i, _i, _i, _p, _i, _p, _p], _i),
     "dora_linear_fwd": ([_i, _i, _i, _i, _f, _f, _i, _p, _i, _p, _i, _p, _p, _p, _p, _p, _p, _i, _p, _i, _p, _i,
                          _p, _p, _z, _p], _i),
@@ -216,6 +218,39 @@ def lora_linear_bwd_noalloc(dY, X, W0, A, B, s, U=None, need_dx=True, need_dbias
     args = args[:4] + (float(s),) + args[5:]
     _check(lib().lora_linear_bwd_noalloc(*args, _stream()), "lora_linear_bwd_noalloc")
     return out
+
+
+# ------------------------------------------------------------------ LoRA merge
+def lora_merge_fwd(W0, A, B, s, out=None):
+    """W = W0 + s.B.A (W0 None: the delta s.B.A).  out may be W0 itself (merge in place) or a
+    strided view."""
+    r, K = A.shape
+    N = B.shape[0]
+    dt = A.dtype
+    _need(A, "A", dt, (r, K))
+    _need(B, "B", dt, (N, r))
+    ldw = _mat(W0, "W0", dt, (N, K)) if W0 is not None else 0
+    out, ldo = _out(out, "out", dt, (N, K), A.device)
+    _check(lib().lora_merge_fwd(N, K, r, float(s), _dt(A), _ptr(W0), ldw, _ptr(A), _ptr(B), _ptr(out), ldo,
+                                _stream()), "lora_merge_fwd")
+    return out
+
+
+def lora_merge_bwd(dW, A, B, s):
+    """dA = s.B^T.dW, dB = s.dW.A^T for a gradient dW of the merged weight."""
+    r, K = A.shape
+    N = B.shape[0]
+    dt = A.dtype
+    lddw = _mat(dW, "dW", dt, (N, K))
+    _need(A, "A", dt, (r, K))
+    _need(B, "B", dt, (N, r))
+    dA = torch.empty((r, K), dtype=torch.float32, device=A.device)
+    dB = torch.empty((N, r), dtype=torch.float32, device=A.device)
+    n = workspace_bytes("merge_bwd", 0, N, K, r, _dt(A))
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=A.device)
+    _check(lib().lora_merge_bwd(N, K, r, float(s), _dt(A), _ptr(dW), lddw, _ptr(A), _ptr(B), _ptr(dA), _ptr(dB),
+                                _ptr(ws), n, _stream()), "lora_merge_bwd")
+    return {"dA": dA, "dB": dB}
 
 
 # ------------------------------------------------------------------ DoRA

@@ -123,6 +123,20 @@ LoraBwdWs plan_lora_bwd(Bump& b, int M, int N, int K, int r, bool need_u) {
   return w;
 }
 
+struct MergeBwdWs {
+  float* Bf; float* part; uint32_t* pk;
+  int ns, ms, rp;
+};
+MergeBwdWs plan_merge_bwd(Bump& b, int N, int K, int r) {
+  MergeBwdWs w{};
+  w.rp = colproj_rp(r);
+  colproj_plan(N, K, &w.ns, &w.ms, 512);
+  w.Bf = b.take<float>((size_t)N * r);
+  w.part = b.take<float>((size_t)w.ns * K * w.rp);
+  w.pk = b.take<uint32_t>(colproj_spk_words(N, r));
+  return w;
+}
+
 struct DoraBwdWs {
   float* V; float* partT; float* cs; float* wB; float* partA; float* partQ; float* Qm;
   uint16_t* dYg;                   // dY.diag(g) in bf16 [M, N]
@@ -393,6 +407,9 @@ size_t ldl_workspace_bytes(int op, int M, int N, int K, int r, int dtype) {
     case LDL_OP_SWIGLU_BWD:
       plan_mlp_bwd(b, M, K, N, r);
       break;
+    case LDL_OP_MERGE_BWD:   // M unused; N x K weight
+      if (dtype != LDL_F32) plan_merge_bwd(b, N, K, r);
+      break;
     default:
       return 0;
   }
@@ -537,6 +554,53 @@ int lora_linear_bwd_noalloc(int M, int N, int K, int r, float s, int dtype, cons
 }
 
 size_t ldl_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+// =========================================================================== LoRA merge
+int lora_merge_fwd(int N, int K, int r, float s, int dtype, const void* W0, int ldw, const void* A, const void* B,
+                   void* W, int ldo, void* stream) {
+  if (!nonnull({A, B, W})) return LDL_E_INVAL;
+  if (dtype != LDL_F32 && dtype != LDL_BF16) return LDL_E_INVAL;
+  if (N <= 0 || K <= 0 || r <= 0) return LDL_E_INVAL;
+  if (r > 128 || K % (dtype == LDL_BF16 ? 64 : 8)) return LDL_E_UNSUPPORTED;
+  const int g = dtype == LDL_BF16 ? 8 : 4;
+  const size_t e = dtype == LDL_BF16 ? 2 : 4;
+  LDL_LD(ldw, K, g); LDL_LD(ldo, K, g);
+  if (W0 == W && ldw != ldo) return LDL_E_INVAL;       // in place: the same rows
+  if (!al({W0, A, B, W})) return LDL_E_UNSUPPORTED;
+  if (!fits(N, ldw, e) || !fits(N, ldo, e) || !small((size_t)N + r, K, e)) return LDL_E_UNSUPPORTED;
+  LDL_TRY(launch_merge(N, K, r, s, dtype == LDL_BF16, W0, ldw, A, B, W, ldo, S(stream)));
+  return LDL_OK;
+}
+
+int lora_merge_bwd(int N, int K, int r, float s, int dtype, const void* dW, int lddw, const void* A, const void* B,
+                   float* dA, float* dB, void* ws, size_t ws_bytes, void* stream) {
+  if (!nonnull({dW, A, B, dA, dB})) return LDL_E_INVAL;
+  if (dtype != LDL_F32 && dtype != LDL_BF16) return LDL_E_INVAL;
+  if (N <= 0 || K <= 0 || r <= 0) return LDL_E_INVAL;
+  if (r > 128 || K % (dtype == LDL_BF16 ? 64 : 8)) return LDL_E_UNSUPPORTED;
+  const int g = dtype == LDL_BF16 ? 8 : 1;
+  LDL_LD(lddw, K, g);
+  if (!al({dW, A, B, dA, dB, ws})) return LDL_E_UNSUPPORTED;
+  if (!fits(N, lddw, dtype == LDL_BF16 ? 2 : 4)) return LDL_E_UNSUPPORTED;
+  if (ldl_workspace_bytes(LDL_OP_MERGE_BWD, 0, N, K, r, dtype) > ws_bytes) return LDL_E_WORKSPACE;
+  if (ws_bytes > 0 && !ws) return LDL_E_INVAL;
+  const hipStream_t st = S(stream);
+  if (dtype == LDL_F32) {
+    const float *dw = (const float*)dW, *a = (const float*)A, *bb = (const float*)B;
+    LDL_TRY(f32(N, r, K, dw, lddw, 1, a, 1, K, dB, r, s, 0.f, nullptr, st));      // dB = s.dW.A^T
+    LDL_TRY(f32(r, K, N, bb, 1, r, dw, lddw, 1, dA, K, s, 0.f, nullptr, st));     // dA = s.B^T.dW
+    return LDL_OK;
+  }
+  Bump wb(ws);
+  MergeBwdWs w = plan_merge_bwd(wb, N, K, r);
+  // dB = s.dW.A^T: a row projection of dW; dA = s.B^T.dW: a column projection of dW against
+  // B (as fp32) and the fixed-order reduction of its split partials
+  LDL_TRY(rowproj(N, K, r, dW, lddw, A, nullptr, r, K, dB, r, s, st));
+  LDL_TRY(launch_bf16_to_f32(B, (size_t)N * r, w.Bf, st));
+  LDL_TRY(colproj(N, K, r, dW, lddw, w.Bf, r, 1.f, nullptr, 0, 0, w.ns, w.ms, w.part, nullptr, st, w.pk));
+  LDL_TRY(reduce(r, K, w.part, (size_t)K * w.rp, w.ns, w.rp, true, s, dA, K, st));
+  return LDL_OK;
+}
 
 // =========================================================================== DoRA
 int dora_prepare(int N, int K, int dtype, const void* W0, int ldw, float* w0_sumsq, void* stream) {

@@ -85,6 +85,11 @@ hipError_t launch_dora_finalize(int N, int r, float s, float eps, const float* p
                                 const float* P, const float* G, const uint16_t* B,
                                 float* dB, float* dm, float* wB, hipStream_t st);
 
+// LoRA merge: W = W0 + s.B.A (W0 may be null: the delta alone); bf16 or fp32 elements
+hipError_t launch_merge(int N, int K, int r, float s, int bf16, const void* W0, int ldw, const void* A, const void* B,
+                        void* W, int ldo, hipStream_t st);
+hipError_t launch_bf16_to_f32(const void* in, size_t n, float* out, hipStream_t st);
+
 // W8A8 helpers
 hipError_t launch_quantize_rows(const void* X, int in_f32, int M, int K, int ldx, int8_t* q, float* scale,
                                 hipStream_t st);

@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
               "swiglu_lora_mlp_fwd", "swiglu_lora_mlp_bwd", "w8a8_lora_linear_fwd", "w8a8_lora_linear_bwd",
               "w8a8_quantize_weight", "w8a8_quantize_rows", "int8_gemm_raw", "ldl_workspace_bytes",
               "ldl_status_string", "dora_state_floats", "ldl_set_tuning", "ldl_version", "lora_linear_bwd_noalloc",
-              "ldl_noalloc_scratch_bytes"):
+              "ldl_noalloc_scratch_bytes", "lora_merge_fwd", "lora_merge_bwd"):
         assert n in names, n
 
 
@@ -54,7 +54,7 @@ def test_status_strings_and_version(L):
 
 
 def test_workspace_sizes(L):
-    for op in range(8):
+    for op in range(9):
         n1 = L.ldl_workspace_bytes(op, 4096, 4096, 4096, 16, 1)
         n2 = L.ldl_workspace_bytes(op, 8192, 4096, 4096, 16, 1)
         assert n1 % 256 == 0 and n2 >= n1
@@ -215,6 +215,22 @@ def test_swiglu_and_w8a8_validation(L):
     assert L.int8_gemm_raw(64, 128, 96, P, 0, P, 0, P, 0, NUL) == UNSUP
     assert L.w8a8_quantize_weight(64, 64, 3, P, 0, P, P, NUL) == INVAL
     assert L.w8a8_quantize_rows(64, 12, P, 0, P, P, NUL) == UNSUP
+
+
+def test_merge_validation(L):
+    f = L.lora_merge_fwd
+    assert f(64, 72, 16, 0.5, 1, P, 0, P, P, P, 0, NUL) == UNSUP            # bf16: K % 64
+    assert f(64, 60, 16, 0.5, 0, P, 0, P, P, P, 0, NUL) == UNSUP            # fp32: K % 8
+    assert f(64, 64, 129, 0.5, 1, P, 0, P, P, P, 0, NUL) == UNSUP           # r > 128
+    assert f(64, 64, 16, 0.5, 1, P, 0, NUL, P, P, 0, NUL) == INVAL          # A null
+    assert f(64, 64, 16, 0.5, 1, P, 72, P, P, P, 0, NUL) == INVAL           # in place with different strides
+    assert f(64, 64, 16, 0.5, 1, P, 0, P, P, P2, 60, NUL) == INVAL          # ldo below the row length
+    assert f(64, 64, 16, 0.5, 2, P, 0, P, P, P2, 0, NUL) == INVAL           # dtype
+    b = L.lora_merge_bwd
+    need = L.ldl_workspace_bytes(8, 0, 64, 64, 16, 1)
+    assert need > 0
+    assert b(64, 64, 16, 0.5, 1, P, 0, P, P, P, P, P, need - 256, NUL) == WS
+    assert b(64, 64, 16, 0.5, 1, P, 0, P, P, NUL, P, P, need, NUL) == INVAL
 
 
 def test_workspace_query_with_empty_batch(L):
