@@ -28,9 +28,10 @@ Modules
   swiglu - LoRA MLP with the SwiGLU activation (gate, up, down adapters).
   w8a8   - per-row / per-channel int8 quantiser and the int8 base + LoRA layer.
   merge  - the LoRA merge (adapted weight formed explicitly) and its backward.
+  geglu  - LoRA MLP with the GeGLU activation (exact and tanh forms of GELU).
 
 Parity status of every function is listed in its own docstring; functions
 with no independent pin say "parity unpinned".
 """
 
-from . import lora, dora, swiglu, w8a8, merge  # noqa: F401
+from . import lora, dora, swiglu, w8a8, merge, geglu  # noqa: F401
