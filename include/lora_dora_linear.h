@@ -273,6 +273,34 @@ int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, fl
                         float* dAd, float* dBd,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ GeGLU MLP
+ * The LoRA MLP with the GeGLU activation: h = gelu(e) * u with gelu(e) = e . Phi(e), Phi the
+ * standard normal distribution function (approximate = 0), or its tanh form
+ * 0.5 e (1 + tanh(sqrt(2/pi) (e + 0.044715 e^3))) (approximate = 1) ("How Unsloth's FastLoRA
+ * Kernel ...", sections "Activation Function Fusion" and "Fused Forward Pass Architecture":
+ * the LoRA update injected with the SwiGLU and GeGLU activations computed in the same
+ * kernels).  Arguments, outputs, saved tensors, limits and routes as for the SwiGLU MLP;
+ * approximate other than 0 or 1 is LDL_E_INVAL. */
+int geglu_lora_mlp_fwd(int M, int K, int H, int r, float s_gate, float s_up, float s_down, int approximate,
+                       const void* X, int ldx, const void* Wg, const void* Ag, const void* Bg,
+                       const void* Wu, const void* Au, const void* Bu,
+                       const void* Wd, const void* Ad, const void* Bd,
+                       void* Out, int ldout, void* E_save, void* Gu_save, void* H_save, float* U_save,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the GeGLU LoRA MLP: dE = dH (.) u (.) gelu'(e), dU = dH (.) gelu(e), the rest as
+ * swiglu_lora_mlp_bwd. */
+int geglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, float s_down, int approximate,
+                       const void* dOut, int lddout, const void* X, int ldx,
+                       const void* Wg, const void* Ag, const void* Bg,
+                       const void* Wu, const void* Au, const void* Bu,
+                       const void* Wd, const void* Ad, const void* Bd,
+                       const void* E_saved, const void* Gu_saved, const void* H_saved,
+                       const float* U_saved,
+                       void* dX, int lddx, float* dAg, float* dBg, float* dAu, float* dBu,
+                       float* dAd, float* dBd,
+                       void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ W8A8
  * int8 weight x int8 activation base with per-row (activation) and per-column
  * (weight) dequant scales and the rank-tiled LoRA epilogue; the int32 product is

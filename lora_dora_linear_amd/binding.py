@@ -46,6 +46,10 @@ SIGNATURES = {
     "swiglu_lora_mlp_fwd": ([_i, _i, _i, _i, _f, _f, _f, _p, _i] + [_p] * 9 + [_p, _i] + [_p] * 5 + [_z, _p], _i),
     "swiglu_lora_mlp_bwd": ([_i, _i, _i, _i, _f, _f, _f, _p, _i, _p, _i] + [_p] * 13 + [_p, _i] + [_p] * 7
                             + [_z, _p], _i),
+    "geglu_lora_mlp_fwd": ([_i, _i, _i, _i, _f, _f, _f, _i, _p, _i] + [_p] * 9 + [_p, _i] + [_p] * 5 + [_z, _p],
+                           _i),
+    "geglu_lora_mlp_bwd": ([_i, _i, _i, _i, _f, _f, _f, _i, _p, _i, _p, _i] + [_p] * 13 + [_p, _i] + [_p] * 7
+                           + [_z, _p], _i),
     "w8a8_quantize_weight": ([_i, _i, _i, _p, _i, _p, _p, _p], _i),
     "w8a8_quantize_rows": ([_i, _i, _p, _i, _p, _p, _p], _i),
     "int8_gemm_raw": ([_i, _i, _i, _p, _i, _p, _i, _p, _i, _p], _i),
@@ -322,6 +326,15 @@ def dora_linear_bwd(dY, X, W0, A, B, m, U, Z, state, s, eps=1e-12, need_dx=True,
 # ------------------------------------------------------------------ SwiGLU MLP
 def swiglu_lora_mlp_fwd(X, gate, up, down, Out=None):
     """gate/up/down = (W, A, B, s).  Returns (Out, saved) with saved = dict(E, Gu, H, U)."""
+    return _glu_fwd("swiglu_lora_mlp_fwd", (), X, gate, up, down, Out)
+
+
+def geglu_lora_mlp_fwd(X, gate, up, down, approximate=False, Out=None):
+    """The GeGLU MLP (gelu exact, or its tanh form when approximate); as swiglu_lora_mlp_fwd."""
+    return _glu_fwd("geglu_lora_mlp_fwd", (int(bool(approximate)),), X, gate, up, down, Out)
+
+
+def _glu_fwd(name, extra, X, gate, up, down, Out):
     M, K = X.shape
     (Wg, Ag, Bg, sg), (Wu, Au, Bu, su), (Wd, Ad, Bd, sd) = gate, up, down
     H, r = Bg.shape
@@ -338,14 +351,21 @@ def swiglu_lora_mlp_fwd(X, gate, up, down, Out=None):
     Hs = torch.empty((M, H), dtype=bf, device=dev)
     U = torch.empty((M, 3 * r), dtype=torch.float32, device=dev)
     ws, n = _ws("swiglu_fwd", M, H, K, r, LDL_BF16, dev)
-    _check(lib().swiglu_lora_mlp_fwd(M, K, H, r, float(sg), float(su), float(sd), _ptr(X), ldx, _ptr(Wg), _ptr(Ag),
-                                     _ptr(Bg), _ptr(Wu), _ptr(Au), _ptr(Bu), _ptr(Wd), _ptr(Ad), _ptr(Bd), _ptr(Out),
-                                     ldo, _ptr(E), _ptr(Gu), _ptr(Hs), _ptr(U), _ptr(ws), n, _stream()),
-           "swiglu_lora_mlp_fwd")
+    _check(getattr(lib(), name)(M, K, H, r, float(sg), float(su), float(sd), *extra, _ptr(X), ldx, _ptr(Wg),
+                                _ptr(Ag), _ptr(Bg), _ptr(Wu), _ptr(Au), _ptr(Bu), _ptr(Wd), _ptr(Ad), _ptr(Bd),
+                                _ptr(Out), ldo, _ptr(E), _ptr(Gu), _ptr(Hs), _ptr(U), _ptr(ws), n, _stream()), name)
     return Out, {"E": E, "Gu": Gu, "H": Hs, "U": U}
 
 
 def swiglu_lora_mlp_bwd(dOut, X, gate, up, down, saved, need_dx=True, dX=None):
+    return _glu_bwd("swiglu_lora_mlp_bwd", (), dOut, X, gate, up, down, saved, need_dx, dX)
+
+
+def geglu_lora_mlp_bwd(dOut, X, gate, up, down, saved, approximate=False, need_dx=True, dX=None):
+    return _glu_bwd("geglu_lora_mlp_bwd", (int(bool(approximate)),), dOut, X, gate, up, down, saved, need_dx, dX)
+
+
+def _glu_bwd(name, extra, dOut, X, gate, up, down, saved, need_dx, dX):
     M, K = X.shape
     (Wg, Ag, Bg, sg), (Wu, Au, Bu, su), (Wd, Ad, Bd, sd) = gate, up, down
     H, r = Bg.shape
@@ -364,12 +384,12 @@ def swiglu_lora_mlp_bwd(dOut, X, gate, up, down, saved, need_dx=True, dX=None):
            "dA_up": torch.empty((r, K), dtype=f32, device=dev), "dB_up": torch.empty((H, r), dtype=f32, device=dev),
            "dA_down": torch.empty((r, H), dtype=f32, device=dev), "dB_down": torch.empty((K, r), dtype=f32, device=dev)}
     ws, n = _ws("swiglu_bwd", M, H, K, r, LDL_BF16, dev)
-    _check(lib().swiglu_lora_mlp_bwd(M, K, H, r, float(sg), float(su), float(sd), _ptr(dOut), lddo, _ptr(X), ldx,
-                                     _ptr(Wg), _ptr(Ag), _ptr(Bg), _ptr(Wu), _ptr(Au), _ptr(Bu), _ptr(Wd), _ptr(Ad),
-                                     _ptr(Bd), _ptr(saved["E"]), _ptr(saved["Gu"]), _ptr(saved["H"]),
-                                     _ptr(saved["U"]), _ptr(dX), lddx, _ptr(out["dA_gate"]), _ptr(out["dB_gate"]),
-                                     _ptr(out["dA_up"]), _ptr(out["dB_up"]), _ptr(out["dA_down"]),
-                                     _ptr(out["dB_down"]), _ptr(ws), n, _stream()), "swiglu_lora_mlp_bwd")
+    _check(getattr(lib(), name)(M, K, H, r, float(sg), float(su), float(sd), *extra, _ptr(dOut), lddo, _ptr(X), ldx,
+                                _ptr(Wg), _ptr(Ag), _ptr(Bg), _ptr(Wu), _ptr(Au), _ptr(Bu), _ptr(Wd), _ptr(Ad),
+                                _ptr(Bd), _ptr(saved["E"]), _ptr(saved["Gu"]), _ptr(saved["H"]), _ptr(saved["U"]),
+                                _ptr(dX), lddx, _ptr(out["dA_gate"]), _ptr(out["dB_gate"]), _ptr(out["dA_up"]),
+                                _ptr(out["dB_up"]), _ptr(out["dA_down"]), _ptr(out["dB_down"]), _ptr(ws), n,
+                                _stream()), name)
     return out
 
 

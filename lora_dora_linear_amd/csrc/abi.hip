@@ -747,11 +747,11 @@ static int mlp_check(int M, int K, int H, int r) {
   return LDL_OK;
 }
 
-int swiglu_lora_mlp_fwd(int M, int K, int H, int r, float s_gate, float s_up, float s_down, const void* X, int ldx,
-                        const void* Wg, const void* Ag, const void* Bg, const void* Wu, const void* Au,
-                        const void* Bu, const void* Wd, const void* Ad, const void* Bd, void* Out, int ldout,
-                        void* E_save, void* Gu_save, void* H_save, float* U_save, void* ws, size_t ws_bytes,
-                        void* stream) {
+static int glu_mlp_fwd(int act, int M, int K, int H, int r, float s_gate, float s_up, float s_down, const void* X,
+                       int ldx, const void* Wg, const void* Ag, const void* Bg, const void* Wu, const void* Au,
+                       const void* Bu, const void* Wd, const void* Ad, const void* Bd, void* Out, int ldout,
+                       void* E_save, void* Gu_save, void* H_save, float* U_save, void* ws, size_t ws_bytes,
+                       void* stream) {
   (void)ws; (void)ws_bytes;
   if (!nonnull({Wg, Ag, Bg, Wu, Au, Bu, Wd, Ad, Bd}) || (M > 0 && !nonnull({X, Out, E_save, Gu_save, H_save, U_save})))
     return LDL_E_INVAL;
@@ -775,6 +775,7 @@ int swiglu_lora_mlp_fwd(int M, int K, int H, int r, float s_gate, float s_up, fl
   p.S = U_save; p.ld_s = r3; p.r_epi = 2 * r; p.s_epi = s_gate; p.s_epi2 = s_up;
   p.e0 = Bg; p.e1 = Bu; p.e_ldn = r; p.e_ldj = 1; p.e_jsplit = r;
   p.out = E_save; p.ldo = H; p.out2 = Gu_save; p.ldo2 = H; p.out3 = H_save; p.ldo3 = H;
+  p.act = act;
   LDL_TRY(launch_gemm(GK_NT_SWIGLU_DUAL, p, st));
   // U_d = H.Ad^T, then the down projection
   LDL_TRY(rowproj(M, H, r, H_save, H, Ad, nullptr, r, H, U_save + 2 * r, r3, 1.f, st));
@@ -788,12 +789,12 @@ int swiglu_lora_mlp_fwd(int M, int K, int H, int r, float s_gate, float s_up, fl
   return LDL_OK;
 }
 
-int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, float s_down, const void* dOut,
-                        int lddout, const void* X, int ldx, const void* Wg, const void* Ag, const void* Bg,
-                        const void* Wu, const void* Au, const void* Bu, const void* Wd, const void* Ad, const void* Bd,
-                        const void* E_saved, const void* Gu_saved, const void* H_saved, const float* U_saved,
-                        void* dX, int lddx, float* dAg, float* dBg, float* dAu, float* dBu, float* dAd, float* dBd,
-                        void* ws, size_t ws_bytes, void* stream) {
+static int glu_mlp_bwd(int act, int M, int K, int H, int r, float s_gate, float s_up, float s_down,
+                       const void* dOut, int lddout, const void* X, int ldx, const void* Wg, const void* Ag,
+                       const void* Bg, const void* Wu, const void* Au, const void* Bu, const void* Wd, const void* Ad,
+                       const void* Bd, const void* E_saved, const void* Gu_saved, const void* H_saved,
+                       const float* U_saved, void* dX, int lddx, float* dAg, float* dBg, float* dAu, float* dBu,
+                       float* dAd, float* dBd, void* ws, size_t ws_bytes, void* stream) {
   if (!nonnull({Wg, Ag, Bg, Wu, Au, Bu, Wd, Ad, Bd, dAg, dBg, dAu, dBu, dAd, dBd, ws}) ||
       (M > 0 && !nonnull({dOut, X, E_saved, Gu_saved, H_saved, U_saved})))
     return LDL_E_INVAL;
@@ -830,6 +831,7 @@ int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, fl
     p.e0 = Ad; p.e1 = Ad; p.e_ldn = 1; p.e_ldj = H; p.e_jsplit = r;
     p.aux0 = E_saved; p.ld_aux0 = H; p.aux1 = Gu_saved; p.ld_aux1 = H;
     p.out = w.dEGu; p.ldo = 2 * H; p.out2 = w.dEGu + H; p.ldo2 = 2 * H;
+    p.act = act;
     LDL_TRY(launch_gemm(GK_NN_SWIGLU, p, st));
   }
   // dBd = s_d.dOut^T.U_d and dAd = s_d.V_d^T.H
@@ -876,6 +878,48 @@ int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, fl
                            rdp(r, K, w.partAgu + r, (size_t)K * w.rp2, w.nsAgu, w.rp2, true, 1.f, dAu, K), st));
   }
   return LDL_OK;
+}
+
+int swiglu_lora_mlp_fwd(int M, int K, int H, int r, float s_gate, float s_up, float s_down, const void* X, int ldx,
+                        const void* Wg, const void* Ag, const void* Bg, const void* Wu, const void* Au,
+                        const void* Bu, const void* Wd, const void* Ad, const void* Bd, void* Out, int ldout,
+                        void* E_save, void* Gu_save, void* H_save, float* U_save, void* ws, size_t ws_bytes,
+                        void* stream) {
+  return glu_mlp_fwd(ACT_SILU, M, K, H, r, s_gate, s_up, s_down, X, ldx, Wg, Ag, Bg, Wu, Au, Bu, Wd, Ad, Bd, Out,
+                     ldout, E_save, Gu_save, H_save, U_save, ws, ws_bytes, stream);
+}
+
+int swiglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, float s_down, const void* dOut,
+                        int lddout, const void* X, int ldx, const void* Wg, const void* Ag, const void* Bg,
+                        const void* Wu, const void* Au, const void* Bu, const void* Wd, const void* Ad, const void* Bd,
+                        const void* E_saved, const void* Gu_saved, const void* H_saved, const float* U_saved,
+                        void* dX, int lddx, float* dAg, float* dBg, float* dAu, float* dBu, float* dAd, float* dBd,
+                        void* ws, size_t ws_bytes, void* stream) {
+  return glu_mlp_bwd(ACT_SILU, M, K, H, r, s_gate, s_up, s_down, dOut, lddout, X, ldx, Wg, Ag, Bg, Wu, Au, Bu, Wd, Ad,
+                     Bd, E_saved, Gu_saved, H_saved, U_saved, dX, lddx, dAg, dBg, dAu, dBu, dAd, dBd, ws, ws_bytes,
+                     stream);
+}
+
+int geglu_lora_mlp_fwd(int M, int K, int H, int r, float s_gate, float s_up, float s_down, int approximate,
+                       const void* X, int ldx, const void* Wg, const void* Ag, const void* Bg, const void* Wu,
+                       const void* Au, const void* Bu, const void* Wd, const void* Ad, const void* Bd, void* Out,
+                       int ldout, void* E_save, void* Gu_save, void* H_save, float* U_save, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (approximate != 0 && approximate != 1) return LDL_E_INVAL;
+  return glu_mlp_fwd(approximate ? ACT_GELU_TANH : ACT_GELU, M, K, H, r, s_gate, s_up, s_down, X, ldx, Wg, Ag, Bg, Wu,
+                     Au, Bu, Wd, Ad, Bd, Out, ldout, E_save, Gu_save, H_save, U_save, ws, ws_bytes, stream);
+}
+
+int geglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, float s_down, int approximate,
+                       const void* dOut, int lddout, const void* X, int ldx, const void* Wg, const void* Ag,
+                       const void* Bg, const void* Wu, const void* Au, const void* Bu, const void* Wd, const void* Ad,
+                       const void* Bd, const void* E_saved, const void* Gu_saved, const void* H_saved,
+                       const float* U_saved, void* dX, int lddx, float* dAg, float* dBg, float* dAu, float* dBu,
+                       float* dAd, float* dBd, void* ws, size_t ws_bytes, void* stream) {
+  if (approximate != 0 && approximate != 1) return LDL_E_INVAL;
+  return glu_mlp_bwd(approximate ? ACT_GELU_TANH : ACT_GELU, M, K, H, r, s_gate, s_up, s_down, dOut, lddout, X, ldx,
+                     Wg, Ag, Bg, Wu, Au, Bu, Wd, Ad, Bd, E_saved, Gu_saved, H_saved, U_saved, dX, lddx, dAg, dBg,
+                     dAu, dBu, dAd, dBd, ws, ws_bytes, stream);
 }
 
 // =========================================================================== W8A8

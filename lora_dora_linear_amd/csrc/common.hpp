@@ -151,4 +151,26 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4
 __device__ __forceinline__ float sigmoid_f(float e) { return __builtin_amdgcn_rcpf(1.0f + __expf(-e)); }
 __device__ __forceinline__ float silu_f(float e) { return e * sigmoid_f(e); }
 
+// Gate activations of the gated MLPs (GemmParams::act): SiLU e.sigma(e) (SwiGLU); GELU
+// e.Phi(e) with Phi the standard normal distribution function, 0.5 (1 + erf(e / sqrt 2))
+// (GeGLU); and GELU in its tanh form 0.5 e (1 + tanh(sqrt(2/pi) (e + 0.044715 e^3))).
+enum : int { ACT_SILU = 0, ACT_GELU = 1, ACT_GELU_TANH = 2 };
+__device__ __forceinline__ float glu_act(float e, int act) {
+  if (act == ACT_GELU) return 0.5f * e * (1.f + erff(e * 0.70710678118654752f));
+  if (act == ACT_GELU_TANH) return 0.5f * e * (1.f + tanhf(0.79788456080286536f * (e + 0.044715f * e * e * e)));
+  return silu_f(e);
+}
+// d act / d e:  SiLU sigma (1 + e (1 - sigma));  GELU Phi(e) + e phi(e), phi the normal density;
+// tanh form 0.5 (1 + t) + 0.5 e (1 - t^2) sqrt(2/pi) (1 + 3 . 0.044715 e^2)
+__device__ __forceinline__ float glu_act_grad(float e, int act) {
+  if (act == ACT_GELU)
+    return 0.5f * (1.f + erff(e * 0.70710678118654752f)) + e * 0.39894228040143268f * __expf(-0.5f * e * e);
+  if (act == ACT_GELU_TANH) {
+    const float t = tanhf(0.79788456080286536f * (e + 0.044715f * e * e * e));
+    return 0.5f * (1.f + t) + 0.5f * e * (1.f - t * t) * 0.79788456080286536f * (1.f + 0.134145f * e * e);
+  }
+  const float sg = sigmoid_f(e);
+  return sg * (1.f + e * (1.f - sg));
+}
+
 }  // namespace ldl

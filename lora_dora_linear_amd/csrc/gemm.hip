@@ -149,7 +149,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
     if (swb_split(p, h)) {
       hipError_t e = launch_gemm(GK_NN_PLAIN, h, st);
       if (e == hipSuccess)
-        e = launch_swiglu_bwd(p.out, p.ldo, p.aux0, p.ld_aux0, p.aux1, p.ld_aux1, p.out2, p.ldo2, p.M, p.N, st);
+        e = launch_swiglu_bwd(p.out, p.ldo, p.aux0, p.ld_aux0, p.aux1, p.ld_aux1, p.out2, p.ldo2, p.M, p.N, p.act, st);
       return e;
     }
   }

@@ -38,15 +38,15 @@ __host__ __device__ constexpr int g16_nn_row(int k) { return k * kG16NNRow + (k 
 // NN: Q is [K, N] (else [N, K]); LR: number of low-rank k-tiles in front of the loop (0: no
 // low-rank term; 1: rank r_epi <= 64 of one segment; 2: the dual tile's gate and up terms);
 // DORA (NT only): two outputs, out2 = z (the unscaled sum) and out = z * col_scale[n] + bias[n];
-// SWB (NN only): the SwiGLU backward of the product dh with e = aux0, u = aux1:
-// out = dh u sigma(e) (1 + e (1 - sigma(e))) (de) and out2 = dh e sigma(e) (du)
+// SWB (NN only): the gated-MLP backward of the product dh with e = aux0, u = aux1:
+// out = dh u act'(e) (de) and out2 = dh act(e) (du), act = p.act (SiLU: act' = sigma (1 + e (1 - sigma)))
 // BN_: tile width, 256, or 192 for NT (3072 columns at 4096 rows then make 256 tiles, one full
 // round of the 256 CUs, where 256-column tiles leave a quarter of the chip idle)
 // SWF (NT only, the SwiGLU forward): each tile covers 128 hidden units; its Q rows are the 128
 // gate rows (b0) then the 128 up rows (b1) of those units, so the waves with wn = 0 hold
 // e and the waves with wn = 1 hold u of the same (token, unit) in the same lanes.  Outputs:
-// out = e, out2 = u, out3 = h = silu(e) u, all from the fp32 accumulators (e is handed to
-// the u waves through LDS).
+// out = e, out2 = u, out3 = h = act(e) u (act = p.act: SiLU or GELU), all from the fp32
+// accumulators (e is handed to the u waves through LDS).
 // I8 (NT only, the W8A8 forward): P and Q are int8 with 128 k per k-tile (the same 128-byte
 // LDS rows and 16-byte fragments), v_mfma_i32_16x16x64_i8 into exact int32 accumulators,
 // dequantised after the loop to acc . row_scale[m] . col_scale[n] in fp32; the low-rank term
@@ -508,13 +508,10 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
             const u32x2 uu = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux1) + m * p.ld_aux1 + n0 + cl);
             const float u4[4] = {bf16_lo(uu[0]), bf16_hi(uu[0]), bf16_lo(uu[1]), bf16_hi(uu[1])};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float sg = sigmoid_f(e4[e]);
-              r4[e] = v[e] * u4[e] * sg * (1.f + e4[e] * (1.f - sg));
-            }
+            for (int e = 0; e < 4; ++e) r4[e] = v[e] * u4[e] * glu_act_grad(e4[e], p.act);
           } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) r4[e] = v[e] * e4[e] * sigmoid_f(e4[e]);
+            for (int e = 0; e < 4; ++e) r4[e] = v[e] * glu_act(e4[e], p.act);
           }
           u32x2 w;
           w[0] = pack_bf16x2(r4[0], r4[1]);
@@ -597,8 +594,8 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
           const f32x4 e = *reinterpret_cast<const f32x4*>(smem0 + xoff(2 * wm, i, j));
           const f32x4 u = *reinterpret_cast<const f32x4*>(smem0 + xoff(2 * wm + 1, i, j));
           u32x2 w;
-          w[0] = pack_bf16x2(silu_f(e[0]) * u[0], silu_f(e[1]) * u[1]);
-          w[1] = pack_bf16x2(silu_f(e[2]) * u[2], silu_f(e[3]) * u[3]);
+          w[0] = pack_bf16x2(glu_act(e[0], p.act) * u[0], glu_act(e[1], p.act) * u[1]);
+          w[1] = pack_bf16x2(glu_act(e[2], p.act) * u[2], glu_act(e[3], p.act) * u[3]);
           *reinterpret_cast<u32x2*>(h_ptr(r, j * 16 + 4 * lq)) = w;
         }
       }

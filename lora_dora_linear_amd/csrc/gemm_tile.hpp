@@ -63,6 +63,7 @@ struct GemmParams {
   const void* aux1; int ld_aux1;
   float* side_save; int ld_side_save;
   int seed_hilo;                     // four-wave tile: low-rank term as bf16 hi + lo (set by the launcher)
+  int act;                           // gated MLP activation: ACT_SILU, ACT_GELU, ACT_GELU_TANH
 };
 
 template <int BM_, int BN_, bool I8_, bool NN_, bool BINT8_, bool ASCALE_, int SIDE_RSP_, bool SLOAD_, int EPI_,
@@ -728,12 +729,12 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
   auto out_vals = [&](auto o_const, int m, int n, const float* v, const float* vu) -> u32x2 {
     constexpr int o = decltype(o_const)::value;
     u32x2 w;
-    if constexpr (DUAL) {            // o: 0 e, 1 u, 2 silu(e) * u
+    if constexpr (DUAL) {            // o: 0 e, 1 u, 2 act(e) * u
       if constexpr (o == 0) { w[0] = pack_bf16x2(v[0], v[1]); w[1] = pack_bf16x2(v[2], v[3]); }
       else if constexpr (o == 1) { w[0] = pack_bf16x2(vu[0], vu[1]); w[1] = pack_bf16x2(vu[2], vu[3]); }
       else {
-        w[0] = pack_bf16x2(silu_f(v[0]) * vu[0], silu_f(v[1]) * vu[1]);
-        w[1] = pack_bf16x2(silu_f(v[2]) * vu[2], silu_f(v[3]) * vu[3]);
+        w[0] = pack_bf16x2(glu_act(v[0], p.act) * vu[0], glu_act(v[1], p.act) * vu[1]);
+        w[1] = pack_bf16x2(glu_act(v[2], p.act) * vu[2], glu_act(v[3], p.act) * vu[3]);
       }
     } else if constexpr (EPI == EPI_PLAIN || EPI == EPI_DEQUANT || EPI == EPI_DORA) {
       float b4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -750,20 +751,19 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
         w[1] = pack_bf16x2(v[2] + b4[2], v[3] + b4[3]);
       }
     } else if constexpr (EPI == EPI_SWIGLU_BWD) {  // o: 0 de, 1 dgu
-      const u32x2 ee = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux0) + (size_t)m * p.ld_aux0 + n);
+      // rows past M are staged but never written out; their e and u reads stay on row M - 1
+      const size_t mr = (size_t)min(m, M - 1);
+      const u32x2 ee = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux0) + mr * p.ld_aux0 + n);
       const float e4[4] = {bf16_lo(ee[0]), bf16_hi(ee[0]), bf16_lo(ee[1]), bf16_hi(ee[1])};
       float r4[4];
       if constexpr (o == 0) {
-        const u32x2 gg = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux1) + (size_t)m * p.ld_aux1 + n);
+        const u32x2 gg = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.aux1) + mr * p.ld_aux1 + n);
         const float g4[4] = {bf16_lo(gg[0]), bf16_hi(gg[0]), bf16_lo(gg[1]), bf16_hi(gg[1])};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float sg = sigmoid_f(e4[e]);
-          r4[e] = v[e] * g4[e] * sg * (1.f + e4[e] * (1.f - sg));
-        }
+        for (int e = 0; e < 4; ++e) r4[e] = v[e] * g4[e] * glu_act_grad(e4[e], p.act);
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r4[e] = v[e] * e4[e] * sigmoid_f(e4[e]);
+        for (int e = 0; e < 4; ++e) r4[e] = v[e] * glu_act(e4[e], p.act);
       }
       w[0] = pack_bf16x2(r4[0], r4[1]);
       w[1] = pack_bf16x2(r4[2], r4[3]);

@@ -77,9 +77,9 @@ hipError_t launch_dora_norm(int N, int r, float s, float eps, const float* w0_su
 hipError_t launch_scale_cols(const void* in, int M, int N, int ld, const float* g, void* out, int ldo,
                              hipStream_t st);
 
-// SwiGLU backward over bf16 [M, N] arrays: dh (read from dE) -> de in place, du written
+// gated-MLP backward over bf16 [M, N] arrays: dh (read from dE) -> de in place, du written (act: ACT_*)
 hipError_t launch_swiglu_bwd(void* dE, int ld_de, const void* E, int ld_e, const void* U, int ld_u, void* dU,
-                             int ld_du, int M, int N, hipStream_t st);
+                             int ld_du, int M, int N, int act, hipStream_t st);
 hipError_t launch_dora_finalize(int N, int r, float s, float eps, const float* partT, const float* cspart,
                                 int nsplit, int rpT, const float* norm, const float* g, const float* m,
                                 const float* P, const float* G, const uint16_t* B,

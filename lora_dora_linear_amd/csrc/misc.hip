@@ -179,12 +179,12 @@ hipError_t launch_scale_cols(const void* in, int M, int N, int ld, const float* 
   return hipGetLastError();
 }
 
-// SwiGLU backward from the stored bf16 dh, e and u (8 columns per thread):
-// de = dh u sigma(e) (1 + e (1 - sigma(e))) overwrites dh in place, du = dh e sigma(e).
+// Gated-MLP backward from the stored bf16 dh, e and u (8 columns per thread):
+// de = dh u act'(e) overwrites dh in place, du = dh act(e) (SiLU: act' = sigma (1 + e (1 - sigma))).
 // Each thread reads its own dh chunk before writing de there.
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(uint16_t* dE, int ld_de, const uint16_t* E, int ld_e,
                                                          const uint16_t* U, int ld_u, uint16_t* dU, int ld_du, int M,
-                                                         int N) {
+                                                         int N, int act) {
   const unsigned per_row = (unsigned)N / 8u;
   const size_t total = (size_t)M * per_row;
   for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (size_t)gridDim.x * blockDim.x) {
@@ -194,10 +194,8 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(uint16_t* dE, int ld_de
     u32x4 de, du;
     for (int i = 0; i < 4; ++i) {
       const float e0 = bf16_lo(e[i]), e1 = bf16_hi(e[i]), d0 = bf16_lo(d[i]), d1 = bf16_hi(d[i]);
-      const float s0 = sigmoid_f(e0), s1 = sigmoid_f(e1);
-      de[i] = pack_bf16x2(d0 * bf16_lo(u[i]) * s0 * (1.f + e0 * (1.f - s0)),
-                          d1 * bf16_hi(u[i]) * s1 * (1.f + e1 * (1.f - s1)));
-      du[i] = pack_bf16x2(d0 * e0 * s0, d1 * e1 * s1);
+      de[i] = pack_bf16x2(d0 * bf16_lo(u[i]) * glu_act_grad(e0, act), d1 * bf16_hi(u[i]) * glu_act_grad(e1, act));
+      du[i] = pack_bf16x2(d0 * glu_act(e0, act), d1 * glu_act(e1, act));
     }
     st16(dE + m * (size_t)ld_de + c, de);
     st16(dU + m * (size_t)ld_du + c, du);
@@ -205,7 +203,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(uint16_t* dE, int ld_de
 }
 
 hipError_t launch_swiglu_bwd(void* dE, int ld_de, const void* E, int ld_e, const void* U, int ld_u, void* dU,
-                             int ld_du, int M, int N, hipStream_t st) {
+                             int ld_du, int M, int N, int act, hipStream_t st) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (N % 8 || ld_de % 8 || ld_e % 8 || ld_u % 8 || ld_du % 8 || ld_de < N || ld_e < N || ld_u < N || ld_du < N)
     return hipErrorInvalidValue;
@@ -214,7 +212,7 @@ hipError_t launch_swiglu_bwd(void* dE, int ld_de, const void* E, int ld_e, const
   if (blocks > 8192) blocks = 8192;   // ~7 grid-stride steps a thread at 8192 x 14336 (2048 blocks: 222 -> 213 us)
   hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<uint16_t*>(dE), ld_de,
                      static_cast<const uint16_t*>(E), ld_e, static_cast<const uint16_t*>(U), ld_u,
-                     static_cast<uint16_t*>(dU), ld_du, M, N);
+                     static_cast<uint16_t*>(dU), ld_du, M, N, act);
   return hipGetLastError();
 }
 

@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
               "swiglu_lora_mlp_fwd", "swiglu_lora_mlp_bwd", "w8a8_lora_linear_fwd", "w8a8_lora_linear_bwd",
               "w8a8_quantize_weight", "w8a8_quantize_rows", "int8_gemm_raw", "ldl_workspace_bytes",
               "ldl_status_string", "dora_state_floats", "ldl_set_tuning", "ldl_version", "lora_linear_bwd_noalloc",
-              "ldl_noalloc_scratch_bytes", "lora_merge_fwd", "lora_merge_bwd"):
+              "ldl_noalloc_scratch_bytes", "lora_merge_fwd", "lora_merge_bwd", "geglu_lora_mlp_fwd",
+              "geglu_lora_mlp_bwd"):
         assert n in names, n
 
 
@@ -200,6 +201,11 @@ def test_swiglu_and_w8a8_validation(L):
     assert f(*sw(K=96)) == UNSUP              # K not a multiple of 64
     assert f(*sw(Wg=NUL)) == INVAL
     assert f(*sw(ldo=32)) == INVAL
+    g = L.geglu_lora_mlp_fwd
+    a = list(sw(r=65)); a.insert(7, 0)
+    assert g(*a) == UNSUP
+    a = list(sw()); a.insert(7, 2)
+    assert g(*a) == INVAL                      # approximate must be 0 or 1
     w = L.w8a8_lora_linear_fwd
     need = L.ldl_workspace_bytes(6, 64, 128, 128, 16, 1)
 
