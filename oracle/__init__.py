@@ -29,9 +29,10 @@ Modules
   w8a8   - per-row / per-channel int8 quantiser and the int8 base + LoRA layer.
   merge  - the LoRA merge (adapted weight formed explicitly) and its backward.
   geglu  - LoRA MLP with the GeGLU activation (exact and tanh forms of GELU).
+  dropout - weight-space dropout of the adapters (a keep mask over lora_down's inputs).
 
 Parity status of every function is listed in its own docstring; functions
 with no independent pin say "parity unpinned".
 """
 
-from . import lora, dora, swiglu, w8a8, merge, geglu  # noqa: F401
+from . import lora, dora, swiglu, w8a8, merge, geglu, dropout  # noqa: F401
