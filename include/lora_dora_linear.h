@@ -172,6 +172,20 @@ int lora_linear_bwd_noalloc(int M, int N, int K, int r, float s, int dtype,
 /* Size in bytes of the per-device scratch array lora_linear_bwd_noalloc uses. */
 size_t ldl_noalloc_scratch_bytes(void);
 
+/* ------------------------------------------------------------------------ weight-space dropout
+ * Dropout of the adapter drawn once per forward in weight space and shared with the DoRA norm
+ * terms ("LoRA/DoRA fast forward: no weight materialization", section "Fidelity"): a keep
+ * mask over the input features of lora_down (the same for every rank), drawn by the caller,
+ * with the inverted-dropout scale 1 / (1 - p).  The layer with dropout is the plain layer run
+ * with A_drop = A . diag(keep) and s / (1 - p) in place of A and s (lora_linear_* ,
+ * dora_linear_*, w8a8_lora_linear_*: the DoRA norm then sees the same dropped factor), after
+ * which lora_dropout_grad zeroes the dropped columns of the factor gradient dA.  Exact: the
+ * kernels copy or zero elements.
+ *   lora_dropout_mask: A [r,K] (dtype), keep [K] (0 drops feature k), A_drop [r,K] (dtype;
+ *   may be A itself).  lora_dropout_grad: dA [r,K] fp32 masked in place. */
+int lora_dropout_mask(int r, int K, int dtype, const void* A, const uint8_t* keep, void* A_drop, void* stream);
+int lora_dropout_grad(int r, int K, const uint8_t* keep, float* dA, void* stream);
+
 /* ------------------------------------------------------------------------ LoRA merge
  * The adapted weight formed explicitly, for export or for merging an adapter into its base
  * weight: the merge forward (the delta) and merge backward of the lora family ("Fused

@@ -36,6 +36,8 @@ SIGNATURES = {
     "lora_linear_bwd_noalloc": ([_i, _i, _i, _i, _f, _i, _p, _i, _p, _i, _p, _i, _p, _p, _p, _i, _p, _i, _p, _p,
                                  _p, _p], _i),
     "ldl_noalloc_scratch_bytes": ([], _z),
+    "lora_dropout_mask": ([_i, _i, _i, _p, _p, _p, _p], _i),
+    "lora_dropout_grad": ([_i, _i, _p, _p, _p], _i),
     "lora_merge_fwd": ([_i, _i, _i, _f, _i, _p, _i, _p, _p, _p, _i, _p], _i),
     "lora_merge_bwd": ([_i, _i, _i, _f, _i, _p, _i, _p, _p, _p, _p, _p, _z, _p], _i),
     "dora_prepare": ([_i, _i, _i, _p, _i, _p, _p], _i),
@@ -222,6 +224,26 @@ def lora_linear_bwd_noalloc(dY, X, W0, A, B, s, U=None, need_dx=True, need_dbias
     args = args[:4] + (float(s),) + args[5:]
     _check(lib().lora_linear_bwd_noalloc(*args, _stream()), "lora_linear_bwd_noalloc")
     return out
+
+
+# ------------------------------------------------------------------ weight-space dropout
+def lora_dropout_mask(A, keep):
+    """A . diag(keep): lora_down with the dropped input features zeroed (keep: uint8 [K])."""
+    r, K = A.shape
+    _need(A, "A", A.dtype, (r, K))
+    _need(keep, "keep", torch.uint8, (K,))
+    out = torch.empty_like(A)
+    _check(lib().lora_dropout_mask(r, K, _dt(A), _ptr(A), _ptr(keep), _ptr(out), _stream()), "lora_dropout_mask")
+    return out
+
+
+def lora_dropout_grad(dA, keep):
+    """Zeroes the dropped columns of a factor gradient dA [r, K] (fp32) in place; returns dA."""
+    r, K = dA.shape
+    _need(dA, "dA", torch.float32, (r, K))
+    _need(keep, "keep", torch.uint8, (K,))
+    _check(lib().lora_dropout_grad(r, K, _ptr(keep), _ptr(dA), _stream()), "lora_dropout_grad")
+    return dA
 
 
 # ------------------------------------------------------------------ LoRA merge

@@ -555,6 +555,24 @@ int lora_linear_bwd_noalloc(int M, int N, int K, int r, float s, int dtype, cons
 
 size_t ldl_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
+// =========================================================================== weight-space dropout
+int lora_dropout_mask(int r, int K, int dtype, const void* A, const uint8_t* keep, void* A_drop, void* stream) {
+  if (!nonnull({A, keep, A_drop})) return LDL_E_INVAL;
+  if (dtype != LDL_F32 && dtype != LDL_BF16) return LDL_E_INVAL;
+  if (r <= 0 || K <= 0) return LDL_E_INVAL;
+  if (!small(r, K, 4)) return LDL_E_UNSUPPORTED;
+  LDL_TRY(launch_mask_cols(A, keep, r, K, dtype == LDL_BF16 ? 2 : 4, A_drop, S(stream)));
+  return LDL_OK;
+}
+
+int lora_dropout_grad(int r, int K, const uint8_t* keep, float* dA, void* stream) {
+  if (!nonnull({keep, dA})) return LDL_E_INVAL;
+  if (r <= 0 || K <= 0) return LDL_E_INVAL;
+  if (!small(r, K, 4)) return LDL_E_UNSUPPORTED;
+  LDL_TRY(launch_mask_cols(dA, keep, r, K, 4, dA, S(stream)));
+  return LDL_OK;
+}
+
 // =========================================================================== LoRA merge
 int lora_merge_fwd(int N, int K, int r, float s, int dtype, const void* W0, int ldw, const void* A, const void* B,
                    void* W, int ldo, void* stream) {

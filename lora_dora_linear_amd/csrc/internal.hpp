@@ -90,6 +90,9 @@ hipError_t launch_merge(int N, int K, int r, float s, int bf16, const void* W0, 
                         void* W, int ldo, hipStream_t st);
 hipError_t launch_bf16_to_f32(const void* in, size_t n, float* out, hipStream_t st);
 
+// weight-space dropout: out[j, k] = keep[k] ? in[j, k] : 0 (esz 2: bf16, 4: fp32; in place allowed)
+hipError_t launch_mask_cols(const void* in, const uint8_t* keep, int rows, int K, int esz, void* out, hipStream_t st);
+
 // W8A8 helpers
 hipError_t launch_quantize_rows(const void* X, int in_f32, int M, int K, int ldx, int8_t* q, float* scale,
                                 hipStream_t st);

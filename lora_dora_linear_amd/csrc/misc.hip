@@ -239,6 +239,30 @@ hipError_t launch_dora_finalize(int N, int r, float s, float eps, const float* p
   return hipGetLastError();
 }
 
+// ============================================================================ weight-space dropout
+// out[j, k] = keep[k] ? A[j, k] : 0 over an [r, K] factor (element size esz bytes), and the
+// same masking in place on an fp32 gradient.  Exact (elements are copied or zeroed).
+template <class T>
+__global__ void mask_cols_kernel(const T* in, const uint8_t* keep, size_t rows, int K, T* out) {
+  const size_t n = rows * (size_t)K;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    out[i] = keep[i % K] ? in[i] : T(0);
+}
+
+hipError_t launch_mask_cols(const void* in, const uint8_t* keep, int rows, int K, int esz, void* out, hipStream_t st) {
+  const size_t n = (size_t)rows * K;
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  if (esz == 2)
+    hipLaunchKernelGGL(mask_cols_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(in), keep, (size_t)rows, K, static_cast<uint16_t*>(out));
+  else
+    hipLaunchKernelGGL(mask_cols_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const float*>(in),
+                       keep, (size_t)rows, K, static_cast<float*>(out));
+  return hipGetLastError();
+}
+
 // ============================================================================ int8 quantiser
 // Symmetric per-row codes: scale = absmax / 127 (fp32), q = clamp(rint(x / scale), +-127)
 // with the quotient in fp32 and ties to even; scale 0 -> q = 0.  One wave per row.

@@ -34,6 +34,7 @@ def test_header_declares_the_entry_points():
               "w8a8_quantize_weight", "w8a8_quantize_rows", "int8_gemm_raw", "ldl_workspace_bytes",
               "ldl_status_string", "dora_state_floats", "ldl_set_tuning", "ldl_version", "lora_linear_bwd_noalloc",
               "ldl_noalloc_scratch_bytes", "lora_merge_fwd", "lora_merge_bwd", "geglu_lora_mlp_fwd",
+              "lora_dropout_mask", "lora_dropout_grad",
               "geglu_lora_mlp_bwd"):
         assert n in names, n
 
