@@ -172,6 +172,43 @@ int lora_linear_bwd_noalloc(int M, int N, int K, int r, float s, int dtype,
 /* Size in bytes of the per-device scratch array lora_linear_bwd_noalloc uses. */
 size_t ldl_noalloc_scratch_bytes(void);
 
+/* ------------------------------------------------------------------------ fused QKV leaves
+ * Several LoRA adapters ("leaves", e.g. query / key / value) over one concatenated base
+ * weight, computed as one base GEMM in which each output column takes its own leaf's
+ * adapter ("How Unsloth's FastLoRA Kernel ...", section "Fused Forward Pass Architecture":
+ * a fused Function for the attention projections; "nunchaku-style kernel fusion ...",
+ * LoRA-epilogue commit: fused-qkv adapters narrow lora_up to the leaf's rows).  bf16 only.
+ *   Leaf l has n_leaf[l] output columns, scale s_leaf[l] and factors A_l [r,K], B_l
+ *   [n_leaf[l], r]; W0 = [W0_1; ..; W0_L] [N,K] with N = sum n_leaf (row stride ldw),
+ *   A = [A_1; ..; A_L] [L r, K], B = [B_1; ..; B_L] [N, r] (both dense), bias [N] or NULL.
+ *   Y[:, leaf l] = X.W0_l^T + s_l.(X.A_l^T).B_l^T (+ bias).  Y [M,N] (ldy); U_save [M, L r]
+ *   fp32 (ldu) or NULL receives [X.A_1^T | .. | X.A_L^T].
+ *   n_leaf and s_leaf are HOST arrays of nleaf entries, read during the call only.
+ *   Limits: 1 <= nleaf <= 8, every n_leaf[l] a multiple of 64, K a multiple of 64, r a
+ *   multiple of 8 with L r <= 128.  When L r <= 64 and the shape runs on the four-wave
+ *   tile (more than 128 rows, N a multiple of 256 or filling 192-column tiles) the whole
+ *   layer is one rank-(L r) projection plus one GEMM; otherwise each leaf runs as
+ *   lora_linear_fwd on its column block.
+ *   Workspace: ldl_multi_workspace_bytes(LDL_OP_LORA_FWD, ...) (0 needed with U_save). */
+size_t ldl_multi_workspace_bytes(int op, int M, int K, int nleaf, const int* n_leaf, int r);
+
+int lora_multi_linear_fwd(int M, int K, int nleaf, const int* n_leaf, int r, const float* s_leaf, int dtype,
+                          const void* X, int ldx, const void* W0, int ldw, const void* A, const void* B,
+                          const void* bias, void* Y, int ldy, float* U_save, int ldu,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the fused leaves (W0 frozen):
+ *   V_l = s_l.dY_l.B_l;  dX = dY.W0 + sum_l V_l.A_l (one GEMM of rank L r);
+ *   dA_l = V_l^T.X;  dB_l = s_l.dY_l^T.U_l;  dbias = sum_m dY.
+ *   dY [M,N] (lddy), X (ldx), W0 (ldw), U_saved [M, L r] (ldu) or NULL (recomputed).
+ *   dX [M,K] bf16 (lddx) or NULL; dA [L r, K], dB [N, r] fp32 (overwritten); dbias [N] fp32
+ *   or NULL.  Workspace: ldl_multi_workspace_bytes(LDL_OP_LORA_BWD, ...). */
+int lora_multi_linear_bwd(int M, int K, int nleaf, const int* n_leaf, int r, const float* s_leaf, int dtype,
+                          const void* dY, int lddy, const void* X, int ldx, const void* W0, int ldw,
+                          const void* A, const void* B, const float* U_saved, int ldu,
+                          void* dX, int lddx, float* dA, float* dB, float* dbias,
+                          void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ weight-space dropout
  * Dropout of the adapter drawn once per forward in weight space and shared with the DoRA norm
  * terms ("LoRA/DoRA fast forward: no weight materialization", section "Fidelity"): a keep

@@ -36,6 +36,11 @@ SIGNATURES = {
     "lora_linear_bwd_noalloc": ([_i, _i, _i, _i, _f, _i, _p, _i, _p, _i, _p, _i, _p, _p, _p, _i, _p, _i, _p, _p,
                                  _p, _p], _i),
     "ldl_noalloc_scratch_bytes": ([], _z),
+    "ldl_multi_workspace_bytes": ([_i, _i, _i, _i, _p, _i], _z),
+    "lora_multi_linear_fwd": ([_i, _i, _i, _p, _i, _p, _i, _p, _i, _p, _i, _p, _p, _p, _p, _i, _p, _i, _p, _z, _p],
+                              _i),
+    "lora_multi_linear_bwd": ([_i, _i, _i, _p, _i, _p, _i, _p, _i, _p, _i, _p, _i, _p, _p, _p, _i, _p, _i, _p, _p,
+                               _p, _p, _z, _p], _i),
     "lora_dropout_mask": ([_i, _i, _i, _p, _p, _p, _p], _i),
     "lora_dropout_grad": ([_i, _i, _p, _p, _p], _i),
     "lora_merge_fwd": ([_i, _i, _i, _f, _i, _p, _i, _p, _p, _p, _i, _p], _i),
@@ -224,6 +229,78 @@ def lora_linear_bwd_noalloc(dY, X, W0, A, B, s, U=None, need_dx=True, need_dbias
     args = args[:4] + (float(s),) + args[5:]
     _check(lib().lora_linear_bwd_noalloc(*args, _stream()), "lora_linear_bwd_noalloc")
     return out
+
+
+# ------------------------------------------------------------------ fused QKV leaves
+def _leaf_arrays(n_leaf, s_leaf):
+    L = len(n_leaf)
+    if len(s_leaf) != L:
+        raise ValueError("n_leaf and s_leaf must have the same length")
+    return L, (ctypes.c_int * L)(*[int(n) for n in n_leaf]), (ctypes.c_float * L)(*[float(v) for v in s_leaf])
+
+
+def multi_workspace_bytes(op, M, K, n_leaf, r):
+    L = len(n_leaf)
+    arr = (ctypes.c_int * L)(*[int(n) for n in n_leaf])
+    return int(lib().ldl_multi_workspace_bytes(OPS[op] if isinstance(op, str) else op, M, K, L,
+                                               ctypes.cast(arr, _p), r))
+
+
+def lora_multi_linear_fwd(X, W0, A, B, n_leaf, s_leaf, bias=None, save_u=True, Y=None, U=None):
+    """Several adapters over one concatenated base weight: Y[:, leaf l] = X.W0_l^T +
+    s_l.(X.A_l^T).B_l^T (+ bias).  A = [A_1; ..; A_L] [L r, K], B = [B_1; ..; B_L] [N, r].
+    Returns (Y, U [M, L r] or None)."""
+    M, K = X.shape
+    N, r = B.shape
+    L, nl, sl = _leaf_arrays(n_leaf, s_leaf)
+    if sum(int(n) for n in n_leaf) != N:
+        raise ValueError("the leaf widths must add up to the rows of B")
+    dt = X.dtype
+    ldx = _mat(X, "X", dt, (M, K))
+    ldw = _mat(W0, "W0", dt, (N, K))
+    _need(A, "A", dt, (L * r, K))
+    _need(B, "B", dt, (N, r))
+    if bias is not None:
+        _need(bias, "bias", dt, (N,))
+    Y, ldy = _out(Y, "Y", dt, (M, N), X.device)
+    ldu = 0
+    if save_u or U is not None:
+        U, ldu = _out(U, "U", torch.float32, (M, L * r), X.device)
+    n = multi_workspace_bytes("lora_fwd", M, K, n_leaf, r)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=X.device)
+    _check(lib().lora_multi_linear_fwd(M, K, L, ctypes.cast(nl, _p), r, ctypes.cast(sl, _p), _dt(X), _ptr(X), ldx,
+                                       _ptr(W0), ldw, _ptr(A), _ptr(B), _ptr(bias), _ptr(Y), ldy, _ptr(U), ldu,
+                                       _ptr(ws), n, _stream()), "lora_multi_linear_fwd")
+    return Y, U
+
+
+def lora_multi_linear_bwd(dY, X, W0, A, B, n_leaf, s_leaf, U=None, need_dx=True, need_dbias=False, dX=None):
+    """Gradients of the fused leaves: dict(dX, dA [L r, K], dB [N, r], dbias)."""
+    M, K = X.shape
+    N, r = B.shape
+    L, nl, sl = _leaf_arrays(n_leaf, s_leaf)
+    dt = X.dtype
+    lddy = _mat(dY, "dY", dt, (M, N))
+    ldx = _mat(X, "X", dt, (M, K))
+    ldw = _mat(W0, "W0", dt, (N, K))
+    _need(A, "A", dt, (L * r, K))
+    _need(B, "B", dt, (N, r))
+    ldu = _mat(U, "U", torch.float32, (M, L * r)) if U is not None else 0
+    dev = X.device
+    lddx = 0
+    if need_dx:
+        dX, lddx = _out(dX, "dX", dt, (M, K), dev)
+    else:
+        dX = None
+    dA = torch.empty((L * r, K), dtype=torch.float32, device=dev)
+    dB = torch.empty((N, r), dtype=torch.float32, device=dev)
+    db = torch.empty((N,), dtype=torch.float32, device=dev) if need_dbias else None
+    n = multi_workspace_bytes("lora_bwd", M, K, n_leaf, r)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    _check(lib().lora_multi_linear_bwd(M, K, L, ctypes.cast(nl, _p), r, ctypes.cast(sl, _p), _dt(X), _ptr(dY), lddy,
+                                       _ptr(X), ldx, _ptr(W0), ldw, _ptr(A), _ptr(B), _ptr(U), ldu, _ptr(dX), lddx,
+                                       _ptr(dA), _ptr(dB), _ptr(db), _ptr(ws), n, _stream()), "lora_multi_linear_bwd")
+    return {"dX": dX, "dA": dA, "dB": dB, "dbias": db}
 
 
 # ------------------------------------------------------------------ weight-space dropout

@@ -555,6 +555,186 @@ int lora_linear_bwd_noalloc(int M, int N, int K, int r, float s, int dtype, cons
 
 size_t ldl_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
+}  // extern "C"
+
+namespace {
+
+// =========================================================================== several adapters, one base GEMM
+constexpr int kMaxLeaves = 8;
+
+struct MultiBwdWs {
+  float* U; float* V; float* partA; uint32_t* pkA;
+  float* part[kMaxLeaves]; float* cs[kMaxLeaves]; uint32_t* pk[kMaxLeaves];
+  int nsA, msA, rpR, rp, ns[kMaxLeaves], ms[kMaxLeaves];
+};
+MultiBwdWs plan_multi_bwd(Bump& b, int M, int K, int nleaf, const int* n_leaf, int r) {
+  MultiBwdWs w{};
+  const int R = nleaf * r;
+  w.rpR = colproj_rp(R);
+  w.rp = colproj_rp(r);
+  colproj_plan(M, K, &w.nsA, &w.msA, 512);
+  w.U = b.take<float>((size_t)M * R);
+  w.V = b.take<float>((size_t)M * R);
+  w.partA = b.take<float>((size_t)w.nsA * K * w.rpR);
+  w.pkA = b.take<uint32_t>(colproj_spk_words(M, R));
+  for (int l = 0; l < nleaf; ++l) {
+    colproj_plan(M, n_leaf[l], &w.ns[l], &w.ms[l], 512);
+    w.part[l] = b.take<float>((size_t)w.ns[l] * n_leaf[l] * w.rp);
+    w.cs[l] = b.take<float>((size_t)w.ns[l] * n_leaf[l]);
+    w.pk[l] = b.take<uint32_t>(colproj_spk_words(M, r));
+  }
+  return w;
+}
+
+// shapes shared by the multi-leaf calls: leaf widths multiples of 64, at most 8 leaves, one rank
+int multi_check(int M, int K, int nleaf, const int* n_leaf, int r, int dtype, int* Ntot) {
+  if (!n_leaf || nleaf <= 0 || M < 0 || K <= 0 || r <= 0) return LDL_E_INVAL;
+  if (dtype != LDL_BF16) return dtype == LDL_F32 ? LDL_E_UNSUPPORTED : LDL_E_INVAL;
+  if (nleaf > kMaxLeaves || r % 8 || nleaf * r > 128) return LDL_E_UNSUPPORTED;
+  long n = 0;
+  for (int l = 0; l < nleaf; ++l) {
+    if (n_leaf[l] <= 0) return LDL_E_INVAL;
+    if (n_leaf[l] % 64) return LDL_E_UNSUPPORTED;
+    n += n_leaf[l];
+  }
+  if (n > (1 << 30)) return LDL_E_UNSUPPORTED;
+  *Ntot = (int)n;
+  return check_bf16_layer(M, (int)n, K, nleaf * r);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ldl_multi_workspace_bytes(int op, int M, int K, int nleaf, const int* n_leaf, int r) {
+  int Ntot = 0;
+  if (multi_check(M, K, nleaf, n_leaf, r, LDL_BF16, &Ntot) != LDL_OK) return 0;
+  Bump b(nullptr);
+  if (op == LDL_OP_LORA_FWD) b.take<float>((size_t)M * nleaf * r);
+  else if (op == LDL_OP_LORA_BWD) plan_multi_bwd(b, M, K, nleaf, n_leaf, r);
+  else return 0;
+  return b.size();
+}
+
+int lora_multi_linear_fwd(int M, int K, int nleaf, const int* n_leaf, int r, const float* s_leaf, int dtype,
+                          const void* X, int ldx, const void* W0, int ldw, const void* A, const void* B,
+                          const void* bias, void* Y, int ldy, float* U_save, int ldu, void* ws, size_t ws_bytes,
+                          void* stream) {
+  int N = 0;
+  const int chk = multi_check(M, K, nleaf, n_leaf, r, dtype, &N);
+  if (chk != LDL_OK) return chk;
+  if (!nonnull({s_leaf, W0, A, B}) || (M > 0 && !nonnull({X, Y}))) return LDL_E_INVAL;
+  const int R = nleaf * r;
+  LDL_LD(ldx, K, 8); LDL_LD(ldw, K, 8); LDL_LD(ldy, N, 8); LDL_LD(ldu, R, 4);
+  if (!al({X, W0, A, B, bias, Y, U_save, ws})) return LDL_E_UNSUPPORTED;
+  if (!fits(M, ldx, 2) || !fits(N, ldw, 2) || !fits(M, ldy, 2) || !fits(M, ldu, 4)) return LDL_E_UNSUPPORTED;
+  if (!U_save && ldl_multi_workspace_bytes(LDL_OP_LORA_FWD, M, K, nleaf, n_leaf, r) > ws_bytes) return LDL_E_WORKSPACE;
+  if (!U_save && !ws) return LDL_E_INVAL;
+  if (M == 0) return LDL_OK;
+  const hipStream_t st = S(stream);
+  Bump wb(ws);
+  float* U = U_save ? U_save : wb.take<float>((size_t)M * R);
+  const int lu = U_save ? ldu : R;
+  GemmParams p = gp0();
+  p.M = M; p.N = N; p.K = K;
+  p.a = X; p.lda = ldx; p.b0 = W0; p.ldb = ldw; p.kseg = K;
+  p.r_epi = R; p.s_epi = 1.f; p.e0 = B; p.e1 = B; p.e_ldn = r; p.e_ldj = 1; p.e_jsplit = R;
+  p.bias = bias; p.out = Y; p.ldo = ldy; p.S = U; p.ld_s = lu;
+  p.nleaf = nleaf; p.leaf_r = r;
+  for (int l = 0, end = 0; l < nleaf; ++l) {
+    end += n_leaf[l];
+    p.leaf_end[l] = end;
+    p.leaf_s[l] = s_leaf[l];
+  }
+  const uint16_t* Bh = static_cast<const uint16_t*>(B);
+  if (gemm_multi_leaf_ok(p)) {
+    // U = X.[A_1; ..; A_L]^T in one pass, then one GEMM over the concatenated weight whose
+    // low-rank seed takes each output column's leaf
+    LDL_TRY(rowproj(M, K, R, X, ldx, A, nullptr, R, K, U, lu, 1.f, st));
+    LDL_TRY(gemm_timed(0, GK_NT_PLAIN, p, st));
+    return LDL_OK;
+  }
+  // otherwise one LoRA product per leaf into its column slice of Y
+  for (int l = 0, off = 0; l < nleaf; off += n_leaf[l], ++l) {
+    const int rc = lora_linear_fwd(M, n_leaf[l], K, r, s_leaf[l], LDL_BF16, X, ldx,
+                                   static_cast<const uint16_t*>(W0) + (size_t)off * ldw, ldw,
+                                   static_cast<const uint16_t*>(A) + (size_t)l * r * K, Bh + (size_t)off * r,
+                                   bias ? static_cast<const uint16_t*>(bias) + off : nullptr,
+                                   static_cast<uint16_t*>(Y) + off, ldy, U + (size_t)l * r, lu, nullptr, 0, stream);
+    if (rc != LDL_OK) return rc;
+  }
+  return LDL_OK;
+}
+
+int lora_multi_linear_bwd(int M, int K, int nleaf, const int* n_leaf, int r, const float* s_leaf, int dtype,
+                          const void* dY, int lddy, const void* X, int ldx, const void* W0, int ldw, const void* A,
+                          const void* B, const float* U_saved, int ldu, void* dX, int lddx, float* dA, float* dB,
+                          float* dbias, void* ws, size_t ws_bytes, void* stream) {
+  int N = 0;
+  const int chk = multi_check(M, K, nleaf, n_leaf, r, dtype, &N);
+  if (chk != LDL_OK) return chk;
+  if (!nonnull({s_leaf, W0, A, B, dA, dB, ws}) || (M > 0 && !nonnull({dY, X}))) return LDL_E_INVAL;
+  const int R = nleaf * r;
+  LDL_LD(lddy, N, 8); LDL_LD(ldx, K, 8); LDL_LD(ldw, K, 8); LDL_LD(ldu, R, 4); LDL_LD(lddx, K, 8);
+  if (!al({dY, X, W0, A, B, U_saved, dX, dA, dB, dbias, ws})) return LDL_E_UNSUPPORTED;
+  if (!fits(M, lddy, 2) || !fits(M, ldx, 2) || !fits(N, ldw, 2) || !fits(M, ldu, 4) || !fits(M, lddx, 2))
+    return LDL_E_UNSUPPORTED;
+  if (ldl_multi_workspace_bytes(LDL_OP_LORA_BWD, M, K, nleaf, n_leaf, r) > ws_bytes) return LDL_E_WORKSPACE;
+  const hipStream_t st = S(stream);
+  if (M == 0) {
+    LDL_TRY(zero(dA, (size_t)R * K, st));
+    LDL_TRY(zero(dB, (size_t)N * r, st));
+    LDL_TRY(zero(dbias, (size_t)N, st));
+    return LDL_OK;
+  }
+  Bump wb(ws);
+  MultiBwdWs w = plan_multi_bwd(wb, M, K, nleaf, n_leaf, r);
+  int off[kMaxLeaves];
+  for (int l = 0, o = 0; l < nleaf; o += n_leaf[l], ++l) off[l] = o;
+  const uint16_t* Bh = static_cast<const uint16_t*>(B);
+  const uint16_t* dYh = static_cast<const uint16_t*>(dY);
+  const float* U = U_saved;
+  int lu = ldu;
+  if (!U) {
+    LDL_TRY(rowproj(M, K, R, X, ldx, A, nullptr, R, K, w.U, R, 1.f, st));
+    U = w.U;
+    lu = R;
+  }
+  // V_l = s_l.dY_l.B_l for each leaf (dY_l: the leaf's columns), side by side in V [M, R]
+  for (int l = 0; l < nleaf; ++l)
+    LDL_TRY(rowproj_t(M, n_leaf[l], r, dYh + off[l], lddy, Bh + (size_t)off[l] * r, r, nullptr, w.V + (size_t)l * r,
+                      R, s_leaf[l], st));
+  // dX = dY.W0 + V.[A_1; ..; A_L]: one GEMM over the concatenated weight, rank R
+  if (dX) {
+    GemmParams p = gp0();
+    p.M = M; p.N = K; p.K = N;
+    p.a = dY; p.lda = lddy; p.b0 = W0; p.b1 = W0; p.ldb = ldw; p.kseg = N;
+    p.S = w.V; p.ld_s = R; p.r_epi = R; p.s_epi = 1.f;
+    p.e0 = A; p.e1 = A; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = R;
+    p.out = dX; p.ldo = lddx;
+    LDL_TRY(gemm_timed(1, GK_NN_PLAIN, p, st));
+  }
+  // dA_l = V_l^T.X for every leaf in one column projection of X; dB_l = s_l.dY_l^T.U_l per leaf
+  LDL_TRY(colproj(M, K, R, X, ldx, w.V, R, 1.f, nullptr, 0, 0, w.nsA, w.msA, w.partA, nullptr, st, w.pkA));
+  LDL_TRY(reduce(R, K, w.partA, (size_t)K * w.rpR, w.nsA, w.rpR, true, 1.f, dA, K, st));
+  for (int l0 = 0; l0 < nleaf; l0 += kColProjBatch) {
+    ColProjParams jobs[kColProjBatch];
+    int ns[kColProjBatch], nj = 0;
+    for (int l = l0; l < nleaf && nj < kColProjBatch; ++l) {
+      jobs[nj] = pk(cpp(M, n_leaf[l], r, dYh + off[l], lddy, U + (size_t)l * r, lu, 1.f, nullptr, 0, dbias ? 2 : 0,
+                        w.ms[l], w.part[l], w.cs[l]), w.pk[l]);
+      ns[nj++] = w.ns[l];
+    }
+    LDL_TRY(launch_colproj_batch(jobs, ns, nj, st));
+  }
+  for (int l = 0; l < nleaf; ++l) {
+    LDL_TRY(reduce(n_leaf[l], r, w.part[l], (size_t)n_leaf[l] * w.rp, w.ns[l], w.rp, false, s_leaf[l],
+                   dB + (size_t)off[l] * r, r, st));
+    if (dbias) LDL_TRY(launch_reduce_colsum(w.cs[l], w.ns[l], n_leaf[l], dbias + off[l], st));
+  }
+  return LDL_OK;
+}
+
 // =========================================================================== weight-space dropout
 int lora_dropout_mask(int r, int K, int dtype, const void* A, const uint8_t* keep, void* A_drop, void* stream) {
   if (!nonnull({A, keep, A_drop})) return LDL_E_INVAL;

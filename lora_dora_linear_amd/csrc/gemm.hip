@@ -139,8 +139,16 @@ static bool swb_split(const GemmParams& p, GemmParams& h) {
   return seed_ok(GK_NN_PLAIN, h);
 }
 
+// Several adapters over one concatenated output: the leaf-aware low-rank seed exists on the
+// four-wave NT tile only (the caller runs one product per leaf otherwise).
+bool gemm_multi_leaf_ok(const GemmParams& p) {
+  return g_gemm_4wave && p.M > 128 && p.side == nullptr && p.r_epi <= 64 && seed_ok(GK_NT_PLAIN, p) &&
+         (p.N % 256 == 0 || b192_fills(p.M, p.N));
+}
+
 hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
   if (p.M <= 0) return hipSuccess;
+  if (p.nleaf > 0 && (kind != GK_NT_PLAIN || !gemm_multi_leaf_ok(p))) return hipErrorInvalidValue;
   const int bn = pick_bn(kind, p.N);
   const bool big = p.M > 128;
   if (kind == GK_NT_SWIGLU_DUAL && dual16_ok(p)) return run16_dual(p, st);

@@ -235,6 +235,12 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   if constexpr (LR == 1) {
     const int cps = p.r_epi >> 3;                     // chunks per part
     const int nparts = p.seed_hilo ? 2 : 1;
+    // several adapters (NT): this thread's output column n0 + t lies in leaf myleaf
+    const int nrow = (BN == 256 || tid < BN) ? n0 + tid : n0;
+    int myleaf = 0;
+    if constexpr (!NN) {
+      for (int l = 0; l + 1 < p.nleaf; ++l) myleaf += nrow >= p.leaf_end[l] ? 1 : 0;
+    }
     f32x4 sa[8], sb[8];
     u32x4 ev[8];
 #pragma unroll
@@ -245,23 +251,25 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
       sb[c] = *reinterpret_cast<const f32x4*>(srow + jl + 4);
       if constexpr (NN) {       // rank row jl + t / 32, 16-byte chunk t % 32 of its 256 columns
         ev[c] = *reinterpret_cast<const u32x4*>(e0 + (size_t)(jl + (tid >> 5)) * p.e_ldj + n0 + 8 * (tid & 31));
-      } else {                  // ranks jl .. jl + 7 of row n0 + t (t < BN)
-        const int n = (BN == 256 || tid < BN) ? n0 + tid : n0;
-        ev[c] = *reinterpret_cast<const u32x4*>(e0 + (size_t)n * p.e_ldn + jl);
+      } else {                  // ranks jl .. jl + 7 of row n0 + t (t < BN); with leaves, of the leaf's row
+        const int je = p.nleaf ? jl % p.leaf_r : jl;
+        ev[c] = *reinterpret_cast<const u32x4*>(e0 + (size_t)nrow * p.e_ldn + je);
       }
     }
     copy_stage(0, smem0);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const int part = c / cps;
+      const int part = c / cps, j0 = 8 * (c - part * cps);
       const bool on = part < nparts;
+      const int lc = p.nleaf ? j0 / p.leaf_r : 0;      // leaf of these rank slots
+      const float sc = p.nleaf ? p.leaf_s[lc] : p.s_epi;
       const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-      lds_st16(smem1, g16_off(tid, c), on ? pack8(sa[c], sb[c], live ? p.s_epi : 0.f, part == 1) : z);
+      lds_st16(smem1, g16_off(tid, c), on ? pack8(sa[c], sb[c], live ? sc : 0.f, part == 1) : z);
       if constexpr (NN) {
         const int j = 8 * c + (tid >> 5), ch = tid & 31;
         lds_st16(smem1, BM * 128 + g16_nn_row(j) + ((ch ^ (2 * (j & 3))) << 4), on ? ev[c] : z);
       } else if (BN == 256 || tid < BN) {
-        lds_st16(smem1, BM * 128 + g16_off(tid, c), on ? ev[c] : z);
+        lds_st16(smem1, BM * 128 + g16_off(tid, c), (on && lc == myleaf) ? ev[c] : z);
       }
     }
     __syncthreads();

@@ -64,6 +64,13 @@ struct GemmParams {
   float* side_save; int ld_side_save;
   int seed_hilo;                     // four-wave tile: low-rank term as bf16 hi + lo (set by the launcher)
   int act;                           // gated MLP activation: ACT_SILU, ACT_GELU, ACT_GELU_TANH
+  // several adapters over one concatenated output (four-wave NT seed only): output column n
+  // belongs to leaf l for leaf_end[l - 1] <= n < leaf_end[l]; rank slots [l r_leaf, (l + 1) r_leaf)
+  // of S hold that leaf's down-projection, scaled by leaf_s[l]; E row n holds its leaf's
+  // lora_up row (e_ldn = r_leaf) in those slots and zero in the others
+  int nleaf, leaf_r;
+  int leaf_end[8];
+  float leaf_s[8];
 };
 
 template <int BM_, int BN_, bool I8_, bool NN_, bool BINT8_, bool ASCALE_, int SIDE_RSP_, bool SLOAD_, int EPI_,

@@ -51,6 +51,7 @@ enum GemmKind : int {
 hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st);
 extern int g_gemm_4wave;   // plain bf16 GEMMs on the four-wave 16x16x32 tile (tuning switch)
 bool gemm_shape_ok(GemmKind kind, int M, int N, int K);
+bool gemm_multi_leaf_ok(const GemmParams& p);
 
 hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st);
 int colproj_rp(int R);

@@ -105,6 +105,23 @@ def linear_case(config_id, M, N, K, r, s, dtype, with_bias=False, dora=False,
     return c
 
 
+def multi_case(config_id, M, K, n_leaf, r, s_leaf, with_bias=False):
+    """Several adapters over one concatenated weight (bf16): X, W0 [sum n_leaf, K],
+    A = [A_1; ..; A_L] [L r, K], B = [B_1; ..; B_L] [sum n_leaf, r], dY (+ bias).  The
+    leaf widths and scales ride along as c.n_leaf / c.s_leaf."""
+    N, L = int(sum(n_leaf)), len(n_leaf)
+    c = LinearCase(M, N, K, r, 1.0, "bf16")
+    c.n_leaf, c.s_leaf = [int(n) for n in n_leaf], [float(v) for v in s_leaf]
+    c.t["X"] = normal(config_id, 0, (M, K), 1.0, "bf16")
+    c.t["W0"] = normal(config_id, 1, (N, K), 1.0 / np.sqrt(K), "bf16")
+    c.t["A"] = normal(config_id, 2, (L * r, K), 1.0 / np.sqrt(K), "bf16")
+    c.t["B"] = normal(config_id, 3, (N, r), B_STD, "bf16")
+    c.t["dY"] = normal(config_id, 4, (M, N), 1.0, "bf16")
+    if with_bias:
+        c.t["bias"] = normal(config_id, 6, (N,), 0.5, "bf16")
+    return c
+
+
 @dataclass
 class MlpCase:
     M: int

@@ -240,6 +240,47 @@ def test_merge_validation(L):
     assert b(64, 64, 16, 0.5, 1, P, 0, P, P, NUL, P, P, need, NUL) == INVAL
 
 
+def _ints(*v):
+    return ctypes.cast((ctypes.c_int * len(v))(*v), ctypes.c_void_p)
+
+
+def _floats(*v):
+    return ctypes.cast((ctypes.c_float * len(v))(*v), ctypes.c_void_p)
+
+
+def test_multi_leaf_validation(L):
+    n3, s3 = _ints(128, 64, 64), _floats(0.5, 1.0, 2.0)
+    q = L.ldl_multi_workspace_bytes
+
+    def fwd(M=64, K=64, nl=3, n=n3, r=16, sl=s3, dtype=1, ldy=0, U=P, nws=0):
+        return L.lora_multi_linear_fwd(M, K, nl, n, r, sl, dtype, P, 0, P, 0, P, P, NUL, P, ldy, U, 0, P, nws, NUL)
+
+    assert fwd(nl=0) == INVAL
+    assert fwd(n=NUL) == INVAL
+    assert fwd(sl=NUL) == INVAL
+    assert fwd(nl=9, n=_ints(*[64] * 9), sl=_floats(*[1.0] * 9)) == UNSUP       # more than eight leaves
+    assert fwd(n=_ints(128, 100, 64)) == UNSUP                                   # leaf width % 64
+    assert fwd(n=_ints(128, 0, 64)) == INVAL                                     # empty leaf
+    assert fwd(r=12) == UNSUP                                                    # r % 8
+    assert fwd(r=48) == UNSUP                                                    # L r = 144 > 128
+    assert fwd(dtype=0) == UNSUP                                                 # fp32 not taken
+    assert fwd(dtype=2) == INVAL
+    assert fwd(ldy=200) == INVAL                                                 # ldy below N = 256
+    assert fwd(U=NUL, nws=q(0, 64, 64, 3, n3, 16) - 256) == WS
+    assert q(0, 64, 64, 3, n3, 16) == 64 * 48 * 4
+    assert q(0, 64, 64, 0, n3, 16) == 0 and q(5, 64, 64, 3, n3, 16) == 0
+    need = q(1, 64, 64, 3, n3, 16)
+    assert need > 0
+
+    def bwd(dA=P, nws=need, dtype=1):
+        return L.lora_multi_linear_bwd(64, 64, 3, n3, 16, s3, dtype, P, 0, P, 0, P, 0, P, P, NUL, 0, P, 0, dA, P,
+                                       NUL, P, nws, NUL)
+
+    assert bwd(nws=need - 256) == WS
+    assert bwd(dA=NUL) == INVAL
+    assert bwd(dtype=0) == UNSUP
+
+
 def test_workspace_query_with_empty_batch(L):
     # M == 0 is valid everywhere; the size queries must not divide by zero
     for op in range(8):
