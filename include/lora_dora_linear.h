@@ -71,7 +71,9 @@ typedef enum {
   LDL_OP_SWIGLU_BWD = 5, /* N = hidden size H */
   LDL_OP_W8A8_FWD = 6,
   LDL_OP_W8A8_BWD = 7,
-  LDL_OP_MERGE_BWD = 8   /* M unused; N x K weight */
+  LDL_OP_MERGE_BWD = 8,  /* M unused; N x K weight */
+  LDL_OP_DORA_COLS_FWD = 9,
+  LDL_OP_DORA_COLS_BWD = 10
 } ldl_op;
 
 /* Human-readable text of a status code (static storage). */
@@ -284,6 +286,50 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype,
                     const void* Z_saved, int ldz, const float* state,
                     void* dX, int lddx, float* dA, float* dB, float* dm, float* dbias,
                     void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ DoRA, column form
+ * Column-scaled DoRA ("dora-cols"), bf16 only: the norm is taken per input column k of
+ * W' = W0 + s.B.A and the magnitude m [K] over it scales the layer input per feature
+ * ("LoRA/DoRA fast forward: no weight materialization", section "What": lora, dora-rows
+ * and dora-cols; section "Fidelity": norm in the graph, eps clamp, bias un-scaled).  The
+ * column norm comes from the closed form colsum(W0^2)_k + 2s <A_k, (B^T W0)_k> +
+ * s^2 A_k^T (B^T B) A_k with the cached constant colsum(W0^2) and the rank-sized terms
+ * Pc = B^T.W0 [r,K] and Gc = B^T.B [r,r]; the adapted weight is never formed.
+ */
+
+/* Once per frozen W0 [N,K] (row stride ldw, dtype LDL_F32 or LDL_BF16):
+ * w0_colsq[k] = sum_n W0[n,k]^2 (fp32 [K]).  Recompute whenever W0 changes. */
+int dora_cols_prepare(int N, int K, int dtype, const void* W0, int ldw, float* w0_colsq, void* stream);
+
+/*   nu_k = ||W'[:,k]||;  g_k = m_k / max(nu_k, eps);  Xs = X.diag(g);
+ *   Y = Xs.W0^T + s.(Xs.A^T).B^T (+ bias)   (= X.(W'.diag(g))^T + bias).
+ *   X [M,K] (ldx), W0 [N,K] (ldw), A [r,K], B [N,r], m [K] fp32, w0_colsq [K] from
+ *   dora_cols_prepare, bias [N] or NULL, Y [M,N] (ldy).  Xs_save [M,K] bf16 (ldxs,
+ *   required: the scaled input, read by the backward); U_save [M,r] fp32 (ldu) or NULL
+ *   receives Xs.A^T.  state: dora_state_floats(K, r) fp32 (required) = norm [K] | g [K] |
+ *   Pc [r*K] | Gc [r*r].  Limits: those of the bf16 layer, r a multiple of 8, r <= 64.
+ *   Workspace: ldl_workspace_bytes(LDL_OP_DORA_COLS_FWD, M, N, K, r, dtype). */
+int dora_cols_linear_fwd(int M, int N, int K, int r, float s, float eps, int dtype,
+                         const void* X, int ldx, const void* W0, int ldw, const void* A, const void* B,
+                         const float* m, const float* w0_colsq, const void* bias,
+                         void* Y, int ldy, float* U_save, int ldu, void* Xs_save, int ldxs, float* state,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Gradients of the column-scaled layer, norm kept in the graph:
+ *   dXs = dY.W';  dX = dXs.diag(g);  dg_k = sum_m dXs[m,k] X[m,k];  dm = dg / max(nu, eps);
+ *   w_k = -dg_k m_k / (2 nu_k^3) (0 where nu_k <= eps);
+ *   dA = s.(dY.B)^T.Xs + 2s (Pc + s.Gc.A).diag(w)
+ *   dB = s.dY^T.U + 2s W0.diag(w).A^T + 2s^2 B.(A.diag(w).A^T);  dbias = sum_m dY.
+ *   Inputs as in the forward plus dY [M,N] (lddy), Xs_saved (ldxs), U_saved (ldu) or NULL
+ *   (recomputed), state.  Outputs dX [M,K] bf16 (lddx) or NULL; dA [r,K], dB [N,r], dm [K]
+ *   fp32; dbias [N] fp32 or NULL.
+ *   Workspace: ldl_workspace_bytes(LDL_OP_DORA_COLS_BWD, M, N, K, r, dtype). */
+int dora_cols_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype,
+                         const void* dY, int lddy, const void* X, int ldx, const void* Xs_saved, int ldxs,
+                         const void* W0, int ldw, const void* A, const void* B, const float* m,
+                         const float* U_saved, int ldu, const float* state,
+                         void* dX, int lddx, float* dA, float* dB, float* dm, float* dbias,
+                         void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ SwiGLU MLP
  * LoRA MLP with SwiGLU: e = lora(X; gate), u = lora(X; up), h = silu(e) * u,

@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(HERE, "liblora_dora_linear.so")
 
 LDL_F32, LDL_BF16 = 0, 1
 OPS = {"lora_fwd": 0, "lora_bwd": 1, "dora_fwd": 2, "dora_bwd": 3,
-       "swiglu_fwd": 4, "swiglu_bwd": 5, "w8a8_fwd": 6, "w8a8_bwd": 7, "merge_bwd": 8}
+       "swiglu_fwd": 4, "swiglu_bwd": 5, "w8a8_fwd": 6, "w8a8_bwd": 7, "merge_bwd": 8,
+       "dora_cols_fwd": 9, "dora_cols_bwd": 10}
 
 _lib = None
 
@@ -57,6 +58,11 @@ SIGNATURES = {
                            _i),
     "geglu_lora_mlp_bwd": ([_i, _i, _i, _i, _f, _f, _f, _i, _p, _i, _p, _i] + [_p] * 13 + [_p, _i] + [_p] * 7
                            + [_z, _p], _i),
+    "dora_cols_prepare": ([_i, _i, _i, _p, _i, _p, _p], _i),
+    "dora_cols_linear_fwd": ([_i, _i, _i, _i, _f, _f, _i, _p, _i, _p, _i, _p, _p, _p, _p, _p, _p, _i, _p, _i, _p,
+                              _i, _p, _p, _z, _p], _i),
+    "dora_cols_linear_bwd": ([_i, _i, _i, _i, _f, _f, _i, _p, _i, _p, _i, _p, _i, _p, _i, _p, _p, _p, _p, _i, _p,
+                              _p, _i, _p, _p, _p, _p, _p, _z, _p], _i),
     "w8a8_quantize_weight": ([_i, _i, _i, _p, _i, _p, _p, _p], _i),
     "w8a8_quantize_rows": ([_i, _i, _p, _i, _p, _p, _p], _i),
     "int8_gemm_raw": ([_i, _i, _i, _p, _i, _p, _i, _p, _i, _p], _i),
@@ -419,6 +425,74 @@ def dora_linear_bwd(dY, X, W0, A, B, m, U, Z, state, s, eps=1e-12, need_dx=True,
                                  ldw, _ptr(A), _ptr(B), _ptr(m), _ptr(U), ldu, _ptr(Z), ldz, _ptr(state), _ptr(dX),
                                  lddx, _ptr(dA), _ptr(dB), _ptr(dm), _ptr(db), _ptr(ws), n, _stream()),
            "dora_linear_bwd")
+    return {"dX": dX, "dA": dA, "dB": dB, "dm": dm, "dbias": db}
+
+
+# ------------------------------------------------------------------ DoRA, column form
+def dora_cols_prepare(W0):
+    """Column sums of W0^2 ([K] fp32), once per frozen W0."""
+    N, K = W0.shape
+    ldw = _mat(W0, "W0", W0.dtype, (N, K))
+    out = torch.empty((K,), dtype=torch.float32, device=W0.device)
+    _check(lib().dora_cols_prepare(N, K, _dt(W0), _ptr(W0), ldw, _ptr(out), _stream()), "dora_cols_prepare")
+    return out
+
+
+def dora_cols_linear_fwd(X, W0, A, B, m, w0_colsq, s, eps=1e-12, bias=None, Y=None):
+    """Column-scaled DoRA forward.  Returns (Y, U, Xs, state) with Xs = X.diag(g) (bf16)
+    and state = [norm | g | Pc | Gc] (fp32, dora_state_floats(K, r))."""
+    M, K = X.shape
+    N, r = B.shape
+    dt = X.dtype
+    ldx = _mat(X, "X", dt, (M, K))
+    ldw = _mat(W0, "W0", dt, (N, K))
+    _need(A, "A", dt, (r, K))
+    _need(B, "B", dt, (N, r))
+    _need(m, "m", torch.float32, (K,))
+    _need(w0_colsq, "w0_colsq", torch.float32, (K,))
+    if bias is not None:
+        _need(bias, "bias", dt, (N,))
+    dev = X.device
+    Y, ldy = _out(Y, "Y", dt, (M, N), dev)
+    Xs = torch.empty((M, K), dtype=dt, device=dev)
+    U = torch.empty((M, r), dtype=torch.float32, device=dev)
+    state = torch.empty((dora_state_floats(K, r),), dtype=torch.float32, device=dev)
+    ws, n = _ws("dora_cols_fwd", M, N, K, r, _dt(X), dev)
+    _check(lib().dora_cols_linear_fwd(M, N, K, r, float(s), float(eps), _dt(X), _ptr(X), ldx, _ptr(W0), ldw,
+                                      _ptr(A), _ptr(B), _ptr(m), _ptr(w0_colsq), _ptr(bias), _ptr(Y), ldy, _ptr(U), r,
+                                      _ptr(Xs), K, _ptr(state), _ptr(ws), n, _stream()), "dora_cols_linear_fwd")
+    return Y, U, Xs, state
+
+
+def dora_cols_linear_bwd(dY, X, Xs, W0, A, B, m, U, state, s, eps=1e-12, need_dx=True, need_dbias=False, dX=None):
+    """Returns dict(dX, dA, dB, dm [K], dbias) of the column-scaled layer (U may be None)."""
+    M, K = X.shape
+    N, r = B.shape
+    dt = X.dtype
+    lddy = _mat(dY, "dY", dt, (M, N))
+    ldx = _mat(X, "X", dt, (M, K))
+    ldxs = _mat(Xs, "Xs", dt, (M, K))
+    ldw = _mat(W0, "W0", dt, (N, K))
+    _need(A, "A", dt, (r, K))
+    _need(B, "B", dt, (N, r))
+    _need(m, "m", torch.float32, (K,))
+    ldu = _mat(U, "U", torch.float32, (M, r)) if U is not None else 0
+    _need(state, "state", torch.float32, (dora_state_floats(K, r),))
+    dev = X.device
+    lddx = 0
+    if need_dx:
+        dX, lddx = _out(dX, "dX", dt, (M, K), dev)
+    else:
+        dX = None
+    dA = torch.empty((r, K), dtype=torch.float32, device=dev)
+    dB = torch.empty((N, r), dtype=torch.float32, device=dev)
+    dm = torch.empty((K,), dtype=torch.float32, device=dev)
+    db = torch.empty((N,), dtype=torch.float32, device=dev) if need_dbias else None
+    ws, n = _ws("dora_cols_bwd", M, N, K, r, _dt(X), dev)
+    _check(lib().dora_cols_linear_bwd(M, N, K, r, float(s), float(eps), _dt(X), _ptr(dY), lddy, _ptr(X), ldx,
+                                      _ptr(Xs), ldxs, _ptr(W0), ldw, _ptr(A), _ptr(B), _ptr(m), _ptr(U), ldu,
+                                      _ptr(state), _ptr(dX), lddx, _ptr(dA), _ptr(dB), _ptr(dm), _ptr(db), _ptr(ws), n,
+                                      _stream()), "dora_cols_linear_bwd")
     return {"dX": dX, "dA": dA, "dB": dB, "dm": dm, "dbias": db}
 
 

@@ -137,6 +137,48 @@ MergeBwdWs plan_merge_bwd(Bump& b, int N, int K, int r) {
   return w;
 }
 
+// Column-scaled DoRA.  Forward: B as fp32, the split partials of Pc = B^T.W0 and
+// Gc = B^T.B, U when not saved.  Backward: dXs (the gradient of the scaled input) when dX is
+// not requested, the LoRA backward's own workspace, the partial column sums of dXs.X, dg,
+// A.diag(w) as bf16 hi / lo, and T = [W0; A].(A.diag(w))^T.
+struct DoraColsFwdWs {
+  float* Bf; float* partP; float* partG; uint32_t* pkP; uint32_t* pkG; float* U;
+  int nsP, msP, nsG, msG, rp;
+};
+DoraColsFwdWs plan_dora_cols_fwd(Bump& b, int M, int N, int K, int r) {
+  DoraColsFwdWs w{};
+  w.rp = colproj_rp(r);
+  colproj_plan(N, K, &w.nsP, &w.msP, 512);
+  colproj_plan(N, r, &w.nsG, &w.msG, 64);
+  w.Bf = b.take<float>((size_t)N * r);
+  w.partP = b.take<float>((size_t)w.nsP * K * w.rp);
+  w.partG = b.take<float>((size_t)w.nsG * r * w.rp);
+  w.pkP = b.take<uint32_t>(colproj_spk_words(N, r));
+  w.pkG = b.take<uint32_t>(colproj_spk_words(N, r));
+  w.U = b.take<float>((size_t)M * r);
+  return w;
+}
+
+struct DoraColsBwdWs {
+  uint16_t* dXs; void* lora; size_t lora_bytes; float* partD; float* csD; float* dg; uint16_t* Aw; float* T;
+  int nsD, msD;
+};
+DoraColsBwdWs plan_dora_cols_bwd(Bump& b, int M, int N, int K, int r) {
+  DoraColsBwdWs w{};
+  colproj_plan(M, K, &w.nsD, &w.msD, 512);
+  w.dXs = b.take<uint16_t>((size_t)M * K);
+  Bump lb(nullptr);
+  plan_lora_bwd(lb, M, N, K, r, true);
+  w.lora_bytes = lb.size();
+  w.lora = b.take<uint8_t>(w.lora_bytes);
+  w.partD = b.take<float>((size_t)w.nsD * K * 16);
+  w.csD = b.take<float>((size_t)w.nsD * K);
+  w.dg = b.take<float>((size_t)K);
+  w.Aw = b.take<uint16_t>((size_t)2 * r * K);
+  w.T = b.take<float>((size_t)(N + r) * 2 * r);
+  return w;
+}
+
 struct DoraBwdWs {
   float* V; float* partT; float* cs; float* wB; float* partA; float* partQ; float* Qm;
   uint16_t* dYg;                   // dY.diag(g) in bf16 [M, N]
@@ -409,6 +451,12 @@ size_t ldl_workspace_bytes(int op, int M, int N, int K, int r, int dtype) {
       break;
     case LDL_OP_MERGE_BWD:   // M unused; N x K weight
       if (dtype != LDL_F32) plan_merge_bwd(b, N, K, r);
+      break;
+    case LDL_OP_DORA_COLS_FWD:
+      plan_dora_cols_fwd(b, M, N, K, r);
+      break;
+    case LDL_OP_DORA_COLS_BWD:
+      plan_dora_cols_bwd(b, M, N, K, r);
       break;
     default:
       return 0;
@@ -934,6 +982,139 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, c
       LDL_TRY(zero(dbias, (size_t)N, st));
     }
   }
+  return LDL_OK;
+}
+
+// =========================================================================== DoRA, column form
+int dora_cols_prepare(int N, int K, int dtype, const void* W0, int ldw, float* w0_colsq, void* stream) {
+  if (!nonnull({W0, w0_colsq})) return LDL_E_INVAL;
+  if (N <= 0 || K <= 0) return LDL_E_INVAL;
+  if (dtype != LDL_F32 && dtype != LDL_BF16) return LDL_E_INVAL;
+  if (!al({W0, w0_colsq})) return LDL_E_UNSUPPORTED;
+  LDL_LD(ldw, K, 1);
+  if (!fits(N, ldw, dtype == LDL_BF16 ? 2 : 4)) return LDL_E_UNSUPPORTED;
+  LDL_TRY(launch_col_sumsq(W0, dtype == LDL_BF16, N, K, ldw, w0_colsq, S(stream)));
+  return LDL_OK;
+}
+
+static int dora_cols_check(int M, int N, int K, int r, int dtype) {
+  const int chk = dora_check(M, N, K, r, dtype);
+  if (chk != LDL_OK) return chk;
+  return r > 64 ? LDL_E_UNSUPPORTED : LDL_OK;
+}
+
+int dora_cols_linear_fwd(int M, int N, int K, int r, float s, float eps, int dtype, const void* X, int ldx,
+                         const void* W0, int ldw, const void* A, const void* B, const float* m, const float* w0_colsq,
+                         const void* bias, void* Y, int ldy, float* U_save, int ldu, void* Xs_save, int ldxs,
+                         float* state, void* ws, size_t ws_bytes, void* stream) {
+  if (!nonnull({W0, A, B, m, w0_colsq, state, ws}) || (M > 0 && !nonnull({X, Y, Xs_save}))) return LDL_E_INVAL;
+  if (M < 0 || N <= 0 || K <= 0 || r <= 0 || !(eps >= 0.f)) return LDL_E_INVAL;
+  const int chk = dora_cols_check(M, N, K, r, dtype);
+  if (chk != LDL_OK) return chk;
+  LDL_LD(ldx, K, 8); LDL_LD(ldw, K, 8); LDL_LD(ldy, N, 8); LDL_LD(ldu, r, 4); LDL_LD(ldxs, K, 8);
+  if (!al({X, W0, A, B, m, w0_colsq, bias, Y, U_save, Xs_save, state, ws})) return LDL_E_UNSUPPORTED;
+  if (!fits(M, ldx, 2) || !fits(N, ldw, 2) || !fits(M, ldy, 2) || !fits(M, ldu, 4) || !fits(M, ldxs, 2))
+    return LDL_E_UNSUPPORTED;
+  if (ldl_workspace_bytes(LDL_OP_DORA_COLS_FWD, M, N, K, r, dtype) > ws_bytes) return LDL_E_WORKSPACE;
+  const hipStream_t st = S(stream);
+  Bump wb(ws);
+  DoraColsFwdWs w = plan_dora_cols_fwd(wb, M, N, K, r);
+  float* norm = state;
+  float* g = state + K;
+  float* Pc = state + 2 * (size_t)K;
+  float* Gc = Pc + (size_t)K * r;
+  // the norm terms Pc = B^T.W0 and Gc = B^T.B (one column-projection launch over the rows of
+  // W0 and of B against B), then nu and g (independent of M)
+  LDL_TRY(launch_bf16_to_f32(B, (size_t)N * r, w.Bf, st));
+  {
+    ColProjParams jobs[2] = {pk(cpp(N, K, r, W0, ldw, w.Bf, r, 1.f, nullptr, 0, 0, w.msP, w.partP, nullptr), w.pkP),
+                             pk(cpp(N, r, r, B, r, w.Bf, r, 1.f, nullptr, 0, 0, w.msG, w.partG, nullptr), w.pkG)};
+    int ns[2] = {w.nsP, w.nsG};
+    LDL_TRY(launch_colproj_batch(jobs, ns, 2, st));
+  }
+  LDL_TRY(launch_reduce2(rdp(r, K, w.partP, (size_t)K * w.rp, w.nsP, w.rp, true, 1.f, Pc, K),
+                         rdp(r, r, w.partG, (size_t)r * w.rp, w.nsG, w.rp, true, 1.f, Gc, r), st));
+  LDL_TRY(launch_dora_cols_norm(K, r, s, eps, w0_colsq, m, A, Pc, Gc, norm, g, st));
+  if (M == 0) return LDL_OK;
+  // the layer input scaled per feature, kept for the backward, then the LoRA layer on it
+  LDL_TRY(launch_scale_cols(X, M, K, ldx, g, Xs_save, ldxs, st));
+  return lora_linear_fwd(M, N, K, r, s, LDL_BF16, Xs_save, ldxs, W0, ldw, A, B, bias, Y, ldy,
+                         U_save ? U_save : w.U, U_save ? ldu : r, nullptr, 0, stream);
+}
+
+int dora_cols_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, const void* dY, int lddy,
+                         const void* X, int ldx, const void* Xs_saved, int ldxs, const void* W0, int ldw,
+                         const void* A, const void* B, const float* m, const float* U_saved, int ldu,
+                         const float* state, void* dX, int lddx, float* dA, float* dB, float* dm, float* dbias,
+                         void* ws, size_t ws_bytes, void* stream) {
+  if (!nonnull({W0, A, B, m, state, dA, dB, dm, ws}) || (M > 0 && !nonnull({dY, X, Xs_saved}))) return LDL_E_INVAL;
+  if (M < 0 || N <= 0 || K <= 0 || r <= 0 || !(eps >= 0.f)) return LDL_E_INVAL;
+  const int chk = dora_cols_check(M, N, K, r, dtype);
+  if (chk != LDL_OK) return chk;
+  LDL_LD(lddy, N, 8); LDL_LD(ldx, K, 8); LDL_LD(ldxs, K, 8); LDL_LD(ldw, K, 8); LDL_LD(ldu, r, 4); LDL_LD(lddx, K, 8);
+  if (!al({dY, X, Xs_saved, W0, A, B, m, U_saved, state, dX, dA, dB, dm, dbias, ws})) return LDL_E_UNSUPPORTED;
+  if (!fits(M, lddy, 2) || !fits(M, ldx, 2) || !fits(M, ldxs, 2) || !fits(N, ldw, 2) || !fits(M, ldu, 4) ||
+      !fits(M, lddx, 2))
+    return LDL_E_UNSUPPORTED;
+  if (ldl_workspace_bytes(LDL_OP_DORA_COLS_BWD, M, N, K, r, dtype) > ws_bytes) return LDL_E_WORKSPACE;
+  const hipStream_t st = S(stream);
+  Bump wb(ws);
+  DoraColsBwdWs w = plan_dora_cols_bwd(wb, M, N, K, r);
+  const float* norm = state;
+  const float* g = state + K;
+  const float* Pc = state + 2 * (size_t)K;
+  const float* Gc = Pc + (size_t)K * r;
+  const float* U = U_saved;
+  int lu = ldu;
+  if (M > 0) {
+    // the LoRA layer on the scaled input (V = dY.B; U = Xs.A^T unless saved), with the input
+    // gradient's feature scale in the GEMM epilogue from the fp32 accumulators:
+    // dXs = dY.W0 + s.V.A (bf16, kept for dg) and dX = dXs.diag(g)
+    Bump lb(w.lora);
+    LoraBwdWs lw = plan_lora_bwd(lb, M, N, K, r, true);
+    if (!U) {
+      LDL_TRY(rowproj(M, K, r, Xs_saved, ldxs, A, nullptr, r, K, lw.U, r, 1.f, st));
+      U = lw.U;
+      lu = r;
+    }
+    LDL_TRY(rowproj_t(M, N, r, dY, lddy, B, r, nullptr, lw.V, r, 1.f, st));
+    GemmParams p = gp0();
+    p.M = M; p.N = K; p.K = N;
+    p.a = dY; p.lda = lddy; p.b0 = W0; p.b1 = W0; p.ldb = ldw; p.kseg = N;
+    p.S = lw.V; p.ld_s = r; p.r_epi = r; p.s_epi = s;
+    p.e0 = A; p.e1 = A; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = r;
+    if (dX) {
+      p.out = dX; p.ldo = lddx; p.out2 = w.dXs; p.ldo2 = K; p.col_scale = g;
+      LDL_TRY(gemm_timed(1, GK_NN_DORA, p, st));
+    } else {
+      p.out = w.dXs; p.ldo = K;
+      LDL_TRY(gemm_timed(1, GK_NN_PLAIN, p, st));
+    }
+    // dB = s.dY^T.U (+ dbias), dA = s.V^T.Xs, and dg_k = sum_m dXs[m,k] X[m,k] as column
+    // sums of the product: split partials, then fixed-order reductions
+    {
+      ColProjParams jobs[3] = {
+          pk(cpp(M, N, r, dY, lddy, U, lu, 1.f, nullptr, 0, dbias ? 2 : 0, lw.msB, lw.partB, lw.csB), lw.pkB),
+          pk(cpp(M, K, r, Xs_saved, ldxs, lw.V, r, 1.f, nullptr, 0, 0, lw.msA, lw.partA, nullptr), lw.pkA),
+          cpp(M, K, 0, w.dXs, K, nullptr, 0, 1.f, X, ldx, 1, w.msD, w.partD, w.csD)};
+      int ns[3] = {lw.nsB, lw.nsA, w.nsD};
+      LDL_TRY(launch_colproj_batch(jobs, ns, 3, st));
+    }
+    LDL_TRY(launch_reduce2(rdp(N, r, lw.partB, (size_t)N * lw.rp, lw.nsB, lw.rp, false, s, dB, r),
+                           rdp(r, K, lw.partA, (size_t)K * lw.rp, lw.nsA, lw.rp, true, s, dA, K), st));
+    if (dbias) LDL_TRY(launch_reduce_colsum(lw.csB, lw.nsB, N, dbias, st));
+    LDL_TRY(launch_reduce_colsum(w.csD, w.nsD, K, w.dg, st));
+  } else {
+    LDL_TRY(zero(dA, (size_t)r * K, st));
+    LDL_TRY(zero(dB, (size_t)N * r, st));
+    LDL_TRY(zero(dbias, (size_t)N, st));
+    LDL_TRY(zero(w.dg, (size_t)K, st));
+  }
+  // dm, and the norm's terms: dA += 2s (Pc + s.Gc.A).diag(w); dB += 2s W0.diag(w).A^T +
+  // 2s^2 B.(A.diag(w).A^T), the two products over K as one row projection of [W0; A]
+  LDL_TRY(launch_dora_cols_bwd(K, r, s, eps, w.dg, norm, m, A, Pc, Gc, dm, dA, w.Aw, st));
+  LDL_TRY(rowproj2(N, r, K, 2 * r, W0, ldw, A, K, w.Aw, K, w.T, 2 * r, 1.f, st));
+  LDL_TRY(launch_dora_cols_db(N, r, s, B, w.T, dB, st));
   return LDL_OK;
 }
 

@@ -25,10 +25,11 @@ static hipError_t run(const GemmParams& p, hipStream_t st) {
 }
 
 static int pick_bn(GemmKind kind, int N) {
-  const bool wide_ok = (kind == GK_NT_PLAIN || kind == GK_NT_DORA || kind == GK_NN_PLAIN ||
+  const bool wide_ok = (kind == GK_NT_PLAIN || kind == GK_NT_DORA || kind == GK_NN_PLAIN || kind == GK_NN_DORA ||
                         kind == GK_NN_SCALE || kind == GK_NN_I8_SCALE || kind == GK_NN_SWIGLU || kind == GK_NT_FUSED ||
                         kind == GK_NT_I8_DEQ || kind == GK_NT_I8_RAW);
-  const bool b192_ok = (kind == GK_NT_PLAIN || kind == GK_NT_DORA || kind == GK_NN_PLAIN || kind == GK_NN_SCALE ||
+  const bool b192_ok = (kind == GK_NT_PLAIN || kind == GK_NT_DORA || kind == GK_NN_PLAIN || kind == GK_NN_DORA ||
+                        kind == GK_NN_SCALE ||
                         kind == GK_NN_I8_SCALE);
   if (wide_ok && N % 256 == 0) return 256;
   if (b192_ok && N % 192 == 0) return 192;
@@ -118,7 +119,7 @@ static bool half_tiles_pay(int M, int N) {
 static bool seed_ok(GemmKind kind, const GemmParams& p) {
   return p.r_epi == 0 ||
       (p.r_epi % 8 == 0 && p.ld_s % 4 == 0 && a16(p.S) && a16(p.e0) && p.e_jsplit >= p.r_epi &&
-       ((kind == GK_NN_PLAIN || kind == GK_NN_SWIGLU) ? (p.e_ldn == 1 && p.e_ldj % 8 == 0)
+       ((kind == GK_NN_PLAIN || kind == GK_NN_SWIGLU || kind == GK_NN_DORA) ? (p.e_ldn == 1 && p.e_ldj % 8 == 0)
                                                       : (p.e_ldj == 1 && p.e_ldn % 8 == 0)));
 }
 
@@ -178,6 +179,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
     if (kind == GK_NT_PLAIN) return run16<false>(p, st);
     if (kind == GK_NT_DORA) return run16<false, true>(p, st);
     if (kind == GK_NN_PLAIN && p.kseg == p.K) return run16<true>(p, st);
+    if (kind == GK_NN_DORA && p.kseg == p.K) return run16<true, true>(p, st);
     if (kind == GK_NN_SWIGLU && p.kseg == p.K) return run16<true, false, true>(p, st);
   }
   switch (kind) {
@@ -227,6 +229,13 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
       if (bn >= 128) return big ? run<256, 128, false, true, false, false, 0, true, EPI_PLAIN>(p, st)
                                 : run<128, 128, false, true, false, false, 0, true, EPI_PLAIN>(p, st);
       return run<128, 64, false, true, false, false, 0, true, EPI_PLAIN>(p, st);
+    case GK_NN_DORA:
+      if (bn == 256 && big) return run<256, 256, false, true, false, false, 0, true, EPI_DORA>(p, st);
+      if (bn == 192) return big ? run<256, 192, false, true, false, false, 0, true, EPI_DORA>(p, st)
+                                : run<128, 64, false, true, false, false, 0, true, EPI_DORA>(p, st);
+      if (bn >= 128) return big ? run<256, 128, false, true, false, false, 0, true, EPI_DORA>(p, st)
+                                : run<128, 128, false, true, false, false, 0, true, EPI_DORA>(p, st);
+      return run<128, 64, false, true, false, false, 0, true, EPI_DORA>(p, st);
     case GK_NN_SCALE:
       if (bn == 256 && big) return run<256, 256, false, true, false, true, 0, true, EPI_PLAIN>(p, st);
       if (bn == 192) return big ? run<256, 192, false, true, false, true, 0, true, EPI_PLAIN>(p, st)

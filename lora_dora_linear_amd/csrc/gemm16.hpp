@@ -37,7 +37,7 @@ __host__ __device__ constexpr int g16_nn_row(int k) { return k * kG16NNRow + (k 
 
 // NN: Q is [K, N] (else [N, K]); LR: number of low-rank k-tiles in front of the loop (0: no
 // low-rank term; 1: rank r_epi <= 64 of one segment; 2: the dual tile's gate and up terms);
-// DORA (NT only): two outputs, out2 = z (the unscaled sum) and out = z * col_scale[n] + bias[n];
+// DORA (NT: DoRA's row scale; NN: a per-feature scale of an input gradient): two outputs, out2 = z (the unscaled sum) and out = z * col_scale[n] + bias[n];
 // SWB (NN only): the gated-MLP backward of the product dh with e = aux0, u = aux1:
 // out = dh u act'(e) (de) and out2 = dh act(e) (du), act = p.act (SiLU: act' = sigma (1 + e (1 - sigma)))
 // BN_: tile width, 256, or 192 for NT (3072 columns at 4096 rows then make 256 tiles, one full
@@ -54,7 +54,6 @@ __host__ __device__ constexpr int g16_nn_row(int k) { return k * kG16NNRow + (k 
 template <bool NN, int LR, bool DORA = false, bool SWB = false, int BN_ = 256, bool SWF = false, bool I8 = false>
 __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   static_assert(BN_ == 256 || (!NN && BN_ == 192), "tile widths: 256, or 192 for NT");
-  static_assert(!(NN && DORA), "the row-scaled epilogue is a forward (NT) epilogue");
   static_assert(!SWB || (NN && !DORA), "the SwiGLU backward epilogue is an NN epilogue");
   static_assert(!SWF || (!NN && !DORA && !SWB && BN_ == 256 && LR != 1), "the dual tile is a plain 256-wide NT tile");
   static_assert(LR >= 0 && LR <= 2 && (LR != 2 || SWF), "two low-rank k-tiles: the dual tile's two segments");

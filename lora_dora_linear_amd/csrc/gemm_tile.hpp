@@ -20,10 +20,9 @@
 // kernel fusion - 20-30% faster training" (LoRA-epilogue commit): the [N,K]
 // product B.A and the [M,N] low-rank product are never stored.
 //
-// Tiling: 4 waves (2 x 2), block tile BM x BN, wave tile (BM/2) x (BN/2) in
-// 32x32 MFMA blocks (v_mfma_f32_32x32x16_bf16 / v_mfma_i32_32x32x32_i8: one
-// wave per SIMD keeps the matrix pipe ~80 % busy with these, against ~55 %
-// with the 16x16 shapes), k-tile of 128 bytes per row (64 bf16 or 128 int8),
+// Tiling: 2 x WN waves (WN = 2 or 4: four or eight waves), block tile BM x BN, wave
+// tile (BM/2) x (BN/WN) in 32x32 MFMA blocks (v_mfma_f32_32x32x16_bf16 /
+// v_mfma_i32_32x32x32_i8), k-tile of 128 bytes per row (64 bf16 or 128 int8),
 // a two-stage LDS ring filled by direct buffer-to-LDS copies, one barrier per
 // k-tile.  The NN operand is staged through registers instead, transposed
 // 8 x 8 and optionally row-scaled (DoRA g, W8A8 sw) on its way into LDS.

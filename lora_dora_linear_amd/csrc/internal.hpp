@@ -46,7 +46,8 @@ struct ReduceParams {
 // GEMM tile families (see gemm_tile.hpp); selected by the entry points.
 enum GemmKind : int {
   GK_NT_PLAIN, GK_NT_FUSED, GK_NT_DORA, GK_NT_SWIGLU_DUAL, GK_NT_I8_DEQ, GK_NT_I8_RAW,
-  GK_NN_PLAIN, GK_NN_SCALE, GK_NN_I8_SCALE, GK_NN_SWIGLU
+  GK_NN_PLAIN, GK_NN_SCALE, GK_NN_I8_SCALE, GK_NN_SWIGLU,
+  GK_NN_DORA     // NN with the two-output column-scale epilogue: out2 = z, out = z * col_scale[n]
 };
 hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st);
 extern int g_gemm_4wave;   // plain bf16 GEMMs on the four-wave 16x16x32 tile (tuning switch)
@@ -92,6 +93,14 @@ hipError_t launch_merge(int N, int K, int r, float s, int bf16, const void* W0, 
 hipError_t launch_bf16_to_f32(const void* in, size_t n, float* out, hipStream_t st);
 
 // weight-space dropout: out[j, k] = keep[k] ? in[j, k] : 0 (esz 2: bf16, 4: fp32; in place allowed)
+hipError_t launch_col_sumsq(const void* W0, int bf16, int N, int K, int ldw, float* colsq, hipStream_t st);
+hipError_t launch_dora_cols_norm(int K, int r, float s, float eps, const float* colsq, const float* m,
+                                 const void* A, const float* Pc, const float* Gc, float* norm, float* g,
+                                 hipStream_t st);
+hipError_t launch_dora_cols_bwd(int K, int r, float s, float eps, const float* dg, const float* norm, const float* m,
+                                const void* A, const float* Pc, const float* Gc, float* dm, float* dA, void* Aw,
+                                hipStream_t st);
+hipError_t launch_dora_cols_db(int N, int r, float s, const void* B, const float* T, float* dB, hipStream_t st);
 hipError_t launch_mask_cols(const void* in, const uint8_t* keep, int rows, int K, int esz, void* out, hipStream_t st);
 
 // W8A8 helpers

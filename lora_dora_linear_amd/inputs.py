@@ -13,7 +13,8 @@ Recipe (one stream per tensor):
 
 Distributions (the workloads of the layer as the configurations state them):
   X, dY ~ N(0, 1);  W0, A ~ N(0, 1/fan_in);  B ~ N(0, 0.02) read as a
-  variance (std = sqrt(0.02));  DoRA magnitude m_n = ||W0_n|| . U(0.9, 1.1).
+  variance (std = sqrt(0.02));  DoRA magnitude m_n = ||W0_n|| . U(0.9, 1.1) (row
+  form) or m_k = ||W0[:,k]|| . U(0.9, 1.1) (column form).
 """
 
 from dataclasses import dataclass, field
@@ -84,7 +85,7 @@ class LinearCase:
 
 
 def linear_case(config_id, M, N, K, r, s, dtype, with_bias=False, dora=False,
-                zero_B=False, zero_W0=False):
+                zero_B=False, zero_W0=False, dora_cols=False):
     """X, W0, A, B, dY (+ bias, + DoRA magnitude m) for a LoRA / DoRA layer."""
     c = LinearCase(M, N, K, r, float(s), dtype)
     c.t["X"] = normal(config_id, 0, (M, K), 1.0, dtype)
@@ -102,6 +103,10 @@ def linear_case(config_id, M, N, K, r, s, dtype, with_bias=False, dora=False,
         w0 = to_f64(c.t["W0"], dtype)
         rownorm = np.sqrt(np.sum(w0 * w0, axis=1))
         c.t["m"] = (rownorm * uniform(config_id, 5, (N,), 0.9, 1.1)).astype(np.float32)
+    if dora_cols:
+        w0 = to_f64(c.t["W0"], dtype)
+        colnorm = np.sqrt(np.sum(w0 * w0, axis=0))
+        c.t["m"] = (colnorm * uniform(config_id, 5, (K,), 0.9, 1.1)).astype(np.float32)
     return c
 
 

@@ -281,9 +281,36 @@ def test_multi_leaf_validation(L):
     assert bwd(dtype=0) == UNSUP
 
 
+def test_dora_cols_validation(L):
+    f = L.dora_cols_linear_fwd
+    need = L.ldl_workspace_bytes(9, 64, 64, 64, 16, 1)
+    assert need > 0 and L.ldl_workspace_bytes(10, 64, 64, 64, 16, 1) > 0
+
+    def fwd(M=64, N=64, K=64, r=16, dtype=1, Xs=P, st=P, nws=need, eps=1e-12):
+        return f(M, N, K, r, 0.5, eps, dtype, P, 0, P, 0, P, P, P, P, NUL, P, 0, NUL, 0, Xs, 0, st, P, nws, NUL)
+
+    assert fwd(r=72) == UNSUP              # r above 64
+    assert fwd(r=12) == UNSUP              # r % 8
+    assert fwd(dtype=0) == UNSUP
+    assert fwd(Xs=NUL) == INVAL            # the scaled input is required
+    assert fwd(st=NUL) == INVAL
+    assert fwd(eps=-1.0) == INVAL
+    assert fwd(nws=need - 256) == WS
+    b = L.dora_cols_linear_bwd
+    needb = L.ldl_workspace_bytes(10, 64, 64, 64, 16, 1)
+
+    def bwd(dm=P, nws=needb):
+        return b(64, 64, 64, 16, 0.5, 1e-12, 1, P, 0, P, 0, P, 0, P, 0, P, P, P, NUL, 0, P, P, 0, P, P, dm, NUL, P,
+                 nws, NUL)
+
+    assert bwd(dm=NUL) == INVAL
+    assert bwd(nws=needb - 256) == WS
+    assert L.dora_cols_prepare(64, 64, 2, P, 0, P, NUL) == INVAL
+
+
 def test_workspace_query_with_empty_batch(L):
     # M == 0 is valid everywhere; the size queries must not divide by zero
-    for op in range(8):
+    for op in range(11):
         assert L.ldl_workspace_bytes(op, 0, 256, 256, 16, 1) % 256 == 0
 
 
