@@ -31,9 +31,10 @@ Modules
   geglu  - LoRA MLP with the GeGLU activation (exact and tanh forms of GELU).
   dropout - weight-space dropout of the adapters (a keep mask over lora_down's inputs).
   multi  - several adapters over one concatenated base weight (fused QKV).
+  fp8    - per-row e4m3 quantiser and the 8-bit float base + LoRA layer.
 
 Parity status of every function is listed in its own docstring; functions
 with no independent pin say "parity unpinned".
 """
 
-from . import lora, dora, swiglu, w8a8, merge, geglu, dropout, multi  # noqa: F401
+from . import lora, dora, swiglu, w8a8, merge, geglu, dropout, multi, fp8  # noqa: F401
