@@ -21,7 +21,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16 = 2516.6    # TFLOP/s dense bf16 MFMA, MI355X (256 CU x 2.4 GHz x 4096 flop/clk)
-PEAK_INT8 = 5033.2    # TOP/s dense int8 MFMA
+PEAK_INT8 = 5033.2    # TOP/s dense int8 MFMA (and TFLOP/s dense fp8)
 PEAK_HBM = 8000.0     # GB/s
 
 METRIC = "fused LoRA/DoRA linear fwd+bwd TFLOP/s and % of bf16 MFMA peak (1 GPU)"
@@ -34,8 +34,8 @@ def parse():
     # 200 untimed steps reach the sustained clock, 1000 timed steps take about 0.3 s
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="lora", choices=["lora", "dora", "swiglu", "w8a8", "tiny", "merge"])
-    ap.add_argument("--M", type=int, default=None, help="token count override (w8a8 sweep point)")
+    ap.add_argument("--workload", default="lora", choices=["lora", "dora", "swiglu", "w8a8", "fp8", "tiny", "merge"])
+    ap.add_argument("--M", type=int, default=None, help="token count override (w8a8 / fp8 sweep point)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused-downproj", type=int, default=None, choices=[0, 1])
     ap.add_argument("--gemm-4wave", type=int, default=None, choices=[0, 1],
@@ -390,11 +390,15 @@ def main():
         c = inputs.linear_case(5, M, N, K, r, s, "bf16")
         X, A, B, dY = (up(c.t[k], "bf16") for k in ("X", "A", "B", "dY"))
         W0f = up(inputs.normal(5, 1, (N, K), 1.0 / np.sqrt(K), "f32"), "f32")
-        Wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+        f8 = wl == "fp8"
+        pre = "fp8" if f8 else "w8a8"
+        code_t = torch.uint8 if f8 else torch.int8
+        Wq = torch.empty((N, K), dtype=code_t, device=dev)
         sw = torch.empty((N,), dtype=f32, device=dev)
-        check(L.w8a8_quantize_weight(N, K, 0, P(W0f), K, P(Wq), P(sw), st()), "w8a8_quantize_weight")
+        check(getattr(L, pre + "_quantize_weight")(N, K, 0, P(W0f), K, P(Wq), P(sw), st()), pre + "_quantize_weight")
+        fwd, bwd = getattr(L, pre + "_lora_linear_fwd"), getattr(L, pre + "_lora_linear_bwd")
         Y = torch.empty((M, N), dtype=bf, device=dev)
-        Xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+        Xq = torch.empty((M, K), dtype=code_t, device=dev)
         sx = torch.empty((M,), dtype=f32, device=dev)
         U = torch.empty((M, r), dtype=f32, device=dev)
         dX = torch.empty((M, K), dtype=bf, device=dev)
@@ -405,13 +409,14 @@ def main():
         ws = torch.empty(max(nf, nb, 256), dtype=torch.uint8, device=dev)
 
         def step():
-            check(L.w8a8_lora_linear_fwd(M, N, K, r, s, P(X), K, P(Wq), K, P(sw), P(A), P(B), None, P(Y), N, P(Xq),
-                                         P(sx), P(U), r, P(ws), nf, st()), "w8a8_lora_linear_fwd")
-            check(L.w8a8_lora_linear_bwd(M, N, K, r, s, P(dY), N, P(X), K, P(Wq), K, P(sw), P(A), P(B), P(U), r,
-                                         P(dX), K, P(dA), P(dB), P(ws), nb, st()), "w8a8_lora_linear_bwd")
-        flops = 4.0 * M * N * K + 6.0 * M * r * (K + N)   # int8 ops of the base counted with the bf16 ones
+            check(fwd(M, N, K, r, s, P(X), K, P(Wq), K, P(sw), P(A), P(B), None, P(Y), N, P(Xq), P(sx), P(U), r,
+                      P(ws), nf, st()), pre + "_lora_linear_fwd")
+            check(bwd(M, N, K, r, s, P(dY), N, P(X), K, P(Wq), K, P(sw), P(A), P(B), P(U), r, P(dX), K, P(dA), P(dB),
+                      P(ws), nb, st()), pre + "_lora_linear_bwd")
+        flops = 4.0 * M * N * K + 6.0 * M * r * (K + N)   # 8-bit ops of the base counted with the bf16 ones
         gemm_flops = {0: 2.0 * M * N * K + 2.0 * M * N * r, 1: 2.0 * M * N * K + 2.0 * M * K * r}
-        config = {"workload": f"W8A8 int8 base + bf16 LoRA fwd+bwd, M={M}, K=N={K}, r={r}, s={s}",
+        base = "e4m3 (fp8)" if f8 else "W8A8 int8"
+        config = {"workload": f"{base} base + bf16 LoRA fwd+bwd, M={M}, K=N={K}, r={r}, s={s}",
                   "M": M, "N": N, "K": K, "r": r, "s": s}
 
     # ------------------------------------------------------------------ warmup, then the timed region
@@ -446,7 +451,7 @@ def main():
 
     out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K_steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "bf16" if wl != "w8a8" else "int8+bf16", "data": "synthetic",
+           "vs_baseline": None, "dtype": {"w8a8": "int8+bf16", "fp8": "e4m3+bf16"}.get(wl, "bf16"), "data": "synthetic",
            "config": config, "pct_bf16_peak": round(100.0 * value / PEAK_BF16, 2)}
     if kern:
         dom = max(kern, key=lambda k: kern[k]["avg_us"])
@@ -459,7 +464,13 @@ def main():
             names = {0: "down-projection GEMM (" + ("gemm16_kernel NT" if args.gemm_4wave != 0 else "gemm_kernel NT")
                         + ")",
                      1: "input-gradient GEMM over gate and up (gemm_kernel NN)"}
-        peak = PEAK_INT8 if (wl == "w8a8" and dom == 0) else PEAK_BF16
+        if wl == "fp8":
+            names[0] = "forward base GEMM (gemm_f8_kernel NT, e4m3 block-scaled MFMA)"
+        if wl in ("w8a8", "fp8"):
+            if wl == "w8a8":
+                names[0] = "forward base GEMM (int8 NT tile: gemm16_kernel, or gemm_kernel 256x128 at few tiles)"
+            names[1] = "input-gradient GEMM (gemm_kernel NN, 8-bit weight widened to bf16 in LDS)"
+        peak = PEAK_INT8 if (wl in ("w8a8", "fp8") and dom == 0) else PEAK_BF16
         traffic = recorded_traffic(f"{wl}:{names[dom]}")
         out["roofline"] = {"bound": "mfma", "kernel": names[dom], "achieved": round(kern[dom]["tflops"], 1),
                            "peak": peak, "unit": "TFLOP/s", "frac": round(kern[dom]["tflops"] / peak, 4),

@@ -441,6 +441,32 @@ int w8a8_lora_linear_bwd(int M, int N, int K, int r, float s,
                          void* dX, int lddx, float* dA, float* dB,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ 8-bit float base
+ * The same layer over an e4m3 base ("nunchaku-style kernel fusion ...", LoRA-epilogue commit:
+ * the per-axis quantiser serves both 8-bit dtypes; MXFP8 commit: the block-scaled 8-bit float
+ * instruction with unit block scales computes the plain product at the full 8-bit rate).
+ * Codes are e4m3 bytes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, largest
+ * finite 448) passed as uint8.  Quantisation is symmetric per row: scale = absmax / 448
+ * (fp32), code = e4m3 rounding (nearest, ties to even) of the fp32 quotient x / scale
+ * clamped to +-448; a zero row has scale 0 and codes 0.  The product runs on
+ * v_mfma_scale_f32_32x32x64_f8f6f4 with every block scale 1.0 (fp32 accumulation; the
+ * instruction's internal sums keep about 17 bits relative to the largest term).
+ * Arguments, outputs, workspace (ldl_workspace_bytes with LDL_OP_W8A8_FWD / _BWD) and the
+ * straight-through backward as for the int8 base, with uint8 codes; the forward also
+ * needs N a multiple of 128 and r a multiple of 8 with r <= 64. */
+int fp8_quantize_weight(int N, int K, int dtype, const void* W0, int ldw, uint8_t* Wq, float* sw, void* stream);
+int fp8_quantize_rows(int M, int K, const void* X, int ldx, uint8_t* Xq, float* sx, void* stream);
+int fp8_lora_linear_fwd(int M, int N, int K, int r, float s,
+                        const void* X, int ldx, const uint8_t* Wq, int ldw, const float* sw,
+                        const void* A, const void* B, const void* bias,
+                        void* Y, int ldy, uint8_t* Xq_save, float* sx_save, float* U_save, int ldu,
+                        void* ws, size_t ws_bytes, void* stream);
+int fp8_lora_linear_bwd(int M, int N, int K, int r, float s,
+                        const void* dY, int lddy, const void* X, int ldx, const uint8_t* Wq, int ldw,
+                        const float* sw, const void* A, const void* B, const float* U_saved, int ldu,
+                        void* dX, int lddx, float* dA, float* dB,
+                        void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

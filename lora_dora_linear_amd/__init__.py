@@ -10,7 +10,8 @@ _EXPORTS = (
     "lora_linear_fwd", "lora_linear_bwd", "lora_linear_bwd_noalloc", "lora_dropout_mask", "lora_dropout_grad", "lora_merge_fwd", "lora_merge_bwd", "lora_multi_linear_fwd", "lora_multi_linear_bwd", "multi_workspace_bytes", "dora_prepare", "dora_linear_fwd", "dora_linear_bwd",
     "dora_cols_prepare", "dora_cols_linear_fwd", "dora_cols_linear_bwd",
     "swiglu_lora_mlp_fwd", "swiglu_lora_mlp_bwd", "geglu_lora_mlp_fwd", "geglu_lora_mlp_bwd", "w8a8_quantize_weight", "w8a8_quantize_rows",
-    "int8_gemm_raw", "w8a8_lora_linear_fwd", "w8a8_lora_linear_bwd", "workspace_bytes",
+    "int8_gemm_raw", "w8a8_lora_linear_fwd", "w8a8_lora_linear_bwd",
+    "fp8_quantize_weight", "fp8_quantize_rows", "fp8_lora_linear_fwd", "fp8_lora_linear_bwd", "workspace_bytes",
     "dora_state_floats", "set_tuning", "status_string", "lib", "LdlError",
 )
 

@@ -66,6 +66,12 @@ SIGNATURES = {
     "w8a8_quantize_weight": ([_i, _i, _i, _p, _i, _p, _p, _p], _i),
     "w8a8_quantize_rows": ([_i, _i, _p, _i, _p, _p, _p], _i),
     "int8_gemm_raw": ([_i, _i, _i, _p, _i, _p, _i, _p, _i, _p], _i),
+    "fp8_quantize_weight": ([_i, _i, _i, _p, _i, _p, _p, _p], _i),
+    "fp8_quantize_rows": ([_i, _i, _p, _i, _p, _p, _p], _i),
+    "fp8_lora_linear_fwd": ([_i, _i, _i, _i, _f, _p, _i, _p, _i, _p, _p, _p, _p, _p, _i, _p, _p, _p, _i, _p, _z,
+                             _p], _i),
+    "fp8_lora_linear_bwd": ([_i, _i, _i, _i, _f, _p, _i, _p, _i, _p, _i, _p, _p, _p, _p, _i, _p, _i, _p, _p, _p,
+                             _z, _p], _i),
     "w8a8_lora_linear_fwd": ([_i, _i, _i, _i, _f, _p, _i, _p, _i, _p, _p, _p, _p, _p, _i, _p, _p, _p, _i, _p, _z,
                               _p], _i),
     "w8a8_lora_linear_bwd": ([_i, _i, _i, _i, _f, _p, _i, _p, _i, _p, _i, _p, _p, _p, _p, _i, _p, _i, _p, _p, _p,
@@ -567,23 +573,40 @@ def _glu_bwd(name, extra, dOut, X, gate, up, down, saved, need_dx, dX):
 
 
 # ------------------------------------------------------------------ W8A8
-def w8a8_quantize_weight(W0):
+def _quantize_weight8(W0, fn, code_dtype):
     N, K = W0.shape
     ldw = _mat(W0, "W0", W0.dtype, (N, K))
-    Wq = torch.empty((N, K), dtype=torch.int8, device=W0.device)
+    Wq = torch.empty((N, K), dtype=code_dtype, device=W0.device)
     sw = torch.empty((N,), dtype=torch.float32, device=W0.device)
-    _check(lib().w8a8_quantize_weight(N, K, _dt(W0), _ptr(W0), ldw, _ptr(Wq), _ptr(sw), _stream()),
-           "w8a8_quantize_weight")
+    _check(getattr(lib(), fn)(N, K, _dt(W0), _ptr(W0), ldw, _ptr(Wq), _ptr(sw), _stream()), fn)
     return Wq, sw
 
 
-def w8a8_quantize_rows(X):
+def _quantize_rows8(X, fn, code_dtype):
     M, K = X.shape
     ldx = _mat(X, "X", torch.bfloat16, (M, K))
-    Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    Xq = torch.empty((M, K), dtype=code_dtype, device=X.device)
     sx = torch.empty((M,), dtype=torch.float32, device=X.device)
-    _check(lib().w8a8_quantize_rows(M, K, _ptr(X), ldx, _ptr(Xq), _ptr(sx), _stream()), "w8a8_quantize_rows")
+    _check(getattr(lib(), fn)(M, K, _ptr(X), ldx, _ptr(Xq), _ptr(sx), _stream()), fn)
     return Xq, sx
+
+
+def w8a8_quantize_weight(W0):
+    """Per-output-channel int8 codes (int8 [N,K]) and scales (fp32 [N])."""
+    return _quantize_weight8(W0, "w8a8_quantize_weight", torch.int8)
+
+
+def w8a8_quantize_rows(X):
+    return _quantize_rows8(X, "w8a8_quantize_rows", torch.int8)
+
+
+def fp8_quantize_weight(W0):
+    """Per-output-channel e4m3 codes (as uint8 [N,K]: the byte of each code) and scales."""
+    return _quantize_weight8(W0, "fp8_quantize_weight", torch.uint8)
+
+
+def fp8_quantize_rows(X):
+    return _quantize_rows8(X, "fp8_quantize_rows", torch.uint8)
 
 
 def int8_gemm_raw(Xq, Wq):
@@ -596,13 +619,12 @@ def int8_gemm_raw(Xq, Wq):
     return C
 
 
-def w8a8_lora_linear_fwd(X, Wq, sw, A, B, s, bias=None, save=True, Y=None):
-    """Returns (Y, Xq, sx, U)."""
+def _lora8_fwd(fn, code_dtype, X, Wq, sw, A, B, s, bias, save, Y):
     M, K = X.shape
     N, r = B.shape
     bf = torch.bfloat16
     ldx = _mat(X, "X", bf, (M, K))
-    ldw = _mat(Wq, "Wq", torch.int8, (N, K))
+    ldw = _mat(Wq, "Wq", code_dtype, (N, K))
     _need(sw, "sw", torch.float32, (N,))
     _need(A, "A", bf, (r, K))
     _need(B, "B", bf, (N, r))
@@ -610,23 +632,22 @@ def w8a8_lora_linear_fwd(X, Wq, sw, A, B, s, bias=None, save=True, Y=None):
         _need(bias, "bias", bf, (N,))
     dev = X.device
     Y, ldy = _out(Y, "Y", bf, (M, N), dev)
-    Xq = torch.empty((M, K), dtype=torch.int8, device=dev) if save else None
+    Xq = torch.empty((M, K), dtype=code_dtype, device=dev) if save else None
     sx = torch.empty((M,), dtype=torch.float32, device=dev) if save else None
     U = torch.empty((M, r), dtype=torch.float32, device=dev) if save else None
     ws, n = _ws("w8a8_fwd", M, N, K, r, LDL_BF16, dev)
-    _check(lib().w8a8_lora_linear_fwd(M, N, K, r, float(s), _ptr(X), ldx, _ptr(Wq), ldw, _ptr(sw), _ptr(A), _ptr(B),
-                                      _ptr(bias), _ptr(Y), ldy, _ptr(Xq), _ptr(sx), _ptr(U), r, _ptr(ws), n,
-                                      _stream()), "w8a8_lora_linear_fwd")
+    _check(getattr(lib(), fn)(M, N, K, r, float(s), _ptr(X), ldx, _ptr(Wq), ldw, _ptr(sw), _ptr(A), _ptr(B),
+                              _ptr(bias), _ptr(Y), ldy, _ptr(Xq), _ptr(sx), _ptr(U), r, _ptr(ws), n, _stream()), fn)
     return Y, Xq, sx, U
 
 
-def w8a8_lora_linear_bwd(dY, X, Wq, sw, A, B, s, U=None, need_dx=True, dX=None):
+def _lora8_bwd(fn, code_dtype, dY, X, Wq, sw, A, B, s, U, need_dx, dX):
     M, K = X.shape
     N, r = B.shape
     bf = torch.bfloat16
     lddy = _mat(dY, "dY", bf, (M, N))
     ldx = _mat(X, "X", bf, (M, K))
-    ldw = _mat(Wq, "Wq", torch.int8, (N, K))
+    ldw = _mat(Wq, "Wq", code_dtype, (N, K))
     ldu = _mat(U, "U", torch.float32, (M, r)) if U is not None else 0
     dev = X.device
     lddx = 0
@@ -637,7 +658,24 @@ def w8a8_lora_linear_bwd(dY, X, Wq, sw, A, B, s, U=None, need_dx=True, dX=None):
     dA = torch.empty((r, K), dtype=torch.float32, device=dev)
     dB = torch.empty((N, r), dtype=torch.float32, device=dev)
     ws, n = _ws("w8a8_bwd", M, N, K, r, LDL_BF16, dev)
-    _check(lib().w8a8_lora_linear_bwd(M, N, K, r, float(s), _ptr(dY), lddy, _ptr(X), ldx, _ptr(Wq), ldw, _ptr(sw),
-                                      _ptr(A), _ptr(B), _ptr(U), ldu, _ptr(dX), lddx, _ptr(dA), _ptr(dB), _ptr(ws), n,
-                                      _stream()), "w8a8_lora_linear_bwd")
+    _check(getattr(lib(), fn)(M, N, K, r, float(s), _ptr(dY), lddy, _ptr(X), ldx, _ptr(Wq), ldw, _ptr(sw), _ptr(A),
+                              _ptr(B), _ptr(U), ldu, _ptr(dX), lddx, _ptr(dA), _ptr(dB), _ptr(ws), n, _stream()), fn)
     return {"dX": dX, "dA": dA, "dB": dB}
+
+
+def w8a8_lora_linear_fwd(X, Wq, sw, A, B, s, bias=None, save=True, Y=None):
+    """int8 base + LoRA.  Returns (Y, Xq, sx, U)."""
+    return _lora8_fwd("w8a8_lora_linear_fwd", torch.int8, X, Wq, sw, A, B, s, bias, save, Y)
+
+
+def w8a8_lora_linear_bwd(dY, X, Wq, sw, A, B, s, U=None, need_dx=True, dX=None):
+    return _lora8_bwd("w8a8_lora_linear_bwd", torch.int8, dY, X, Wq, sw, A, B, s, U, need_dx, dX)
+
+
+def fp8_lora_linear_fwd(X, Wq, sw, A, B, s, bias=None, save=True, Y=None):
+    """e4m3 base + LoRA (Wq: uint8 bytes of the e4m3 codes).  Returns (Y, Xq, sx, U)."""
+    return _lora8_fwd("fp8_lora_linear_fwd", torch.uint8, X, Wq, sw, A, B, s, bias, save, Y)
+
+
+def fp8_lora_linear_bwd(dY, X, Wq, sw, A, B, s, U=None, need_dx=True, dX=None):
+    return _lora8_bwd("fp8_lora_linear_bwd", torch.uint8, dY, X, Wq, sw, A, B, s, U, need_dx, dX)

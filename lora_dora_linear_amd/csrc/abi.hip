@@ -1302,25 +1302,39 @@ int geglu_lora_mlp_bwd(int M, int K, int H, int r, float s_gate, float s_up, flo
 }
 
 // =========================================================================== W8A8
-int w8a8_quantize_weight(int N, int K, int dtype, const void* W0, int ldw, int8_t* Wq, float* sw, void* stream) {
+static int quantize_weight8(int N, int K, int dtype, const void* W0, int ldw, int8_t* Wq, float* sw, void* stream,
+                            int fp8) {
   if (!nonnull({W0, Wq, sw})) return LDL_E_INVAL;
   if (N <= 0 || K <= 0) return LDL_E_INVAL;
   if (dtype != LDL_F32 && dtype != LDL_BF16) return LDL_E_INVAL;
   if (K % 8 || !al({W0, Wq, sw})) return LDL_E_UNSUPPORTED;
   LDL_LD(ldw, K, dtype == LDL_BF16 ? 8 : 1);
   if (!fits(N, ldw, dtype == LDL_BF16 ? 2 : 4) || !fits(N, K, 1)) return LDL_E_UNSUPPORTED;
-  LDL_TRY(launch_quantize_rows(W0, dtype == LDL_F32, N, K, ldw, Wq, sw, S(stream)));
+  LDL_TRY(launch_quantize_rows(W0, dtype == LDL_F32, N, K, ldw, Wq, sw, S(stream), fp8));
   return LDL_OK;
 }
 
-int w8a8_quantize_rows(int M, int K, const void* X, int ldx, int8_t* Xq, float* sx, void* stream) {
+static int quantize_rows8(int M, int K, const void* X, int ldx, int8_t* Xq, float* sx, void* stream, int fp8) {
   if (M > 0 && !nonnull({X, Xq, sx})) return LDL_E_INVAL;
   if (M < 0 || K <= 0) return LDL_E_INVAL;
   if (K % 8 || !al({X, Xq, sx})) return LDL_E_UNSUPPORTED;
   LDL_LD(ldx, K, 8);
   if (!fits(M, ldx, 2)) return LDL_E_UNSUPPORTED;
-  LDL_TRY(launch_quantize_rows(X, 0, M, K, ldx, Xq, sx, S(stream)));
+  LDL_TRY(launch_quantize_rows(X, 0, M, K, ldx, Xq, sx, S(stream), fp8));
   return LDL_OK;
+}
+
+int w8a8_quantize_weight(int N, int K, int dtype, const void* W0, int ldw, int8_t* Wq, float* sw, void* stream) {
+  return quantize_weight8(N, K, dtype, W0, ldw, Wq, sw, stream, 0);
+}
+int w8a8_quantize_rows(int M, int K, const void* X, int ldx, int8_t* Xq, float* sx, void* stream) {
+  return quantize_rows8(M, K, X, ldx, Xq, sx, stream, 0);
+}
+int fp8_quantize_weight(int N, int K, int dtype, const void* W0, int ldw, uint8_t* Wq, float* sw, void* stream) {
+  return quantize_weight8(N, K, dtype, W0, ldw, reinterpret_cast<int8_t*>(Wq), sw, stream, 1);
+}
+int fp8_quantize_rows(int M, int K, const void* X, int ldx, uint8_t* Xq, float* sx, void* stream) {
+  return quantize_rows8(M, K, X, ldx, reinterpret_cast<int8_t*>(Xq), sx, stream, 1);
 }
 
 int int8_gemm_raw(int M, int N, int K, const int8_t* Xq, int ldxq, const int8_t* Wq, int ldwq, int32_t* C, int ldc,
@@ -1337,15 +1351,16 @@ int int8_gemm_raw(int M, int N, int K, const int8_t* Xq, int ldxq, const int8_t*
   return LDL_OK;
 }
 
-int w8a8_lora_linear_fwd(int M, int N, int K, int r, float s, const void* X, int ldx, const int8_t* Wq, int ldw,
-                         const float* sw, const void* A, const void* B, const void* bias, void* Y, int ldy,
-                         int8_t* Xq_save, float* sx_save, float* U_save, int ldu, void* ws, size_t ws_bytes,
-                         void* stream) {
+static int lora8_fwd(int fp8, int M, int N, int K, int r, float s, const void* X, int ldx, const int8_t* Wq, int ldw,
+                     const float* sw, const void* A, const void* B, const void* bias, void* Y, int ldy,
+                     int8_t* Xq_save, float* sx_save, float* U_save, int ldu, void* ws, size_t ws_bytes,
+                     void* stream) {
   if (!nonnull({Wq, sw, A, B}) || (M > 0 && !nonnull({X, Y}))) return LDL_E_INVAL;
   if ((Xq_save == nullptr) != (sx_save == nullptr)) return LDL_E_INVAL;
   const int chk = check_bf16_layer(M, N, K, r);
   if (chk != LDL_OK) return chk;
   if (K % 128) return LDL_E_UNSUPPORTED;
+  if (fp8 && (N % 128 || r % 8 || r > 64)) return LDL_E_UNSUPPORTED;
   LDL_LD(ldx, K, 8); LDL_LD(ldw, K, 16); LDL_LD(ldy, N, 8); LDL_LD(ldu, r, 4);
   if (!fits(M, ldx, 2) || !fits(N, ldw, 1) || !fits(M, ldy, 2) || !fits(M, ldu, 4)) return LDL_E_UNSUPPORTED;
   if (!al({X, Wq, sw, A, B, bias, Y, Xq_save, sx_save, U_save, ws})) return LDL_E_UNSUPPORTED;
@@ -1361,7 +1376,7 @@ int w8a8_lora_linear_fwd(int M, int N, int K, int r, float s, const void* X, int
   const int lu = U_save ? ldu : r;
   int8_t* Xq = Xq_save ? Xq_save : Xqw;
   float* sx = sx_save ? sx_save : sxw;
-  LDL_TRY(launch_quantize_rows(X, 0, M, K, ldx, Xq, sx, st));
+  LDL_TRY(launch_quantize_rows(X, 0, M, K, ldx, Xq, sx, st, fp8));
   LDL_TRY(rowproj(M, K, r, X, ldx, A, nullptr, r, K, U, lu, 1.f, st));
   GemmParams p = gp0();
   p.M = M; p.N = N; p.K = K;
@@ -1370,14 +1385,30 @@ int w8a8_lora_linear_fwd(int M, int N, int K, int r, float s, const void* X, int
   p.S = U; p.ld_s = lu; p.r_epi = r; p.s_epi = s;
   p.e0 = B; p.e1 = B; p.e_ldn = r; p.e_ldj = 1; p.e_jsplit = r;
   p.bias = bias; p.out = Y; p.ldo = ldy;
-  LDL_TRY(gemm_timed(0, GK_NT_I8_DEQ, p, st));
+  LDL_TRY(gemm_timed(0, fp8 ? GK_NT_F8_DEQ : GK_NT_I8_DEQ, p, st));
   return LDL_OK;
 }
 
-int w8a8_lora_linear_bwd(int M, int N, int K, int r, float s, const void* dY, int lddy, const void* X, int ldx,
-                         const int8_t* Wq, int ldw, const float* sw, const void* A, const void* B,
-                         const float* U_saved, int ldu, void* dX, int lddx, float* dA, float* dB, void* ws,
-                         size_t ws_bytes, void* stream) {
+int w8a8_lora_linear_fwd(int M, int N, int K, int r, float s, const void* X, int ldx, const int8_t* Wq, int ldw,
+                         const float* sw, const void* A, const void* B, const void* bias, void* Y, int ldy,
+                         int8_t* Xq_save, float* sx_save, float* U_save, int ldu, void* ws, size_t ws_bytes,
+                         void* stream) {
+  return lora8_fwd(0, M, N, K, r, s, X, ldx, Wq, ldw, sw, A, B, bias, Y, ldy, Xq_save, sx_save, U_save, ldu, ws,
+                   ws_bytes, stream);
+}
+
+int fp8_lora_linear_fwd(int M, int N, int K, int r, float s, const void* X, int ldx, const uint8_t* Wq, int ldw,
+                        const float* sw, const void* A, const void* B, const void* bias, void* Y, int ldy,
+                        uint8_t* Xq_save, float* sx_save, float* U_save, int ldu, void* ws, size_t ws_bytes,
+                        void* stream) {
+  return lora8_fwd(1, M, N, K, r, s, X, ldx, reinterpret_cast<const int8_t*>(Wq), ldw, sw, A, B, bias, Y, ldy,
+                   reinterpret_cast<int8_t*>(Xq_save), sx_save, U_save, ldu, ws, ws_bytes, stream);
+}
+
+static int lora8_bwd(int fp8, int M, int N, int K, int r, float s, const void* dY, int lddy, const void* X, int ldx,
+                     const int8_t* Wq, int ldw, const float* sw, const void* A, const void* B,
+                     const float* U_saved, int ldu, void* dX, int lddx, float* dA, float* dB, void* ws,
+                     size_t ws_bytes, void* stream) {
   if (!nonnull({Wq, sw, A, B, dA, dB, ws}) || (M > 0 && !nonnull({dY, X}))) return LDL_E_INVAL;
   const int chk = check_bf16_layer(M, N, K, r);
   if (chk != LDL_OK) return chk;
@@ -1408,7 +1439,7 @@ int w8a8_lora_linear_bwd(int M, int N, int K, int r, float s, const void* dY, in
     p.a = dY; p.lda = lddy; p.a_colscale = sw; p.b0 = Wq; p.b1 = Wq; p.ldb = ldw; p.kseg = N;
     p.S = w.V; p.ld_s = r; p.r_epi = r; p.s_epi = s;
     p.e0 = A; p.e1 = A; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = r;
-    p.out = dX; p.ldo = lddx;
+    p.out = dX; p.ldo = lddx; p.q_fp8 = fp8;
     LDL_TRY(gemm_timed(1, GK_NN_I8_SCALE, p, st));
   }
   LDL_TRY(launch_colproj2(
@@ -1417,6 +1448,22 @@ int w8a8_lora_linear_bwd(int M, int N, int K, int r, float s, const void* dY, in
   LDL_TRY(launch_reduce2(rdp(N, r, w.partB, (size_t)N * w.rp, w.nsB, w.rp, false, s, dB, r),
                          rdp(r, K, w.partA, (size_t)K * w.rp, w.nsA, w.rp, true, s, dA, K), st));
   return LDL_OK;
+}
+
+int w8a8_lora_linear_bwd(int M, int N, int K, int r, float s, const void* dY, int lddy, const void* X, int ldx,
+                         const int8_t* Wq, int ldw, const float* sw, const void* A, const void* B,
+                         const float* U_saved, int ldu, void* dX, int lddx, float* dA, float* dB, void* ws,
+                         size_t ws_bytes, void* stream) {
+  return lora8_bwd(0, M, N, K, r, s, dY, lddy, X, ldx, Wq, ldw, sw, A, B, U_saved, ldu, dX, lddx, dA, dB, ws,
+                   ws_bytes, stream);
+}
+
+int fp8_lora_linear_bwd(int M, int N, int K, int r, float s, const void* dY, int lddy, const void* X, int ldx,
+                        const uint8_t* Wq, int ldw, const float* sw, const void* A, const void* B,
+                        const float* U_saved, int ldu, void* dX, int lddx, float* dA, float* dB, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return lora8_bwd(1, M, N, K, r, s, dY, lddy, X, ldx, reinterpret_cast<const int8_t*>(Wq), ldw, sw, A, B, U_saved,
+                   ldu, dX, lddx, dA, dB, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

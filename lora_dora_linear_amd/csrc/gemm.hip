@@ -10,6 +10,7 @@
 //   NN (bf16/int8 Q) 256x256, 256x192, 256x128, 128x128, 128x64
 #include "internal.hpp"
 #include "gemm16.hpp"
+#include "gemm_f8.hpp"
 
 namespace ldl {
 
@@ -147,8 +148,24 @@ bool gemm_multi_leaf_ok(const GemmParams& p) {
          (p.N % 256 == 0 || b192_fills(p.M, p.N));
 }
 
+// e4m3 base: 256-column tiles, or 128-column ones where those fill the chip better or the
+// width is not a multiple of 256 (a multiple of 128 is required), K a multiple of 128
+static hipError_t run_f8(const GemmParams& p0, hipStream_t st) {
+  GemmParams p = p0;
+  if (p.N % 128 || p.K % 128 || p.r_epi > 64 || !seed_ok(GK_NT_PLAIN, p) || !a16(p.col_scale))
+    return hipErrorInvalidValue;
+  p.seed_hilo = (p.r_epi > 0 && 2 * p.r_epi <= 64) ? 1 : 0;
+  const int tm = (p.M + 255) / 256;
+  if (p.N % 256 == 0 && !half_tiles_pay(p.M, p.N))
+    hipLaunchKernelGGL(gemm_f8_kernel<256>, dim3(tm * (p.N / 256)), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL(gemm_f8_kernel<128>, dim3(tm * (p.N / 128)), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
   if (p.M <= 0) return hipSuccess;
+  if (kind == GK_NT_F8_DEQ) return run_f8(p, st);
   if (p.nleaf > 0 && (kind != GK_NT_PLAIN || !gemm_multi_leaf_ok(p))) return hipErrorInvalidValue;
   const int bn = pick_bn(kind, p.N);
   const bool big = p.M > 128;

@@ -61,6 +61,7 @@ struct GemmParams {
   const void* aux0; int ld_aux0;
   const void* aux1; int ld_aux1;
   float* side_save; int ld_side_save;
+  int q_fp8;                         // NN with 8-bit Q: the codes are e4m3 (else int8)
   int seed_hilo;                     // four-wave tile: low-rank term as bf16 hi + lo (set by the launcher)
   int act;                           // gated MLP activation: ACT_SILU, ACT_GELU, ACT_GELU_TANH
   // several adapters over one concatenated output (four-wave NT seed only): output column n
@@ -88,7 +89,8 @@ struct GemmCfg {
   // a 64-float slice of the scale vector copied with each stage)
   static constexpr bool kNNTr = NN_ && (BN_ == 64 || BN_ == 128 || BN_ == 256);
   // int8 Q on the transposed path: its rows copied as stored into an int8 staging tile and
-  // widened (times the row scale) into the bf16 Q tile at the stage hand-over
+  // widened (times the row scale) into the bf16 Q tile at the stage hand-over (int8 or e4m3
+  // codes, p.q_fp8)
   static constexpr bool kQ8 = kNNTr && BINT8_;
   static constexpr int kSideRsp = SIDE_RSP_;// fused side rows (padded to 16), 0: none
   static constexpr bool kSLoad = SLOAD_;    // epilogue S from global
@@ -549,6 +551,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
       typedef __bf16 b2 __attribute__((ext_vector_type(2)));
       uint8_t* sB = sbuf + BM * 128;
       const float* sc8 = reinterpret_cast<const float*>(s8 + 64 * BN);
+      const bool f8 = p.q_fp8 != 0;
 #pragma unroll
       for (int u = tid; u < 4 * BN; u += C::kThreads) {
         const int k = u / (BN / 16), c16 = u % (BN / 16);
@@ -559,9 +562,16 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmParams p
           u32x4 o;
 #pragma unroll
           for (int d = 0; d < 2; ++d) {
-            const uint32_t w = v[2 * h + d] ^ 0x80808080u;
-            const f2 lo = {__builtin_fmaf((float)(w & 0xffu), sc, c0), __builtin_fmaf((float)((w >> 8) & 0xffu), sc, c0)};
-            const f2 hi = {__builtin_fmaf((float)((w >> 16) & 0xffu), sc, c0), __builtin_fmaf((float)(w >> 24), sc, c0)};
+            f2 lo, hi;
+            if (f8) {            // e4m3 codes: exact fp32 values, times the row scale
+              const uint32_t w = v[2 * h + d];
+              lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false) * sc;
+              hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true) * sc;
+            } else {
+              const uint32_t w = v[2 * h + d] ^ 0x80808080u;
+              lo = f2{__builtin_fmaf((float)(w & 0xffu), sc, c0), __builtin_fmaf((float)((w >> 8) & 0xffu), sc, c0)};
+              hi = f2{__builtin_fmaf((float)((w >> 16) & 0xffu), sc, c0), __builtin_fmaf((float)(w >> 24), sc, c0)};
+            }
             o[2 * d] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, b2));
             o[2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, b2));
           }

@@ -47,7 +47,8 @@ struct ReduceParams {
 enum GemmKind : int {
   GK_NT_PLAIN, GK_NT_FUSED, GK_NT_DORA, GK_NT_SWIGLU_DUAL, GK_NT_I8_DEQ, GK_NT_I8_RAW,
   GK_NN_PLAIN, GK_NN_SCALE, GK_NN_I8_SCALE, GK_NN_SWIGLU,
-  GK_NN_DORA     // NN with the two-output column-scale epilogue: out2 = z, out = z * col_scale[n]
+  GK_NN_DORA,    // NN with the two-output column-scale epilogue: out2 = z, out = z * col_scale[n]
+  GK_NT_F8_DEQ   // e4m3 P and Q, dequantised by row_scale[m] col_scale[n], + low-rank term (+ bias)
 };
 hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st);
 extern int g_gemm_4wave;   // plain bf16 GEMMs on the four-wave 16x16x32 tile (tuning switch)
@@ -104,8 +105,9 @@ hipError_t launch_dora_cols_db(int N, int r, float s, const void* B, const float
 hipError_t launch_mask_cols(const void* in, const uint8_t* keep, int rows, int K, int esz, void* out, hipStream_t st);
 
 // W8A8 helpers
+// fp8: e4m3 codes (scale absmax / 448) instead of int8 (absmax / 127)
 hipError_t launch_quantize_rows(const void* X, int in_f32, int M, int K, int ldx, int8_t* q, float* scale,
-                                hipStream_t st);
+                                hipStream_t st, int fp8 = 0);
 
 // fp32 path: C[m, n] = alpha * sum_k A(m, k) B(k, n) + beta * C[m, n] (+ bias[n])
 struct F32GemmParams {

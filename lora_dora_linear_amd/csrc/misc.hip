@@ -263,10 +263,25 @@ hipError_t launch_mask_cols(const void* in, const uint8_t* keep, int rows, int K
   return hipGetLastError();
 }
 
-// ============================================================================ int8 quantiser
-// Symmetric per-row codes: scale = absmax / 127 (fp32), q = clamp(rint(x / scale), +-127)
-// with the quotient in fp32 and ties to even; scale 0 -> q = 0.  One wave per row.
-template <bool F32IN>
+// ============================================================================ 8-bit quantisers
+// Symmetric per-row codes with the quotient x / scale in fp32; scale 0 -> code 0.  One wave
+// per row.  int8: scale = absmax / 127, code = clamp(rint(x / scale), +-127) (ties to even).
+// e4m3 (FP8): scale = absmax / 448, code = the e4m3 rounding (nearest, ties to even) of the
+// quotient clamped to +-448, by the hardware conversion.
+template <bool FP8>
+__device__ __forceinline__ uint32_t q8_code(float x, float sc) {
+  if (!(sc > 0.f)) return 0u;
+  if constexpr (FP8) {
+    const float t = fminf(fmaxf(x / sc, -448.f), 448.f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t, 0.f, 0, false) & 0xffu;
+  } else {
+    float t = rintf(x / sc);
+    t = fminf(fmaxf(t, -127.f), 127.f);
+    return (uint32_t)((int)t & 0xff);
+  }
+}
+
+template <bool F32IN, bool FP8>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* X, int M, int K, int ldx, int8_t* q,
                                                             float* scale) {
   const int lane = threadIdx.x & 63;
@@ -285,18 +300,13 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* X, int M
     }
   }
   amax = wave_max(amax);
-  const float sc = amax / 127.0f;
+  const float sc = amax / (FP8 ? 448.0f : 127.0f);
   if (lane == 0) scale[row] = sc;
   int8_t* qrow = q + (size_t)row * K;
-  auto code = [&](float x) -> int {
-    if (!(sc > 0.f)) return 0;
-    float t = rintf(x / sc);
-    t = fminf(fmaxf(t, -127.f), 127.f);
-    return (int)t;
-  };
+  auto code = [&](float x) -> uint32_t { return q8_code<FP8>(x, sc); };
   if (F32IN) {
     const float* x = static_cast<const float*>(X) + (size_t)row * ldx;
-    for (int k = lane; k < K; k += 64) qrow[k] = (int8_t)code(x[k]);
+    for (int k = lane; k < K; k += 64) qrow[k] = (int8_t)(uint8_t)code(x[k]);
   } else {
     const uint16_t* x = static_cast<const uint16_t*>(X) + (size_t)row * ldx;
     for (int k = lane * 8; k < K; k += 512) {
@@ -304,10 +314,10 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* X, int M
       u32x2 o;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const uint32_t b0 = (uint32_t)(code(bf16_lo(v[2 * h])) & 0xff);
-        const uint32_t b1 = (uint32_t)(code(bf16_hi(v[2 * h])) & 0xff);
-        const uint32_t b2 = (uint32_t)(code(bf16_lo(v[2 * h + 1])) & 0xff);
-        const uint32_t b3 = (uint32_t)(code(bf16_hi(v[2 * h + 1])) & 0xff);
+        const uint32_t b0 = code(bf16_lo(v[2 * h]));
+        const uint32_t b1 = code(bf16_hi(v[2 * h]));
+        const uint32_t b2 = code(bf16_lo(v[2 * h + 1]));
+        const uint32_t b3 = code(bf16_hi(v[2 * h + 1]));
         o[h] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
       }
       *reinterpret_cast<u32x2*>(qrow + k) = o;
@@ -318,6 +328,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* X, int M
 // bf16 rows of K <= 512 QV elements (K a multiple of 512): the same codes from one read of
 // the row, kept in registers (QV 16-byte pieces per lane) between the absmax and the codes.
 constexpr int kQuantRegPieces = 16;
+template <bool FP8>
 __global__ __launch_bounds__(256) void quantize_rows_reg_kernel(const uint16_t* X, int M, int K, int ldx, int8_t* q,
                                                                 float* scale) {
   constexpr int QV = kQuantRegPieces;
@@ -335,14 +346,9 @@ __global__ __launch_bounds__(256) void quantize_rows_reg_kernel(const uint16_t* 
 #pragma unroll
     for (int t = 0; t < 4; ++t) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[i][t])), fabsf(bf16_hi(v[i][t]))));
   amax = wave_max(amax);
-  const float sc = amax / 127.0f;
+  const float sc = amax / (FP8 ? 448.0f : 127.0f);
   if (lane == 0) scale[row] = sc;
-  auto code = [&](float xv) -> uint32_t {
-    if (!(sc > 0.f)) return 0u;
-    float t = rintf(xv / sc);
-    t = fminf(fmaxf(t, -127.f), 127.f);
-    return (uint32_t)((int)t & 0xff);
-  };
+  auto code = [&](float xv) -> uint32_t { return q8_code<FP8>(xv, sc); };
   int8_t* qrow = q + (size_t)row * K + lane * 8;
 #pragma unroll
   for (int i = 0; i < QV; ++i) {
@@ -358,16 +364,23 @@ __global__ __launch_bounds__(256) void quantize_rows_reg_kernel(const uint16_t* 
 }
 
 // X rows of leading dimension ldx (16-byte aligned rows for bf16), codes written as dense [M, K].
-hipError_t launch_quantize_rows(const void* X, int in_f32, int M, int K, int ldx, int8_t* q, float* scale,
-                                hipStream_t st) {
-  if (M <= 0) return hipSuccess;
+template <bool FP8>
+static void quantize_rows_launch(const void* X, int in_f32, int M, int K, int ldx, int8_t* q, float* scale,
+                                 hipStream_t st) {
   const dim3 grid((M + 3) / 4), block(256);
-  if (in_f32) hipLaunchKernelGGL(quantize_rows_kernel<true>, grid, block, 0, st, X, M, K, ldx, q, scale);
+  if (in_f32) hipLaunchKernelGGL((quantize_rows_kernel<true, FP8>), grid, block, 0, st, X, M, K, ldx, q, scale);
   else if (K % 512 == 0 && K <= 512 * kQuantRegPieces &&
            (reinterpret_cast<uintptr_t>(X) & 15) == 0 && (reinterpret_cast<uintptr_t>(q) & 7) == 0)
-    hipLaunchKernelGGL(quantize_rows_reg_kernel, grid, block, 0, st, static_cast<const uint16_t*>(X), M, K, ldx, q,
-                       scale);
-  else hipLaunchKernelGGL(quantize_rows_kernel<false>, grid, block, 0, st, X, M, K, ldx, q, scale);
+    hipLaunchKernelGGL(quantize_rows_reg_kernel<FP8>, grid, block, 0, st, static_cast<const uint16_t*>(X), M, K, ldx,
+                       q, scale);
+  else hipLaunchKernelGGL((quantize_rows_kernel<false, FP8>), grid, block, 0, st, X, M, K, ldx, q, scale);
+}
+
+hipError_t launch_quantize_rows(const void* X, int in_f32, int M, int K, int ldx, int8_t* q, float* scale,
+                                hipStream_t st, int fp8) {
+  if (M <= 0) return hipSuccess;
+  if (fp8) quantize_rows_launch<true>(X, in_f32, M, K, ldx, q, scale, st);
+  else quantize_rows_launch<false>(X, in_f32, M, K, ldx, q, scale, st);
   return hipGetLastError();
 }
 
