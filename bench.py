@@ -34,7 +34,8 @@ def parse():
     # 200 untimed steps reach the sustained clock, 1000 timed steps take about 0.3 s
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="lora", choices=["lora", "dora", "swiglu", "w8a8", "fp8", "tiny", "merge"])
+    ap.add_argument("--workload", default="lora", choices=["lora", "dora", "dora_cols", "qkv", "swiglu", "geglu", "w8a8", "fp8", "tiny",
+                                                           "merge"])
     ap.add_argument("--M", type=int, default=None, help="token count override (w8a8 / fp8 sweep point)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused-downproj", type=int, default=None, choices=[0, 1])
@@ -354,7 +355,65 @@ def main():
         gemm_flops = {0: 2.0 * M * N * K + 2.0 * M * N * r, 1: 2.0 * M * N * K + 2.0 * M * K * r}
         config = {"workload": f"bf16 DoRA (row-scaled) linear fwd+bwd, M={M}, K=N={K}, r={r}, s={s}, eps={eps}",
                   "M": M, "N": N, "K": K, "r": r, "s": s}
-    elif wl == "swiglu":
+    elif wl == "dora_cols":
+        M, N, K, r, s, eps = 4096, 3072, 3072, 32, 1.0, 1e-12
+        c = inputs.linear_case(3, M, N, K, r, s, "bf16", dora_cols=True)
+        X, W0, A, B, dY = (up(c.t[k], "bf16") for k in ("X", "W0", "A", "B", "dY"))
+        m = up(c.t["m"], "f32")
+        w0sq = torch.empty((K,), dtype=f32, device=dev)
+        check(L.dora_cols_prepare(N, K, 1, P(W0), K, P(w0sq), st()), "dora_cols_prepare")
+        Y = torch.empty((M, N), dtype=bf, device=dev)
+        Xs = torch.empty((M, K), dtype=bf, device=dev)
+        U = torch.empty((M, r), dtype=f32, device=dev)
+        state = torch.empty((binding.dora_state_floats(K, r),), dtype=f32, device=dev)
+        dX = torch.empty((M, K), dtype=bf, device=dev)
+        dA = torch.empty((r, K), dtype=f32, device=dev)
+        dB = torch.empty((N, r), dtype=f32, device=dev)
+        dm = torch.empty((K,), dtype=f32, device=dev)
+        nf = binding.workspace_bytes("dora_cols_fwd", M, N, K, r)
+        nb = binding.workspace_bytes("dora_cols_bwd", M, N, K, r)
+        ws = torch.empty(max(nf, nb, 256), dtype=torch.uint8, device=dev)
+
+        def step():
+            check(L.dora_cols_linear_fwd(M, N, K, r, s, eps, 1, P(X), K, P(W0), K, P(A), P(B), P(m), P(w0sq), None,
+                                         P(Y), N, P(U), r, P(Xs), K, P(state), P(ws), nf, st()), "dora_cols_linear_fwd")
+            check(L.dora_cols_linear_bwd(M, N, K, r, s, eps, 1, P(dY), N, P(X), K, P(Xs), K, P(W0), K, P(A), P(B),
+                                         P(m), P(U), r, P(state), P(dX), K, P(dA), P(dB), P(dm), None, P(ws), nb, st()),
+                  "dora_cols_linear_bwd")
+        lora_flops = 4.0 * M * N * K + 6.0 * M * r * (K + N)
+        dora_flops = 2.0 * N * K * r * 2 + 2.0 * N * r * r        # Pc = B^T.W0 and W0.(A.diag(w))^T, plus Gc
+        flops = lora_flops + dora_flops
+        gemm_flops = {0: 2.0 * M * N * K + 2.0 * M * N * r, 1: 2.0 * M * N * K + 2.0 * M * K * r}
+        config = {"workload": f"bf16 DoRA (column-scaled) linear fwd+bwd, M={M}, K=N={K}, r={r}, s={s}, eps={eps}",
+                  "M": M, "N": N, "K": K, "r": r, "s": s}
+    elif wl == "qkv":
+        M, K, r = 4096, 4096, 16
+        leaves, s_leaf = (4096, 1024, 1024), (2.0, 2.0, 2.0)
+        N, nl = sum(leaves), len(leaves)
+        c = inputs.multi_case(6, M, K, leaves, r, s_leaf)
+        X, W0, A, B, dY = (up(c.t[k], "bf16") for k in ("X", "W0", "A", "B", "dY"))
+        nleaf = (ctypes.c_int * nl)(*leaves)
+        sleaf = (ctypes.c_float * nl)(*s_leaf)
+        Y = torch.empty((M, N), dtype=bf, device=dev)
+        U = torch.empty((M, nl * r), dtype=f32, device=dev)
+        dX = torch.empty((M, K), dtype=bf, device=dev)
+        dA = torch.empty((nl * r, K), dtype=f32, device=dev)
+        dB = torch.empty((N, r), dtype=f32, device=dev)
+        nb = binding.multi_workspace_bytes("lora_bwd", M, K, leaves, r)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        cp = lambda a: ctypes.cast(a, ctypes.c_void_p)  # noqa: E731
+
+        def step():
+            check(L.lora_multi_linear_fwd(M, K, nl, cp(nleaf), r, cp(sleaf), 1, P(X), K, P(W0), K, P(A), P(B), None,
+                                          P(Y), N, P(U), nl * r, P(ws), 0, st()), "lora_multi_linear_fwd")
+            check(L.lora_multi_linear_bwd(M, K, nl, cp(nleaf), r, cp(sleaf), 1, P(dY), N, P(X), K, P(W0), K, P(A),
+                                          P(B), P(U), nl * r, P(dX), K, P(dA), P(dB), None, P(ws), nb, st()),
+                  "lora_multi_linear_bwd")
+        flops = 4.0 * M * N * K + 6.0 * M * r * (nl * K + N)
+        gemm_flops = {0: 2.0 * M * N * K + 2.0 * M * N * nl * r, 1: 2.0 * M * N * K + 2.0 * M * K * nl * r}
+        config = {"workload": f"bf16 fused QKV leaves fwd+bwd, M={M}, K={K}, leaves q/k/v={leaves}, r={r} each, "
+                              f"s={s_leaf[0]}", "M": M, "N": N, "K": K, "r": r, "leaves": list(leaves)}
+    elif wl in ("swiglu", "geglu"):
         M, K, H, r, s = 8192, 4096, 14336, 64, 0.25
         c = inputs.mlp_case(4, M, K, H, r, s)
         Xd, dO = up(c.t["X"], "bf16"), up(c.t["dY"], "bf16")
@@ -371,18 +430,24 @@ def main():
         ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
         w = [P(Wt[k]) for k in ("Wg", "Ag", "Bg", "Wu", "Au", "Bu", "Wd", "Ad", "Bd")]
 
+        if wl == "swiglu":
+            fwd, bwd, act = L.swiglu_lora_mlp_fwd, L.swiglu_lora_mlp_bwd, ()
+        else:
+            fwd, bwd, act = L.geglu_lora_mlp_fwd, L.geglu_lora_mlp_bwd, (0,)   # exact gelu
+
         def step():
-            check(L.swiglu_lora_mlp_fwd(M, K, H, r, s, s, s, P(Xd), K, *w, P(Out), K, P(E), P(Gu), P(Hs), P(U),
-                                        P(ws), 0, st()), "swiglu_lora_mlp_fwd")
-            check(L.swiglu_lora_mlp_bwd(M, K, H, r, s, s, s, P(dO), K, P(Xd), K, *w, P(E), P(Gu), P(Hs), P(U),
-                                        P(dX), K, P(gr["dAg"]), P(gr["dBg"]), P(gr["dAu"]), P(gr["dBu"]),
-                                        P(gr["dAd"]), P(gr["dBd"]), P(ws), nb, st()), "swiglu_lora_mlp_bwd")
+            check(fwd(M, K, H, r, s, s, s, *act, P(Xd), K, *w, P(Out), K, P(E), P(Gu), P(Hs), P(U), P(ws), 0, st()),
+                  wl + "_lora_mlp_fwd")
+            check(bwd(M, K, H, r, s, s, s, *act, P(dO), K, P(Xd), K, *w, P(E), P(Gu), P(Hs), P(U), P(dX), K,
+                      P(gr["dAg"]), P(gr["dBg"]), P(gr["dAu"]), P(gr["dBu"]), P(gr["dAd"]), P(gr["dBd"]), P(ws), nb,
+                      st()), wl + "_lora_mlp_bwd")
         base = 2.0 * M * K * H * 3 * 2           # three projections, forward + input gradient
         lora = 3 * (6.0 * M * r * (K + H))
         flops = base + lora
         # timed: the down projection (NT, four-wave) and dX over the 2H reduction (NN, eight-wave)
         gemm_flops = {0: 2.0 * M * K * H + 2.0 * M * K * r, 1: 2.0 * M * K * 2 * H + 2.0 * M * K * 2 * r}
-        config = {"workload": f"bf16 LoRA MLP with fused SwiGLU fwd+bwd, M={M}, K={K}, H={H}, r={r}, s={s}",
+        actname = "SwiGLU" if wl == "swiglu" else "GeGLU (exact gelu)"
+        config = {"workload": f"bf16 LoRA MLP with fused {actname} fwd+bwd, M={M}, K={K}, H={H}, r={r}, s={s}",
                   "M": M, "K": K, "H": H, "r": r, "s": s}
     else:
         M = args.M or 4096
@@ -457,10 +522,10 @@ def main():
         dom = max(kern, key=lambda k: kern[k]["avg_us"])
         # the LoRA and DoRA products (N a multiple of 256) run on the four-wave tile unless
         # it is switched off
-        four = wl in ("lora", "dora") and args.gemm_4wave != 0
+        four = wl in ("lora", "dora", "dora_cols", "qkv") and args.gemm_4wave != 0
         names = {0: "forward base GEMM (" + ("gemm16_kernel NT" if four else "gemm_kernel NT") + ")",
                  1: "input-gradient GEMM (" + ("gemm16_kernel NN" if four else "gemm_kernel NN") + ")"}
-        if wl == "swiglu":
+        if wl in ("swiglu", "geglu"):
             names = {0: "down-projection GEMM (" + ("gemm16_kernel NT" if args.gemm_4wave != 0 else "gemm_kernel NT")
                         + ")",
                      1: "input-gradient GEMM over gate and up (gemm_kernel NN)"}

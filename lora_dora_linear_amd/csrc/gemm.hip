@@ -63,6 +63,13 @@ static hipError_t run16(const GemmParams& p0, hipStream_t st) {
   GemmParams p = p0;
   p.seed_hilo = (p.r_epi > 0 && 2 * p.r_epi <= 64) ? 1 : 0;
   const int tiles = ((p.M + 255) / 256) * (p.N / BN);
+  if constexpr (!NN && !DORA && !SWB) {
+    if (p.nleaf > 0) {
+      hipLaunchKernelGGL((gemm16_kernel<false, 1, false, false, BN, false, false, true>), dim3(tiles), dim3(256), 0, st,
+                         p);
+      return hipGetLastError();
+    }
+  }
   if (p.r_epi > 0) hipLaunchKernelGGL((gemm16_kernel<NN, 1, DORA, SWB, BN>), dim3(tiles), dim3(256), 0, st, p);
   else hipLaunchKernelGGL((gemm16_kernel<NN, 0, DORA, SWB, BN>), dim3(tiles), dim3(256), 0, st, p);
   return hipGetLastError();
@@ -99,10 +106,15 @@ static hipError_t run16_dual(const GemmParams& p, hipStream_t st) {
 }
 
 // 192-column four-wave NT tiles when the 256-column tiles leave CUs idle in their only round
-// and the 192-column ones still fit it (3072 columns at 4096 rows: 192 -> 256 tiles)
+// and the 192-column ones still fit it (3072 columns at 4096 rows: 192 -> 256 tiles), or, over
+// several rounds, when the 192-column rounds weighted by their width (3/4) are fewer
+// (6144 columns at 4096 rows: two rounds of 256-column tiles, the second half empty, against
+// two full rounds of 192-column ones)
 static bool b192_fills(int M, int N) {
+  if (N % 192) return false;
   const long t256 = (long)((M + 255) / 256) * (N / 256), t192 = (long)((M + 255) / 256) * (N / 192);
-  return N % 192 == 0 && t256 < 256 && t192 <= 256 && t192 > t256;
+  if (t256 < 256 && t192 <= 256 && t192 > t256) return true;
+  return N % 256 == 0 && t256 > 256 && 3 * ((t192 + 255) / 256) < 4 * ((t256 + 255) / 256);
 }
 
 // 256x128 tiles instead of 256x256 when twice as many tiles still fit one round over the

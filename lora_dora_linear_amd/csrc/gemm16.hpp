@@ -51,8 +51,13 @@ __host__ __device__ constexpr int g16_nn_row(int k) { return k * kG16NNRow + (k 
 // LDS rows and 16-byte fragments), v_mfma_i32_16x16x64_i8 into exact int32 accumulators,
 // dequantised after the loop to acc . row_scale[m] . col_scale[n] in fp32; the low-rank term
 // is then one bf16 k-tile on those fp32 accumulators (LR = 0 in the loop).
-template <bool NN, int LR, bool DORA = false, bool SWB = false, int BN_ = 256, bool SWF = false, bool I8 = false>
+// LEAF (NT, LR = 1): several adapters over the concatenated output (p.nleaf leaves of rank
+// p.leaf_r): the k-tile's E slot of rank j holds the up row of output column n only where n's
+// leaf owns rank j, and the S side carries each leaf's own scale.
+template <bool NN, int LR, bool DORA = false, bool SWB = false, int BN_ = 256, bool SWF = false, bool I8 = false,
+          bool LEAF = false>
 __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
+  static_assert(!LEAF || (!NN && LR == 1 && !DORA && !I8), "leaves: the plain NT tile with one low-rank k-tile");
   static_assert(BN_ == 256 || (!NN && BN_ == 192), "tile widths: 256, or 192 for NT");
   static_assert(!SWB || (NN && !DORA), "the SwiGLU backward epilogue is an NN epilogue");
   static_assert(!SWF || (!NN && !DORA && !SWB && BN_ == 256 && LR != 1), "the dual tile is a plain 256-wide NT tile");
@@ -234,10 +239,10 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   if constexpr (LR == 1) {
     const int cps = p.r_epi >> 3;                     // chunks per part
     const int nparts = p.seed_hilo ? 2 : 1;
-    // several adapters (NT): this thread's output column n0 + t lies in leaf myleaf
+    // (LEAF) this thread's output column n0 + t lies in leaf myleaf
     const int nrow = (BN == 256 || tid < BN) ? n0 + tid : n0;
     int myleaf = 0;
-    if constexpr (!NN) {
+    if constexpr (LEAF) {
       for (int l = 0; l + 1 < p.nleaf; ++l) myleaf += nrow >= p.leaf_end[l] ? 1 : 0;
     }
     f32x4 sa[8], sb[8];
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
       if constexpr (NN) {       // rank row jl + t / 32, 16-byte chunk t % 32 of its 256 columns
         ev[c] = *reinterpret_cast<const u32x4*>(e0 + (size_t)(jl + (tid >> 5)) * p.e_ldj + n0 + 8 * (tid & 31));
       } else {                  // ranks jl .. jl + 7 of row n0 + t (t < BN); with leaves, of the leaf's row
-        const int je = p.nleaf ? jl % p.leaf_r : jl;
+        const int je = LEAF ? jl % p.leaf_r : jl;
         ev[c] = *reinterpret_cast<const u32x4*>(e0 + (size_t)nrow * p.e_ldn + je);
       }
     }
@@ -260,15 +265,19 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
     for (int c = 0; c < 8; ++c) {
       const int part = c / cps, j0 = 8 * (c - part * cps);
       const bool on = part < nparts;
-      const int lc = p.nleaf ? j0 / p.leaf_r : 0;      // leaf of these rank slots
-      const float sc = p.nleaf ? p.leaf_s[lc] : p.s_epi;
       const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-      lds_st16(smem1, g16_off(tid, c), on ? pack8(sa[c], sb[c], live ? sc : 0.f, part == 1) : z);
-      if constexpr (NN) {
-        const int j = 8 * c + (tid >> 5), ch = tid & 31;
-        lds_st16(smem1, BM * 128 + g16_nn_row(j) + ((ch ^ (2 * (j & 3))) << 4), on ? ev[c] : z);
-      } else if (BN == 256 || tid < BN) {
-        lds_st16(smem1, BM * 128 + g16_off(tid, c), (on && lc == myleaf) ? ev[c] : z);
+      if constexpr (LEAF) {
+        const int lc = j0 / p.leaf_r;                 // leaf of these rank slots
+        lds_st16(smem1, g16_off(tid, c), on ? pack8(sa[c], sb[c], live ? p.leaf_s[lc] : 0.f, part == 1) : z);
+        if (BN == 256 || tid < BN) lds_st16(smem1, BM * 128 + g16_off(tid, c), (on && lc == myleaf) ? ev[c] : z);
+      } else {
+        lds_st16(smem1, g16_off(tid, c), on ? pack8(sa[c], sb[c], live ? p.s_epi : 0.f, part == 1) : z);
+        if constexpr (NN) {
+          const int j = 8 * c + (tid >> 5), ch = tid & 31;
+          lds_st16(smem1, BM * 128 + g16_nn_row(j) + ((ch ^ (2 * (j & 3))) << 4), on ? ev[c] : z);
+        } else if (BN == 256 || tid < BN) {
+          lds_st16(smem1, BM * 128 + g16_off(tid, c), on ? ev[c] : z);
+        }
       }
     }
     __syncthreads();
