@@ -534,7 +534,8 @@ def main():
         if wl in ("w8a8", "fp8"):
             if wl == "w8a8":
                 names[0] = "forward base GEMM (int8 NT tile: gemm16_kernel, or gemm_kernel 256x128 at few tiles)"
-            names[1] = "input-gradient GEMM (gemm_kernel NN, 8-bit weight widened to bf16 in LDS)"
+            names[1] = ("input-gradient GEMM (gemm16_kernel NN on the weight dequantised to bf16 once per step)"
+                        if M >= 512 else "input-gradient GEMM (gemm_kernel NN, 8-bit weight widened to bf16 in LDS)")
         peak = PEAK_INT8 if (wl in ("w8a8", "fp8") and dom == 0) else PEAK_BF16
         traffic = recorded_traffic(f"{wl}:{names[dom]}")
         out["roofline"] = {"bound": "mfma", "kernel": names[dom], "achieved": round(kern[dom]["tflops"], 1),

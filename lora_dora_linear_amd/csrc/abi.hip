@@ -101,6 +101,11 @@ inline hipStream_t S(void* st) { return static_cast<hipStream_t>(st); }
   } while (0)
 
 // ------------------------------------------------------------------ workspace plans
+// From this many rows the 8-bit backward dequantises the weight into a bf16 copy once per call
+// and runs the plain four-wave input-gradient product on it (the copy pays for itself against
+// widening the codes inside the product at every k-tile of every row tile).
+constexpr int kDequantRows = 512;
+
 struct LoraBwdWs {
   float* V; float* U; float* partB; float* csB; float* partA;
   uint32_t* pkB; uint32_t* pkA;    // packed S of the two column projections
@@ -438,6 +443,7 @@ size_t ldl_workspace_bytes(int op, int M, int N, int K, int r, int dtype) {
     case LDL_OP_W8A8_BWD:
       if (dtype == LDL_F32 && op == LDL_OP_LORA_BWD) { b.take<float>((size_t)M * r); b.take<float>((size_t)M * r); }
       else plan_lora_bwd(b, M, N, K, r, true);
+      if (op == LDL_OP_W8A8_BWD && M >= kDequantRows) b.take<uint16_t>((size_t)N * K);   // the dequantised weight
       break;
     case LDL_OP_DORA_FWD:
       break;
@@ -1440,7 +1446,15 @@ static int lora8_bwd(int fp8, int M, int N, int K, int r, float s, const void* d
     p.S = w.V; p.ld_s = r; p.r_epi = r; p.s_epi = s;
     p.e0 = A; p.e1 = A; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = r;
     p.out = dX; p.ldo = lddx; p.q_fp8 = fp8;
-    LDL_TRY(gemm_timed(1, GK_NN_I8_SCALE, p, st));
+    if (M >= kDequantRows) {
+      // diag(sw).Wq in bf16 (the same rounding as the widening in the tile), then the plain product
+      uint16_t* Wd = wb.take<uint16_t>((size_t)N * K);
+      LDL_TRY(launch_dequant8(Wq, N, K, ldw, sw, fp8, Wd, st));
+      p.a_colscale = nullptr; p.b0 = Wd; p.b1 = Wd; p.ldb = K;
+      LDL_TRY(gemm_timed(1, GK_NN_PLAIN, p, st));
+    } else {
+      LDL_TRY(gemm_timed(1, GK_NN_I8_SCALE, p, st));
+    }
   }
   LDL_TRY(launch_colproj2(
       pk(cpp(M, N, r, dY, lddy, U, lu, 1.f, nullptr, 0, 0, w.msB, w.partB, nullptr), w.pkB), w.nsB,

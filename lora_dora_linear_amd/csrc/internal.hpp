@@ -105,6 +105,9 @@ hipError_t launch_dora_cols_db(int N, int r, float s, const void* B, const float
 hipError_t launch_mask_cols(const void* in, const uint8_t* keep, int rows, int K, int esz, void* out, hipStream_t st);
 
 // W8A8 helpers
+// bf16 [N, K] (dense) = codes [N, K] (row stride ldq) times the row scale; int8 or e4m3 codes
+hipError_t launch_dequant8(const void* q, int N, int K, int ldq, const float* scale, int fp8, void* out,
+                           hipStream_t st);
 // fp8: e4m3 codes (scale absmax / 448) instead of int8 (absmax / 127)
 hipError_t launch_quantize_rows(const void* X, int in_f32, int M, int K, int ldx, int8_t* q, float* scale,
                                 hipStream_t st, int fp8 = 0);

@@ -263,6 +263,50 @@ hipError_t launch_mask_cols(const void* in, const uint8_t* keep, int rows, int K
   return hipGetLastError();
 }
 
+// ============================================================================ 8-bit weight, dequantised
+// out[n, k] = bf16(value(q[n, k]) * scale[n]) for int8 or e4m3 codes: the value times the
+// scale rounded once to fp32, then to bf16 (the rounding the widening in the input-gradient
+// tile applies).  16 codes per thread and step; K a multiple of 16, 16-byte aligned rows.
+__global__ __launch_bounds__(256) void dequant8_kernel(const uint8_t* q, int N, int K, int ldq, const float* scale,
+                                                       int fp8, uint16_t* out) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const int per_row = K / 16;
+  const size_t total = (size_t)N * per_row;
+  for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (size_t)gridDim.x * blockDim.x) {
+    const int n = (int)(t / per_row), c = (int)(t % per_row) * 16;
+    const u32x4 v = ld16(q + (size_t)n * ldq + c);
+    const float sc = scale[n];
+    uint32_t o[8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      f2 lo, hi;
+      if (fp8) {
+        lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[w], false) * sc;
+        hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[w], true) * sc;
+      } else {
+        lo = f2{(float)(int8_t)(v[w] & 0xffu) * sc, (float)(int8_t)((v[w] >> 8) & 0xffu) * sc};
+        hi = f2{(float)(int8_t)((v[w] >> 16) & 0xffu) * sc, (float)(int8_t)(v[w] >> 24) * sc};
+      }
+      o[2 * w] = pack_bf16x2(lo[0], lo[1]);
+      o[2 * w + 1] = pack_bf16x2(hi[0], hi[1]);
+    }
+    uint16_t* dst = out + (size_t)n * K + c;
+    st16(dst, u32x4{o[0], o[1], o[2], o[3]});
+    st16(dst + 8, u32x4{o[4], o[5], o[6], o[7]});
+  }
+}
+
+hipError_t launch_dequant8(const void* q, int N, int K, int ldq, const float* scale, int fp8, void* out,
+                           hipStream_t st) {
+  const size_t total = (size_t)N * (K / 16);
+  if (total == 0) return hipSuccess;
+  size_t blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(dequant8_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const uint8_t*>(q), N, K,
+                     ldq, scale, fp8, static_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
 // ============================================================================ 8-bit quantisers
 // Symmetric per-row codes with the quotient x / scale in fp32; scale 0 -> code 0.  One wave
 // per row.  int8: scale = absmax / 127, code = clamp(rint(x / scale), +-127) (ties to even).
