@@ -186,7 +186,7 @@ DoraColsBwdWs plan_dora_cols_bwd(Bump& b, int M, int N, int K, int r) {
 
 struct DoraBwdWs {
   float* V; float* partT; float* cs; float* wB; float* partA; float* partQ; float* Qm;
-  uint16_t* dYg;                   // dY.diag(g) in bf16 [M, N]
+  uint16_t* gW0; uint16_t* gB;     // diag(g).W0 [N, K] and diag(g).B [N, r] in bf16 (weight-sized)
   float* partbias; float* csbias;
   uint32_t* pkT; uint32_t* pkA; uint32_t* pkW; uint32_t* pkQ;
   int nsT, msT, nsA, msA, nsW, msW, nsQ, msQ, rp;
@@ -207,7 +207,8 @@ DoraBwdWs plan_dora_bwd(Bump& b, int M, int N, int K, int r) {
   w.Qm = b.take<float>((size_t)r * r);
   w.partbias = b.take<float>((size_t)w.nsT * N * 16);
   w.csbias = b.take<float>((size_t)w.nsT * N);
-  w.dYg = b.take<uint16_t>((size_t)M * N);
+  w.gW0 = b.take<uint16_t>((size_t)N * K);
+  w.gB = b.take<uint16_t>((size_t)N * r);
   w.pkT = b.take<uint32_t>(colproj_spk_words(M, r));
   w.pkA = b.take<uint32_t>(colproj_spk_words(M, r));
   w.pkW = b.take<uint32_t>(colproj_spk_words(N, r));
@@ -947,21 +948,18 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, c
   ColProjParams jobs[3];
   int ns[3], nj = 0;
   if (M > 0) {
+    // dZ = dY.diag(g) is never formed: the row scale goes into bf16 copies of the weight and of
+    // lora_up (rounded once, weight-sized), V = dY.(diag(g).B) and dX = dY.(diag(g).W0) + s.V.A
+    LDL_TRY(launch_scale_rows(W0, N, dX ? K : 0, ldw, B, r, g, w.gW0, w.gB, st));
+    LDL_TRY(rowproj_t(M, N, r, dY, lddy, w.gB, r, nullptr, w.V, r, 1.f, st));
     if (dX) {
-      // dY.diag(g) rounded to bf16 once; V = (dY.diag(g)).B and dX = (dY.diag(g)).W0 + s.V.A
-      // are then plain products of it (B read in place as a [N, r] matrix)
-      LDL_TRY(launch_scale_cols(dY, M, N, lddy, g, w.dYg, N, st));
-      LDL_TRY(rowproj_t(M, N, r, w.dYg, N, Bh, r, nullptr, w.V, r, 1.f, st));
       GemmParams p = gp0();
       p.M = M; p.N = K; p.K = N;
-      p.a = w.dYg; p.lda = N; p.b0 = W0; p.b1 = W0; p.ldb = ldw; p.kseg = N;
+      p.a = dY; p.lda = lddy; p.b0 = w.gW0; p.b1 = w.gW0; p.ldb = K; p.kseg = N;
       p.S = w.V; p.ld_s = r; p.r_epi = r; p.s_epi = s;
       p.e0 = A; p.e1 = A; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = r;
       p.out = dX; p.ldo = lddx;
       LDL_TRY(gemm_timed(1, GK_NN_PLAIN, p, st));
-    } else {
-      // V = (dY.diag(g)).B with g applied to B's rows on load (no scaled copy of dY)
-      LDL_TRY(rowproj_t(M, N, r, dY, lddy, Bh, r, g, w.V, r, 1.f, st));
     }
     // s.V^T.X into the first nsA partials of dA
     jobs[nj] = pk(cpp(M, K, r, X, ldx, w.V, r, s, nullptr, 0, 0, w.msA, w.partA, nullptr), w.pkA);

@@ -77,6 +77,9 @@ hipError_t launch_fill_zero(float* p, size_t n, hipStream_t st);
 hipError_t launch_rowsumsq(const void* W0, int dtype_bf16, int N, int K, int ldw, float* out, hipStream_t st);
 hipError_t launch_dora_norm(int N, int r, float s, float eps, const float* w0_sumsq, const float* P,
                             const float* G, const uint16_t* B, const float* m, float* norm, float* g, hipStream_t st);
+// out = diag(g).W0 [N, K] and out2 = diag(g).B [N, r] (bf16, dense), one launch
+hipError_t launch_scale_rows(const void* in, int N, int K, int ld, const void* in2, int r, const float* g, void* out,
+                             void* out2, hipStream_t st);
 hipError_t launch_scale_cols(const void* in, int M, int N, int ld, const float* g, void* out, int ldo,
                              hipStream_t st);
 

@@ -168,6 +168,38 @@ __global__ __launch_bounds__(256) void scale_cols_kernel(const uint16_t* in, int
   }
 }
 
+// Two row-scaled copies in one launch: out[n, :] = bf16(in[n, :] * g[n]) for in = W0 [N, K]
+// (row stride ld) and in2 = B [N, r] (dense), each into a dense bf16 array; 8 columns per
+// thread, 16-byte aligned rows.
+__global__ __launch_bounds__(256) void scale_rows_kernel(const uint16_t* in, int N, int K, int ld, const uint16_t* in2,
+                                                         int r, const float* g, uint16_t* out, uint16_t* out2) {
+  const int pr1 = K / 8, pr2 = r / 8;
+  const size_t t1 = (size_t)N * pr1, total = t1 + (size_t)N * pr2;
+  for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (size_t)gridDim.x * blockDim.x) {
+    const bool first = t < t1;
+    const size_t u = first ? t : t - t1;
+    const int per = first ? pr1 : pr2;
+    const int n = (int)(u / per), c = (int)(u % per) * 8;
+    const float gn = g[n];
+    const f32x4 s4 = f32x4{gn, gn, gn, gn};
+    const uint16_t* src = first ? in + (size_t)n * ld + c : in2 + (size_t)n * r + c;
+    uint16_t* dst = first ? out + (size_t)n * K + c : out2 + (size_t)n * r + c;
+    st16(dst, scale_bf16x8(ld16(src), s4, s4));
+  }
+}
+
+hipError_t launch_scale_rows(const void* in, int N, int K, int ld, const void* in2, int r, const float* g, void* out,
+                             void* out2, hipStream_t st) {
+  const size_t total = (size_t)N * (K / 8 + r / 8);
+  if (total == 0) return hipSuccess;
+  size_t blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(scale_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const uint16_t*>(in), N,
+                     K, ld, static_cast<const uint16_t*>(in2), r, g, static_cast<uint16_t*>(out),
+                     static_cast<uint16_t*>(out2));
+  return hipGetLastError();
+}
+
 hipError_t launch_scale_cols(const void* in, int M, int N, int ld, const float* g, void* out, int ldo,
                              hipStream_t st) {
   if (M <= 0) return hipSuccess;
