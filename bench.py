@@ -91,19 +91,35 @@ def copy_calibrate(mib):
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}))
 
 
-def _events(torch, n):
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    for e in evs:          # torch creates the underlying hipEvent on first record
-        e.record()
-    torch.cuda.synchronize()
-    return evs
+class TimingEvents:
+    """n HIP timing events created with hipEventDisableSystemFence: recording one then costs no
+    system-scope fence (cache write-back and invalidate), which with default events left ~5 us
+    gaps around every timed launch and slowed the step itself.  They are read only after a
+    device-wide synchronisation, so the missing host-visibility fence changes no result."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
 
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")    # the runtime torch has loaded
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(ev), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.arr[i] = ev
 
-def _ptrs(evs):
-    arr = (ctypes.c_void_p * len(evs))()
-    for i, e in enumerate(evs):
-        arr[i] = ctypes.c_void_p(e.cuda_event)
-    return arr
+    def record(self, i, stream):
+        if self.hip.hipEventRecord(self.arr[i], stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, stop, i):
+        """Milliseconds from this set's event i to stop's event i."""
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[i], stop.arr[i]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
 
 
 def cpu_model():
@@ -219,15 +235,14 @@ def merge(args, torch, np, binding, inputs, L, up, P, st, check):
     nb = binding.workspace_bytes("merge_bwd", 0, N, K, r)
     ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
     K_steps = args.steps
-    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(K_steps)]
-    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(K_steps)]
+    e0, e1 = TimingEvents(K_steps), TimingEvents(K_steps)
 
     def step(i=None):
         if i is not None:
-            e0[i].record()
+            e0.record(i, st())
         check(L.lora_merge_fwd(N, K, r, s, 1, P(W0), K, P(A), P(B), P(W), K, st()), "lora_merge_fwd")
         if i is not None:
-            e1[i].record()
+            e1.record(i, st())
         check(L.lora_merge_bwd(N, K, r, s, 1, P(dW), K, P(A), P(B), P(dA), P(dB), P(ws), nb, st()), "lora_merge_bwd")
 
     for _ in range(args.warmup):
@@ -240,7 +255,7 @@ def merge(args, torch, np, binding, inputs, L, up, P, st, check):
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / K_steps
-    fwd_us = 1e3 * sum(a.elapsed_time(b) for a, b in zip(e0, e1)) / K_steps
+    fwd_us = 1e3 * sum(e0.elapsed_ms(e1, i) for i in range(K_steps)) / K_steps
     fwd_bytes = 2.0 * N * K * 2 + (N + K) * r * 2          # read W0, write W, read the factors
     gbs = fwd_bytes / (fwd_us * 1e-6) / 1e9
     flops = 2.0 * N * K * r + 4.0 * N * K * r
@@ -488,12 +503,12 @@ def main():
     # (the per-kernel timing events are created first, so that nothing idles the GPU between
     # the warm-up and the timed steps)
     K_steps = args.steps
-    evs = {k: (_events(torch, K_steps), _events(torch, K_steps)) for k in gemm_kinds}
+    evs = {k: (TimingEvents(K_steps), TimingEvents(K_steps)) for k in gemm_kinds}
     for _ in range(args.warmup):
         step()
     keep = []
     for k in gemm_kinds:
-        a, b = _ptrs(evs[k][0]), _ptrs(evs[k][1])
+        a, b = evs[k][0].arr, evs[k][1].arr
         keep.append((a, b))
         check(L.ldl_set_kernel_events(k, a, b, K_steps), "ldl_set_kernel_events")
     t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -510,7 +525,7 @@ def main():
 
     kern = {}
     for k in gemm_kinds:
-        times = [a.elapsed_time(b) for a, b in zip(*evs[k])]
+        times = [evs[k][0].elapsed_ms(evs[k][1], i) for i in range(K_steps)]
         avg = sum(times) / len(times)
         kern[k] = {"avg_us": avg * 1e3, "tflops": gemm_flops[k] / (avg * 1e-3) / 1e12}
 
