@@ -297,8 +297,8 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype,
  * Pc = B^T.W0 [r,K] and Gc = B^T.B [r,r]; the adapted weight is never formed.
  */
 
-/* Once per frozen W0 [N,K] (row stride ldw, dtype LDL_F32 or LDL_BF16):
- * w0_colsq[k] = sum_n W0[n,k]^2 (fp32 [K]).  Recompute whenever W0 changes. */
+/* Once per frozen W0 [N,K] (row stride ldw, dtype LDL_F32 or LDL_BF16; bf16 needs K and ldw
+ * multiples of 8): w0_colsq[k] = sum_n W0[n,k]^2 (fp32 [K]).  Recompute whenever W0 changes. */
 int dora_cols_prepare(int N, int K, int dtype, const void* W0, int ldw, float* w0_colsq, void* stream);
 
 /*   nu_k = ||W'[:,k]||;  g_k = m_k / max(nu_k, eps);  Xs = X.diag(g);

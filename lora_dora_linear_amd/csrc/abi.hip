@@ -995,7 +995,8 @@ int dora_cols_prepare(int N, int K, int dtype, const void* W0, int ldw, float* w
   if (N <= 0 || K <= 0) return LDL_E_INVAL;
   if (dtype != LDL_F32 && dtype != LDL_BF16) return LDL_E_INVAL;
   if (!al({W0, w0_colsq})) return LDL_E_UNSUPPORTED;
-  LDL_LD(ldw, K, 1);
+  LDL_LD(ldw, K, dtype == LDL_BF16 ? 8 : 1);
+  if (dtype == LDL_BF16 && K % 8) return LDL_E_UNSUPPORTED;
   if (!fits(N, ldw, dtype == LDL_BF16 ? 2 : 4)) return LDL_E_UNSUPPORTED;
   LDL_TRY(launch_col_sumsq(W0, dtype == LDL_BF16, N, K, ldw, w0_colsq, S(stream)));
   return LDL_OK;
