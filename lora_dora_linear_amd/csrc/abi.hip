@@ -771,7 +771,6 @@ int lora_multi_linear_bwd(int M, int K, int nleaf, const int* n_leaf, int r, con
   }
   // dA_l = V_l^T.X for every leaf in one column projection of X; dB_l = s_l.dY_l^T.U_l per leaf
   LDL_TRY(colproj(M, K, R, X, ldx, w.V, R, 1.f, nullptr, 0, 0, w.nsA, w.msA, w.partA, nullptr, st, w.pkA));
-  LDL_TRY(reduce(R, K, w.partA, (size_t)K * w.rpR, w.nsA, w.rpR, true, 1.f, dA, K, st));
   for (int l0 = 0; l0 < nleaf; l0 += kColProjBatch) {
     ColProjParams jobs[kColProjBatch];
     int ns[kColProjBatch], nj = 0;
@@ -782,11 +781,19 @@ int lora_multi_linear_bwd(int M, int K, int nleaf, const int* n_leaf, int r, con
     }
     LDL_TRY(launch_colproj_batch(jobs, ns, nj, st));
   }
-  for (int l = 0; l < nleaf; ++l) {
-    LDL_TRY(reduce(n_leaf[l], r, w.part[l], (size_t)n_leaf[l] * w.rp, w.ns[l], w.rp, false, s_leaf[l],
-                   dB + (size_t)off[l] * r, r, st));
-    if (dbias) LDL_TRY(launch_reduce_colsum(w.cs[l], w.ns[l], n_leaf[l], dbias + off[l], st));
+  // the fixed-order reductions two per launch: dA with the first leaf's dB, then the other leaves
+  // in pairs
+  auto dbjob = [&](int l) {
+    return rdp(n_leaf[l], r, w.part[l], (size_t)n_leaf[l] * w.rp, w.ns[l], w.rp, false, s_leaf[l],
+               dB + (size_t)off[l] * r, r);
+  };
+  LDL_TRY(launch_reduce2(rdp(R, K, w.partA, (size_t)K * w.rpR, w.nsA, w.rpR, true, 1.f, dA, K), dbjob(0), st));
+  for (int l = 1; l < nleaf; l += 2) {
+    if (l + 1 < nleaf) LDL_TRY(launch_reduce2(dbjob(l), dbjob(l + 1), st));
+    else LDL_TRY(launch_reduce(dbjob(l), st));
   }
+  if (dbias)
+    for (int l = 0; l < nleaf; ++l) LDL_TRY(launch_reduce_colsum(w.cs[l], w.ns[l], n_leaf[l], dbias + off[l], st));
   return LDL_OK;
 }
 
