@@ -55,7 +55,7 @@ __host__ __device__ constexpr int g16_nn_row(int k) { return k * kG16NNRow + (k 
 // p.leaf_r): the k-tile's E slot of rank j holds the up row of output column n only where n's
 // leaf owns rank j, and the S side carries each leaf's own scale.
 template <bool NN, int LR, bool DORA = false, bool SWB = false, int BN_ = 256, bool SWF = false, bool I8 = false,
-          bool LEAF = false>
+          bool LEAF = false, int ACT = ACT_SILU>
 __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   static_assert(!LEAF || (!NN && LR == 1 && !DORA && !I8), "leaves: the plain NT tile with one low-rank k-tile");
   static_assert(BN_ == 256 || (!NN && BN_ == 192), "tile widths: 256, or 192 for NT");
@@ -610,8 +610,8 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
           const f32x4 e = *reinterpret_cast<const f32x4*>(smem0 + xoff(2 * wm, i, j));
           const f32x4 u = *reinterpret_cast<const f32x4*>(smem0 + xoff(2 * wm + 1, i, j));
           u32x2 w;
-          w[0] = pack_bf16x2(glu_act(e[0], p.act) * u[0], glu_act(e[1], p.act) * u[1]);
-          w[1] = pack_bf16x2(glu_act(e[2], p.act) * u[2], glu_act(e[3], p.act) * u[3]);
+          w[0] = pack_bf16x2(glu_act(e[0], ACT) * u[0], glu_act(e[1], ACT) * u[1]);
+          w[1] = pack_bf16x2(glu_act(e[2], ACT) * u[2], glu_act(e[3], ACT) * u[3]);
           *reinterpret_cast<u32x2*>(h_ptr(r, j * 16 + 4 * lq)) = w;
         }
       }

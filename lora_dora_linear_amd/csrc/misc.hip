@@ -214,9 +214,11 @@ hipError_t launch_scale_cols(const void* in, int M, int N, int ld, const float* 
 // Gated-MLP backward from the stored bf16 dh, e and u (8 columns per thread):
 // de = dh u act'(e) overwrites dh in place, du = dh act(e) (SiLU: act' = sigma (1 + e (1 - sigma))).
 // Each thread reads its own dh chunk before writing de there.
+template <int ACT>
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(uint16_t* dE, int ld_de, const uint16_t* E, int ld_e,
                                                          const uint16_t* U, int ld_u, uint16_t* dU, int ld_du, int M,
-                                                         int N, int act) {
+                                                         int N) {
+  constexpr int act = ACT;
   const unsigned per_row = (unsigned)N / 8u;
   const size_t total = (size_t)M * per_row;
   for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (size_t)gridDim.x * blockDim.x) {
@@ -242,9 +244,11 @@ hipError_t launch_swiglu_bwd(void* dE, int ld_de, const void* E, int ld_e, const
   const size_t total = (size_t)M * (N / 8);
   size_t blocks = (total + 255) / 256;
   if (blocks > 8192) blocks = 8192;   // ~7 grid-stride steps a thread at 8192 x 14336 (2048 blocks: 222 -> 213 us)
-  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<uint16_t*>(dE), ld_de,
+  auto k = act == ACT_GELU ? swiglu_bwd_kernel<ACT_GELU>
+                            : (act == ACT_GELU_TANH ? swiglu_bwd_kernel<ACT_GELU_TANH> : swiglu_bwd_kernel<ACT_SILU>);
+  hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<uint16_t*>(dE), ld_de,
                      static_cast<const uint16_t*>(E), ld_e, static_cast<const uint16_t*>(U), ld_u,
-                     static_cast<uint16_t*>(dU), ld_du, M, N, act);
+                     static_cast<uint16_t*>(dU), ld_du, M, N);
   return hipGetLastError();
 }
 
