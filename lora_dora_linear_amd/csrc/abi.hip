@@ -431,7 +431,10 @@ size_t dora_state_floats(int N, int r) {
   return (size_t)2 * N + (size_t)N * r + (size_t)r * r;
 }
 
-size_t ldl_workspace_bytes(int op, int M, int N, int K, int r, int dtype) {
+}  // extern "C"
+
+// The workspace an op needs (without the split-reduction partials below)
+static size_t ws_base(int op, int M, int N, int K, int r, int dtype) {
   if (M < 0 || N <= 0 || K <= 0 || r <= 0) return 0;
   Bump b(nullptr);
   switch (op) {
@@ -471,6 +474,35 @@ size_t ldl_workspace_bytes(int op, int M, int N, int K, int r, int dtype) {
   return b.size();
 }
 
+// Optional fp32 partials of the split reduction of the op's plain four-wave product (the
+// tiles past its last full round; 0 when the shape has none): [M, N] forward outputs, [M, K]
+// input gradients.  Calls given less workspace than base + this run without the split.
+static size_t ws_split(int op, int M, int N, int K, int dtype) {
+  if (dtype == LDL_F32) return 0;
+  switch (op) {
+    case LDL_OP_LORA_FWD:
+    case LDL_OP_W8A8_FWD: return gemm_split_bytes(M, N);
+    case LDL_OP_LORA_BWD: return gemm_split_bytes(M, K);
+    case LDL_OP_W8A8_BWD: return M >= kDequantRows ? gemm_split_bytes(M, K) : 0;
+    default: return 0;
+  }
+}
+
+// The split partials carved from the rest of the workspace, or nullptr if they do not fit.
+static float* split_part(Bump& wb, void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0 || ws == nullptr) return nullptr;
+  if (wb.size() + need > ws_bytes) return nullptr;
+  return wb.take<float>(need / sizeof(float));
+}
+
+extern "C" {
+
+size_t ldl_workspace_bytes(int op, int M, int N, int K, int r, int dtype) {
+  const size_t base = ws_base(op, M, N, K, r, dtype);
+  const size_t extra = (M < 0 || N <= 0 || K <= 0 || r <= 0) ? 0 : ws_split(op, M, N, K, dtype);
+  return extra ? (base + kAlign - 1) / kAlign * kAlign + extra : base;
+}
+
 // =========================================================================== LoRA
 int lora_linear_fwd(int M, int N, int K, int r, float s, int dtype, const void* X, int ldx, const void* W0, int ldw,
                     const void* A, const void* B, const void* bias, void* Y, int ldy, float* U_save, int ldu,
@@ -483,7 +515,7 @@ int lora_linear_fwd(int M, int N, int K, int r, float s, int dtype, const void* 
   if (!al({X, W0, A, B, bias, Y, U_save, ws})) return LDL_E_UNSUPPORTED;
   const size_t e = dtype == LDL_BF16 ? 2 : 4;
   if (!fits(M, ldx, e) || !fits(N, ldw, e) || !fits(M, ldy, e) || !fits(M, ldu, 4)) return LDL_E_UNSUPPORTED;
-  if (ldl_workspace_bytes(LDL_OP_LORA_FWD, M, N, K, r, dtype) > ws_bytes && !U_save) return LDL_E_WORKSPACE;
+  if (ws_base(LDL_OP_LORA_FWD, M, N, K, r, dtype) > ws_bytes && !U_save) return LDL_E_WORKSPACE;
   if (ws_bytes > 0 && !ws) return LDL_E_INVAL;
   const hipStream_t st = S(stream);
   Bump wb(ws);
@@ -506,6 +538,7 @@ int lora_linear_fwd(int M, int N, int K, int r, float s, int dtype, const void* 
   p.a = X; p.lda = ldx; p.b0 = W0; p.ldb = ldw; p.kseg = K;
   p.r_epi = r; p.s_epi = s; p.e0 = B; p.e1 = B; p.e_ldn = r; p.e_ldj = 1; p.e_jsplit = r;
   p.bias = bias; p.out = Y; p.ldo = ldy;
+  p.part = split_part(wb, ws, ws_bytes, ws_split(LDL_OP_LORA_FWD, M, N, K, dtype));
   if (g_fwd_fused && r <= 64 && N % 128 == 0) {
     p.side = A; p.r_side = r; p.side_save = U_save; p.ld_side_save = ldu;
     LDL_TRY(gemm_timed(0, GK_NT_FUSED, p, st));
@@ -533,7 +566,7 @@ int lora_linear_bwd(int M, int N, int K, int r, float s, int dtype, const void* 
     const int chk = check_bf16_layer(M, N, K, r);
     if (chk != LDL_OK) return chk;
   }
-  if (ldl_workspace_bytes(LDL_OP_LORA_BWD, M, N, K, r, dtype) > ws_bytes) return LDL_E_WORKSPACE;
+  if (ws_base(LDL_OP_LORA_BWD, M, N, K, r, dtype) > ws_bytes) return LDL_E_WORKSPACE;
   if (!ws) return LDL_E_INVAL;
   const hipStream_t st = S(stream);
   if (M == 0) {
@@ -585,6 +618,7 @@ int lora_linear_bwd(int M, int N, int K, int r, float s, int dtype, const void* 
     p.S = w.V; p.ld_s = r; p.r_epi = r; p.s_epi = s;
     p.e0 = A; p.e1 = A; p.e_ldn = 1; p.e_ldj = K; p.e_jsplit = r;
     p.out = dX; p.ldo = lddx;
+    p.part = split_part(wb, ws, ws_bytes, ws_split(LDL_OP_LORA_BWD, M, N, K, dtype));
     LDL_TRY(gemm_timed(1, GK_NN_PLAIN, p, st));
   }
   // dB = s.dY^T.U (+ dbias = column sums of dY in the same pass) and dA = s.V^T.X: one launch each
@@ -601,7 +635,7 @@ int lora_linear_bwd(int M, int N, int K, int r, float s, int dtype, const void* 
 int lora_linear_bwd_noalloc(int M, int N, int K, int r, float s, int dtype, const void* dY, int lddy, const void* X,
                             int ldx, const void* W0, int ldw, const void* A, const void* B, const float* U_saved,
                             int ldu, void* dX, int lddx, float* dA, float* dB, float* dbias, void* stream) {
-  if (ldl_workspace_bytes(LDL_OP_LORA_BWD, M, N, K, r, dtype) > kScratchBytes) return LDL_E_WORKSPACE;
+  if (ws_base(LDL_OP_LORA_BWD, M, N, K, r, dtype) > kScratchBytes) return LDL_E_WORKSPACE;
   void* ws = scratch_for_current_device();
   if (!ws) return LDL_E_HIP;
   return lora_linear_bwd(M, N, K, r, s, dtype, dY, lddy, X, ldx, W0, ldw, A, B, U_saved, ldu, dX, lddx, dA, dB, dbias,
@@ -1376,7 +1410,7 @@ static int lora8_fwd(int fp8, int M, int N, int K, int r, float s, const void* X
   LDL_LD(ldx, K, 8); LDL_LD(ldw, K, 16); LDL_LD(ldy, N, 8); LDL_LD(ldu, r, 4);
   if (!fits(M, ldx, 2) || !fits(N, ldw, 1) || !fits(M, ldy, 2) || !fits(M, ldu, 4)) return LDL_E_UNSUPPORTED;
   if (!al({X, Wq, sw, A, B, bias, Y, Xq_save, sx_save, U_save, ws})) return LDL_E_UNSUPPORTED;
-  if (ldl_workspace_bytes(LDL_OP_W8A8_FWD, M, N, K, r, LDL_BF16) > ws_bytes) return LDL_E_WORKSPACE;
+  if (ws_base(LDL_OP_W8A8_FWD, M, N, K, r, LDL_BF16) > ws_bytes) return LDL_E_WORKSPACE;
   if (!ws) return LDL_E_INVAL;
   if (M == 0) return LDL_OK;
   const hipStream_t st = S(stream);
@@ -1397,6 +1431,7 @@ static int lora8_fwd(int fp8, int M, int N, int K, int r, float s, const void* X
   p.S = U; p.ld_s = lu; p.r_epi = r; p.s_epi = s;
   p.e0 = B; p.e1 = B; p.e_ldn = r; p.e_ldj = 1; p.e_jsplit = r;
   p.bias = bias; p.out = Y; p.ldo = ldy;
+  if (!fp8) p.part = split_part(wb, ws, ws_bytes, ws_split(LDL_OP_W8A8_FWD, M, N, K, LDL_BF16));
   LDL_TRY(gemm_timed(0, fp8 ? GK_NT_F8_DEQ : GK_NT_I8_DEQ, p, st));
   return LDL_OK;
 }
@@ -1428,7 +1463,7 @@ static int lora8_bwd(int fp8, int M, int N, int K, int r, float s, const void* d
   if (!fits(M, lddy, 2) || !fits(M, ldx, 2) || !fits(N, ldw, 1) || !fits(M, ldu, 4) || !fits(M, lddx, 2))
     return LDL_E_UNSUPPORTED;
   if (!al({dY, X, Wq, sw, A, B, U_saved, dX, dA, dB, ws})) return LDL_E_UNSUPPORTED;
-  if (ldl_workspace_bytes(LDL_OP_W8A8_BWD, M, N, K, r, LDL_BF16) > ws_bytes) return LDL_E_WORKSPACE;
+  if (ws_base(LDL_OP_W8A8_BWD, M, N, K, r, LDL_BF16) > ws_bytes) return LDL_E_WORKSPACE;
   const hipStream_t st = S(stream);
   if (M == 0) {
     LDL_TRY(zero(dA, (size_t)r * K, st));
@@ -1457,6 +1492,7 @@ static int lora8_bwd(int fp8, int M, int N, int K, int r, float s, const void* d
       uint16_t* Wd = wb.take<uint16_t>((size_t)N * K);
       LDL_TRY(launch_dequant8(Wq, N, K, ldw, sw, fp8, Wd, st));
       p.a_colscale = nullptr; p.b0 = Wd; p.b1 = Wd; p.ldb = K;
+      p.part = split_part(wb, ws, ws_bytes, ws_split(LDL_OP_W8A8_BWD, M, N, K, LDL_BF16));
       LDL_TRY(gemm_timed(1, GK_NN_PLAIN, p, st));
     } else {
       LDL_TRY(gemm_timed(1, GK_NN_I8_SCALE, p, st));

@@ -58,16 +58,97 @@ static bool a16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) ==
 // (NN: Q in one segment).
 // The low-rank term takes one k-tile of 64 rank slots; where 2 r fit in it, s.S enters as a
 // bf16 pair hi + lo (its rounding error then ~2^-17 relative instead of ~2^-9) at no extra cost.
+// Split reduction of the tiles past the last full round of the 256 CUs (plain 256-wide
+// four-wave tiles, when the caller gave a partial buffer): the R remaining tiles are each
+// computed by S = min(4, 256 / R) blocks over a quarter (third, half) of the k-tiles, so the
+// last round is full, and the fixup pass sums the S fp32 partials in order (+ bias, bf16).
+// (5120 x 5120 outputs at 4096 tokens: 320 tiles = one full round + 64 tiles.)
+static void plan_split(GemmParams& p, int tiles, int kt) {
+  p.split_s = 0;
+  p.split_first = 0;
+  if (p.part == nullptr) return;
+  const int full = tiles / 256 * 256, R = tiles - full;
+  if (R == 0) return;
+  const int S = std::min(4, std::min(256 / R, kt));
+  if (S < 2) return;
+  p.split_s = S;
+  p.split_first = full;
+}
+
+// blockIdx.x = 64 t + c: remaining tile split_first + t, f32x4 slots 256 c .. 256 c + 255 of
+// the lane-linear partial layout (slot ((wave 8 + i) 8 + j) 64 + lane: the four columns
+// 4 (lane >> 4) .. +3 of accumulator block (i, j) of wave (wm, wn) = (wave >> 1, wave & 1))
+__global__ __launch_bounds__(256) void split_fixup_kernel(const GemmParams p) {
+  const int t = blockIdx.x >> 6, slot = (blockIdx.x & 63) * 256 + threadIdx.x;
+  const int tiles_m = (p.M + 255) / 256, tiles_n = p.N / 256;
+  const int bid = p.split_first + t;
+  constexpr int GM = 4;
+  const int group = bid / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gm = min(GM, tiles_m - first_m);
+  const int in_g = bid - group * GM * tiles_n;
+  const int m0 = (first_m + in_g % gm) * 256, n0 = (in_g / gm) * 256;
+  const int lane = slot & 63, j = (slot >> 6) & 7, i = (slot >> 9) & 7, wave = slot >> 12;
+  const int row = (wave >> 1) * 128 + 16 * i + (lane & 15), col = (wave & 1) * 128 + 16 * j + 4 * (lane >> 4);
+  if (m0 + row >= p.M) return;
+  const float* src = p.part + (size_t)t * p.split_s * 65536 + (size_t)slot * 4;
+  f32x4 v = *reinterpret_cast<const f32x4*>(src);
+  for (int q = 1; q < p.split_s; ++q) v += *reinterpret_cast<const f32x4*>(src + (size_t)q * 65536);
+  float b4[4] = {0.f, 0.f, 0.f, 0.f};
+  if (p.bias != nullptr) {
+    const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n0 + col);
+    b4[0] = bf16_lo(bb[0]); b4[1] = bf16_hi(bb[0]); b4[2] = bf16_lo(bb[1]); b4[3] = bf16_hi(bb[1]);
+  }
+  u32x2 w;
+  w[0] = pack_bf16x2(v[0] + b4[0], v[1] + b4[1]);
+  w[1] = pack_bf16x2(v[2] + b4[2], v[3] + b4[3]);
+  *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (size_t)(m0 + row) * p.ldo + n0 + col) = w;
+}
+
+static hipError_t launch_split_fixup(const GemmParams& p, int tiles, hipStream_t st) {
+  const int R = tiles - p.split_first;
+  hipLaunchKernelGGL(split_fixup_kernel, dim3(R * 64), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+size_t gemm_split_bytes(int M, int N) {
+  if (M <= 128 || N % 256) return 0;
+  const int tiles = ((M + 255) / 256) * (N / 256), R = tiles % 256;
+  if (R == 0) return 0;
+  const int S = std::min(4, 256 / R);
+  return S < 2 ? 0 : (size_t)R * S * 65536 * sizeof(float);
+}
+
 template <bool NN, bool DORA = false, bool SWB = false, int BN = 256>
 static hipError_t run16(const GemmParams& p0, hipStream_t st) {
   GemmParams p = p0;
   p.seed_hilo = (p.r_epi > 0 && 2 * p.r_epi <= 64) ? 1 : 0;
+  p.split_s = 0;
   const int tiles = ((p.M + 255) / 256) * (p.N / BN);
   if constexpr (!NN && !DORA && !SWB) {
     if (p.nleaf > 0) {
       hipLaunchKernelGGL((gemm16_kernel<false, 1, false, false, BN, false, false, true>), dim3(tiles), dim3(256), 0, st,
                          p);
       return hipGetLastError();
+    }
+  }
+  if constexpr (!DORA && !SWB && BN == 256) {
+    plan_split(p, tiles, p.K / 64);
+    if (p.split_s > 1) {            // the full rounds, then the split blocks, then the fixup
+      const int nsplit = (tiles - p.split_first) * p.split_s;
+      if (p.split_first > 0) {
+        if (p.r_epi > 0) hipLaunchKernelGGL((gemm16_kernel<NN, 1, false, false, 256>), dim3(p.split_first), dim3(256), 0, st, p);
+        else hipLaunchKernelGGL((gemm16_kernel<NN, 0, false, false, 256>), dim3(p.split_first), dim3(256), 0, st, p);
+      }
+      if (p.r_epi > 0)
+        hipLaunchKernelGGL((gemm16_kernel<NN, 1, false, false, 256, false, false, false, ACT_SILU, true>), dim3(nsplit),
+                           dim3(256), 0, st, p);
+      else
+        hipLaunchKernelGGL((gemm16_kernel<NN, 0, false, false, 256, false, false, false, ACT_SILU, true>), dim3(nsplit),
+                           dim3(256), 0, st, p);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_split_fixup(p, tiles, st);
     }
   }
   if (p.r_epi > 0) hipLaunchKernelGGL((gemm16_kernel<NN, 1, DORA, SWB, BN>), dim3(tiles), dim3(256), 0, st, p);
@@ -95,6 +176,17 @@ static hipError_t run16_i8(const GemmParams& p0, hipStream_t st) {
   GemmParams p = p0;
   p.seed_hilo = (p.r_epi > 0 && 2 * p.r_epi <= 64) ? 1 : 0;
   const int tiles = ((p.M + 255) / 256) * (p.N / 256);
+  plan_split(p, tiles, p.K / 128);
+  if (p.split_s > 1) {              // the full rounds, then the split blocks, then the fixup
+    if (p.split_first > 0)
+      hipLaunchKernelGGL((gemm16_kernel<false, 0, false, false, 256, false, true>), dim3(p.split_first), dim3(256), 0,
+                         st, p);
+    hipLaunchKernelGGL((gemm16_kernel<false, 0, false, false, 256, false, true, false, ACT_SILU, true>),
+                       dim3((tiles - p.split_first) * p.split_s), dim3(256), 0, st, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_split_fixup(p, tiles, st);
+  }
   hipLaunchKernelGGL((gemm16_kernel<false, 0, false, false, 256, false, true>), dim3(tiles), dim3(256), 0, st, p);
   return hipGetLastError();
 }
@@ -205,7 +297,8 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
   // (measured at 5120 x 5120, r = 32: 2048 tokens 88 -> 72 us, 4096 182 -> 145, 8192 303 -> 245,
   // 16384 523 -> 415 us against the eight-wave tile; at 1024 tokens the eight-wave 256 x 128
   // tiles, twice as many in the one round, stay faster: 67 against 71 us)
-  if (kind == GK_NT_I8_DEQ && g_gemm_4wave && big && bn == 256 && (g_gemm_4wave == 2 || !half_tiles_pay(p.M, p.N)) &&
+  if (kind == GK_NT_I8_DEQ && g_gemm_4wave && big && bn == 256 &&
+      (g_gemm_4wave == 2 || p.part != nullptr || !half_tiles_pay(p.M, p.N)) &&
       p.side == nullptr &&
       p.r_epi <= 64 && seed && p.K % 128 == 0 && a16(p.col_scale))
     return run16_i8(p, st);

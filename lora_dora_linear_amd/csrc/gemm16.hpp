@@ -55,8 +55,9 @@ __host__ __device__ constexpr int g16_nn_row(int k) { return k * kG16NNRow + (k 
 // p.leaf_r): the k-tile's E slot of rank j holds the up row of output column n only where n's
 // leaf owns rank j, and the S side carries each leaf's own scale.
 template <bool NN, int LR, bool DORA = false, bool SWB = false, int BN_ = 256, bool SWF = false, bool I8 = false,
-          bool LEAF = false, int ACT = ACT_SILU>
+          bool LEAF = false, int ACT = ACT_SILU, bool SPLITK = false>
 __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
+  static_assert(!SPLITK || (!DORA && !SWB && !SWF && !LEAF && BN_ == 256), "split reduction: the plain 256-wide tiles");
   static_assert(!LEAF || (!NN && LR == 1 && !DORA && !I8), "leaves: the plain NT tile with one low-rank k-tile");
   static_assert(BN_ == 256 || (!NN && BN_ == 192), "tile widths: 256, or 192 for NT");
   static_assert(!SWB || (NN && !DORA), "the SwiGLU backward epilogue is an NN epilogue");
@@ -72,12 +73,27 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem0[SB];
   __shared__ __attribute__((aligned(16))) uint8_t smem1[SB];
 
-  const int M = p.M, N = p.N, K = p.K;
+  const int M = p.M, N = p.N;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = N / TNO;
-  // XCD-contiguous tile ranges, walked in groups of 4 row-tiles (as gemm_kernel)
+  // XCD-contiguous tile ranges, walked in groups of 4 row-tiles (as gemm_kernel).
+  // SPLITK (the split reduction of the tiles past the last full round of the chip, a launch
+  // of its own after the full rounds): block t S + q computes k-tiles [q KT / S, (q + 1) KT / S)
+  // of tile split_first + t (S = split_s) into an fp32 partial that the fixup pass sums; the
+  // operands are addressed from the first k-tile of the range on, and only q = 0 carries the
+  // low-rank term.
   int bid = blockIdx.x;
-  const int nblk = gridDim.x;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  [[maybe_unused]] int split = 0, kb = 0;
+  int KTl = p.K / KB;
+  if constexpr (SPLITK) {
+    split = bid % p.split_s;
+    bid = p.split_first + bid / p.split_s;
+    kb = split * KTl / p.split_s;
+    KTl = (split + 1) * KTl / p.split_s - kb;
+  } else {
+    const int nblk = gridDim.x;
+    if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  }
+  const int K = KTl * KB;                           // this block's reduction length
   constexpr int GM = 4;
   const int group = bid / (GM * tiles_n);
   const int first_m = group * GM;
@@ -91,8 +107,14 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   const int l16 = lane & 15, lq = lane >> 4;
   const uint32_t lda_b = (uint32_t)p.lda * (I8 ? 1u : 2u), ldb_b = (uint32_t)p.ldb * (I8 ? 1u : 2u);
 
-  const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(p.a, (uint32_t)M * lda_b);
-  const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(p.b0, (uint32_t)(NN ? K : N) * ldb_b);
+  // (SPLITK: P and the NT Q from k-tile kb on, 128 bytes a row per k-tile; the NN Q from its
+  // row kb KB on; the bounds shrink by the same offset)
+  const uint32_t koff_a = SPLITK ? (uint32_t)kb * 128u : 0u;
+  const uint32_t koff_b = SPLITK ? (NN ? (uint32_t)kb * KB * ldb_b : (uint32_t)kb * 128u) : 0u;
+  const __amdgpu_buffer_rsrc_t rs_a =
+      make_rsrc(static_cast<const uint8_t*>(p.a) + koff_a, (uint32_t)M * lda_b - koff_a);
+  const __amdgpu_buffer_rsrc_t rs_b =
+      make_rsrc(static_cast<const uint8_t*>(p.b0) + koff_b, (uint32_t)(NN ? p.K : N) * ldb_b - koff_b);
   const __amdgpu_buffer_rsrc_t rs_b1 = SWF ? make_rsrc(p.b1, (uint32_t)N * ldb_b) : rs_b;   // dual: up rows
   const __amdgpu_buffer_rsrc_t rs_none = make_rsrc(p.a, 0u);    // copies that read nothing
 
@@ -220,7 +242,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   // The caller guarantees 16-byte aligned S rows and E rows (or rank rows), ranks that are
   // multiples of 8, and (LR = 1) a single E segment (e_jsplit >= r_epi).
   const uint16_t* e0 = static_cast<const uint16_t*>(p.e0);
-  const bool live = m0 + tid < M;
+  const bool live = m0 + tid < M && split == 0;     // (SPLITK blocks past the first: no low-rank term)
   const float* srow = p.S + (size_t)min(m0 + tid, M - 1) * p.ld_s;
   auto pack8 = [](f32x4 a, f32x4 b, float sc, bool lo) {
     const float x[8] = {a[0] * sc, a[1] * sc, a[2] * sc, a[3] * sc, b[0] * sc, b[1] * sc, b[2] * sc, b[3] * sc};
@@ -382,6 +404,25 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the last (empty) copies
   __syncthreads();
 
+  // SPLITK: the block's fp32 partial, lane-linear: slot ((wave 8 + i) FN + j) 64 + lane
+  // holds acc[i][j]
+  auto write_partial = [&]() {
+    float* dst = p.part + ((size_t)(bid - p.split_first) * p.split_s + split) * (size_t)(BM * BN);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+      {
+        f32x4 v = __builtin_bit_cast(f32x4, acc[i][j]);
+        asm volatile("" : "+v"(v));                 // (out of the accumulators first)
+        *reinterpret_cast<f32x4*>(dst + ((size_t)((wave * 8 + i) * FN + j) * 64 + lane) * 4) = v;
+      }
+  };
+  if constexpr (SPLITK && !I8) {
+    write_partial();
+    return;
+  }
+
   // staging rows of SROW bytes; 16-byte chunk c of row rr at c ^ (rr & SWZM) (256 columns: all
   // 32 chunks; 192: within each group of 8, so it stays inside the 24 chunks of the row)
   constexpr int SROW = BN * 2, SWZM = BN == 256 ? 31 : 7, NCH = BN / 8;
@@ -471,6 +512,10 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
             acc[i][j] = __builtin_bit_cast(i32x4, mfma_bf16(fb[j], fa[i], __builtin_bit_cast(f32x4, acc[i][j])));
       }
       __syncthreads();
+    }
+    if constexpr (SPLITK) {         // dequantised partial (the low-rank term with the first split)
+      write_partial();
+      return;
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {

@@ -62,6 +62,11 @@ struct GemmParams {
   const void* aux1; int ld_aux1;
   float* side_save; int ld_side_save;
   int q_fp8;                         // NN with 8-bit Q: the codes are e4m3 (else int8)
+  // split reduction of the tiles past the last full round (four-wave plain tiles; set by the
+  // launcher when part is given): split_s blocks per tile from tile split_first on, fp32
+  // partials in part (split_s x 256 x 256 floats per tile), summed by the fixup pass
+  int split_s, split_first;
+  float* part;
   int seed_hilo;                     // four-wave tile: low-rank term as bf16 hi + lo (set by the launcher)
   int act;                           // gated MLP activation: ACT_SILU, ACT_GELU, ACT_GELU_TANH
   // several adapters over one concatenated output (four-wave NT seed only): output column n

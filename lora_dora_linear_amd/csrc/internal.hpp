@@ -54,6 +54,9 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st);
 extern int g_gemm_4wave;   // plain bf16 GEMMs on the four-wave 16x16x32 tile (tuning switch)
 bool gemm_shape_ok(GemmKind kind, int M, int N, int K);
 bool gemm_multi_leaf_ok(const GemmParams& p);
+// fp32 partial bytes the split reduction of a plain 256-wide four-wave product of [M, N]
+// outputs uses (0: no split for this shape); passed as GemmParams::part
+size_t gemm_split_bytes(int M, int N);
 
 hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st);
 int colproj_rp(int R);
