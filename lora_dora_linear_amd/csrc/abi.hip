@@ -1431,7 +1431,7 @@ static int lora8_fwd(int fp8, int M, int N, int K, int r, float s, const void* X
   p.S = U; p.ld_s = lu; p.r_epi = r; p.s_epi = s;
   p.e0 = B; p.e1 = B; p.e_ldn = r; p.e_ldj = 1; p.e_jsplit = r;
   p.bias = bias; p.out = Y; p.ldo = ldy;
-  if (!fp8) p.part = split_part(wb, ws, ws_bytes, ws_split(LDL_OP_W8A8_FWD, M, N, K, LDL_BF16));
+  p.part = split_part(wb, ws, ws_bytes, ws_split(LDL_OP_W8A8_FWD, M, N, K, LDL_BF16));
   LDL_TRY(gemm_timed(0, fp8 ? GK_NT_F8_DEQ : GK_NT_I8_DEQ, p, st));
   return LDL_OK;
 }

@@ -76,8 +76,11 @@ static void plan_split(GemmParams& p, int tiles, int kt) {
 }
 
 // blockIdx.x = 64 t + c: remaining tile split_first + t, f32x4 slots 256 c .. 256 c + 255 of
-// the lane-linear partial layout (slot ((wave 8 + i) 8 + j) 64 + lane: the four columns
-// 4 (lane >> 4) .. +3 of accumulator block (i, j) of wave (wm, wn) = (wave >> 1, wave & 1))
+// the lane-linear partial layout of wave (wm, wn) = (wave >> 1, wave & 1).  16x16 blocks
+// (L32 = 0): slot ((wave 8 + i) 8 + j) 64 + lane holds row 16 i + (lane & 15), the four columns
+// 16 j + 4 (lane >> 4) ..  32x32 blocks (L32 = 1): slot (((wave 4 + i) 4 + j) 4 + q) 64 + lane
+// holds row 32 i + (lane & 31), columns 32 j + 8 q + 4 (lane >> 5) ..
+template <bool L32>
 __global__ __launch_bounds__(256) void split_fixup_kernel(const GemmParams p) {
   const int t = blockIdx.x >> 6, slot = (blockIdx.x & 63) * 256 + threadIdx.x;
   const int tiles_m = (p.M + 255) / 256, tiles_n = p.N / 256;
@@ -88,8 +91,17 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(const GemmParams p) {
   const int gm = min(GM, tiles_m - first_m);
   const int in_g = bid - group * GM * tiles_n;
   const int m0 = (first_m + in_g % gm) * 256, n0 = (in_g / gm) * 256;
-  const int lane = slot & 63, j = (slot >> 6) & 7, i = (slot >> 9) & 7, wave = slot >> 12;
-  const int row = (wave >> 1) * 128 + 16 * i + (lane & 15), col = (wave & 1) * 128 + 16 * j + 4 * (lane >> 4);
+  const int lane = slot & 63, wave = slot >> 12;
+  int row = (wave >> 1) * 128, col = (wave & 1) * 128;
+  if constexpr (L32) {
+    const int q = (slot >> 6) & 3, j = (slot >> 8) & 3, i = (slot >> 10) & 3;
+    row += 32 * i + (lane & 31);
+    col += 32 * j + 8 * q + 4 * (lane >> 5);
+  } else {
+    const int j = (slot >> 6) & 7, i = (slot >> 9) & 7;
+    row += 16 * i + (lane & 15);
+    col += 16 * j + 4 * (lane >> 4);
+  }
   if (m0 + row >= p.M) return;
   const float* src = p.part + (size_t)t * p.split_s * 65536 + (size_t)slot * 4;
   f32x4 v = *reinterpret_cast<const f32x4*>(src);
@@ -105,9 +117,10 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(const GemmParams p) {
   *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (size_t)(m0 + row) * p.ldo + n0 + col) = w;
 }
 
-static hipError_t launch_split_fixup(const GemmParams& p, int tiles, hipStream_t st) {
+static hipError_t launch_split_fixup(const GemmParams& p, int tiles, hipStream_t st, bool l32 = false) {
   const int R = tiles - p.split_first;
-  hipLaunchKernelGGL(split_fixup_kernel, dim3(R * 64), dim3(256), 0, st, p);
+  if (l32) hipLaunchKernelGGL(split_fixup_kernel<true>, dim3(R * 64), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL(split_fixup_kernel<false>, dim3(R * 64), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -270,6 +283,18 @@ static hipError_t run_f8(const GemmParams& p0, hipStream_t st) {
     return hipErrorInvalidValue;
   p.seed_hilo = (p.r_epi > 0 && 2 * p.r_epi <= 64) ? 1 : 0;
   const int tm = (p.M + 255) / 256;
+  p.split_s = 0;
+  if (p.N % 256 == 0 && p.part != nullptr) {
+    const int tiles = tm * (p.N / 256);
+    plan_split(p, tiles, p.K / 128);
+    if (p.split_s > 1) {            // the full rounds, then the split blocks, then the fixup
+      if (p.split_first > 0) hipLaunchKernelGGL(gemm_f8_kernel<256>, dim3(p.split_first), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((gemm_f8_kernel<256, true>), dim3((tiles - p.split_first) * p.split_s), dim3(256), 0, st, p);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_split_fixup(p, tiles, st, true);
+    }
+  }
   if (p.N % 256 == 0 && !half_tiles_pay(p.M, p.N))
     hipLaunchKernelGGL(gemm_f8_kernel<256>, dim3(tm * (p.N / 256)), dim3(256), 0, st, p);
   else

@@ -32,20 +32,35 @@ __device__ __forceinline__ f32x16 mfma_bf16_32(u32x4 a, u32x4 b, f32x16 c) {
 // 32 x 32 blocks: lane l of an operand holds row l & 31 and 32 bytes of the step's 64; the
 // result lane l, value v holds D[8 (v >> 2) + 4 (l >> 5) + (v & 3)][l & 31] with D's rows
 // from the first operand (here Q: output columns) and its columns from the second (P rows).
-template <int BN>
+// SPLITK (256-wide tiles): the split reduction of the tiles past the last full round, as in
+// the bf16 tile: block t S + q takes k-tiles [q KT / S, (q + 1) KT / S) of tile split_first + t
+// and writes its dequantised fp32 partial (the low-rank term with q = 0 only) for the fixup
+// pass; slot (((wave 4 + i) 4 + j) 4 + q') 64 + lane holds acc[i][j][4 q' .. 4 q' + 3].
+template <int BN, bool SPLITK = false>
 __global__ __launch_bounds__(256, 1) void gemm_f8_kernel(const GemmParams p) {
   static_assert(BN == 256 || BN == 128, "tile widths 256 and 128");
+  static_assert(!SPLITK || BN == 256, "split reduction: 256-wide tiles");
   constexpr int BM = 256, NW = 4, FI = 4, FJ = BN / 64;
   constexpr int SB = BM * 128 + BN * 128;
   constexpr int NCB = BN / 32;                      // Q copies per wave and stage
   __shared__ __attribute__((aligned(16))) uint8_t smem0[SB];
   __shared__ __attribute__((aligned(16))) uint8_t smem1[SB];
 
-  const int M = p.M, N = p.N, K = p.K;
+  const int M = p.M, N = p.N;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
   int bid = blockIdx.x;
-  const int nblk = gridDim.x;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  [[maybe_unused]] int split = 0, kb = 0;
+  int KTl = p.K / 128;
+  if constexpr (SPLITK) {
+    split = bid % p.split_s;
+    bid = p.split_first + bid / p.split_s;
+    kb = split * KTl / p.split_s;
+    KTl = (split + 1) * KTl / p.split_s - kb;
+  } else {
+    const int nblk = gridDim.x;
+    if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  }
+  const int K = KTl * 128;                          // this block's reduction length
   constexpr int GM = 4;
   const int group = bid / (GM * tiles_n);
   const int first_m = group * GM;
@@ -57,8 +72,9 @@ __global__ __launch_bounds__(256, 1) void gemm_f8_kernel(const GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const uint32_t lda_b = (uint32_t)p.lda, ldb_b = (uint32_t)p.ldb;
-  const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(p.a, (uint32_t)M * lda_b);
-  const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(p.b0, (uint32_t)N * ldb_b);
+  const uint32_t koff = SPLITK ? (uint32_t)kb * 128u : 0u;   // (both operands from k-tile kb on)
+  const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(static_cast<const uint8_t*>(p.a) + koff, (uint32_t)M * lda_b - koff);
+  const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(static_cast<const uint8_t*>(p.b0) + koff, (uint32_t)N * ldb_b - koff);
   const __amdgpu_buffer_rsrc_t rs_none = make_rsrc(p.a, 0u);
 
   // copies: 1 KB (8 rows) per instruction; copy i of a wave covers rows 32 i + 8 wave ..
@@ -189,7 +205,7 @@ __global__ __launch_bounds__(256, 1) void gemm_f8_kernel(const GemmParams p) {
   }
   // the low-rank term s.S.E^T as one bf16 k-tile in smem0 (P rows: s.S of row m0 + t as
   // bf16 hi + lo where 2 r <= 64, else hi; Q rows: E row n0 + t), four 16-k steps
-  if (p.r_epi > 0) {
+  if (p.r_epi > 0 && split == 0) {
     const uint16_t* e0 = static_cast<const uint16_t*>(p.e0);
     const bool live = m0 + tid < M;
     const float* srow = p.S + (size_t)min(m0 + tid, M - 1) * p.ld_s;
@@ -236,6 +252,20 @@ __global__ __launch_bounds__(256, 1) void gemm_f8_kernel(const GemmParams p) {
         for (int j = 0; j < FJ; ++j) acc[i][j] = mfma_bf16_32(fb[j], fa[i], acc[i][j]);
     }
     __syncthreads();
+  }
+  if constexpr (SPLITK) {
+    float* dst = p.part + ((size_t)(bid - p.split_first) * p.split_s + split) * (size_t)(BM * BN);
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+      for (int j = 0; j < FJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4 v = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          asm volatile("" : "+v"(v));               // (out of the accumulators first)
+          *reinterpret_cast<f32x4*>(dst + ((size_t)(((wave * FI + i) * FJ + j) * 4 + q) * 64 + lane) * 4) = v;
+        }
+    return;
   }
   // bias, bf16, staged through LDS (rows < 128 in smem0, the rest in smem1), written out as
   // whole 16-byte row segments
