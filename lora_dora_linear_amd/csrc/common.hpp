@@ -35,15 +35,26 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// Round to nearest even (inputs here are finite; NaN is kept quiet).
+// fp32 -> bf16, round to nearest even, on the conversion unit (v_cvt_pk_bf16_f32: two
+// values per instruction, where the integer form of the rounding took ~12); NaN stays NaN.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+// The same rounding in integer arithmetic (finite inputs; NaN becomes the quiet NaN 0x7fc0),
+// for kernels whose register allocation the conversion instruction upsets.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits_int(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
 }
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+__device__ __forceinline__ uint32_t pack_bf16x2_int(float lo, float hi) {
+  return f32_to_bf16_bits_int(lo) | (f32_to_bf16_bits_int(hi) << 16);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }

@@ -428,44 +428,60 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   constexpr int SROW = BN * 2, SWZM = BN == 256 ? 31 : 7, NCH = BN / 8;
   static_assert(128 * SROW <= SB, "half of the output tile fits in a stage buffer");
   // ---- epilogue: bias, bf16, staged through LDS (rows < 128 in smem0, the rest in smem1),
-  // written out as whole 16-byte row segments.  DORA writes z first, then y = z g + bias
-  // (both from the fp32 accumulators).
+  // written out as whole 16-byte row segments (full 128-byte lines per store instruction;
+  // 8-byte stores straight from the accumulator layout touch 16 lines each and were slower).
+  // DORA writes z first, then y = z g + bias (both from the fp32 accumulators).
   auto st_ptr = [&](int r, int col) -> uint8_t* {
     uint8_t* base = r < 128 ? smem0 : smem1;
     const int rr = r & 127;
     return base + rr * SROW + ((((col >> 3) ^ (rr & SWZM))) << 4) + ((col & 4) << 1);
   };
+  // the staged bf16 tile to dst as 16-byte row segments, eight LDS reads in flight before
+  // their stores (one read, wait and store per segment had been bound by the LDS latency:
+  // ~6800 cycles per tile)
+  auto write_staged = [&](void* dst, int ldo) __attribute__((always_inline)) {
+    uint16_t* out = static_cast<uint16_t*>(dst);
+    constexpr int NIT = BM * NCH / 256;
+    static_assert(NIT % 8 == 0, "row segments per thread in groups of eight");
+#pragma unroll
+    for (int b = 0; b < NIT; b += 8) {
+      u32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = tid + (b + u) * 256, r = idx / NCH, c = idx % NCH, rr = r & 127;
+        v[u] = lds_ld16(r < 128 ? smem0 : smem1, rr * SROW + ((c ^ (rr & SWZM)) << 4));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = tid + (b + u) * 256, r = idx / NCH, c = idx % NCH;
+        if (m0 + r < M) st16(out + (size_t)(m0 + r) * ldo + n0 + c * 8, v[u]);
+      }
+    }
+  };
+  // (column blocks outermost: the bias and column scale of the lane's four columns are read
+  // once per column block, not once per accumulator block)
   auto emit = [&](auto z_c, void* dst, int ldo) {
     constexpr bool Z = decltype(z_c)::value;       // DORA's unscaled output
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = wm * 128 + i * 16 + l16;
+    for (int j = 0; j < FN; ++j) {
+      const int cl = wn * (BN / 2) + j * 16 + 4 * lq;
+      u32x2 bb = u32x2{0u, 0u};
+      if (!Z && p.bias != nullptr) bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n0 + cl);
+      f32x4 cs = f32x4{1.f, 1.f, 1.f, 1.f};
+      if constexpr (DORA && !Z) cs = *reinterpret_cast<const f32x4*>(p.col_scale + n0 + cl);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int cl = wn * (BN / 2) + j * 16 + 4 * lq;
-        float b4[4] = {0.f, 0.f, 0.f, 0.f};
-        if (!Z && p.bias != nullptr) {
-          const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n0 + cl);
-          b4[0] = bf16_lo(bb[0]); b4[1] = bf16_hi(bb[0]); b4[2] = bf16_lo(bb[1]); b4[3] = bf16_hi(bb[1]);
-        }
+      for (int i = 0; i < 8; ++i) {
+        const int r = wm * 128 + i * 16 + l16;
         auto v = acc[i][j];         // (fp32 in every kernel that calls this)
-        if constexpr (DORA && !Z) v *= *reinterpret_cast<const f32x4*>(p.col_scale + n0 + cl);
+        if constexpr (DORA && !Z) v *= cs;
         u32x2 w;
-        w[0] = pack_bf16x2(v[0] + b4[0], v[1] + b4[1]);
-        w[1] = pack_bf16x2(v[2] + b4[2], v[3] + b4[3]);
+        w[0] = pack_bf16x2(v[0] + bf16_lo(bb[0]), v[1] + bf16_hi(bb[0]));
+        w[1] = pack_bf16x2(v[2] + bf16_lo(bb[1]), v[3] + bf16_hi(bb[1]));
         *reinterpret_cast<u32x2*>(st_ptr(r, cl)) = w;
       }
     }
     __syncthreads();
-    uint16_t* out = static_cast<uint16_t*>(dst);
-    for (int idx = tid; idx < BM * NCH; idx += 256) {
-      const int r = idx / NCH, c = idx % NCH;
-      if (m0 + r < M) {
-        const uint8_t* base = r < 128 ? smem0 : smem1;
-        const int rr = r & 127;
-        st16(out + (size_t)(m0 + r) * ldo + n0 + c * 8, lds_ld16(base, rr * SROW + ((c ^ (rr & SWZM)) << 4)));
-      }
-    }
+    write_staged(dst, ldo);
   };
   if constexpr (I8) {
     // dequantise the exact int32 products in place: acc . sx[m] . sw[n] in fp32 (the fp32 bits
@@ -518,33 +534,22 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
       return;
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = wm * 128 + i * 16 + l16;
+    for (int j = 0; j < FN; ++j) {
+      const int cl = wn * (BN / 2) + j * 16 + 4 * lq;
+      u32x2 bb = u32x2{0u, 0u};
+      if (p.bias != nullptr) bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n0 + cl);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int cl = wn * (BN / 2) + j * 16 + 4 * lq;
-        float b4[4] = {0.f, 0.f, 0.f, 0.f};
-        if (p.bias != nullptr) {
-          const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n0 + cl);
-          b4[0] = bf16_lo(bb[0]); b4[1] = bf16_hi(bb[0]); b4[2] = bf16_lo(bb[1]); b4[3] = bf16_hi(bb[1]);
-        }
+      for (int i = 0; i < 8; ++i) {
+        const int r = wm * 128 + i * 16 + l16;
         const f32x4 v = __builtin_bit_cast(f32x4, acc[i][j]);
         u32x2 w;
-        w[0] = pack_bf16x2(v[0] + b4[0], v[1] + b4[1]);
-        w[1] = pack_bf16x2(v[2] + b4[2], v[3] + b4[3]);
+        w[0] = pack_bf16x2(v[0] + bf16_lo(bb[0]), v[1] + bf16_hi(bb[0]));
+        w[1] = pack_bf16x2(v[2] + bf16_lo(bb[1]), v[3] + bf16_hi(bb[1]));
         *reinterpret_cast<u32x2*>(st_ptr(r, cl)) = w;
       }
     }
     __syncthreads();
-    uint16_t* out = static_cast<uint16_t*>(p.out);
-    for (int idx = tid; idx < BM * NCH; idx += 256) {
-      const int r = idx / NCH, c = idx % NCH;
-      if (m0 + r < M) {
-        const uint8_t* base = r < 128 ? smem0 : smem1;
-        const int rr = r & 127;
-        st16(out + (size_t)(m0 + r) * p.ldo + n0 + c * 8, lds_ld16(base, rr * SROW + ((c ^ (rr & SWZM)) << 4)));
-      }
-    }
+    write_staged(p.out, p.ldo);
   } else if constexpr (DORA) {
     emit(std::true_type{}, p.out2, p.ldo2);
     __syncthreads();                               // the staging buffers are free again
@@ -607,8 +612,8 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
       for (int j = 0; j < 8; ++j) {
         const f32x4 v = acc[i][j];
         u32x2 w;
-        w[0] = pack_bf16x2(v[0], v[1]);
-        w[1] = pack_bf16x2(v[2], v[3]);
+        w[0] = pack_bf16x2_int(v[0], v[1]);
+        w[1] = pack_bf16x2_int(v[2], v[3]);
         *reinterpret_cast<u32x2*>(st_ptr(r, wn * 128 + j * 16 + 4 * lq)) = w;
       }
     }
@@ -655,8 +660,8 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
           const f32x4 e = *reinterpret_cast<const f32x4*>(smem0 + xoff(2 * wm, i, j));
           const f32x4 u = *reinterpret_cast<const f32x4*>(smem0 + xoff(2 * wm + 1, i, j));
           u32x2 w;
-          w[0] = pack_bf16x2(glu_act(e[0], ACT) * u[0], glu_act(e[1], ACT) * u[1]);
-          w[1] = pack_bf16x2(glu_act(e[2], ACT) * u[2], glu_act(e[3], ACT) * u[3]);
+          w[0] = pack_bf16x2_int(glu_act(e[0], ACT) * u[0], glu_act(e[1], ACT) * u[1]);
+          w[1] = pack_bf16x2_int(glu_act(e[2], ACT) * u[2], glu_act(e[3], ACT) * u[3]);
           *reinterpret_cast<u32x2*>(h_ptr(r, j * 16 + 4 * lq)) = w;
         }
       }
@@ -672,33 +677,22 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
     // (written out rather than through emit: the lambda changed the register allocation of
     // the NN k-loop and cost ~10 % there)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = wm * 128 + i * 16 + l16;
+    for (int j = 0; j < FN; ++j) {
+      const int cl = wn * (BN / 2) + j * 16 + 4 * lq;
+      u32x2 bb = u32x2{0u, 0u};
+      if (p.bias != nullptr) bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n0 + cl);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int cl = wn * (BN / 2) + j * 16 + 4 * lq;
-        float b4[4] = {0.f, 0.f, 0.f, 0.f};
-        if (p.bias != nullptr) {
-          const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n0 + cl);
-          b4[0] = bf16_lo(bb[0]); b4[1] = bf16_hi(bb[0]); b4[2] = bf16_lo(bb[1]); b4[3] = bf16_hi(bb[1]);
-        }
+      for (int i = 0; i < 8; ++i) {
+        const int r = wm * 128 + i * 16 + l16;
         const f32x4 v = acc[i][j];
         u32x2 w;
-        w[0] = pack_bf16x2(v[0] + b4[0], v[1] + b4[1]);
-        w[1] = pack_bf16x2(v[2] + b4[2], v[3] + b4[3]);
+        w[0] = pack_bf16x2(v[0] + bf16_lo(bb[0]), v[1] + bf16_hi(bb[0]));
+        w[1] = pack_bf16x2(v[2] + bf16_lo(bb[1]), v[3] + bf16_hi(bb[1]));
         *reinterpret_cast<u32x2*>(st_ptr(r, cl)) = w;
       }
     }
     __syncthreads();
-    uint16_t* out = static_cast<uint16_t*>(p.out);
-    for (int idx = tid; idx < BM * NCH; idx += 256) {
-      const int r = idx / NCH, c = idx % NCH;
-      if (m0 + r < M) {
-        const uint8_t* base = r < 128 ? smem0 : smem1;
-        const int rr = r & 127;
-        st16(out + (size_t)(m0 + r) * p.ldo + n0 + c * 8, lds_ld16(base, rr * SROW + ((c ^ (rr & SWZM)) << 4)));
-      }
-    }
+    write_staged(p.out, p.ldo);
   }
 }
 

@@ -276,33 +276,40 @@ __global__ __launch_bounds__(256, 1) void gemm_f8_kernel(const GemmParams p) {
     const int rr = r & 127;
     return base + rr * SROW + ((((col >> 3) ^ (rr & SWZM))) << 4) + ((col & 4) << 1);
   };
+  // (column groups outermost: the bias of the lane's four columns is read once per group)
 #pragma unroll
-  for (int i = 0; i < FI; ++i) {
-    const int r = wm * 128 + 32 * i + r32;
+  for (int j = 0; j < FJ; ++j)
 #pragma unroll
-    for (int j = 0; j < FJ; ++j)
+    for (int q = 0; q < 4; ++q) {
+      const int cl = wn * (BN / 2) + 32 * j + 8 * q + 4 * hh;
+      u32x2 bb = u32x2{0u, 0u};
+      if (p.bias != nullptr) bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n0 + cl);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int cl = wn * (BN / 2) + 32 * j + 8 * q + 4 * hh;
-        float b4[4] = {0.f, 0.f, 0.f, 0.f};
-        if (p.bias != nullptr) {
-          const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n0 + cl);
-          b4[0] = bf16_lo(bb[0]); b4[1] = bf16_hi(bb[0]); b4[2] = bf16_lo(bb[1]); b4[3] = bf16_hi(bb[1]);
-        }
+      for (int i = 0; i < FI; ++i) {
+        const int r = wm * 128 + 32 * i + r32;
         u32x2 w;
-        w[0] = pack_bf16x2(acc[i][j][4 * q] + b4[0], acc[i][j][4 * q + 1] + b4[1]);
-        w[1] = pack_bf16x2(acc[i][j][4 * q + 2] + b4[2], acc[i][j][4 * q + 3] + b4[3]);
+        w[0] = pack_bf16x2(acc[i][j][4 * q] + bf16_lo(bb[0]), acc[i][j][4 * q + 1] + bf16_hi(bb[0]));
+        w[1] = pack_bf16x2(acc[i][j][4 * q + 2] + bf16_lo(bb[1]), acc[i][j][4 * q + 3] + bf16_hi(bb[1]));
         *reinterpret_cast<u32x2*>(st_ptr(r, cl)) = w;
       }
-  }
+    }
   __syncthreads();
+  // (eight LDS reads in flight before their stores)
   uint16_t* out = static_cast<uint16_t*>(p.out);
-  for (int idx = tid; idx < BM * NCH; idx += 256) {
-    const int r = idx / NCH, c = idx % NCH;
-    if (m0 + r < M) {
-      const uint8_t* base = r < 128 ? smem0 : smem1;
-      const int rr = r & 127;
-      st16(out + (size_t)(m0 + r) * p.ldo + n0 + c * 8, lds_ld16(base, rr * SROW + ((c ^ (rr & SWZM)) << 4)));
+  constexpr int NIT = BM * NCH / 256;
+  static_assert(NIT % 8 == 0, "row segments per thread in groups of eight");
+#pragma unroll
+  for (int b = 0; b < NIT; b += 8) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = tid + (b + u) * 256, r = idx / NCH, c = idx % NCH, rr = r & 127;
+      v[u] = lds_ld16(r < 128 ? smem0 : smem1, rr * SROW + ((c ^ (rr & SWZM)) << 4));
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = tid + (b + u) * 256, r = idx / NCH, c = idx % NCH;
+      if (m0 + r < M) st16(out + (size_t)(m0 + r) * p.ldo + n0 + c * 8, v[u]);
     }
   }
 }
