@@ -460,26 +460,39 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   };
   // (column blocks outermost: the bias and column scale of the lane's four columns are read
   // once per column block, not once per accumulator block)
-  auto emit = [&](auto z_c, void* dst, int ldo) {
+  // Staging of the bf16 tile (bias, DORA's column scale).  256 columns: the lane's LDS address
+  // is a lane constant plus compile-time parts: row 16 i + l16 of its half (wm), 16-byte chunk
+  // (col >> 3) ^ (row & 31) = y ^ ((i & 1) << 4) ^ (j << 1) with y = l16 ^ (lq >> 1) ^ (wn << 4)
+  // (col = 128 wn + 16 j + 4 lq), byte 8 (lq & 1) in it.  (A separate path without the bias
+  // additions made the allocator move the k-loop's accumulators.)
+  auto stage_out = [&](auto z_c) __attribute__((always_inline)) {
     constexpr bool Z = decltype(z_c)::value;       // DORA's unscaled output
+    constexpr bool CS = DORA && !Z;
+    [[maybe_unused]] uint8_t* const sb = (wm ? smem1 : smem0) + l16 * SROW + (lq & 1) * 8;
+    [[maybe_unused]] const int y = l16 ^ (lq >> 1) ^ (wn << 4);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int cl = wn * (BN / 2) + j * 16 + 4 * lq;
       u32x2 bb = u32x2{0u, 0u};
       if (!Z && p.bias != nullptr) bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n0 + cl);
       f32x4 cs = f32x4{1.f, 1.f, 1.f, 1.f};
-      if constexpr (DORA && !Z) cs = *reinterpret_cast<const f32x4*>(p.col_scale + n0 + cl);
+      if constexpr (CS) cs = *reinterpret_cast<const f32x4*>(p.col_scale + n0 + cl);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int r = wm * 128 + i * 16 + l16;
-        auto v = acc[i][j];         // (fp32 in every kernel that calls this)
-        if constexpr (DORA && !Z) v *= cs;
+        auto v = __builtin_bit_cast(f32x4, acc[i][j]);   // (fp32 in every kernel that calls this)
+        if constexpr (CS) v *= cs;
         u32x2 w;
         w[0] = pack_bf16x2(v[0] + bf16_lo(bb[0]), v[1] + bf16_hi(bb[0]));
         w[1] = pack_bf16x2(v[2] + bf16_lo(bb[1]), v[3] + bf16_hi(bb[1]));
-        *reinterpret_cast<u32x2*>(st_ptr(r, cl)) = w;
+        if constexpr (BN == 256)
+          *reinterpret_cast<u32x2*>(sb + ((y ^ ((i & 1) << 4) ^ (j << 1)) << 4) + i * 16 * SROW) = w;
+        else
+          *reinterpret_cast<u32x2*>(st_ptr(wm * 128 + i * 16 + l16, cl)) = w;
       }
     }
+  };
+  auto emit = [&](auto z_c, void* dst, int ldo) {
+    stage_out(z_c);
     __syncthreads();
     write_staged(dst, ldo);
   };
@@ -533,21 +546,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
       write_partial();
       return;
     }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int cl = wn * (BN / 2) + j * 16 + 4 * lq;
-      u32x2 bb = u32x2{0u, 0u};
-      if (p.bias != nullptr) bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n0 + cl);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = wm * 128 + i * 16 + l16;
-        const f32x4 v = __builtin_bit_cast(f32x4, acc[i][j]);
-        u32x2 w;
-        w[0] = pack_bf16x2(v[0] + bf16_lo(bb[0]), v[1] + bf16_hi(bb[0]));
-        w[1] = pack_bf16x2(v[2] + bf16_lo(bb[1]), v[3] + bf16_hi(bb[1]));
-        *reinterpret_cast<u32x2*>(st_ptr(r, cl)) = w;
-      }
-    }
+    stage_out(std::false_type{});
     __syncthreads();
     write_staged(p.out, p.ldo);
   } else if constexpr (DORA) {
@@ -674,23 +673,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
              lds_ld16(smem1, r * 256 + ((c ^ (r & 15)) << 4)));
     }
   } else {
-    // (written out rather than through emit: the lambda changed the register allocation of
-    // the NN k-loop and cost ~10 % there)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int cl = wn * (BN / 2) + j * 16 + 4 * lq;
-      u32x2 bb = u32x2{0u, 0u};
-      if (p.bias != nullptr) bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n0 + cl);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = wm * 128 + i * 16 + l16;
-        const f32x4 v = acc[i][j];
-        u32x2 w;
-        w[0] = pack_bf16x2(v[0] + bf16_lo(bb[0]), v[1] + bf16_hi(bb[0]));
-        w[1] = pack_bf16x2(v[2] + bf16_lo(bb[1]), v[3] + bf16_hi(bb[1]));
-        *reinterpret_cast<u32x2*>(st_ptr(r, cl)) = w;
-      }
-    }
+    stage_out(std::false_type{});
     __syncthreads();
     write_staged(p.out, p.ldo);
   }
