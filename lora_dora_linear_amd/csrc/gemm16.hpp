@@ -269,36 +269,67 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
     }
     f32x4 sa[8], sb[8];
     u32x4 ev[8];
+    if constexpr (!LEAF && !NN) {
+      // only the cps chunks that hold ranks are read (the lo part reuses the hi part's S and E):
+      // the loads of every clamped chunk had cost ~3000 cycles of memory-pipeline issue at the
+      // start, when every CU issues them at once
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int part = c / cps, j0 = 8 * (c - part * cps);
-      const int jl = part < nparts ? j0 : 0;           // clamped rank offset
-      sa[c] = *reinterpret_cast<const f32x4*>(srow + jl);
-      sb[c] = *reinterpret_cast<const f32x4*>(srow + jl + 4);
-      if constexpr (NN) {       // rank row jl + t / 32, 16-byte chunk t % 32 of its 256 columns
-        ev[c] = *reinterpret_cast<const u32x4*>(e0 + (size_t)(jl + (tid >> 5)) * p.e_ldj + n0 + 8 * (tid & 31));
-      } else {                  // ranks jl .. jl + 7 of row n0 + t (t < BN); with leaves, of the leaf's row
-        const int je = LEAF ? jl % p.leaf_r : jl;
-        ev[c] = *reinterpret_cast<const u32x4*>(e0 + (size_t)nrow * p.e_ldn + je);
-      }
-    }
-    copy_stage(0, smem0);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int part = c / cps, j0 = 8 * (c - part * cps);
-      const bool on = part < nparts;
+      for (int q = 0; q < 8; ++q)
+        if (q < cps) {
+          sa[q] = *reinterpret_cast<const f32x4*>(srow + 8 * q);
+          sb[q] = *reinterpret_cast<const f32x4*>(srow + 8 * q + 4);
+          ev[q] = *reinterpret_cast<const u32x4*>(e0 + (size_t)nrow * p.e_ldn + 8 * q);   // ranks 8q.. of row n0 + t
+        }
+      copy_stage(0, smem0);
       const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-      if constexpr (LEAF) {
-        const int lc = j0 / p.leaf_r;                 // leaf of these rank slots
-        lds_st16(smem1, g16_off(tid, c), on ? pack8(sa[c], sb[c], live ? p.leaf_s[lc] : 0.f, part == 1) : z);
-        if (BN == 256 || tid < BN) lds_st16(smem1, BM * 128 + g16_off(tid, c), (on && lc == myleaf) ? ev[c] : z);
-      } else {
-        lds_st16(smem1, g16_off(tid, c), on ? pack8(sa[c], sb[c], live ? p.s_epi : 0.f, part == 1) : z);
-        if constexpr (NN) {
+      const float sc = live ? p.s_epi : 0.f;
+      auto put_e = [&](int c, u32x4 v) {
+        if (BN == 256 || tid < BN) lds_st16(smem1, BM * 128 + g16_off(tid, c), v);
+      };
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q < cps) {
+          lds_st16(smem1, g16_off(tid, q), pack8(sa[q], sb[q], sc, false));
+          put_e(q, ev[q]);
+          if (nparts == 2) {
+            lds_st16(smem1, g16_off(tid, q + cps), pack8(sa[q], sb[q], sc, true));
+            put_e(q + cps, ev[q]);
+          }
+        }
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        if (c >= cps * nparts) {
+          lds_st16(smem1, g16_off(tid, c), z);
+          put_e(c, z);
+        }
+    } else {
+      // (NN, leaves) every chunk loaded, clamped into range: branch-free
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int part = c / cps, j0 = 8 * (c - part * cps);
+        const int jl = part < nparts ? j0 : 0;           // clamped rank offset
+        sa[c] = *reinterpret_cast<const f32x4*>(srow + jl);
+        sb[c] = *reinterpret_cast<const f32x4*>(srow + jl + 4);
+        if constexpr (NN) {       // rank row jl + t / 32, 16-byte chunk t % 32 of its 256 columns
+          ev[c] = *reinterpret_cast<const u32x4*>(e0 + (size_t)(jl + (tid >> 5)) * p.e_ldj + n0 + 8 * (tid & 31));
+        } else {                  // ranks jl .. jl + 7 of the leaf's row n0 + t (t < BN)
+          ev[c] = *reinterpret_cast<const u32x4*>(e0 + (size_t)nrow * p.e_ldn + jl % p.leaf_r);
+        }
+      }
+      copy_stage(0, smem0);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int part = c / cps, j0 = 8 * (c - part * cps);
+        const bool on = part < nparts;
+        const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (LEAF) {
+          const int lc = j0 / p.leaf_r;                 // leaf of these rank slots
+          lds_st16(smem1, g16_off(tid, c), on ? pack8(sa[c], sb[c], live ? p.leaf_s[lc] : 0.f, part == 1) : z);
+          if (BN == 256 || tid < BN) lds_st16(smem1, BM * 128 + g16_off(tid, c), (on && lc == myleaf) ? ev[c] : z);
+        } else {
+          lds_st16(smem1, g16_off(tid, c), on ? pack8(sa[c], sb[c], live ? p.s_epi : 0.f, part == 1) : z);
           const int j = 8 * c + (tid >> 5), ch = tid & 31;
           lds_st16(smem1, BM * 128 + g16_nn_row(j) + ((ch ^ (2 * (j & 3))) << 4), on ? ev[c] : z);
-        } else if (BN == 256 || tid < BN) {
-          lds_st16(smem1, BM * 128 + g16_off(tid, c), on ? ev[c] : z);
         }
       }
     }
