@@ -32,7 +32,8 @@
  *    host before anything is enqueued, so an error leaves all outputs
  *    untouched.  LDL_E_INVAL: null required pointer, negative size, bad dtype;
  *    LDL_E_UNSUPPORTED: shape outside what the kernels take (listed per call);
- *    LDL_E_WORKSPACE: ws_bytes below ldl_workspace_bytes(); LDL_E_HIP: a kernel
+ *    LDL_E_WORKSPACE: ws_bytes below ldl_workspace_bytes() (without its optional
+ *    split-reduction partials, see there); LDL_E_HIP: a kernel
  *    launch failed (hipGetLastError is left set).  M == 0 is valid and does
  *    nothing (weight-gradient outputs are zeroed).
  *  - Shape limits of the bf16 / int8 kernels: K and N multiples of 64
@@ -117,7 +118,11 @@ int ldl_set_kernel_events(int kind, void** start_events, void** stop_events, int
 
 /* Bytes of device workspace the entry point `op` needs for these sizes (256-byte
  * aligned, 0 when none).  Pure host arithmetic; never fails (returns 0 for
- * invalid sizes, which the entry point then rejects). */
+ * invalid sizes, which the entry point then rejects).  For the LoRA and 8-bit
+ * forward and backward this includes fp32 partials for the split reduction of the
+ * output tiles past the last full round of the GPU's compute units; a call given
+ * less (but at least what it needs without them) runs those tiles unsplit, with
+ * the same results up to fp32 summation order. */
 size_t ldl_workspace_bytes(int op, int M, int N, int K, int r, int dtype);
 
 /* ------------------------------------------------------------------------ LoRA
