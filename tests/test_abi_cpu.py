@@ -67,6 +67,22 @@ def test_workspace_sizes(L):
     assert L.ldl_workspace_bytes(1, 4096, 4096, 4096, 16, 1) >= 4096 * 16 * 4
 
 
+def test_workspace_counts_split_partials(L):
+    """The LoRA forward's workspace holds fp32 partials for the tiles past the last full round
+    of the 256 compute units: 4096 x 5120 outputs are 320 tiles of 256 x 256, the 64 past the
+    first round split four ways (256 x 256 fp32 = 256 KiB per block); 4096 x 4096 (256 tiles)
+    has no tail, the forward's other workspace does not depend on N, and fp32 calls never split."""
+    fwd = 0
+    a = L.ldl_workspace_bytes(fwd, 4096, 5120, 4096, 16, 1)
+    b = L.ldl_workspace_bytes(fwd, 4096, 4096, 4096, 16, 1)
+    assert a - b == 64 * 4 * 256 * 256 * 4
+    # 1024 tokens: 80 tiles each split three ways, against 64 tiles split four ways at 4096 columns
+    a = L.ldl_workspace_bytes(fwd, 1024, 5120, 4096, 16, 1)
+    b = L.ldl_workspace_bytes(fwd, 1024, 4096, 4096, 16, 1)
+    assert a - b == 80 * 3 * 256 * 256 * 4 - 64 * 4 * 256 * 256 * 4
+    assert L.ldl_workspace_bytes(fwd, 4096, 5120, 4096, 16, 0) == L.ldl_workspace_bytes(fwd, 4096, 4096, 4096, 16, 0)
+
+
 def test_tuning_switch(L):
     assert L.ldl_set_tuning(0, 1) == OK
     assert L.ldl_set_tuning(0, 0) == OK
