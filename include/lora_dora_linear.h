@@ -250,7 +250,8 @@ int lora_merge_bwd(int N, int K, int r, float s, int dtype, const void* dW, int 
 
 /* ------------------------------------------------------------------------ DoRA
  * Row-scaled DoRA ("dora-rows"), bf16 only.  The row norm of W' = W0 + s.B.A uses
- * the closed form with the cached constant rowsum(W0^2) and the two rank-sized terms
+ * the closed form: the row sums of W0^2 (computed once per frozen weight by
+ * dora_prepare) plus the two rank-sized terms
  * P = W0.A^T [N,r] and G = A.A^T [r,r]; the bias is added after the row scale; the
  * norm stays in the autograd graph; eps clamps the norm from below
  * ("LoRA/DoRA fast forward: no weight materialization", commit message, sections
