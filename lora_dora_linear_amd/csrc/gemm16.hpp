@@ -470,12 +470,19 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   // the staged bf16 tile to dst as 16-byte row segments, eight LDS reads in flight before
   // their stores (one read, wait and store per segment had been bound by the LDS latency:
   // ~6800 cycles per tile)
-  auto write_staged = [&](void* dst, int ldo) __attribute__((always_inline)) {
+  // part_c: -1 every row, 0 / 1 (256 columns) the groups of 64 rows with even / odd index
+  // (tile rows [0, 64) and [128, 192) / [64, 128) and [192, 256))
+  auto write_staged = [&](void* dst, int ldo, auto part_c) __attribute__((always_inline)) {
+    constexpr int PART = decltype(part_c)::value;
     uint16_t* out = static_cast<uint16_t*>(dst);
     constexpr int NIT = BM * NCH / 256;
     static_assert(NIT % 8 == 0, "row segments per thread in groups of eight");
+    static_assert(PART < 0 || NCH == 32, "row halves: 256 columns");
 #pragma unroll
     for (int b = 0; b < NIT; b += 8) {
+      if constexpr (PART >= 0) {
+        if ((b / 8) % 2 != PART) continue;
+      }
       u32x4 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -496,8 +503,11 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   // (col >> 3) ^ (row & 31) = y ^ ((i & 1) << 4) ^ (j << 1) with y = l16 ^ (lq >> 1) ^ (wn << 4)
   // (col = 128 wn + 16 j + 4 lq), byte 8 (lq & 1) in it.  (A separate path without the bias
   // additions made the allocator move the k-loop's accumulators.)
-  auto stage_out = [&](auto z_c) __attribute__((always_inline)) {
+  // half_c: -1 every accumulator block, 0 / 1 the blocks i < 4 / i >= 4 (rows [0, 64) /
+  // [64, 128) of the wave's half)
+  auto stage_out = [&](auto z_c, auto half_c) __attribute__((always_inline)) {
     constexpr bool Z = decltype(z_c)::value;       // DORA's unscaled output
+    constexpr int HALF = decltype(half_c)::value;
     constexpr bool CS = DORA && !Z;
     [[maybe_unused]] uint8_t* const sb = (wm ? smem1 : smem0) + l16 * SROW + (lq & 1) * 8;
     [[maybe_unused]] const int y = l16 ^ (lq >> 1) ^ (wn << 4);
@@ -510,6 +520,9 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
       if constexpr (CS) cs = *reinterpret_cast<const f32x4*>(p.col_scale + n0 + cl);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
+        if constexpr (HALF >= 0) {
+          if (i / 4 != HALF) continue;
+        }
         auto v = __builtin_bit_cast(f32x4, acc[i][j]);   // (fp32 in every kernel that calls this)
         if constexpr (CS) v *= cs;
         u32x2 w;
@@ -522,10 +535,24 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
       }
     }
   };
-  auto emit = [&](auto z_c, void* dst, int ldo) {
-    stage_out(z_c);
-    __syncthreads();
-    write_staged(dst, ldo);
+  // 256 columns: the rows of the second halves are staged while the first halves' stores
+  // drain (the stores do not hold up the wave; the two halves use different LDS rows)
+  auto emit = [&](auto z_c, void* dst, int ldo) __attribute__((always_inline)) {
+    using H0 = std::integral_constant<int, 0>;
+    using H1 = std::integral_constant<int, 1>;
+    using HA = std::integral_constant<int, -1>;
+    if constexpr (BN == 256) {
+      stage_out(z_c, H0{});
+      __syncthreads();
+      write_staged(dst, ldo, H0{});
+      stage_out(z_c, H1{});
+      __syncthreads();
+      write_staged(dst, ldo, H1{});
+    } else {
+      stage_out(z_c, HA{});
+      __syncthreads();
+      write_staged(dst, ldo, HA{});
+    }
   };
   if constexpr (I8) {
     // dequantise the exact int32 products in place: acc . sx[m] . sw[n] in fp32 (the fp32 bits
@@ -577,9 +604,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
       write_partial();
       return;
     }
-    stage_out(std::false_type{});
-    __syncthreads();
-    write_staged(p.out, p.ldo);
+    emit(std::false_type{}, p.out, p.ldo);
   } else if constexpr (DORA) {
     emit(std::true_type{}, p.out2, p.ldo2);
     __syncthreads();                               // the staging buffers are free again
@@ -704,9 +729,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
              lds_ld16(smem1, r * 256 + ((c ^ (r & 15)) << 4)));
     }
   } else {
-    stage_out(std::false_type{});
-    __syncthreads();
-    write_staged(p.out, p.ldo);
+    emit(std::false_type{}, p.out, p.ldo);
   }
 }
 
