@@ -543,7 +543,9 @@ def main():
         if wl in ("swiglu", "geglu"):
             names = {0: "down-projection GEMM (" + ("gemm16_kernel NT" if args.gemm_4wave != 0 else "gemm_kernel NT")
                         + ")",
-                     1: "input-gradient GEMM over gate and up (gemm_kernel NN)"}
+                     1: "input-gradient GEMM over gate and up (" +
+                        ("gemm16_kernel NN over the two stacked weights" if args.gemm_4wave != 0 else "gemm_kernel NN")
+                        + ")"}
         if wl == "fp8":
             names[0] = "forward base GEMM (gemm_f8_kernel NT, e4m3 block-scaled MFMA)"
         if wl in ("w8a8", "fp8"):

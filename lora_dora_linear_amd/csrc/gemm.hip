@@ -185,6 +185,26 @@ static bool dual16_ok(const GemmParams& p) {
 }
 // W8A8 forward on the four-wave tile: int8 16x16x64 MFMAs into exact int32 accumulators, then
 // the dequantisation and the low-rank k-tile on fp32 accumulators after the loop.
+// The input gradient over two stacked weights (the gated MLP's gate and up projections):
+// the four-wave NN tile with Q rows k < kseg from b0 and the rest from b1, and the rank-(2 r)
+// low-rank term as two seed k-tiles (S columns [0, r) against the rank rows of e0, [r, 2 r)
+// against e1, bf16 hi).
+static bool nn2_ok(const GemmParams& p) {
+  const int rs = p.e_jsplit;
+  return p.kseg > 0 && p.kseg < p.K && p.kseg % 64 == 0 && (p.K - p.kseg) % 64 == 0 && p.b1 != nullptr &&
+         p.r_epi > 0 && p.r_epi == 2 * rs && rs % 8 == 0 && rs <= 64 && p.ld_s % 4 == 0 && a16(p.S) &&
+         a16(p.e0) && a16(p.e1) && p.e_ldn == 1 && p.e_ldj % 8 == 0 && p.ldb % 8 == 0 && a16(p.b0) && a16(p.b1);
+}
+
+static hipError_t run16_nn2(const GemmParams& p0, hipStream_t st) {
+  GemmParams p = p0;
+  p.seed_hilo = 0;
+  p.split_s = 0;
+  const int tiles = ((p.M + 255) / 256) * (p.N / 256);
+  hipLaunchKernelGGL((gemm16_kernel<true, 2, false, false, 256>), dim3(tiles), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
 static hipError_t run16_i8(const GemmParams& p0, hipStream_t st) {
   GemmParams p = p0;
   p.seed_hilo = (p.r_epi > 0 && 2 * p.r_epi <= 64) ? 1 : 0;
@@ -332,6 +352,8 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
     if (kind == GK_NT_PLAIN) return run16<false, false, false, 192>(p, st);
     return run16<false, true, false, 192>(p, st);
   }
+  if (kind == GK_NN_PLAIN && g_gemm_4wave && bn == 256 && big && p.side == nullptr && nn2_ok(p))
+    return run16_nn2(p, st);
   if (g_gemm_4wave && bn == 256 && big && p.side == nullptr && p.r_epi <= 64 && seed) {
     if (kind == GK_NT_PLAIN) return run16<false>(p, st);
     if (kind == GK_NT_DORA) return run16<false, true>(p, st);

@@ -62,7 +62,11 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   static_assert(BN_ == 256 || (!NN && BN_ == 192), "tile widths: 256, or 192 for NT");
   static_assert(!SWB || (NN && !DORA), "the SwiGLU backward epilogue is an NN epilogue");
   static_assert(!SWF || (!NN && !DORA && !SWB && BN_ == 256 && LR != 1), "the dual tile is a plain 256-wide NT tile");
-  static_assert(LR >= 0 && LR <= 2 && (LR != 2 || SWF), "two low-rank k-tiles: the dual tile's two segments");
+  // NN2: the NN tile over two stacked Q segments (rows k < kseg from b0, the rest from b1)
+  // with a two-segment low-rank term (two seed k-tiles)
+  constexpr bool NN2 = NN && LR == 2;
+  static_assert(LR >= 0 && LR <= 2 && (LR != 2 || SWF || (NN && !DORA && !SWB && !I8 && !LEAF && BN_ == 256)),
+                "two low-rank k-tiles: the dual tile's two segments, or the NN tile over two stacked weights");
   static_assert(!I8 || (!NN && !DORA && !SWB && !SWF && LR == 0 && BN_ == 256), "int8: the plain 256-wide NT tile");
   constexpr int KB = I8 ? 128 : 64;                 // reduction elements per k-tile (128 bytes per row)
   constexpr int BM = 256, BN = BN_, NW = 4;
@@ -114,8 +118,10 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   const __amdgpu_buffer_rsrc_t rs_a =
       make_rsrc(static_cast<const uint8_t*>(p.a) + koff_a, (uint32_t)M * lda_b - koff_a);
   const __amdgpu_buffer_rsrc_t rs_b =
-      make_rsrc(static_cast<const uint8_t*>(p.b0) + koff_b, (uint32_t)(NN ? p.K : N) * ldb_b - koff_b);
-  const __amdgpu_buffer_rsrc_t rs_b1 = SWF ? make_rsrc(p.b1, (uint32_t)N * ldb_b) : rs_b;   // dual: up rows
+      make_rsrc(static_cast<const uint8_t*>(p.b0) + koff_b, (uint32_t)(NN ? (NN2 ? p.kseg : p.K) : N) * ldb_b - koff_b);
+  // dual: up rows; NN2: the second segment's k-rows
+  const __amdgpu_buffer_rsrc_t rs_b1 =
+      SWF ? make_rsrc(p.b1, (uint32_t)N * ldb_b) : (NN2 ? make_rsrc(p.b1, (uint32_t)(p.K - p.kseg) * ldb_b) : rs_b);
   const __amdgpu_buffer_rsrc_t rs_none = make_rsrc(p.a, 0u);    // copies that read nothing
 
   // Copies: 8 instructions per tile per wave, 1 KB each; rows past M read as zero.  Copy i
@@ -150,12 +156,20 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
     const uint32_t ka = (uint32_t)kt * 128u, kb = NN ? (uint32_t)kt * 64u * ldb_b : (uint32_t)kt * 128u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) copy(ra, a_off[NN ? i : 0], ka + i * a_step, sb + (i * NW + wave) * 1024);
+    if constexpr (NN2) {      // k-tiles never straddle kseg (a multiple of 64)
+      const bool seg1 = kt * KB >= p.kseg;
+      const __amdgpu_buffer_rsrc_t rq = seg1 ? rb1 : rb;
+      const uint32_t kq = (uint32_t)(seg1 ? kt * KB - p.kseg : kt * KB) * ldb_b;
 #pragma unroll
-    for (int i = 0; i < (NN ? 8 : FN); ++i) {
-      if constexpr (SWF)    // Q rows 0..127 gate rows n0.., rows 128..255 up rows n0..
-        copy(i < FN / 2 ? rb : rb1, b_off[0], kb + (i & (FN / 2 - 1)) * b_step, sb + q_dst(i));
-      else
-        copy(rb, b_off[NN ? i : 0], kb + i * b_step, sb + q_dst(i));
+      for (int i = 0; i < 8; ++i) copy(rq, b_off[i], kq, sb + q_dst(i));
+    } else {
+#pragma unroll
+      for (int i = 0; i < (NN ? 8 : FN); ++i) {
+        if constexpr (SWF)    // Q rows 0..127 gate rows n0.., rows 128..255 up rows n0..
+          copy(i < FN / 2 ? rb : rb1, b_off[0], kb + (i & (FN / 2 - 1)) * b_step, sb + q_dst(i));
+        else
+          copy(rb, b_off[NN ? i : 0], kb + i * b_step, sb + q_dst(i));
+      }
     }
   };
 
@@ -335,6 +349,38 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
     }
     __syncthreads();
     ldf(smem1, 0, fa0, fb0);
+  } else if constexpr (NN2) {
+    // two seed k-tiles: segment g (k-tile g - 2) holds s.S[.., g rs .. g rs + rs) (bf16 hi)
+    // against the rank rows of E_g (e0, e1: [rs, N] rows at e_ldj), rs = e_jsplit <= 64; one
+    // segment at a time, as the dual tile.  The loop starts on smem1 as with one seed k-tile
+    // (starting on smem0 made the allocator move the NN loop's accumulators), so segment 0 is
+    // staged in smem1 and segment 1 in smem0.
+    const int rs = p.e_jsplit;
+    const float sc = live ? p.s_epi : 0.f;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const uint16_t* eg = g ? static_cast<const uint16_t*>(p.e1) : e0;
+      f32x4 sa[8], sb[8];
+      u32x4 ev[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int jl = 8 * c < rs ? 8 * c : 0;
+        sa[c] = *reinterpret_cast<const f32x4*>(srow + g * rs + jl);
+        sb[c] = *reinterpret_cast<const f32x4*>(srow + g * rs + jl + 4);
+        ev[c] = *reinterpret_cast<const u32x4*>(eg + (size_t)(jl + (tid >> 5)) * p.e_ldj + n0 + 8 * (tid & 31));
+      }
+      uint8_t* buf = g ? smem0 : smem1;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const bool on = 8 * c < rs;
+        const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+        lds_st16(buf, g16_off(tid, c), on ? pack8(sa[c], sb[c], sc, false) : z);
+        const int j = 8 * c + (tid >> 5), ch = tid & 31;
+        lds_st16(buf, BM * 128 + g16_nn_row(j) + ((ch ^ (2 * (j & 3))) << 4), on ? ev[c] : z);
+      }
+    }
+    __syncthreads();
+    ldf(smem1, 0, fa0, fb0);
   } else if constexpr (LR == 2) {
     const int rs = p.e_jsplit;                        // rank of each segment
     const int own = tid >> 7;                         // segment of this thread's Q row (wave-uniform)
@@ -427,7 +473,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(const GemmParams p) {
   // One loop body for every k-tile (from the low-rank tile -1 when there is one), so the
   // accumulators keep their registers to the end: an odd count runs one more tile, whose
   // stage the empty copies filled with zeros.
-  constexpr int P0 = LR & 1;
+  constexpr int P0 = (LR & 1) || NN2 ? 1 : 0;
   for (int kt = -LR; kt < KT; kt += 2) {
     tile(std::integral_constant<int, P0>{}, kt);
     tile(std::integral_constant<int, 1 - P0>{}, kt + 1);
