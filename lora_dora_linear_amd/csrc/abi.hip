@@ -525,6 +525,11 @@ int lora_linear_fwd(int M, int N, int K, int r, float s, int dtype, const void* 
 
   if (dtype == LDL_F32) {
     const float *x = (const float*)X, *w = (const float*)W0, *a = (const float*)A, *bb = (const float*)B;
+    if (f32_small_ok(M, N, K, r) && ldx % 4 == 0 && ldw % 4 == 0) {
+      LDL_TRY(launch_f32_small_fwd(M, N, K, r, s, x, ldx, w, ldw, a, bb, (const float*)bias, (float*)Y, ldy,
+                                   U_save, ldu, st));
+      return LDL_OK;
+    }
     LDL_TRY(f32(M, r, K, x, ldx, 1, a, 1, K, U, lu, 1.f, 0.f, nullptr, st));
     LDL_TRY(f32(M, N, K, x, ldx, 1, w, 1, ldw, (float*)Y, ldy, 1.f, 0.f, (const float*)bias, st));
     LDL_TRY(f32(M, N, r, U, lu, 1, bb, 1, r, (float*)Y, ldy, s, 1.f, nullptr, st));
@@ -576,6 +581,11 @@ int lora_linear_bwd(int M, int N, int K, int r, float s, int dtype, const void* 
     return LDL_OK;
   }
 
+  if (dtype == LDL_F32 && f32_small_ok(M, N, K, r) && lddy % 4 == 0 && ldx % 4 == 0) {
+    LDL_TRY(launch_f32_small_bwd(M, N, K, r, s, (const float*)dY, lddy, (const float*)X, ldx, (const float*)W0, ldw,
+                                 (const float*)A, (const float*)B, U_saved, ldu, (float*)dX, lddx, dA, dB, dbias, st));
+    return LDL_OK;
+  }
   if (dtype == LDL_F32) {
     Bump wb(ws);
     float* V = wb.take<float>((size_t)M * r);

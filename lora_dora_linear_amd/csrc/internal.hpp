@@ -128,6 +128,14 @@ struct F32GemmParams {
   const float* bias;
 };
 hipError_t launch_f32_gemm(const F32GemmParams& p, hipStream_t st);
+// the fp32 LoRA layer at small sizes: forward and backward in one launch each
+bool f32_small_ok(int M, int N, int K, int r);
+hipError_t launch_f32_small_fwd(int M, int N, int K, int r, float s, const float* X, int ldx, const float* W0,
+                                int ldw, const float* A, const float* B, const float* bias, float* Y, int ldy,
+                                float* U, int ldu, hipStream_t st);
+hipError_t launch_f32_small_bwd(int M, int N, int K, int r, float s, const float* dY, int lddy, const float* X,
+                                int ldx, const float* W0, int ldw, const float* A, const float* B, const float* U,
+                                int ldu, float* dX, int lddx, float* dA, float* dB, float* dbias, hipStream_t st);
 hipError_t launch_f32_colsum(const float* X, int M, int N, int ld, float* out, hipStream_t st);
 
 }  // namespace ldl

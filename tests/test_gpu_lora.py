@@ -55,6 +55,40 @@ def test_fp32_tiny(variant):
         assert_close(host(Y), X @ W0.T + c.f64("bias"), 1e-5, "Y vs base")
 
 
+# fp32 layers small enough for the one-launch forward / backward (M <= 256, N and K multiples
+# of 16 up to 1024, r <= 16), a ragged M tail, r not a multiple of 4, and shapes just outside
+# those limits (the multi-launch path): each against the oracle, and the factor gradients the
+# same bits with U saved and with U recomputed.
+F32_SHAPES = [
+    (37, 80, 48, 5),      # ragged M, odd r
+    (200, 1024, 64, 16),  # four row blocks per wave in the dA / dB jobs, N at its limit
+    (256, 32, 1024, 3),   # K at its limit
+    (1, 16, 16, 1),       # one row, one rank
+    (64, 250, 256, 8),    # N not a multiple of 16: multi-launch
+    (300, 256, 256, 8),   # M above 256: multi-launch
+    (64, 256, 256, 17),   # r above 16: multi-launch
+]
+
+
+@pytest.mark.parametrize("M,N,K,r", F32_SHAPES)
+def test_fp32_small_shapes(M, N, K, r):
+    require_gpu()
+    import lora_dora_linear_amd as L
+    c = inputs.linear_case(5, M, N, K, r, 1.5, "f32", with_bias=True)
+    Y, U, g = _run(c, with_bias=True, need_dbias=True)
+    Yr, gr, Ur = _oracle(c, with_bias=True)
+    assert_close(host(Y), Yr, 1e-5, "Y")
+    assert_close(host(U), Ur, 1e-5, "U")
+    for k in ("dX", "dA", "dB"):
+        assert_close(host(g[k]), gr[k], 1e-4, k)
+    assert_close(host(g["dbias"]), gr["db"], 1e-4, "dbias")
+    X, W0, A, B, dY = (dev(c.t[k], "f32") for k in ("X", "W0", "A", "B", "dY"))
+    g2 = L.lora_linear_bwd(dY, X, W0, A, B, c.s, U=None)
+    torch.cuda.synchronize()
+    for k in ("dA", "dB"):
+        assert torch.equal(g[k], g2[k]), k + " with U recomputed"
+
+
 # ---------------------------------------------------------------- bf16 at several tile shapes with a ragged M tail
 SHAPES = [
     # M, N, K, r     (256x256 tiles, 256x192, 256x128, 128-row tiles; r not a multiple of 16; r = 128)
