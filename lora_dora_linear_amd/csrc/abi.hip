@@ -269,6 +269,7 @@ hipError_t rowproj(int M, int K, int R, const void* P, int ldp, const void* q0, 
   p.P1 = nullptr; p.p_split = M; p.ldp1 = ldp;
   p.q_trans = 0; p.q_kscale = nullptr;
   p.out = out; p.ldo = ldo; p.scale = scale;
+  p.P2 = nullptr; p.p_split2 = p.M; p.ldp2 = ldp; p.out2 = nullptr; p.ldo2 = 0;
   return launch_rowproj(p, st);
 }
 
@@ -282,7 +283,27 @@ hipError_t rowproj2(int M0, int M1, int K, int R, const void* P, int ldp, const 
   p.q0 = p.q1 = static_cast<const uint16_t*>(q0); p.ldq = ldq;
   p.q_trans = 0; p.q_kscale = nullptr;
   p.out = out; p.ldo = ldo; p.scale = scale;
+  p.P2 = nullptr; p.p_split2 = p.M; p.ldp2 = ldp; p.out2 = nullptr; p.ldo2 = 0;
   return launch_rowproj(p, st);
+}
+
+// rowproj2 over the rows of P then P1 into out, and the rows of P2 against the same Q into out2, in
+// one launch when the streamed kernel takes the three segments; otherwise two launches
+hipError_t rowproj3(int M0, int M1, int M2, int K, int R, const void* P, int ldp, const void* P1, int ldp1,
+                    const void* P2, int ldp2, const void* q0, int ldq, float* out, int ldo, float* out2, int ldo2,
+                    hipStream_t st) {
+  RowProjParams p;
+  p.M = M0 + M1 + M2; p.K = K; p.R = R; p.R0 = R;
+  p.P = static_cast<const uint16_t*>(P); p.ldp = ldp;
+  p.P1 = static_cast<const uint16_t*>(P1); p.p_split = M0; p.ldp1 = ldp1;
+  p.q0 = p.q1 = static_cast<const uint16_t*>(q0); p.ldq = ldq;
+  p.q_trans = 0; p.q_kscale = nullptr;
+  p.out = out; p.ldo = ldo; p.scale = 1.f;
+  p.P2 = static_cast<const uint16_t*>(P2); p.p_split2 = M0 + M1; p.ldp2 = ldp2; p.out2 = out2; p.ldo2 = ldo2;
+  if (M2 > 0 && rowproj_three_ok(p)) return launch_rowproj(p, st);
+  const hipError_t e = rowproj2(M0, M1, K, R, P, ldp, P1, ldp1, q0, ldq, out, ldo, 1.f, st);
+  if (e != hipSuccess || M2 == 0) return e;
+  return rowproj(M2, K, R, P2, ldp2, q0, nullptr, R, ldq, out2, ldo2, 1.f, st);
 }
 
 // out[m, j] = scale * sum_k P[m, k] * bf16(Bq[k, j] * kscale[k]) with Bq a [K, R] matrix, leading dim ldb
@@ -295,6 +316,7 @@ hipError_t rowproj_t(int M, int K, int R, const void* P, int ldp, const void* Bq
   p.q0 = p.q1 = static_cast<const uint16_t*>(Bq); p.ldq = ldb;
   p.q_trans = 1; p.q_kscale = kscale;
   p.out = out; p.ldo = ldo; p.scale = scale;
+  p.P2 = nullptr; p.p_split2 = p.M; p.ldp2 = ldp; p.out2 = nullptr; p.ldo2 = 0;
   return launch_rowproj(p, st);
 }
 
@@ -945,12 +967,11 @@ int dora_linear_fwd(int M, int N, int K, int r, float s, float eps, int dtype, c
   float* g = state + N;
   float* P = state + 2 * (size_t)N;
   float* G = P + (size_t)N * r;
-  // the norm terms: P = W0.A^T, G = A.A^T, then nu and g (independent of M)
-  // (G is stored right after P with the same row length: one launch over the rows of W0 then A)
-  LDL_TRY(rowproj2(N, r, K, r, W0, ldw, A, K, A, K, P, r, 1.f, st));
+  // the norm terms P = W0.A^T and G = A.A^T (G stored right after P with the same row length)
+  // and U = X.A^T: one launch over the rows of W0, A and X; then nu and g
+  LDL_TRY(rowproj3(N, r, M, K, r, W0, ldw, A, K, X, ldx, A, K, P, r, U_save, ldu, st));
   LDL_TRY(launch_dora_norm(N, r, s, eps, w0_sumsq, P, G, static_cast<const uint16_t*>(B), m, norm, g, st));
   if (M == 0) return LDL_OK;
-  LDL_TRY(rowproj(M, K, r, X, ldx, A, nullptr, r, K, U_save, ldu, 1.f, st));
   GemmParams p = gp0();
   p.M = M; p.N = N; p.K = K;
   p.a = X; p.lda = ldx; p.b0 = W0; p.ldb = ldw; p.kseg = K;

@@ -16,6 +16,10 @@ struct RowProjParams {
   const float* q_kscale;           // q_trans only, optional: Q(j, k) *= q_kscale[k] (rounded to bf16)
   float* out; int ldo;             // out[m * ldo + j] = scale * sum_k P[m,k] Q[j,k]
   float scale;
+  // optional third segment (streamed kernel only): rows m >= p_split2 come from P2 (row
+  // m - p_split2, leading dim ldp2) and go to out2 (row m - p_split2, leading dim ldo2)
+  const uint16_t* P2; int p_split2; int ldp2;
+  float* out2; int ldo2;
 };
 
 struct ColProjParams {
@@ -59,6 +63,7 @@ bool gemm_multi_leaf_ok(const GemmParams& p);
 size_t gemm_split_bytes(int M, int N);
 
 hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st);
+bool rowproj_three_ok(const RowProjParams& p);   // the streamed kernel takes P2
 int colproj_rp(int R);
 extern int g_rowstream32;   // rank 33..128 row projections on 32-row blocks: 0 never, 1 auto, 2 always
 // size in 32-bit words of the packed S a column projection of M rows and rank R needs

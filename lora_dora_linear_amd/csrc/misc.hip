@@ -52,10 +52,19 @@ __device__ __forceinline__ float lane_bcast(float v, int l) {
 // g = m / max(nu, eps).  One wave per output row, lane j holding ranks j and j + 64
 // (r <= 128); G staged in LDS transposed so that lane j reads G[j][l] at consecutive
 // addresses; B_n[l] broadcast from the lane that holds it.
+// the r x r Gram matrix into LDS, 16 bytes per thread and load (G 16-byte aligned, r a
+// multiple of 8), then a block barrier
+__device__ __forceinline__ void stage_g(float* sG, const float* G, int r) {
+  const int nq = r * r / 4;
+  for (int i = threadIdx.x; i < nq; i += blockDim.x)
+    reinterpret_cast<f32x4*>(sG)[i] = reinterpret_cast<const f32x4*>(G)[i];
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(256) void dora_norm_kernel(int N, int r, float s, float eps, const float* c,
                                                         const float* P, const float* G, const uint16_t* B,
                                                         const float* m, float* norm, float* g) {
-  extern __shared__ float sGt[];                 // sGt[l r + j] = G[j][l]
+  extern __shared__ float sG[];                  // G = A.A^T as stored (symmetric: row l = column l)
   const int lane = threadIdx.x & 63;
   const int n = min(blockIdx.x * 4 + (threadIdx.x >> 6), N - 1);   // rows past N redo row N-1, unstored
   // the row's operands first, so their latency overlaps the staging of G
@@ -65,14 +74,13 @@ __global__ __launch_bounds__(256) void dora_norm_kernel(int N, int r, float s, f
   const float b0 = h0 ? bf16_to_f32(bn[lane]) : 0.f, b1 = h1 ? bf16_to_f32(bn[lane + 64]) : 0.f;
   const float p0 = h0 ? pn[lane] : 0.f, p1 = h1 ? pn[lane + 64] : 0.f;
   const float cn = c[n], mn = m[n];
-  for (int i = threadIdx.x; i < r * r; i += blockDim.x) sGt[(i % r) * r + i / r] = G[i];
-  __syncthreads();
+  stage_g(sG, G, r);
   float t1 = b0 * p0 + b1 * p1;
-  float bg0 = 0.f, bg1 = 0.f;                    // (G B_n^T)[j] for the lane's ranks
+  float bg0 = 0.f, bg1 = 0.f;                    // (B_n G)[j] = (G B_n^T)[j] for the lane's ranks
   for (int l = 0; l < r; ++l) {
     const float bl = l < 64 ? lane_bcast(b0, l) : lane_bcast(b1, l - 64);
-    if (h0) bg0 += sGt[l * r + lane] * bl;
-    if (h1) bg1 += sGt[l * r + lane + 64] * bl;
+    if (h0) bg0 += bl * sG[l * r + lane];
+    if (h1) bg1 += bl * sG[l * r + lane + 64];
   }
   float t2 = b0 * bg0 + b1 * bg1;
   t1 = wave_sum(t1);
@@ -131,8 +139,7 @@ __global__ __launch_bounds__(256) void dora_finalize_kernel(int N, int r, float 
   const float b0 = h0 ? bf16_to_f32(bn[lane]) : 0.f, b1 = h1 ? bf16_to_f32(bn[lane + 64]) : 0.f;
   const float p0 = h0 ? P[(size_t)n * r + lane] : 0.f, p1 = h1 ? P[(size_t)n * r + lane + 64] : 0.f;
   const float nu = norm[n], gn = g[n], mn = m[n];
-  for (int i = threadIdx.x; i < r * r; i += blockDim.x) sG[i] = G[i];
-  __syncthreads();
+  stage_g(sG, G, r);
   const float den = fmaxf(nu, eps);
   if (lane == 0 && live) dm[n] = dg / den;
   const float w = (nu > eps) ? (-dg * mn / (2.f * nu * nu * nu)) : 0.f;

@@ -176,12 +176,16 @@ __global__ __launch_bounds__(256) void rowstream_kernel(const RowProjParams p) {
   const int nch = (p.K + KC - 1) / KC;
   const bool tq = p.q_trans != 0;
 
-  // a block's BMR rows lie in one P segment (the split is a multiple of BMR)
-  const bool seg1 = p.P1 != nullptr && m0 >= p.p_split;
-  const uint32_t ldp_b = (uint32_t)(seg1 ? p.ldp1 : p.ldp) * 2u, ldq_b = (uint32_t)p.ldq * 2u;
-  const int pm0 = seg1 ? m0 - p.p_split : m0;
-  const __amdgpu_buffer_rsrc_t rs_p = seg1 ? make_rsrc(p.P1, (uint32_t)(p.M - p.p_split) * ldp_b)
-                                           : make_rsrc(p.P, (uint32_t)(p.P1 != nullptr ? p.p_split : p.M) * ldp_b);
+  // a block's BMR rows lie in one P segment (the splits are multiples of BMR)
+  const bool seg2 = p.P2 != nullptr && m0 >= p.p_split2;
+  const int end1 = p.P2 != nullptr ? p.p_split2 : p.M;          // end of the first two segments
+  const bool seg1 = !seg2 && p.P1 != nullptr && m0 >= p.p_split;
+  const uint32_t ldp_b = (uint32_t)(seg2 ? p.ldp2 : seg1 ? p.ldp1 : p.ldp) * 2u, ldq_b = (uint32_t)p.ldq * 2u;
+  const int pm0 = seg2 ? m0 - p.p_split2 : seg1 ? m0 - p.p_split : m0;
+  const __amdgpu_buffer_rsrc_t rs_p =
+      seg2 ? make_rsrc(p.P2, (uint32_t)(p.M - p.p_split2) * ldp_b)
+           : seg1 ? make_rsrc(p.P1, (uint32_t)(end1 - p.p_split) * ldp_b)
+                  : make_rsrc(p.P, (uint32_t)(p.P1 != nullptr ? p.p_split : end1) * ldp_b);
   const __amdgpu_buffer_rsrc_t rs_q0 =
       make_rsrc(p.q0, tq ? (uint32_t)p.K * (uint32_t)p.R * 2u : (uint32_t)p.R0 * ldq_b);
   const __amdgpu_buffer_rsrc_t rs_q1 = make_rsrc(p.q1, tq ? 0u : (uint32_t)(p.R - p.R0) * ldq_b);
@@ -285,9 +289,9 @@ __global__ __launch_bounds__(256) void rowstream_kernel(const RowProjParams p) {
     f32x4 v = red[(h * NB + jb) * 64 + lane];
 #pragma unroll
     for (int w = 1; w < 4; ++w) v += red[((w * NH + h) * NB + jb) * 64 + lane];
-    if (m < p.M) {
+    if (m < (seg2 ? p.M : end1)) {
       const int j0 = jb * 16 + 4 * lq;
-      float* dst = p.out + (size_t)m * p.ldo;
+      float* dst = seg2 ? p.out2 + (size_t)(m - p.p_split2) * p.ldo2 : p.out + (size_t)m * p.ldo;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (j0 + i < p.R) dst[j0 + i] = v[i] * p.scale;
@@ -780,6 +784,7 @@ static bool rowstream_ok(const RowProjParams& p, int rp) {
   const int rows_per_inst = 1024 / rl;
   if (p.ldp % 8 || (((uintptr_t)p.P) & 15) || (((uintptr_t)p.q0) & 15)) return false;
   if (p.P1 != nullptr && (p.p_split % 16 || p.ldp1 % 8 || (((uintptr_t)p.P1) & 15))) return false;
+  if (p.P2 != nullptr && (p.p_split2 % 16 || p.ldp2 % 8 || (((uintptr_t)p.P2) & 15))) return false;
   if (p.q_kscale && (((uintptr_t)p.q_kscale) & 15)) return false;
   if (p.q_trans) return p.R % 4 == 0 && p.R0 == p.R;
   if (p.ldq % 8 || (((uintptr_t)p.q1) & 15)) return false;
@@ -797,12 +802,19 @@ int g_rowstream32 = 1;
 static bool rowstream32(const RowProjParams& p, int rp) {
   if ((rp != 64 && rp != 128) || p.q_kscale != nullptr || g_rowstream32 == 0) return false;
   if (p.P1 != nullptr && p.p_split % 32) return false;
+  if (p.P2 != nullptr && p.p_split2 % 32) return false;
   return g_rowstream32 == 2 || (p.M + 31) / 32 >= 256;
+}
+
+bool rowproj_three_ok(const RowProjParams& p) {
+  const int rp = p.R <= 16 ? 16 : p.R <= 32 ? 32 : p.R <= 64 ? 64 : 128;
+  return p.P2 != nullptr && rowstream_ok(p, rp);
 }
 
 hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st) {
   if (p.M <= 0) return hipSuccess;
   const int rp = p.R <= 16 ? 16 : p.R <= 32 ? 32 : p.R <= 64 ? 64 : 128;
+  if (p.P2 != nullptr && !rowstream_ok(p, rp)) return hipErrorInvalidValue;   // (callers check first)
   if (rowstream_ok(p, rp)) {
     if (rowstream32(p, rp)) {
       if (rp == 64) hipLaunchKernelGGL((rowstream_kernel<64, false, 32>), dim3((p.M + 31) / 32), dim3(256), 0, st, p);
