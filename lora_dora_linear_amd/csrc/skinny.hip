@@ -692,13 +692,30 @@ struct ReduceBatch {
   int blocks0;                    // blocks [0, blocks0) reduce job 0, the rest job 1
 };
 
-// One block per 32 partial rows c of one job: the [32][rp] slices of all splits
-// are summed in split order (float4 loads, coalesced, eight splits in flight),
-// staged in LDS, then written out with the finishing terms, consecutive threads on
-// consecutive output columns.  The optional Qm.Am addend (transposed jobs only: the
+// One block per 8 partial rows c of one job: the [8][rp] slice of every split is read as
+// float4 groups; where the slice has fewer groups than the block has threads, the T threads
+// of a group each sum a contiguous run of the splits in order (eight in flight) and the runs
+// are added in thread order, so the order of the sum is fixed by the shape alone.  The
+// sums are staged in LDS, then written out with the finishing terms, consecutive threads
+// on consecutive output columns.  The optional Qm.Am addend (transposed jobs only: the
 // partial rows are the output columns) reads both operands from dynamic LDS: Qm
-// [rows, rq] (row stride rq + 1) and the block's 32 columns of Am [rq, cols].
-constexpr int kReduceRows = 32;
+// [rows, rq] (row stride rq + 1) and the block's 8 columns of Am [rq, cols].
+constexpr int kReduceRows = 8;
+
+// sum over splits [s0, s1) of the float4 at src (split stride pstride), in split order
+__device__ __forceinline__ f32x4 sum_splits(const float* src, size_t pstride, int s0, int s1) {
+  f32x4 acc = {0, 0, 0, 0};
+  int sp = s0;
+  for (; sp + 8 <= s1; sp += 8) {
+    f32x4 a[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a[q] = *reinterpret_cast<const f32x4*>(src + (size_t)(sp + q) * pstride);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc += a[q];
+  }
+  for (; sp < s1; ++sp) acc += *reinterpret_cast<const f32x4*>(src + (size_t)sp * pstride);
+  return acc;
+}
 __global__ __launch_bounds__(256) void reduce_parts_kernel(const ReduceBatch batch) {
   constexpr int RB = kReduceRows;
   __shared__ float tile[RB * 129];
@@ -725,24 +742,33 @@ __global__ __launch_bounds__(256) void reduce_parts_kernel(const ReduceBatch bat
       sA[e] = cc < nc ? bf16_to_f32(p.Am[(size_t)l * p.lda + c0 + cc]) : 0.f;
     }
   }
-  for (int e4 = tid; e4 < RB * p.rp / 4; e4 += 256) {
-    const int e = e4 * 4;                           // element offset inside the [RB][rp] slice
-    const int cc = e / p.rp, j = e % p.rp;
+  const int E = RB * p.rp / 4;                     // float4 groups of the slice
+  const int T = (E < 256 && 256 % E == 0) ? 256 / E : 1;
+  if (T > 1) {
+    __shared__ f32x4 runs[256];
+    const int e4 = tid % E, t = tid / E;
+    const int e = e4 * 4, cc = e / p.rp, j = e % p.rp;
     f32x4 acc = {0, 0, 0, 0};
-    if (c0 + cc < C && j < R) {                     // columns >= R are padding (or another job's)
-      const float* src = p.part + (size_t)(c0 + cc) * p.rp + j;
-      int sp = 0;
-      for (; sp + 8 <= p.nsplit; sp += 8) {
-        f32x4 a[8];
+    if (c0 + cc < C && j < R)                       // columns >= R are padding (or another job's)
+      acc = sum_splits(p.part + (size_t)(c0 + cc) * p.rp + j, p.pstride, t * p.nsplit / T,
+                       (t + 1) * p.nsplit / T);
+    runs[tid] = acc;
+    __syncthreads();
+    if (tid < E) {
+      f32x4 v = runs[tid];
+      for (int u = 1; u < T; ++u) v += runs[u * E + tid];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) a[q] = *reinterpret_cast<const f32x4*>(src + (size_t)(sp + q) * p.pstride);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) acc += a[q];
-      }
-      for (; sp < p.nsplit; ++sp) acc += *reinterpret_cast<const f32x4*>(src + (size_t)sp * p.pstride);
+      for (int i = 0; i < 4; ++i) tile[cc * ld + j + i] = v[i];
     }
+  } else {
+    for (int e4 = tid; e4 < E; e4 += 256) {
+      const int e = e4 * 4;                         // element offset inside the [RB][rp] slice
+      const int cc = e / p.rp, j = e % p.rp;
+      f32x4 acc = {0, 0, 0, 0};
+      if (c0 + cc < C && j < R) acc = sum_splits(p.part + (size_t)(c0 + cc) * p.rp + j, p.pstride, 0, p.nsplit);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) tile[cc * ld + j + i] = acc[i];
+      for (int i = 0; i < 4; ++i) tile[cc * ld + j + i] = acc[i];
+    }
   }
   __syncthreads();
   for (int e = tid; e < R * RB; e += 256) {
