@@ -503,11 +503,13 @@ def main():
     # (the per-kernel timing events are created first, so that nothing idles the GPU between
     # the warm-up and the timed steps)
     K_steps = args.steps
-    evs = {k: (TimingEvents(K_steps), TimingEvents(K_steps)) for k in gemm_kinds}
+    # hook 2: the gated MLP backward's activation pass (dE, dGu from dH, E, Gu in place)
+    hook_kinds = tuple(gemm_kinds) + ((2,) if wl in ("swiglu", "geglu") else ())
+    evs = {k: (TimingEvents(K_steps), TimingEvents(K_steps)) for k in hook_kinds}
     for _ in range(args.warmup):
         step()
     keep = []
-    for k in gemm_kinds:
+    for k in hook_kinds:
         a, b = evs[k][0].arr, evs[k][1].arr
         keep.append((a, b))
         check(L.ldl_set_kernel_events(k, a, b, K_steps), "ldl_set_kernel_events")
@@ -518,7 +520,7 @@ def main():
         step()
     t_stop.record()
     torch.cuda.synchronize()
-    for k in gemm_kinds:
+    for k in hook_kinds:
         L.ldl_set_kernel_events(k, None, None, 0)
     ms = t_start.elapsed_time(t_stop) / K_steps
     value = flops / (ms * 1e-3) / 1e12
@@ -528,6 +530,15 @@ def main():
         times = [evs[k][0].elapsed_ms(evs[k][1], i) for i in range(K_steps)]
         avg = sum(times) / len(times)
         kern[k] = {"avg_us": avg * 1e3, "tflops": gemm_flops[k] / (avg * 1e-3) / 1e12}
+    act_pass = None
+    if 2 in hook_kinds:
+        # reads dH, E, Gu and writes dE, dGu: 10 bytes per hidden unit and token (bf16)
+        times = [evs[2][0].elapsed_ms(evs[2][1], i) for i in range(K_steps)]
+        avg = sum(times) / len(times)
+        nbytes = 10 * M * H
+        act_pass = {"kernel": "swiglu_bwd_kernel (dE, dGu in place over dH)", "avg_us": round(avg * 1e3, 2),
+                    "bytes": nbytes, "GB/s": round(nbytes / (avg * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(nbytes / (avg * 1e-3) / 1e9 / 8000.0, 4)}
 
     out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K_steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
@@ -560,6 +571,8 @@ def main():
                            "traffic": None if traffic is None else int(traffic)}
         out["kernels"] = {names[k]: {"avg_us": round(v["avg_us"], 2), "TFLOP/s": round(v["tflops"], 1)}
                           for k, v in kern.items()}
+    if act_pass is not None:
+        out["activation_pass"] = act_pass
     if wl == "lora" and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_lora(4096, 4096, 4096, 16, 0.5)
         out["cpu_baseline"].pop("seconds", None)

@@ -113,6 +113,8 @@ int ldl_set_tuning(int key, int value);
  * off.  The arrays must stay valid while the hook is set.
  *   kind 0: the base GEMM of the LoRA / DoRA / W8A8 forward (the [M,N] output GEMM)
  *   kind 1: the input-gradient GEMM of the LoRA / DoRA / W8A8 backward (the [M,K] dX GEMM)
+ *   kind 2: the gated MLP backward's activation pass (the streaming pass over dH, E and Gu
+ *           that writes dE and dGu; recorded only where that pass is a launch of its own)
  * Returns LDL_OK or LDL_E_INVAL. */
 int ldl_set_kernel_events(int kind, void** start_events, void** stop_events, int count);
 

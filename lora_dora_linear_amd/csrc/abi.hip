@@ -43,24 +43,17 @@ struct EventHook {
   int count = 0;
   int next = 0;
 };
-EventHook g_hooks[2];
+constexpr int kHooks = 3;
+EventHook g_hooks[kHooks];
 
 // Launch a GEMM; when a hook is set for `hook_kind`, bracket it with the caller's events.
 hipError_t gemm_timed(int hook_kind, GemmKind kind, const GemmParams& p, hipStream_t st) {
-  EventHook* h = (hook_kind >= 0 && hook_kind < 2) ? &g_hooks[hook_kind] : nullptr;
-  const bool rec = h && h->count > 0 && h->next < h->count;
-  if (rec) {
-    const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(h->start[h->next]), st);
-    if (e != hipSuccess) return e;
-  }
+  bool rec = false;
+  const hipError_t e0 = hook_start(hook_kind, st, &rec);
+  if (e0 != hipSuccess) return e0;
   const hipError_t e = launch_gemm(kind, p, st);
   if (e != hipSuccess) return e;
-  if (rec) {
-    const hipError_t e2 = hipEventRecord(static_cast<hipEvent_t>(h->stop[h->next]), st);
-    ++h->next;
-    return e2;
-  }
-  return hipSuccess;
+  return hook_stop(hook_kind, st, rec);
 }
 
 constexpr size_t kAlign = 256;
@@ -406,6 +399,21 @@ hipError_t f32(int M, int N, int K, const float* A, long sam, long sak, const fl
 
 }  // namespace
 
+// Start / stop of a timed launch: records the caller's events while the hook is set
+hipError_t ldl::hook_start(int hook_kind, hipStream_t st, bool* rec) {
+  EventHook* h = (hook_kind >= 0 && hook_kind < kHooks) ? &g_hooks[hook_kind] : nullptr;
+  *rec = h && h->count > 0 && h->next < h->count;
+  return *rec ? hipEventRecord(static_cast<hipEvent_t>(h->start[h->next]), st) : hipSuccess;
+}
+hipError_t ldl::hook_stop(int hook_kind, hipStream_t st, bool rec) {
+  if (!rec) return hipSuccess;
+  EventHook* h = &g_hooks[hook_kind];
+  const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(h->stop[h->next]), st);
+  ++h->next;
+  return e;
+}
+
+
 extern "C" {
 
 const char* ldl_status_string(int status) {
@@ -422,7 +430,7 @@ const char* ldl_status_string(int status) {
 int ldl_version(void) { return 100; }
 
 int ldl_set_kernel_events(int kind, void** start_events, void** stop_events, int count) {
-  if (kind < 0 || kind > 1 || count < 0) return LDL_E_INVAL;
+  if (kind < 0 || kind >= kHooks || count < 0) return LDL_E_INVAL;
   if (count > 0 && (!start_events || !stop_events)) return LDL_E_INVAL;
   g_hooks[kind].start = count > 0 ? start_events : nullptr;
   g_hooks[kind].stop = count > 0 ? stop_events : nullptr;

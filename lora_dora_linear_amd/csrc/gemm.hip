@@ -333,8 +333,11 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st) {
     GemmParams h;
     if (swb_split(p, h)) {
       hipError_t e = launch_gemm(GK_NN_PLAIN, h, st);
+      bool rec = false;
+      if (e == hipSuccess) e = hook_start(2, st, &rec);
       if (e == hipSuccess)
         e = launch_swiglu_bwd(p.out, p.ldo, p.aux0, p.ld_aux0, p.aux1, p.ld_aux1, p.out2, p.ldo2, p.M, p.N, p.act, st);
+      if (e == hipSuccess) e = hook_stop(2, st, rec);
       return e;
     }
   }

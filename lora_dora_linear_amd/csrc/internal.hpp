@@ -55,6 +55,9 @@ enum GemmKind : int {
   GK_NT_F8_DEQ   // e4m3 P and Q, dequantised by row_scale[m] col_scale[n], + low-rank term (+ bias)
 };
 hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t st);
+// timing hook of ldl_set_kernel_events around one launch (rec: whether events were recorded)
+hipError_t hook_start(int hook_kind, hipStream_t st, bool* rec);
+hipError_t hook_stop(int hook_kind, hipStream_t st, bool rec);
 extern int g_gemm_4wave;   // plain bf16 GEMMs on the four-wave 16x16x32 tile (tuning switch)
 bool gemm_shape_ok(GemmKind kind, int M, int N, int K);
 bool gemm_multi_leaf_ok(const GemmParams& p);
