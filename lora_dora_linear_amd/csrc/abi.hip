@@ -158,7 +158,7 @@ DoraColsFwdWs plan_dora_cols_fwd(Bump& b, int M, int N, int K, int r) {
 }
 
 struct DoraColsBwdWs {
-  uint16_t* dXs; void* lora; size_t lora_bytes; float* partD; float* csD; float* dg; uint16_t* Aw; float* T;
+  uint16_t* dXs; void* lora; size_t lora_bytes; float* partD; float* csD; uint16_t* Aw; float* T;
   int nsD, msD;
 };
 DoraColsBwdWs plan_dora_cols_bwd(Bump& b, int M, int N, int K, int r) {
@@ -171,7 +171,6 @@ DoraColsBwdWs plan_dora_cols_bwd(Bump& b, int M, int N, int K, int r) {
   w.lora = b.take<uint8_t>(w.lora_bytes);
   w.partD = b.take<float>((size_t)w.nsD * K * 16);
   w.csD = b.take<float>((size_t)w.nsD * K);
-  w.dg = b.take<float>((size_t)K);
   w.Aw = b.take<uint16_t>((size_t)2 * r * K);
   w.T = b.take<float>((size_t)(N + r) * 2 * r);
   return w;
@@ -322,12 +321,20 @@ ColProjParams cpp(int M, int C, int R, const void* X, int ldx, const float* Sm, 
   p.Z = static_cast<const uint16_t*>(Z); p.ldz = ldz; p.colsum_mode = mode;
   p.msplit = msplit; p.part = part; p.cspart = cspart;
   p.spk = nullptr;
+  p.S16 = nullptr;
   return p;
 }
 
 // the same job with its packed-S workspace
 ColProjParams pk(ColProjParams p, uint32_t* spk) {
   p.spk = spk;
+  return p;
+}
+
+// the same job reading its S operand in bf16 (row stride unchanged)
+ColProjParams s16(ColProjParams p, const void* S16) {
+  p.S = nullptr;
+  p.S16 = static_cast<const uint16_t*>(S16);
   return p;
 }
 
@@ -1110,11 +1117,16 @@ int dora_cols_linear_fwd(int M, int N, int K, int r, float s, float eps, int dty
   float* Gc = Pc + (size_t)K * r;
   // the norm terms Pc = B^T.W0 and Gc = B^T.B (one column-projection launch over the rows of
   // W0 and of B against B), then nu and g (independent of M)
-  LDL_TRY(launch_bf16_to_f32(B, (size_t)N * r, w.Bf, st));
   {
     ColProjParams jobs[2] = {pk(cpp(N, K, r, W0, ldw, w.Bf, r, 1.f, nullptr, 0, 0, w.msP, w.partP, nullptr), w.pkP),
                              pk(cpp(N, r, r, B, r, w.Bf, r, 1.f, nullptr, 0, 0, w.msG, w.partG, nullptr), w.pkG)};
     int ns[2] = {w.nsP, w.nsG};
+    if (colproj_takes_bf16_s(jobs, 2)) {         // B packed from bf16 directly
+      jobs[0] = s16(jobs[0], B);
+      jobs[1] = s16(jobs[1], B);
+    } else {
+      LDL_TRY(launch_bf16_to_f32(B, (size_t)N * r, w.Bf, st));
+    }
     LDL_TRY(launch_colproj_batch(jobs, ns, 2, st));
   }
   LDL_TRY(launch_reduce2(rdp(r, K, w.partP, (size_t)K * w.rp, w.nsP, w.rp, true, 1.f, Pc, K),
@@ -1188,16 +1200,15 @@ int dora_cols_linear_bwd(int M, int N, int K, int r, float s, float eps, int dty
     LDL_TRY(launch_reduce2(rdp(N, r, lw.partB, (size_t)N * lw.rp, lw.nsB, lw.rp, false, s, dB, r),
                            rdp(r, K, lw.partA, (size_t)K * lw.rp, lw.nsA, lw.rp, true, s, dA, K), st));
     if (dbias) LDL_TRY(launch_reduce_colsum(lw.csB, lw.nsB, N, dbias, st));
-    LDL_TRY(launch_reduce_colsum(w.csD, w.nsD, K, w.dg, st));
   } else {
     LDL_TRY(zero(dA, (size_t)r * K, st));
     LDL_TRY(zero(dB, (size_t)N * r, st));
     LDL_TRY(zero(dbias, (size_t)N, st));
-    LDL_TRY(zero(w.dg, (size_t)K, st));
   }
   // dm, and the norm's terms: dA += 2s (Pc + s.Gc.A).diag(w); dB += 2s W0.diag(w).A^T +
   // 2s^2 B.(A.diag(w).A^T), the two products over K as one row projection of [W0; A]
-  LDL_TRY(launch_dora_cols_bwd(K, r, s, eps, w.dg, norm, m, A, Pc, Gc, dm, dA, w.Aw, st));
+  // (dg_k: the split column sums of dXs.X, summed in split order by the same launch; none at M = 0)
+  LDL_TRY(launch_dora_cols_bwd(K, r, s, eps, w.csD, M > 0 ? w.nsD : 0, norm, m, A, Pc, Gc, dm, dA, w.Aw, st));
   LDL_TRY(rowproj2(N, r, K, 2 * r, W0, ldw, A, K, w.Aw, K, w.T, 2 * r, 1.f, st));
   LDL_TRY(launch_dora_cols_db(N, r, s, B, w.T, dB, st));
   return LDL_OK;

@@ -101,17 +101,32 @@ __global__ __launch_bounds__(256) void dora_cols_norm_kernel(int K, int r, float
 //   dm_k = dg_k / max(nu_k, eps);  w_k = -dg_k m_k / (2 nu_k^3) (0 where nu_k <= eps);
 //   dA[:,k] += 2s w_k (Pc[:,k] + s Gc A[:,k]);
 //   Aw = A.diag(w) as bf16 hi ([0, r) rows) and lo ([r, 2r) rows) for the dB products.
-__global__ __launch_bounds__(256) void dora_cols_bwd_kernel(int K, int r, float s, float eps, const float* dg,
-                                                            const float* norm, const float* m, const uint16_t* A,
+__global__ __launch_bounds__(256) void dora_cols_bwd_kernel(int K, int r, float s, float eps, const float* dg_part,
+                                                            int dg_nsplit, const float* norm, const float* m,
+                                                            const uint16_t* A,
                                                             const float* Pc, const float* Gc, float* dm, float* dA,
                                                             uint16_t* Aw) {
   __shared__ float sa[64][kColBlk];
   __shared__ float sg[64 * 64];
   const int k0 = blockIdx.x * kColBlk, c = threadIdx.x % kColBlk, q = threadIdx.x / kColBlk, k = k0 + c;
+  // dg_k: the split partial sums in split order, eight loads in flight, issued before the
+  // staging so that their latency overlaps it
+  float d = 0.f;
+  if (k < K) {
+    int sp = 0;
+    for (; sp + 8 <= dg_nsplit; sp += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = dg_part[(size_t)(sp + u) * K + k];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) d += v[u];
+    }
+    for (; sp < dg_nsplit; ++sp) d += dg_part[(size_t)sp * K + k];
+  }
   stage_cols(A, Gc, K, r, k0, sa, sg);
   __syncthreads();
   if (k >= K) return;
-  const float nu = norm[k], d = dg[k];
+  const float nu = norm[k];
   if (q == 0) dm[k] = d / fmaxf(nu, eps);
   const float w = nu > eps ? -d * m[k] / (2.f * nu * nu * nu) : 0.f;
   for (int j = q; j < r; j += kRankGroups) {
@@ -170,12 +185,12 @@ hipError_t launch_dora_cols_norm(int K, int r, float s, float eps, const float* 
   return hipGetLastError();
 }
 
-hipError_t launch_dora_cols_bwd(int K, int r, float s, float eps, const float* dg, const float* norm, const float* m,
-                                const void* A, const float* Pc, const float* Gc, float* dm, float* dA, void* Aw,
-                                hipStream_t st) {
+hipError_t launch_dora_cols_bwd(int K, int r, float s, float eps, const float* dg_part, int dg_nsplit,
+                                const float* norm, const float* m, const void* A, const float* Pc, const float* Gc,
+                                float* dm, float* dA, void* Aw, hipStream_t st) {
   if (r > 64) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(dora_cols_bwd_kernel, dim3((K + kColBlk - 1) / kColBlk), dim3(256), 0, st, K, r, s, eps, dg,
-                     norm, m, static_cast<const uint16_t*>(A), Pc, Gc, dm, dA, static_cast<uint16_t*>(Aw));
+  hipLaunchKernelGGL(dora_cols_bwd_kernel, dim3((K + kColBlk - 1) / kColBlk), dim3(256), 0, st, K, r, s, eps,
+                     dg_part, dg_nsplit, norm, m, static_cast<const uint16_t*>(A), Pc, Gc, dm, dA, static_cast<uint16_t*>(Aw));
   return hipGetLastError();
 }
 

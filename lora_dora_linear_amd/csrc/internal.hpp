@@ -34,6 +34,8 @@ struct ColProjParams {
   float* cspart;                   // [nsplit][C]
   uint32_t* spk;                   // workspace for S pre-split into bf16 hi / lo fragments,
                                    // colproj_spk_words(M, R) words (used from rank 32 up)
+  const uint16_t* S16;             // optional: S given in bf16 (row stride lds) instead of fp32;
+                                   // only where colproj_takes_bf16_s says so
 };
 
 struct ReduceParams {
@@ -68,6 +70,8 @@ size_t gemm_split_bytes(int M, int N);
 hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st);
 bool rowproj_three_ok(const RowProjParams& p);   // the streamed kernel takes P2
 int colproj_rp(int R);
+// whether a column-projection batch runs on the packed streaming path, which can read S in bf16
+bool colproj_takes_bf16_s(const ColProjParams* jobs, int njobs);
 extern int g_rowstream32;   // rank 33..128 row projections on 32-row blocks: 0 never, 1 auto, 2 always
 // size in 32-bit words of the packed S a column projection of M rows and rank R needs
 size_t colproj_spk_words(int M, int R);
@@ -112,9 +116,9 @@ hipError_t launch_col_sumsq(const void* W0, int bf16, int N, int K, int ldw, flo
 hipError_t launch_dora_cols_norm(int K, int r, float s, float eps, const float* colsq, const float* m,
                                  const void* A, const float* Pc, const float* Gc, float* norm, float* g,
                                  hipStream_t st);
-hipError_t launch_dora_cols_bwd(int K, int r, float s, float eps, const float* dg, const float* norm, const float* m,
-                                const void* A, const float* Pc, const float* Gc, float* dm, float* dA, void* Aw,
-                                hipStream_t st);
+hipError_t launch_dora_cols_bwd(int K, int r, float s, float eps, const float* dg_part, int dg_nsplit,
+                                const float* norm, const float* m, const void* A, const float* Pc, const float* Gc,
+                                float* dm, float* dA, void* Aw, hipStream_t st);
 hipError_t launch_dora_cols_db(int N, int r, float s, const void* B, const float* T, float* dB, hipStream_t st);
 hipError_t launch_mask_cols(const void* in, const uint8_t* keep, int rows, int K, int esz, void* out, hipStream_t st);
 

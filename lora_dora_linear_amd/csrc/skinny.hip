@@ -877,6 +877,7 @@ size_t colproj_spk_words(int M, int R) { return M > 0 && R > 0 ? (size_t)((M + 7
 // g * 2RP + RP + j.  One thread per (g, j); blockIdx.y selects the job.
 struct PackSBatch {
   const float* S[kColProjBatch];
+  const uint16_t* S16[kColProjBatch];              // bf16 S where set (S unused)
   int lds[kColProjBatch], M[kColProjBatch], R[kColProjBatch];
   float s_in[kColProjBatch];
   uint32_t* out[kColProjBatch];
@@ -895,8 +896,14 @@ __global__ __launch_bounds__(256) void pack_s_kernel(const PackSBatch b) {
     const int m0 = 8 * g + 2 * e;
     float v0 = 0.f, v1 = 0.f;
     if (j < R) {
-      if (m0 < M) v0 = b.S[job][(size_t)m0 * b.lds[job] + j] * b.s_in[job];
-      if (m0 + 1 < M) v1 = b.S[job][(size_t)(m0 + 1) * b.lds[job] + j] * b.s_in[job];
+      const uint16_t* s16 = b.S16[job];
+      if (s16 != nullptr) {
+        if (m0 < M) v0 = bf16_to_f32(s16[(size_t)m0 * b.lds[job] + j]) * b.s_in[job];
+        if (m0 + 1 < M) v1 = bf16_to_f32(s16[(size_t)(m0 + 1) * b.lds[job] + j]) * b.s_in[job];
+      } else {
+        if (m0 < M) v0 = b.S[job][(size_t)m0 * b.lds[job] + j] * b.s_in[job];
+        if (m0 + 1 < M) v1 = b.S[job][(size_t)(m0 + 1) * b.lds[job] + j] * b.s_in[job];
+      }
     }
     const uint32_t h0 = f32_to_bf16_bits(v0), h1 = f32_to_bf16_bits(v1);
     hi[e] = h0 | (h1 << 16);
@@ -912,7 +919,7 @@ static hipError_t pack_s_launch(const ColProjParams* jobs, int njobs, int RP, hi
   int nj = 0, maxt = 0;
   for (int i = 0; i < njobs; ++i) {
     if (jobs[i].R <= 0 || jobs[i].M <= 0) continue;
-    b.S[nj] = jobs[i].S; b.lds[nj] = jobs[i].lds; b.M[nj] = jobs[i].M; b.R[nj] = jobs[i].R;
+    b.S[nj] = jobs[i].S; b.S16[nj] = jobs[i].S16; b.lds[nj] = jobs[i].lds; b.M[nj] = jobs[i].M; b.R[nj] = jobs[i].R;
     b.s_in[nj] = jobs[i].s_in; b.out[nj] = jobs[i].spk;
     const int tcount = ((jobs[i].M + 7) / 8) * RP;
     if (tcount > maxt) maxt = tcount;
@@ -1015,11 +1022,13 @@ hipError_t launch_colproj_batch(const ColProjParams* jobs, const int* nsplit, in
     b.first[i + 1] = b.first[i] + (i < njobs ? nsplit[i] : 0);
     if (i < njobs && jobs[i].C > maxc) maxc = jobs[i].C;
   }
-  bool stream = true, hasz = false;
+  bool stream = true, hasz = false, s16 = false;
   for (int i = 0; i < njobs; ++i) {
     stream = stream && colstream_ok(jobs[i]);
     hasz = hasz || jobs[i].colsum_mode == 1;
+    s16 = s16 || jobs[i].S16 != nullptr;
   }
+  if (s16 && !colproj_takes_bf16_s(jobs, njobs)) return hipErrorInvalidValue;
   if (stream && colproj_rp(jobs[0].R) <= 64) {      // rank 128: the register-transposing kernel is faster
     if (colproj_rp(jobs[0].R) >= 32) {
       const hipError_t e = pack_s_launch(jobs, njobs, colproj_rp(jobs[0].R), st);
@@ -1029,6 +1038,15 @@ hipError_t launch_colproj_batch(const ColProjParams* jobs, const int* nsplit, in
                 : colstream_launch<false>(b, (maxc + 63) / 64, b.first[njobs], jobs[0].R, st);
   }
   return colproj_launch(b, (maxc + 63) / 64, b.first[njobs], jobs[0].R, st);
+}
+
+bool colproj_takes_bf16_s(const ColProjParams* jobs, int njobs) {
+  if (njobs < 1 || njobs > kColProjBatch) return false;
+  const int rp = colproj_rp(jobs[0].R);
+  if (rp < 32 || rp > 64) return false;              // packed streaming path: rank 17 .. 64
+  for (int i = 0; i < njobs; ++i)
+    if (colproj_rp(jobs[i].R) != rp || !colstream_ok(jobs[i])) return false;
+  return true;
 }
 
 hipError_t launch_colproj(const ColProjParams& p, int nsplit, hipStream_t st) {

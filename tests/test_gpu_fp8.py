@@ -117,9 +117,10 @@ def test_fp8_base_only_and_no_dx():
                  TOL, "Y base")
 
 
-@pytest.mark.parametrize("M", [1024, 4096])
+@pytest.mark.parametrize("M", [1024, 2048, 4096, 8192, 16384])
 def test_fp8_full_size_sampled(M):
-    """K = N = 5120, r = 32, s = 0.5: sampled rows and gradient entries."""
+    """K = N = 5120, r = 32, s = 0.5, every token count of the sweep (tails split three, four
+    and two ways over k at 1024, 4096 and 8192 tokens): sampled rows and gradient entries."""
     require_gpu()
     c, W0f = _case(M, 5120, 5120, 32)
     Y, Xq, sx, g = _run(c, W0f, with_bias=False)
