@@ -75,11 +75,12 @@ static void plan_split(GemmParams& p, int tiles, int kt) {
   p.split_first = full;
 }
 
-// blockIdx.x = 64 t + c: remaining tile split_first + t, f32x4 slots 256 c .. 256 c + 255 of
-// the lane-linear partial layout of wave (wm, wn) = (wave >> 1, wave & 1).  16x16 blocks
-// (L32 = 0): slot ((wave 8 + i) 8 + j) 64 + lane holds row 16 i + (lane & 15), the four columns
-// 16 j + 4 (lane >> 4) ..  32x32 blocks (L32 = 1): slot (((wave 4 + i) 4 + j) 4 + q) 64 + lane
-// holds row 32 i + (lane & 31), columns 32 j + 8 q + 4 (lane >> 5) ..
+// blockIdx.x = 64 * t + c: remaining tile split_first + t, f32x4 slots 256 * c .. 256 * c + 255
+// of the lane-linear partial layout of wave (wm, wn) = (wave >> 1, wave & 1).  16x16 blocks
+// (L32 = 0): slot ((wave * 8 + i) * 8 + j) * 64 + lane holds row 16 * i + (lane & 15) and the
+// four columns from 16 * j + 4 * (lane >> 4).  32x32 blocks (L32 = 1): slot
+// (((wave * 4 + i) * 4 + j) * 4 + q) * 64 + lane holds row 32 * i + (lane & 31) and the four
+// columns from 32 * j + 8 * q + 4 * (lane >> 5).
 template <bool L32>
 __global__ __launch_bounds__(256) void split_fixup_kernel(const GemmParams p) {
   const int t = blockIdx.x >> 6, slot = (blockIdx.x & 63) * 256 + threadIdx.x;
