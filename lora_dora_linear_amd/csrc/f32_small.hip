@@ -106,6 +106,15 @@ __global__ __launch_bounds__(256) void f32_small_fwd_kernel(const F32SmallFwd p)
   const float* xr = p.X + (size_t)(vm ? m0 + lr : 0) * p.ldx;
   const float* wr = p.W0 + (size_t)(vn ? n0 + lr : 0) * p.ldw;
   const float* ar = p.A + (size_t)(vj ? lr : 0) * p.K;
+  // the rank slab of B and the bias, loaded before the reduction so that their latency
+  // overlaps it (r <= 16: four rank groups of four)
+  float bv[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int j = 4 * c + q;
+    bv[c] = (vn && j < p.r) ? p.B[(size_t)(n0 + lr) * p.r + j] : 0.f;
+  }
+  const float bn = (p.bias != nullptr && vn) ? p.bias[n0 + lr] : 0.f;
   f32x4 accY = kZero4, accU = kZero4;
   const int kq = p.K / 4;
   reduce_q<true>(wave * kq, (wave + 1) * kq, q, [&](int k) { return vm ? ld4(xr + k) : kZero4; },
@@ -125,14 +134,10 @@ __global__ __launch_bounds__(256) void f32_small_fwd_kernel(const F32SmallFwd p)
   }
   // + (s.U).B^T: s.U as the row operand (rank = reduction index) through LDS
   to_lds(su, accU, p.s, q, lr);
-  for (int c = 0; 4 * c < p.r; ++c) {
-    const int j = 4 * c + q;
-    const float a = su[lr][j];
-    const float b = (vn && j < p.r) ? p.B[(size_t)(n0 + lr) * p.r + j] : 0.f;
-    accY = mfma4(a, b, accY);
-  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (4 * c < p.r) accY = mfma4(su[lr][4 * c + q], bv[c], accY);
   if (!vn) return;
-  const float bn = p.bias != nullptr ? p.bias[n0 + lr] : 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (m0 + 4 * q + i < p.M) p.Y[(size_t)(m0 + 4 * q + i) * p.ldy + n0 + lr] = accY[i] + bn;
@@ -171,6 +176,12 @@ __global__ __launch_bounds__(256) void f32_small_bwd_kernel(const F32SmallBwd p)
     const float* dyr = p.dY + (size_t)(vm ? m0 + lr : 0) * p.lddy;
     const float* wc = p.W0 + c0 + (vc ? lr : 0);
     const float* bc = p.B + (vj ? lr : 0);
+    float av[4];                               // A's rank rows at the tile's columns, prefetched
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = 4 * c + q;
+      av[c] = (vc && j < p.r) ? p.A[(size_t)j * p.K + c0 + lr] : 0.f;
+    }
     f32x4 accX = kZero4, accV = kZero4;
     const int nq = p.N / 4;
     reduce_q<true>(wave * nq, (wave + 1) * nq, q, [&](int n) { return vm ? ld4(dyr + n) : kZero4; },
@@ -183,12 +194,9 @@ __global__ __launch_bounds__(256) void f32_small_bwd_kernel(const F32SmallBwd p)
     accX = wave_sum4(part[0], lane);
     accV = wave_sum4(part[1], lane);
     to_lds(t, accV, p.s, q, lr);
-    for (int c = 0; 4 * c < p.r; ++c) {
-      const int j = 4 * c + q;
-      const float a = t[lr][j];
-      const float b = (vc && j < p.r) ? p.A[(size_t)j * p.K + c0 + lr] : 0.f;
-      accX = mfma4(a, b, accX);
-    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (4 * c < p.r) accX = mfma4(t[lr][4 * c + q], av[c], accX);
     if (!vc) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -206,6 +214,12 @@ __global__ __launch_bounds__(256) void f32_small_bwd_kernel(const F32SmallBwd p)
     for (int m0 = wave * 16; m0 < p.M; m0 += 64) {
       const bool vm = m0 + lr < p.M;
       const float* dyr = p.dY + (size_t)(vm ? m0 + lr : 0) * p.lddy;
+      float xv[4];                             // X[m][c0 + lr] of the block's rows, prefetched
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int mm = 4 * c + q;
+        xv[c] = (vc && m0 + mm < p.M) ? p.X[(size_t)(m0 + mm) * p.ldx + c0 + lr] : 0.f;
+      }
       f32x4 accV = kZero4, unused = kZero4;
       reduce_q<false>(0, p.N, q, [&](int n) { return vm ? ld4(dyr + n) : kZero4; },
                       [&](int n) { return vj ? ld4s(bc + (size_t)n * p.r, p.r) : kZero4; },
@@ -214,12 +228,7 @@ __global__ __launch_bounds__(256) void f32_small_bwd_kernel(const F32SmallBwd p)
       // row operand: (s.V)^T (rank lr, reduction index = row 4 c + q of the block); column
       // operand: X[m][c0 + lr]
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int mm = 4 * c + q;
-        const float a = t[mm][lr];
-        const float b = (vc && m0 + mm < p.M) ? p.X[(size_t)(m0 + mm) * p.ldx + c0 + lr] : 0.f;
-        accA = mfma4(a, b, accA);
-      }
+      for (int c = 0; c < 4; ++c) accA = mfma4(t[4 * c + q][lr], xv[c], accA);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // (the tile is rewritten next)
     }
     part[0][wave][lane] = accA;
