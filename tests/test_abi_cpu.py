@@ -96,6 +96,17 @@ def test_tuning_switch(L):
     assert L.ldl_set_tuning(2, 3) == INVAL
 
 
+def test_kernel_event_hook_arguments(L):
+    """Kinds 0 (forward GEMM), 1 (input-gradient GEMM) and 2 (gated-MLP activation pass) take
+    a hook; turning one off (count 0, no arrays) records nothing and needs no GPU."""
+    for kind in (0, 1, 2):
+        assert L.ldl_set_kernel_events(kind, None, None, 0) == OK
+    assert L.ldl_set_kernel_events(3, None, None, 0) == INVAL
+    assert L.ldl_set_kernel_events(-1, None, None, 0) == INVAL
+    assert L.ldl_set_kernel_events(0, None, None, -1) == INVAL
+    assert L.ldl_set_kernel_events(2, None, None, 4) == INVAL      # events missing
+
+
 # fake, 256-aligned, never dereferenced: every call below fails validation first
 P = ctypes.c_void_p(0x100000)
 P2 = ctypes.c_void_p(0x200000)
