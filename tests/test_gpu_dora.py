@@ -50,6 +50,28 @@ def test_dora_parity(M, N, K, r, s):
     assert_close(host(g["dbias"]), gr["db"], 1e-5, "dbias")
 
 
+def test_dora_rank64_norm_terms_and_u_in_one_row_launch():
+    """r = 64 with N + r + M = 8256 rows: P = W0.A^T, G = A.A^T and U = X.A^T run as one
+    row-projection launch on 32-row blocks (three row segments, each a multiple of 32)."""
+    require_gpu()
+    eps = 1e-12
+    M, N, K, r = 4096, 4096, 256, 64
+    c = inputs.linear_case(7, M, N, K, r, 1.0, "bf16", dora=True)
+    import lora_dora_linear_amd as L
+    X, W0, A, B, dY = (dev(c.t[k], "bf16") for k in ("X", "W0", "A", "B", "dY"))
+    m = dev(c.t["m"], "f32")
+    c0 = L.dora_prepare(W0)
+    Y, U, Z, state = L.dora_linear_fwd(X, W0, A, B, m, c0, c.s, eps)
+    g = L.dora_linear_bwd(dY, X, W0, A, B, m, U, Z, state, c.s, eps)
+    torch.cuda.synchronize()
+    f, gr = _oracle(c, eps)
+    assert_close(host(U), c.f64("X") @ c.f64("A").T, 1e-5, "U")
+    assert_close(host(state[:N]), f["nu"], 1e-5, "norm")
+    assert_close(host(Y), f["Y"], TOL, "Y")
+    for k in ("dX", "dA", "dB", "dm"):
+        assert_close(host(g[k]), gr[k], TOL, k)
+
+
 def test_dora_unit_scale_is_base():
     """B = 0 and m = ||W0_n||: g = 1 and Y = X.W0^T."""
     require_gpu()
