@@ -318,6 +318,7 @@ def main():
         return
     gemm_kinds = (0, 1)
     gemm_flops = {}
+    prep = None          # (call, kernel, bytes): a one-time preparation timed apart from the step
     if wl == "lora":
         M, N, K, r, s = 4096, 4096, 4096, 16, 0.5
         c = inputs.linear_case(2, M, N, K, r, s, "bf16")
@@ -346,7 +347,9 @@ def main():
         X, W0, A, B, dY = (up(c.t[k], "bf16") for k in ("X", "W0", "A", "B", "dY"))
         m = up(c.t["m"], "f32")
         w0sq = torch.empty((N,), dtype=f32, device=dev)
-        check(L.dora_prepare(N, K, 1, P(W0), K, P(w0sq), st()), "dora_prepare")
+        prep = (lambda: check(L.dora_prepare(N, K, 1, P(W0), K, P(w0sq), st()), "dora_prepare"),  # noqa: E731
+                "rowsumsq_kernel (cached rowsum(W0^2), once per frozen weight)", 2.0 * N * K + 4.0 * N)
+        prep[0]()
         Y = torch.empty((M, N), dtype=bf, device=dev)
         Z = torch.empty((M, N), dtype=bf, device=dev)
         U = torch.empty((M, r), dtype=f32, device=dev)
@@ -376,7 +379,9 @@ def main():
         X, W0, A, B, dY = (up(c.t[k], "bf16") for k in ("X", "W0", "A", "B", "dY"))
         m = up(c.t["m"], "f32")
         w0sq = torch.empty((K,), dtype=f32, device=dev)
-        check(L.dora_cols_prepare(N, K, 1, P(W0), K, P(w0sq), st()), "dora_cols_prepare")
+        prep = (lambda: check(L.dora_cols_prepare(N, K, 1, P(W0), K, P(w0sq), st()), "dora_cols_prepare"),  # noqa
+                "col_sumsq_kernel (cached column sums of W0^2, once per frozen weight)", 2.0 * N * K + 4.0 * K)
+        prep[0]()
         Y = torch.empty((M, N), dtype=bf, device=dev)
         Xs = torch.empty((M, K), dtype=bf, device=dev)
         U = torch.empty((M, r), dtype=f32, device=dev)
@@ -573,6 +578,18 @@ def main():
                           for k, v in kern.items()}
     if act_pass is not None:
         out["activation_pass"] = act_pass
+    if prep is not None:
+        # not part of the step: once per frozen weight; timed here over 20 calls
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        prep[0]()
+        p0.record()
+        for _ in range(20):
+            prep[0]()
+        p1.record()
+        torch.cuda.synchronize()
+        us = p0.elapsed_time(p1) / 20 * 1e3
+        out["prepare"] = {"kernel": prep[1], "us": round(us, 2), "bytes": int(prep[2]),
+                          "GB/s": round(prep[2] / (us * 1e-6) / 1e9, 1)}
     if wl == "lora" and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_lora(4096, 4096, 4096, 16, 0.5)
         out["cpu_baseline"].pop("seconds", None)
