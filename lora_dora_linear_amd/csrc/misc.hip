@@ -110,14 +110,30 @@ __global__ __launch_bounds__(256) void dora_finalize_kernel(int N, int r, float 
   const int n = min(row, N - 1);                 // rows past N redo row N-1, unstored
   const bool live = row < N;
   const bool h0 = lane < r, h1 = lane + 64 < r;
-  // loads first (their latency overlaps the staging of G): the split partials of dg and of
-  // T for the lane's ranks, eight splits in flight, each sum in split order
+  // loads first (their latency overlaps the staging of G): the row's own operands, then the
+  // split partials of dg and of T for the lane's ranks, eight splits in flight, each sum in
+  // split order
+  const uint16_t* bn = B + (size_t)n * r;
+  const float b0 = h0 ? bf16_to_f32(bn[lane]) : 0.f, b1 = h1 ? bf16_to_f32(bn[lane + 64]) : 0.f;
+  const float p0 = h0 ? P[(size_t)n * r + lane] : 0.f, p1 = h1 ? P[(size_t)n * r + lane + 64] : 0.f;
+  const float nu = norm[n], gn = g[n], mn = m[n];
   float dg = 0.f, t0 = 0.f, t1 = 0.f;
   {
     const float* cp = cspart + n;
     const float* tp = partT + (size_t)n * rpT + lane;
     const size_t ts = (size_t)N * rpT;
     int sp = 0;
+    for (; sp + 16 <= nsplit; sp += 16) {        // sixteen splits in flight
+      float c8[16], a8[16], b8[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        c8[q] = cp[(size_t)(sp + q) * N];
+        a8[q] = h0 ? tp[(sp + q) * ts] : 0.f;
+        b8[q] = h1 ? tp[(sp + q) * ts + 64] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) { dg += c8[q]; t0 += a8[q]; t1 += b8[q]; }
+    }
     for (; sp + 8 <= nsplit; sp += 8) {
       float c8[8], a8[8], b8[8];
 #pragma unroll
@@ -135,10 +151,6 @@ __global__ __launch_bounds__(256) void dora_finalize_kernel(int N, int r, float 
       if (h1) t1 += tp[sp * ts + 64];
     }
   }
-  const uint16_t* bn = B + (size_t)n * r;
-  const float b0 = h0 ? bf16_to_f32(bn[lane]) : 0.f, b1 = h1 ? bf16_to_f32(bn[lane + 64]) : 0.f;
-  const float p0 = h0 ? P[(size_t)n * r + lane] : 0.f, p1 = h1 ? P[(size_t)n * r + lane + 64] : 0.f;
-  const float nu = norm[n], gn = g[n], mn = m[n];
   stage_g(sG, G, r);
   const float den = fmaxf(nu, eps);
   if (lane == 0 && live) dm[n] = dg / den;
