@@ -262,6 +262,7 @@ hipError_t rowproj(int M, int K, int R, const void* P, int ldp, const void* q0, 
   p.q_trans = 0; p.q_kscale = nullptr;
   p.out = out; p.ldo = ldo; p.scale = scale;
   p.P2 = nullptr; p.p_split2 = p.M; p.ldp2 = ldp; p.out2 = nullptr; p.ldo2 = 0;
+  p.pk = nullptr; p.pk_rp = 0; p.pk_scale = 1.f;
   return launch_rowproj(p, st);
 }
 
@@ -276,6 +277,7 @@ hipError_t rowproj2(int M0, int M1, int K, int R, const void* P, int ldp, const 
   p.q_trans = 0; p.q_kscale = nullptr;
   p.out = out; p.ldo = ldo; p.scale = scale;
   p.P2 = nullptr; p.p_split2 = p.M; p.ldp2 = ldp; p.out2 = nullptr; p.ldo2 = 0;
+  p.pk = nullptr; p.pk_rp = 0; p.pk_scale = 1.f;
   return launch_rowproj(p, st);
 }
 
@@ -292,10 +294,29 @@ hipError_t rowproj3(int M0, int M1, int M2, int K, int R, const void* P, int ldp
   p.q_trans = 0; p.q_kscale = nullptr;
   p.out = out; p.ldo = ldo; p.scale = 1.f;
   p.P2 = static_cast<const uint16_t*>(P2); p.p_split2 = M0 + M1; p.ldp2 = ldp2; p.out2 = out2; p.ldo2 = ldo2;
+  p.pk = nullptr; p.pk_rp = 0; p.pk_scale = 1.f;
   if (M2 > 0 && rowproj_three_ok(p)) return launch_rowproj(p, st);
   const hipError_t e = rowproj2(M0, M1, K, R, P, ldp, P1, ldp1, q0, ldq, out, ldo, 1.f, st);
   if (e != hipSuccess || M2 == 0) return e;
   return rowproj(M2, K, R, P2, ldp2, q0, nullptr, R, ldq, out2, ldo2, 1.f, st);
+}
+
+// rowproj_t with no k-scale that also writes pk_scale * out packed for a column projection of
+// rank padding pk_rp, where the streamed kernel takes it (*packed says whether it did)
+hipError_t rowproj_t_pk(int M, int K, int R, const void* P, int ldp, const void* Bq, int ldb, float* out, int ldo,
+                        uint16_t* pk, int pk_rp, float pk_scale, bool* packed, hipStream_t st) {
+  RowProjParams p;
+  p.M = M; p.K = K; p.R = R; p.R0 = R;
+  p.P = static_cast<const uint16_t*>(P); p.ldp = ldp;
+  p.P1 = nullptr; p.p_split = M; p.ldp1 = ldp;
+  p.q0 = p.q1 = static_cast<const uint16_t*>(Bq); p.ldq = ldb;
+  p.q_trans = 1; p.q_kscale = nullptr;
+  p.out = out; p.ldo = ldo; p.scale = 1.f;
+  p.P2 = nullptr; p.p_split2 = p.M; p.ldp2 = ldp; p.out2 = nullptr; p.ldo2 = 0;
+  p.pk = pk; p.pk_rp = pk_rp; p.pk_scale = pk_scale;
+  *packed = pk != nullptr && rowproj_packs(p);
+  if (!*packed) p.pk = nullptr;
+  return launch_rowproj(p, st);
 }
 
 // out[m, j] = scale * sum_k P[m, k] * bf16(Bq[k, j] * kscale[k]) with Bq a [K, R] matrix, leading dim ldb
@@ -309,6 +330,7 @@ hipError_t rowproj_t(int M, int K, int R, const void* P, int ldp, const void* Bq
   p.q_trans = 1; p.q_kscale = kscale;
   p.out = out; p.ldo = ldo; p.scale = scale;
   p.P2 = nullptr; p.p_split2 = p.M; p.ldp2 = ldp; p.out2 = nullptr; p.ldo2 = 0;
+  p.pk = nullptr; p.pk_rp = 0; p.pk_scale = 1.f;
   return launch_rowproj(p, st);
 }
 
@@ -322,6 +344,7 @@ ColProjParams cpp(int M, int C, int R, const void* X, int ldx, const float* Sm, 
   p.msplit = msplit; p.part = part; p.cspart = cspart;
   p.spk = nullptr;
   p.S16 = nullptr;
+  p.spk_ready = false;
   return p;
 }
 
@@ -1030,15 +1053,22 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, c
     LDL_TRY(zero(w.partT, (size_t)w.nsT * N * w.rp, st));
     LDL_TRY(zero(w.cs, (size_t)w.nsT * N, st));
   }
+  // The rank-r factors of the last column projections are written pre-packed (bf16 hi / lo,
+  // the layout pack_s_kernel writes) by the kernels that form them, where that path applies
+  // (ranks 17 .. 64): wB by the finalize pass, V by its row projection.  No pack pass then.
+  const bool prepack = w.rp >= 32 && w.rp <= 64;
   // dB, dm and wB = 2s.w.B per output row
-  LDL_TRY(launch_dora_finalize(N, r, s, eps, w.partT, w.cs, w.nsT, w.rp, norm, g, m, P, G, Bh, dB, dm, w.wB, st));
+  LDL_TRY(launch_dora_finalize(N, r, s, eps, w.partT, w.cs, w.nsT, w.rp, norm, g, m, P, G, Bh, dB, dm, w.wB,
+                               prepack ? reinterpret_cast<uint16_t*>(w.pkW) : nullptr, w.rp, st));
   ColProjParams jobs[3];
   int ns[3], nj = 0;
+  bool v_packed = false;
   if (M > 0) {
     // dZ = dY.diag(g) is never formed: the row scale goes into bf16 copies of the weight and of
     // lora_up (rounded once, weight-sized), V = dY.(diag(g).B) and dX = dY.(diag(g).W0) + s.V.A
     LDL_TRY(launch_scale_rows(W0, N, dX ? K : 0, ldw, B, r, g, w.gW0, w.gB, st));
-    LDL_TRY(rowproj_t(M, N, r, dY, lddy, w.gB, r, nullptr, w.V, r, 1.f, st));
+    LDL_TRY(rowproj_t_pk(M, N, r, dY, lddy, w.gB, r, w.V, r, prepack ? reinterpret_cast<uint16_t*>(w.pkA) : nullptr,
+                         w.rp, s, &v_packed, st));
     if (dX) {
       GemmParams p = gp0();
       p.M = M; p.N = K; p.K = N;
@@ -1050,15 +1080,18 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, c
     }
     // s.V^T.X into the first nsA partials of dA
     jobs[nj] = pk(cpp(M, K, r, X, ldx, w.V, r, s, nullptr, 0, 0, w.msA, w.partA, nullptr), w.pkA);
+    jobs[nj].spk_ready = v_packed;
     ns[nj++] = w.nsA;
   } else {
     LDL_TRY(zero(w.partA, (size_t)w.nsA * K * w.rp, st));
   }
-  // (2s.w.B)^T.W0 into the next nsW partials; Q = B^T.(2s.w.B)
+  // (2s.w.B)^T.W0 into the next nsW partials; Q = B^T.(2s.w.B) (both read the one packed wB)
   jobs[nj] = pk(cpp(N, K, r, W0, ldw, w.wB, r, 1.f, nullptr, 0, 0, w.msW, w.partA + (size_t)w.nsA * K * w.rp,
                     nullptr), w.pkW);
+  jobs[nj].spk_ready = prepack;
   ns[nj++] = w.nsW;
-  jobs[nj] = pk(cpp(N, r, r, B, r, w.wB, r, 1.f, nullptr, 0, 0, w.msQ, w.partQ, nullptr), w.pkQ);
+  jobs[nj] = pk(cpp(N, r, r, B, r, w.wB, r, 1.f, nullptr, 0, 0, w.msQ, w.partQ, nullptr), prepack ? w.pkW : w.pkQ);
+  jobs[nj].spk_ready = prepack;
   ns[nj++] = w.nsQ;
   LDL_TRY(launch_colproj_batch(jobs, ns, nj, st));
   LDL_TRY(reduce(r, r, w.partQ, (size_t)r * w.rp, w.nsQ, w.rp, false, 1.f, w.Qm, r, st));

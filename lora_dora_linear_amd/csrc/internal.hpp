@@ -20,6 +20,9 @@ struct RowProjParams {
   // m - p_split2, leading dim ldp2) and go to out2 (row m - p_split2, leading dim ldo2)
   const uint16_t* P2; int p_split2; int ldp2;
   float* out2; int ldo2;
+  // optional (streamed kernel, one segment): also write pk_scale * out in the packed bf16
+  // hi / lo layout a column projection of rank padding pk_rp reads (pack_s_kernel's layout)
+  uint16_t* pk; int pk_rp; float pk_scale;
 };
 
 struct ColProjParams {
@@ -36,6 +39,7 @@ struct ColProjParams {
                                    // colproj_spk_words(M, R) words (used from rank 32 up)
   const uint16_t* S16;             // optional: S given in bf16 (row stride lds) instead of fp32;
                                    // only where colproj_takes_bf16_s says so
+  bool spk_ready;                  // spk already holds s_in * S packed (no pack pass)
 };
 
 struct ReduceParams {
@@ -69,6 +73,7 @@ size_t gemm_split_bytes(int M, int N);
 
 hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st);
 bool rowproj_three_ok(const RowProjParams& p);   // the streamed kernel takes P2
+bool rowproj_packs(const RowProjParams& p);       // the streamed kernel takes p with its pk
 int colproj_rp(int R);
 // whether a column-projection batch runs on the packed streaming path, which can read S in bf16
 bool colproj_takes_bf16_s(const ColProjParams* jobs, int njobs);
@@ -104,7 +109,7 @@ hipError_t launch_swiglu_bwd(void* dE, int ld_de, const void* E, int ld_e, const
 hipError_t launch_dora_finalize(int N, int r, float s, float eps, const float* partT, const float* cspart,
                                 int nsplit, int rpT, const float* norm, const float* g, const float* m,
                                 const float* P, const float* G, const uint16_t* B,
-                                float* dB, float* dm, float* wB, hipStream_t st);
+                                float* dB, float* dm, float* wB, uint16_t* wB_pk, int pk_rp, hipStream_t st);
 
 // LoRA merge: W = W0 + s.B.A (W0 may be null: the delta alone); bf16 or fp32 elements
 hipError_t launch_merge(int N, int K, int r, float s, int bf16, const void* W0, int ldw, const void* A, const void* B,

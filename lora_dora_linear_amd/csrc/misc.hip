@@ -103,7 +103,8 @@ __global__ __launch_bounds__(256) void dora_finalize_kernel(int N, int r, float 
                                                             const float* cspart, int nsplit, int rpT,
                                                             const float* norm, const float* g, const float* m,
                                                             const float* P, const float* G, const uint16_t* B,
-                                                            float* dB, float* dm, float* wB) {
+                                                            float* dB, float* dm, float* wB, uint16_t* wB_pk,
+                                                            int pk_rp) {
   extern __shared__ float sG[];
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -169,6 +170,17 @@ __global__ __launch_bounds__(256) void dora_finalize_kernel(int N, int r, float 
   if (h1) {
     dB[(size_t)n * r + lane + 64] = s * gn * t1 + w * (2.f * s * p1 + 2.f * s * s * bg1);
     wB[(size_t)n * r + lane + 64] = 2.f * s * w * b1;
+  }
+  if (wB_pk != nullptr && lane < pk_rp) {
+    // wB also in the packed bf16 hi / lo layout of the column projections that read it
+    // (rank padding pk_rp <= 64, zero past r): row n is half (n & 1) of word
+    // 4 lane + ((n & 7) >> 1) of its 8-row group (hi) and of word 4 (pk_rp + lane) + .. (lo)
+    const float x = h0 ? 2.f * s * w * b0 : 0.f;
+    const uint32_t hi = f32_to_bf16_bits(x);
+    uint16_t* grp = wB_pk + (size_t)(n >> 3) * (16 * pk_rp) + (n & 1);
+    const int e = (n & 7) >> 1;
+    grp[2 * (4 * lane + e)] = (uint16_t)hi;
+    grp[2 * (4 * (pk_rp + lane) + e)] = (uint16_t)f32_to_bf16_bits(x - __uint_as_float(hi << 16));
   }
 }
 
@@ -288,9 +300,10 @@ hipError_t launch_dora_norm(int N, int r, float s, float eps, const float* w0_su
 hipError_t launch_dora_finalize(int N, int r, float s, float eps, const float* partT, const float* cspart,
                                 int nsplit, int rpT, const float* norm, const float* g, const float* m,
                                 const float* P, const float* G, const uint16_t* B,
-                                float* dB, float* dm, float* wB, hipStream_t st) {
+                                float* dB, float* dm, float* wB, uint16_t* wB_pk, int pk_rp, hipStream_t st) {
+  if (wB_pk != nullptr && (pk_rp < r || pk_rp > 64 || N % 8)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(dora_finalize_kernel, dim3((N + 3) / 4), dim3(256), r * r * sizeof(float), st,
-                     N, r, s, eps, partT, cspart, nsplit, rpT, norm, g, m, P, G, B, dB, dm, wB);
+                     N, r, s, eps, partT, cspart, nsplit, rpT, norm, g, m, P, G, B, dB, dm, wB, wB_pk, pk_rp);
   return hipGetLastError();
 }
 

@@ -296,6 +296,22 @@ __global__ __launch_bounds__(256) void rowstream_kernel(const RowProjParams p) {
       for (int i = 0; i < 4; ++i)
         if (j0 + i < p.R) dst[j0 + i] = v[i] * p.scale;
     }
+    if (p.pk != nullptr && m < ((p.M + 7) & ~7)) {
+      // the packed copy: pk_scale * out as bf16 hi and lo (zero past R and past M), 16 bits
+      // per value: row m is half (m & 1) of word 4 j + ((m & 7) >> 1) of its 8-row group
+      // (hi) and of word 4 (pk_rp + j) + ((m & 7) >> 1) (lo)
+      uint16_t* g = p.pk + (size_t)(m >> 3) * (16 * p.pk_rp) + (m & 1);
+      const int e = (m & 7) >> 1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = jb * 16 + 4 * lq + i;
+        if (j >= p.pk_rp) continue;
+        const float x = (m < p.M && j < p.R) ? (v[i] * p.scale) * p.pk_scale : 0.f;
+        const uint32_t hi = f32_to_bf16_bits(x);
+        g[2 * (4 * j + e)] = (uint16_t)hi;
+        g[2 * (4 * (p.pk_rp + j) + e)] = (uint16_t)f32_to_bf16_bits(x - __uint_as_float(hi << 16));
+      }
+    }
   }
 }
 
@@ -832,6 +848,12 @@ static bool rowstream32(const RowProjParams& p, int rp) {
   return g_rowstream32 == 2 || (p.M + 31) / 32 >= 256;
 }
 
+bool rowproj_packs(const RowProjParams& p) {
+  if (p.M <= 0 || p.P2 != nullptr) return false;
+  const int rp = p.R <= 16 ? 16 : p.R <= 32 ? 32 : p.R <= 64 ? 64 : 128;
+  return rowstream_ok(p, rp) && p.pk_rp == rp && !rowstream32(p, rp);
+}
+
 bool rowproj_three_ok(const RowProjParams& p) {
   const int rp = p.R <= 16 ? 16 : p.R <= 32 ? 32 : p.R <= 64 ? 64 : 128;
   return p.P2 != nullptr && rowstream_ok(p, rp);
@@ -840,7 +862,8 @@ bool rowproj_three_ok(const RowProjParams& p) {
 hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st) {
   if (p.M <= 0) return hipSuccess;
   const int rp = p.R <= 16 ? 16 : p.R <= 32 ? 32 : p.R <= 64 ? 64 : 128;
-  if (p.P2 != nullptr && !rowstream_ok(p, rp)) return hipErrorInvalidValue;   // (callers check first)
+  if ((p.P2 != nullptr || p.pk != nullptr) && !rowstream_ok(p, rp)) return hipErrorInvalidValue;   // (callers check first)
+  if (p.pk != nullptr && (p.P2 != nullptr || p.pk_rp != rp || rowstream32(p, rp))) return hipErrorInvalidValue;
   if (rowstream_ok(p, rp)) {
     if (rowstream32(p, rp)) {
       if (rp == 64) hipLaunchKernelGGL((rowstream_kernel<64, false, 32>), dim3((p.M + 31) / 32), dim3(256), 0, st, p);
@@ -919,6 +942,7 @@ static hipError_t pack_s_launch(const ColProjParams* jobs, int njobs, int RP, hi
   int nj = 0, maxt = 0;
   for (int i = 0; i < njobs; ++i) {
     if (jobs[i].R <= 0 || jobs[i].M <= 0) continue;
+    if (jobs[i].spk_ready) continue;               // packed by the kernel that wrote S
     b.S[nj] = jobs[i].S; b.S16[nj] = jobs[i].S16; b.lds[nj] = jobs[i].lds; b.M[nj] = jobs[i].M; b.R[nj] = jobs[i].R;
     b.s_in[nj] = jobs[i].s_in; b.out[nj] = jobs[i].spk;
     const int tcount = ((jobs[i].M + 7) / 8) * RP;
