@@ -304,14 +304,14 @@ hipError_t rowproj3(int M0, int M1, int M2, int K, int R, const void* P, int ldp
 // rowproj_t with no k-scale that also writes pk_scale * out packed for a column projection of
 // rank padding pk_rp, where the streamed kernel takes it (*packed says whether it did)
 hipError_t rowproj_t_pk(int M, int K, int R, const void* P, int ldp, const void* Bq, int ldb, float* out, int ldo,
-                        uint16_t* pk, int pk_rp, float pk_scale, bool* packed, hipStream_t st) {
+                        float scale, uint16_t* pk, int pk_rp, float pk_scale, bool* packed, hipStream_t st) {
   RowProjParams p;
   p.M = M; p.K = K; p.R = R; p.R0 = R;
   p.P = static_cast<const uint16_t*>(P); p.ldp = ldp;
   p.P1 = nullptr; p.p_split = M; p.ldp1 = ldp;
   p.q0 = p.q1 = static_cast<const uint16_t*>(Bq); p.ldq = ldb;
   p.q_trans = 1; p.q_kscale = nullptr;
-  p.out = out; p.ldo = ldo; p.scale = 1.f;
+  p.out = out; p.ldo = ldo; p.scale = scale;
   p.P2 = nullptr; p.p_split2 = p.M; p.ldp2 = ldp; p.out2 = nullptr; p.ldo2 = 0;
   p.pk = pk; p.pk_rp = pk_rp; p.pk_scale = pk_scale;
   *packed = pk != nullptr && rowproj_packs(p);
@@ -1067,8 +1067,8 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, c
     // dZ = dY.diag(g) is never formed: the row scale goes into bf16 copies of the weight and of
     // lora_up (rounded once, weight-sized), V = dY.(diag(g).B) and dX = dY.(diag(g).W0) + s.V.A
     LDL_TRY(launch_scale_rows(W0, N, dX ? K : 0, ldw, B, r, g, w.gW0, w.gB, st));
-    LDL_TRY(rowproj_t_pk(M, N, r, dY, lddy, w.gB, r, w.V, r, prepack ? reinterpret_cast<uint16_t*>(w.pkA) : nullptr,
-                         w.rp, s, &v_packed, st));
+    LDL_TRY(rowproj_t_pk(M, N, r, dY, lddy, w.gB, r, w.V, r, 1.f,
+                         prepack ? reinterpret_cast<uint16_t*>(w.pkA) : nullptr, w.rp, s, &v_packed, st));
     if (dX) {
       GemmParams p = gp0();
       p.M = M; p.N = K; p.K = N;
@@ -1350,8 +1350,13 @@ static int glu_mlp_bwd(int act, int M, int K, int H, int r, float s_gate, float 
   LDL_TRY(launch_reduce2(rdp(K, r, w.partDd, (size_t)K * w.rp, w.nsDd, w.rp, false, s_down, dBd, r),
                          rdp(r, H, w.partAd, (size_t)H * w.rp, w.nsAd, w.rp, true, s_down, dAd, H), st));
   // ---- gate / up: V_g = s_g.dE.Bg, V_u = s_u.dGu.Bu (pre-scaled), dBg, dBu
-  LDL_TRY(rowproj_t(M, H, r, w.dEGu, 2 * H, Bg, r, nullptr, w.Vgu, 2 * r, s_gate, st));
-  LDL_TRY(rowproj_t(M, H, r, w.dEGu + H, 2 * H, Bu, r, nullptr, w.Vgu + r, 2 * r, s_up, st));
+  // (with dAg and dAu as two rank-r column projections, V_g and V_u are also written packed
+  // for them by these launches, so that projection needs no pack pass)
+  uint16_t* pk_g = w.agu_split ? reinterpret_cast<uint16_t*>(w.pkAgu) : nullptr;
+  uint16_t* pk_u = w.agu_split ? reinterpret_cast<uint16_t*>(w.pkAgu + colproj_spk_words(M, r)) : nullptr;
+  bool g_packed = false, u_packed = false;
+  LDL_TRY(rowproj_t_pk(M, H, r, w.dEGu, 2 * H, Bg, r, w.Vgu, 2 * r, s_gate, pk_g, w.rp, 1.f, &g_packed, st));
+  LDL_TRY(rowproj_t_pk(M, H, r, w.dEGu + H, 2 * H, Bu, r, w.Vgu + r, 2 * r, s_up, pk_u, w.rp, 1.f, &u_packed, st));
   LDL_TRY(launch_colproj2(pk(cpp(M, H, r, w.dEGu, 2 * H, Ug, r3, 1.f, nullptr, 0, 0, w.msBg, w.partBg, nullptr), w.pkBg),
                           w.nsBg,
                           pk(cpp(M, H, r, w.dEGu + H, 2 * H, Uu, r3, 1.f, nullptr, 0, 0, w.msBg, w.partBu, nullptr),
@@ -1372,11 +1377,12 @@ static int glu_mlp_bwd(int act, int M, int K, int H, int r, float s_gate, float 
   // dAg, dAu = [V_g | V_u]^T.X in one pass over X
   if (w.agu_split) {
     float* partAu = w.partAgu + (size_t)w.nsAgu * K * w.rp;
-    LDL_TRY(launch_colproj2(
-        pk(cpp(M, K, r, X, ldx, w.Vgu, 2 * r, 1.f, nullptr, 0, 0, w.msAgu, w.partAgu, nullptr), w.pkAgu), w.nsAgu,
-        pk(cpp(M, K, r, X, ldx, w.Vgu + r, 2 * r, 1.f, nullptr, 0, 0, w.msAgu, partAu, nullptr),
-           w.pkAgu + colproj_spk_words(M, r)),
-        w.nsAgu, st));
+    ColProjParams jg = pk(cpp(M, K, r, X, ldx, w.Vgu, 2 * r, 1.f, nullptr, 0, 0, w.msAgu, w.partAgu, nullptr), w.pkAgu);
+    ColProjParams ju = pk(cpp(M, K, r, X, ldx, w.Vgu + r, 2 * r, 1.f, nullptr, 0, 0, w.msAgu, partAu, nullptr),
+                          w.pkAgu + colproj_spk_words(M, r));
+    jg.spk_ready = g_packed;
+    ju.spk_ready = u_packed;
+    LDL_TRY(launch_colproj2(jg, w.nsAgu, ju, w.nsAgu, st));
     LDL_TRY(launch_reduce2(rdp(r, K, w.partAgu, (size_t)K * w.rp, w.nsAgu, w.rp, true, 1.f, dAg, K),
                            rdp(r, K, partAu, (size_t)K * w.rp, w.nsAgu, w.rp, true, 1.f, dAu, K), st));
   } else {

@@ -851,7 +851,7 @@ static bool rowstream32(const RowProjParams& p, int rp) {
 bool rowproj_packs(const RowProjParams& p) {
   if (p.M <= 0 || p.P2 != nullptr) return false;
   const int rp = p.R <= 16 ? 16 : p.R <= 32 ? 32 : p.R <= 64 ? 64 : 128;
-  return rowstream_ok(p, rp) && p.pk_rp == rp && !rowstream32(p, rp);
+  return rowstream_ok(p, rp) && p.pk_rp == rp;
 }
 
 bool rowproj_three_ok(const RowProjParams& p) {
@@ -863,7 +863,7 @@ hipError_t launch_rowproj(const RowProjParams& p, hipStream_t st) {
   if (p.M <= 0) return hipSuccess;
   const int rp = p.R <= 16 ? 16 : p.R <= 32 ? 32 : p.R <= 64 ? 64 : 128;
   if ((p.P2 != nullptr || p.pk != nullptr) && !rowstream_ok(p, rp)) return hipErrorInvalidValue;   // (callers check first)
-  if (p.pk != nullptr && (p.P2 != nullptr || p.pk_rp != rp || rowstream32(p, rp))) return hipErrorInvalidValue;
+  if (p.pk != nullptr && (p.P2 != nullptr || p.pk_rp != rp)) return hipErrorInvalidValue;
   if (rowstream_ok(p, rp)) {
     if (rowstream32(p, rp)) {
       if (rp == 64) hipLaunchKernelGGL((rowstream_kernel<64, false, 32>), dim3((p.M + 31) / 32), dim3(256), 0, st, p);
