@@ -301,27 +301,10 @@ hipError_t rowproj3(int M0, int M1, int M2, int K, int R, const void* P, int ldp
   return rowproj(M2, K, R, P2, ldp2, q0, nullptr, R, ldq, out2, ldo2, 1.f, st);
 }
 
-// rowproj_t with no k-scale that also writes pk_scale * out packed for a column projection of
-// rank padding pk_rp, where the streamed kernel takes it (*packed says whether it did)
-hipError_t rowproj_t_pk(int M, int K, int R, const void* P, int ldp, const void* Bq, int ldb, float* out, int ldo,
-                        float scale, uint16_t* pk, int pk_rp, float pk_scale, bool* packed, hipStream_t st) {
-  RowProjParams p;
-  p.M = M; p.K = K; p.R = R; p.R0 = R;
-  p.P = static_cast<const uint16_t*>(P); p.ldp = ldp;
-  p.P1 = nullptr; p.p_split = M; p.ldp1 = ldp;
-  p.q0 = p.q1 = static_cast<const uint16_t*>(Bq); p.ldq = ldb;
-  p.q_trans = 1; p.q_kscale = nullptr;
-  p.out = out; p.ldo = ldo; p.scale = scale;
-  p.P2 = nullptr; p.p_split2 = p.M; p.ldp2 = ldp; p.out2 = nullptr; p.ldo2 = 0;
-  p.pk = pk; p.pk_rp = pk_rp; p.pk_scale = pk_scale;
-  *packed = pk != nullptr && rowproj_packs(p);
-  if (!*packed) p.pk = nullptr;
-  return launch_rowproj(p, st);
-}
-
-// out[m, j] = scale * sum_k P[m, k] * bf16(Bq[k, j] * kscale[k]) with Bq a [K, R] matrix, leading dim ldb
-hipError_t rowproj_t(int M, int K, int R, const void* P, int ldp, const void* Bq, int ldb, const float* kscale,
-                     float* out, int ldo, float scale, hipStream_t st) {
+// The parameters of a row projection against a transposed Q: out[m, j] = scale * sum_k P[m, k]
+// * bf16(Bq[k, j] * kscale[k]) with Bq a [K, R] matrix of leading dim ldb (kscale optional)
+static RowProjParams rowproj_t_params(int M, int K, int R, const void* P, int ldp, const void* Bq, int ldb,
+                                      const float* kscale, float* out, int ldo, float scale) {
   RowProjParams p;
   p.M = M; p.K = K; p.R = R; p.R0 = R;
   p.P = static_cast<const uint16_t*>(P); p.ldp = ldp;
@@ -331,6 +314,22 @@ hipError_t rowproj_t(int M, int K, int R, const void* P, int ldp, const void* Bq
   p.out = out; p.ldo = ldo; p.scale = scale;
   p.P2 = nullptr; p.p_split2 = p.M; p.ldp2 = ldp; p.out2 = nullptr; p.ldo2 = 0;
   p.pk = nullptr; p.pk_rp = 0; p.pk_scale = 1.f;
+  return p;
+}
+
+hipError_t rowproj_t(int M, int K, int R, const void* P, int ldp, const void* Bq, int ldb, const float* kscale,
+                     float* out, int ldo, float scale, hipStream_t st) {
+  return launch_rowproj(rowproj_t_params(M, K, R, P, ldp, Bq, ldb, kscale, out, ldo, scale), st);
+}
+
+// rowproj_t with no k-scale that also writes pk_scale * out packed for a column projection of
+// rank padding pk_rp, where the streamed kernel takes it (*packed says whether it did)
+hipError_t rowproj_t_pk(int M, int K, int R, const void* P, int ldp, const void* Bq, int ldb, float* out, int ldo,
+                        float scale, uint16_t* pk, int pk_rp, float pk_scale, bool* packed, hipStream_t st) {
+  RowProjParams p = rowproj_t_params(M, K, R, P, ldp, Bq, ldb, nullptr, out, ldo, scale);
+  p.pk = pk; p.pk_rp = pk_rp; p.pk_scale = pk_scale;
+  *packed = pk != nullptr && rowproj_packs(p);
+  if (!*packed) p.pk = nullptr;
   return launch_rowproj(p, st);
 }
 
