@@ -71,6 +71,36 @@ def test_lora_strided(dtype, M, N, K, r):
         assert_close(host(gs[k]), gr[k], tol_g, k)
 
 
+def test_lora_fp32_odd_strides():
+    """fp32 rows whose strides are not a multiple of four floats (16-byte aligned bases, odd
+    leading dimensions): the one-launch small-layer kernels load rows 16 bytes at a time and
+    are not taken, the general fp32 products are; results match the oracle, and the columns
+    outside the output slices stay untouched."""
+    require_gpu()
+    import lora_dora_linear_amd as L
+    M, N, K, r = 64, 256, 256, 8
+    c = inputs.linear_case(32, M, N, K, r, 0.5, "f32", with_bias=True)
+    X, W0, A, B, dY, bias = (dev(c.t[k], "f32") for k in ("X", "W0", "A", "B", "dY", "bias"))
+    _, Xs = _embed(X, 4, 1)
+    _, W0s = _embed(W0, 8, 3)
+    _, dYs = _embed(dY, 4, 5)
+    Ybig, Ys = _slot((M, N), torch.float32, 4, 1)
+    Ubig, Us = _slot((M, r), torch.float32, 4, 1)
+    dXbig, dXs = _slot((M, K), torch.float32, 4, 3)
+    assert Xs.stride(0) % 4 and W0s.stride(0) % 4 and dYs.stride(0) % 4 and Ys.stride(0) % 4
+    L.lora_linear_fwd(Xs, W0s, A, B, c.s, bias=bias, Y=Ys, U=Us)
+    gs = L.lora_linear_bwd(dYs, Xs, W0s, A, B, c.s, U=Us, dX=dXs, need_dbias=True)
+    torch.cuda.synchronize()
+    assert _untouched(Ybig, N, 4) and _untouched(dXbig, K, 4) and _untouched(Ubig, r, 4)
+    Xf, W0f, Af, Bf, dYf = (c.f64(k) for k in ("X", "W0", "A", "B", "dY"))
+    assert_close(host(Ys), olora.lora_forward(Xf, W0f, Af, Bf, c.s, bias=c.f64("bias")), 1e-5, "Y")
+    assert_close(host(Us), Xf @ Af.T, 1e-5, "U")
+    gr = olora.lora_backward(dYf, Xf, W0f, Af, Bf, c.s)
+    for k in ("dX", "dA", "dB"):
+        assert_close(host(gs[k]), gr[k], 1e-4, k)
+    assert_close(host(gs["dbias"]), gr["db"], 1e-4, "dbias")
+
+
 def test_dora_strided():
     require_gpu()
     import lora_dora_linear_amd as L
