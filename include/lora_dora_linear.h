@@ -102,8 +102,14 @@ int ldl_version(void);
  *     (U = X.A^T, V = dY.B and their like) on 32-row blocks that stage the rank
  *     factor once per 32 rows: 1 when those blocks still fill the 256 CUs
  *     (M >= 8161), 2 whenever the rank allows, 0 never.  Results are identical.
+ *   LDL_TUNE_PREPACK (0/1, default 1): in the DoRA and gated-MLP backwards, the rank
+ *     factors of the last column projections (ranks 17..64) written in their packed
+ *     bf16 hi / lo form by the kernels that compute them, instead of by a separate
+ *     packing pass (0).  Results are identical.
  * Returns LDL_OK, or LDL_E_INVAL for an unknown key or value. */
-typedef enum { LDL_TUNE_FWD_FUSED_DOWNPROJ = 0, LDL_TUNE_GEMM_4WAVE = 1, LDL_TUNE_ROWSTREAM_32 = 2 } ldl_tune_key;
+typedef enum {
+  LDL_TUNE_FWD_FUSED_DOWNPROJ = 0, LDL_TUNE_GEMM_4WAVE = 1, LDL_TUNE_ROWSTREAM_32 = 2, LDL_TUNE_PREPACK = 3
+} ldl_tune_key;
 int ldl_set_tuning(int key, int value);
 
 /* Kernel timing hook for profilers and benchmarks.  While set, the library

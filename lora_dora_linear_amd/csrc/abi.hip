@@ -35,6 +35,7 @@ void* scratch_for_current_device() {
 }
 
 int g_fwd_fused = 0;   // LDL_TUNE_FWD_FUSED_DOWNPROJ
+int g_prepack = 1;     // LDL_TUNE_PREPACK
 
 // Kernel timing hook (ldl_set_kernel_events).
 struct EventHook {
@@ -479,6 +480,10 @@ int ldl_set_tuning(int key, int value) {
   }
   if (key == LDL_TUNE_ROWSTREAM_32 && value >= 0 && value <= 2) {
     g_rowstream32 = value;
+    return LDL_OK;
+  }
+  if (key == LDL_TUNE_PREPACK && (value == 0 || value == 1)) {
+    g_prepack = value;
     return LDL_OK;
   }
 
@@ -1055,7 +1060,7 @@ int dora_linear_bwd(int M, int N, int K, int r, float s, float eps, int dtype, c
   // The rank-r factors of the last column projections are written pre-packed (bf16 hi / lo,
   // the layout pack_s_kernel writes) by the kernels that form them, where that path applies
   // (ranks 17 .. 64): wB by the finalize pass, V by its row projection.  No pack pass then.
-  const bool prepack = w.rp >= 32 && w.rp <= 64;
+  const bool prepack = g_prepack && w.rp >= 32 && w.rp <= 64;
   // dB, dm and wB = 2s.w.B per output row
   LDL_TRY(launch_dora_finalize(N, r, s, eps, w.partT, w.cs, w.nsT, w.rp, norm, g, m, P, G, Bh, dB, dm, w.wB,
                                prepack ? reinterpret_cast<uint16_t*>(w.pkW) : nullptr, w.rp, st));
@@ -1351,8 +1356,9 @@ static int glu_mlp_bwd(int act, int M, int K, int H, int r, float s_gate, float 
   // ---- gate / up: V_g = s_g.dE.Bg, V_u = s_u.dGu.Bu (pre-scaled), dBg, dBu
   // (with dAg and dAu as two rank-r column projections, V_g and V_u are also written packed
   // for them by these launches, so that projection needs no pack pass)
-  uint16_t* pk_g = w.agu_split ? reinterpret_cast<uint16_t*>(w.pkAgu) : nullptr;
-  uint16_t* pk_u = w.agu_split ? reinterpret_cast<uint16_t*>(w.pkAgu + colproj_spk_words(M, r)) : nullptr;
+  const bool prepack = g_prepack && w.agu_split;
+  uint16_t* pk_g = prepack ? reinterpret_cast<uint16_t*>(w.pkAgu) : nullptr;
+  uint16_t* pk_u = prepack ? reinterpret_cast<uint16_t*>(w.pkAgu + colproj_spk_words(M, r)) : nullptr;
   bool g_packed = false, u_packed = false;
   LDL_TRY(rowproj_t_pk(M, H, r, w.dEGu, 2 * H, Bg, r, w.Vgu, 2 * r, s_gate, pk_g, w.rp, 1.f, &g_packed, st));
   LDL_TRY(rowproj_t_pk(M, H, r, w.dEGu + H, 2 * H, Bu, r, w.Vgu + r, 2 * r, s_up, pk_u, w.rp, 1.f, &u_packed, st));

@@ -94,6 +94,9 @@ def test_tuning_switch(L):
     for v in (0, 2, 1):
         assert L.ldl_set_tuning(2, v) == OK
     assert L.ldl_set_tuning(2, 3) == INVAL
+    for v in (0, 1):
+        assert L.ldl_set_tuning(3, v) == OK
+    assert L.ldl_set_tuning(3, 2) == INVAL
 
 
 def test_kernel_event_hook_arguments(L):

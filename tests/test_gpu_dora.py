@@ -72,6 +72,24 @@ def test_dora_rank64_norm_terms_and_u_in_one_row_launch():
         assert_close(host(g[k]), gr[k], TOL, k)
 
 
+@pytest.mark.parametrize("r", [32, 64])
+def test_dora_prepacked_factors_match_the_packing_pass(r):
+    """V and w.B written packed by the kernels that form them give the same bits as packing
+    them in a separate pass (every gradient, equal)."""
+    require_gpu()
+    from lora_dora_linear_amd import binding
+    c = inputs.linear_case(11, 300, 384, 256, r, 1.0, "bf16", with_bias=True, dora=True)
+    try:
+        binding.set_tuning(3, 1)
+        _, _, _, g1, _ = _run(c, 1e-12, with_bias=True, need_dbias=True)
+        binding.set_tuning(3, 0)
+        _, _, _, g0, _ = _run(c, 1e-12, with_bias=True, need_dbias=True)
+    finally:
+        binding.set_tuning(3, 1)
+    for k in ("dX", "dA", "dB", "dm", "dbias"):
+        assert torch.equal(g1[k], g0[k]), k
+
+
 def test_dora_unit_scale_is_base():
     """B = 0 and m = ||W0_n||: g = 1 and Y = X.W0^T."""
     require_gpu()

@@ -25,6 +25,24 @@ def _run(c):
     return Out, saved, g
 
 
+def test_swiglu_prepacked_factors_match_the_packing_pass():
+    """r = 64 (dAg, dAu as two rank-64 column projections): V_g and V_u written packed by their
+    row projections give the same bits as packing them in a separate pass."""
+    require_gpu()
+    from lora_dora_linear_amd import binding
+    c = inputs.mlp_case(9, 300, 256, 384, 64, 0.25)
+    try:
+        binding.set_tuning(3, 1)
+        _, _, g1 = _run(c)
+        binding.set_tuning(3, 0)
+        _, _, g0 = _run(c)
+    finally:
+        binding.set_tuning(3, 1)
+    for k in g1:
+        if g1[k] is not None:
+            assert torch.equal(g1[k], g0[k]), k
+
+
 @pytest.mark.parametrize("M,K,H,r", [(200, 256, 384, 16), (300, 384, 256, 64), (64, 256, 512, 32),
                                      (100, 192, 256, 16), (300, 256, 320, 16)])
 def test_swiglu_parity(M, K, H, r):
