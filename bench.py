@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--fused-downproj", type=int, default=None, choices=[0, 1])
     ap.add_argument("--gemm-4wave", type=int, default=None, choices=[0, 1],
                     help="four-wave 256x256 tile for the plain NT products (library default 1)")
+    ap.add_argument("--step-times", action="store_true",
+                    help="also report every timed step's duration (fence-free events between steps)")
     ap.add_argument("--copy-calibrate", type=int, default=None, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (reference kernel for the HBM byte counters)")
     return ap.parse_args()
@@ -113,6 +115,13 @@ class TimingEvents:
     def record(self, i, stream):
         if self.hip.hipEventRecord(self.arr[i], stream) != 0:
             raise RuntimeError("hipEventRecord failed")
+
+    def between_ms(self, i, j):
+        """Milliseconds from this set's event i to its event j."""
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[i], self.arr[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
 
     def elapsed_ms(self, stop, i):
         """Milliseconds from this set's event i to stop's event i."""
@@ -519,10 +528,15 @@ def main():
         keep.append((a, b))
         check(L.ldl_set_kernel_events(k, a, b, K_steps), "ldl_set_kernel_events")
     t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = TimingEvents(K_steps + 1) if args.step_times else None
     torch.cuda.synchronize()
     t_start.record()
-    for _ in range(K_steps):
+    if marks is not None:
+        marks.record(0, st())
+    for i in range(K_steps):
         step()
+        if marks is not None:
+            marks.record(i + 1, st())
     t_stop.record()
     torch.cuda.synchronize()
     for k in hook_kinds:
@@ -576,6 +590,8 @@ def main():
                            "traffic": None if traffic is None else int(traffic)}
         out["kernels"] = {names[k]: {"avg_us": round(v["avg_us"], 2), "TFLOP/s": round(v["tflops"], 1)}
                           for k, v in kern.items()}
+    if marks is not None:
+        out["step_us"] = [round(1e3 * marks.between_ms(i, i + 1), 1) for i in range(K_steps)]
     if act_pass is not None:
         out["activation_pass"] = act_pass
     if prep is not None:
