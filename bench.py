@@ -489,7 +489,11 @@ def main():
         code_t = torch.uint8 if f8 else torch.int8
         Wq = torch.empty((N, K), dtype=code_t, device=dev)
         sw = torch.empty((N,), dtype=f32, device=dev)
-        check(getattr(L, pre + "_quantize_weight")(N, K, 0, P(W0f), K, P(Wq), P(sw), st()), pre + "_quantize_weight")
+        prep = (lambda: check(getattr(L, pre + "_quantize_weight")(N, K, 0, P(W0f), K, P(Wq), P(sw), st()),  # noqa
+                              pre + "_quantize_weight"),
+                ("e4m3" if f8 else "int8") + " per-channel codes of the frozen fp32 weight (once per weight)",
+                4.0 * N * K + 1.0 * N * K + 4.0 * N)
+        prep[0]()
         fwd, bwd = getattr(L, pre + "_lora_linear_fwd"), getattr(L, pre + "_lora_linear_bwd")
         Y = torch.empty((M, N), dtype=bf, device=dev)
         Xq = torch.empty((M, K), dtype=code_t, device=dev)
